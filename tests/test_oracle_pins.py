@@ -1,0 +1,343 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+hand-worked fixtures, closed forms, exact integer arithmetic, brute force on
+tiny inputs and invariants.  CPU only."""
+import json
+import math
+import os
+import random
+
+import numpy as np
+import pytest
+
+import oracle as orc
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+# ----------------------------------------------------------------------------- format
+
+def test_blob_size_matches_pages():
+    # ~3.36 MB per expert, 30 x 128 experts ~ 12.9 GB (TurboFieldfare video transcript,
+    # paragraph on the two weight piles)
+    nbytes = orc.blob_bytes(2816, 704)
+    assert nbytes == 3_345_408
+    assert abs(nbytes / 3.36e6 - 1) < 0.01
+    assert abs(30 * 128 * nbytes / 12.9e9 - 1) < 0.01
+    sec = orc.blob_sections(2816, 704)
+    assert [sec[n][0] for n in orc.SECTION_NAMES] == [0, 991_232, 1_982_464, 2_973_696, 3_097_600, 3_221_504]
+    # the generator's payload split agrees with the format's sections
+    nib, pairs = synth.blob_payload_sizes(2816, 704)
+    assert nib == sec["gate_sb"][0] and nib + 4 * pairs == nbytes
+
+
+def test_layout_worked_example():
+    g = _load("layout_worked_example.json")
+    R, C = g["R"], g["C"]
+    nib = np.zeros(R * C // 2, dtype=np.uint8)
+    for n in g["nibbles"]:
+        nib[n["byte"]] |= np.uint8(n["q"] << (4 if n["high"] else 0))
+    pairs = np.zeros(R * (C // 64) * 2, dtype=np.float16)
+    pairs[0::2] = g["default_scale"]
+    pairs[1::2] = g["default_bias"]
+    for p in g["pairs"]:
+        pairs[p["byte"] // 2] = p["scale"]
+        pairs[p["byte"] // 2 + 1] = p["bias"]
+    blob = np.concatenate([nib, pairs.view(np.uint8)])
+    w = orc.dequant(blob, 0, nib.size, R, C)
+    special = {(e["r"], e["c"]): e["w"] for e in g["expect"]}
+    for (r, c), v in special.items():
+        assert w[r, c] == v, (r, c, w[r, c], v)
+    # every element not named by a nibble or pair entry is scale*0 + bias of its group
+    named_rows_groups = {(p["r"], p["g"]) for p in g["pairs"]}
+    named_elems = {(n["r"], n["c"]) for n in g["nibbles"]}
+    for r in range(R):
+        for c in range(C):
+            if (r, c) in named_elems or (r, c // 64) in named_rows_groups:
+                continue
+            assert w[r, c] == 0.0
+
+
+def test_known_bytes():
+    # byte 0x21 holds column 0 = 1 (low nibble) and column 1 = 2 (high nibble)
+    R, C = 64, 64
+    nib = np.zeros(R * C // 2, dtype=np.uint8)
+    nib[0] = 0x21
+    pairs = np.zeros(R * 2, dtype=np.float16)
+    pairs[0::2] = 1.0
+    w = orc.dequant(np.concatenate([nib, pairs.view(np.uint8)]), 0, nib.size, R, C)
+    assert w[0, 0] == 1.0 and w[0, 1] == 2.0 and np.count_nonzero(w) == 2
+
+
+def test_quant_roundtrip_exact():
+    rs = np.random.default_rng(1)
+    R, C = 128, 192
+    q = rs.integers(0, 16, (R, C))
+    s = rs.uniform(0.005, 0.02, (R, C // 64)).astype(np.float16).astype(np.float64)
+    b = rs.uniform(-0.1, 0.1, (R, C // 64)).astype(np.float16).astype(np.float64)
+    nib, pairs = orc.encode_matrix(q, s, b)
+    w = orc.dequant(np.concatenate([nib, pairs]), 0, nib.size, R, C)
+    g = np.arange(C) // 64
+    assert np.array_equal(w, s[:, g] * q + b[:, g])
+    assert np.array_equal(orc.quantize_group_affine(w, s, b), q)
+
+
+def test_unit_scale_integer_matvec_exact():
+    # unit scale, zero bias: weights are the nibbles; with x in {-1,0,1} every
+    # partial sum is a small integer, so the float result equals integer arithmetic
+    rs = np.random.default_rng(2)
+    R, C = 128, 256
+    q = rs.integers(0, 16, (R, C))
+    nib, pairs = orc.encode_matrix(q, np.ones((R, C // 64)), np.zeros((R, C // 64)))
+    w = orc.dequant(np.concatenate([nib, pairs]), 0, nib.size, R, C)
+    x = rs.integers(-1, 2, C)
+    assert np.array_equal(w @ x.astype(np.float64), (q @ x).astype(np.float64))
+
+
+# ----------------------------------------------------------------------------- GELU
+
+def test_gelu_closed_forms():
+    assert orc.gelu_tanh(0.0) == 0.0
+    for z in (10.0, 12.5, 40.0):
+        assert orc.gelu_tanh(z) == z
+        assert orc.gelu_tanh(-z) == 0.0
+    assert abs(float(orc.gelu_tanh(1.0)) - 0.8411919906) < 1e-9
+
+
+def test_gelu_close_to_erf_gelu():
+    # the tanh form approximates x * Phi(x) to within about 4.7e-4 everywhere
+    z = np.linspace(-8, 8, 4001)
+    exact = np.array([0.5 * v * (1 + math.erf(v / math.sqrt(2))) for v in z])
+    err = np.abs(orc.gelu_tanh(z) - exact)
+    assert err.max() < 5e-4
+    assert err.max() > 4e-4  # it is the tanh approximation, not erf itself
+
+
+# ----------------------------------------------------------------------------- routing
+
+def test_router_zero_weights_equal_bias():
+    E, d, k = 128, 64, 8
+    h, lg, idx, w = orc.route(np.ones((1, d)), None, np.zeros((E, d)), np.full(E, 0.25), k)
+    assert idx.tolist() == [list(range(8))]
+    assert np.all(w == 1.0 / 8)
+
+
+def test_router_planted_ties_lowest_id():
+    E, d, k = 16, 8, 4
+    bias = np.zeros(E)
+    bias[[3, 9, 12]] = 2.0       # three tied at the top
+    bias[[1, 5, 7]] = 1.0        # ties across the k boundary: 1 wins over 5 and 7
+    _, _, idx, _ = orc.route(np.ones((1, d)), None, np.zeros((E, d)), bias, k)
+    assert idx.tolist() == [[3, 9, 12, 1]]
+
+
+def test_topk_matches_bruteforce_subsets():
+    rs = random.Random(3)
+    for trial in range(300):
+        E, k = rs.randint(3, 10), 0
+        k = rs.randint(1, E)
+        # small integers to force ties often
+        row = [float(rs.randint(-3, 3)) / 4 for _ in range(E)]
+        assert orc.select_topk(row, k) == orc.topk_bruteforce(row, k), (row, k)
+
+
+def test_weights_sum_to_one_and_closed_form():
+    rs = np.random.default_rng(4)
+    lg = rs.normal(0, 2, 128)
+    sel = orc.select_topk(lg, 8)
+    w = orc.routing_weights(lg, sel)
+    assert abs(w.sum() - 1.0) < 8 * np.finfo(np.float64).eps
+    # softmax over 128 then renormalise == softmax over the selected logits
+    z = np.exp(lg[sel] - lg[sel].max())
+    assert np.allclose(w, z / z.sum(), rtol=1e-14, atol=0)
+    assert np.all(np.diff(w) <= 0)
+
+
+# ----------------------------------------------------------------------------- layer
+
+def _tiny_model(seed, d=128, f=64, E=8):
+    """Random tiny experts built with Python's own RNG as dense (q, s, b)."""
+    rs = random.Random(seed)
+    experts = []
+    for _ in range(E):
+        mats = {}
+        for name, (R, C) in (("gate", (f, d)), ("up", (f, d)), ("down", (d, f))):
+            q = [[rs.randint(0, 15) for _ in range(C)] for _ in range(R)]
+            s = [[float(np.float16(rs.uniform(0.005, 0.02))) for _ in range(C // 64)] for _ in range(R)]
+            b = [[float(np.float16(rs.uniform(-0.1, 0.1))) for _ in range(C // 64)] for _ in range(R)]
+            mats[name] = (q, s, b)
+        experts.append(mats)
+    return experts
+
+
+def _loops_ffn(mats, h):
+    """Expert FFN with Python loops over the dense (q, s, b) lists."""
+    def dense_row(m, r, c):
+        q, s, b = m
+        return s[r][c // 64] * q[r][c] + b[r][c // 64]
+    gq = mats["gate"]
+    f, d = len(gq[0]), len(gq[0][0])
+    act = []
+    for r in range(f):
+        g = 0.0
+        u = 0.0
+        for c in range(d):
+            g += dense_row(mats["gate"], r, c) * h[c]
+            u += dense_row(mats["up"], r, c) * h[c]
+        gl = 0.5 * g * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (g + 0.044715 * g * g * g)))
+        act.append(gl * u)
+    out = []
+    for i in range(d):
+        acc = 0.0
+        for r in range(f):
+            acc += dense_row(mats["down"], i, r) * act[r]
+        out.append(acc)
+    return np.array(act), np.array(out)
+
+
+def _blob_of_tiny(mats, d, f):
+    enc = {n: (np.array(m[0]), np.array(m[1]), np.array(m[2])) for n, m in mats.items()}
+    return orc.encode_expert(enc, d, f)
+
+
+def test_expert_ffn_bruteforce_tiny():
+    d, f = 128, 64
+    experts = _tiny_model(5, d, f, E=2)
+    h = np.random.default_rng(5).normal(0, 1, d)
+    for mats in experts:
+        blob = _blob_of_tiny(mats, d, f)
+        act_ref, out_ref = _loops_ffn(mats, h)
+        act = orc.expert_gateup(blob, h, d, f)[0]
+        out = orc.expert_down(blob, act, d, f)[0]
+        assert np.allclose(act, act_ref, rtol=1e-12, atol=1e-12 * np.abs(act_ref).max())
+        assert np.allclose(out, out_ref, rtol=1e-12, atol=1e-12 * np.abs(out_ref).max())
+
+
+def test_moe_layer_bruteforce_tiny():
+    # E=8, k=2, d=128, f=64, T=3 through textbook loops: softmax over 8, top-2 by
+    # sort, renormalise, sum of the two experts' outputs plus the residual.
+    d, f, E, k, T = 128, 64, 8, 2, 3
+    experts = _tiny_model(6, d, f, E)
+    blobs = [_blob_of_tiny(m, d, f) for m in experts]
+    rs = np.random.default_rng(6)
+    x = rs.normal(0, 1, (T, d))
+    nw = rs.normal(1, 0.1, d)
+    rw = rs.normal(0, 0.1, (E, d))
+    bias = rs.normal(0, 0.5, E)
+    y, idx, w, h, lg = orc.moe_layer(x, nw, rw, bias, lambda e: blobs[e], d, f, k)
+    for t in range(T):
+        ms = sum(v * v for v in x[t]) / d
+        hh = [x[t][i] / math.sqrt(ms + 1e-6) * nw[i] for i in range(d)]
+        logits = [sum(rw[e][i] * hh[i] for i in range(d)) + bias[e] for e in range(E)]
+        mx = max(logits)
+        p = [math.exp(v - mx) for v in logits]
+        p = [v / sum(p) for v in p]
+        order = sorted(range(E), key=lambda e: (-logits[e], e))[:k]
+        assert idx[t].tolist() == order
+        ws = [p[e] / sum(p[o] for o in order) for e in order]
+        acc = list(x[t])
+        for j, e in enumerate(order):
+            _, out = _loops_ffn(experts[e], hh)
+            acc = [a + ws[j] * o for a, o in zip(acc, out)]
+        assert np.allclose(y[t], acc, rtol=1e-10, atol=1e-10 * np.abs(acc).max())
+
+
+def test_one_hot_routing_is_single_expert():
+    d, f, E, k = 128, 64, 8, 8
+    experts = _tiny_model(7, d, f, E)
+    blobs = [_blob_of_tiny(m, d, f) for m in experts]
+    x = np.random.default_rng(7).normal(0, 1, (1, d))
+    for star in (0, 5):
+        bias = np.zeros(E)
+        bias[star] = 1000.0
+        y, idx, w, h, _ = orc.moe_layer(x, None, np.zeros((E, d)), bias, lambda e: blobs[e], d, f, k)
+        assert idx[0, 0] == star and w[0, 0] == 1.0 and np.all(w[0, 1:] == 0.0)
+        single = orc.expert_down(blobs[star], orc.expert_gateup(blobs[star], x, d, f), d, f)
+        assert np.array_equal(y, x + single)
+
+
+def test_slot_permutation_invariance():
+    d, f, E, k = 128, 64, 8, 3
+    experts = _tiny_model(8, d, f, E)
+    blobs = [_blob_of_tiny(m, d, f) for m in experts]
+    stride = blobs[0].size
+    rs = np.random.default_rng(8)
+    x = rs.normal(0, 1, (4, d))
+    rw = rs.normal(0, 0.1, (E, d))
+    outs = []
+    for perm in (np.arange(E), rs.permutation(E), rs.permutation(E)):
+        arena = np.zeros(E * stride, dtype=np.uint8)
+        for e in range(E):
+            arena[perm[e] * stride:(perm[e] + 1) * stride] = blobs[e]
+        blob_of = lambda e, perm=perm, arena=arena: arena[perm[e] * stride:(perm[e] + 1) * stride]
+        outs.append(orc.moe_layer(x, None, rw, None, blob_of, d, f, k)[0])
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_rms_rescale_unit_rms():
+    x = np.random.default_rng(9).normal(3, 7, (5, 2816))
+    y = orc.rms_rescale(x)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0, rtol=1e-9)
+
+
+# ----------------------------------------------------------------------------- permute
+
+@pytest.mark.parametrize("T,k,E", [(1, 8, 128), (3, 2, 8), (32, 8, 128), (257, 8, 128), (2048, 8, 128)])
+def test_permute_invariants_and_bruteforce(T, k, E):
+    rs = np.random.default_rng(T)
+    idx = np.stack([rs.choice(E, k, replace=False) for _ in range(T)])
+    counts, offsets, sorted_pair, pair_pos = orc.permute(idx, E)
+    assert counts.sum() == T * k and offsets[0] == 0 and offsets[-1] == T * k
+    assert np.array_equal(np.diff(offsets), counts)
+    assert sorted(sorted_pair.tolist()) == list(range(T * k))
+    assert np.array_equal(sorted_pair[pair_pos], np.arange(T * k))
+    flat = idx.ravel()
+    buckets = [[p for p in range(T * k) if flat[p] == e] for e in range(E)]
+    assert sorted_pair.tolist() == [p for b in buckets for p in b]
+
+
+# ----------------------------------------------------------------------------- LRU
+
+def test_lru_hand_worked_trace():
+    g = _load("lru_trace_4slots.json")
+    c = orc.LruSlotCache(g["n_slots"], g["n_experts"])
+    for t, st in enumerate(g["steps"]):
+        hit, installs = c.step(t, st["sel"])
+        assert hit == st["hit"], t
+        assert [list(i) for i in installs] == st["installs"], t
+        assert c.slot_expert == st["slots"], t
+        assert c.stamp == st["stamps"], t
+
+
+def test_lru_invariants_and_resume():
+    E, S, k, steps = 128, 64, 8, 512
+    sel = synth.markov_selections(E, k, steps, seed=0, layer=3)
+    a = orc.LruSlotCache(S, E)
+    hits = 0
+    for t in range(steps):
+        before = set(e for e in a.slot_expert if e >= 0)
+        hit, installs = a.step(t, sel[t].tolist())
+        after = set(e for e in a.slot_expert if e >= 0)
+        assert set(sel[t].tolist()) <= after
+        assert sum(not h for h in hit) == len(set(sel[t].tolist()) - before) == len(installs)
+        hits += sum(hit)
+        if t == 255:
+            state = a.export_state()
+    # resume from the exported state reproduces the straight run
+    b = orc.LruSlotCache(S, E)
+    b.import_state(state)
+    for t in range(256, steps):
+        b.step(t, sel[t].tolist())
+    assert b.export_state() == a.export_state()
+    # with as many slots as experts every expert hits after its first use
+    full = orc.LruSlotCache(E, E)
+    seen = set()
+    for t in range(steps):
+        hit, _ = full.step(t, sel[t].tolist())
+        assert hit == [e in seen for e in sel[t].tolist()]
+        seen |= set(sel[t].tolist())
