@@ -1,0 +1,288 @@
+/*
+ * libmoe — routed int4 mixture-of-experts layer for AMD Instinct MI355X (gfx950).
+ *
+ * One MoE layer as the pages describe it: a small router picks 8 of 128
+ * feed-forward experts per token and only those run (TurboFieldfare video
+ * transcript, paragraph on Gemma 4 as a mixture-of-experts model); the experts'
+ * projections are INT4 in affine groups of 64 with a scale and a bias per group
+ * ("Optimizing a 14.3 GB model for an 8 GB machine", section "Vectorization
+ * helped when it respected the storage layout"); expert weights are read through
+ * preallocated per-layer cache slots kept by a bounded cache (same page, sections
+ * "Explicit reads made expert streaming work" and "MoE needed parallel work,
+ * reuse, and coarse overlap").
+ *
+ * Conventions shared by every call
+ *  - Every pointer named *_dev or documented as "device" is device memory the
+ *    caller allocated (hipMalloc or a torch tensor); *_host is host memory.
+ *    The library keeps no pointer after a call returns, except those registered
+ *    with moe_cache_create.  It allocates no device memory on any compute call.
+ *  - Every compute call is asynchronous and ordered on the stream it is given
+ *    (0 = the null stream).  Argument checks run on the host before anything is
+ *    enqueued; a failed check enqueues nothing and returns an error code.
+ *    Faults inside kernels surface at the next synchronisation as HIP errors.
+ *  - Float and int32 buffers must be 16-byte aligned (MOE_ERR_ALIGN otherwise):
+ *    kernels use 128-bit loads and the pages show what a wider load does to a
+ *    sub-tensor that is only 2-byte aligned (same page, section
+ *    "Vectorization helped when it respected the storage layout").
+ *  - Workspaces ("ws") are caller-owned device buffers of moe_workspace_size()
+ *    bytes.  A workspace must be zero-filled before its first use; every call
+ *    leaves the counters it uses at zero again, so it can be reused by later
+ *    calls on the same stream without clearing.  Two calls in flight at the same
+ *    time must not share a workspace.
+ *  - moe_last_error() returns a thread-local text for the last failing call.
+ *
+ * Dimensions (moe_dims): d = hidden size, f = expert width, n_experts = E,
+ * top_k = k.  Requirements: d % 64 == 0, f % 64 == 0, 1 <= k <= 16,
+ * k <= E <= 256.  The layer the pages describe has d = 2816, f = 704, E = 128,
+ * k = 8.  Token t's j-th routed expert forms the pair p = t * k + j.
+ *
+ * Expert blob format (one expert; byte offsets from moe_expert_blob_offsets):
+ *   six sections, each starting on a 256-byte boundary, in this order:
+ *   gate nibbles [f x d], up nibbles [f x d], down nibbles [d x f],
+ *   gate (scale, bias) [f x d/64], up (scale, bias) [f x d/64],
+ *   down (scale, bias) [d x f/64].
+ *   A matrix of R rows (outputs) and C columns (inputs) stores element (r, c):
+ *     nibble byte = (r/64)*(64*C/2) + (c/32)*1024 + (r%64)*16 + (c%32)/2,
+ *                   low 4 bits for even c, high 4 bits for odd c;
+ *     pair byte   = (r/64)*(64*(C/64)*4) + (c/64)*256 + (r%64)*4,
+ *                   fp16 scale at +0 and fp16 bias at +2 (little-endian);
+ *   and w[r][c] = scale * q + bias with q in 0..15.  Rows are tiled by 64 and,
+ *   inside a tile, the 16-byte column chunks of the 64 rows sit side by side, so
+ *   that one 64-lane wavefront reads 1 KiB contiguous per load with one row per
+ *   lane.  Staging an expert copies its blob verbatim: the stored layout is the
+ *   layout the kernels read (TurboFieldfare video transcript, paragraph on the
+ *   installer storing weights in the kernel's layout).
+ *
+ * Expert FFN: act = gelu_tanh(W_gate h) * (W_up h);  out = W_down act, with
+ * gelu_tanh(z) = 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+ * Routing: logits = W_router h (+ bias); the k largest logits are chosen (equal
+ * logits: the lower expert id wins), in descending order; their weights are the
+ * softmax over all E renormalised over the k chosen.
+ * Combine: y[t] = residual[t] + sum_j w[t][j] * out[t*k+j], j in rank order.
+ */
+#ifndef LIBMOE_H
+#define LIBMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,         /* null pointer, bad size or dimension */
+  MOE_ERR_ALIGN = 2,       /* a buffer violates the alignment contract */
+  MOE_ERR_UNSUPPORTED = 3, /* a valid combination this build does not implement */
+  MOE_ERR_HIP = 4,         /* a HIP runtime call failed */
+  MOE_ERR_STATE = 5,       /* a cache call in the wrong state */
+  MOE_ERR_CAPACITY = 6     /* workspace too small */
+} moe_status;
+
+typedef struct moe_dims {
+  int32_t d;         /* hidden size (router input, expert input and output) */
+  int32_t f;         /* expert FFN width */
+  int32_t n_experts; /* experts per layer, E */
+  int32_t top_k;     /* experts chosen per token, k */
+} moe_dims;
+
+typedef enum moe_precision {
+  MOE_PREC_FP32 = 0,      /* int4 -> fp32 dequant, fp32 FMA accumulate (decode) */
+  MOE_PREC_BF16_MFMA = 1  /* int4 -> bf16 tiles in LDS, bf16 MFMA, fp32 accumulate (prefill) */
+} moe_precision;
+
+typedef enum moe_call {
+  MOE_CALL_ROUTE = 0,
+  MOE_CALL_PERMUTE = 1,
+  MOE_CALL_GATEUP = 2,
+  MOE_CALL_DOWN_COMBINE = 3
+} moe_call;
+
+/* Text of a status code, and the thread-local detail of the last failure. */
+const char* moe_status_string(moe_status s);
+const char* moe_last_error(void);
+
+/* Bytes of one expert blob (format above), or -1 for invalid dims. */
+int64_t moe_expert_blob_bytes(moe_dims dims);
+
+/* Byte offsets of the six blob sections: gate_q, up_q, down_q, gate_sb, up_sb,
+ * down_sb, written to offsets[0..5]. */
+moe_status moe_expert_blob_offsets(moe_dims dims, int64_t offsets[6]);
+
+/* Workspace bytes a call needs for T tokens (0 when it needs none; SIZE_MAX
+ * for invalid dims). */
+size_t moe_workspace_size(moe_call call, int32_t T, moe_dims dims, moe_precision prec);
+
+/* ---------------------------------------------------------------------------
+ * moe_route — RMSNorm, router matvec, softmax, top-k, renormalisation.
+ * The router picks 8 of 128 experts from the layer's input (TurboFieldfare
+ * video transcript, paragraphs on the router naming the experts it wants).
+ *   x        device fp32 [T][d]      layer input (residual stream)
+ *   norm_w   device fp32 [d] or NULL RMSNorm weight; NULL: h = x (no norm)
+ *   eps      RMSNorm epsilon: h = x / sqrt(mean(x^2) + eps) * norm_w
+ *   router_w device fp32 [E][d]      router matrix, row-major
+ *   router_bias device fp32 [E] or NULL   added to the logits
+ *   h_out    device fp32 [T][d]      the normalised input the experts read
+ *   topk_idx device int32 [T][k]     chosen experts, descending logit order
+ *   topk_w   device fp32 [T][k]      their renormalised softmax weights
+ *   ws       workspace of moe_workspace_size(MOE_CALL_ROUTE, T, ...) bytes
+ * Errors: MOE_ERR_ARG (null/bad dims/T < 1), MOE_ERR_ALIGN, MOE_ERR_CAPACITY.
+ * NaN logits are outside the contract.
+ * ------------------------------------------------------------------------- */
+moe_status moe_route(const float* x, const float* norm_w, float eps,
+                     const float* router_w, const float* router_bias,
+                     int32_t T, moe_dims dims,
+                     float* h_out, int32_t* topk_idx, float* topk_w,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_permute — group the T*k (token, rank) pairs by expert so that all tokens
+ * routed to one expert run against one read of its weights (the batched routed
+ * MoE of "Optimizing a 14.3 GB model for an 8 GB machine", section "Splitting
+ * the work improved attention and prefill").
+ *   topk_idx    device int32 [T][k]   from moe_route (values in 0..E-1)
+ *   counts      device int32 [E]      pairs per expert
+ *   offsets     device int32 [E+1]    exclusive prefix sum of counts; offsets[E] = T*k
+ *   sorted_pair device int32 [T*k]    pair ids grouped by expert, ascending inside a group
+ *   pair_pos    device int32 [T*k]    inverse: sorted_pair[pair_pos[p]] = p
+ * Deterministic; no atomics whose order reaches the output.  T*k <= 65536.
+ * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN.
+ * ------------------------------------------------------------------------- */
+moe_status moe_permute(const int32_t* topk_idx, int32_t T, moe_dims dims,
+                       int32_t* counts, int32_t* offsets,
+                       int32_t* sorted_pair, int32_t* pair_pos,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_expert_q4_gateup — act[p] = gelu_tanh(W_gate[e] h[t]) * (W_up[e] h[t])
+ * for every pair p = t*k + j with e = topk_idx[p]; the expert's blob is found
+ * through the layer's slot table: arena + slot_of_expert[e] * slot_stride
+ * (preallocated per-layer cache slots, "Optimizing a 14.3 GB model for an 8 GB
+ * machine", section "Explicit reads made expert streaming work").
+ *   h              device fp32 [T][d]     from moe_route
+ *   topk_idx       device int32 [T][k]
+ *   slot_of_expert device int32 [E]       this layer's slot per expert (-1 = absent)
+ *   n_slots        slots in the arena; a pair whose slot is outside 0..n_slots-1
+ *                  gets NaN outputs instead of a read
+ *   arena          device, n_slots * slot_stride bytes, 256-byte aligned
+ *   slot_stride    bytes between slots, a multiple of 256, >= blob bytes
+ *   offsets, sorted_pair  device, from moe_permute, or both NULL.  Given: each
+ *                  expert's weights are read once for all its pairs.  NULL:
+ *                  every pair reads its expert on its own (batch-1 decode).
+ *   pair_mask      device uint8 [T*k] or NULL: only pairs with
+ *                  pair_mask[p] == mask_value are computed, the others are left
+ *                  untouched (cache hits first, then the misses, "Optimizing a
+ *                  14.3 GB model for an 8 GB machine", section "MoE needed
+ *                  parallel work, reuse, and coarse overlap").  Only with
+ *                  offsets == NULL.
+ *   prec           MOE_PREC_FP32: act is fp32 [T*k][f];
+ *                  MOE_PREC_BF16_MFMA: act is bf16 [T*k][f] (needs offsets).
+ * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_CAPACITY, MOE_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------- */
+moe_status moe_expert_q4_gateup(const float* h, const int32_t* topk_idx,
+                                const int32_t* slot_of_expert, int32_t n_slots,
+                                const uint8_t* arena, int64_t slot_stride,
+                                const int32_t* offsets, const int32_t* sorted_pair,
+                                const uint8_t* pair_mask, int32_t mask_value,
+                                int32_t T, moe_dims dims, moe_precision prec,
+                                void* act, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_expert_q4_down_combine — out[p] = W_down[e] act[p], then
+ * y[t] = residual[t] + sum_j topk_w[t][j] * out[t*k+j], summed in rank order
+ * (deterministic).  Same slot-table, offsets and precision rules as gateup.
+ *   act       device fp32 or bf16 [T*k][f]  from moe_expert_q4_gateup
+ *   topk_w    device fp32 [T][k]
+ *   pair_pos  device int32 [T*k] from moe_permute, or NULL with offsets NULL
+ *   residual  device fp32 [T][d] or NULL (then y is the expert mix alone);
+ *             may equal y (in place)
+ *   y         device fp32 [T][d]
+ * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_CAPACITY, MOE_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------- */
+moe_status moe_expert_q4_down_combine(const void* act, const int32_t* topk_idx, const float* topk_w,
+                                      const int32_t* slot_of_expert, int32_t n_slots,
+                                      const uint8_t* arena, int64_t slot_stride,
+                                      const int32_t* offsets, const int32_t* sorted_pair,
+                                      const int32_t* pair_pos, const float* residual,
+                                      int32_t T, moe_dims dims, moe_precision prec,
+                                      float* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Bounded per-layer expert cache with side-stream staging.
+ * A cache keeps, for each of n_layers layers, n_slots device slots of an arena
+ * and the expert each holds; misses are copied from a pinned host pool into the
+ * least-recently-used slot on a side stream while the compute stream runs other
+ * work (bounded per-layer cache: "Optimizing a 14.3 GB model for an 8 GB
+ * machine", section "MoE needed parallel work, reuse, and coarse overlap";
+ * LRU over resident slots: goinfer "When the model doesn't fit").
+ * LRU rule per layer, step t, selection S: first every hit is stamped t; then
+ * each miss, in ascending expert id, takes the slot with the smallest
+ * (stamp, slot index); empty slots have stamp -1 and so fill lowest first.
+ * ------------------------------------------------------------------------- */
+typedef struct moe_cache moe_cache;
+
+typedef struct moe_stage_stats {
+  int64_t hits;         /* cumulative over the cache's life */
+  int64_t misses;
+  int64_t bytes_staged;
+} moe_stage_stats;
+
+/* host_pool: pinned host memory, n_layers * n_experts * blob_bytes, expert
+ *   (l, e) at ((l * n_experts) + e) * blob_bytes (registered, not copied).
+ * arena: device, n_layers * n_slots * slot_stride bytes; slot s of layer l at
+ *   ((l * n_slots) + s) * slot_stride.
+ * slot_tables: device int32 [n_layers][n_experts]; the cache writes it (-1 =
+ *   not resident) and kernels read it as slot_of_expert = slot_tables + l * E.
+ *   The cache fills it with -1 on creation (synchronously).
+ * Requires top_k <= n_slots <= n_experts. */
+moe_status moe_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_slots, int32_t top_k,
+                            const uint8_t* host_pool, int64_t blob_bytes,
+                            uint8_t* arena, int64_t slot_stride,
+                            int32_t* slot_tables, moe_cache** out);
+moe_status moe_cache_destroy(moe_cache* c);
+
+/* One step of one layer.  sel_host: the k chosen experts (host int32, rank
+ * order).  Runs the LRU rule on the host, then enqueues on `side`: a wait for
+ * all work already enqueued on `compute` (so no kernel still reads a victim
+ * slot), one hipMemcpyAsync per miss (pinned pool -> its slot), and the copy of
+ * the layer's new slot table.  hit_mask_dev (device uint8 [k]) receives 1 for
+ * hits and 0 for misses through a copy enqueued on `compute`; hit_mask_host
+ * (may be NULL) gets the same on return.  Entries of hit experts keep their
+ * slot, so kernels for hits may run on `compute` before moe_cache_wait. */
+moe_status moe_slot_stage(moe_cache* c, int32_t layer, int32_t step, const int32_t* sel_host,
+                          hipStream_t side, hipStream_t compute,
+                          uint8_t* hit_mask_dev, uint8_t* hit_mask_host,
+                          moe_stage_stats* stats);
+/* Make `compute` wait until the layer's last staging has landed. */
+moe_status moe_cache_wait(moe_cache* c, int32_t layer, hipStream_t compute);
+/* Host copy of a layer's slot table (expert -> slot, -1 absent), int32 [E]. */
+moe_status moe_cache_slot_table(const moe_cache* c, int32_t layer, int32_t* out_host);
+/* Checkpoint: per layer the expert of each slot [L][S] and its stamp [L][S]. */
+moe_status moe_cache_export(const moe_cache* c, int32_t* slot_expert_host, int64_t* stamp_host);
+/* Restore exported state; rewrites the device slot tables synchronously.  The
+ * arena contents are the caller's business (restage or keep). */
+moe_status moe_cache_import(moe_cache* c, const int32_t* slot_expert_host, const int64_t* stamp_host);
+
+/* ---------------------------------------------------------------------------
+ * Shared-path GEMV with bf16 weights: out[t][r] = sum_c W[r][c] * h[t][c].
+ * The always-resident work the GPU runs while expert misses are being copied
+ * (coarse overlap: "Optimizing a 14.3 GB model for an 8 GB machine", section
+ * "MoE needed parallel work, reuse, and coarse overlap").
+ *   w   device bf16 bits [rows][cols] row-major, 16-byte aligned; cols % 8 == 0
+ *   h   device fp32 [T][cols];  out device fp32 [T][rows]
+ * ------------------------------------------------------------------------- */
+moe_status moe_shared_gemv_bf16(const uint16_t* w, const float* h, int32_t T,
+                                int32_t rows, int32_t cols, float* out, hipStream_t stream);
+
+/* Unit-RMS rescale out[t] = x[t] / sqrt(mean(x[t]^2) + eps), used to feed one
+ * decode step's output back as the next step's input.  out may equal x. */
+moe_status moe_rms_rescale(const float* x, int32_t T, int32_t d, float eps,
+                           float* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMOE_H */

@@ -1,0 +1,88 @@
+// Internal helpers shared by the libmoe HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/libmoe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kGroup = 64;      // int4 affine group along the input dimension
+constexpr int kTileRows = 64;   // rows per blob tile: one row per lane
+constexpr int kChunkCols = 32;  // 16 bytes of nibbles
+
+// Byte offsets of the six blob sections (see the blob format in libmoe.h).
+struct BlobLayout {
+  int64_t gate_q, up_q, down_q, gate_sb, up_sb, down_sb, total;
+};
+
+inline __host__ __device__ int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
+
+inline __host__ BlobLayout blob_layout(int d, int f) {
+  BlobLayout b;
+  int64_t o = 0;
+  b.gate_q = o;  o = round256(o + (int64_t)f * d / 2);
+  b.up_q = o;    o = round256(o + (int64_t)f * d / 2);
+  b.down_q = o;  o = round256(o + (int64_t)d * f / 2);
+  b.gate_sb = o; o = round256(o + (int64_t)f * (d / kGroup) * 4);
+  b.up_sb = o;   o = round256(o + (int64_t)f * (d / kGroup) * 4);
+  b.down_sb = o; o = round256(o + (int64_t)d * (f / kGroup) * 4);
+  b.total = o;
+  return b;
+}
+
+// ---------------------------------------------------------------- numerics
+
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// tanh-form GELU in fp32.
+__device__ __forceinline__ float gelu_tanh(float z) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  const float k1 = 0.044715f;
+  return 0.5f * z * (1.0f + tanhf(k0 * (z + k1 * z * z * z)));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Sum over aligned groups of 16 lanes (lanes 16g..16g+15 end with the same value).
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_bcast(int v, int lane) { return __shfl(v, lane, kWave); }
+
+__device__ __forceinline__ float f32_nan() { return __builtin_nanf(""); }
+
+// Device-scope (all XCDs) release/acquire helpers for last-arriver reductions.
+__device__ __forceinline__ void release_fence() { __atomic_thread_fence(__ATOMIC_RELEASE); }
+__device__ __forceinline__ void acquire_fence() { __atomic_thread_fence(__ATOMIC_ACQUIRE); }
+
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Arrival counter: returns the number of earlier arrivals (0-based ticket).
+__device__ __forceinline__ uint32_t arrive(uint32_t* counter) {
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void reset_counter(uint32_t* counter) {
+  __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace moe

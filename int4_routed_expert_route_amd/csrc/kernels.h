@@ -1,0 +1,86 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- routing (route.hip)
+size_t route_workspace_bytes(int T, int E);
+hipError_t launch_route(const float* x, const float* norm_w, float eps, const float* router_w,
+                        const float* router_bias, int T, int d, int E, int k, float* h_out,
+                        int32_t* topk_idx, float* topk_w, void* ws, hipStream_t s);
+hipError_t launch_rms_rescale(const float* x, int T, int d, float eps, float* out, hipStream_t s);
+
+// ---- pair permutation (permute.hip)
+hipError_t launch_permute(const int32_t* topk_idx, int n_pairs, int E, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, hipStream_t s);
+
+// ---- fp32 dequant-GEMV (q4_gemv.hip)
+struct GemvPlan {
+  int nch;       // 16-byte chunks per K-slice
+  int nks;       // K-slices per row
+  int n_rt;      // 64-row tiles
+  int n_groups;  // pairs (ungrouped) or experts (grouped)
+  int ntasks;
+  size_t partial_floats;
+  size_t counters;
+};
+
+struct GateupArgs {
+  const float* h;
+  const int32_t* topk_idx;
+  const int32_t* slot_of_expert;
+  int n_slots;
+  const uint8_t* arena;
+  int64_t slot_stride;
+  const int32_t* offsets;
+  const int32_t* sorted_pair;
+  const uint8_t* pair_mask;
+  int mask_value;
+  int T, d, f, E, k;
+  int64_t off_q0, off_q1, off_sb0, off_sb1;  // gate and up sections
+  float* act;
+  // set by the launcher
+  float* partial;
+  uint32_t* counters;
+  uint32_t* claim;
+  int nks, n_rt, ntasks;
+  int persistent;
+};
+
+struct DownArgs {
+  const float* act;
+  const int32_t* topk_idx;
+  const float* topk_w;
+  const int32_t* slot_of_expert;
+  int n_slots;
+  const uint8_t* arena;
+  int64_t slot_stride;
+  const int32_t* offsets;
+  const int32_t* sorted_pair;
+  const float* residual;
+  float* y;
+  int T, d, f, E, k;
+  int64_t off_q, off_sb;  // down sections
+  // set by the launcher
+  float* partial;
+  uint32_t* counters;
+  uint32_t* claim;
+  int nks, n_rt, n_groups, ntasks;
+  int persistent;
+};
+
+GemvPlan plan_gateup(int T, int d, int f, int E, int k, bool grouped);
+GemvPlan plan_down(int T, int d, int f, int E, int k, bool grouped);
+size_t gemv_workspace_bytes(const GemvPlan& p);
+hipError_t launch_gateup_fp32(GateupArgs a, const GemvPlan& p, void* ws, int max_resident, hipStream_t s);
+hipError_t launch_down_fp32(DownArgs a, const GemvPlan& p, void* ws, int max_resident, hipStream_t s);
+
+// ---- bf16 shared-path GEMV (shared_gemv.hip)
+hipError_t launch_shared_gemv_bf16(const uint16_t* w, const float* h, int T, int rows, int cols,
+                                   float* out, hipStream_t s);
+
+}  // namespace moe

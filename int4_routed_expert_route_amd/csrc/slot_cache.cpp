@@ -1,0 +1,253 @@
+// Bounded per-layer expert cache: host LRU bookkeeping, pinned-host -> HBM
+// staging of misses on a side stream, device slot tables.
+//
+// The pages keep a bounded number of routed experts per layer in preallocated
+// slots, read misses explicitly into them, and run cached hits first while the
+// misses are still arriving ("Optimizing a 14.3 GB model for an 8 GB machine",
+// sections "Explicit reads made expert streaming work" and "MoE needed parallel
+// work, reuse, and coarse overlap"); goinfer ("When the model doesn't fit")
+// keeps an LRU over resident slots.  On MI355X the pool sits in pinned host
+// memory and a miss is one DMA copy of the expert blob, verbatim, over PCIe.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/libmoe.h"
+
+struct moe_cache {
+  int L = 0, E = 0, S = 0, k = 0;
+  const uint8_t* pool = nullptr;
+  int64_t blob = 0;
+  uint8_t* arena = nullptr;
+  int64_t stride = 0;
+  int32_t* tables_dev = nullptr;
+  std::vector<int32_t> slot_expert;  // [L][S], -1 empty
+  std::vector<int64_t> stamp;        // [L][S], -1 never used
+  int32_t* table_host = nullptr;     // pinned [L][E]: source of the slot-table copies
+  uint8_t* mask_host = nullptr;      // pinned [L][k]: source of the hit-mask copies
+  std::vector<hipEvent_t> staged;    // per layer: last staging on the side stream
+  std::vector<hipEvent_t> masked;    // per layer: last hit-mask copy on the compute stream
+  std::vector<char> staged_used, masked_used;
+  hipEvent_t compute_mark = nullptr;
+  moe_stage_stats stats{0, 0, 0};
+};
+
+// Failures are reported through the library's thread-local error text (api.cpp).
+namespace moe_bridge {
+void set_error(const std::string& s);
+}
+
+namespace {
+
+moe_status cfail(moe_status s, const std::string& msg) {
+  moe_bridge::set_error(msg);
+  return s;
+}
+
+moe_status hipcheck(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return cfail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+void rebuild_table(moe_cache* c, int layer) {
+  int32_t* t = c->table_host + (int64_t)layer * c->E;
+  for (int e = 0; e < c->E; ++e) t[e] = -1;
+  for (int s = 0; s < c->S; ++s) {
+    const int e = c->slot_expert[(int64_t)layer * c->S + s];
+    if (e >= 0) t[e] = s;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_slots, int32_t top_k,
+                            const uint8_t* host_pool, int64_t blob_bytes, uint8_t* arena,
+                            int64_t slot_stride, int32_t* slot_tables, moe_cache** out) {
+  if (!out || !host_pool || !arena || !slot_tables)
+    return cfail(MOE_ERR_ARG, "moe_cache_create: null pointer");
+  *out = nullptr;
+  if (n_layers < 1 || n_experts < 1 || n_experts > 256 || top_k < 1 || n_slots < top_k ||
+      n_slots > n_experts || blob_bytes < 1 || slot_stride < blob_bytes || slot_stride % 256)
+    return cfail(MOE_ERR_ARG, "moe_cache_create: bad sizes (need k <= slots <= experts <= 256, "
+                              "slot_stride % 256 == 0 and >= blob_bytes)");
+  if (reinterpret_cast<uintptr_t>(arena) % 256 || reinterpret_cast<uintptr_t>(slot_tables) % 16)
+    return cfail(MOE_ERR_ALIGN, "moe_cache_create: arena must be 256-byte and tables 16-byte aligned");
+  moe_cache* c = new moe_cache();
+  c->L = n_layers; c->E = n_experts; c->S = n_slots; c->k = top_k;
+  c->pool = host_pool; c->blob = blob_bytes; c->arena = arena; c->stride = slot_stride;
+  c->tables_dev = slot_tables;
+  c->slot_expert.assign((size_t)n_layers * n_slots, -1);
+  c->stamp.assign((size_t)n_layers * n_slots, -1);
+  c->staged.assign(n_layers, nullptr);
+  c->masked.assign(n_layers, nullptr);
+  c->staged_used.assign(n_layers, 0);
+  c->masked_used.assign(n_layers, 0);
+  moe_status st = MOE_OK;
+  if ((st = hipcheck(hipHostMalloc((void**)&c->table_host, sizeof(int32_t) * n_layers * n_experts,
+                                   hipHostMallocDefault), "hipHostMalloc")) ||
+      (st = hipcheck(hipHostMalloc((void**)&c->mask_host, (size_t)n_layers * top_k, hipHostMallocDefault),
+                     "hipHostMalloc")) ||
+      (st = hipcheck(hipEventCreateWithFlags(&c->compute_mark, hipEventDisableTiming), "hipEventCreate"))) {
+    moe_cache_destroy(c);
+    return st;
+  }
+  for (int l = 0; l < n_layers; ++l) {
+    if ((st = hipcheck(hipEventCreateWithFlags(&c->staged[l], hipEventDisableTiming), "hipEventCreate")) ||
+        (st = hipcheck(hipEventCreateWithFlags(&c->masked[l], hipEventDisableTiming), "hipEventCreate"))) {
+      moe_cache_destroy(c);
+      return st;
+    }
+    rebuild_table(c, l);
+  }
+  if ((st = hipcheck(hipMemcpy(slot_tables, c->table_host, sizeof(int32_t) * n_layers * n_experts,
+                               hipMemcpyHostToDevice), "hipMemcpy"))) {
+    moe_cache_destroy(c);
+    return st;
+  }
+  *out = c;
+  return MOE_OK;
+}
+
+moe_status moe_cache_destroy(moe_cache* c) {
+  if (!c) return MOE_OK;
+  for (size_t l = 0; l < c->staged.size(); ++l) {
+    if (c->staged[l]) { hipEventSynchronize(c->staged[l]); hipEventDestroy(c->staged[l]); }
+    if (c->masked[l]) { hipEventSynchronize(c->masked[l]); hipEventDestroy(c->masked[l]); }
+  }
+  if (c->compute_mark) hipEventDestroy(c->compute_mark);
+  if (c->table_host) hipHostFree(c->table_host);
+  if (c->mask_host) hipHostFree(c->mask_host);
+  delete c;
+  return MOE_OK;
+}
+
+moe_status moe_slot_stage(moe_cache* c, int32_t layer, int32_t step, const int32_t* sel_host,
+                          hipStream_t side, hipStream_t compute, uint8_t* hit_mask_dev,
+                          uint8_t* hit_mask_host, moe_stage_stats* stats) {
+  if (!c || !sel_host || !hit_mask_dev) return cfail(MOE_ERR_ARG, "moe_slot_stage: null pointer");
+  if (layer < 0 || layer >= c->L) return cfail(MOE_ERR_ARG, "moe_slot_stage: layer out of range");
+  for (int j = 0; j < c->k; ++j) {
+    if (sel_host[j] < 0 || sel_host[j] >= c->E)
+      return cfail(MOE_ERR_ARG, "moe_slot_stage: expert id out of range");
+    for (int i = 0; i < j; ++i)
+      if (sel_host[i] == sel_host[j]) return cfail(MOE_ERR_ARG, "moe_slot_stage: repeated expert");
+  }
+  // The pinned sources of this layer's previous copies must have been consumed.
+  moe_status st;
+  if (c->staged_used[layer] && (st = hipcheck(hipEventSynchronize(c->staged[layer]), "hipEventSynchronize")))
+    return st;
+  if (c->masked_used[layer] && (st = hipcheck(hipEventSynchronize(c->masked[layer]), "hipEventSynchronize")))
+    return st;
+
+  int32_t* se = c->slot_expert.data() + (int64_t)layer * c->S;
+  int64_t* sp = c->stamp.data() + (int64_t)layer * c->S;
+  // expert -> slot for this layer
+  std::vector<int> where(c->E, -1);
+  for (int s = 0; s < c->S; ++s)
+    if (se[s] >= 0) where[se[s]] = s;
+  // phase 1: stamp the hits
+  uint8_t* mask = c->mask_host + (int64_t)layer * c->k;
+  std::vector<int> misses;
+  for (int j = 0; j < c->k; ++j) {
+    const int e = sel_host[j];
+    mask[j] = where[e] >= 0 ? 1 : 0;
+    if (where[e] >= 0) sp[where[e]] = step;
+    else misses.push_back(e);
+  }
+  // phase 2: misses in ascending expert id take the (stamp, slot)-smallest slot
+  std::vector<int> sorted = misses;
+  for (size_t i = 1; i < sorted.size(); ++i)
+    for (size_t j = i; j > 0 && sorted[j - 1] > sorted[j]; --j) std::swap(sorted[j - 1], sorted[j]);
+  std::vector<std::pair<int, int>> installs;  // (expert, slot)
+  for (int e : sorted) {
+    int victim = 0;
+    for (int s = 1; s < c->S; ++s)
+      if (sp[s] < sp[victim]) victim = s;
+    se[victim] = e;
+    sp[victim] = step;
+    installs.emplace_back(e, victim);
+  }
+  // enqueue: side waits for everything already on compute, then copies
+  if ((st = hipcheck(hipEventRecord(c->compute_mark, compute), "hipEventRecord")) ||
+      (st = hipcheck(hipStreamWaitEvent(side, c->compute_mark, 0), "hipStreamWaitEvent")))
+    return st;
+  for (const auto& in : installs) {
+    const uint8_t* src = c->pool + ((int64_t)layer * c->E + in.first) * c->blob;
+    uint8_t* dst = c->arena + ((int64_t)layer * c->S + in.second) * c->stride;
+    if ((st = hipcheck(hipMemcpyAsync(dst, src, c->blob, hipMemcpyHostToDevice, side), "hipMemcpyAsync")))
+      return st;
+  }
+  if (!installs.empty()) {
+    rebuild_table(c, layer);
+    if ((st = hipcheck(hipMemcpyAsync(c->tables_dev + (int64_t)layer * c->E,
+                                      c->table_host + (int64_t)layer * c->E, sizeof(int32_t) * c->E,
+                                      hipMemcpyHostToDevice, side), "hipMemcpyAsync")))
+      return st;
+  }
+  if ((st = hipcheck(hipEventRecord(c->staged[layer], side), "hipEventRecord"))) return st;
+  c->staged_used[layer] = 1;
+  if ((st = hipcheck(hipMemcpyAsync(hit_mask_dev, mask, c->k, hipMemcpyHostToDevice, compute),
+                     "hipMemcpyAsync")) ||
+      (st = hipcheck(hipEventRecord(c->masked[layer], compute), "hipEventRecord")))
+    return st;
+  c->masked_used[layer] = 1;
+  if (hit_mask_host) std::memcpy(hit_mask_host, mask, c->k);
+  c->stats.hits += c->k - (int64_t)misses.size();
+  c->stats.misses += (int64_t)misses.size();
+  c->stats.bytes_staged += (int64_t)misses.size() * c->blob;
+  if (stats) *stats = c->stats;
+  return MOE_OK;
+}
+
+moe_status moe_cache_wait(moe_cache* c, int32_t layer, hipStream_t compute) {
+  if (!c || layer < 0 || layer >= c->L) return cfail(MOE_ERR_ARG, "moe_cache_wait: bad cache or layer");
+  if (!c->staged_used[layer]) return MOE_OK;
+  return hipcheck(hipStreamWaitEvent(compute, c->staged[layer], 0), "hipStreamWaitEvent");
+}
+
+moe_status moe_cache_slot_table(const moe_cache* c, int32_t layer, int32_t* out_host) {
+  if (!c || !out_host || layer < 0 || layer >= c->L)
+    return cfail(MOE_ERR_ARG, "moe_cache_slot_table: bad argument");
+  for (int e = 0; e < c->E; ++e) out_host[e] = -1;
+  for (int s = 0; s < c->S; ++s) {
+    const int e = c->slot_expert[(int64_t)layer * c->S + s];
+    if (e >= 0) out_host[e] = s;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_cache_export(const moe_cache* c, int32_t* slot_expert_host, int64_t* stamp_host) {
+  if (!c || !slot_expert_host || !stamp_host) return cfail(MOE_ERR_ARG, "moe_cache_export: null pointer");
+  std::memcpy(slot_expert_host, c->slot_expert.data(), sizeof(int32_t) * c->slot_expert.size());
+  std::memcpy(stamp_host, c->stamp.data(), sizeof(int64_t) * c->stamp.size());
+  return MOE_OK;
+}
+
+moe_status moe_cache_import(moe_cache* c, const int32_t* slot_expert_host, const int64_t* stamp_host) {
+  if (!c || !slot_expert_host || !stamp_host) return cfail(MOE_ERR_ARG, "moe_cache_import: null pointer");
+  for (int l = 0; l < c->L; ++l) {
+    std::vector<char> seen(c->E, 0);
+    for (int s = 0; s < c->S; ++s) {
+      const int e = slot_expert_host[(int64_t)l * c->S + s];
+      if (e < -1 || e >= c->E || (e >= 0 && seen[e]))
+        return cfail(MOE_ERR_STATE, "moe_cache_import: invalid slot assignment");
+      if (e >= 0) seen[e] = 1;
+    }
+  }
+  for (int l = 0; l < c->L; ++l) {
+    if (c->staged_used[l]) hipEventSynchronize(c->staged[l]);
+    if (c->masked_used[l]) hipEventSynchronize(c->masked[l]);
+  }
+  std::memcpy(c->slot_expert.data(), slot_expert_host, sizeof(int32_t) * c->slot_expert.size());
+  std::memcpy(c->stamp.data(), stamp_host, sizeof(int64_t) * c->stamp.size());
+  for (int l = 0; l < c->L; ++l) rebuild_table(c, l);
+  return hipcheck(hipMemcpy(c->tables_dev, c->table_host, sizeof(int32_t) * c->L * c->E,
+                            hipMemcpyHostToDevice), "hipMemcpy");
+}
+
+}  // extern "C"
