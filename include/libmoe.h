@@ -276,6 +276,13 @@ moe_status moe_cache_import(moe_cache* c, const int32_t* slot_expert_host, const
 moe_status moe_shared_gemv_bf16(const uint16_t* w, const float* h, int32_t T,
                                 int32_t rows, int32_t cols, float* out, hipStream_t stream);
 
+/* Kernel timing: the next launch of `call`'s main kernel (the dequant-GEMV of
+ * gate/up or down, or the router kernel) records `start` and `stop` at the
+ * kernel's own begin and end (hipExtLaunchKernelGGL events), so the caller
+ * can measure one kernel's duration on its stream without the launch gap.
+ * One-shot and per calling thread; NULL events disarm. */
+moe_status moe_profile_next_launch(moe_call call, hipEvent_t start, hipEvent_t stop);
+
 /* Unit-RMS rescale out[t] = x[t] / sqrt(mean(x[t]^2) + eps), used to feed one
  * decode step's output back as the next step's input.  out may equal x. */
 moe_status moe_rms_rescale(const float* x, int32_t T, int32_t d, float eps,

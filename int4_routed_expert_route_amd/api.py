@@ -67,6 +67,7 @@ _SIGNATURES = {
     "moe_cache_import": (ctypes.c_int, [_P, _P, _P]),
     "moe_shared_gemv_bf16": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P]),
     "moe_rms_rescale": (ctypes.c_int, [_P, _I32, _I32, _F, _P, _P]),
+    "moe_profile_next_launch": (ctypes.c_int, [ctypes.c_int, _P, _P]),
 }
 
 _lib = None
@@ -184,6 +185,13 @@ def moe_shared_gemv_bf16(w, h, T, rows, cols, out, stream=None):
 
 def moe_rms_rescale(x, T, d, eps, out, stream=None):
     _check(lib().moe_rms_rescale(_dev(x, "x"), int(T), int(d), float(eps), _dev(out, "out"), _stream(stream)))
+
+
+def moe_profile_next_launch(call, start_event, stop_event):
+    """Arm torch.cuda.Event(enable_timing=True) pairs for the next launch of `call`."""
+    s = None if start_event is None else ctypes.c_void_p(start_event.cuda_event)
+    e = None if stop_event is None else ctypes.c_void_p(stop_event.cuda_event)
+    _check(lib().moe_profile_next_launch(int(call), s, e))
 
 
 # ------------------------------------------------------------------ expert cache

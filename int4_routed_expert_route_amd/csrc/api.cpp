@@ -5,7 +5,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -49,22 +48,6 @@ moe_status check_dims(const moe_dims& d) {
     if ((p) && !aligned16(p)) return fail(MOE_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, #p); \
   } while (0)
 
-// Waves kept resident by the persistent expert kernels: 8 per compute unit.
-int max_resident_waves() {
-  static int cached = 0;
-  static std::mutex mu;
-  std::lock_guard<std::mutex> lk(mu);
-  if (cached == 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
-      cached = cus * 8;
-    else
-      cached = 2048;
-  }
-  return cached;
-}
-
 moe_status check_slots(const char* fn, const int32_t* slot_of_expert, int32_t n_slots,
                        const uint8_t* arena, int64_t slot_stride, const moe_dims& dims) {
   CHECK_PTR(slot_of_expert);
@@ -80,6 +63,22 @@ moe_status check_slots(const char* fn, const int32_t* slot_of_expert, int32_t n_
 }
 
 }  // namespace
+
+namespace {
+struct ProfileArm {
+  int call = -1;
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local ProfileArm g_profile;
+}  // namespace
+
+bool moe::take_profile_events(int call, hipEvent_t* start, hipEvent_t* stop) {
+  if (g_profile.call != call || !g_profile.start || !g_profile.stop) return false;
+  *start = g_profile.start;
+  *stop = g_profile.stop;
+  g_profile = ProfileArm{};
+  return true;
+}
 
 namespace moe_bridge {
 void set_error(const std::string& s) { g_last_error = s; }
@@ -128,18 +127,9 @@ size_t moe_workspace_size(moe_call call, int32_t T, moe_dims dims, moe_precision
     case MOE_CALL_ROUTE: return moe::route_workspace_bytes(T, dims.n_experts);
     case MOE_CALL_PERMUTE: return 0;
     case MOE_CALL_GATEUP:
-    case MOE_CALL_DOWN_COMBINE: {
-      if (prec != MOE_PREC_FP32) return 256;  // the MFMA path needs no partials
-      size_t best = 0;
-      for (int grouped = 0; grouped < 2; ++grouped) {
-        moe::GemvPlan p = call == MOE_CALL_GATEUP
-                              ? moe::plan_gateup(T, dims.d, dims.f, dims.n_experts, dims.top_k, grouped)
-                              : moe::plan_down(T, dims.d, dims.f, dims.n_experts, dims.top_k, grouped);
-        size_t b = moe::gemv_workspace_bytes(p);
-        if (b > best) best = b;
-      }
-      return best;
-    }
+    case MOE_CALL_DOWN_COMBINE:
+      if (prec != MOE_PREC_FP32) return 0;
+      return moe::gemv_workspace_bytes((int)call, T, dims.d, dims.top_k, true);
   }
   return SIZE_MAX;
 }
@@ -185,7 +175,7 @@ moe_status moe_expert_q4_gateup(const float* h, const int32_t* topk_idx, const i
   const char* fn = "moe_expert_q4_gateup";
   if (moe_status s = check_dims(dims)) return s;
   if (T < 1) return fail(MOE_ERR_ARG, "%s: T=%d", fn, T);
-  CHECK_PTR(h); CHECK_PTR(topk_idx); CHECK_PTR(act); CHECK_PTR(ws);
+  CHECK_PTR(h); CHECK_PTR(topk_idx); CHECK_PTR(act);
   CHECK_ALIGN(h); CHECK_ALIGN(topk_idx); CHECK_ALIGN(act); CHECK_ALIGN(ws); CHECK_ALIGN(offsets);
   CHECK_ALIGN(sorted_pair);
   if (moe_status s = check_slots(fn, slot_of_expert, n_slots, arena, slot_stride, dims)) return s;
@@ -196,8 +186,9 @@ moe_status moe_expert_q4_gateup(const float* h, const int32_t* topk_idx, const i
   const bool grouped = offsets != nullptr;
   const moe::BlobLayout L = moe::blob_layout(dims.d, dims.f);
   if (prec == MOE_PREC_FP32) {
-    const moe::GemvPlan p = moe::plan_gateup(T, dims.d, dims.f, dims.n_experts, dims.top_k, grouped);
-    const size_t need = moe::gemv_workspace_bytes(p);
+    if (!moe::gemv_supported(dims.d, dims.f, dims.top_k))
+      return fail(MOE_ERR_UNSUPPORTED, "%s: dims d=%d f=%d outside the fp32 kernels' range", fn, dims.d, dims.f);
+    const size_t need = moe::gemv_workspace_bytes(MOE_CALL_GATEUP, T, dims.d, dims.top_k, grouped);
     if (ws_bytes < need) return fail(MOE_ERR_CAPACITY, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
     moe::GateupArgs a{};
     a.h = h; a.topk_idx = topk_idx; a.slot_of_expert = slot_of_expert; a.n_slots = n_slots;
@@ -206,7 +197,7 @@ moe_status moe_expert_q4_gateup(const float* h, const int32_t* topk_idx, const i
     a.T = T; a.d = dims.d; a.f = dims.f; a.E = dims.n_experts; a.k = dims.top_k;
     a.off_q0 = L.gate_q; a.off_q1 = L.up_q; a.off_sb0 = L.gate_sb; a.off_sb1 = L.up_sb;
     a.act = reinterpret_cast<float*>(act);
-    hipError_t e = moe::launch_gateup_fp32(a, p, ws, max_resident_waves(), stream);
+    hipError_t e = moe::launch_gateup_fp32(a, stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
   }
   return fail(MOE_ERR_UNSUPPORTED, "%s: precision %d not available", fn, (int)prec);
@@ -223,7 +214,7 @@ moe_status moe_expert_q4_down_combine(const void* act, const int32_t* topk_idx, 
   (void)pair_pos;
   if (moe_status s = check_dims(dims)) return s;
   if (T < 1) return fail(MOE_ERR_ARG, "%s: T=%d", fn, T);
-  CHECK_PTR(act); CHECK_PTR(topk_idx); CHECK_PTR(topk_w); CHECK_PTR(y); CHECK_PTR(ws);
+  CHECK_PTR(act); CHECK_PTR(topk_idx); CHECK_PTR(topk_w); CHECK_PTR(y);
   CHECK_ALIGN(act); CHECK_ALIGN(topk_idx); CHECK_ALIGN(topk_w); CHECK_ALIGN(y); CHECK_ALIGN(ws);
   CHECK_ALIGN(offsets); CHECK_ALIGN(sorted_pair); CHECK_ALIGN(pair_pos); CHECK_ALIGN(residual);
   if (moe_status s = check_slots(fn, slot_of_expert, n_slots, arena, slot_stride, dims)) return s;
@@ -232,8 +223,9 @@ moe_status moe_expert_q4_down_combine(const void* act, const int32_t* topk_idx, 
   const bool grouped = offsets != nullptr;
   const moe::BlobLayout L = moe::blob_layout(dims.d, dims.f);
   if (prec == MOE_PREC_FP32) {
-    const moe::GemvPlan p = moe::plan_down(T, dims.d, dims.f, dims.n_experts, dims.top_k, grouped);
-    const size_t need = moe::gemv_workspace_bytes(p);
+    if (!moe::gemv_supported(dims.d, dims.f, dims.top_k))
+      return fail(MOE_ERR_UNSUPPORTED, "%s: dims d=%d f=%d outside the fp32 kernels' range", fn, dims.d, dims.f);
+    const size_t need = moe::gemv_workspace_bytes(MOE_CALL_DOWN_COMBINE, T, dims.d, dims.top_k, grouped);
     if (ws_bytes < need) return fail(MOE_ERR_CAPACITY, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
     moe::DownArgs a{};
     a.act = reinterpret_cast<const float*>(act); a.topk_idx = topk_idx; a.topk_w = topk_w;
@@ -241,7 +233,7 @@ moe_status moe_expert_q4_down_combine(const void* act, const int32_t* topk_idx, 
     a.offsets = offsets; a.sorted_pair = sorted_pair; a.residual = residual; a.y = y;
     a.T = T; a.d = dims.d; a.f = dims.f; a.E = dims.n_experts; a.k = dims.top_k;
     a.off_q = L.down_q; a.off_sb = L.down_sb;
-    hipError_t e = moe::launch_down_fp32(a, p, ws, max_resident_waves(), stream);
+    hipError_t e = moe::launch_down_fp32(a, ws, stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
   }
   return fail(MOE_ERR_UNSUPPORTED, "%s: precision %d not available", fn, (int)prec);
@@ -256,6 +248,15 @@ moe_status moe_shared_gemv_bf16(const uint16_t* w, const float* h, int32_t T, in
     return fail(MOE_ERR_ARG, "%s: T=%d rows=%d cols=%d (cols %% 8 == 0)", fn, T, rows, cols);
   hipError_t e = moe::launch_shared_gemv_bf16(w, h, T, rows, cols, out, stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
+}
+
+moe_status moe_profile_next_launch(moe_call call, hipEvent_t start, hipEvent_t stop) {
+  if ((int)call < 0 || (int)call > MOE_CALL_DOWN_COMBINE)
+    return fail(MOE_ERR_ARG, "moe_profile_next_launch: unknown call %d", (int)call);
+  g_profile.call = (start && stop) ? (int)call : -1;
+  g_profile.start = start;
+  g_profile.stop = stop;
+  return MOE_OK;
 }
 
 moe_status moe_rms_rescale(const float* x, int32_t T, int32_t d, float eps, float* out,

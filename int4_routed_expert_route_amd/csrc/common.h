@@ -1,6 +1,7 @@
 // Internal helpers shared by the libmoe HIP kernels (gfx950, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -83,6 +84,17 @@ __device__ __forceinline__ uint32_t arrive(uint32_t* counter) {
 }
 __device__ __forceinline__ void reset_counter(uint32_t* counter) {
   __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Plain launch, or (when timing events are armed) a launch that records the
+// events at the kernel's own begin and end.
+template <typename Kernel, typename... Args>
+inline void launch_maybe_timed(Kernel k, int grid, int block, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
+                               Args... args) {
+  if (ev0 && ev1)
+    hipExtLaunchKernelGGL(k, dim3(grid), dim3(block), 0, s, ev0, ev1, 0, args...);
+  else
+    hipLaunchKernelGGL(k, dim3(grid), dim3(block), 0, s, args...);
 }
 
 }  // namespace moe

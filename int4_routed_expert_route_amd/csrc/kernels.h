@@ -7,6 +7,10 @@
 
 namespace moe {
 
+// ---- one-shot kernel timing events (api.cpp); take_profile_events returns
+// true and clears the arm when `call` was armed on this thread.
+bool take_profile_events(int call, hipEvent_t* start, hipEvent_t* stop);
+
 // ---- routing (route.hip)
 size_t route_workspace_bytes(int T, int E);
 hipError_t launch_route(const float* x, const float* norm_w, float eps, const float* router_w,
@@ -19,16 +23,6 @@ hipError_t launch_permute(const int32_t* topk_idx, int n_pairs, int E, int32_t* 
                           int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, hipStream_t s);
 
 // ---- fp32 dequant-GEMV (q4_gemv.hip)
-struct GemvPlan {
-  int nch;       // 16-byte chunks per K-slice
-  int nks;       // K-slices per row
-  int n_rt;      // 64-row tiles
-  int n_groups;  // pairs (ungrouped) or experts (grouped)
-  int ntasks;
-  size_t partial_floats;
-  size_t counters;
-};
-
 struct GateupArgs {
   const float* h;
   const int32_t* topk_idx;
@@ -43,12 +37,8 @@ struct GateupArgs {
   int T, d, f, E, k;
   int64_t off_q0, off_q1, off_sb0, off_sb1;  // gate and up sections
   float* act;
-  // set by the launcher
-  float* partial;
-  uint32_t* counters;
-  uint32_t* claim;
-  int nks, n_rt, ntasks;
-  int persistent;
+  int n_rb;  // set by the launcher
+  int nck;   // set by the launcher: chunks per lane
 };
 
 struct DownArgs {
@@ -65,19 +55,15 @@ struct DownArgs {
   float* y;
   int T, d, f, E, k;
   int64_t off_q, off_sb;  // down sections
-  // set by the launcher
-  float* partial;
-  uint32_t* counters;
-  uint32_t* claim;
-  int nks, n_rt, n_groups, ntasks;
-  int persistent;
+  float* pair_out;        // grouped path: per-pair outputs (workspace), set by the launcher
+  int n_rb;               // set by the launcher
+  int nck;                // set by the launcher: chunks per lane
 };
 
-GemvPlan plan_gateup(int T, int d, int f, int E, int k, bool grouped);
-GemvPlan plan_down(int T, int d, int f, int E, int k, bool grouped);
-size_t gemv_workspace_bytes(const GemvPlan& p);
-hipError_t launch_gateup_fp32(GateupArgs a, const GemvPlan& p, void* ws, int max_resident, hipStream_t s);
-hipError_t launch_down_fp32(DownArgs a, const GemvPlan& p, void* ws, int max_resident, hipStream_t s);
+bool gemv_supported(int d, int f, int k);
+size_t gemv_workspace_bytes(int call, int T, int d, int k, bool grouped);
+hipError_t launch_gateup_fp32(GateupArgs a, hipStream_t s);
+hipError_t launch_down_fp32(DownArgs a, void* ws, hipStream_t s);
 
 // ---- bf16 shared-path GEMV (shared_gemv.hip)
 hipError_t launch_shared_gemv_bf16(const uint16_t* w, const float* h, int T, int rows, int cols,

@@ -3,28 +3,39 @@
 // The routed experts' projections are INT4 with affine groups of 64 columns,
 // one scale and one bias per group ("Optimizing a 14.3 GB model for an 8 GB
 // machine", section "Vectorization helped when it respected the storage
-// layout").  Once expert reads are explicit, these matvecs are the largest GPU
+// layout").  Once expert reads are explicit these matvecs are the largest GPU
 // cost of a decode step, and the kernel that won on the pages gave the GPU many
-// independent workgroups that claim rows until the dispatch is done (same page,
-// section "MoE needed parallel work, reuse, and coarse overlap").
+// independent workgroups instead of making lanes cooperate on one expert (same
+// page, section "MoE needed parallel work, reuse, and coarse overlap").  The
+// same section's four-groups-at-a-time lesson (shorter dependency chains) is
+// what the per-lane multi-group loop below keeps.
 //
-// gfx950 design
-//  * One blob row tile = 64 rows = one row per lane.  Inside a tile the 16-byte
-//    column chunks of the 64 rows are adjacent, so every 128-bit load of a wave
-//    reads 1 KiB of contiguous HBM, and a lane's (scale, bias) pairs are 4-byte
-//    loads that also coalesce to 256 bytes per group.
-//  * A task is (expert group, row tile, K-slice).  A wave issues all of its
-//    slice's nibble and pair loads up front, so several KiB per wave are in
-//    flight, then dequantises in registers.
-//  * Group-factored dequant: sum_c (s q_c + b) x_c = s * sum_c q_c x_c + b * sum_c x_c,
-//    so each weight costs one byte extract, one int->float convert and one FMA;
-//    the per-group x sums come from a 16-lane shuffle reduction.
-//  * The activations x are wave-uniform and read through uniform loads.
-//  * K-slices of the same (group, tile) write fp32 partials; the last task to
-//    arrive (device-scope counter) sums them in slice order and finishes the row
-//    (GELU * up, or the rank-ordered combine), so results are deterministic.
-//  * Tasks beyond the grid are claimed from an atomic counter (persistent
-//    workgroups).  Counters are returned to zero by the last arrival.
+// gfx950 design (batch-1 decode moves ~27 MB per layer, ~3.4 us at 8 TB/s, so
+// every wave puts all of its bytes in flight in one round trip and the VALU
+// cost per weight has to stay well under the ~4 ops/weight the CUs can issue
+// at that bandwidth):
+//  * A wave owns R rows of one matrix; its 64 lanes are P K-parts x R rows
+//    (gate/up: 8 x 8, down: 4 x 16).  In the blob layout the 16-byte chunks of
+//    64 consecutive rows sit side by side, so each 128-bit load instruction
+//    reads P runs of R*16 bytes.  Every lane issues all of its nibble and
+//    (scale, bias) loads before it computes anything.
+//  * Dequant without converts: a nibble pair masked into the two halves of a
+//    32-bit word is a pair of fp16 subnormals q * 2^-24, exactly; v_dot2_f32_f16
+//    multiplies it with an activation pair and accumulates in fp32.  The 2^24
+//    is folded into the group scale.  Activations are split into fp16 hi + lo
+//    pairs (x = hi + lo to ~22 bits) after scaling each 64-column group by a
+//    power of two that puts its largest magnitude in [2^14, 2^15), so the
+//    result keeps fp32-grade accuracy: 7 bit operations and 8 dot2 per 8 weights.
+//  * Group-factored dequant: sum_c (s q_c + b) x_c = s * sum_c q_c x_c + b * sum_c x_c.
+//  * The activation row is staged once per workgroup in LDS as hi/lo pairs,
+//    each K-part at its own bank offset so the parts' broadcast reads do not
+//    conflict; group sums and group exponents are reduced during the staging.
+//  * K-parts are summed with cross-lane shuffles; gate and up (two waves of
+//    one workgroup) meet in LDS, so GELU(gate) * up needs no global sync.
+//  * Down: a workgroup holds the k experts of one token for 16 output rows, one
+//    wave each, and sums them in rank order in LDS (deterministic combine).
+//    The grouped path writes per-pair outputs and a gather kernel combines them,
+//    again in rank order.
 #include "common.h"
 #include "kernels.h"
 
@@ -32,58 +43,39 @@ namespace moe {
 
 namespace {
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
 constexpr int kMBGrouped = 4;  // tokens per pass over the loaded weights (grouped path)
 
-// Activations are read-only for the whole kernel and wave-uniform at every use
-// in the dot products; reading them through the constant address space lets
-// the compiler fetch them with scalar loads into SGPR operands of the FMAs.
-typedef __attribute__((address_space(4))) const float cfloat;
-__device__ __forceinline__ const cfloat* uniform_ptr(const float* p) { return (const cfloat*)p; }
+__device__ __forceinline__ float dot2(uint32_t q, uint32_t x, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q), __builtin_bit_cast(half2_t, x), acc, false);
+}
 
-// Dot of 8 nibbles (one 32-bit word: columns 0..7, even column = low nibble)
-// with 8 consecutive x values.  The masks are kept opaque to the optimiser so
-// that the byte extracts map onto v_cvt_f32_ubyte{0,1,2,3}: 3 bit operations,
-// 8 converts and 8 FMAs per 8 weights.
-__device__ __forceinline__ float dot8(uint32_t w, const cfloat* x, float acc) {
-  uint32_t lo = w & 0x0F0F0F0Fu;
-  uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-  asm volatile("" : "+v"(lo));
-  asm volatile("" : "+v"(hi));
-  acc = fmaf((float)(lo & 0xffu), x[0], acc);
-  acc = fmaf((float)(hi & 0xffu), x[1], acc);
-  acc = fmaf((float)((lo >> 8) & 0xffu), x[2], acc);
-  acc = fmaf((float)((hi >> 8) & 0xffu), x[3], acc);
-  acc = fmaf((float)((lo >> 16) & 0xffu), x[4], acc);
-  acc = fmaf((float)((hi >> 16) & 0xffu), x[5], acc);
-  acc = fmaf((float)(lo >> 24), x[6], acc);
-  acc = fmaf((float)(hi >> 24), x[7], acc);
+// Dot of the 8 nibbles of one 32-bit word (columns 0..7, even column = low
+// nibble) with 8 activations given as 4 hi and 4 lo fp16 pairs ordered
+// (x0,x4) (x1,x5) (x2,x6) (x3,x7).  Result scaled by 2^-24.
+__device__ __forceinline__ float dot8(uint32_t w, const uint4 xh, const uint4 xl, float acc) {
+  const uint32_t m = 0x000F000Fu;
+  uint32_t w4 = w >> 4;
+  const uint32_t p0 = w & m;           // columns 0, 4
+  const uint32_t p1 = w4 & m;          // columns 1, 5
+  const uint32_t p2 = (w >> 8) & m;    // columns 2, 6
+  const uint32_t p3 = (w4 >> 8) & m;   // columns 3, 7
+  acc = dot2(p0, xh.x, acc);
+  acc = dot2(p1, xh.y, acc);
+  acc = dot2(p2, xh.z, acc);
+  acc = dot2(p3, xh.w, acc);
+  acc = dot2(p0, xl.x, acc);
+  acc = dot2(p1, xl.y, acc);
+  acc = dot2(p2, xl.z, acc);
+  acc = dot2(p3, xl.w, acc);
   return acc;
 }
 
-// Sums of x over the groups of a K-slice for one token: lanes 16g..16g+15 load
-// group g's 64 values as float4 and reduce; result broadcast to all lanes.
-template <int G>
-__device__ __forceinline__ void group_sums(const float* __restrict__ x, int ngroups, float (&out)[G]) {
-  const int lane = threadIdx.x % kWave;
-#pragma unroll
-  for (int gb = 0; gb < (G + 3) / 4; ++gb) {
-    const int g = gb * 4 + lane / 16;
-    float s = 0.0f;
-    if (g < ngroups) {
-      float4 v = reinterpret_cast<const float4*>(x + g * kGroup)[lane % 16];
-      s = (v.x + v.y) + (v.z + v.w);
-    }
-    s = sum16(s);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (gb * 4 + q < G) out[gb * 4 + q] = __shfl(s, q * 16, kWave);
-  }
-}
-
 struct Members {
-  int expert;  // -1: nothing to do
+  int expert;  // may be out of range: the blob lookup then fails
   int count;
-  int first;   // mode A: the pair itself; mode B: index into sorted_pair
+  int first;   // ungrouped: the pair itself; grouped: index into sorted_pair
 };
 
 __device__ __forceinline__ Members resolve_group(int group, const int32_t* __restrict__ topk_idx,
@@ -107,374 +99,520 @@ __device__ __forceinline__ Members resolve_group(int group, const int32_t* __res
   return m;
 }
 
-__device__ __forceinline__ int member_pair(const Members& m, int i,
-                                           const int32_t* __restrict__ sorted_pair, bool grouped,
-                                           int n_pairs) {
+__device__ __forceinline__ int member_pair(const Members& m, int i, const int32_t* __restrict__ sorted_pair,
+                                           bool grouped, int n_pairs) {
   if (!grouped) return m.first;
-  int p = sorted_pair[m.first + i];
+  const int p = sorted_pair[m.first + i];
   return (p >= 0 && p < n_pairs) ? p : -1;
 }
 
-// Resolve the expert's blob through the slot table; nullptr if not resident.
-__device__ __forceinline__ const uint8_t* expert_blob(int expert, int E,
-                                                      const int32_t* __restrict__ slot_of_expert,
-                                                      int n_slots, const uint8_t* arena,
-                                                      int64_t slot_stride) {
+// The expert's blob through the slot table, or nullptr if it is not resident.
+__device__ __forceinline__ const uint8_t* expert_blob(int expert, int E, const int32_t* __restrict__ slot_of_expert,
+                                                      int n_slots, const uint8_t* arena, int64_t slot_stride) {
   if (expert < 0 || expert >= E) return nullptr;
-  int slot = slot_of_expert[expert];
+  const int slot = slot_of_expert[expert];
   if (slot < 0 || slot >= n_slots) return nullptr;
   return arena + (int64_t)slot * slot_stride;
 }
 
-// ------------------------------------------------------------------ gate/up
-
-// Loads of one K-slice of one matrix tile: NCH 16-byte nibble chunks and NCH/2
-// (scale, bias) pairs for this lane's row.
-template <int NCH>
-struct SliceRegs {
-  uint4 q[NCH];
-  uint32_t sb[NCH / 2];
+// XCD-aware block mapping.  Workgroups are dispatched round-robin over the 8
+// XCDs (block b runs on XCD b % 8), and every XCD has its own L2.  The `per`
+// workgroups that cover one 64-row tile read neighbouring halves of the same
+// 128-byte lines (scale/bias words), so they are given block ids with equal
+// b % 8: the lines are then fetched from HBM once, into one L2.
+constexpr int kXcds = 8;
+struct TileSub {
+  int tile, sub;
 };
-
-template <int NCH>
-__device__ __forceinline__ void load_slice(SliceRegs<NCH>& r, const uint8_t* q, const uint8_t* sb) {
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) r.q[c] = *reinterpret_cast<const uint4*>(q + c * 1024);
-#pragma unroll
-  for (int g = 0; g < NCH / 2; ++g) r.sb[g] = *reinterpret_cast<const uint32_t*>(sb + g * 256);
+__device__ __forceinline__ TileSub xcd_tile_map(int b, int n_tiles, int per) {
+  const int span = kXcds * per;
+  const int full = (n_tiles * per) / span * span;
+  if (b < full) return TileSub{(b / span) * kXcds + b % kXcds, (b / kXcds) % per};
+  return TileSub{b / per, b % per};
 }
 
-// Dequantised dot of the slice with one token's x: sum_g s_g * (q . x)_g + b_g * xsum_g.
-template <int NCH>
-__device__ __forceinline__ float slice_dot(const SliceRegs<NCH>& r, const float* x, const float* xs) {
-  const cfloat* xc = uniform_ptr(x);
-  float acc = 0.0f;
+// K-part j of a row with G groups split over P parts: groups [g0, g0 + ng).
+struct Part {
+  int g0, ng;
+};
+template <int P>
+__device__ __forceinline__ Part part_of(int j, int G) {
+  const int base = G / P, rem = G % P;
+  return Part{j * base + min(j, rem), base + (j < rem ? 1 : 0)};
+}
+template <int P>
+__device__ __forceinline__ int part_of_group(int g, int G) {
+  const int base = G / P, rem = G % P;
+  const int big = rem * (base + 1);  // groups covered by the first `rem` (longer) parts
+  return g < big ? g / (base + 1) : rem + (g - big) / max(base, 1);
+}
+
+// One lane's share of its rows: up to GPP groups (2*GPP chunks) of its K-part
+// plus their (scale, bias) words.
+template <int GPP>
+struct LaneSlice {
+  uint4 q[2 * GPP];
+  uint32_t sb[GPP];
+};
+
+// Every lane issues GPP groups' worth of loads unconditionally (conditional
+// loads into registers with a default value make the compiler wait for them
+// early).  A part shorter than GPP groups re-reads its last group (a cache hit)
+// and lane_dot gives those padding groups a zero scale and bias.  The (scale,
+// bias) words go first, so code that only needs them waits for them alone; the
+// scheduling barrier keeps later arithmetic below the loads.
+template <int GPP>
+__device__ __forceinline__ void load_lane(LaneSlice<GPP>& s, const uint8_t* q, const uint8_t* sb, Part pt, int G) {
 #pragma unroll
-  for (int g = 0; g < NCH / 2; ++g) {
-    float d = 0.0f;
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const uint4 w = r.q[2 * g + cc];
-      const cfloat* xw = xc + (2 * g + cc) * kChunkCols;
-      d = dot8(w.x, xw + 0, d);
-      d = dot8(w.y, xw + 8, d);
-      d = dot8(w.z, xw + 16, d);
-      d = dot8(w.w, xw + 24, d);
-    }
-    acc = fmaf(half_lo(r.sb[g]), d, fmaf(half_hi(r.sb[g]), xs[g], acc));
+  for (int i = 0; i < GPP; ++i) {
+    const int g = max(0, min(pt.g0 + min(i, pt.ng - 1), G - 1));
+    s.sb[i] = *reinterpret_cast<const uint32_t*>(sb + (int64_t)g * 256);
   }
+#pragma unroll
+  for (int i = 0; i < 2 * GPP; ++i) {
+    const int c = max(0, min(2 * pt.g0 + min(i, 2 * pt.ng - 1), 2 * G - 1));
+    s.q[i] = *reinterpret_cast<const uint4*>(q + (int64_t)c * 1024);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// LDS image of one activation row of G <= GMAX groups: per 8-column word 4 hi
+// and 4 lo fp16 pairs (32 bytes); part j's words start 16*j bytes later than
+// packed (bank offset); per group its fp32 sum and its power-of-two scale.
+template <int P, int GMAX>
+struct XRow {
+  static constexpr int kWords = GMAX * 8;
+  uint4 v[2 * kWords + 2 * P];  // 16-byte units: word w of part j at 2*w + j
+  float gsum[GMAX];
+  float gscale[GMAX];
+};
+
+// Staging of an activation row x[0 .. 64*G) into LDS, split in two so that the
+// activation loads can be issued before the weight loads (and waited for on
+// their own): stage_load reads this thread's 8-column words into registers,
+// stage_store converts them and writes LDS.  `nthreads` threads (a multiple
+// of 64) all call both; NPASS >= ceil(8*G / nthreads).
+template <int NPASS>
+struct StageRegs {
+  float4 a[NPASS], b[NPASS];
+};
+
+template <int NPASS>
+__device__ __forceinline__ void stage_load(StageRegs<NPASS>& sr, const float* __restrict__ x, int G, int tid,
+                                           int nthreads) {
+  const int nw = G * 8;
+#pragma unroll
+  for (int ps = 0; ps < NPASS; ++ps) {
+    const int wi = min(ps * nthreads + tid, nw - 1);  // clamped: stage_store skips the extra words
+    sr.a[ps] = reinterpret_cast<const float4*>(x)[2 * wi];
+    sr.b[ps] = reinterpret_cast<const float4*>(x)[2 * wi + 1];
+  }
+}
+
+template <int P, int GMAX, int NPASS>
+__device__ __forceinline__ void stage_store(XRow<P, GMAX>& dst, const StageRegs<NPASS>& sr, int G, int tid,
+                                            int nthreads) {
+  const int nw = G * 8;
+#pragma unroll
+  for (int ps = 0; ps < NPASS; ++ps) {
+    if (ps * nthreads >= nw) break;  // uniform
+    const int wi = ps * nthreads + tid;
+    const bool live = wi < nw;
+    const float4 a = sr.a[ps], b = sr.b[ps];
+    // group (8 consecutive words = 8 consecutive lanes) sum and max magnitude
+    float s = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+    float mx = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                     fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+#pragma unroll
+    for (int o = 4; o >= 1; o >>= 1) {
+      s += __shfl_xor(s, o, kWave);
+      mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+    }
+    // 2^-e with max * 2^-e in [2^14, 2^15) (1 for zero or non-finite maxima)
+    int e = 0;
+    if (mx > 0.0f && mx < INFINITY) e = __builtin_amdgcn_frexp_expf(mx) - 15;
+    const float down = __builtin_ldexpf(1.0f, -e);
+    if (live) {
+      const float xs[8] = {a.x * down, a.y * down, a.z * down, a.w * down,
+                           b.x * down, b.y * down, b.z * down, b.w * down};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const _Float16 h0 = (_Float16)xs[i], h1 = (_Float16)xs[i + 4];
+        const _Float16 l0 = (_Float16)(xs[i] - (float)h0), l1 = (_Float16)(xs[i + 4] - (float)h1);
+        hi[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        lo[i] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+      }
+      const int g = wi / 8;
+      const int j = part_of_group<P>(g, G);
+      dst.v[2 * wi + j] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      dst.v[2 * wi + j + 1] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      if ((wi % 8) == 0) {
+        dst.gsum[g] = s;
+        dst.gscale[g] = __builtin_ldexpf(16777216.0f, e);  // 2^24 * 2^e
+      }
+    }
+  }
+}
+
+// sum over the lane's groups of s_g * (q . x)_g + b_g * xsum_g, then over the
+// P K-parts (lanes r, r + R, r + 2R, ...).  Every lane runs GPP groups (padding
+// groups have zero weights and reuse finite activations).  The next
+// 32-column chunk's activations are read from LDS while the current chunk is
+// multiplied.
+//
+// `nck` is 2*GPP passed at run time: the branch on it puts every chunk in its
+// own basic block, which keeps the scheduler from hoisting all LDS reads and
+// nibble extractions to the top (that needs hundreds of registers).
+template <int P, int GPP, int GMAX>
+__device__ __forceinline__ float lane_dot(const LaneSlice<GPP>& s, const XRow<P, GMAX>& x, int j, Part pt, int G,
+                                          int nck) {
+  float acc = 0.0f, d0 = 0.0f, d1 = 0.0f;
+  // chunk c's activations live in xb[c & 1]; padding chunks keep the finite
+  // values of an earlier chunk (their weights are zero)
+  uint4 xb[2][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    xb[0][i] = make_uint4(0u, 0u, 0u, 0u);
+    xb[1][i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (pt.ng > 0) {
+    const uint4* xv = &x.v[16 * pt.g0 + j];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xb[0][i] = xv[i];
+  }
+#pragma unroll
+  for (int c = 0; c < 2 * GPP; ++c) {
+    if (c < nck) {
+      if (c + 1 < 2 * GPP && c + 1 < 2 * pt.ng) {
+        const uint4* xv = &x.v[16 * (pt.g0 + (c + 1) / 2) + j + 8 * ((c + 1) & 1)];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xb[(c + 1) & 1][i] = xv[i];
+      }
+      const uint4* xc = xb[c & 1];
+      // opaque copy: waits for this chunk only and keeps its nibble extraction
+      // here (not hoisted out of the token loop)
+      uint4 w = s.q[c];
+      asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+      d0 = dot8(w.x, xc[0], xc[1], d0);
+      d1 = dot8(w.y, xc[2], xc[3], d1);
+      d0 = dot8(w.z, xc[4], xc[5], d0);
+      d1 = dot8(w.w, xc[6], xc[7], d1);
+      if (c & 1) {
+        const int g = min(pt.g0 + c / 2, G - 1);
+        const uint32_t sb = (c / 2 < pt.ng) ? s.sb[c / 2] : 0u;  // padding group: zero scale and bias
+        acc = fmaf(half_lo(sb) * x.gscale[g], d0 + d1, fmaf(half_hi(sb), x.gsum[g], acc));
+        d0 = 0.0f;
+        d1 = 0.0f;
+      }
+    }
+  }
+  constexpr int R = kWave / P;
+#pragma unroll
+  for (int o = R; o < kWave; o <<= 1) acc += __shfl_xor(acc, o, kWave);
   return acc;
 }
 
-// Gate and up slices against the same x in one pass, so every x value is used
-// twice right after it is loaded.
-template <int NCH>
-__device__ __forceinline__ void slice_dot2(const SliceRegs<NCH>& r0, const SliceRegs<NCH>& r1,
-                                           const float* x, const float* xs, float& out0, float& out1) {
-  const cfloat* xc = uniform_ptr(x);
-  float acc0 = 0.0f, acc1 = 0.0f;
-#pragma unroll
-  for (int g = 0; g < NCH / 2; ++g) {
-    float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const uint4 w0 = r0.q[2 * g + cc];
-      const uint4 w1 = r1.q[2 * g + cc];
-      const cfloat* xw = xc + (2 * g + cc) * kChunkCols;
-      d0 = dot8(w0.x, xw + 0, d0);
-      d1 = dot8(w1.x, xw + 0, d1);
-      d0 = dot8(w0.y, xw + 8, d0);
-      d1 = dot8(w1.y, xw + 8, d1);
-      d0 = dot8(w0.z, xw + 16, d0);
-      d1 = dot8(w1.z, xw + 16, d1);
-      d0 = dot8(w0.w, xw + 24, d0);
-      d1 = dot8(w1.w, xw + 24, d1);
-    }
-    acc0 = fmaf(half_lo(r0.sb[g]), d0, fmaf(half_hi(r0.sb[g]), xs[g], acc0));
-    acc1 = fmaf(half_lo(r1.sb[g]), d1, fmaf(half_hi(r1.sb[g]), xs[g], acc1));
-  }
-  out0 = acc0;
-  out1 = acc1;
-}
+// ------------------------------------------------------------------ gate/up
 
-template <int NCH, int MB>
-__global__ __launch_bounds__(kWave) void k_gateup_fp32(GateupArgs a) {
-  constexpr int G = NCH / 2;
-  const int lane = threadIdx.x;
+// Workgroup = 2 x RB waves: (gate, up) x RB blocks of R rows of one expert
+// group; lanes = P parts x R rows.  The staged activation row is shared by all
+// 2 * RB waves.
+#ifndef MOE_GATEUP_RB
+#define MOE_GATEUP_RB 2
+#endif
+constexpr int kGateRB = MOE_GATEUP_RB;
+
+template <int P, int GPP, int MB, bool GROUPED>
+__global__ __launch_bounds__(2 * kGateRB * kWave) void k_gateup(GateupArgs a) {
+  constexpr int R = kWave / P;
+  constexpr int GMAX = P * GPP;
+  constexpr int NT = 2 * kGateRB * kWave;
+  constexpr int NPASS = (8 * GMAX + NT - 1) / NT;
+  __shared__ XRow<P, GMAX> xs[MB];
+  __shared__ float g_lds[MB][kGateRB][R];
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int mat = wave / kGateRB;  // 0: gate, 1: up
+  const int rbi = wave % kGateRB;
+  const int lane = tid % kWave;
+  const int j = lane / R, r = lane % R;
   const int n_pairs = a.T * a.k;
-  const bool grouped = a.offsets != nullptr;
-  int task = blockIdx.x;
-  while (task < a.ntasks) {
-    const int ks = task % a.nks;
-    const int rt = (task / a.nks) % a.n_rt;
-    const int group = task / (a.nks * a.n_rt);
-    const Members m = resolve_group(group, a.topk_idx, a.offsets, a.pair_mask, a.mask_value, n_pairs);
-    if (m.count > 0) {
-      const uint8_t* blob = expert_blob(m.expert, a.E, a.slot_of_expert, a.n_slots, a.arena, a.slot_stride);
-      const bool ok = blob != nullptr;
-      if (!ok) blob = a.arena;  // keep the loads in bounds; outputs become NaN
-      const int c0 = ks * NCH;
-      const int64_t tile_q = (int64_t)rt * (kTileRows * a.d / 2) + (int64_t)c0 * 1024 + lane * 16;
-      const int64_t tile_sb = (int64_t)rt * (kTileRows * (a.d / kGroup) * 4) + (int64_t)(c0 / 2) * 256 + lane * 4;
-      SliceRegs<NCH> rg, ru;
-      load_slice(rg, blob + a.off_q0 + tile_q, blob + a.off_sb0 + tile_sb);
-      load_slice(ru, blob + a.off_q1 + tile_q, blob + a.off_sb1 + tile_sb);
-      for (int i0 = 0; i0 < m.count; i0 += MB) {
-        const int nm = min(MB, m.count - i0);
+  constexpr int kPer = kTileRows / (kGateRB * R);  // workgroups per 64-row tile
+  const int tiles_per_group = a.f / kTileRows;
+  const TileSub ts = xcd_tile_map(blockIdx.x, a.n_rb / kPer * (GROUPED ? a.E : a.T * a.k), kPer);
+  const int group = ts.tile / tiles_per_group;
+  const int row0 = (ts.tile % tiles_per_group) * kTileRows + ts.sub * (kGateRB * R) + rbi * R;
+  const Members m = resolve_group(group, a.topk_idx, GROUPED ? a.offsets : nullptr, a.pair_mask, a.mask_value,
+                                  n_pairs);
+  if (m.count <= 0) return;
+  const uint8_t* blob = expert_blob(m.expert, a.E, a.slot_of_expert, a.n_slots, a.arena, a.slot_stride);
+  const bool ok = blob != nullptr;
+  if (!ok) blob = a.arena;  // keep the loads in bounds; the outputs become NaN
+  const int G = a.d / kGroup;
+  const Part pt = part_of<P>(j, G);
+  const int trow = (row0 % kTileRows) + r;
+  const int64_t tile = (int64_t)(row0 / kTileRows);
+  const uint8_t* qbase = blob + (mat ? a.off_q1 : a.off_q0) + tile * (kTileRows * a.d / 2) + trow * 16;
+  const uint8_t* sbase = blob + (mat ? a.off_sb1 : a.off_sb0) + tile * (kTileRows * G * 4) + trow * 4;
+  LaneSlice<GPP> w;
+  if constexpr (!GROUPED) {
+    // one token: activation loads, then every weight load, then compute as
+    // the weights arrive (in issue order)
+    const int p = m.first;
+    StageRegs<NPASS> sr;
+    stage_load<NPASS>(sr, a.h + (int64_t)(p / a.k) * a.d, G, tid, NT);
+    load_lane<GPP>(w, qbase, sbase, pt, G);
+    stage_store<P, GMAX, NPASS>(xs[0], sr, G, tid, NT);
+    __syncthreads();
+    float v = lane_dot<P, GPP, GMAX>(w, xs[0], j, pt, G, a.nck);
+    if (!ok) v = f32_nan();
+    if (mat == 0 && j == 0) g_lds[0][rbi][r] = v;
+    __syncthreads();
+    if (mat == 1 && j == 0) a.act[(int64_t)p * a.f + row0 + r] = gelu_tanh(g_lds[0][rbi][r]) * v;
+  } else {
+    load_lane<GPP>(w, qbase, sbase, pt, G);
+    for (int i0 = 0; i0 < m.count; i0 += MB) {
+      const int nm = min(MB, m.count - i0);
+      int pm[MB];
+      StageRegs<NPASS> sr[MB];
 #pragma unroll
-        for (int j = 0; j < MB; ++j) {
-          if (j < nm) {
-            const int p = member_pair(m, i0 + j, a.sorted_pair, grouped, n_pairs);
-            if (p < 0) continue;
-            const float* x = a.h + (int64_t)(p / a.k) * a.d + (int64_t)c0 * kChunkCols;
-            float xs[G];
-            group_sums<G>(x, G, xs);
-            float g, u;
-            slice_dot2<NCH>(rg, ru, x, xs, g, u);
-            if (!ok) { g = f32_nan(); u = f32_nan(); }
-            if (a.nks == 1) {
-              a.act[(int64_t)p * a.f + rt * kTileRows + lane] = gelu_tanh(g) * u;
-            } else {
-              float* dst = a.partial + (((int64_t)p * a.n_rt + rt) * a.nks + ks) * (2 * kTileRows);
-              dst[lane] = g;
-              dst[kTileRows + lane] = u;
-            }
-          }
+      for (int t = 0; t < MB; ++t) {
+        pm[t] = t < nm ? member_pair(m, i0 + t, a.sorted_pair, true, n_pairs) : -1;
+        if (pm[t] >= 0) stage_load<NPASS>(sr[t], a.h + (int64_t)(pm[t] / a.k) * a.d, G, tid, NT);
+      }
+#pragma unroll
+      for (int t = 0; t < MB; ++t)
+        if (pm[t] >= 0) stage_store<P, GMAX, NPASS>(xs[t], sr[t], G, tid, NT);
+      __syncthreads();
+      float u[MB];
+#pragma unroll
+      for (int t = 0; t < MB; ++t) {
+        u[t] = 0.0f;
+        if (pm[t] >= 0) {
+          float v = lane_dot<P, GPP, GMAX>(w, xs[t], j, pt, G, a.nck);
+          if (!ok) v = f32_nan();
+          if (mat == 0 && j == 0) g_lds[t][rbi][r] = v;
+          u[t] = v;
         }
       }
-      // the last K-slice of this (group, tile) to arrive finishes its rows
-      if (a.nks > 1) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        uint32_t* ctr = a.counters + (int64_t)group * a.n_rt + rt;
-        uint32_t ticket = 0;
-        if (lane == 0) ticket = arrive(ctr);
-        ticket = __builtin_amdgcn_readfirstlane(ticket);
-        if (ticket == (uint32_t)a.nks - 1) {
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-          for (int i = 0; i < m.count; ++i) {
-            const int p = member_pair(m, i, a.sorted_pair, grouped, n_pairs);
-            if (p < 0) continue;
-            const float* src = a.partial + ((int64_t)p * a.n_rt + rt) * a.nks * (2 * kTileRows);
-            float g = 0.0f, u = 0.0f;
-            for (int s = 0; s < a.nks; ++s) {
-              g += src[s * 2 * kTileRows + lane];
-              u += src[s * 2 * kTileRows + kTileRows + lane];
-            }
-            a.act[(int64_t)p * a.f + rt * kTileRows + lane] = gelu_tanh(g) * u;
-          }
-          if (lane == 0) reset_counter(ctr);
-        }
+      __syncthreads();
+      if (mat == 1 && j == 0) {
+#pragma unroll
+        for (int t = 0; t < MB; ++t)
+          if (pm[t] >= 0) a.act[(int64_t)pm[t] * a.f + row0 + r] = gelu_tanh(g_lds[t][rbi][r]) * u[t];
       }
-    }
-    if (!a.persistent) break;
-    int next = 0;
-    if (lane == 0) next = (int)atomicAdd(a.claim, 1u) + (int)gridDim.x;
-    task = __builtin_amdgcn_readfirstlane(next);
-  }
-  if (a.persistent && lane == 0) {
-    uint32_t done = arrive(a.claim + 1);
-    if (done == gridDim.x - 1) {
-      reset_counter(a.claim);
-      reset_counter(a.claim + 1);
+      if (i0 + MB < m.count) __syncthreads();
     }
   }
 }
 
 // ------------------------------------------------------------------ down + combine
 
-template <int NCH, int MB>
-__global__ __launch_bounds__(kWave) void k_down_fp32(DownArgs a) {
-  constexpr int G = NCH / 2;
+constexpr int kDownP = 4;              // down: lanes = 4 K-parts x 16 rows
+constexpr int kDownR = kWave / kDownP;
+
+// Ungrouped: workgroup = k waves (the k experts of token t) x 16 output rows.
+template <int GPP>
+__global__ __launch_bounds__(1024) void k_down_token(DownArgs a) {
+  constexpr int GMAX = kDownP * GPP;
+  __shared__ XRow<kDownP, GMAX> xs[16];
+  __shared__ float o_lds[16][kDownR];
+  const int tid = threadIdx.x;
+  const int jr = tid / kWave;  // rank of the expert this wave runs
+  const int lane = tid % kWave;
+  const int j = lane / kDownR, r = lane % kDownR;
+  constexpr int kPer = kTileRows / kDownR;
+  const int tiles_per_tok = a.d / kTileRows;
+  const TileSub ts = xcd_tile_map(blockIdx.x, a.T * tiles_per_tok, kPer);
+  const int t = ts.tile / tiles_per_tok;
+  const int row0 = (ts.tile % tiles_per_tok) * kTileRows + ts.sub * kDownR;
+  const int p = t * a.k + jr;
+  const uint8_t* blob = expert_blob(a.topk_idx[p], a.E, a.slot_of_expert, a.n_slots, a.arena, a.slot_stride);
+  const bool ok = blob != nullptr;
+  if (!ok) blob = a.arena;
+  const int G = a.f / kGroup;
+  const Part pt = part_of<kDownP>(j, G);
+  const int trow = (row0 % kTileRows) + r;
+  const int64_t tile = (int64_t)(row0 / kTileRows);
+  constexpr int NPASS = (8 * GMAX + kWave - 1) / kWave;
+  StageRegs<NPASS> sr;
+  stage_load<NPASS>(sr, a.act + (int64_t)p * a.f, G, lane, kWave);
+  LaneSlice<GPP> w;
+  load_lane<GPP>(w, blob + a.off_q + tile * (kTileRows * a.f / 2) + trow * 16,
+                 blob + a.off_sb + tile * (kTileRows * G * 4) + trow * 4, pt, G);
+  stage_store<kDownP, GMAX, NPASS>(xs[jr], sr, G, lane, kWave);
+  __syncthreads();
+  float v = lane_dot<kDownP, GPP, GMAX>(w, xs[jr], j, pt, G, a.nck);
+  if (!ok) v = f32_nan();
+  if (j == 0) o_lds[jr][r] = v;
+  __syncthreads();
+  if (jr == 0 && j == 0) {
+    const int row = row0 + r;
+    float y = a.residual ? a.residual[(int64_t)t * a.d + row] : 0.0f;
+    for (int jj = 0; jj < a.k; ++jj) y = fmaf(a.topk_w[t * a.k + jj], o_lds[jj][r], y);
+    a.y[(int64_t)t * a.d + row] = y;
+  }
+}
+
+// Grouped: workgroup = 1 wave x 16 output rows of one expert, all its pairs;
+// per-pair outputs go to pair_out[p][row].
+template <int GPP, int MB>
+__global__ __launch_bounds__(kWave) void k_down_grouped(DownArgs a) {
+  constexpr int GMAX = kDownP * GPP;
+  __shared__ XRow<kDownP, GMAX> xs[MB];
   const int lane = threadIdx.x;
+  const int j = lane / kDownR, r = lane % kDownR;
   const int n_pairs = a.T * a.k;
-  const bool grouped = a.offsets != nullptr;
-  int task = blockIdx.x;
-  while (task < a.ntasks) {
-    const int ks = task % a.nks;
-    const int rt = (task / a.nks) % a.n_rt;
-    const int group = task / (a.nks * a.n_rt);
-    const Members m = resolve_group(group, a.topk_idx, a.offsets, nullptr, 0, n_pairs);
-    if (m.count > 0) {
-      const uint8_t* blob = expert_blob(m.expert, a.E, a.slot_of_expert, a.n_slots, a.arena, a.slot_stride);
-      const bool ok = blob != nullptr;
-      if (!ok) blob = a.arena;
-      const int c0 = ks * NCH;
-      const int64_t tile_q = (int64_t)rt * (kTileRows * a.f / 2) + (int64_t)c0 * 1024 + lane * 16;
-      const int64_t tile_sb = (int64_t)rt * (kTileRows * (a.f / kGroup) * 4) + (int64_t)(c0 / 2) * 256 + lane * 4;
-      SliceRegs<NCH> rd;
-      load_slice(rd, blob + a.off_q + tile_q, blob + a.off_sb + tile_sb);
-      for (int i0 = 0; i0 < m.count; i0 += MB) {
-        const int nm = min(MB, m.count - i0);
+  constexpr int kPer = kTileRows / kDownR;
+  const int tiles_per_e = a.d / kTileRows;
+  const TileSub ts = xcd_tile_map(blockIdx.x, a.E * tiles_per_e, kPer);
+  const int e = ts.tile / tiles_per_e;
+  const int row0 = (ts.tile % tiles_per_e) * kTileRows + ts.sub * kDownR;
+  const Members m = resolve_group(e, a.topk_idx, a.offsets, nullptr, 0, n_pairs);
+  if (m.count <= 0) return;
+  const uint8_t* blob = expert_blob(m.expert, a.E, a.slot_of_expert, a.n_slots, a.arena, a.slot_stride);
+  const bool ok = blob != nullptr;
+  if (!ok) blob = a.arena;
+  const int G = a.f / kGroup;
+  const Part pt = part_of<kDownP>(j, G);
+  const int trow = (row0 % kTileRows) + r;
+  const int64_t tile = (int64_t)(row0 / kTileRows);
+  constexpr int NPASS = (8 * GMAX + kWave - 1) / kWave;
+  LaneSlice<GPP> w;
+  load_lane<GPP>(w, blob + a.off_q + tile * (kTileRows * a.f / 2) + trow * 16,
+                 blob + a.off_sb + tile * (kTileRows * G * 4) + trow * 4, pt, G);
+  for (int i0 = 0; i0 < m.count; i0 += MB) {
+    const int nm = min(MB, m.count - i0);
+    int pm[MB];
+    StageRegs<NPASS> sr[MB];
 #pragma unroll
-        for (int j = 0; j < MB; ++j) {
-          if (j < nm) {
-            const int p = member_pair(m, i0 + j, a.sorted_pair, grouped, n_pairs);
-            if (p < 0) continue;
-            const float* x = a.act + (int64_t)p * a.f + (int64_t)c0 * kChunkCols;
-            float xs[G];
-            group_sums<G>(x, G, xs);
-            float o = slice_dot<NCH>(rd, x, xs);
-            if (!ok) o = f32_nan();
-            a.partial[(((int64_t)p * a.n_rt + rt) * a.nks + ks) * kTileRows + lane] = o;
-          }
-        }
+    for (int t = 0; t < MB; ++t) {
+      pm[t] = t < nm ? member_pair(m, i0 + t, a.sorted_pair, true, n_pairs) : -1;
+      if (pm[t] >= 0) stage_load<NPASS>(sr[t], a.act + (int64_t)pm[t] * a.f, G, lane, kWave);
+    }
+#pragma unroll
+    for (int t = 0; t < MB; ++t)
+      if (pm[t] >= 0) stage_store<kDownP, GMAX, NPASS>(xs[t], sr[t], G, lane, kWave);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+      if (pm[t] >= 0) {
+        float v = lane_dot<kDownP, GPP, GMAX>(w, xs[t], j, pt, G, a.nck);
+        if (!ok) v = f32_nan();
+        if (j == 0) a.pair_out[(int64_t)pm[t] * a.d + row0 + r] = v;
       }
     }
-    // every task of a row tile arrives, empty ones included; the last combines
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    uint32_t* ctr = a.counters + rt;
-    uint32_t ticket = 0;
-    if (lane == 0) ticket = arrive(ctr);
-    ticket = __builtin_amdgcn_readfirstlane(ticket);
-    if (ticket == (uint32_t)(a.n_groups * a.nks) - 1) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      const int row = rt * kTileRows + lane;
-      for (int t = 0; t < a.T; ++t) {
-        float yv = a.residual ? a.residual[(int64_t)t * a.d + row] : 0.0f;
-        for (int j = 0; j < a.k; ++j) {
-          const int p = t * a.k + j;
-          const float* src = a.partial + ((int64_t)p * a.n_rt + rt) * a.nks * kTileRows;
-          float o = 0.0f;
-          for (int s = 0; s < a.nks; ++s) o += src[s * kTileRows + lane];
-          yv = fmaf(a.topk_w[p], o, yv);
-        }
-        a.y[(int64_t)t * a.d + row] = yv;
-      }
-      if (lane == 0) reset_counter(ctr);
-    }
-    if (!a.persistent) break;
-    int next = 0;
-    if (lane == 0) next = (int)atomicAdd(a.claim, 1u) + (int)gridDim.x;
-    task = __builtin_amdgcn_readfirstlane(next);
+    if (i0 + MB < m.count) __syncthreads();
   }
-  if (a.persistent && lane == 0) {
-    uint32_t done = arrive(a.claim + 1);
-    if (done == gridDim.x - 1) {
-      reset_counter(a.claim);
-      reset_counter(a.claim + 1);
-    }
+}
+
+// y[t][i] = residual[t][i] + sum_j w[t][j] * pair_out[t*k+j][i], j in rank order.
+__global__ __launch_bounds__(256) void k_combine(DownArgs a) {
+  const int64_t n4 = (int64_t)a.T * a.d / 4;
+  const int64_t i4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i4 >= n4) return;
+  const int t = (int)(i4 * 4 / a.d);
+  const int col = (int)(i4 * 4 - (int64_t)t * a.d);
+  float4 y = a.residual ? reinterpret_cast<const float4*>(a.residual)[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int jj = 0; jj < a.k; ++jj) {
+    const float wj = a.topk_w[t * a.k + jj];
+    const float4 o = *reinterpret_cast<const float4*>(a.pair_out + (int64_t)(t * a.k + jj) * a.d + col);
+    y.x = fmaf(wj, o.x, y.x);
+    y.y = fmaf(wj, o.y, y.y);
+    y.z = fmaf(wj, o.z, y.z);
+    y.w = fmaf(wj, o.w, y.w);
   }
+  reinterpret_cast<float4*>(a.y)[i4] = y;
 }
 
 }  // namespace
 
 // ------------------------------------------------------------------ host side
 
-// Chunks per K-slice: the largest supported even count that divides the row.
-// Gate/up rows (2816 columns = 88 chunks) take 8-chunk slices (256 columns),
-// down rows (704 columns = 22 chunks) are read whole.
-static int pick_nch(int nch_total, const int* options, int n) {
-  for (int i = 0; i < n; ++i)
-    if (nch_total % options[i] == 0) return options[i];
-  return 2;
-}
-static int gateup_nch(int d) {
-  static const int opts[] = {8, 4, 2};
-  return pick_nch(d / kChunkCols, opts, 3);
-}
-static int down_nch(int f) {
-  static const int opts[] = {22, 16, 12, 8, 4, 2};
-  return pick_nch(f / kChunkCols, opts, 6);
+constexpr int kGateP = 8;  // gate/up: lanes = 8 K-parts x 8 rows
+
+// Groups per K-part: the smallest instantiated count covering the row's groups
+// (gate/up 2816 columns: 44 groups / 8 parts -> 6; down 704 columns: 11 / 4 -> 3).
+static int pick_gpp(int groups, int parts) {
+  static const int opts[] = {1, 2, 3, 4, 6, 8};
+  const int need = (groups + parts - 1) / parts;
+  for (int o : opts)
+    if (o >= need) return o;
+  return -1;
 }
 
-static int ceil_div(int a, int b) { return (a + b - 1) / b; }
-
-GemvPlan plan_gateup(int T, int d, int f, int E, int k, bool grouped) {
-  GemvPlan p;
-  p.nch = gateup_nch(d);
-  p.nks = (d / kChunkCols) / p.nch;
-  p.n_rt = f / kTileRows;
-  p.n_groups = grouped ? E : T * k;
-  p.ntasks = p.n_groups * p.n_rt * p.nks;
-  p.partial_floats = p.nks > 1 ? (size_t)T * k * p.n_rt * p.nks * 2 * kTileRows : 0;
-  p.counters = p.nks > 1 ? (size_t)p.n_groups * p.n_rt : 0;
-  return p;
+bool gemv_supported(int d, int f, int k) {
+  return pick_gpp(d / kGroup, kGateP) > 0 && pick_gpp(f / kGroup, kDownP) > 0 && k <= 16;
 }
 
-GemvPlan plan_down(int T, int d, int f, int E, int k, bool grouped) {
-  GemvPlan p;
-  p.nch = down_nch(f);
-  p.nks = (f / kChunkCols) / p.nch;
-  p.n_rt = d / kTileRows;
-  p.n_groups = grouped ? E : T * k;
-  p.ntasks = p.n_groups * p.n_rt * p.nks;
-  p.partial_floats = (size_t)T * k * p.n_rt * p.nks * kTileRows;
-  p.counters = (size_t)p.n_rt;
-  return p;
+size_t gemv_workspace_bytes(int call, int T, int d, int k, bool grouped) {
+  if (call == MOE_CALL_DOWN_COMBINE && grouped) return round256((int64_t)T * k * d * 4);
+  return 0;
 }
 
-// Workspace: [claim counters 256 B][task counters][partials], all 256-B aligned.
-size_t gemv_workspace_bytes(const GemvPlan& p) {
-  size_t b = 256;
-  b += round256((int64_t)p.counters * 4);
-  b += round256((int64_t)p.partial_floats * 4);
-  return b;
-}
-
-static void carve(void* ws, const GemvPlan& p, uint32_t** claim, uint32_t** counters, float** partial) {
-  char* c = reinterpret_cast<char*>(ws);
-  *claim = reinterpret_cast<uint32_t*>(c);
-  *counters = reinterpret_cast<uint32_t*>(c + 256);
-  *partial = reinterpret_cast<float*>(c + 256 + round256((int64_t)p.counters * 4));
-}
-
-static int grid_for(const GemvPlan& p, int max_resident) {
-  if (max_resident > 0 && p.ntasks > max_resident) return max_resident;
-  return p.ntasks;
-}
-
-hipError_t launch_gateup_fp32(GateupArgs a, const GemvPlan& p, void* ws, int max_resident, hipStream_t s) {
-  carve(ws, p, &a.claim, &a.counters, &a.partial);
-  a.nks = p.nks;
-  a.n_rt = p.n_rt;
-  a.ntasks = p.ntasks;
-  const int grid = grid_for(p, max_resident);
-  a.persistent = grid < p.ntasks;
-  const bool grouped = a.offsets != nullptr;
-#define MOE_GATEUP_CASE(N)                                                                    \
-  case N:                                                                                     \
-    if (grouped)                                                                              \
-      hipLaunchKernelGGL((k_gateup_fp32<N, kMBGrouped>), dim3(grid), dim3(kWave), 0, s, a);  \
-    else                                                                                      \
-      hipLaunchKernelGGL((k_gateup_fp32<N, 1>), dim3(grid), dim3(kWave), 0, s, a);           \
-    break;
-  switch (p.nch) {
-    MOE_GATEUP_CASE(2)
-    MOE_GATEUP_CASE(4)
-    MOE_GATEUP_CASE(8)
-    default: return hipErrorInvalidValue;
+#define MOE_GPP_SWITCH(GPPV, CASE)        \
+  switch (GPPV) {                         \
+    CASE(1)                               \
+    CASE(2)                               \
+    CASE(3)                               \
+    CASE(4)                               \
+    CASE(6)                               \
+    CASE(8)                               \
+    default: return hipErrorInvalidValue; \
   }
+
+hipError_t launch_gateup_fp32(GateupArgs a, hipStream_t s) {
+  const bool grouped = a.offsets != nullptr;
+  constexpr int R = kWave / kGateP;
+  if (a.f % (kGateRB * R)) return hipErrorInvalidValue;
+  a.n_rb = a.f / (kGateRB * R);
+  const int n_groups = grouped ? a.E : a.T * a.k;
+  const int grid = n_groups * a.n_rb;
+  a.nck = 2 * pick_gpp(a.d / kGroup, kGateP);
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  take_profile_events(MOE_CALL_GATEUP, &ev0, &ev1);
+#define MOE_GATEUP_CASE(N)                                                                      \
+  case N:                                                                                       \
+    if (grouped)                                                                                \
+      launch_maybe_timed((k_gateup<kGateP, N, kMBGrouped, true>), grid, 2 * kGateRB * kWave, s, ev0, ev1, a); \
+    else                                                                                                       \
+      launch_maybe_timed((k_gateup<kGateP, N, 1, false>), grid, 2 * kGateRB * kWave, s, ev0, ev1, a);         \
+    break;
+  MOE_GPP_SWITCH(pick_gpp(a.d / kGroup, kGateP), MOE_GATEUP_CASE)
 #undef MOE_GATEUP_CASE
   return hipGetLastError();
 }
 
-hipError_t launch_down_fp32(DownArgs a, const GemvPlan& p, void* ws, int max_resident, hipStream_t s) {
-  carve(ws, p, &a.claim, &a.counters, &a.partial);
-  a.nks = p.nks;
-  a.n_rt = p.n_rt;
-  a.n_groups = p.n_groups;
-  a.ntasks = p.ntasks;
-  const int grid = grid_for(p, max_resident);
-  a.persistent = grid < p.ntasks;
+hipError_t launch_down_fp32(DownArgs a, void* ws, hipStream_t s) {
   const bool grouped = a.offsets != nullptr;
-#define MOE_DOWN_CASE(N)                                                                   \
-  case N:                                                                                  \
-    if (grouped)                                                                           \
-      hipLaunchKernelGGL((k_down_fp32<N, kMBGrouped>), dim3(grid), dim3(kWave), 0, s, a); \
-    else                                                                                   \
-      hipLaunchKernelGGL((k_down_fp32<N, 1>), dim3(grid), dim3(kWave), 0, s, a);          \
+  a.n_rb = a.d / kDownR;
+  a.pair_out = reinterpret_cast<float*>(ws);
+  a.nck = 2 * pick_gpp(a.f / kGroup, kDownP);
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  take_profile_events(MOE_CALL_DOWN_COMBINE, &ev0, &ev1);
+  if (!grouped) {
+    const int grid = a.T * a.n_rb;
+#define MOE_DOWN_CASE(N)                                                       \
+  case N:                                                                      \
+    launch_maybe_timed((k_down_token<N>), grid, a.k * kWave, s, ev0, ev1, a); \
     break;
-  switch (p.nch) {
-    MOE_DOWN_CASE(2)
-    MOE_DOWN_CASE(4)
-    MOE_DOWN_CASE(8)
-    MOE_DOWN_CASE(12)
-    MOE_DOWN_CASE(16)
-    MOE_DOWN_CASE(22)
-    default: return hipErrorInvalidValue;
-  }
+    MOE_GPP_SWITCH(pick_gpp(a.f / kGroup, kDownP), MOE_DOWN_CASE)
 #undef MOE_DOWN_CASE
+    return hipGetLastError();
+  }
+  const int grid = a.E * a.n_rb;
+#define MOE_DOWNG_CASE(N)                                                              \
+  case N:                                                                              \
+    launch_maybe_timed((k_down_grouped<N, kMBGrouped>), grid, kWave, s, ev0, ev1, a); \
+    break;
+  MOE_GPP_SWITCH(pick_gpp(a.f / kGroup, kDownP), MOE_DOWNG_CASE)
+#undef MOE_DOWNG_CASE
+  const int64_t n4 = (int64_t)a.T * a.d / 4;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
+
+#undef MOE_GPP_SWITCH
 
 }  // namespace moe

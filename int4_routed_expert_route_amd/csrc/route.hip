@@ -5,6 +5,8 @@
 // taken on fp32 logits: largest first, equal logits to the lower expert id; the
 // weights are the softmax over all experts renormalised over the chosen ones,
 // which equals the softmax over the chosen logits alone.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -65,6 +67,55 @@ __device__ void wave_topk(const float* logits, int E, int k, int32_t* idx_out, f
   }
 }
 
+// Top-k of one token's E <= 256 logits by one workgroup of 256 threads.  The
+// rank of expert e is the number of experts that beat it (larger logit, or
+// equal logit and lower id); 2 threads per expert (E <= 128) or 1 (E <= 256)
+// count over halves of the list with 4-wide LDS reads.  No dependent shuffle
+// chains.
+__device__ void block_topk(const float* logits, int E, int k, int32_t* idx_out, float* w_out) {
+  __shared__ float4 s_l4[64];
+  __shared__ int s_cnt[256];
+  __shared__ float s_val[16];
+  __shared__ int s_idx[16];
+  float* s_l = reinterpret_cast<float*>(s_l4);
+  const int tid = threadIdx.x;
+  const int E4 = (E + 3) / 4;
+  s_l[tid] = tid < E ? load_coherent(logits + tid) : -INFINITY;
+  __syncthreads();
+  const int split = E <= 128 ? 2 : 1;
+  const int e = tid / split, h = tid % split;
+  int cnt = 0;
+  if (e < E) {
+    const float v = s_l[e];
+    const int q0 = h * (E4 / split), q1 = (h + 1 == split) ? E4 : (h + 1) * (E4 / split);
+#pragma unroll 4
+    for (int q = q0; q < q1; ++q) {
+      const float4 o = s_l4[q];
+      const int b = 4 * q;
+      cnt += (o.x > v || (o.x == v && b + 0 < e)) ? 1 : 0;
+      cnt += (o.y > v || (o.y == v && b + 1 < e)) ? 1 : 0;
+      cnt += (o.z > v || (o.z == v && b + 2 < e)) ? 1 : 0;
+      cnt += (o.w > v || (o.w == v && b + 3 < e)) ? 1 : 0;
+    }
+  }
+  if (split == 2) cnt += __shfl_xor(cnt, 1, kWave);
+  if (e < E && h == 0 && cnt < k) {
+    s_idx[cnt] = e;
+    s_val[cnt] = s_l[e];
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    const float m = s_val[0];
+    const float ex = tid < k ? expf(s_val[tid] - m) : 0.0f;
+    const float sum = wave_sum(ex);
+    if (tid < k) {
+      idx_out[tid] = s_idx[tid];
+      w_out[tid] = ex / sum;
+    }
+  }
+  __syncthreads();
+}
+
 // 1 / sqrt(mean(x^2) + eps) of one row, by one wave.
 __device__ float wave_rinv(const float* x, int d, float eps) {
   const int lane = threadIdx.x % kWave;
@@ -78,8 +129,12 @@ __device__ float wave_rinv(const float* x, int d, float eps) {
   return 1.0f / sqrtf(s / (float)d + eps);
 }
 
-// Fused path for T <= kSmallT: every wave computes one expert's logit for all
-// tokens; the last workgroup to finish runs top-k.  Workgroup 0 writes h.
+// Fused path for T <= kSmallT and d <= 4096: every wave computes one expert's
+// logit for all tokens, with all of its loads issued before any arithmetic
+// (one memory round trip); the last workgroup to finish runs top-k.
+// Workgroup 0 also writes h.
+constexpr int kMaxV = 16;  // float4 per lane per row (d <= 64 * 4 * 16)
+
 __global__ __launch_bounds__(kRouteWaves * kWave) void k_route_small(
     const float* __restrict__ x, const float* __restrict__ norm_w, float eps,
     const float* __restrict__ router_w, const float* __restrict__ router_bias, int T, int d, int E,
@@ -87,57 +142,70 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void k_route_small(
     float* __restrict__ logits, uint32_t* __restrict__ counter) {
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int e = blockIdx.x * kRouteWaves + wave;
+  const int e = min(blockIdx.x * kRouteWaves + wave, E - 1);
+  const bool has_e = blockIdx.x * kRouteWaves + wave < E;
   __shared__ uint32_t s_ticket;
+  const int n4 = d / 4;
+  const float4* w4 = reinterpret_cast<const float4*>(router_w + (size_t)e * d);
+  const float4* nw4 = reinterpret_cast<const float4*>(norm_w);
+  float4 wv[kMaxV], nv[kMaxV];
+#pragma unroll
+  for (int i = 0; i < kMaxV; ++i) {
+    const int fi = lane + kWave * i;
+    if (fi < n4) {
+      wv[i] = w4[fi];
+      nv[i] = norm_w ? nw4[fi] : make_float4(1.f, 1.f, 1.f, 1.f);
+    }
+  }
+  const float bias = router_bias ? router_bias[e] : 0.0f;
   for (int t = 0; t < T; ++t) {
-    const float* xt = x + (size_t)t * d;
-    float rinv = norm_w ? wave_rinv(xt, d, eps) : 1.0f;
-    if (e < E) {
-      const float4* w4 = reinterpret_cast<const float4*>(router_w + (size_t)e * d);
-      const float4* x4 = reinterpret_cast<const float4*>(xt);
-      const float4* n4 = reinterpret_cast<const float4*>(norm_w);
-      float acc = 0.0f;
-      for (int i = lane; i < d / 4; i += kWave) {
-        float4 a = x4[i];
-        float4 b = w4[i];
-        if (norm_w) {
-          float4 n = n4[i];
-          a.x = a.x * rinv * n.x; a.y = a.y * rinv * n.y;
-          a.z = a.z * rinv * n.z; a.w = a.w * rinv * n.w;
-        }
-        acc += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
-      }
-      acc = wave_sum(acc);
-      if (lane == 0) {
-        if (router_bias) acc += router_bias[e];
-        store_coherent(logits + (size_t)t * E + e, acc);
+    const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)t * d);
+    float4 xv[kMaxV];
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxV; ++i) {
+      const int fi = lane + kWave * i;
+      if (fi < n4) {
+        xv[i] = x4[fi];
+        ss += xv[i].x * xv[i].x + xv[i].y * xv[i].y + xv[i].z * xv[i].z + xv[i].w * xv[i].w;
       }
     }
-    if (blockIdx.x == 0 && wave == (t % kRouteWaves)) {
-      const float4* x4 = reinterpret_cast<const float4*>(xt);
-      const float4* n4 = reinterpret_cast<const float4*>(norm_w);
-      float4* h4 = reinterpret_cast<float4*>(h_out + (size_t)t * d);
-      for (int i = lane; i < d / 4; i += kWave) {
-        float4 a = x4[i];
+    const float rinv = norm_w ? 1.0f / sqrtf(wave_sum(ss) / (float)d + eps) : 1.0f;
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxV; ++i) {
+      const int fi = lane + kWave * i;
+      if (fi < n4) {
+        float4 a = xv[i];
         if (norm_w) {
-          float4 n = n4[i];
-          a.x = a.x * rinv * n.x; a.y = a.y * rinv * n.y;
-          a.z = a.z * rinv * n.z; a.w = a.w * rinv * n.w;
+          a.x = a.x * rinv * nv[i].x; a.y = a.y * rinv * nv[i].y;
+          a.z = a.z * rinv * nv[i].z; a.w = a.w * rinv * nv[i].w;
         }
-        h4[i] = a;
+        xv[i] = a;
+        acc += a.x * wv[i].x + a.y * wv[i].y + a.z * wv[i].z + a.w * wv[i].w;
+      }
+    }
+    acc = wave_sum(acc);
+    if (has_e && lane == 0) store_coherent(logits + (size_t)t * E + e, acc + bias);
+    if (blockIdx.x == 0 && wave == (t % kRouteWaves)) {
+      float4* h4 = reinterpret_cast<float4*>(h_out + (size_t)t * d);
+#pragma unroll
+      for (int i = 0; i < kMaxV; ++i) {
+        const int fi = lane + kWave * i;
+        if (fi < n4) h4[fi] = xv[i];
       }
     }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    release_fence();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     s_ticket = arrive(counter);
   }
   __syncthreads();
   if (s_ticket != gridDim.x - 1) return;
-  acquire_fence();
-  for (int t = wave; t < T; t += kRouteWaves)
-    wave_topk(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k, true);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  for (int t = 0; t < T; ++t)
+    block_topk(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
   if (threadIdx.x == 0) reset_counter(counter);
 }
 
@@ -226,15 +294,21 @@ hipError_t launch_route(const float* x, const float* norm_w, float eps, const fl
                         int32_t* topk_idx, float* topk_w, void* ws, hipStream_t s) {
   uint32_t* counter = reinterpret_cast<uint32_t*>(ws);
   float* logits = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + 256);
-  if (T <= kSmallT) {
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  take_profile_events(MOE_CALL_ROUTE, &ev0, &ev1);
+  if (T <= kSmallT && d <= kWave * 4 * kMaxV) {
     int grid = (E + kRouteWaves - 1) / kRouteWaves;
-    hipLaunchKernelGGL(k_route_small, dim3(grid), dim3(kRouteWaves * kWave), 0, s, x, norm_w, eps,
-                       router_w, router_bias, T, d, E, k, h_out, topk_idx, topk_w, logits, counter);
+    launch_maybe_timed(k_route_small, grid, kRouteWaves * kWave, s, ev0, ev1, x, norm_w, eps, router_w,
+                       router_bias, T, d, E, k, h_out, topk_idx, topk_w, logits, counter);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_rmsnorm, dim3((T + 3) / 4), dim3(256), 0, s, x, norm_w, eps, T, d, h_out);
-  hipLaunchKernelGGL(k_router_gemm, dim3((E + kGE - 1) / kGE, (T + kGT - 1) / kGT), dim3(256), 0, s,
-                     h_out, router_w, router_bias, T, d, E, logits);
+  if (ev0 && ev1)
+    hipExtLaunchKernelGGL(k_router_gemm, dim3((E + kGE - 1) / kGE, (T + kGT - 1) / kGT), dim3(256), 0, s,
+                          ev0, ev1, 0, h_out, router_w, router_bias, T, d, E, logits);
+  else
+    hipLaunchKernelGGL(k_router_gemm, dim3((E + kGE - 1) / kGE, (T + kGT - 1) / kGT), dim3(256), 0, s, h_out,
+                       router_w, router_bias, T, d, E, logits);
   hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, topk_idx, topk_w);
   return hipGetLastError();
 }

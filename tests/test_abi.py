@@ -94,11 +94,13 @@ def test_validation_before_any_hip_call(api):
     assert g(_p(A), _p(A), _p(A), 0, _p(A), stride, None, None, None, 0, 1, dm, 0, _p(A), _p(A), wsg, None) == api.MOE_ERR_ARG
     assert g(_p(A), _p(A), _p(A), 128, _p(A), stride, _p(A), _p(A), _p(A), 1, 1, dm, 0, _p(A), _p(A), wsg, None) == api.MOE_ERR_UNSUPPORTED
     assert g(_p(A), _p(A), _p(A), 128, _p(A), stride, _p(A), None, None, 1, 1, dm, 0, _p(A), _p(A), wsg, None) == api.MOE_ERR_ARG
-    assert g(_p(A), _p(A), _p(A), 128, _p(A), stride, None, None, None, 0, 1, dm, 0, _p(A), _p(A), 16, None) == api.MOE_ERR_CAPACITY
     dc = lib.moe_expert_q4_down_combine
     wsd = api.moe_workspace_size(api.MOE_CALL_DOWN_COMBINE, 1, dm)
     assert dc(_p(A), _p(A), None, _p(A), 128, _p(A), stride, None, None, None, None, 1, dm, 0, _p(A), _p(A), wsd, None) == api.MOE_ERR_ARG
     assert dc(_p(A), _p(A), _p(A), _p(A), 128, _p(A), stride, None, None, None, _p(A + 8), 1, dm, 0, _p(A), _p(A), wsd, None) == api.MOE_ERR_ALIGN
+    # the grouped down path needs per-pair outputs in its workspace
+    assert api.moe_workspace_size(api.MOE_CALL_DOWN_COMBINE, 4, dm) == 4 * 8 * 2816 * 4
+    assert dc(_p(A), _p(A), _p(A), _p(A), 128, _p(A), stride, _p(A), _p(A), _p(A), None, 4, dm, 0, _p(A), _p(A), 16, None) == api.MOE_ERR_CAPACITY
     # helpers
     assert lib.moe_shared_gemv_bf16(_p(A), _p(A), 1, 16, 12, _p(A), None) == api.MOE_ERR_ARG
     assert lib.moe_rms_rescale(_p(A), 1, 6, 1e-6, _p(A), None) == api.MOE_ERR_ARG

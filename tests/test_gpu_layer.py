@@ -323,3 +323,44 @@ def test_rms_rescale():
     x = torch.from_numpy(x_np).cuda()
     L.moe_rms_rescale(x, 5, D, 1e-6, x)
     assert row_rel_err(_np(x), orc.rms_rescale(x_np)) < 1e-5
+
+
+@pytest.mark.parametrize("d,f,E,k,T", [(256, 128, 16, 4, 2), (128, 64, 8, 2, 3), (640, 192, 32, 8, 1),
+                                       (2816, 704, 128, 8, 1)])
+def test_other_shapes_parity(d, f, E, k, T):
+    """Shapes whose groups do not fill every K-part (and the full shape again),
+    ungrouped and grouped."""
+    dm = L.dims(d, f, E, k)
+    stride = L.moe_expert_blob_bytes(dm)
+    blobs = [synth.expert_blob(d, f, 3, 0, e) for e in range(E)]
+    arena = torch.from_numpy(np.concatenate(blobs)).cuda()
+    slots = torch.arange(E, dtype=torch.int32, device="cuda")
+    rw = synth.router_weight(d, E, 3, 0)
+    nw = synth.norm_weight(d, 3, 0)
+    x_np = synth.tokens(T, d, 3, stream=d)
+    x = torch.from_numpy(x_np).cuda()
+    h = torch.empty(T, d, device="cuda")
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, device="cuda")
+    ws = lambda c: torch.zeros(max(L.moe_workspace_size(c, T, dm), 256), dtype=torch.uint8, device="cuda")
+    L.moe_route(x, torch.from_numpy(nw).cuda(), 1e-6, torch.from_numpy(rw).cuda(), None, T, dm, h, idx, w, ws(0))
+    gi = _np(idx)
+    ry, *_ = orc.moe_layer(x_np, nw, rw, None, lambda e: blobs[e], d, f, k, idx_override=gi)
+    act = torch.empty(T * k, f, device="cuda")
+    y = torch.empty(T, d, device="cuda")
+    L.moe_expert_q4_gateup(h, idx, slots, E, arena, stride, None, None, None, 0, T, dm, L.MOE_PREC_FP32, act, ws(2))
+    L.moe_expert_q4_down_combine(act, idx, w, slots, E, arena, stride, None, None, None, x, T, dm, L.MOE_PREC_FP32,
+                                 y, ws(3))
+    assert row_rel_err(_np(y), ry) < TOL_FP32
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    L.moe_permute(idx, T, dm, counts, offsets, sp, pp)
+    act2 = torch.empty(T * k, f, device="cuda")
+    y2 = torch.empty(T, d, device="cuda")
+    L.moe_expert_q4_gateup(h, idx, slots, E, arena, stride, offsets, sp, None, 0, T, dm, L.MOE_PREC_FP32, act2,
+                           ws(2))
+    L.moe_expert_q4_down_combine(act2, idx, w, slots, E, arena, stride, offsets, sp, pp, x, T, dm,
+                                 L.MOE_PREC_FP32, y2, ws(3))
+    assert row_rel_err(_np(y2), ry) < TOL_FP32
