@@ -89,8 +89,11 @@ typedef struct moe_dims {
 } moe_dims;
 
 typedef enum moe_precision {
-  MOE_PREC_FP32 = 0,      /* int4 -> fp32 dequant, fp32 FMA accumulate (decode) */
-  MOE_PREC_BF16_MFMA = 1  /* int4 -> bf16 tiles in LDS, bf16 MFMA, fp32 accumulate (prefill) */
+  MOE_PREC_FP32 = 0,      /* int4 weights, activations kept to ~fp32 accuracy, fp32 accumulate (decode) */
+  MOE_PREC_BF16_MFMA = 1, /* int4 -> bf16 tiles in LDS, bf16 activations, bf16 MFMA, fp32 accumulate */
+  MOE_PREC_F16_MFMA = 2   /* int4 -> fp16 tiles in LDS, fp16 activations, fp16 MFMA, fp32 accumulate:
+                             the same MFMA rate with 3 more mantissa bits; activations must stay
+                             below 65504 in magnitude */
 } moe_precision;
 
 typedef enum moe_call {
@@ -178,7 +181,8 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t T, moe_dims dims,
  *                  parallel work, reuse, and coarse overlap").  Only with
  *                  offsets == NULL.
  *   prec           MOE_PREC_FP32: act is fp32 [T*k][f];
- *                  MOE_PREC_BF16_MFMA: act is bf16 [T*k][f] (needs offsets).
+ *                  MOE_PREC_BF16_MFMA / MOE_PREC_F16_MFMA: act is bf16 / fp16
+ *                  [T*k][f]; grouped GEMM on MFMA (needs offsets, T*k <= 65536).
  * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_CAPACITY, MOE_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------- */
 moe_status moe_expert_q4_gateup(const float* h, const int32_t* topk_idx,
@@ -193,7 +197,7 @@ moe_status moe_expert_q4_gateup(const float* h, const int32_t* topk_idx,
  * moe_expert_q4_down_combine — out[p] = W_down[e] act[p], then
  * y[t] = residual[t] + sum_j topk_w[t][j] * out[t*k+j], summed in rank order
  * (deterministic).  Same slot-table, offsets and precision rules as gateup.
- *   act       device fp32 or bf16 [T*k][f]  from moe_expert_q4_gateup
+ *   act       device fp32, bf16 or fp16 [T*k][f]  from moe_expert_q4_gateup (per prec)
  *   topk_w    device fp32 [T][k]
  *   pair_pos  device int32 [T*k] from moe_permute, or NULL with offsets NULL
  *   residual  device fp32 [T][d] or NULL (then y is the expert mix alone);

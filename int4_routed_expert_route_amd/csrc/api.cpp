@@ -128,7 +128,8 @@ size_t moe_workspace_size(moe_call call, int32_t T, moe_dims dims, moe_precision
     case MOE_CALL_PERMUTE: return 0;
     case MOE_CALL_GATEUP:
     case MOE_CALL_DOWN_COMBINE:
-      if (prec != MOE_PREC_FP32) return 0;
+      if (prec == MOE_PREC_BF16_MFMA || prec == MOE_PREC_F16_MFMA)
+        return moe::mfma_workspace_bytes((int)call, T, dims.d, dims.f, dims.n_experts, dims.top_k);
       return moe::gemv_workspace_bytes((int)call, T, dims.d, dims.top_k, true);
   }
   return SIZE_MAX;
@@ -200,6 +201,18 @@ moe_status moe_expert_q4_gateup(const float* h, const int32_t* topk_idx, const i
     hipError_t e = moe::launch_gateup_fp32(a, stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
   }
+  if (prec == MOE_PREC_BF16_MFMA || prec == MOE_PREC_F16_MFMA) {
+    if (!grouped)
+      return fail(MOE_ERR_UNSUPPORTED, "%s: the MFMA path needs offsets and sorted_pair (moe_permute)", fn);
+    if ((int64_t)T * dims.top_k > 65536) return fail(MOE_ERR_ARG, "%s: T*k must be <= 65536", fn);
+    const size_t need = moe::mfma_workspace_bytes(MOE_CALL_GATEUP, T, dims.d, dims.f, dims.n_experts, dims.top_k);
+    if (!ws) return fail(MOE_ERR_ARG, "%s: ws is null", fn);
+    if (ws_bytes < need) return fail(MOE_ERR_CAPACITY, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+    hipError_t e = moe::launch_gateup_mfma(prec == MOE_PREC_F16_MFMA, h, offsets, sorted_pair, slot_of_expert, n_slots, arena, slot_stride, T,
+                                           dims.d, dims.f, dims.n_experts, dims.top_k, L.gate_q, L.up_q, L.gate_sb,
+                                           L.up_sb, act, ws, stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
+  }
   return fail(MOE_ERR_UNSUPPORTED, "%s: precision %d not available", fn, (int)prec);
 }
 
@@ -234,6 +247,21 @@ moe_status moe_expert_q4_down_combine(const void* act, const int32_t* topk_idx, 
     a.T = T; a.d = dims.d; a.f = dims.f; a.E = dims.n_experts; a.k = dims.top_k;
     a.off_q = L.down_q; a.off_sb = L.down_sb;
     hipError_t e = moe::launch_down_fp32(a, ws, stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
+  }
+  if (prec == MOE_PREC_BF16_MFMA || prec == MOE_PREC_F16_MFMA) {
+    if (!grouped)
+      return fail(MOE_ERR_UNSUPPORTED, "%s: the MFMA path needs offsets and sorted_pair (moe_permute)", fn);
+    if ((int64_t)T * dims.top_k > 65536) return fail(MOE_ERR_ARG, "%s: T*k must be <= 65536", fn);
+    const size_t need =
+        moe::mfma_workspace_bytes(MOE_CALL_DOWN_COMBINE, T, dims.d, dims.f, dims.n_experts, dims.top_k);
+    if (!ws) return fail(MOE_ERR_ARG, "%s: ws is null", fn);
+    if (ws_bytes < need) return fail(MOE_ERR_CAPACITY, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+    float* pair_out = nullptr;
+    hipError_t e = moe::launch_down_mfma(prec == MOE_PREC_F16_MFMA, act, offsets, sorted_pair, slot_of_expert, n_slots, arena, slot_stride, T,
+                                         dims.d, dims.f, dims.n_experts, dims.top_k, L.down_q, L.down_sb, ws,
+                                         &pair_out, stream);
+    if (e == hipSuccess) e = moe::launch_combine(pair_out, topk_w, residual, y, T, dims.d, dims.top_k, stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
   }
   return fail(MOE_ERR_UNSUPPORTED, "%s: precision %d not available", fn, (int)prec);

@@ -65,6 +65,21 @@ size_t gemv_workspace_bytes(int call, int T, int d, int k, bool grouped);
 hipError_t launch_gateup_fp32(GateupArgs a, hipStream_t s);
 hipError_t launch_down_fp32(DownArgs a, void* ws, hipStream_t s);
 
+// rank-ordered gather combine of per-pair outputs (q4_gemv.hip)
+hipError_t launch_combine(const float* pair_out, const float* topk_w, const float* residual, float* y, int T,
+                          int d, int k, hipStream_t s);
+
+// ---- grouped bf16 MFMA GEMM for batched prefill (q4_grouped_mfma.hip)
+size_t mfma_workspace_bytes(int call, int T, int d, int f, int E, int k);
+hipError_t launch_gateup_mfma(bool f16, const float* h, const int32_t* offsets, const int32_t* sorted_pair,
+                              const int32_t* slot_of_expert, int n_slots, const uint8_t* arena, int64_t slot_stride,
+                              int T, int d, int f, int E, int k, int64_t off_q0, int64_t off_q1, int64_t off_sb0,
+                              int64_t off_sb1, void* act_out, void* ws, hipStream_t s);
+hipError_t launch_down_mfma(bool f16, const void* act_in, const int32_t* offsets, const int32_t* sorted_pair,
+                            const int32_t* slot_of_expert, int n_slots, const uint8_t* arena, int64_t slot_stride,
+                            int T, int d, int f, int E, int k, int64_t off_q, int64_t off_sb, void* ws,
+                            float** pair_out, hipStream_t s);
+
 // ---- bf16 shared-path GEMV (shared_gemv.hip)
 hipError_t launch_shared_gemv_bf16(const uint16_t* w, const float* h, int T, int rows, int cols,
                                    float* out, hipStream_t s);

@@ -615,4 +615,19 @@ hipError_t launch_down_fp32(DownArgs a, void* ws, hipStream_t s) {
 
 #undef MOE_GPP_SWITCH
 
+hipError_t launch_combine(const float* pair_out, const float* topk_w, const float* residual, float* y, int T,
+                          int d, int k, hipStream_t s) {
+  DownArgs a{};
+  a.pair_out = const_cast<float*>(pair_out);
+  a.topk_w = topk_w;
+  a.residual = residual;
+  a.y = y;
+  a.T = T;
+  a.d = d;
+  a.k = k;
+  const int64_t n4 = (int64_t)T * d / 4;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -94,6 +94,8 @@ def test_validation_before_any_hip_call(api):
     assert g(_p(A), _p(A), _p(A), 0, _p(A), stride, None, None, None, 0, 1, dm, 0, _p(A), _p(A), wsg, None) == api.MOE_ERR_ARG
     assert g(_p(A), _p(A), _p(A), 128, _p(A), stride, _p(A), _p(A), _p(A), 1, 1, dm, 0, _p(A), _p(A), wsg, None) == api.MOE_ERR_UNSUPPORTED
     assert g(_p(A), _p(A), _p(A), 128, _p(A), stride, _p(A), None, None, 1, 1, dm, 0, _p(A), _p(A), wsg, None) == api.MOE_ERR_ARG
+    # the bf16 MFMA path needs the permutation
+    assert g(_p(A), _p(A), _p(A), 128, _p(A), stride, None, None, None, 0, 1, dm, 1, _p(A), _p(A), wsg, None) == api.MOE_ERR_UNSUPPORTED
     dc = lib.moe_expert_q4_down_combine
     wsd = api.moe_workspace_size(api.MOE_CALL_DOWN_COMBINE, 1, dm)
     assert dc(_p(A), _p(A), None, _p(A), 128, _p(A), stride, None, None, None, None, 1, dm, 0, _p(A), _p(A), wsd, None) == api.MOE_ERR_ARG
