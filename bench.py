@@ -1,21 +1,32 @@
 #!/usr/bin/env python3
 """Benchmark of the routed int4 MoE hot path on one MI355X.
 
-Default workload: batch-1 decode through a 30-layer stack of the routed MoE
-layer (d=2816, f=704, 128 experts, top-8, int4 groups of 64 with fp16
-scale/bias), all 3,840 experts resident in HBM slots (12.85 GB), Zipf(1.1)
-expert popularity per layer.  One step = one token through all 30 layers:
-per layer route -> gate/up -> down+combine, then the unit-RMS feedback to the
-next step.  The step is captured once as a HIP graph and replayed.
+Workloads (all over the same routed MoE layer: d=2816, f=704, 128 experts,
+top-8, int4 groups of 64 with fp16 scale/bias, 30 layers, seeded synthetic
+weights and inputs):
+
+  decode   (default) batch-1 decode, all 3,840 experts resident in HBM slots
+           (12.85 GB), Zipf(1.1) expert popularity per layer.  One step = one
+           token through the 30 layers (route -> gate/up -> down+combine per
+           layer, then the unit-RMS feedback), captured once as a HIP graph.
+  batched  32 concurrent decode streams per step: route, permute, grouped
+           gate/up and down GEMV over variable tokens-per-expert.
+  prefill  2048 tokens through the 30 layers: route, permute, grouped int4
+           GEMM on MFMA (gate/up with GELU, then down), gather combine.
+  cache    batch-1 decode with a bounded cache of 64 HBM slots per layer; the
+           full expert pool in pinned host memory; Markov routing (each expert
+           kept with probability 0.8); misses staged on a side stream while a
+           shared-path bf16 GEMV (4d x d) runs on the compute stream.
 
 Prints one JSON line.  `value` is tokens/s; the `roofline` object covers the
-dominant kernel (gate/up dequant-GEMV), timed with HIP events at the kernel's
-own begin/end on its stream; `cpu_baseline` is the CPU oracle on a bounded
-sample of the same workload.
+dominant kernel, timed with HIP events at the kernel's own begin/end on its
+stream; `cpu_baseline` is the CPU oracle on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -31,44 +42,170 @@ import synth  # noqa: E402
 D, F, E, K, NL = synth.D_MODEL, synth.D_FF, synth.N_EXPERTS, synth.TOP_K, synth.N_LAYERS
 METRIC = "routed-MoE tokens/s + achieved HBM GB/s (int4 decode), MFMA util (prefill)"
 HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16
 EPS = 1e-6
+CSRC = os.path.join(ROOT, "int4_routed_expert_route_amd", "csrc")
 
-# HBM bytes per gate/up launch measured with rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE (scaled by a 256 MiB copy's readings), for the kernel source with
-# this fingerprint; reported as null once the source differs.
-GATEUP_TRAFFIC = {"source_sha256_16": "c35bc92e4b26bf04", "fetch_bytes": 18126218, "write_bytes": 22528}
+# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
+# (scaled by a 256 MiB copy's readings), keyed by the workload, for the kernel
+# sources with this fingerprint; reported as null once the sources differ.
+TRAFFIC = {
+    "decode": {"sources": ("q4_gemv.hip", "common.h"), "sha256_16": "c35bc92e4b26bf04",
+               "fetch_bytes": 18126218, "write_bytes": 22528},
+}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes():
-    """Bytes one decode token must read: per layer the router (fp32 E x d), the
-    RMSNorm weight and the 8 selected expert blobs."""
-    blob = 3 * D * F // 2 + 3 * D * F // 64 * 4
-    per_layer = E * D * 4 + D * 4 + K * blob
-    gateup_launch = K * (2 * F * D // 2 + 2 * F * (D // 64) * 4) + D * 4 + K * F * 4
-    down_launch = K * (D * F // 2 + D * (F // 64) * 4) + K * F * 4 + K * 4 + 2 * D * 4
-    return blob, per_layer, gateup_launch, down_launch
+def blob_bytes():
+    return 3 * D * F // 2 + 3 * D * F // 64 * 4
 
+
+def gateup_expert_bytes():
+    return 2 * F * D // 2 + 2 * F * (D // 64) * 4
+
+
+def down_expert_bytes():
+    return D * F // 2 + D * (F // 64) * 4
+
+
+def decode_bytes():
+    """Bytes one decode token must read: per layer the router (fp32 E x d), the
+    RMSNorm weight and the 8 selected expert blobs; and per gate/up / down launch."""
+    per_layer = E * D * 4 + D * 4 + K * blob_bytes()
+    gateup_launch = K * gateup_expert_bytes() + D * 4 + K * F * 4
+    down_launch = K * down_expert_bytes() + K * F * 4 + K * 4 + 2 * D * 4
+    return per_layer, gateup_launch, down_launch
+
+
+def traffic_of(workload):
+    t = TRAFFIC.get(workload)
+    if not t:
+        return None
+    try:
+        src = b"".join(open(os.path.join(CSRC, n), "rb").read() for n in t["sources"])
+    except OSError:
+        return None
+    if hashlib.sha256(src).hexdigest()[:16] != t["sha256_16"]:
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
+
+
+def build_arena(torch, api, seed):
+    """Device arena of NL * E expert blobs; slot e of layer l holds expert e."""
+    dm = api.dims(D, F, E, K)
+    stride = api.moe_expert_blob_bytes(dm)
+    t0 = time.time()
+    arena = torch.empty(NL * E * stride, dtype=torch.uint8, device="cuda")
+    for l in range(NL):
+        blobs = synth.expert_blobs(D, F, seed, l, range(E), threads=16)
+        arena[l * E * stride:(l + 1) * E * stride].copy_(torch.from_numpy(np.concatenate(blobs)))
+    torch.cuda.synchronize()
+    log(f"arena {arena.numel() / 1e9:.2f} GB filled in {time.time() - t0:.1f} s")
+    return arena, stride
+
+
+def time_launch(api, torch, call, launch, n):
+    """Average duration (us) of one call's main kernel over n eager launches
+    (launch(i) enqueues the i-th on the current stream), with events recorded at
+    the kernel's own begin/end."""
+    durs = []
+    for i in range(n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        e1.record()
+        api.moe_profile_next_launch(call, e0, e1)
+        launch(i)
+        e1.synchronize()
+        durs.append(e0.elapsed_time(e1) * 1000.0)
+    durs = np.array(durs[2:] if len(durs) > 4 else durs)
+    return float(np.mean(durs)), float(np.median(durs))
+
+
+def oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(seed, T, budget_s, what, bias_of=None):
+    """The CPU oracle on a bounded sample of the workload: T tokens through the
+    layers in order until ~budget_s of oracle time (at most all 30); expert
+    blob generation is untimed.  Scaled to tokens/s of the 30-layer stack."""
+    import oracle as orc
+    x = synth.tokens(T, D, seed, stream=7 if T > 1 else 0).astype(np.float64)
+    spent, done = 0.0, 0
+    for l in range(NL):
+        blobs = dict(zip(range(E), synth.expert_blobs(D, F, seed, l, range(E), threads=16)))
+        rw = synth.router_weight(D, E, seed, l)
+        nw = synth.norm_weight(D, seed, l)
+        bias = synth.zipf_bias(E, seed, l) if bias_of is None else bias_of(l)
+        t0 = time.perf_counter()
+        x, *_ = orc.moe_layer(x, nw, rw, bias, blobs.__getitem__, D, F, K)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    per_pass = spent / done * NL
+    return {"value": T / per_pass, "unit": "tokens/s", "cores": int(oracle_threads()), "kind": "oracle",
+            "sample": f"{T} token(s) through layers 0-{done - 1} of one {what} step, {spent:.1f} s of oracle time"
+                      + ("" if done == NL else f", scaled x{NL / done:.2f} to the 30-layer stack")}
+
+
+def graph_of(torch, fn):
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        fn()  # eager warm-up on the capture stream
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    return graph
+
+
+def timed(torch, run, steps, warm):
+    log(f"warmup {warm} steps")
+    run(warm)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record()
+    run(steps)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, time.perf_counter() - t_wall
+
+
+def base_record(value, steps, warm, ms, dtype, workload, extra_cfg):
+    cfg = {"workload": workload, "layers": NL}
+    cfg.update(extra_cfg)
+    return {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+            "warmup": warm, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": dtype, "data": "synthetic", "config": cfg}
+
+
+def rounded_steps(n, period):
+    return max(period, (n + period - 1) // period * period)
+
+
+# ----------------------------------------------------------------------------- decode
 
 class DecodeStack:
-    """Device state of the 30-layer decode workload."""
+    """Device state of the 30-layer batch-1 decode workload."""
 
     def __init__(self, api, torch, seed=0, cold=False):
         self.api, self.torch = api, torch
         self.dm = api.dims(D, F, E, K)
-        self.stride = api.moe_expert_blob_bytes(self.dm)
+        self.arena, self.stride = build_arena(torch, api, seed)
         dev = "cuda"
-        t0 = time.time()
-        self.arena = torch.empty(NL * E * self.stride, dtype=torch.uint8, device=dev)
-        for l in range(NL):
-            blobs = synth.expert_blobs(D, F, seed, l, range(E), threads=16)
-            host = torch.from_numpy(np.concatenate(blobs))
-            self.arena[l * E * self.stride:(l + 1) * E * self.stride].copy_(host)
-        torch.cuda.synchronize()
-        log(f"arena {self.arena.numel() / 1e9:.2f} GB filled in {time.time() - t0:.1f} s")
         self.slots = torch.arange(E, dtype=torch.int32, device=dev)
         self.router_w = [torch.from_numpy(synth.router_weight(D, E, seed, l)).to(dev) for l in range(NL)]
         self.norm_w = [torch.from_numpy(synth.norm_weight(D, seed, l)).to(dev) for l in range(NL)]
@@ -93,99 +230,387 @@ class DecodeStack:
         self.idx = torch.zeros(self.period, NL, K, dtype=torch.int32, device=dev)
         self.w = torch.zeros(self.period, NL, K, dtype=torch.float32, device=dev)
         self.act = torch.empty(K, F, dtype=torch.float32, device=dev)
+        self.y_probe = torch.empty(1, D, dtype=torch.float32, device=dev)
         ws = lambda c: torch.zeros(max(api.moe_workspace_size(c, 1, self.dm), 256), dtype=torch.uint8, device=dev)
         self.ws_route, self.ws_gateup, self.ws_down = ws(0), ws(2), ws(3)
 
     def arena_of(self, l):
         return self.arena[l * E * self.stride:(l + 1) * E * self.stride]
 
-    def layer(self, s, l, stream=None):
-        a, dm = self.api, self.dm
-        a.moe_route(self.x[l:l + 1], self.norm_w[l], EPS, self.router_w[l], self.bias[s, l], 1, dm, self.h,
-                    self.idx[s, l:l + 1], self.w[s, l:l + 1], self.ws_route, stream)
+    def route(self, s, l, stream=None):
+        self.api.moe_route(self.x[l:l + 1], self.norm_w[l], EPS, self.router_w[l], self.bias[s, l], 1, self.dm,
+                           self.h, self.idx[s, l:l + 1], self.w[s, l:l + 1], self.ws_route, stream)
+
+    def gateup(self, s, l, stream=None):
+        a = self.api
         a.moe_expert_q4_gateup(self.h, self.idx[s, l:l + 1], self.slots, E, self.arena_of(l), self.stride, None,
-                               None, None, 0, 1, dm, a.MOE_PREC_FP32, self.act, self.ws_gateup, stream)
+                               None, None, 0, 1, self.dm, a.MOE_PREC_FP32, self.act, self.ws_gateup, stream)
+
+    def down(self, s, l, out, stream=None):
+        a = self.api
         a.moe_expert_q4_down_combine(self.act, self.idx[s, l:l + 1], self.w[s, l:l + 1], self.slots, E,
-                                     self.arena_of(l), self.stride, None, None, None, self.x[l:l + 1], 1, dm,
-                                     a.MOE_PREC_FP32, self.x[l + 1:l + 2], self.ws_down, stream)
+                                     self.arena_of(l), self.stride, None, None, None, self.x[l:l + 1], 1,
+                                     self.dm, a.MOE_PREC_FP32, out, self.ws_down, stream)
 
     def steps(self, n_periods=1, stream=None):
         for _ in range(n_periods):
             for s in range(self.period):
                 for l in range(NL):
-                    self.layer(s, l, stream)
+                    self.route(s, l, stream)
+                    self.gateup(s, l, stream)
+                    self.down(s, l, self.x[l + 1:l + 2], stream)
                 self.api.moe_rms_rescale(self.x[NL:NL + 1], 1, D, EPS, self.x[0:1], stream)
 
 
-def time_kernel(api, torch, stack, call, n):
-    """Average duration (us) of one call's main kernel over n eager launches,
-    cycling through layers, with events recorded at the kernel's own begin/end."""
-    durs = []
-    for i in range(n):
-        l = i % NL
-        s = (i // NL) % stack.period
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        e1.record()
-        api.moe_profile_next_launch(call, e0, e1)
-        a, dm = api, stack.dm
-        if call == api.MOE_CALL_ROUTE:
-            a.moe_route(stack.x[l:l + 1], stack.norm_w[l], EPS, stack.router_w[l], stack.bias[s, l], 1, dm, stack.h,
-                        stack.idx[s, l:l + 1], stack.w[s, l:l + 1], stack.ws_route)
-        elif call == api.MOE_CALL_GATEUP:
-            a.moe_expert_q4_gateup(stack.h, stack.idx[s, l:l + 1], stack.slots, E, stack.arena_of(l), stack.stride,
-                                   None, None, None, 0, 1, dm, a.MOE_PREC_FP32, stack.act, stack.ws_gateup)
-        else:
-            out = torch.empty(1, D, device="cuda")
-            a.moe_expert_q4_down_combine(stack.act, stack.idx[s, l:l + 1], stack.w[s, l:l + 1], stack.slots, E,
-                                         stack.arena_of(l), stack.stride, None, None, None, stack.x[l:l + 1], 1,
-                                         dm, a.MOE_PREC_FP32, out, stack.ws_down)
-        e1.synchronize()
-        durs.append(e0.elapsed_time(e1) * 1000.0)
-    durs = np.array(durs[2:] if len(durs) > 4 else durs)
-    return float(np.mean(durs)), float(np.median(durs))
+def run_decode(args, api, torch):
+    stack = DecodeStack(api, torch, args.seed, cold=args.control == "cold")
+    period = stack.period
+    steps, warm = rounded_steps(args.steps, period), rounded_steps(args.warmup, period)
+    if args.no_graph:
+        run = lambda n: stack.steps(n // period)
+    else:
+        # one replay = one routing period (1 step for Zipf, 16 for the cold arm)
+        graph = graph_of(torch, lambda: stack.steps(1))
+        run = lambda n: [graph.replay() for _ in range(n // period)]
+    ms, t_wall = timed(torch, run, steps, warm)
+    tok_s = 1000.0 / ms
+    per_layer, gu_bytes, _ = decode_bytes()
+    step_bytes = NL * per_layer
+    log(f"{steps} steps: {ms * 1000:.1f} us/step, {tok_s:.1f} tok/s, {step_bytes * tok_s / 1e9:.0f} GB/s algorithmic")
+
+    # the step's kernels one at a time, each at its own begin/end; layer and
+    # routing-period index cycle so every layer's weights are used
+    sl = lambda i: ((i // NL) % period, i % NL)
+    n = args.kernel_samples
+    rt_us, _ = time_launch(api, torch, api.MOE_CALL_ROUTE, lambda i: stack.route(*sl(i)), n)
+    gu_us, gu_med = time_launch(api, torch, api.MOE_CALL_GATEUP, lambda i: stack.gateup(*sl(i)), n)
+    dn_us, _ = time_launch(api, torch, api.MOE_CALL_DOWN_COMBINE, lambda i: stack.down(*sl(i), stack.y_probe), n)
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    log(f"kernels (eager, mean us): route {rt_us:.2f}  gate/up {gu_us:.2f} (median {gu_med:.2f})  down {dn_us:.2f}")
+
+    out = base_record(tok_s, steps, warm, ms, "fp32",
+                      "batch-1 decode, 30 routed MoE layers x 128 experts (d=2816, f=704, top-8, int4 groups of "
+                      "64, fp16 scale/bias), all experts resident in HBM, "
+                      + ("Zipf(1.1) routing" if not stack.cold else
+                         "cold routing control (no expert reuse within 16 steps)"),
+                      {"tokens_per_step": 1, "graph": not args.no_graph})
+    out.update({
+        "algorithmic_bytes_per_token": step_bytes,
+        "algorithmic_GBps": round(step_bytes * tok_s / 1e9, 1),
+        "hbm_frac_step": round(step_bytes * tok_s / 1e9 / HBM_PEAK_GBPS, 4),
+        "kernel_us": {"route": round(rt_us, 3), "gateup": round(gu_us, 3), "down_combine": round(dn_us, 3)},
+        "roofline": {
+            "kernel": "k_gateup (int4 gate/up dequant-GEMV, 8 experts, fp32 accumulate)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_of("decode"),
+            "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 3),
+        },
+        "wall_s_timed": round(t_wall, 3),
+    })
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(args.seed, 1, 20.0, "batch-1 decode (Zipf routing)")
+    return out
 
 
-def cpu_baseline(seed, budget_s=20.0):
-    """The CPU oracle on a bounded sample of the same workload: the layers of
-    one batch-1 decode step, in order, until ~budget_s of oracle time (at most
-    all 30); expert blob generation is untimed.  Scaled to tokens/s of the
-    30-layer stack."""
-    import oracle as orc
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    x = synth.tokens(1, D, seed).astype(np.float64)
-    spent, done = 0.0, 0
+# ----------------------------------------------------------------------------- batched / prefill
+
+class BatchStack:
+    """T tokens per step through the 30 layers, experts grouped by moe_permute.
+    prec FP32: grouped dequant-GEMV (batched decode); F16/BF16 MFMA: grouped
+    GEMM (prefill).  decode=True feeds the last layer's output back (unit-RMS
+    rescale) as the next step's input; otherwise every step re-reads the same
+    input tokens."""
+
+    def __init__(self, api, torch, seed, T, prec, decode):
+        self.api, self.torch, self.T, self.prec, self.decode = api, torch, T, prec, decode
+        self.dm = api.dims(D, F, E, K)
+        self.arena, self.stride = build_arena(torch, api, seed)
+        dev = "cuda"
+        self.slots = torch.arange(E, dtype=torch.int32, device=dev)
+        self.router_w = [torch.from_numpy(synth.router_weight(D, E, seed, l)).to(dev) for l in range(NL)]
+        self.norm_w = [torch.from_numpy(synth.norm_weight(D, seed, l)).to(dev) for l in range(NL)]
+        self.bias = torch.from_numpy(np.stack([synth.zipf_bias(E, seed, l) for l in range(NL)])).to(dev)
+        self.x = torch.zeros(NL + 1, T, D, dtype=torch.float32, device=dev)  # layer l: x[l] -> x[l + 1]
+        self.x[0].copy_(torch.from_numpy(synth.tokens(T, D, seed, stream=7)))
+        self.h = torch.empty(T, D, dtype=torch.float32, device=dev)
+        self.idx = torch.zeros(NL, T, K, dtype=torch.int32, device=dev)
+        self.w = torch.zeros(NL, T, K, dtype=torch.float32, device=dev)
+        self.counts = torch.zeros(NL, E, dtype=torch.int32, device=dev)
+        # rows padded to 16 bytes: every device pointer the library takes is 16-byte aligned
+        self.offsets = torch.zeros(NL, (E + 1 + 3) // 4 * 4, dtype=torch.int32, device=dev)[:, :E + 1]
+        self.sp = torch.zeros(NL, T * K, dtype=torch.int32, device=dev)
+        self.pp = torch.zeros(NL, T * K, dtype=torch.int32, device=dev)
+        self.act = torch.zeros(api.moe_act_bytes(T, self.dm, prec), dtype=torch.uint8, device=dev)
+        self.y_probe = torch.empty(T, D, dtype=torch.float32, device=dev)
+        ws = lambda c: torch.zeros(max(api.moe_workspace_size(c, T, self.dm, prec if c >= 2 else 0), 256),
+                                   dtype=torch.uint8, device=dev)
+        self.ws_route, self.ws_gateup, self.ws_down = ws(0), ws(2), ws(3)
+
+    def arena_of(self, l):
+        return self.arena[l * E * self.stride:(l + 1) * E * self.stride]
+
+    def route(self, l, stream=None):
+        a = self.api
+        a.moe_route(self.x[l], self.norm_w[l], EPS, self.router_w[l], self.bias[l], self.T, self.dm, self.h,
+                    self.idx[l], self.w[l], self.ws_route, stream)
+        a.moe_permute(self.idx[l], self.T, self.dm, self.counts[l], self.offsets[l], self.sp[l], self.pp[l],
+                      None, stream)
+
+    def gateup(self, l, stream=None):
+        self.api.moe_expert_q4_gateup(self.h, self.idx[l], self.slots, E, self.arena_of(l), self.stride,
+                                      self.offsets[l], self.sp[l], None, 0, self.T, self.dm, self.prec, self.act,
+                                      self.ws_gateup, stream)
+
+    def down(self, l, out, stream=None):
+        self.api.moe_expert_q4_down_combine(self.act, self.idx[l], self.w[l], self.slots, E, self.arena_of(l),
+                                            self.stride, self.offsets[l], self.sp[l], self.pp[l], self.x[l],
+                                            self.T, self.dm, self.prec, out, self.ws_down, stream)
+
+    def step(self, stream=None):
+        for l in range(NL):
+            self.route(l, stream)
+            self.gateup(l, stream)
+            self.down(l, self.x[l + 1], stream)
+        if self.decode:
+            self.api.moe_rms_rescale(self.x[NL], self.T, D, EPS, self.x[0], stream)
+
+
+def distinct_experts(torch, stack):
+    """Per layer, the number of experts with at least one routed token."""
+    torch.cuda.synchronize()
+    return (stack.counts > 0).sum(dim=1).cpu().numpy()
+
+
+def run_batched(args, api, torch):
+    T = args.tokens or 32
+    stack = BatchStack(api, torch, args.seed, T, api.MOE_PREC_FP32, decode=True)
+    graph = None if args.no_graph else graph_of(torch, stack.step)
+    run = (lambda n: [stack.step() for _ in range(n)]) if graph is None else \
+        (lambda n: [graph.replay() for _ in range(n)])
+    ms, t_wall = timed(torch, run, args.steps, args.warmup)
+    tok_s = T * 1000.0 / ms
+    nd = distinct_experts(torch, stack)  # routing of the last step
+    per_layer = E * D * 4 + D * 4 + nd * blob_bytes()
+    step_bytes = int(per_layer.sum())
+    log(f"{args.steps} steps: {ms * 1000:.1f} us/step, {tok_s:.1f} tok/s, distinct experts/layer "
+        f"{nd.mean():.1f}, {step_bytes / ms / 1e6:.0f} GB/s algorithmic")
+    n = args.kernel_samples
+    rt_us, _ = time_launch(api, torch, api.MOE_CALL_ROUTE, lambda i: stack.route(i % NL), n)
+    pm_us, _ = time_launch(api, torch, api.MOE_CALL_PERMUTE, lambda i: stack.route(i % NL), n)
+    gu_us, gu_med = time_launch(api, torch, api.MOE_CALL_GATEUP, lambda i: stack.gateup(i % NL), n)
+    dn_us, _ = time_launch(api, torch, api.MOE_CALL_DOWN_COMBINE, lambda i: stack.down(i % NL, stack.y_probe), n)
+    # the sampled gate/up launches cycle over the layers: average their bytes
+    layers = [i % NL for i in range(n)]
+    layers = layers[2:] if n > 4 else layers
+    gu_bytes = float(np.mean([nd[l] * gateup_expert_bytes() + T * D * 4 + T * K * F * 4 for l in layers]))
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    log(f"kernels (eager, mean us): route {rt_us:.2f}  permute {pm_us:.2f}  gate/up {gu_us:.2f}  down {dn_us:.2f}")
+    out = base_record(tok_s, args.steps, args.warmup, ms, "fp32",
+                      f"batched decode, {T} concurrent tokens per step, 30 routed MoE layers x 128 experts "
+                      "(d=2816, f=704, top-8, int4 groups of 64), all experts resident in HBM, Zipf(1.1) routing "
+                      "independent per token", {"tokens_per_step": T, "graph": graph is not None})
+    out.update({
+        "distinct_experts_per_layer": round(float(nd.mean()), 2),
+        "algorithmic_bytes_per_step": step_bytes,
+        "algorithmic_GBps": round(step_bytes / ms / 1e6, 1),
+        "hbm_frac_step": round(step_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
+        "kernel_us": {"route": round(rt_us, 3), "permute": round(pm_us, 3), "gateup": round(gu_us, 3),
+                      "down_combine": round(dn_us, 3)},
+        "roofline": {
+            "kernel": "k_gateup grouped (int4 gate/up dequant-GEMV over experts' token groups)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_of("batched"),
+            "algorithmic_bytes_per_launch": int(gu_bytes), "avg_launch_us": round(gu_us, 3),
+        },
+        "wall_s_timed": round(t_wall, 3),
+    })
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(args.seed, T, 20.0, f"{T}-token batched decode")
+    return out
+
+
+def run_prefill(args, api, torch):
+    T = args.tokens or 2048
+    prec = api.MOE_PREC_BF16_MFMA if args.operands == "bf16" else api.MOE_PREC_F16_MFMA
+    stack = BatchStack(api, torch, args.seed, T, prec, decode=False)
+    graph = None if args.no_graph else graph_of(torch, stack.step)
+    run = (lambda n: [stack.step() for _ in range(n)]) if graph is None else \
+        (lambda n: [graph.replay() for _ in range(n)])
+    ms, t_wall = timed(torch, run, args.steps, args.warmup)
+    tok_s = T * 1000.0 / ms
+    flop_gu = 2.0 * T * K * (2 * F) * D
+    flop_dn = 2.0 * T * K * D * F
+    step_flop = NL * (flop_gu + flop_dn)
+    step_tflops = step_flop / (ms * 1e-3) / 1e12
+    log(f"{args.steps} steps: {ms:.3f} ms/step, {tok_s:.0f} tok/s, expert GEMMs {step_tflops:.0f} TFLOP/s "
+        f"over the step ({step_tflops / MFMA_PEAK_TFLOPS:.1%} of peak)")
+    torch.cuda.synchronize()
+    cnt = stack.counts.cpu().numpy()
+    n = args.kernel_samples
+    rt_us, _ = time_launch(api, torch, api.MOE_CALL_ROUTE, lambda i: stack.route(i % NL), n)
+    pm_us, _ = time_launch(api, torch, api.MOE_CALL_PERMUTE, lambda i: stack.route(i % NL), n)
+    gu_us, gu_med = time_launch(api, torch, api.MOE_CALL_GATEUP, lambda i: stack.gateup(i % NL), n)
+    dn_us, _ = time_launch(api, torch, api.MOE_CALL_DOWN_COMBINE, lambda i: stack.down(i % NL, stack.y_probe), n)
+    achieved = flop_gu / (gu_us * 1e-6) / 1e12
+    dn_tflops = flop_dn / (dn_us * 1e-6) / 1e12
+    log(f"kernels (eager, mean us): route {rt_us:.1f}  permute {pm_us:.1f}  gate/up GEMM {gu_us:.1f} "
+        f"({achieved:.0f} TFLOP/s)  down GEMM {dn_us:.1f} ({dn_tflops:.0f} TFLOP/s)")
+    out = base_record(tok_s, args.steps, args.warmup, ms, "fp16" if args.operands == "f16" else "bf16",
+                      f"prefill, {T} tokens x 30 routed MoE layers x 128 experts (d=2816, f=704, top-8, int4 "
+                      "groups of 64), Zipf(1.1) routing, expert-grouped int4 GEMM on MFMA "
+                      f"({args.operands} operands, fp32 accumulate)",
+                      {"tokens_per_step": T, "graph": graph is not None})
+    out.update({
+        "tokens_per_expert": {"max": int(cnt.max()), "median": float(np.median(cnt)), "mean": float(cnt.mean())},
+        "algorithmic_flop_per_step": step_flop,
+        "mfma_frac_step": round(step_tflops / MFMA_PEAK_TFLOPS, 4),
+        "kernel_us": {"route": round(rt_us, 2), "permute": round(pm_us, 2), "gateup_gemm": round(gu_us, 2),
+                      "down_gemm": round(dn_us, 2)},
+        "roofline": {
+            "kernel": f"k_grouped_mfma gate/up ({args.operands} MFMA 16x16x32, int4 tiles dequantised in LDS)",
+            "bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": traffic_of("prefill"),
+            "algorithmic_flop_per_launch": flop_gu, "avg_launch_us": round(gu_us, 2),
+        },
+        "wall_s_timed": round(t_wall, 3),
+    })
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(args.seed, 256, 20.0, "prefill")
+    return out
+
+
+# ----------------------------------------------------------------------------- bounded cache
+
+def run_cache(args, api, torch):
+    n_slots = args.slots
+    dm = api.dims(D, F, E, K)
+    stride = api.moe_expert_blob_bytes(dm)
+    blob = blob_bytes()
+    dev = "cuda"
+    total_steps = args.warmup + args.steps
+    t0 = time.time()
+    pool = torch.empty(NL * E * blob, dtype=torch.uint8, pin_memory=True)
     for l in range(NL):
-        blobs = dict(zip(range(E), synth.expert_blobs(D, F, seed, l, range(E), threads=16)))
-        rw = synth.router_weight(D, E, seed, l)
-        nw = synth.norm_weight(D, seed, l)
-        bias = synth.zipf_bias(E, seed, l)
-        t0 = time.perf_counter()
-        x, *_ = orc.moe_layer(x, nw, rw, bias, blobs.__getitem__, D, F, K)
-        spent += time.perf_counter() - t0
-        done += 1
-        if spent >= budget_s:
-            break
-    per_token = spent / done * NL
-    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"layers 0-{done - 1} of one batch-1 decode step (Zipf routing), {spent:.1f} s of oracle "
-                      f"time" + ("" if done == NL else f", scaled x{NL / done:.2f} to the 30-layer token")}
+        pool[l * E * blob:(l + 1) * E * blob].copy_(
+            torch.from_numpy(np.concatenate(synth.expert_blobs(D, F, args.seed, l, range(E), threads=16))))
+    log(f"pinned host pool {pool.numel() / 1e9:.2f} GB filled in {time.time() - t0:.1f} s")
+    arena = torch.zeros(NL * n_slots * stride, dtype=torch.uint8, device=dev)
+    tables = torch.full((NL, E), -1, dtype=torch.int32, device=dev)
+    cache = api.MoeCache(NL, E, n_slots, K, pool, blob, arena, stride, tables)
+    sel = np.stack([synth.markov_selections(E, K, total_steps, args.seed, l) for l in range(NL)], axis=1)
+    bias = torch.from_numpy(synth.selection_bias(sel, E)).to(dev)  # [steps, NL, E]
+    router_w = [torch.from_numpy(synth.router_weight(D, E, args.seed, l)).to(dev) for l in range(NL)]
+    norm_w = [torch.from_numpy(synth.norm_weight(D, args.seed, l)).to(dev) for l in range(NL)]
+    w_sh = torch.from_numpy(synth.shared_weight_bf16(4 * D, D, args.seed, 0).view(np.int16)).to(dev)
+    w_sh_layers = w_sh.unsqueeze(0).repeat(NL, 1, 1)  # one HBM copy per layer: no cache reuse across layers
+    del w_sh
+    s_out = torch.empty(1, 4 * D, dtype=torch.float32, device=dev)
+    x = torch.zeros(NL + 1, 1, D, dtype=torch.float32, device=dev)
+    x[0].copy_(torch.from_numpy(synth.tokens(1, D, args.seed)))
+    h = torch.empty(1, D, dtype=torch.float32, device=dev)
+    idx = torch.zeros(NL, 1, K, dtype=torch.int32, device=dev)
+    wts = torch.zeros(NL, 1, K, dtype=torch.float32, device=dev)
+    idx_host = torch.zeros(NL, K, dtype=torch.int32, pin_memory=True)
+    hit_dev = torch.zeros(NL, 16, dtype=torch.uint8, device=dev)[:, :K]  # 16-byte aligned rows
+    act = torch.zeros(K, F, dtype=torch.float32, device=dev)
+    ws = lambda c: torch.zeros(max(api.moe_workspace_size(c, 1, dm), 256), dtype=torch.uint8, device=dev)
+    ws_route, ws_gu, ws_dn = ws(0), ws(2), ws(3)
+    compute = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    routed_ok = [0, 0]
+
+    def step(t):
+        stats = None
+        for l in range(NL):
+            a_l = arena[l * n_slots * stride:(l + 1) * n_slots * stride]
+            table = tables[l]
+            api.moe_route(x[l], norm_w[l], EPS, router_w[l], bias[t, l], 1, dm, h, idx[l], wts[l], ws_route)
+            idx_host[l].copy_(idx[l, 0], non_blocking=True)
+            compute.synchronize()
+            routed_ok[0] += int(np.array_equal(np.sort(idx_host[l].numpy()), sel[t, l]))
+            routed_ok[1] += 1
+            stats = api.moe_slot_stage(cache, l, t, idx_host[l], side, compute, hit_dev[l])
+            # hits first: their slots are already resident
+            api.moe_expert_q4_gateup(h, idx[l], table, n_slots, a_l, stride, None, None, hit_dev[l], 1, 1, dm,
+                                     api.MOE_PREC_FP32, act, ws_gu)
+            # shared-path work on the compute stream while misses land
+            api.moe_shared_gemv_bf16(w_sh_layers[l], h, 1, 4 * D, D, s_out)
+            api.moe_cache_wait(cache, l, compute)
+            api.moe_expert_q4_gateup(h, idx[l], table, n_slots, a_l, stride, None, None, hit_dev[l], 0, 1, dm,
+                                     api.MOE_PREC_FP32, act, ws_gu)
+            api.moe_expert_q4_down_combine(act, idx[l], wts[l], table, n_slots, a_l, stride, None, None, None,
+                                           x[l], 1, dm, api.MOE_PREC_FP32, x[l + 1], ws_dn)
+        api.moe_rms_rescale(x[NL], 1, D, EPS, x[0])
+        return stats
+
+    log(f"warmup {args.warmup} steps (cold cache included in the hit statistics)")
+    st0 = None
+    for t in range(args.warmup):
+        st0 = step(t)
+    torch.cuda.synchronize()
+    h0, m0, b0 = (st0.hits, st0.misses, st0.bytes_staged) if st0 is not None else (0, 0, 0)
+    t_wall = time.perf_counter()
+    st = None
+    for t in range(args.warmup, total_steps):
+        st = step(t)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = t_wall * 1000.0 / args.steps
+    tok_s = 1000.0 / ms
+    hits, misses, staged = st.hits, st.misses, st.bytes_staged
+    th, tm, tb = hits - h0, misses - m0, staged - b0
+    log(f"{args.steps} steps: {ms:.3f} ms/step, {tok_s:.1f} tok/s; hit rate {hits / (hits + misses):.4f} "
+        f"(timed {th / max(1, th + tm):.4f}); {tb / args.steps / 1e6:.1f} MB staged per token")
+    out = base_record(tok_s, args.steps, args.warmup, ms, "fp32",
+                      f"batch-1 decode with a bounded expert cache: {n_slots} HBM slots per layer of 128 experts, "
+                      "expert pool in pinned host memory, misses staged on a side stream, Markov routing "
+                      "(keep 0.8, Zipf refill), bf16 shared-path GEMV (4d x d) overlapped on the compute stream",
+                      {"tokens_per_step": 1, "slots_per_layer": n_slots, "graph": False})
+    out.update({
+        "hit_rate": round(hits / max(1, hits + misses), 5),
+        "hit_rate_timed": round(th / max(1, th + tm), 5),
+        "staged_bytes_per_token": round(tb / args.steps, 1),
+        "staged_GBps": round(tb / t_wall / 1e9, 2),
+        "routing_matches_selection": routed_ok[0] == routed_ok[1],
+        "wall_s_timed": round(t_wall, 3),
+    })
+    cache.close()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(args.seed, 1, 20.0, "batch-1 decode (Markov routing)",
+                                           bias_of=lambda l: synth.selection_bias(sel[0, l], E))
+    return out
+
+
+def run_copy_calibration(mib):
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}))
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
-    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--workload", choices=["decode", "batched", "prefill", "cache"], default="decode")
     ap.add_argument("--control", choices=["zipf", "cold"], default="zipf",
-                    help="zipf: the Zipf(1.1) routing workload; cold: routing that never reuses an expert "
-                         "within 16 steps (defeats the last-level cache)")
+                    help="decode: zipf = the Zipf(1.1) routing workload; cold = routing that never reuses an "
+                         "expert within 16 steps (defeats the last-level cache)")
+    ap.add_argument("--tokens", type=int, default=0, help="batched / prefill: tokens per step (32 / 2048)")
+    ap.add_argument("--operands", choices=["f16", "bf16"], default="f16", help="prefill: MFMA operand type")
+    ap.add_argument("--slots", type=int, default=64, help="cache: HBM slots per layer")
     ap.add_argument("--kernel-samples", type=int, default=62)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
@@ -193,122 +618,24 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB (for scaling HBM counters)")
     args = ap.parse_args()
     if args.copy_calibration:
-        import torch
-        n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}))
+        run_copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the routed MoE hot path is built and "
                                    "measured on a single MI355X (multi-GPU expert parallelism is design-only)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    defaults = {"decode": (256, 16), "batched": (64, 4), "prefill": (10, 2), "cache": (448, 64)}
+    ds, dw = defaults[args.workload]
+    args.steps = ds if args.steps is None else args.steps
+    args.warmup = dw if args.warmup is None else args.warmup
 
     import torch
     import int4_routed_expert_route_amd.api as api
     api.lib()
     torch.cuda.set_device(0)
-    stack = DecodeStack(api, torch, args.seed, cold=args.control == "cold")
-    period = stack.period
-    steps = max(period, (args.steps + period - 1) // period * period)
-    warm = max(period, (args.warmup + period - 1) // period * period)
-
-    stream = torch.cuda.Stream()
-    torch.cuda.synchronize()
-    if args.no_graph:
-        run = lambda n: stack.steps(n // period)
-    else:
-        # one replay = one routing period (1 step for Zipf, 16 for the cold arm)
-        with torch.cuda.stream(stream):
-            stack.steps(1)  # eager warm-up on the capture stream
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            stack.steps(1)
-        torch.cuda.synchronize()
-        run = lambda n: [graph.replay() for _ in range(n // period)]
-    log(f"warmup {warm} steps")
-    run(warm)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    e0.record()
-    run(steps)
-    e1.record()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / steps
-    tok_s = 1000.0 / ms
-    blob, per_layer, gu_bytes, down_bytes = algorithmic_bytes()
-    step_bytes = NL * per_layer
-    log(f"{steps} steps: {ms * 1000:.1f} us/step, {tok_s:.1f} tok/s, {step_bytes * tok_s / 1e9:.0f} GB/s algorithmic")
-
-    # dominant kernel: gate/up dequant-GEMV, timed at its own begin/end
-    gu_us, gu_med = time_kernel(api, torch, stack, api.MOE_CALL_GATEUP, args.kernel_samples)
-    dn_us, _ = time_kernel(api, torch, stack, api.MOE_CALL_DOWN_COMBINE, args.kernel_samples)
-    rt_us, _ = time_kernel(api, torch, stack, api.MOE_CALL_ROUTE, args.kernel_samples)
-    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
-    traffic = None
-    try:
-        import hashlib
-        src = b"".join(open(os.path.join(ROOT, "int4_routed_expert_route_amd", "csrc", n), "rb").read()
-                       for n in ("q4_gemv.hip", "common.h"))
-        if hashlib.sha256(src).hexdigest()[:16] == GATEUP_TRAFFIC["source_sha256_16"]:
-            traffic = GATEUP_TRAFFIC["fetch_bytes"] + GATEUP_TRAFFIC["write_bytes"]
-    except OSError:
-        pass
-    log(f"kernels (eager, mean us): route {rt_us:.2f}  gate/up {gu_us:.2f} (median {gu_med:.2f})  down {dn_us:.2f}")
-
-    out = {
-        "metric": METRIC,
-        "value": round(tok_s, 2),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": warm,
-        "ms_per_step": round(ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp32",
-        "data": "synthetic",
-        "config": {
-            "workload": "batch-1 decode, 30 routed MoE layers x 128 experts (d=2816, f=704, top-8, int4 "
-                        "groups of 64, fp16 scale/bias), all experts resident in HBM, "
-                        + ("Zipf(1.1) routing" if not stack.cold else "cold routing control (no expert reuse "
-                                                                           "within 16 steps)"),
-            "tokens_per_step": 1,
-            "layers": NL,
-            "graph": not args.no_graph,
-        },
-        "algorithmic_bytes_per_token": step_bytes,
-        "algorithmic_GBps": round(step_bytes * tok_s / 1e9, 1),
-        "hbm_frac_step": round(step_bytes * tok_s / 1e9 / HBM_PEAK_GBPS, 4),
-        "kernel_us": {"route": round(rt_us, 3), "gateup": round(gu_us, 3), "down_combine": round(dn_us, 3)},
-        "roofline": {
-            "kernel": "k_gateup_fp32 (int4 gate/up dequant-GEMV, 8 experts)",
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "algorithmic_bytes_per_launch": gu_bytes,
-            "avg_launch_us": round(gu_us, 3),
-        },
-        "wall_s_timed": round(t_wall, 3),
-    }
-    if not args.no_cpu_baseline:
-        log("cpu baseline (oracle) on a bounded sample ...")
-        out["cpu_baseline"] = cpu_baseline(args.seed)
-    print(json.dumps(out), flush=True)
+    run = {"decode": run_decode, "batched": run_batched, "prefill": run_prefill, "cache": run_cache}[args.workload]
+    print(json.dumps(run(args, api, torch)), flush=True)
 
 
 if __name__ == "__main__":

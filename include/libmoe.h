@@ -90,10 +90,11 @@ typedef struct moe_dims {
 
 typedef enum moe_precision {
   MOE_PREC_FP32 = 0,      /* int4 weights, activations kept to ~fp32 accuracy, fp32 accumulate (decode) */
-  MOE_PREC_BF16_MFMA = 1, /* int4 -> bf16 tiles in LDS, bf16 activations, bf16 MFMA, fp32 accumulate */
-  MOE_PREC_F16_MFMA = 2   /* int4 -> fp16 tiles in LDS, fp16 activations, fp16 MFMA, fp32 accumulate:
-                             the same MFMA rate with 3 more mantissa bits; activations must stay
-                             below 65504 in magnitude */
+  MOE_PREC_BF16_MFMA = 1, /* grouped GEMM: int4 -> bf16 weights, bf16 activations, bf16 MFMA, fp32
+                             accumulate (batched prefill) */
+  MOE_PREC_F16_MFMA = 2   /* grouped GEMM: int4 -> fp16 weights, fp16 activations, fp16 MFMA, fp32
+                             accumulate: the same MFMA rate as bf16 with 3 more significand bits;
+                             intermediate values are block-scaled, so fp16's range does not bind */
 } moe_precision;
 
 typedef enum moe_call {
@@ -117,6 +118,22 @@ moe_status moe_expert_blob_offsets(moe_dims dims, int64_t offsets[6]);
 /* Workspace bytes a call needs for T tokens (0 when it needs none; SIZE_MAX
  * for invalid dims). */
 size_t moe_workspace_size(moe_call call, int32_t T, moe_dims dims, moe_precision prec);
+
+/* Bytes of the act buffer that moe_expert_q4_gateup writes and
+ * moe_expert_q4_down_combine reads, for T tokens at precision prec:
+ *   MOE_PREC_FP32       fp32 [T*k][f].
+ *   MOE_PREC_*_MFMA     block-scaled: 16-bit values (bf16 or fp16) [T*k][f],
+ *                       then int8 exponents [T*k][f/64] at byte offset
+ *                       T*k*f*2.  Inside each block of 8 columns the values
+ *                       are stored in the order 0,4,1,5,2,6,3,7 (the order the
+ *                       matrix cores consume them): element (p, 8b + j) is
+ *                       value[p][8b + pos(j)] * 2^exp[p][(8b + j) / 64] with
+ *                       pos(j) = 2*(j%4) + j/4.  fp16 exponents are shared by
+ *                       the pairs an expert processes together and put the
+ *                       group's largest magnitude in [2^14, 2^15); bf16
+ *                       exponents are 0.
+ * SIZE_MAX for invalid dims. */
+size_t moe_act_bytes(int32_t T, moe_dims dims, moe_precision prec);
 
 /* ---------------------------------------------------------------------------
  * moe_route — RMSNorm, router matvec, softmax, top-k, renormalisation.
@@ -181,8 +198,10 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t T, moe_dims dims,
  *                  parallel work, reuse, and coarse overlap").  Only with
  *                  offsets == NULL.
  *   prec           MOE_PREC_FP32: act is fp32 [T*k][f];
- *                  MOE_PREC_BF16_MFMA / MOE_PREC_F16_MFMA: act is bf16 / fp16
- *                  [T*k][f]; grouped GEMM on MFMA (needs offsets, T*k <= 65536).
+ *                  MOE_PREC_BF16_MFMA / MOE_PREC_F16_MFMA: grouped GEMM on MFMA
+ *                  (needs offsets, T*k <= 2^22); act is block-scaled 16-bit
+ *                  (layout and size: moe_act_bytes).
+ *   act            device, moe_act_bytes(T, dims, prec) bytes
  * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_CAPACITY, MOE_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------- */
 moe_status moe_expert_q4_gateup(const float* h, const int32_t* topk_idx,
@@ -197,7 +216,7 @@ moe_status moe_expert_q4_gateup(const float* h, const int32_t* topk_idx,
  * moe_expert_q4_down_combine — out[p] = W_down[e] act[p], then
  * y[t] = residual[t] + sum_j topk_w[t][j] * out[t*k+j], summed in rank order
  * (deterministic).  Same slot-table, offsets and precision rules as gateup.
- *   act       device fp32, bf16 or fp16 [T*k][f]  from moe_expert_q4_gateup (per prec)
+ *   act       device, from moe_expert_q4_gateup at the same prec (layout: moe_act_bytes)
  *   topk_w    device fp32 [T][k]
  *   pair_pos  device int32 [T*k] from moe_permute, or NULL with offsets NULL
  *   residual  device fp32 [T][d] or NULL (then y is the expert mix alone);

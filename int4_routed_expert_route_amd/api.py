@@ -52,6 +52,7 @@ _SIGNATURES = {
     "moe_expert_blob_bytes": (_I64, [moe_dims]),
     "moe_expert_blob_offsets": (ctypes.c_int, [moe_dims, ctypes.POINTER(_I64)]),
     "moe_workspace_size": (_SZ, [ctypes.c_int, _I32, moe_dims, ctypes.c_int]),
+    "moe_act_bytes": (_SZ, [_I32, moe_dims, ctypes.c_int]),
     "moe_route": (ctypes.c_int, [_P, _P, _F, _P, _P, _I32, moe_dims, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute": (ctypes.c_int, [_P, _I32, moe_dims, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_expert_q4_gateup": (ctypes.c_int, [_P, _P, _P, _I32, _P, _I64, _P, _P, _P, _I32, _I32, moe_dims,
@@ -140,6 +141,10 @@ def moe_expert_blob_offsets(dm: moe_dims) -> list:
 
 def moe_workspace_size(call: int, T: int, dm: moe_dims, prec: int = MOE_PREC_FP32) -> int:
     return int(lib().moe_workspace_size(call, T, dm, prec))
+
+
+def moe_act_bytes(T: int, dm: moe_dims, prec: int) -> int:
+    return int(lib().moe_act_bytes(T, dm, prec))
 
 
 # ------------------------------------------------------------------ compute calls

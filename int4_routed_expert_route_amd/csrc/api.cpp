@@ -12,6 +12,14 @@
 
 namespace {
 
+constexpr int kMaxMfmaPairs = 1 << 22;  // T*k bound of the MFMA path (int32 work lists)
+
+// The MFMA kernels address h, act and one slot with 32-bit buffer offsets.
+bool mfma_fits_32bit(int32_t T, const moe_dims& d, int64_t slot_stride) {
+  const int64_t lim = INT32_MAX;
+  return (int64_t)T * d.d * 2 < lim && (int64_t)T * d.top_k * d.f * 2 < lim && slot_stride < lim;
+}
+
 thread_local std::string g_last_error;
 
 moe_status fail(moe_status s, const char* fmt, ...) {
@@ -121,6 +129,16 @@ moe_status moe_expert_blob_offsets(moe_dims dims, int64_t offsets[6]) {
   return MOE_OK;
 }
 
+size_t moe_act_bytes(int32_t T, moe_dims dims, moe_precision prec) {
+  if (T < 1 || check_dims(dims) != MOE_OK) return SIZE_MAX;
+  switch (prec) {
+    case MOE_PREC_FP32: return (size_t)T * dims.top_k * dims.f * 4;
+    case MOE_PREC_BF16_MFMA:
+    case MOE_PREC_F16_MFMA: return moe::mfma_act_bytes(T, dims.f, dims.top_k);
+  }
+  return SIZE_MAX;
+}
+
 size_t moe_workspace_size(moe_call call, int32_t T, moe_dims dims, moe_precision prec) {
   if (T < 1 || check_dims(dims) != MOE_OK) return SIZE_MAX;
   switch (call) {
@@ -204,13 +222,16 @@ moe_status moe_expert_q4_gateup(const float* h, const int32_t* topk_idx, const i
   if (prec == MOE_PREC_BF16_MFMA || prec == MOE_PREC_F16_MFMA) {
     if (!grouped)
       return fail(MOE_ERR_UNSUPPORTED, "%s: the MFMA path needs offsets and sorted_pair (moe_permute)", fn);
-    if ((int64_t)T * dims.top_k > 65536) return fail(MOE_ERR_ARG, "%s: T*k must be <= 65536", fn);
+    if ((int64_t)T * dims.top_k > kMaxMfmaPairs)
+      return fail(MOE_ERR_ARG, "%s: T*k must be <= %d on the MFMA path", fn, kMaxMfmaPairs);
+    if (!mfma_fits_32bit(T, dims, slot_stride))
+      return fail(MOE_ERR_ARG, "%s: h, act and a slot must each stay below 2 GiB on the MFMA path", fn);
     const size_t need = moe::mfma_workspace_bytes(MOE_CALL_GATEUP, T, dims.d, dims.f, dims.n_experts, dims.top_k);
     if (!ws) return fail(MOE_ERR_ARG, "%s: ws is null", fn);
     if (ws_bytes < need) return fail(MOE_ERR_CAPACITY, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
-    hipError_t e = moe::launch_gateup_mfma(prec == MOE_PREC_F16_MFMA, h, offsets, sorted_pair, slot_of_expert, n_slots, arena, slot_stride, T,
-                                           dims.d, dims.f, dims.n_experts, dims.top_k, L.gate_q, L.up_q, L.gate_sb,
-                                           L.up_sb, act, ws, stream);
+    hipError_t e = moe::launch_gateup_mfma(prec == MOE_PREC_F16_MFMA, h, offsets, sorted_pair, slot_of_expert,
+                                           n_slots, arena, slot_stride, T, dims.d, dims.f, dims.n_experts,
+                                           dims.top_k, L.gate_q, L.up_q, L.gate_sb, L.up_sb, act, ws, stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
   }
   return fail(MOE_ERR_UNSUPPORTED, "%s: precision %d not available", fn, (int)prec);
@@ -252,16 +273,17 @@ moe_status moe_expert_q4_down_combine(const void* act, const int32_t* topk_idx, 
   if (prec == MOE_PREC_BF16_MFMA || prec == MOE_PREC_F16_MFMA) {
     if (!grouped)
       return fail(MOE_ERR_UNSUPPORTED, "%s: the MFMA path needs offsets and sorted_pair (moe_permute)", fn);
-    if ((int64_t)T * dims.top_k > 65536) return fail(MOE_ERR_ARG, "%s: T*k must be <= 65536", fn);
+    if ((int64_t)T * dims.top_k > kMaxMfmaPairs)
+      return fail(MOE_ERR_ARG, "%s: T*k must be <= %d on the MFMA path", fn, kMaxMfmaPairs);
+    if (!mfma_fits_32bit(T, dims, slot_stride))
+      return fail(MOE_ERR_ARG, "%s: h, act and a slot must each stay below 2 GiB on the MFMA path", fn);
     const size_t need =
         moe::mfma_workspace_bytes(MOE_CALL_DOWN_COMBINE, T, dims.d, dims.f, dims.n_experts, dims.top_k);
     if (!ws) return fail(MOE_ERR_ARG, "%s: ws is null", fn);
     if (ws_bytes < need) return fail(MOE_ERR_CAPACITY, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
-    float* pair_out = nullptr;
-    hipError_t e = moe::launch_down_mfma(prec == MOE_PREC_F16_MFMA, act, offsets, sorted_pair, slot_of_expert, n_slots, arena, slot_stride, T,
-                                         dims.d, dims.f, dims.n_experts, dims.top_k, L.down_q, L.down_sb, ws,
-                                         &pair_out, stream);
-    if (e == hipSuccess) e = moe::launch_combine(pair_out, topk_w, residual, y, T, dims.d, dims.top_k, stream);
+    hipError_t e = moe::launch_down_mfma(prec == MOE_PREC_F16_MFMA, act, offsets, sorted_pair, slot_of_expert,
+                                         n_slots, arena, slot_stride, T, dims.d, dims.f, dims.n_experts,
+                                         dims.top_k, L.down_q, L.down_sb, topk_w, residual, y, ws, stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
   }
   return fail(MOE_ERR_UNSUPPORTED, "%s: precision %d not available", fn, (int)prec);

@@ -69,7 +69,10 @@ hipError_t launch_down_fp32(DownArgs a, void* ws, hipStream_t s);
 hipError_t launch_combine(const float* pair_out, const float* topk_w, const float* residual, float* y, int T,
                           int d, int k, hipStream_t s);
 
-// ---- grouped bf16 MFMA GEMM for batched prefill (q4_grouped_mfma.hip)
+// ---- grouped int4 GEMM on MFMA for batched prefill (q4_grouped_mfma.hip).
+// act for these calls is block-scaled: 16-bit values [T*k][f], then int8
+// exponents [T*k][f/64]; element (p, c) = value * 2^exp[p][c/64].
+size_t mfma_act_bytes(int T, int f, int k);
 size_t mfma_workspace_bytes(int call, int T, int d, int f, int E, int k);
 hipError_t launch_gateup_mfma(bool f16, const float* h, const int32_t* offsets, const int32_t* sorted_pair,
                               const int32_t* slot_of_expert, int n_slots, const uint8_t* arena, int64_t slot_stride,
@@ -77,8 +80,8 @@ hipError_t launch_gateup_mfma(bool f16, const float* h, const int32_t* offsets, 
                               int64_t off_sb1, void* act_out, void* ws, hipStream_t s);
 hipError_t launch_down_mfma(bool f16, const void* act_in, const int32_t* offsets, const int32_t* sorted_pair,
                             const int32_t* slot_of_expert, int n_slots, const uint8_t* arena, int64_t slot_stride,
-                            int T, int d, int f, int E, int k, int64_t off_q, int64_t off_sb, void* ws,
-                            float** pair_out, hipStream_t s);
+                            int T, int d, int f, int E, int k, int64_t off_q, int64_t off_sb, const float* topk_w,
+                            const float* residual, float* y, void* ws, hipStream_t s);
 
 // ---- bf16 shared-path GEMV (shared_gemv.hip)
 hipError_t launch_shared_gemv_bf16(const uint16_t* w, const float* h, int T, int rows, int cols,

@@ -1,28 +1,35 @@
-// Grouped int4 GEMM on bf16 MFMA for batched prefill.
+// Grouped int4 GEMM on MFMA for batched prefill.
 //
-// With many tokens the routed experts are run as batched kernels over all the
+// With many tokens the routed experts run as batched kernels over all the
 // tokens routed to each expert ("Optimizing a 14.3 GB model for an 8 GB
-// machine", section "Splitting the work improved attention and prefill": batched
-// routed MoE), and the quantised weights go through the matrix hardware as small
-// staged dequantised tiles that are thrown away after use (same section: staged
-// affine tiles; a direct in-register int4 path was slower there).
+// machine", section "Splitting the work improved attention and prefill":
+// batched routed MoE), and the quantised weights reach the matrix hardware as
+// small dequantised tiles that are used once and thrown away (same section:
+// staged affine tiles).
 //
 // gfx950 design
-//  * Work item = (expert, 128-row M tile of its sorted pairs) x one N tile.  A
-//    one-workgroup scheduler orders experts by pair count, largest first, so the
-//    Zipf-skewed big experts start early and the small ones fill the tail.
-//  * Workgroup = 4 waves (2 x 2); each wave owns a 64 x 64 block of the 128 x 128
-//    output tile = 4 x 4 v_mfma_f32_16x16x32_bf16 tiles, fp32 accumulate.
-//  * K steps are one quantisation group (64 columns).  Per step a thread loads
-//    64 bytes of activation rows (gathered through sorted_pair) and 16 bytes of
-//    nibbles plus one (scale, bias) word; the weights are dequantised in fp32
-//    (w = s*q + b, exact), rounded to bf16 and written to LDS.  Two LDS stages:
-//    the next step's global loads are in flight while the current one feeds the
-//    MFMAs.
-//  * Gate/up tile = 64 gate rows + the same 64 up rows, so GELU(gate) * up is
-//    computed in the epilogue from accumulators held by the same lane; the
-//    activation is stored as bf16 for the down GEMM.  Down writes fp32 per-pair
-//    outputs and the rank-ordered gather combine sums them.
+//  * Work item = (expert, 128-pair M tile, N tile).  A one-workgroup scheduler
+//    lists experts by pair count, largest first, and within an expert M tile
+//    by M tile its N tiles.  Workgroup b takes item (b % 8) * per + b / 8:
+//    each XCD works through one contiguous stretch of the list, so an
+//    expert's weights and an M tile's activation rows are shared in one L2.
+//  * Workgroup = 4 waves side by side along N.  A wave owns all 128 M rows x 64
+//    weight rows: 8 x 4 tiles of v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulate.
+//  * K step = one quantisation group (64 columns).  The activation tile
+//    (128 rows x 64 columns, 16-bit) is staged in LDS, double buffered, and
+//    read by all four waves.  The weights do not go through LDS: each lane
+//    loads the 8 nibble bytes and the (scale, bias) word that its own MFMA B
+//    fragments need and dequantises them in registers.  The K order inside
+//    each 8-column block is (0,4,1,5,2,6,3,7), the order in which nibbles
+//    come out of a 32-bit word; activations are stored in LDS in that order.
+//  * Gate/up: a wave's 64 weight rows are 32 gate rows and the same 32 up
+//    rows, so gelu(gate) * up is formed from accumulators held by one lane.
+//  * fp16 results are block-scaled: one power-of-two exponent per row and
+//    64-column group keeps the group's largest magnitude in [2^14, 2^15), so
+//    nothing overflows fp16 whatever the activations' range.
+#include <algorithm>
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -30,45 +37,96 @@ namespace moe {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Operand element traits: bf16 (the specified format) or fp16 (three more
-// mantissa bits at the same MFMA rate on gfx950).
+constexpr int BM = 128;               // pair rows per work item
+constexpr int WN = 64;                // weight rows per wave
+constexpr int kWaves = 4;             // waves per workgroup, side by side along N
+constexpr int BN = WN * kWaves;       // weight rows per workgroup
+constexpr int BK = 64;                // K step = one quantisation group
+constexpr int LDA = BK + 8;           // padded LDS row (16-bit elements)
+constexpr int kThreads = kWaves * kWave;
+constexpr int kMaxExp = 100;          // block exponents are clamped to [-kMaxExp, kMaxExp]
+constexpr int kRsrcWord3 = 0x00020000;  // buffer resource word 3: raw 32-bit data, no swizzle
+
+// Position p inside an 8-column block holds column kSlot[p].
+__host__ __device__ constexpr int slot_col(int p) { return (p & 1) ? 4 + (p >> 1) : (p >> 1); }
+
+// ------------------------------------------------------------------ operand types
+
 template <typename ET>
-struct Elem;
+struct Op;
+
 template <>
-struct Elem<__bf16> {
-  typedef bf16x8 V8;
-  static __device__ __forceinline__ floatx4 mfma(V8 a, V8 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-template <>
-struct Elem<_Float16> {
+struct Op<_Float16> {
   typedef f16x8 V8;
   static __device__ __forceinline__ floatx4 mfma(V8 a, V8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
+  // One nibble word (columns 0..7 of a block) -> 8 weights in slot order.
+  // Nibble pairs are masked into fp16 1024 + q (exact), 1024 is subtracted
+  // (exact) and w = fma(q, s, b) rounds once.
+  static __device__ __forceinline__ uint4 dequant8(uint32_t w, uint32_t sb, uint32_t m, uint32_t M) {
+    const f16x2 s2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sb, sb, 0x01000100u));
+    const f16x2 b2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sb, sb, 0x03020302u));
+    const f16x2 off = {(_Float16)1024.0f, (_Float16)1024.0f};
+    const uint32_t p[4] = {(w & m) | M, ((w >> 4) & m) | M, ((w >> 8) & m) | M, ((w >> 12) & m) | M};
+    uint32_t v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2, p[j]) - off, s2, b2));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  static constexpr bool kScaled = true;
 };
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDK = BK + 8;  // padded LDS row (bf16): 144 bytes
-constexpr int kThreads = 256;
-
-struct Work {
-  int expert, m0;
+template <>
+struct Op<__bf16> {
+  typedef bf16x8 V8;
+  static __device__ __forceinline__ floatx4 mfma(V8 a, V8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // w = s*q + b in fp32 (exact for fp16 s, b), rounded to nearest-even bf16.
+  static __device__ __forceinline__ uint4 dequant8(uint32_t w, uint32_t sb, uint32_t, uint32_t) {
+    const float s = half_lo(sb), b = half_hi(sb);
+    __bf16 v[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) v[p] = (__bf16)fmaf(s, (float)((w >> (4 * slot_col(p))) & 0xFu), b);
+    return *reinterpret_cast<const uint4*>(v);
+  }
+  static constexpr bool kScaled = false;  // bf16 has fp32's range: exponents stay 0
 };
+
+// Block exponent for a group whose largest magnitude is m: m * 2^-e in [2^14, 2^15).
+__device__ __forceinline__ int block_exp(float m) {
+  if (!(m > 0.0f) || !(m <= 3.0e38f)) return 0;  // zero, NaN or inf: leave as is
+  const int ex = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 0xffu) - 127 - 14;
+  return ex < -kMaxExp ? -kMaxExp : (ex > kMaxExp ? kMaxExp : ex);
+}
+__device__ __forceinline__ float exp2i(int e) { return __builtin_bit_cast(float, (uint32_t)(127 + e) << 23); }
 
 // ------------------------------------------------------------------ schedule
 
-__global__ __launch_bounds__(256) void k_mfma_schedule(const int32_t* __restrict__ offsets, int E, int n_pairs,
-                                                       int2* __restrict__ work, int* __restrict__ n_work) {
+// Work list: experts by pair count (descending, ties by id); per expert, M tile
+// by M tile, its N tiles in order (the N tiles of one M tile share the
+// activation rows; the expert's weights stay in L2 across its M tiles).
+// Entry = (expert, m0, n tile).  The list is cut into 8 stretches of about
+// equal cost, one per XCD; an item costs 4 + (row groups of 16 in its M tile)
+// units (weights stream whatever the rows, MFMA work follows the rows).
+// meta[0] = items, meta[1 + x] = first item of XCD x (meta[9] = items).
+__global__ __launch_bounds__(256) void k_q4_schedule(const int32_t* __restrict__ offsets, int E, int n_pairs,
+                                                     int NT, int4* __restrict__ work, int* __restrict__ meta) {
   __shared__ int s_cnt[256];
-  __shared__ int s_tiles_by_rank[256];
-  __shared__ int s_base_by_rank[257];
+  __shared__ int s_expert[256];
+  __shared__ int s_rcnt[256];  // pair count by rank
+  __shared__ int s_base[257];
+  __shared__ int s_wsum[256 / kWave];
+  __shared__ int s_start[9];
   const int t = threadIdx.x;
   int cnt = 0;
   if (t < E) {
@@ -77,47 +135,119 @@ __global__ __launch_bounds__(256) void k_mfma_schedule(const int32_t* __restrict
   }
   s_cnt[t] = t < E ? cnt : -1;
   __syncthreads();
-  int rank = 0;
   if (t < E) {
+    int rank = 0;
     for (int e = 0; e < E; ++e) {
       const int c = s_cnt[e];
       rank += (c > cnt || (c == cnt && e < t)) ? 1 : 0;
     }
-    s_tiles_by_rank[rank] = (cnt + BM - 1) / BM;
+    s_expert[rank] = t;
+    s_rcnt[rank] = cnt;
+  }
+  if (t < 9) s_start[t] = -1;
+  __syncthreads();
+  // exclusive scan of items per rank (M tiles * NT) in one wave
+  if (t < kWave) {
+    int run = 0;
+    for (int r0 = 0; r0 < E; r0 += kWave) {
+      const int r = r0 + t;
+      const int v = r < E ? (s_rcnt[r] + BM - 1) / BM * NT : 0;
+      int incl = v;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int u = __shfl_up(incl, o, kWave);
+        if (t >= o) incl += u;
+      }
+      if (r < E) s_base[r] = run + incl - v;
+      run += __shfl(incl, kWave - 1, kWave);
+    }
+    if (t == 0) s_base[E] = run;
+  }
+  __syncthreads();
+  const int W = s_base[E];
+  // item i -> (rank, local index) and its cost
+  auto rank_of = [&](int i) {
+    int lo = 0, hi = E - 1;  // last rank with base <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (s_base[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
+  auto cost_of = [&](int r, int local) {
+    const int rows = min(BM, s_rcnt[r] - (local / NT) * BM);
+    return 4 + (rows + 15) / 16;
+  };
+  const int chunk = (W + blockDim.x - 1) / blockDim.x;
+  const int i0 = min(W, t * chunk), i1 = min(W, i0 + chunk);
+  int sum = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int r = rank_of(i), local = i - s_base[r];
+    work[i] = make_int4(s_expert[r], (local / NT) * BM, local % NT, 0);
+    sum += cost_of(r, local);
+  }
+  // block-wide exclusive scan of the per-thread costs
+  const int lane = t % kWave, wv = t / kWave;
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int u = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += u;
+  }
+  if (lane == kWave - 1) s_wsum[wv] = incl;
+  __syncthreads();
+  int wbase = 0, total = 0;
+  for (int w = 0; w < (int)(blockDim.x / kWave); ++w) {
+    if (w < wv) wbase += s_wsum[w];
+    total += s_wsum[w];
+  }
+  int pre = wbase + incl - sum;  // cost before item i0
+  auto xcd_of = [&](int before) { return min(7, (int)((int64_t)before * 8 / max(total, 1))); };
+  int x_prev = -1;
+  if (i0 > 0 && i0 < i1) {
+    const int r = rank_of(i0 - 1);
+    x_prev = xcd_of(pre - cost_of(r, i0 - 1 - s_base[r]));
+  }
+  for (int i = i0; i < i1; ++i) {
+    const int r = rank_of(i);
+    const int x = xcd_of(pre);
+    for (int xx = x_prev + 1; xx <= x; ++xx) s_start[xx] = i;
+    x_prev = x;
+    pre += cost_of(r, i - s_base[r]);
   }
   __syncthreads();
   if (t == 0) {
-    int run = 0;
-    for (int r = 0; r < E; ++r) {
-      s_base_by_rank[r] = run;
-      run += s_tiles_by_rank[r];
+    meta[0] = W;
+    int next = W;  // XCDs past the last boundary get empty stretches
+    for (int x = 8; x >= 0; --x) {
+      if (x == 8 || s_start[x] < 0) s_start[x] = next;
+      next = s_start[x];
+      meta[1 + x] = s_start[x];
     }
-    s_base_by_rank[E] = run;
-    *n_work = run;
-  }
-  __syncthreads();
-  if (t < E) {
-    const int base = s_base_by_rank[rank];
-    const int nt = (cnt + BM - 1) / BM;
-    for (int i = 0; i < nt; ++i) work[base + i] = make_int2(t, i * BM);
   }
 }
 
-// ------------------------------------------------------------------ fp32 -> bf16
-
+// h (fp32 [n8 * 8]) -> 16-bit, slot order inside each 8-column block.
 template <typename ET>
-__global__ __launch_bounds__(256) void k_convert(const float* __restrict__ x, int64_t n4, ET* __restrict__ y) {
+__global__ __launch_bounds__(256) void k_h_to_slots(const float* __restrict__ x, int64_t n8, ET* __restrict__ y) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n4) return;
-  const float4 v = reinterpret_cast<const float4*>(x)[i];
-  ET o[4] = {(ET)v.x, (ET)v.y, (ET)v.z, (ET)v.w};
-  reinterpret_cast<uint2*>(y)[i] = *reinterpret_cast<const uint2*>(o);
+  if (i >= n8) return;
+  const float4 lo = reinterpret_cast<const float4*>(x)[2 * i];
+  const float4 hi = reinterpret_cast<const float4*>(x)[2 * i + 1];
+  const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  ET o[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) o[p] = (ET)v[slot_col(p)];
+  reinterpret_cast<uint4*>(y)[i] = *reinterpret_cast<const uint4*>(o);
 }
 
-// ------------------------------------------------------------------ shared pieces
+// ------------------------------------------------------------------ the GEMM
 
-struct MfmaArgs {
-  const void* a_rows;     // gate/up: h as ET [T][d]; down: act as ET [T*k][f]
+struct GemmArgs {
+  const void* a_rows;     // gate/up: h [T][d] in slot order; down: act values [T*k][f], natural order
+  int a_bytes;            // bytes of a_rows (buffer loads are 32-bit addressed)
+  const int8_t* a_exp;    // down: act exponents [T*k][f/64]
   int a_by_token;         // 1: A row = token of the pair (gate/up); 0: A row = pair (down)
   const int32_t* offsets;
   const int32_t* sorted_pair;
@@ -127,255 +257,497 @@ struct MfmaArgs {
   int64_t slot_stride;
   int T, d, f, E, k;
   int K;                  // reduction length (d for gate/up, f for down)
-  int64_t off_q0, off_q1, off_sb0, off_sb1;  // gate/up sections, or down in q0/sb0
   int NT;                 // N tiles
-  const int2* work;
-  const int* n_work;
-  void* act_out;          // gate/up output [T*k][f] as ET
-  float* pair_out;        // down output [T*k][d] fp32
+  int64_t off_q0, off_q1, off_sb0, off_sb1;  // gate/up sections, or down in q0/sb0
+  const int4* work;
+  const int* meta;        // [0] items, [1 + x] first item of XCD x, [9] items
+  void* out;              // gate/up: act values [T*k][f] (ET); down: pair values [T*k][d] fp16
+  int8_t* out_exp;        // exponents [T*k][cols/64]
 };
 
-// Dequantise 32 weights of one row (one 16-byte nibble chunk) with the row's
-// (scale, bias) word into 4 x 16 bytes of ET, natural column order.
-//  bf16: w = s*q + b in fp32 (exact for fp16 s, b), rounded to nearest-even bf16.
-//  fp16: nibble pairs are masked into fp16 (1024 + q) (exact), 1024 is
-//        subtracted (exact), then w = fma(q, s, b) rounds once; byte permutes
-//        restore column order.  Packed 16-bit arithmetic: 19 ops per 8 weights.
-template <typename ET>
-__device__ __forceinline__ void dequant_chunk(uint4 q, uint32_t sb, uint4 out[4]);
-
-template <>
-__device__ __forceinline__ void dequant_chunk<_Float16>(uint4 q, uint32_t sb, uint4 out[4]) {
-  const f16x2 s2 = __builtin_bit_cast(f16x2, (sb & 0xffffu) * 0x10001u);
-  const f16x2 b2 = __builtin_bit_cast(f16x2, (sb >> 16) * 0x10001u);
-  const f16x2 off = {(_Float16)1024.0f, (_Float16)1024.0f};
-  const uint32_t m = 0x000F000Fu, M = 0x64006400u;
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t p[4];
-    p[0] = (w[i] & m) | M;          // columns 0, 4 of the word
-    p[1] = ((w[i] >> 4) & m) | M;   // 1, 5
-    p[2] = ((w[i] >> 8) & m) | M;   // 2, 6
-    p[3] = ((w[i] >> 12) & m) | M;  // 3, 7
-    uint32_t v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f16x2 qq = __builtin_bit_cast(f16x2, p[j]) - off;
-      v[j] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qq, s2, b2));
-    }
-    // (c0,c4) (c1,c5) (c2,c6) (c3,c7) -> (c0,c1) (c2,c3) (c4,c5) (c6,c7)
-    out[i] = make_uint4(__builtin_amdgcn_perm(v[1], v[0], 0x05040100u), __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
-                        __builtin_amdgcn_perm(v[1], v[0], 0x07060302u), __builtin_amdgcn_perm(v[3], v[2], 0x07060302u));
-  }
-}
-
-template <>
-__device__ __forceinline__ void dequant_chunk<__bf16>(uint4 q, uint32_t sb, uint4 out[4]) {
-  const float s = half_lo(sb), b = half_hi(sb);
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    __bf16 v[8];
-#pragma unroll
-    for (int n = 0; n < 8; ++n) v[n] = (__bf16)fmaf(s, (float)((w[i] >> (4 * n)) & 0xFu), b);
-    out[i] = *reinterpret_cast<const uint4*>(v);
-  }
-}
-
-// Row r of the B tile (128 weight rows) -> (matrix section, row index in the matrix)
-struct BRow {
-  int64_t q_off, sb_off;  // offsets of the row's tile start in the blob (row already added)
-  bool valid;
+// LDS of one pipeline stage (one K step).
+struct StageLds {
+  uint4 a[BM * 8];             // activation tile: 128 rows x 8 chunks of 16 bytes, swizzled
+  uint4 q[kWaves][2][WN];      // per wave: 2 nibble chunks x 64 weight rows x 16 bytes
+  uint32_t sb[kWaves][WN];     // per wave: (scale, bias) of 64 weight rows
 };
+constexpr int kStages = 3;        // K steps in flight: DMA runs two steps ahead
+constexpr int kDmaPerStep = 7;    // per wave and step: 4 activation + 2 nibble + 1 scale/bias loads
+constexpr int kMaxSteps = 128;    // K steps (groups) a down GEMM may have: f <= 8192
 
-// ------------------------------------------------------------------ the GEMM
+// Chunk position of 16-byte chunk c in activation row r: c ^ swz(r % 16).  Any
+// 8 (or 16) consecutive rows read at one chunk index hit distinct LDS banks.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// GATEUP = true: B rows 0..63 are gate rows of tile nt, 64..127 the same up rows;
-// the epilogue writes bf16 gelu(gate) * up.  GATEUP = false: B rows are down rows
-// nt*128 .. +127; the epilogue writes fp32 per-pair outputs.
+__device__ __forceinline__ void vm_wait_steps(bool one_more_in_flight) {
+  // s_waitcnt vmcnt(N), expcnt and lgkmcnt left unconstrained (gfx9 encoding)
+  if (one_more_in_flight) __builtin_amdgcn_s_waitcnt((kDmaPerStep & 0xF) | (0x7 << 4) | (0xF << 8));
+  else __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ lds_ptr_t to_lds(void* p) { return (lds_ptr_t)(p); }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
+}
+
+// LDS reads the compiler does not see: it would otherwise wait for every
+// outstanding DMA before each of them.  lds_wait() completes them and ties the
+// registers it names to that point.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read128(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read64(uint32_t addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t lds_read32(uint32_t addr) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+__device__ __forceinline__ void lds_wait(u32x4 (&r)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+}
+__device__ __forceinline__ void lds_wait(u32x4 (&r)[4], u32x2 (&q)[4], uint32_t (&sb)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]),
+                 "+v"(sb[0]), "+v"(sb[1]), "+v"(sb[2]), "+v"(sb[3]));
+}
+
+// GATEUP: wave w of N tile nt owns act columns nt*128 + 32w .. +31 (gate rows
+// and up rows of those indices).  Down: wave w owns output rows nt*256 + 64w .. +63.
+// Persistent: workgroup j of XCD x runs items meta[1+x] + j, + gridDim/8, ...
 template <typename ET, bool GATEUP>
-__global__ __launch_bounds__(kThreads, 2) void k_grouped_mfma(MfmaArgs a) {
-  typedef typename Elem<ET>::V8 V8;
-  __shared__ __align__(16) ET sA[2][BM][LDK];
-  __shared__ __align__(16) ET sB[2][BN][LDK];
-  __shared__ int s_arow[BM];   // A row index (token or pair), -1 = padding
+__global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
+  typedef Op<ET> O;
+  typedef typename O::V8 V8;
+  constexpr bool kScaledA = !GATEUP && O::kScaled;  // down: block-scaled fp16 activations
+  __shared__ StageLds lds[kStages];
   __shared__ int s_pair[BM];
+  __shared__ float s_wmax[kWaves];
+  __shared__ int s_gexp[kMaxSteps];  // down: tile exponent of each K group
+  __shared__ int s_fix;              // down: some row's exponents differ from its tile's
   const int t = threadIdx.x;
-  const int wid = t / kWave, lane = t % kWave;
-  const int nw = *a.n_work;
-  const int wi = blockIdx.x / a.NT, nt = blockIdx.x % a.NT;
-  if (wi >= nw) return;
-  const int2 wk = a.work[wi];
-  const int e = wk.x, m0 = wk.y;
+  const int wid = __builtin_amdgcn_readfirstlane(t / kWave), lane = t % kWave;
+  const int n = lane % 16, kq = lane / 16;  // MFMA lane coordinates
+  const int G = a.K / kGroup;               // K steps
   const int n_pairs = a.T * a.k;
-  const int beg = max(0, min(a.offsets[e], n_pairs)), end = max(beg, min(a.offsets[e + 1], n_pairs));
-  const int rows = max(0, min(BM, end - beg - m0));
-  if (t < BM) {
-    int p = -1;
-    if (t < rows) {
-      p = a.sorted_pair[beg + m0 + t];
-      if (p < 0 || p >= n_pairs) p = -1;
+  const int Nrows = GATEUP ? a.f : a.d;
+  const __amdgpu_buffer_rsrc_t rsA =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.a_rows), (short)0, a.a_bytes, kRsrcWord3);
+  uint32_t kMask = 0x000F000Fu, kMagic = 0x64006400u;  // in VGPRs: a gfx9 VOP3 takes no literal
+  asm volatile("" : "+v"(kMask), "+v"(kMagic));
+  // per-lane LDS addresses inside stage 0 (stage st adds st * sizeof(StageLds))
+  const uint32_t lds0 = lds_addr(&lds[0]);
+  const uint32_t a_rd0 = lds0 + n * 128 + (((kq * 2) ^ swz(n)) * 16);
+  const uint32_t a_rd1 = lds0 + n * 128 + (((kq * 2 + 1) ^ swz(n)) * 16);
+  const uint32_t q_rd = lds_addr(&lds[0].q[wid][kq >> 1][n]) + (kq & 1) * 8;
+  const uint32_t sb_rd = lds_addr(&lds[0].sb[wid][n]);
+
+  const int xcd = (int)(blockIdx.x % 8), nper = (int)(gridDim.x / 8);
+  const int i_end = __builtin_amdgcn_readfirstlane(a.meta[2 + xcd]);
+  for (int item = __builtin_amdgcn_readfirstlane(a.meta[1 + xcd]) + (int)(blockIdx.x / 8); item < i_end;
+       item += nper) {
+    __syncthreads();  // the previous item's LDS is no longer in use
+    // values the whole workgroup shares, made wave-uniform for the compiler
+    const int4 wk = a.work[item];
+    const int e = __builtin_amdgcn_readfirstlane(wk.x);
+    const int m0 = __builtin_amdgcn_readfirstlane(wk.y);
+    const int nt = __builtin_amdgcn_readfirstlane(wk.z);
+    const int beg = __builtin_amdgcn_readfirstlane(max(0, min(a.offsets[e], n_pairs)));
+    const int end = __builtin_amdgcn_readfirstlane(max(beg, min(a.offsets[e + 1], n_pairs)));
+    const int rows = max(0, min(BM, end - beg - m0));
+    if (t < BM) {
+      int p = -1;
+      if (t < rows) {
+        p = a.sorted_pair[beg + m0 + t];
+        if (p < 0 || p >= n_pairs) p = -1;
+      }
+      s_pair[t] = p;
     }
-    s_pair[t] = p;
-    s_arow[t] = p < 0 ? -1 : (a.a_by_token ? p / a.k : p);
-  }
-  // weights through the slot table; an absent expert gives NaN outputs
-  const uint8_t* blob = nullptr;
-  if (e >= 0 && e < a.E) {
-    const int slot = a.slot_of_expert[e];
-    if (slot >= 0 && slot < a.n_slots) blob = a.arena + (int64_t)slot * a.slot_stride;
-  }
-  const bool ok = blob != nullptr;
-  if (!ok) blob = a.arena;
-  __syncthreads();
-
-  const int G = a.K / kGroup;  // K steps
-  const int Nrows = GATEUP ? a.f : a.d;  // rows of the weight matrix
-  // this thread's A load: row ar = t/2, 32 columns at (t%2)*32
-  const int ar = t / 2, ah = t % 2;
-  const int arow = s_arow[ar];
-  const ET* a_src = reinterpret_cast<const ET*>(a.a_rows) + (int64_t)max(arow, 0) * a.K + ah * 32;
-  // this thread's B load: row br = t%128 of the tile, chunk bc = t/128 of the step
-  const int br = t % BN, bc = t / BN;
-  int mrow;          // row in the weight matrix
-  int64_t q_sec, sb_sec;
-  if (GATEUP) {
-    mrow = nt * 64 + (br % 64);
-    q_sec = br < 64 ? a.off_q0 : a.off_q1;
-    sb_sec = br < 64 ? a.off_sb0 : a.off_sb1;
-  } else {
-    mrow = nt * BN + br;
-    q_sec = a.off_q0;
-    sb_sec = a.off_sb0;
-  }
-  const bool brow_ok = mrow < Nrows;
-  const int mrow_c = brow_ok ? mrow : Nrows - 1;
-  const uint8_t* q_src = blob + q_sec + (int64_t)(mrow_c / kTileRows) * (kTileRows * a.K / 2) + (mrow_c % kTileRows) * 16;
-  const uint8_t* sb_src = blob + sb_sec + (int64_t)(mrow_c / kTileRows) * (kTileRows * G * 4) + (mrow_c % kTileRows) * 4;
-
-  uint4 ra[4], rq;
-  uint32_t rsb;
-  auto gload = [&](int ks) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      ra[i] = arow >= 0 ? *reinterpret_cast<const uint4*>(a_src + ks * BK + i * 8) : make_uint4(0u, 0u, 0u, 0u);
-    rq = *reinterpret_cast<const uint4*>(q_src + (int64_t)(2 * ks + bc) * 1024);
-    rsb = *reinterpret_cast<const uint32_t*>(sb_src + (int64_t)ks * 256);
-  };
-  auto lstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sA[st][ar][ah * 32 + i * 8]) = ra[i];
-    uint4 o[4];
-    dequant_chunk<ET>(rq, brow_ok ? rsb : 0u, o);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sB[st][br][bc * 32 + i * 8]) = o[i];
-  };
-
-  // wave tile: rows wm*64 .. +63 of the M tile; B rows per n-tile ni
-  const int wm = wid % 2, wn = wid / 2;
-  int brow_of[4];
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    if (GATEUP) brow_of[ni] = (ni < 2 ? 0 : 64) + wn * 32 + (ni % 2) * 16 + lane % 16;
-    else brow_of[ni] = wn * 64 + ni * 16 + lane % 16;
-  }
-  floatx4 acc[4][4];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int ks = 0; ks < G; ++ks) {
-    const int st = ks & 1;
-    if (ks + 1 < G) gload(ks + 1);
-#pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      const int kc = kk * 32 + (lane / 16) * 8;
-      V8 fa[4], fb[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        fa[mi] = *reinterpret_cast<const V8*>(&sA[st][wm * 64 + mi * 16 + lane % 16][kc]);
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) fb[ni] = *reinterpret_cast<const V8*>(&sB[st][brow_of[ni]][kc]);
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = Elem<ET>::mfma(fa[mi], fb[ni], acc[mi][ni]);
-    }
-    if (ks + 1 < G) lstore(st ^ 1);
+    if (kScaledA && t == 0) s_fix = 0;
+    // weights through the slot table; an absent expert gives NaN outputs
+    const int slot = (e >= 0 && e < a.E) ? __builtin_amdgcn_readfirstlane(a.slot_of_expert[e]) : -1;
+    const bool ok = slot >= 0 && slot < a.n_slots;
+    const uint8_t* blob = a.arena + (ok ? (int64_t)slot * a.slot_stride : 0);
     __syncthreads();
-  }
 
-  // epilogue: lane holds C[(lane/16)*4 + i][lane%16] of every 16x16 tile
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
+    // ---- DMA sources.  Activations: wave w, load i fills slots (4w + i)*64 + lane
+    // = row (4w + i)*8 + lane/8, chunk position lane%8.  Padding rows read row 0.
+    int a_off[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = wm * 64 + mi * 16 + (lane / 16) * 4 + i;
-      const int p = s_pair[m];
-      if (p < 0) continue;
-      if (GATEUP) {
+      const int r = (wid * 4 + i) * 8 + lane / 8;
+      const int p = s_pair[r];
+      const int arow = p < 0 ? 0 : (a.a_by_token ? p / a.k : p);
+      a_off[i] = (arow * a.K + ((lane % 8) ^ swz(r % 16)) * 8) * 2;
+    }
+    // Weights: lane = weight row of the wave (gate/up: lanes 0..31 gate rows,
+    // 32..63 the same up rows); ragged tiles read row 0 and discard it.
+    const int wave_base = GATEUP ? nt * (BN / 2) + wid * (WN / 2) : nt * BN + wid * WN;
+    const bool wave_ok = wave_base < Nrows;
+    const __amdgpu_buffer_rsrc_t rsB =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blob), (short)0, (int)a.slot_stride, kRsrcWord3);
+    int q_off, sb_off;
+    {
+      const bool up = GATEUP && lane >= 32;
+      int r = GATEUP ? wave_base + (lane & 31) : wave_base + lane;
+      r = wave_ok ? r : 0;
+      q_off = (int)((up ? a.off_q1 : a.off_q0) + (int64_t)(r / kTileRows) * (kTileRows * a.K / 2) +
+                    (r % kTileRows) * 16);
+      sb_off = (int)((up ? a.off_sb1 : a.off_sb0) + (int64_t)(r / kTileRows) * (kTileRows * G * 4) +
+                     (r % kTileRows) * 4);
+    }
+    auto issue = [&](int s, int st) {
+      const int so_a = __builtin_amdgcn_readfirstlane(s * BK * 2);
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const int col = nt * 64 + wn * 32 + ni * 16 + lane % 16;
-          float g = acc[mi][ni][i], u = acc[mi][ni + 2][i];
-          float v = gelu_tanh(g) * u;
-          if (!ok) v = f32_nan();
-          reinterpret_cast<ET*>(a.act_out)[(int64_t)p * a.f + col] = (ET)v;
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, to_lds(&lds[st].a[(wid * 4 + i) * kWave]), 16, a_off[i], so_a,
+                                                 0, 0);
+      const int so_q = __builtin_amdgcn_readfirstlane(s * 2048);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, to_lds(&lds[st].q[wid][c][0]), 16, q_off + c * 1024, so_q, 0,
+                                                 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, to_lds(&lds[st].sb[wid][0]), 4, sb_off,
+                                               __builtin_amdgcn_readfirstlane(s * 256), 0, 0);
+    };
+    // the first two K steps go out before anything else
+    issue(0, 0);
+    if (G > 1) issue(1, 1);
+
+    // down: each group's tile exponent.  Activations written by the gate/up
+    // kernel share one exponent per tile and group, so the first row's are the
+    // tile's; any row that differs switches on a rescale of its LDS slots.
+    int tile_exp = 0;  // down: activation value = LDS value * 2^(tile_exp + (s_gexp[s] - tile_exp))
+    bool fix_rows = false;
+    if (kScaledA) {
+      const int p = t < BM ? s_pair[t] : -1;
+      const int8_t* ep = a.a_exp + (int64_t)max(p, 0) * G;
+      const int8_t* e0 = a.a_exp + (int64_t)max(s_pair[0], 0) * G;  // row 0 of a tile is a pair
+      bool differs = false;
+      for (int g0 = 0; g0 < G; g0 += 16) {
+        int v[16], v0[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          v[i] = (p >= 0 && g0 + i < G) ? (int)ep[g0 + i] : 0;
+          v0[i] = (g0 + i < G) ? (int)e0[g0 + i] : 0;
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          differs |= p >= 0 && v[i] != v0[i];
+          if (t == 0 && g0 + i < G) s_gexp[g0 + i] = v0[i];
+        }
+      }
+      if (differs) s_fix = 1;
+      __syncthreads();
+      fix_rows = s_fix != 0;
+      if (fix_rows) {
+        // rare: tile exponent = the largest of its rows
+        __syncthreads();
+        if (p >= 0)
+          for (int g = 0; g < G; ++g) atomicMax(&s_gexp[g], (int)ep[g]);
+        __syncthreads();
+      }
+      int te = -128;
+      for (int g = 0; g < G; ++g) te = max(te, s_gexp[g]);
+      tile_exp = te;
+    }
+
+    floatx4 acc[8][4];
+#pragma unroll
+    for (int mg = 0; mg < 8; ++mg)
+#pragma unroll
+      for (int ng = 0; ng < 4; ++ng) acc[mg][ng] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int n_mg = __builtin_amdgcn_readfirstlane((rows + 15) / 16);
+    const bool half1 = n_mg > 4;
+
+    // Rows whose exponent for step s is below the tile's: rescale their slots in LDS.
+    auto fix_step = [&](int s, int st) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int sl = t * 4 + i, r = sl / 8;
+        const int p = s_pair[r];
+        if (p < 0) continue;
+        const int diff = (int)a.a_exp[(int64_t)p * G + s] - s_gexp[s];
+        if (diff == 0) continue;
+        const _Float16 c = diff < -24 ? (_Float16)0.0f : (_Float16)exp2i(diff);
+        const f16x2 c2 = {c, c};
+        uint4 v = lds[st].a[sl];
+        uint32_t* w = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, w[j]) * c2);
+        lds[st].a[sl] = v;
+      }
+    };
+    auto read_half = [&](u32x4 (&fa)[4], uint32_t base) {
+      fa[0] = lds_read128<0>(base);
+      fa[1] = lds_read128<2048>(base);
+      fa[2] = lds_read128<4096>(base);
+      fa[3] = lds_read128<6144>(base);
+    };
+    // gate/up: C[pair row][weight row]; down: C[weight row][pair row] (the
+    // transposed product puts 4 consecutive output columns in one lane)
+    auto mfma_half = [&](const u32x4 (&fa)[4], const V8 (&fb)[4], int h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * h + i < n_mg) {
+#pragma unroll
+          for (int ng = 0; ng < 4; ++ng)
+            acc[4 * h + i][ng] = GATEUP ? O::mfma(__builtin_bit_cast(V8, fa[i]), fb[ng], acc[4 * h + i][ng])
+                                        : O::mfma(fb[ng], __builtin_bit_cast(V8, fa[i]), acc[4 * h + i][ng]);
+        }
+    };
+    auto dequant = [&](V8 (&fb)[4], const u32x2 (&qv)[4], const uint32_t (&sbv)[4], int j) {
+#pragma unroll
+      for (int ng = 0; ng < 4; ++ng)
+        fb[ng] = __builtin_bit_cast(V8, O::dequant8(j == 0 ? qv[ng].x : qv[ng].y, sbv[ng], kMask, kMagic));
+    };
+    auto compute = [&](int s, int st) {
+      const uint32_t so = (uint32_t)st * (uint32_t)sizeof(StageLds);
+      u32x4 fx[4], fy[4];
+      u32x2 qv[4];
+      uint32_t sbv[4];
+      read_half(fx, a_rd0 + so);  // j = 0, rows 0..63
+      qv[0] = lds_read64<0>(q_rd + so);
+      qv[1] = lds_read64<256>(q_rd + so);
+      qv[2] = lds_read64<512>(q_rd + so);
+      qv[3] = lds_read64<768>(q_rd + so);
+      sbv[0] = lds_read32<0>(sb_rd + so);
+      sbv[1] = lds_read32<64>(sb_rd + so);
+      sbv[2] = lds_read32<128>(sb_rd + so);
+      sbv[3] = lds_read32<192>(sb_rd + so);
+      lds_wait(fx, qv, sbv);
+      if (kScaledA) {
+        // this group's activations carry 2^(s_gexp[s] - tile_exp) <= 1: fold it into s and b
+        const int d = s_gexp[s] - tile_exp;
+        if (d != 0) {
+          const _Float16 c = d < -24 ? (_Float16)0.0f : (_Float16)exp2i(d);
+          const f16x2 c2 = {c, c};
+#pragma unroll
+          for (int ng = 0; ng < 4; ++ng)
+            sbv[ng] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, sbv[ng]) * c2);
+        }
+      }
+      V8 fb[4];
+      dequant(fb, qv, sbv, 0);
+      if (half1) read_half(fy, a_rd0 + so + 8192);  // j = 0, rows 64..127
+      mfma_half(fx, fb, 0);
+      if (half1) {
+        lds_wait(fy);
+        read_half(fx, a_rd1 + so);  // j = 1, rows 0..63
+        mfma_half(fy, fb, 1);
       } else {
+        read_half(fx, a_rd1 + so);
+      }
+      dequant(fb, qv, sbv, 1);
+      lds_wait(fx);
+      if (half1) read_half(fy, a_rd1 + so + 8192);  // j = 1, rows 64..127
+      mfma_half(fx, fb, 0);
+      if (half1) {
+        lds_wait(fy);
+        mfma_half(fy, fb, 1);
+      }
+    };
+    for (int s = 0; s < G; ++s) {
+      const int st = s % kStages;
+      vm_wait_steps(s + 1 < G);            // this wave's DMA for step s has landed
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // and its LDS accesses (lgkmcnt 0)
+      __builtin_amdgcn_s_barrier();        // ... and every other wave's
+      if (fix_rows) {
+        fix_step(s, st);
+        __syncthreads();
+      }
+      if (s + 2 < G) issue(s + 2, (s + 2) % kStages);
+      if (wave_ok) compute(s, st);
+    }
+
+    // ---- epilogue
+    if (GATEUP) {
+      // acc[mg][ng][i] = C[pair row mg*16 + kq*4 + i][weight row ng*16 + n of the wave];
+      // act = gelu(gate) * up for wave columns c*16 + n, c = 0, 1
+      float v[8][2][4];
+      float m = 0.0f;
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const int col = nt * BN + wn * 64 + ni * 16 + lane % 16;
-          if (col < a.d) a.pair_out[(int64_t)p * a.d + col] = ok ? acc[mi][ni][i] : f32_nan();
+      for (int mg = 0; mg < 8; ++mg)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float g = acc[mg][c][i], u = acc[mg][c + 2][i];
+            v[mg][c][i] = ok ? gelu_tanh(g) * u : f32_nan();
+            if (mg * 16 + kq * 4 + i < rows) m = fmaxf(m, fabsf(v[mg][c][i]));
+          }
+      int ex = 0;
+      if (O::kScaled) {
+        // one exponent per M tile and 64-column group (waves 2g', 2g'+1)
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+        if (lane == 0) s_wmax[wid] = wave_ok ? m : 0.0f;
+        __syncthreads();
+        ex = block_exp(fmaxf(s_wmax[wid], s_wmax[wid ^ 1]));
+      }
+      if (wave_ok) {
+        const float sc = exp2i(-ex);
+        const int Gf = a.f / kGroup;
+        const int grp = wave_base / kGroup;
+#pragma unroll
+        for (int mg = 0; mg < 8; ++mg)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = mg * 16 + kq * 4 + i;
+            const int p = s_pair[r];
+            if (p < 0) continue;
+            ET* dst = reinterpret_cast<ET*>(a.out) + (int64_t)p * a.f;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const int col = wave_base + c * 16 + n;  // stored at its slot position
+              dst[(col & ~7) + (col & 3) * 2 + ((col >> 2) & 1)] = (ET)(v[mg][c][i] * sc);
+            }
+            if (n == 0 && (wid & 1) == 0) a.out_exp[(int64_t)p * Gf + grp] = (int8_t)ex;
+          }
+      }
+    } else if (wave_ok) {
+      // acc[mg][ng][i] = C[output column ng*16 + kq*4 + i of the wave][pair row mg*16 + n]
+      const int Gd = a.d / kGroup;
+      const int grp = wave_base / kGroup;
+#pragma unroll
+      for (int mg = 0; mg < 8; ++mg) {
+        float m = 0.0f;
+#pragma unroll
+        for (int ng = 0; ng < 4; ++ng)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(acc[mg][ng][i]));
+        m = fmaxf(m, __shfl_xor(m, 16, kWave));
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        const int p = s_pair[mg * 16 + n];
+        if (p < 0) continue;
+        const int ex = block_exp(m);
+        const float sc = exp2i(-ex);
+        _Float16* dst = reinterpret_cast<_Float16*>(a.out) + (int64_t)p * a.d + wave_base + kq * 4;
+#pragma unroll
+        for (int ng = 0; ng < 4; ++ng) {
+          _Float16 h4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) h4[i] = ok ? (_Float16)(acc[mg][ng][i] * sc) : (_Float16)f32_nan();
+          *reinterpret_cast<uint2*>(dst + ng * 16) = *reinterpret_cast<const uint2*>(h4);
         }
+        if (kq == 0) a.out_exp[(int64_t)p * Gd + grp] = (int8_t)max(-127, min(127, ex + tile_exp));
       }
     }
   }
+}
+
+// y[t] = residual[t] + sum_j w[t][j] * pair[t*k + j] in rank order, pair values
+// fp16 block-scaled.  Thread = 8 columns of one token.
+__global__ __launch_bounds__(256) void k_combine_scaled(const _Float16* __restrict__ pv, const int8_t* __restrict__ pe,
+                                                        const float* __restrict__ topk_w,
+                                                        const float* __restrict__ residual, float* __restrict__ y,
+                                                        int T, int d, int k) {
+  const int64_t n8 = (int64_t)T * d / 8;
+  const int64_t i8 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i8 >= n8) return;
+  const int t = (int)(i8 * 8 / d);
+  const int col = (int)(i8 * 8 - (int64_t)t * d);
+  const int Gd = d / kGroup;
+  float acc[8];
+  if (residual) {
+    const float4 r0 = reinterpret_cast<const float4*>(residual)[2 * i8];
+    const float4 r1 = reinterpret_cast<const float4*>(residual)[2 * i8 + 1];
+    acc[0] = r0.x; acc[1] = r0.y; acc[2] = r0.z; acc[3] = r0.w;
+    acc[4] = r1.x; acc[5] = r1.y; acc[6] = r1.z; acc[7] = r1.w;
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+  }
+  for (int j = 0; j < k; ++j) {
+    const int64_t p = (int64_t)t * k + j;
+    const float sc = topk_w[p] * exp2i(pe[p * Gd + col / kGroup]);
+    const uint4 raw = *reinterpret_cast<const uint4*>(pv + p * d + col);
+    const _Float16* h = reinterpret_cast<const _Float16*>(&raw);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = fmaf(sc, (float)h[c], acc[c]);
+  }
+  reinterpret_cast<float4*>(y)[2 * i8] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  reinterpret_cast<float4*>(y)[2 * i8 + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
 }  // namespace
 
 // ------------------------------------------------------------------ host side
 
-static int max_work(int T, int k, int E) { return (T * k + BM - 1) / BM + E; }
+static int gemm_nt(bool gateup, int d, int f) { return gateup ? (f + BN / 2 - 1) / (BN / 2) : (d + BN - 1) / BN; }
+
+// Upper bound of work items: sum over experts of ceil(c_e / BM) <= T*k/BM + E.
+static int max_items(int T, int k, int E, int NT) { return ((T * k + BM - 1) / BM + E) * NT; }
+
+size_t mfma_act_bytes(int T, int f, int k) { return (size_t)T * k * f * 2 + (size_t)T * k * (f / kGroup); }
 
 size_t mfma_workspace_bytes(int call, int T, int d, int f, int E, int k) {
-  size_t b = 256 + round256((int64_t)max_work(T, k, E) * 8);
-  if (call == MOE_CALL_GATEUP) b += round256((int64_t)T * d * 2);  // activations in 16-bit
-  else b += round256((int64_t)T * k * d * 4);
+  const bool gu = call == MOE_CALL_GATEUP;
+  size_t b = 256 + round256((int64_t)max_items(T, k, E, gemm_nt(gu, d, f)) * 16);
+  if (gu) b += round256((int64_t)T * d * 2);  // h in 16-bit, slot order
+  else b += round256((int64_t)T * k * d * 2) + round256((int64_t)T * k * (d / kGroup));
   return b;
 }
 
-static void carve(void* ws, int T, int k, int E, int** n_work, int2** work, char** rest) {
+static void carve(void* ws, int items, int** meta, int4** work, char** rest) {
   char* c = reinterpret_cast<char*>(ws);
-  *n_work = reinterpret_cast<int*>(c);
-  *work = reinterpret_cast<int2*>(c + 256);
-  *rest = c + 256 + round256((int64_t)max_work(T, k, E) * 8);
+  *meta = reinterpret_cast<int*>(c);
+  *work = reinterpret_cast<int4*>(c + 256);
+  *rest = c + 256 + round256((int64_t)items * 16);
+}
+
+// Persistent grid: two workgroups per compute unit (the kernel's occupancy),
+// a multiple of 8 so that every XCD has the same number of workgroups.
+static int persistent_grid(int items) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+      cus = 256;
+  }
+  const int g = (cus * 2) / 8 * 8;
+  return std::max(8, std::min(g, (items + 7) / 8 * 8));
+}
+
+template <typename ET, bool GATEUP>
+static void launch_gemm(const GemmArgs& a, int items, hipStream_t s, int call) {
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  take_profile_events(call, &ev0, &ev1);
+  launch_maybe_timed(k_q4_gemm<ET, GATEUP>, persistent_grid(items), kThreads, s, ev0, ev1, a);
 }
 
 hipError_t launch_gateup_mfma(bool f16, const float* h, const int32_t* offsets, const int32_t* sorted_pair,
                               const int32_t* slot_of_expert, int n_slots, const uint8_t* arena, int64_t slot_stride,
                               int T, int d, int f, int E, int k, int64_t off_q0, int64_t off_q1, int64_t off_sb0,
                               int64_t off_sb1, void* act_out, void* ws, hipStream_t s) {
-  int* n_work;
-  int2* work;
+  const int NT = gemm_nt(true, d, f);
+  const int items = max_items(T, k, E, NT);
+  int* meta;
+  int4* work;
   char* rest;
-  carve(ws, T, k, E, &n_work, &work, &rest);
-  const int64_t n4 = (int64_t)T * d / 4;
+  carve(ws, items, &meta, &work, &rest);
+  const int64_t n8 = (int64_t)T * d / 8;
   if (f16)
-    hipLaunchKernelGGL(k_convert<_Float16>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, h, n4,
+    hipLaunchKernelGGL(k_h_to_slots<_Float16>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, h, n8,
                        reinterpret_cast<_Float16*>(rest));
   else
-    hipLaunchKernelGGL(k_convert<__bf16>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, h, n4,
+    hipLaunchKernelGGL(k_h_to_slots<__bf16>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, h, n8,
                        reinterpret_cast<__bf16*>(rest));
-  hipLaunchKernelGGL(k_mfma_schedule, dim3(1), dim3(256), 0, s, offsets, E, T * k, work, n_work);
-  MfmaArgs a{};
+  hipLaunchKernelGGL(k_q4_schedule, dim3(1), dim3(256), 0, s, offsets, E, T * k, NT, work, meta);
+  GemmArgs a{};
   a.a_rows = rest;
+  a.a_bytes = (int)((int64_t)T * d * 2);
+  a.a_exp = nullptr;
   a.a_by_token = 1;
   a.offsets = offsets;
   a.sorted_pair = sorted_pair;
@@ -385,32 +757,34 @@ hipError_t launch_gateup_mfma(bool f16, const float* h, const int32_t* offsets, 
   a.slot_stride = slot_stride;
   a.T = T; a.d = d; a.f = f; a.E = E; a.k = k;
   a.K = d;
+  a.NT = NT;
   a.off_q0 = off_q0; a.off_q1 = off_q1; a.off_sb0 = off_sb0; a.off_sb1 = off_sb1;
-  a.NT = f / 64;
   a.work = work;
-  a.n_work = n_work;
-  a.act_out = act_out;
-  hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  take_profile_events(MOE_CALL_GATEUP, &ev0, &ev1);
-  if (f16)
-    launch_maybe_timed(k_grouped_mfma<_Float16, true>, max_work(T, k, E) * a.NT, kThreads, s, ev0, ev1, a);
-  else
-    launch_maybe_timed(k_grouped_mfma<__bf16, true>, max_work(T, k, E) * a.NT, kThreads, s, ev0, ev1, a);
+  a.meta = meta;
+  a.out = act_out;
+  a.out_exp = reinterpret_cast<int8_t*>(act_out) + (int64_t)T * k * f * 2;
+  if (f16) launch_gemm<_Float16, true>(a, items, s, MOE_CALL_GATEUP);
+  else launch_gemm<__bf16, true>(a, items, s, MOE_CALL_GATEUP);
   return hipGetLastError();
 }
 
 hipError_t launch_down_mfma(bool f16, const void* act_in, const int32_t* offsets, const int32_t* sorted_pair,
                             const int32_t* slot_of_expert, int n_slots, const uint8_t* arena, int64_t slot_stride,
-                            int T, int d, int f, int E, int k, int64_t off_q, int64_t off_sb, void* ws,
-                            float** pair_out, hipStream_t s) {
-  int* n_work;
-  int2* work;
+                            int T, int d, int f, int E, int k, int64_t off_q, int64_t off_sb, const float* topk_w,
+                            const float* residual, float* y, void* ws, hipStream_t s) {
+  const int NT = gemm_nt(false, d, f);
+  const int items = max_items(T, k, E, NT);
+  int* meta;
+  int4* work;
   char* rest;
-  carve(ws, T, k, E, &n_work, &work, &rest);
-  *pair_out = reinterpret_cast<float*>(rest);
-  hipLaunchKernelGGL(k_mfma_schedule, dim3(1), dim3(256), 0, s, offsets, E, T * k, work, n_work);
-  MfmaArgs a{};
+  carve(ws, items, &meta, &work, &rest);
+  _Float16* pair_val = reinterpret_cast<_Float16*>(rest);
+  int8_t* pair_exp = reinterpret_cast<int8_t*>(rest + round256((int64_t)T * k * d * 2));
+  hipLaunchKernelGGL(k_q4_schedule, dim3(1), dim3(256), 0, s, offsets, E, T * k, NT, work, meta);
+  GemmArgs a{};
   a.a_rows = act_in;
+  a.a_bytes = (int)((int64_t)T * k * f * 2);
+  a.a_exp = reinterpret_cast<const int8_t*>(act_in) + (int64_t)T * k * f * 2;
   a.a_by_token = 0;
   a.offsets = offsets;
   a.sorted_pair = sorted_pair;
@@ -420,17 +794,17 @@ hipError_t launch_down_mfma(bool f16, const void* act_in, const int32_t* offsets
   a.slot_stride = slot_stride;
   a.T = T; a.d = d; a.f = f; a.E = E; a.k = k;
   a.K = f;
+  a.NT = NT;
   a.off_q0 = off_q; a.off_sb0 = off_sb;
-  a.NT = (d + BN - 1) / BN;
   a.work = work;
-  a.n_work = n_work;
-  a.pair_out = *pair_out;
-  hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  take_profile_events(MOE_CALL_DOWN_COMBINE, &ev0, &ev1);
-  if (f16)
-    launch_maybe_timed(k_grouped_mfma<_Float16, false>, max_work(T, k, E) * a.NT, kThreads, s, ev0, ev1, a);
-  else
-    launch_maybe_timed(k_grouped_mfma<__bf16, false>, max_work(T, k, E) * a.NT, kThreads, s, ev0, ev1, a);
+  a.meta = meta;
+  a.out = pair_val;
+  a.out_exp = pair_exp;
+  if (f16) launch_gemm<_Float16, false>(a, items, s, MOE_CALL_DOWN_COMBINE);
+  else launch_gemm<__bf16, false>(a, items, s, MOE_CALL_DOWN_COMBINE);
+  const int64_t n8 = (int64_t)T * d / 8;
+  hipLaunchKernelGGL(k_combine_scaled, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, pair_val, pair_exp,
+                     topk_w, residual, y, T, d, k);
   return hipGetLastError();
 }
 

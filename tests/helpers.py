@@ -69,3 +69,20 @@ class LayerData:
 
     def blob_of(self, e):
         return self.blobs[e]
+
+
+# Stored position of column j inside a block of 8 in the MFMA act layout.
+ACT_POS = np.array([2 * (j % 4) + j // 4 for j in range(8)])
+
+
+def decode_scaled_act(buf, rows, cols, dtype):
+    """Block-scaled act buffer of the MFMA path (16-bit values [rows][cols] in
+    the 0,4,1,5,2,6,3,7 order inside each block of 8, then int8 exponents
+    [rows][cols/64]) -> float64 numpy [rows][cols] in natural column order."""
+    import torch
+    b = buf.detach().cpu()
+    nval = rows * cols * 2
+    vals = b[:nval].view(dtype).reshape(rows, cols).float().numpy().astype(np.float64)
+    vals = vals.reshape(rows, cols // 8, 8)[:, :, ACT_POS].reshape(rows, cols)
+    ex = b[nval:nval + rows * (cols // 64)].view(torch.int8).reshape(rows, cols // 64).numpy().astype(np.int64)
+    return vals * np.repeat(np.exp2(ex.astype(np.float64)), 64, axis=1)
