@@ -385,7 +385,8 @@ def distinct_experts(torch, stack):
 
 def run_batched(args, api, torch):
     T = args.tokens or 32
-    stack = BatchStack(api, torch, args.seed, T, api.MOE_PREC_FP32, decode=True)
+    prec = {"fp32": api.MOE_PREC_FP32, "f16": api.MOE_PREC_F16_MFMA, "bf16": api.MOE_PREC_BF16_MFMA}[args.batched_prec]
+    stack = BatchStack(api, torch, args.seed, T, prec, decode=True)
     graph = None if args.no_graph else graph_of(torch, stack.step)
     run = (lambda n: [stack.step() for _ in range(n)]) if graph is None else \
         (lambda n: [graph.replay() for _ in range(n)])
@@ -407,10 +408,14 @@ def run_batched(args, api, torch):
     gu_bytes = float(np.mean([nd[l] * gateup_expert_bytes() + T * D * 4 + T * K * F * 4 for l in layers]))
     achieved = gu_bytes / (gu_us * 1e-6) / 1e9
     log(f"kernels (eager, mean us): route {rt_us:.2f}  permute {pm_us:.2f}  gate/up {gu_us:.2f}  down {dn_us:.2f}")
-    out = base_record(tok_s, args.steps, args.warmup, ms, "fp32",
+    mfma = args.batched_prec != "fp32"
+    out = base_record(tok_s, args.steps, args.warmup, ms, args.batched_prec,
                       f"batched decode, {T} concurrent tokens per step, 30 routed MoE layers x 128 experts "
                       "(d=2816, f=704, top-8, int4 groups of 64), all experts resident in HBM, Zipf(1.1) routing "
-                      "independent per token", {"tokens_per_step": T, "graph": graph is not None})
+                      "independent per token, expert FFN as "
+                      + (f"grouped int4 GEMM on MFMA ({args.batched_prec} operands)" if mfma else
+                         "grouped int4 dequant-GEMV (fp32 accumulate)"),
+                      {"tokens_per_step": T, "graph": graph is not None})
     out.update({
         "distinct_experts_per_layer": round(float(nd.mean()), 2),
         "algorithmic_bytes_per_step": step_bytes,
@@ -419,7 +424,8 @@ def run_batched(args, api, torch):
         "kernel_us": {"route": round(rt_us, 3), "permute": round(pm_us, 3), "gateup": round(gu_us, 3),
                       "down_combine": round(dn_us, 3)},
         "roofline": {
-            "kernel": "k_gateup grouped (int4 gate/up dequant-GEMV over experts' token groups)",
+            "kernel": ("k_q4_gemm gate/up (grouped int4 GEMM on MFMA)" if mfma else
+                       "k_gateup grouped (int4 gate/up dequant-GEMV over experts' token groups)"),
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_of("batched"),
             "algorithmic_bytes_per_launch": int(gu_bytes), "avg_launch_us": round(gu_us, 3),
@@ -610,6 +616,8 @@ def main():
                          "expert within 16 steps (defeats the last-level cache)")
     ap.add_argument("--tokens", type=int, default=0, help="batched / prefill: tokens per step (32 / 2048)")
     ap.add_argument("--operands", choices=["f16", "bf16"], default="f16", help="prefill: MFMA operand type")
+    ap.add_argument("--batched-prec", choices=["fp32", "f16", "bf16"], default="fp32",
+                    help="batched: fp32 dequant-GEMV or grouped GEMM on MFMA")
     ap.add_argument("--slots", type=int, default=64, help="cache: HBM slots per layer")
     ap.add_argument("--kernel-samples", type=int, default=62)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -142,7 +142,7 @@ size_t moe_act_bytes(int32_t T, moe_dims dims, moe_precision prec) {
 size_t moe_workspace_size(moe_call call, int32_t T, moe_dims dims, moe_precision prec) {
   if (T < 1 || check_dims(dims) != MOE_OK) return SIZE_MAX;
   switch (call) {
-    case MOE_CALL_ROUTE: return moe::route_workspace_bytes(T, dims.n_experts);
+    case MOE_CALL_ROUTE: return moe::route_workspace_bytes(T, dims.d, dims.n_experts);
     case MOE_CALL_PERMUTE: return 0;
     case MOE_CALL_GATEUP:
     case MOE_CALL_DOWN_COMBINE:
@@ -163,7 +163,7 @@ moe_status moe_route(const float* x, const float* norm_w, float eps, const float
   CHECK_ALIGN(x); CHECK_ALIGN(norm_w); CHECK_ALIGN(router_w); CHECK_ALIGN(router_bias);
   CHECK_ALIGN(h_out); CHECK_ALIGN(topk_idx); CHECK_ALIGN(topk_w); CHECK_ALIGN(ws);
   if (!(eps >= 0.0f)) return fail(MOE_ERR_ARG, "%s: eps must be >= 0", fn);
-  const size_t need = moe::route_workspace_bytes(T, dims.n_experts);
+  const size_t need = moe::route_workspace_bytes(T, dims.d, dims.n_experts);
   if (ws_bytes < need) return fail(MOE_ERR_CAPACITY, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   hipError_t e = moe::launch_route(x, norm_w, eps, router_w, router_bias, T, dims.d, dims.n_experts,
                                    dims.top_k, h_out, topk_idx, topk_w, ws, stream);

@@ -97,4 +97,13 @@ inline void launch_maybe_timed(Kernel k, int grid, int block, hipStream_t s, hip
     hipLaunchKernelGGL(k, dim3(grid), dim3(block), 0, s, args...);
 }
 
+template <typename Kernel, typename... Args>
+inline void launch_maybe_timed2(Kernel k, dim3 grid, int block, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
+                                Args... args) {
+  if (ev0 && ev1)
+    hipExtLaunchKernelGGL(k, grid, dim3(block), 0, s, ev0, ev1, 0, args...);
+  else
+    hipLaunchKernelGGL(k, grid, dim3(block), 0, s, args...);
+}
+
 }  // namespace moe

@@ -12,7 +12,7 @@ namespace moe {
 bool take_profile_events(int call, hipEvent_t* start, hipEvent_t* stop);
 
 // ---- routing (route.hip)
-size_t route_workspace_bytes(int T, int E);
+size_t route_workspace_bytes(int T, int d, int E);
 hipError_t launch_route(const float* x, const float* norm_w, float eps, const float* router_w,
                         const float* router_bias, int T, int d, int E, int k, float* h_out,
                         int32_t* topk_idx, float* topk_w, void* ws, hipStream_t s);

@@ -15,21 +15,14 @@ namespace moe {
 namespace {
 
 constexpr int kSmallT = 8;         // fused single-launch path up to this many tokens
+typedef float floatx4r __attribute__((ext_vector_type(4)));
 constexpr int kRouteWaves = 4;     // waves per workgroup in the fused path
 
 // Top-k of one token's logits by one wave: k rounds of a wave-wide arg-max with
 // (larger value, then lower id) order.  Writes idx/w for the token.
-__device__ void wave_topk(const float* logits, int E, int k, int32_t* idx_out, float* w_out,
-                          bool coherent) {
+// v[i], ok[i]: the logit of expert lane + 64 i and whether that expert exists.
+__device__ void wave_topk_vals(float (&v)[4], bool (&ok)[4], int k, int32_t* idx_out, float* w_out) {
   const int lane = threadIdx.x % kWave;
-  float v[4];
-  bool ok[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int e = lane + kWave * i;
-    ok[i] = e < E;
-    v[i] = ok[i] ? (coherent ? load_coherent(logits + e) : logits[e]) : 0.0f;
-  }
   // lane j keeps the j-th choice
   float my_v = 0.0f;
   int my_e = -1;
@@ -65,6 +58,20 @@ __device__ void wave_topk(const float* logits, int E, int k, int32_t* idx_out, f
     idx_out[lane] = my_e;
     w_out[lane] = ex / s;
   }
+}
+
+__device__ void wave_topk(const float* logits, int E, int k, int32_t* idx_out, float* w_out,
+                          bool coherent) {
+  const int lane = threadIdx.x % kWave;
+  float v[4];
+  bool ok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int e = lane + kWave * i;
+    ok[i] = e < E;
+    v[i] = ok[i] ? (coherent ? load_coherent(logits + e) : logits[e]) : 0.0f;
+  }
+  wave_topk_vals(v, ok, k, idx_out, w_out);
 }
 
 // Top-k of one token's E <= 256 logits by one workgroup of 256 threads.  The
@@ -235,59 +242,128 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x,
 
 // logits[T][E] = h[T][d] * Wr[E][d]^T (+ bias).  32x32 output tile per
 // workgroup of 256 threads (2x2 outputs each), K staged through LDS 64 at a time.
-constexpr int kGT = 32, kGE = 32, kGK = 64;
+// Router GEMM for many tokens on fp32 MFMA: logits = h . Wr^T.  Workgroup =
+// 16 tokens x all experts x one K slice; wave w owns expert blocks w, w+4, ...
+// (16 experts each).  Each lane holds 4 consecutive columns of one token row
+// and one expert row per 16-column chunk and feeds them to 4 MFMAs
+// (v_mfma_f32_16x16x4f32), column j of each group of 4 in MFMA j.  Partial
+// logits of K slice ks go to partial[ks][t][e]; the top-k kernel adds the
+// slices in order, so the sums do not depend on scheduling.
+constexpr int kRT = 16;        // tokens per workgroup
+constexpr int kRWaves = 4;
+constexpr int kMaxSlices = 16;
 
-__global__ __launch_bounds__(256) void k_router_gemm(const float* __restrict__ h,
-                                                     const float* __restrict__ router_w,
-                                                     const float* __restrict__ router_bias, int T,
-                                                     int d, int E, float* __restrict__ logits) {
-  __shared__ float sh[kGT][kGK + 4];
-  __shared__ float sw[kGE][kGK + 4];
-  const int t0 = blockIdx.y * kGT, e0 = blockIdx.x * kGE;
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;  // 16 x 16 threads, 2x2 each
-  float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-  for (int k0 = 0; k0 < d; k0 += kGK) {
-    // load 32 rows x 64 cols of each operand: 512 float4 per operand, 2 per thread
-    for (int i = threadIdx.x; i < kGT * kGK / 4; i += 256) {
-      int r = i / (kGK / 4), c4 = i % (kGK / 4);
-      int t = t0 + r, e = e0 + r;
-      float4 a = t < T ? *reinterpret_cast<const float4*>(h + (size_t)t * d + k0 + c4 * 4)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-      float4 b = e < E ? *reinterpret_cast<const float4*>(router_w + (size_t)e * d + k0 + c4 * 4)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-      sh[r][c4 * 4 + 0] = a.x; sh[r][c4 * 4 + 1] = a.y; sh[r][c4 * 4 + 2] = a.z; sh[r][c4 * 4 + 3] = a.w;
-      sw[r][c4 * 4 + 0] = b.x; sw[r][c4 * 4 + 1] = b.y; sw[r][c4 * 4 + 2] = b.z; sw[r][c4 * 4 + 3] = b.w;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < kGK; ++kk) {
-      float a0 = sh[ty * 2 + 0][kk], a1 = sh[ty * 2 + 1][kk];
-      float b0 = sw[tx * 2 + 0][kk], b1 = sw[tx * 2 + 1][kk];
-      acc[0][0] += a0 * b0; acc[0][1] += a0 * b1;
-      acc[1][0] += a1 * b0; acc[1][1] += a1 * b1;
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      int t = t0 + ty * 2 + i, e = e0 + tx * 2 + j;
-      if (t < T && e < E) logits[(size_t)t * E + e] = acc[i][j] + (router_bias ? router_bias[e] : 0.f);
-    }
+struct RouterSplit {
+  int slices, kslice;
+};
+inline RouterSplit router_split(int T, int d) {
+  const int tiles = (T + kRT - 1) / kRT;
+  int ks = (1024 + tiles - 1) / tiles;  // ~4 workgroups per compute unit
+  ks = ks < 1 ? 1 : (ks > kMaxSlices ? kMaxSlices : ks);
+  int kslice = (d + ks - 1) / ks;
+  kslice = (kslice + 15) / 16 * 16;
+  return RouterSplit{(d + kslice - 1) / kslice, kslice};
 }
 
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
-                                              int32_t* __restrict__ topk_idx,
-                                              float* __restrict__ topk_w) {
+__global__ __launch_bounds__(kRWaves * kWave) void k_router_mfma(const float* __restrict__ h,
+                                                                 const float* __restrict__ router_w, int T,
+                                                                 int d, int E, int kslice,
+                                                                 float* __restrict__ partial) {
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int tn = lane % 16, kq = lane / 16;
+  const int t0 = blockIdx.x * kRT, ks = blockIdx.y;
+  const int k_begin = ks * kslice, k_end = min(d, k_begin + kslice);
+  const int nb = (E + 15) / 16;
+  const int t = t0 + tn;
+  const float* hrow = h + (size_t)min(t, T - 1) * d + kq * 4;
+  const float* wrow[4];
+  bool eok[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int e = (w + b * kRWaves) * 16 + tn;
+    eok[b] = (w + b * kRWaves) < nb && e < E;
+    wrow[b] = router_w + (size_t)(eok[b] ? e : 0) * d + kq * 4;
+  }
+  floatx4r acc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b] = floatx4r{0.f, 0.f, 0.f, 0.f};
+  // chunks of 16 columns, loaded two ahead of their MFMAs
+  struct Chunk {
+    float4 a, b[4];
+  };
+  auto load = [&](Chunk& c, int k0) {
+    c.a = *reinterpret_cast<const float4*>(hrow + k0);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      if (w + b * kRWaves < nb) c.b[b] = *reinterpret_cast<const float4*>(wrow[b] + k0);
+  };
+  auto mma = [&](const Chunk& c) {
+    const float av[4] = {c.a.x, c.a.y, c.a.z, c.a.w};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (w + b * kRWaves >= nb) continue;  // wave-uniform
+      const float bv[4] = {c.b[b].x, c.b[b].y, c.b[b].z, c.b[b].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc[b], 0, 0, 0);
+    }
+  };
+  Chunk c0, c1, c2;
+  if (k_begin < k_end) load(c0, k_begin);
+  if (k_begin + 16 < k_end) load(c1, k_begin + 16);
+  for (int k0 = k_begin; k0 < k_end; k0 += 48) {
+    if (k0 + 32 < k_end) load(c2, k0 + 32);
+    mma(c0);
+    if (k0 + 16 >= k_end) break;
+    if (k0 + 48 < k_end) load(c0, k0 + 48);
+    mma(c1);
+    if (k0 + 32 >= k_end) break;
+    if (k0 + 64 < k_end) load(c1, k0 + 64);
+    mma(c2);
+  }
+  // lane holds C[token kq*4 + i][expert tn] of each block
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if (w + b * kRWaves >= nb || !eok[b]) continue;
+    const int e = (w + b * kRWaves) * 16 + tn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tt = t0 + kq * 4 + i;
+      if (tt < T) partial[((size_t)ks * T + tt) * E + e] = acc[b][i];
+    }
+  }
+}
+
+// Per token (one wave): logits = sum of the K-slice partials in slice order +
+// bias, then top-k and the renormalised softmax weights.
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial, int slices,
+                                              const float* __restrict__ router_bias, int T, int E, int k,
+                                              int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= T) return;
-  wave_topk(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k, false);
+  float v[4];
+  bool ok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + kWave * i;
+    ok[i] = e < E;
+    float acc = 0.0f;
+    if (ok[i]) {
+      for (int s = 0; s < slices; ++s) acc += partial[((size_t)s * T + t) * E + e];
+      if (router_bias) acc += router_bias[e];
+    }
+    v[i] = acc;
+  }
+  wave_topk_vals(v, ok, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
 }
 
 }  // namespace
 
-size_t route_workspace_bytes(int T, int E) { return 256 + (size_t)T * E * sizeof(float); }
+size_t route_workspace_bytes(int T, int d, int E) {
+  const size_t small = (size_t)T * E * sizeof(float);
+  const size_t split = T > kSmallT ? (size_t)router_split(T, d).slices * T * E * sizeof(float) : 0;
+  return 256 + (small > split ? small : split);
+}
 
 hipError_t launch_route(const float* x, const float* norm_w, float eps, const float* router_w,
                         const float* router_bias, int T, int d, int E, int k, float* h_out,
@@ -303,13 +379,11 @@ hipError_t launch_route(const float* x, const float* norm_w, float eps, const fl
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_rmsnorm, dim3((T + 3) / 4), dim3(256), 0, s, x, norm_w, eps, T, d, h_out);
-  if (ev0 && ev1)
-    hipExtLaunchKernelGGL(k_router_gemm, dim3((E + kGE - 1) / kGE, (T + kGT - 1) / kGT), dim3(256), 0, s,
-                          ev0, ev1, 0, h_out, router_w, router_bias, T, d, E, logits);
-  else
-    hipLaunchKernelGGL(k_router_gemm, dim3((E + kGE - 1) / kGE, (T + kGT - 1) / kGT), dim3(256), 0, s, h_out,
-                       router_w, router_bias, T, d, E, logits);
-  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, topk_idx, topk_w);
+  const RouterSplit sp = router_split(T, d);
+  launch_maybe_timed2(k_router_mfma, dim3((T + kRT - 1) / kRT, sp.slices), kRWaves * kWave, s, ev0, ev1, h_out,
+                      router_w, T, d, E, sp.kslice, logits);
+  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, sp.slices, router_bias, T, E, k,
+                     topk_idx, topk_w);
   return hipGetLastError();
 }
 

@@ -108,6 +108,7 @@ def markov_selections(n_experts: int, k: int, steps: int, seed: int, layer: int,
     ``refill`` is "zipf" (the layer's Zipf(1.1) prior) or "uniform"."""
     g = rng(seed, _MARKOV, layer, 0 if refill == "zipf" else 1)
     prior = zipf_probs(n_experts, seed, layer) if refill == "zipf" else np.full(n_experts, 1.0 / n_experts)
+    prior = prior / prior.sum()  # the Zipf bias is fp32: renormalise in fp64 for Generator.choice
     out = np.empty((steps, k), dtype=np.int32)
     cur = g.choice(n_experts, size=k, replace=False, p=prior)
     out[0] = np.sort(cur)

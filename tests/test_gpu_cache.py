@@ -1,0 +1,168 @@
+"""GPU tests of the bounded expert cache (moe_slot_stage and friends) against
+the oracle's LRU rule: slot tables, hit masks, staged bytes and arena contents
+after every step, and a layer computed through the cache against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import synth
+from helpers import TOL_FP32, check_topk, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import int4_routed_expert_route_amd.api as api
+    api.lib()
+    return api
+
+
+class Pool:
+    """Pinned host pool of n_layers x E blobs plus the device arena of slots."""
+
+    def __init__(self, api, d, f, E, k, n_layers, n_slots, seed):
+        self.d, self.f, self.E, self.k, self.L, self.S = d, f, E, k, n_layers, n_slots
+        self.dm = api.dims(d, f, E, k)
+        self.blob = orc.blob_bytes(d, f)
+        self.stride = api.moe_expert_blob_bytes(self.dm)
+        self.blobs = [[synth.expert_blob(d, f, seed, l, e) for e in range(E)] for l in range(n_layers)]
+        self.pool = torch.empty(n_layers * E * self.blob, dtype=torch.uint8, pin_memory=True)
+        self.pool.copy_(torch.from_numpy(np.concatenate([b for layer in self.blobs for b in layer])))
+        # the arena starts out filled with a marker byte, so stale slots show
+        self.arena = torch.full((n_layers * n_slots * self.stride,), 0xA5, dtype=torch.uint8, device="cuda")
+        self.tables = torch.zeros(n_layers, E, dtype=torch.int32, device="cuda")
+        self.cache = api.MoeCache(n_layers, E, n_slots, k, self.pool, self.blob, self.arena, self.stride,
+                                  self.tables)
+
+    def slot_bytes(self, l, s):
+        off = (l * self.S + s) * self.stride
+        return self.arena[off:off + self.blob].cpu().numpy()
+
+
+def _stage(api, pool, l, t, sel, side, compute):
+    hit_dev = torch.zeros(16, dtype=torch.uint8, device="cuda")[:pool.k]
+    hit_host = torch.zeros(pool.k, dtype=torch.uint8)
+    sel_host = torch.from_numpy(np.asarray(sel, dtype=np.int32).copy())
+    st = api.moe_slot_stage(pool.cache, l, t, sel_host, side, compute, hit_dev, hit_host)
+    return st, hit_dev, hit_host
+
+
+@pytest.mark.parametrize("n_slots,steps", [(8, 60), (16, 40)])
+def test_slot_tables_follow_oracle_lru(api, n_slots, steps):
+    d, f, E, k, nl = 256, 128, 32, 4, 2
+    pool = Pool(api, d, f, E, k, nl, n_slots, seed=3)
+    side, compute = torch.cuda.Stream(), torch.cuda.current_stream()
+    lru = [orc.LruSlotCache(n_slots, E) for _ in range(nl)]
+    sels = [synth.markov_selections(E, k, steps, 3, l) for l in range(nl)]
+    hits = misses = 0
+    for t in range(steps):
+        for l in range(nl):
+            # the router's rank order: any order of the set; use a seeded shuffle
+            sel = np.random.default_rng(t * 7 + l).permutation(sels[l][t])
+            st, hit_dev, hit_host = _stage(api, pool, l, t, sel, side, compute)
+            want_hit, installs = lru[l].step(t, [int(e) for e in sel])
+            hits += sum(want_hit)
+            misses += len(installs)
+            assert hit_host.numpy().astype(bool).tolist() == want_hit, (t, l)
+            api.moe_cache_wait(pool.cache, l, compute)
+            torch.cuda.synchronize()
+            assert np.array_equal(hit_dev.cpu().numpy().astype(bool), np.array(want_hit)), (t, l)
+            table = torch.zeros(E, dtype=torch.int32)
+            api.moe_cache_slot_table(pool.cache, l, table)
+            want = np.array(lru[l].slot_of_expert(), dtype=np.int32)
+            assert np.array_equal(table.numpy(), want), (t, l)
+            assert np.array_equal(pool.tables[l].cpu().numpy(), want), (t, l)
+            for e, s, _ in installs:  # every staged blob landed whole in its slot
+                assert np.array_equal(pool.slot_bytes(l, s), pool.blobs[l][e]), (t, l, e, s)
+            assert (st.hits, st.misses) == (hits, misses)
+            assert st.bytes_staged == misses * pool.blob
+    # every resident expert's slot holds its blob at the end
+    for l in range(nl):
+        for s, e in enumerate(lru[l].export_state()[0]):
+            if e >= 0:
+                assert np.array_equal(pool.slot_bytes(l, s), pool.blobs[l][e])
+    pool.cache.close()
+
+
+def test_export_import_round_trip(api):
+    d, f, E, k, nl, S = 256, 128, 16, 4, 1, 8
+    pool = Pool(api, d, f, E, k, nl, S, seed=5)
+    side, compute = torch.cuda.Stream(), torch.cuda.current_stream()
+    sels = synth.markov_selections(E, k, 20, 5, 0)
+    lru = orc.LruSlotCache(S, E)
+    for t in range(10):
+        _stage(api, pool, 0, t, sels[t], side, compute)
+        lru.step(t, [int(e) for e in sels[t]])
+    api.moe_cache_wait(pool.cache, 0, compute)
+    torch.cuda.synchronize()
+    se = torch.zeros(nl, S, dtype=torch.int32)
+    stp = torch.zeros(nl, S, dtype=torch.int64)
+    api.moe_cache_export(pool.cache, se, stp)
+    want_se, want_st = lru.export_state()
+    assert se[0].tolist() == want_se and stp[0].tolist() == want_st
+    # a second cache restored from the checkpoint continues exactly like the oracle
+    pool2 = Pool(api, d, f, E, k, nl, S, seed=5)
+    api.moe_cache_import(pool2.cache, se, stp)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool2.tables[0].cpu().numpy(), np.array(lru.slot_of_expert(), dtype=np.int32))
+    for t in range(10, 20):
+        _, _, hit_host = _stage(api, pool2, 0, t, sels[t], side, compute)
+        want_hit, _ = lru.step(t, [int(e) for e in sels[t]])
+        assert hit_host.numpy().astype(bool).tolist() == want_hit
+    api.moe_cache_wait(pool2.cache, 0, compute)
+    torch.cuda.synchronize()
+    table = torch.zeros(E, dtype=torch.int32)
+    api.moe_cache_slot_table(pool2.cache, 0, table)
+    assert np.array_equal(table.numpy(), np.array(lru.slot_of_expert(), dtype=np.int32))
+    pool.cache.close()
+    pool2.cache.close()
+
+
+def test_layer_through_cache_matches_oracle(api):
+    """Decode steps of one layer with 8 of 32 experts resident: route (selection
+    forced by the router bias), stage misses, gate/up for hits, shared-path
+    filler GEMV, wait, gate/up for misses, down + combine; compared with the
+    oracle layer on the full expert set every step."""
+    d, f, E, k, S = 256, 128, 32, 4, 8
+    pool = Pool(api, d, f, E, k, 1, S, seed=9)
+    side, compute = torch.cuda.Stream(), torch.cuda.current_stream()
+    rw = synth.router_weight(d, E, 9, 0)
+    nw = synth.norm_weight(d, 9, 0)
+    sels = synth.markov_selections(E, k, 12, 9, 0)
+    dm = pool.dm
+    rw_d, nw_d = torch.from_numpy(rw).cuda(), torch.from_numpy(nw).cuda()
+    w_sh = torch.from_numpy(synth.shared_weight_bf16(4 * d, d, 9, 0).view(np.int16)).cuda()
+    ws = lambda c: torch.zeros(max(api.moe_workspace_size(c, 1, dm), 256), dtype=torch.uint8, device="cuda")
+    x_np = synth.tokens(1, d, 9)
+    for t in range(len(sels)):
+        bias = synth.selection_bias(sels[t], E)
+        x = torch.from_numpy(x_np).cuda()
+        h = torch.empty(1, d, device="cuda")
+        idx = torch.empty(1, k, dtype=torch.int32, device="cuda")
+        w = torch.empty(1, k, device="cuda")
+        api.moe_route(x, nw_d, 1e-6, rw_d, torch.from_numpy(bias).cuda(), 1, dm, h, idx, w, ws(0))
+        sel = idx.cpu().numpy()[0]
+        assert sorted(sel.tolist()) == sorted(sels[t].tolist())
+        _, hit_dev, _ = _stage(api, pool, 0, t, sel, side, compute)
+        act = torch.zeros(k, f, device="cuda")
+        table = pool.tables[0]
+        api.moe_expert_q4_gateup(h, idx, table, S, pool.arena, pool.stride, None, None, hit_dev, 1, 1, dm,
+                                 api.MOE_PREC_FP32, act, ws(2))
+        s_out = torch.empty(1, 4 * d, device="cuda")
+        api.moe_shared_gemv_bf16(w_sh, h, 1, 4 * d, d, s_out)
+        api.moe_cache_wait(pool.cache, 0, compute)
+        api.moe_expert_q4_gateup(h, idx, table, S, pool.arena, pool.stride, None, None, hit_dev, 0, 1, dm,
+                                 api.MOE_PREC_FP32, act, ws(2))
+        y = torch.empty(1, d, device="cuda")
+        api.moe_expert_q4_down_combine(act, idx, w, table, S, pool.arena, pool.stride, None, None, None, x, 1, dm,
+                                       api.MOE_PREC_FP32, y, ws(3))
+        torch.cuda.synchronize()
+        ry, ridx, _, _, lg = orc.moe_layer(x_np, nw, rw, bias, lambda e: pool.blobs[0][e], d, f, k)
+        check_topk(idx.cpu().numpy(), ridx, lg)
+        assert row_rel_err(y.cpu().numpy() - x_np, ry - x_np) < TOL_FP32, t
+        x_np = orc.rms_rescale(y.cpu().numpy().astype(np.float64), 1e-6).astype(np.float32)
+    pool.cache.close()
