@@ -50,8 +50,10 @@ CSRC = os.path.join(ROOT, "int4_routed_expert_route_amd", "csrc")
 # (scaled by a 256 MiB copy's readings), keyed by the workload, for the kernel
 # sources with this fingerprint; reported as null once the sources differ.
 TRAFFIC = {
-    "decode": {"sources": ("q4_gemv.hip", "common.h"), "sha256_16": "c35bc92e4b26bf04",
-               "fetch_bytes": 18126218, "write_bytes": 22528},
+    "decode": {"sources": ("q4_gemv.hip", "common.h"), "sha256_16": "925f59ad45a09c0d",
+               "fetch_bytes": 18126153, "write_bytes": 22528},
+    "prefill": {"sources": ("q4_grouped_mfma.hip", "common.h"), "sha256_16": "b7d97c1408f289ec",
+                "fetch_bytes": 241528376, "write_bytes": 23917840},
 }
 
 
@@ -479,6 +481,8 @@ def run_prefill(args, api, torch):
             "kernel": f"k_grouped_mfma gate/up ({args.operands} MFMA 16x16x32, int4 tiles dequantised in LDS)",
             "bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": traffic_of("prefill"),
+            "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated, median "
+                            "over the 30 layers' launches)",
             "algorithmic_flop_per_launch": flop_gu, "avg_launch_us": round(gu_us, 2),
         },
         "wall_s_timed": round(t_wall, 3),
