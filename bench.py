@@ -209,8 +209,9 @@ class DecodeStack:
         self.arena, self.stride = build_arena(torch, api, seed)
         dev = "cuda"
         self.slots = torch.arange(E, dtype=torch.int32, device=dev)
-        self.router_w = [torch.from_numpy(synth.router_weight(D, E, seed, l)).to(dev) for l in range(NL)]
-        self.norm_w = [torch.from_numpy(synth.norm_weight(D, seed, l)).to(dev) for l in range(NL)]
+        self.tables = self.slots.repeat(NL, 1).contiguous()  # [NL][E], identity slots
+        self.router_w = torch.from_numpy(np.stack([synth.router_weight(D, E, seed, l) for l in range(NL)])).to(dev)
+        self.norm_w = torch.from_numpy(np.stack([synth.norm_weight(D, seed, l) for l in range(NL)])).to(dev)
         self.cold = cold
         if cold:
             # control arm: step s selects experts {(8s + j + 3l) mod 128}: an expert
@@ -235,9 +236,25 @@ class DecodeStack:
         self.y_probe = torch.empty(1, D, dtype=torch.float32, device=dev)
         ws = lambda c: torch.zeros(max(api.moe_workspace_size(c, 1, self.dm), 256), dtype=torch.uint8, device=dev)
         self.ws_route, self.ws_gateup, self.ws_down = ws(0), ws(2), ws(3)
+        self.ws_fused = torch.zeros(api.moe_workspace_size(api.MOE_CALL_DECODE_LAYERS, NL, self.dm),
+                                    dtype=torch.uint8, device=dev)
+        self.idx_f = torch.zeros(self.period, NL, K, dtype=torch.int32, device=dev)
+        self.w_f = torch.zeros(self.period, NL, K, dtype=torch.float32, device=dev)
 
     def arena_of(self, l):
         return self.arena[l * E * self.stride:(l + 1) * E * self.stride]
+
+    def fused_step(self, s, stream=None):
+        """One token through the 30 layers in one launch; the unit-RMS feedback
+        goes straight back into x[0]."""
+        self.api.moe_decode_layers(self.x, NL, self.norm_w, EPS, self.router_w, self.bias[s], self.tables, E,
+                                   self.arena, E * self.stride, self.stride, self.dm, self.idx_f[s], self.w_f[s],
+                                   self.x[0], self.ws_fused, stream)
+
+    def fused_steps(self, n_periods=1, stream=None):
+        for _ in range(n_periods):
+            for s in range(self.period):
+                self.fused_step(s, stream)
 
     def route(self, s, l, stream=None):
         self.api.moe_route(self.x[l:l + 1], self.norm_w[l], EPS, self.router_w[l], self.bias[s, l], 1, self.dm,
@@ -268,17 +285,22 @@ def run_decode(args, api, torch):
     stack = DecodeStack(api, torch, args.seed, cold=args.control == "cold")
     period = stack.period
     steps, warm = rounded_steps(args.steps, period), rounded_steps(args.warmup, period)
+    fused = args.decode_path == "fused"
+    body = (lambda: stack.fused_steps(1)) if fused else (lambda: stack.steps(1))
     if args.no_graph:
-        run = lambda n: stack.steps(n // period)
+        run = lambda n: [body() for _ in range(n // period)]
     else:
         # one replay = one routing period (1 step for Zipf, 16 for the cold arm)
-        graph = graph_of(torch, lambda: stack.steps(1))
+        graph = graph_of(torch, body)
         run = lambda n: [graph.replay() for _ in range(n // period)]
     ms, t_wall = timed(torch, run, steps, warm)
+    if fused:
+        api.moe_decode_check(stack.ws_fused)
     tok_s = 1000.0 / ms
     per_layer, gu_bytes, _ = decode_bytes()
     step_bytes = NL * per_layer
-    log(f"{steps} steps: {ms * 1000:.1f} us/step, {tok_s:.1f} tok/s, {step_bytes * tok_s / 1e9:.0f} GB/s algorithmic")
+    log(f"{steps} steps ({args.decode_path}): {ms * 1000:.1f} us/step, {tok_s:.1f} tok/s, "
+        f"{step_bytes * tok_s / 1e9:.0f} GB/s algorithmic")
 
     # the step's kernels one at a time, each at its own begin/end; layer and
     # routing-period index cycle so every layer's weights are used
@@ -289,27 +311,44 @@ def run_decode(args, api, torch):
     dn_us, _ = time_launch(api, torch, api.MOE_CALL_DOWN_COMBINE, lambda i: stack.down(*sl(i), stack.y_probe), n)
     achieved = gu_bytes / (gu_us * 1e-6) / 1e9
     log(f"kernels (eager, mean us): route {rt_us:.2f}  gate/up {gu_us:.2f} (median {gu_med:.2f})  down {dn_us:.2f}")
+    if fused:
+        fu_us, _ = time_launch(api, torch, api.MOE_CALL_DECODE_LAYERS, lambda i: stack.fused_step(i % period), n)
+        api.moe_decode_check(stack.ws_fused)
+        f_achieved = step_bytes / (fu_us * 1e-6) / 1e9
+        log(f"fused decode kernel (eager, mean): {fu_us:.1f} us per token, {f_achieved:.0f} GB/s algorithmic")
 
     out = base_record(tok_s, steps, warm, ms, "fp32",
                       "batch-1 decode, 30 routed MoE layers x 128 experts (d=2816, f=704, top-8, int4 groups of "
                       "64, fp16 scale/bias), all experts resident in HBM, "
                       + ("Zipf(1.1) routing" if not stack.cold else
                          "cold routing control (no expert reuse within 16 steps)"),
-                      {"tokens_per_step": 1, "graph": not args.no_graph})
+                      {"tokens_per_step": 1, "graph": not args.no_graph,
+                       "path": "moe_decode_layers (one launch per token)" if fused else
+                               "moe_route + moe_expert_q4_gateup + moe_expert_q4_down_combine per layer"})
     out.update({
         "algorithmic_bytes_per_token": step_bytes,
         "algorithmic_GBps": round(step_bytes * tok_s / 1e9, 1),
         "hbm_frac_step": round(step_bytes * tok_s / 1e9 / HBM_PEAK_GBPS, 4),
         "kernel_us": {"route": round(rt_us, 3), "gateup": round(gu_us, 3), "down_combine": round(dn_us, 3)},
-        "roofline": {
+        "wall_s_timed": round(t_wall, 3),
+    })
+    if fused:
+        out["kernel_us"]["decode_layers_fused"] = round(fu_us, 2)
+        out["roofline"] = {
+            "kernel": "k_decode_fused (30 layers of route + int4 gate/up + down + combine, one launch per token)",
+            "bound": "hbm", "achieved": round(f_achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(f_achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_of("decode_fused"),
+            "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "algorithmic_bytes_per_launch": step_bytes, "avg_launch_us": round(fu_us, 2),
+        }
+    else:
+        out["roofline"] = {
             "kernel": "k_gateup (int4 gate/up dequant-GEMV, 8 experts, fp32 accumulate)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_of("decode"),
             "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 3),
-        },
-        "wall_s_timed": round(t_wall, 3),
-    })
+        }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(args.seed, 1, 20.0, "batch-1 decode (Zipf routing)")
@@ -619,6 +658,8 @@ def main():
                     help="decode: zipf = the Zipf(1.1) routing workload; cold = routing that never reuses an "
                          "expert within 16 steps (defeats the last-level cache)")
     ap.add_argument("--tokens", type=int, default=0, help="batched / prefill: tokens per step (32 / 2048)")
+    ap.add_argument("--decode-path", choices=["fused", "calls"], default="fused",
+                    help="decode: one moe_decode_layers launch per token, or the three calls per layer")
     ap.add_argument("--operands", choices=["f16", "bf16"], default="f16", help="prefill: MFMA operand type")
     ap.add_argument("--batched-prec", choices=["fp32", "f16", "bf16"], default="fp32",
                     help="batched: fp32 dequant-GEMV or grouped GEMM on MFMA")

@@ -101,7 +101,8 @@ typedef enum moe_call {
   MOE_CALL_ROUTE = 0,
   MOE_CALL_PERMUTE = 1,
   MOE_CALL_GATEUP = 2,
-  MOE_CALL_DOWN_COMBINE = 3
+  MOE_CALL_DOWN_COMBINE = 3,
+  MOE_CALL_DECODE_LAYERS = 4
 } moe_call;
 
 /* Text of a status code, and the thread-local detail of the last failure. */
@@ -287,6 +288,51 @@ moe_status moe_cache_export(const moe_cache* c, int32_t* slot_expert_host, int64
 /* Restore exported state; rewrites the device slot tables synchronously.  The
  * arena contents are the caller's business (restage or keep). */
 moe_status moe_cache_import(moe_cache* c, const int32_t* slot_expert_host, const int64_t* stamp_host);
+
+/* ---------------------------------------------------------------------------
+ * moe_decode_layers — batch-1 decode of one token through n_layers routed MoE
+ * layers in one launch: per layer RMSNorm, router, softmax, top-k,
+ * renormalised weights, the selected experts' int4 gate/up, GELU, down and the
+ * rank-ordered combine with the residual, exactly as moe_route +
+ * moe_expert_q4_gateup + moe_expert_q4_down_combine (MOE_PREC_FP32) compute
+ * them, layer after layer (the routed MoE of "Optimizing a 14.3 GB model for an
+ * 8 GB machine" and the router of the TurboFieldfare video transcript).  The
+ * workgroups of the launch meet at device-wide barriers instead of kernel
+ * boundaries (two per layer).
+ *   x_io         device fp32 [n_layers + 1][d]: x_io[0] is the input token;
+ *                layer l writes its output (with the residual) to x_io[l + 1]
+ *   norm_w       device fp32 [n_layers][d] or NULL (no RMSNorm)
+ *   router_w     device fp32 [n_layers][E][d];  router_bias [n_layers][E] or NULL
+ *   slot_tables  device int32 [n_layers][E]: layer l's slot per expert (-1 absent)
+ *   arena        layer l's slot s at arena + l*layer_stride + s*slot_stride
+ *                (256-byte aligned; layer_stride >= n_slots * slot_stride)
+ *   topk_idx, topk_w  device [n_layers][k] (out): each layer's choice and weights
+ *   x_next       device fp32 [d] or NULL: x_io[n_layers] rescaled to unit RMS
+ *                (the next decode step's input; may be x_io itself)
+ *   ws           256-byte aligned workspace of
+ *                moe_workspace_size(MOE_CALL_DECODE_LAYERS, n_layers, ...)
+ *                bytes (the T argument counts layers for this call),
+ *                zero-filled before its first use and then passed
+ *                unchanged to every call (it carries the barrier state); calls
+ *                that share a workspace must be stream-ordered.
+ * Requires the device to run all k*f/32 workgroups at once (one per compute
+ * unit is enough); a barrier that does not complete within ~0.25 s sets an
+ * error word instead of hanging: moe_decode_check reports it.
+ * Supported: d <= 3072, f <= 768, E <= 256, k <= 8, k * f / 32 <= 256 and
+ * d <= 16 * k * f / 32; otherwise MOE_ERR_UNSUPPORTED.
+ * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_CAPACITY, MOE_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------- */
+moe_status moe_decode_layers(float* x_io, int32_t n_layers, const float* norm_w, float eps,
+                             const float* router_w, const float* router_bias,
+                             const int32_t* slot_tables, int32_t n_slots, const uint8_t* arena,
+                             int64_t layer_stride, int64_t slot_stride, moe_dims dims,
+                             int32_t* topk_idx, float* topk_w, float* x_next,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Waits for `stream` and reports MOE_ERR_STATE if a moe_decode_layers call on
+ * this workspace hit its barrier time limit (its outputs are then invalid and
+ * the workspace must be zero-filled again). */
+moe_status moe_decode_check(const void* ws, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Shared-path GEMV with bf16 weights: out[t][r] = sum_c W[r][c] * h[t][c].

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_STATE, MOE_ERR_CAPACITY = range(7)
 MOE_PREC_FP32, MOE_PREC_BF16_MFMA, MOE_PREC_F16_MFMA = 0, 1, 2
-MOE_CALL_ROUTE, MOE_CALL_PERMUTE, MOE_CALL_GATEUP, MOE_CALL_DOWN_COMBINE = range(4)
+MOE_CALL_ROUTE, MOE_CALL_PERMUTE, MOE_CALL_GATEUP, MOE_CALL_DOWN_COMBINE, MOE_CALL_DECODE_LAYERS = range(5)
 
 
 class MoeError(RuntimeError):
@@ -69,6 +69,9 @@ _SIGNATURES = {
     "moe_shared_gemv_bf16": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P]),
     "moe_rms_rescale": (ctypes.c_int, [_P, _I32, _I32, _F, _P, _P]),
     "moe_profile_next_launch": (ctypes.c_int, [ctypes.c_int, _P, _P]),
+    "moe_decode_layers": (ctypes.c_int, [_P, _I32, _P, _F, _P, _P, _P, _I32, _P, _I64, _I64, moe_dims, _P, _P, _P,
+                                         _P, _SZ, _P]),
+    "moe_decode_check": (ctypes.c_int, [_P, _P]),
 }
 
 _lib = None
@@ -190,6 +193,20 @@ def moe_shared_gemv_bf16(w, h, T, rows, cols, out, stream=None):
 
 def moe_rms_rescale(x, T, d, eps, out, stream=None):
     _check(lib().moe_rms_rescale(_dev(x, "x"), int(T), int(d), float(eps), _dev(out, "out"), _stream(stream)))
+
+
+def moe_decode_layers(x_io, n_layers, norm_w, eps, router_w, router_bias, slot_tables, n_slots, arena, layer_stride,
+                      slot_stride, dm, topk_idx, topk_w, x_next, ws, stream=None):
+    _check(lib().moe_decode_layers(_dev(x_io, "x_io"), int(n_layers), _dev(norm_w, "norm_w"), float(eps),
+                                   _dev(router_w, "router_w"), _dev(router_bias, "router_bias"),
+                                   _dev(slot_tables, "slot_tables"), int(n_slots), _dev(arena, "arena"),
+                                   int(layer_stride), int(slot_stride), dm, _dev(topk_idx, "topk_idx"),
+                                   _dev(topk_w, "topk_w"), _dev(x_next, "x_next"), _dev(ws, "ws"), _nbytes(ws),
+                                   _stream(stream)))
+
+
+def moe_decode_check(ws, stream=None):
+    _check(lib().moe_decode_check(_dev(ws, "ws"), _stream(stream)))
 
 
 def moe_profile_next_launch(call, start_event, stop_event):

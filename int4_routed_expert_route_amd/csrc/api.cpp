@@ -149,6 +149,8 @@ size_t moe_workspace_size(moe_call call, int32_t T, moe_dims dims, moe_precision
       if (prec == MOE_PREC_BF16_MFMA || prec == MOE_PREC_F16_MFMA)
         return moe::mfma_workspace_bytes((int)call, T, dims.d, dims.f, dims.n_experts, dims.top_k);
       return moe::gemv_workspace_bytes((int)call, T, dims.d, dims.top_k, true);
+    case MOE_CALL_DECODE_LAYERS:  // T = number of layers
+      return moe::decode_fused_workspace_bytes(T, dims.d, dims.f, dims.n_experts, dims.top_k);
   }
   return SIZE_MAX;
 }
@@ -300,8 +302,60 @@ moe_status moe_shared_gemv_bf16(const uint16_t* w, const float* h, int32_t T, in
   return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
 }
 
+static int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus;
+}
+
+moe_status moe_decode_layers(float* x_io, int32_t n_layers, const float* norm_w, float eps,
+                             const float* router_w, const float* router_bias,
+                             const int32_t* slot_tables, int32_t n_slots, const uint8_t* arena,
+                             int64_t layer_stride, int64_t slot_stride, moe_dims dims,
+                             int32_t* topk_idx, float* topk_w, float* x_next,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "moe_decode_layers";
+  if (moe_status s = check_dims(dims)) return s;
+  if (n_layers < 1) return fail(MOE_ERR_ARG, "%s: n_layers=%d", fn, n_layers);
+  CHECK_PTR(x_io); CHECK_PTR(router_w); CHECK_PTR(topk_idx); CHECK_PTR(topk_w); CHECK_PTR(ws);
+  CHECK_ALIGN(x_io); CHECK_ALIGN(norm_w); CHECK_ALIGN(router_w); CHECK_ALIGN(router_bias);
+  CHECK_ALIGN(topk_idx); CHECK_ALIGN(topk_w); CHECK_ALIGN(x_next); CHECK_ALIGN(ws);
+  if (!(eps >= 0.0f)) return fail(MOE_ERR_ARG, "%s: eps must be >= 0", fn);
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(MOE_ERR_ALIGN, "%s: ws must be 256-byte aligned", fn);
+  if (moe_status s = check_slots(fn, slot_tables, n_slots, arena, slot_stride, dims)) return s;
+  if (layer_stride % 256 || layer_stride < (int64_t)n_slots * slot_stride)
+    return fail(MOE_ERR_ARG, "%s: layer_stride=%lld must be a multiple of 256 and >= n_slots * slot_stride", fn,
+                (long long)layer_stride);
+  int G = 0, rpw = 0;
+  if (!moe::decode_fused_supported(dims.d, dims.f, dims.n_experts, dims.top_k, device_cus(), &G, &rpw))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: dims d=%d f=%d E=%d k=%d outside the fused kernel's range", fn, dims.d,
+                dims.f, dims.n_experts, dims.top_k);
+  const size_t need = moe::decode_fused_workspace_bytes(n_layers, dims.d, dims.f, dims.n_experts, dims.top_k);
+  if (ws_bytes < need) return fail(MOE_ERR_CAPACITY, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  const moe::BlobLayout L = moe::blob_layout(dims.d, dims.f);
+  hipError_t e = moe::launch_decode_fused(x_io, n_layers, norm_w, eps, router_w, router_bias, slot_tables, n_slots,
+                                          arena, layer_stride, slot_stride, dims.d, dims.f, dims.n_experts,
+                                          dims.top_k, L.gate_q, L.up_q, L.down_q, L.gate_sb, L.up_sb, L.down_sb,
+                                          topk_idx, topk_w, x_next, ws, G, rpw, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
+}
+
+moe_status moe_decode_check(const void* ws, hipStream_t stream) {
+  const char* fn = "moe_decode_check";
+  CHECK_PTR(ws);
+  uint32_t flag = 0;
+  hipError_t e = hipMemcpyAsync(&flag, reinterpret_cast<const char*>(ws) + moe::kDecodeErrOffset, 4,
+                                hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  if (flag) return fail(MOE_ERR_STATE, "%s: a device-wide barrier timed out", fn);
+  return MOE_OK;
+}
+
 moe_status moe_profile_next_launch(moe_call call, hipEvent_t start, hipEvent_t stop) {
-  if ((int)call < 0 || (int)call > MOE_CALL_DOWN_COMBINE)
+  if ((int)call < 0 || (int)call > MOE_CALL_DECODE_LAYERS)
     return fail(MOE_ERR_ARG, "moe_profile_next_launch: unknown call %d", (int)call);
   g_profile.call = (start && stop) ? (int)call : -1;
   g_profile.start = start;

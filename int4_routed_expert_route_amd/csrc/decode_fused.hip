@@ -1,0 +1,565 @@
+// Batch-1 decode through many routed MoE layers in one persistent launch.
+//
+// One token per step goes through every layer in order: router, softmax over
+// the experts, top-k, the selected experts' int4 gated FFN and the
+// gate-weighted combine ("Optimizing a 14.3 GB model for an 8 GB machine":
+// routed MoE per layer; TurboFieldfare video transcript: the router naming its
+// experts).  The separate calls (moe_route, moe_expert_q4_gateup,
+// moe_expert_q4_down_combine) cost three kernel launches per layer, and at
+// batch 1 each of them is dominated by its fixed start/drain time, not by its
+// ~27 MB of weights.  Here the layers run inside one kernel whose workgroups
+// meet at device-wide barriers, two per layer:
+//
+//   gate/up phase  every workgroup reduces the router partials of the layer
+//                  (written by the previous phase), takes the top-k and the
+//                  weights, stages h = RMSNorm(x) in LDS and computes 32 act
+//                  columns of one selected expert (k * f/32 workgroups);
+//   --- barrier ---
+//   down phase     workgroup g owns d/G output rows: the k experts' down rows,
+//                  the rank-ordered combine with the residual, and the next
+//                  layer's router partials over its rows (sum_i Wr[e][i] w[i] y[i]
+//                  and sum_i y[i]^2), so the next router needs no phase of its own;
+//   --- barrier ---
+//
+// The first layer's router partials come from a prologue phase (+1 barrier).
+// Values shared between workgroups are stored at agent scope (written through
+// to memory) into one region per layer and loaded with plain loads; a barrier
+// arrival follows the acknowledgement of the workgroup's stores.  Weights that
+// a later phase needs and that are known earlier (the down rows of the chosen
+// experts, the next layer's router rows) are copied into LDS while the
+// current phase's loads are in flight.  Every wait is bounded: a stalled barrier (a workgroup
+// that never became resident) sets the error word and the kernel runs out
+// instead of hanging.  The int4 dot products are those of the decode GEMV
+// kernels (fp16-subnormal nibble pairs against fp16 hi/lo activations).
+#include "common.h"
+#include "kernels.h"
+#include "q4_lane.h"
+
+namespace moe {
+
+namespace {
+
+using namespace lane;
+
+constexpr int kFWaves = 8;
+constexpr int kFThreads = kFWaves * kWave;
+// gate/up phase: 8 waves = (gate, up) x 4 blocks of 8 rows; lanes 8 K-parts x 8 rows
+constexpr int kGP = 8, kGR = kWave / kGP, kGGPP = 6, kGGMAX = kGP * kGGPP;  // d/64 <= 48
+constexpr int kActCols = 4 * kGR;                                          // 32 act columns per workgroup
+// down phase: one wave per selected expert; lanes 4 K-parts x 16 rows
+constexpr int kDP = 4, kDR = kWave / kDP, kDGPP = 3, kDGMAX = kDP * kDGPP;  // f/64 <= 12
+constexpr int kDChunks = 2 * kDGMAX;  // 16-byte chunks (32 nibbles) of one down row at most
+constexpr int kMaxE = 256;
+constexpr int kPartBatch = 12;         // float4 loads in flight per thread when summing router partials
+constexpr uint32_t kSpinLimit = 300000u;  // polling rounds (~1 us each) per barrier at most
+
+struct FusedArgs {
+  float* x_io;  // [L+1][d]
+  int L;
+  const float* norm_w;       // [L][d] or null
+  float eps;
+  const float* router_w;     // [L][E][d]
+  const float* router_bias;  // [L][E] or null
+  const int32_t* slot_tables;  // [L][E]
+  int n_slots;
+  const uint8_t* arena;
+  int64_t layer_stride, slot_stride;
+  int d, f, E, k;
+  int64_t off_gq, off_uq, off_dq, off_gsb, off_usb, off_dsb;
+  int32_t* topk_idx;  // [L][k]
+  float* topk_w;      // [L][k]
+  float* x_next;      // [d] or null
+  uint64_t* sync;     // [0] last barrier sequence number of the previous launch
+  uint32_t* err;
+  uint32_t* flags;    // [G] barrier arrival flags (sequence numbers)
+  // Per-layer regions, each starting on its own 256-byte boundary (act_ls,
+  // part_ls, ss_ls floats apart): a cache line read in one layer never holds
+  // values that another XCD writes later in the launch.
+  float* act;    // [L][act_ls]: [k][f] act rows of the chosen experts
+  float* part;   // [L][part_ls]: [E][G] router partials of each layer's input
+  float* sumsq;  // [L+1][ss_ls]: [G] partial sums of squares of each layer's input (and of the last output)
+  int act_ls, part_ls, ss_ls;
+  int G, rpw;    // workgroups, down rows per workgroup (a multiple of 4, at most 16)
+  int nck_g, nck_d;
+};
+
+constexpr int kRsrcWord3F = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3F);
+}
+// Plain (L2-cached) loads of values written earlier in this launch by other
+// workgroups: every such buffer has one region per layer, so no address is
+// read before its last write in a launch, and the first read on an XCD fetches
+// the written-through line from memory.
+__device__ __forceinline__ float ldn(__amdgpu_buffer_rsrc_t r, int idx) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, idx * 4, 0, 0));
+}
+__device__ __forceinline__ float4 ldn4(__amdgpu_buffer_rsrc_t r, int idx) {  // idx % 4 == 0
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, idx * 4, 0, 0));
+}
+__device__ __forceinline__ void st_c(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ lds_ptr_t to_lds(void* p) { return (lds_ptr_t)(p); }
+
+// Threads that share one expert in the sums over experts (E <= 256).
+__device__ __forceinline__ int threads_per_expert(int E) { return E <= 64 ? 8 : (E <= 128 ? 4 : 2); }
+
+// Device-wide barrier with sequence number `seq` (it grows across launches;
+// compared modulo 2^32).  Each workgroup publishes its arrival in its own
+// flag word with a write-through store; wave 0 of every workgroup then reads
+// all G flags at once with coherent (sc1) loads until none is behind.  No
+// read-modify-write: atomics on one shared counter serialise at the memory
+// side (~15 ns per arrival), flags cost one store and one round of loads.
+__device__ __forceinline__ void grid_sync(const FusedArgs& a, uint32_t seq) {
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores (and LDS copies) are complete
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    if (lane == 0) __hip_atomic_store(a.flags + blockIdx.x, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t* p0 = a.flags + min(lane, a.G - 1);
+    const uint32_t* p1 = a.flags + min(lane + kWave, a.G - 1);
+    const uint32_t* p2 = a.flags + min(lane + 2 * kWave, a.G - 1);
+    const uint32_t* p3 = a.flags + min(lane + 3 * kWave, a.G - 1);
+    uint32_t spins = 0;
+    while (true) {
+      uint32_t v0, v1, v2, v3;
+      asm volatile(
+          "global_load_dword %0, %4, off sc1\n\t"
+          "global_load_dword %1, %5, off sc1\n\t"
+          "global_load_dword %2, %6, off sc1\n\t"
+          "global_load_dword %3, %7, off sc1\n\t"
+          "s_waitcnt vmcnt(0)"
+          : "=v"(v0), "=v"(v1), "=v"(v2), "=v"(v3)
+          : "v"(p0), "v"(p1), "v"(p2), "v"(p3)
+          : "memory");
+      const bool behind = (int32_t)(v0 - seq) < 0 || (int32_t)(v1 - seq) < 0 || (int32_t)(v2 - seq) < 0 ||
+                          (int32_t)(v3 - seq) < 0;
+      if (!__any(behind)) break;
+      if (++spins > kSpinLimit) {
+        if (lane == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
+// Copies into LDS (no registers held while in flight): router rows
+// [r0, r0 + 16) of every expert of `layer` into rw[e*4 + 0..3] (float4
+// units) and the norm weight over the same rows into rnw[0..3].  Rows past d
+// read a clamped address; the values that use them are masked.
+__device__ __forceinline__ void router_rows_to_lds(const FusedArgs& a, int t, int layer, int r0, float4* rw,
+                                                   float4* rnw) {
+  const int wave = __builtin_amdgcn_readfirstlane(t / kWave), lane = t % kWave;
+  const __amdgpu_buffer_rsrc_t r = rsrc_of(a.router_w + (int64_t)layer * a.E * a.d, (int64_t)a.E * a.d * 4);
+  const int row = min(r0 + 4 * (lane % 4), a.d - 4);
+  for (int n = wave; n * 16 < a.E; n += kFWaves) {
+    const int e = min(n * 16 + lane / 4, a.E - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(&rw[n * kWave]), 16, (e * a.d + row) * 4, 0, 0, 0);
+  }
+  if (a.norm_w && wave == kFWaves - 1) {
+    const __amdgpu_buffer_rsrc_t rn = rsrc_of(a.norm_w + (int64_t)layer * a.d, (int64_t)a.d * 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rn, to_lds(rnw), 16, min(r0 + 4 * min(lane, 3), a.d - 4) * 4, 0, 0, 0);
+  }
+}
+
+// Down rows [r0, r0 + nr) of one expert blob into LDS: 16-byte chunk c of row
+// r at dq[c*16 + r], (scale, bias) word of group i of row r at dsb[i*16 + r].
+// Called by one whole wave; nr >= 1.
+__device__ __forceinline__ void down_rows_to_lds(const FusedArgs& a, int t, const uint8_t* blob, int r0, int nr,
+                                                 uint4* dq, uint32_t* dsb) {
+  const int lane = t % kWave;
+  const int Gf = a.f / kGroup;
+  const __amdgpu_buffer_rsrc_t r = rsrc_of(blob, a.slot_stride);
+  const int row = r0 + min(lane % kDR, nr - 1);
+  const int tile = row / kTileRows, trow = row % kTileRows;
+  const int qb = (int)(a.off_dq + (int64_t)tile * (kTileRows * a.f / 2)) + trow * 16;
+  const int sb = (int)(a.off_dsb + (int64_t)tile * (kTileRows * Gf * 4)) + trow * 4;
+  for (int n = 0; n * 4 < 2 * Gf; ++n) {
+    const int c = min(n * 4 + lane / kDR, 2 * Gf - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(&dq[n * kWave]), 16, qb + c * (kTileRows * 16), 0, 0, 0);
+  }
+  for (int n = 0; n * 4 < Gf; ++n) {
+    const int gi = min(n * 4 + lane / kDR, Gf - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(&dsb[n * kWave]), 4, sb + gi * (kTileRows * 4), 0, 0, 0);
+  }
+}
+
+// Router partials of `layer` over this workgroup's rows, from the router rows
+// in LDS and z = w * y (w the norm weight, 1 without one; z = 0 past the
+// rows): part[e][g] = sum_i Wr[e][r0 + i] * z[i], plus sumsq[g] = sum_i y[i]^2.
+// Fixed summation order, the same in every launch.
+__device__ __forceinline__ void write_partials(const FusedArgs& a, int t, int layer, const float4* rw, const float* z,
+                                               const float* y) {
+  const int g = blockIdx.x;
+  if (layer < a.L) {
+    const int tq = threads_per_expert(a.E), rpt = kDR / tq;
+    const int e = t / tq, q = t % tq;
+    float s = 0.0f;
+    if (e < a.E) {
+      const float* w = reinterpret_cast<const float*>(rw) + e * kDR + q * rpt;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < rpt) s = fmaf(w[i], z[q * rpt + i], s);
+    }
+    for (int o = 1; o < tq; o <<= 1) s += __shfl_xor(s, o, kWave);
+    if (e < a.E && q == 0) st_c(a.part + (int64_t)layer * a.part_ls + e * a.G + g, s);
+  }
+  if (t < kWave) {
+    const float v = t < kDR ? y[t] : 0.0f;
+    const float ss = wave_sum(v * v);
+    if (t == 0) st_c(a.sumsq + (int64_t)layer * a.ss_ls + g, ss);
+  }
+}
+
+__global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
+  __shared__ XRow<kGP, kGGMAX> xh;             // h of the current layer (gate/up phase)
+  __shared__ XRow<kDP, kDGMAX> xa[kFWaves];    // act rows of the selected experts (down phase)
+  __shared__ uint4 s_dq[kFWaves][kDChunks * kDR];    // down rows of each selected expert
+  __shared__ uint32_t s_dsb[kFWaves][kDGMAX * kDR];  // and their (scale, bias) words
+  __shared__ float4 s_rw[kMaxE * kDR / 4];     // next layer's router rows over this workgroup's rows
+  __shared__ float4 s_rnw[kWave];              // next layer's norm weight over the rows (first 4 used)
+  __shared__ float4 s_logit4[kMaxE / 4 + 1];   // logits, padded with -inf to a multiple of 4
+  __shared__ int s_table[kMaxE];               // this layer's slot per expert
+  __shared__ float s_val[16];
+  __shared__ float s_inv;
+  __shared__ int s_idx[16];
+  __shared__ float s_w[16];
+  __shared__ float s_g[4][kGR];                // gate values of the 32 act columns
+  __shared__ float s_o[kFWaves][kDR];          // down outputs per expert rank
+  __shared__ float s_y[kDR], s_z[kDR];         // this workgroup's output rows, and norm weight * rows
+  __shared__ uint32_t s_base;
+  float* s_logit = reinterpret_cast<float*>(s_logit4);
+  const int t0 = threadIdx.x;
+  const int g = blockIdx.x;
+  const int t = t0, lane = t0 % kWave;
+  if (t == 0) s_base = (uint32_t)__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (t < 4) s_logit[a.E + t] = -INFINITY;
+  const int Gd = a.d / kGroup, Gf = a.f / kGroup;
+  const int r0 = g * a.rpw, nr = max(0, min(a.rpw, a.d - r0));
+  const __amdgpu_buffer_rsrc_t rX = rsrc_of(a.x_io, (int64_t)(a.L + 1) * a.d * 4);
+  const __amdgpu_buffer_rsrc_t rAct = rsrc_of(a.act, (int64_t)a.L * a.act_ls * 4);
+  const __amdgpu_buffer_rsrc_t rPart = rsrc_of(a.part, (int64_t)a.L * a.part_ls * 4);
+  const __amdgpu_buffer_rsrc_t rSS = rsrc_of(a.sumsq, (int64_t)(a.L + 1) * a.ss_ls * 4);
+  const int tq = threads_per_expert(a.E);
+
+  // ---- prologue: router partials of layer 0 over this workgroup's rows of x_io[0]
+  if (t < kDR) s_y[t] = t < nr ? ldn(rX, r0 + t) : 0.0f;
+  router_rows_to_lds(a, t, 0, r0, s_rw, s_rnw);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const uint32_t base = s_base;
+  int nbar = 0;
+  if (t < kDR) s_z[t] = t < nr ? s_y[t] * (a.norm_w ? reinterpret_cast<const float*>(s_rnw)[t] : 1.0f) : 0.0f;
+  __syncthreads();
+  write_partials(a, t, 0, s_rw, s_z, s_y);
+  grid_sync(a, base + (uint32_t)++nbar);
+
+  for (int l = 0; l < a.L; ++l) {
+    // Thread-derived indices are recomputed from an opaque copy of the thread
+    // id every layer: hoisted out of the loop they would hold hundreds of
+    // registers for the whole launch.
+    int tid = t0;
+    asm volatile("" : "+v"(tid));
+    const int t = tid, lane = t % kWave, wave = __builtin_amdgcn_readfirstlane(t / kWave);
+    const int xo = l * a.d;  // x = x_io[l]
+    // ================= gate/up phase =================
+    // Everything that does not depend on the routing goes out at once: the
+    // slot table, the router bias, the sums of squares, the router partials,
+    // then x and the norm weight.
+    if (t < a.E) s_table[t] = a.slot_tables[(int64_t)l * a.E + t];
+    const int e = t / tq, q = t % tq;
+    const float bias = (a.router_bias && e < a.E) ? a.router_bias[(int64_t)l * a.E + e] : 0.0f;
+    float ssv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ssv[c] = ldn(rSS, l * a.ss_ls + min(lane + c * kWave, a.G - 1));
+    float s = 0.0f;
+    {
+      // tq consecutive threads per expert each sum a contiguous share of the G
+      // partials, then combine in a fixed order (the same in every workgroup)
+      const bool vec = a.G % 4 == 0;
+      const int share = vec ? ((a.G + tq - 1) / tq + 3) / 4 * 4 : (a.G + tq - 1) / tq;
+      if (e < a.E) {
+        const int i0 = min(a.G, q * share), i1 = min(a.G, i0 + share);
+        const int pb = l * a.part_ls + e * a.G;
+        if (vec) {
+          for (int b = i0; b < i1; b += 4 * kPartBatch) {
+            float4 v[kPartBatch];
+#pragma unroll
+            for (int c = 0; c < kPartBatch; ++c) v[c] = ldn4(rPart, pb + min(b + 4 * c, i1 - 4));
+#pragma unroll
+            for (int c = 0; c < kPartBatch; ++c)
+              if (b + 4 * c < i1) s += (v[c].x + v[c].y) + (v[c].z + v[c].w);
+          }
+        } else {
+#pragma unroll 8
+          for (int i = i0; i < i1; ++i) s += ldn(rPart, pb + i);
+        }
+      }
+    }
+    constexpr int NPASSG = (8 * kGGMAX + kFThreads - 1) / kFThreads;
+    StageRegs<NPASSG> xr, nwr;
+    const float* nw = a.norm_w ? a.norm_w + (int64_t)l * a.d : nullptr;
+#pragma unroll
+    for (int ps = 0; ps < NPASSG; ++ps) {
+      const int wi = min(ps * kFThreads + t, 8 * Gd - 1);
+      xr.a[ps] = ldn4(rX, xo + wi * 8);
+      xr.b[ps] = ldn4(rX, xo + wi * 8 + 4);
+      nwr.a[ps] = nw ? *reinterpret_cast<const float4*>(nw + wi * 8) : make_float4(1.f, 1.f, 1.f, 1.f);
+      nwr.b[ps] = nw ? *reinterpret_cast<const float4*>(nw + wi * 8 + 4) : make_float4(1.f, 1.f, 1.f, 1.f);
+    }
+    for (int o = 1; o < tq; o <<= 1) s += __shfl_xor(s, o, kWave);
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ss += lane + c * kWave < a.G ? ssv[c] : 0.0f;
+    ss = wave_sum(ss);
+    const float inv = a.norm_w ? 1.0f / sqrtf(ss / (float)a.d + a.eps) : 1.0f;
+    if (e < a.E && q == 0) s_logit[e] = s * inv + bias;
+    __syncthreads();
+    {
+      // rank of expert e = experts with a larger logit, or an equal one and a
+      // lower id (tq threads per expert, each over a quarter/half/eighth)
+      int beats = 0;
+      float v = 0.0f;
+      if (e < a.E) {
+        v = s_logit[e];
+        const int span = ((a.E + tq - 1) / tq + 3) / 4 * 4, j0 = q * span, j1 = min(a.E, j0 + span);
+#pragma unroll 8
+        for (int jj = j0; jj < j1; jj += 4) {
+          const float4 u = s_logit4[jj / 4];
+          beats += (u.x > v || (u.x == v && jj < e)) ? 1 : 0;
+          beats += (u.y > v || (u.y == v && jj + 1 < e)) ? 1 : 0;
+          beats += (u.z > v || (u.z == v && jj + 2 < e)) ? 1 : 0;
+          beats += (u.w > v || (u.w == v && jj + 3 < e)) ? 1 : 0;
+        }
+      }
+      for (int o = 1; o < tq; o <<= 1) beats += __shfl_xor(beats, o, kWave);
+      if (e < a.E && q == 0 && beats < a.k) {
+        s_idx[beats] = e;
+        s_val[beats] = v;
+      }
+    }
+    __syncthreads();
+    // this workgroup's expert (rank jr) and act columns [c0, c0 + 32)
+    const int jr = g / (a.f / kActCols);
+    const int c0 = (g % (a.f / kActCols)) * kActCols;
+    const uint8_t* larena = a.arena + (int64_t)l * a.layer_stride;
+    const int layer_expert = s_idx[jr];
+    const int slot = (layer_expert >= 0 && layer_expert < a.E) ? s_table[layer_expert] : -1;
+    const bool ok = slot >= 0 && slot < a.n_slots;
+    const uint8_t* blob = larena + (ok ? (int64_t)slot * a.slot_stride : 0);
+    const int mat = wave / 4, rb = wave % 4;
+    const int j = lane / kGR, r = lane % kGR;
+    const Part pt = part_of<kGP>(j, Gd);
+    const int row = c0 + rb * kGR + r;
+    LaneSlice<kGGPP> w;
+    {
+      const int64_t tile = row / kTileRows;
+      const int trow = row % kTileRows;
+      load_lane<kGGPP>(w, blob + (mat ? a.off_uq : a.off_gq) + tile * (kTileRows * a.d / 2) + trow * 16,
+                       blob + (mat ? a.off_usb : a.off_gsb) + tile * (kTileRows * Gd * 4) + trow * 4, pt, Gd);
+    }
+    // the down phase's expert of this wave (rank = wave)
+    const int e2 = wave < a.k ? s_idx[wave] : -1;
+    const int slot2 = (e2 >= 0 && e2 < a.E) ? s_table[e2] : -1;
+    const uint8_t* blob2 = larena + ((slot2 >= 0 && slot2 < a.n_slots) ? (int64_t)slot2 * a.slot_stride : 0);
+    if (wave == 0) {
+      // weights: softmax over the chosen logits (largest first)
+      const float m = s_val[0];
+      const float ex = lane < a.k ? expf(s_val[lane < a.k ? lane : 0] - m) : 0.0f;
+      const float sum = wave_sum(ex);
+      if (lane < a.k) {
+        s_w[lane] = ex / sum;
+        if (g == 0) {
+          a.topk_idx[(int64_t)l * a.k + lane] = s_idx[lane];
+          a.topk_w[(int64_t)l * a.k + lane] = ex / sum;
+        }
+      }
+    }
+    {
+      // h = x * inv * w in 8-column words: thread t stages word t
+      StageRegs<NPASSG> sr;
+#pragma unroll
+      for (int ps = 0; ps < NPASSG; ++ps) {
+        const float4 xa4 = xr.a[ps], xb4 = xr.b[ps], na = nwr.a[ps], nb = nwr.b[ps];
+        sr.a[ps] = make_float4(xa4.x * inv * na.x, xa4.y * inv * na.y, xa4.z * inv * na.z, xa4.w * inv * na.w);
+        sr.b[ps] = make_float4(xb4.x * inv * nb.x, xb4.y * inv * nb.y, xb4.z * inv * nb.z, xb4.w * inv * nb.w);
+      }
+      stage_store<kGP, kGGMAX, NPASSG>(xh, sr, Gd, t, kFThreads);
+    }
+    // the down phase's weights and the next layer's router rows go to LDS
+    // while the gate/up weights are in flight
+    if (wave < a.k && nr > 0) down_rows_to_lds(a, t, blob2, r0, nr, s_dq[wave], s_dsb[wave]);
+    if (l + 1 < a.L) router_rows_to_lds(a, t, l + 1, r0, s_rw, s_rnw);
+    __syncthreads();
+    {
+      float v = lane_dot<kGP, kGGPP, kGGMAX>(w, xh, j, pt, Gd, a.nck_g);
+      if (!ok) v = f32_nan();
+      if (mat == 0 && j == 0) s_g[rb][r] = v;
+      __syncthreads();
+      if (mat == 1 && j == 0) st_c(a.act + (int64_t)l * a.act_ls + jr * a.f + row, gelu_tanh(s_g[rb][r]) * v);
+    }
+    grid_sync(a, base + (uint32_t)++nbar);
+
+    // ================= down phase =================
+    {
+      const int jw = wave;  // expert rank of this wave
+      const bool wave_on = jw < a.k && nr > 0;
+      const int jd = lane / kDR, rd = lane % kDR;
+      const Part pd = part_of<kDP>(jd, Gf);
+      const int ed = wave_on ? s_idx[jw] : -1;
+      const int sd = (ed >= 0 && ed < a.E) ? s_table[ed] : -1;
+      const bool ok2 = sd >= 0 && sd < a.n_slots;
+      constexpr int NPASS = (8 * kDGMAX + kWave - 1) / kWave;
+      StageRegs<NPASS> sr;
+      if (wave_on) {
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps) {
+          const int wi = min(ps * kWave + lane, 8 * Gf - 1);
+          sr.a[ps] = ldn4(rAct, l * a.act_ls + jw * a.f + wi * 8);
+          sr.b[ps] = ldn4(rAct, l * a.act_ls + jw * a.f + wi * 8 + 4);
+        }
+      }
+      const float xres = (t < nr) ? ldn(rX, xo + r0 + t) : 0.0f;
+      LaneSlice<kDGPP> wd;
+      if (wave_on) {
+#pragma unroll
+        for (int i = 0; i < kDGPP; ++i) {
+          const int gi = max(0, min(pd.g0 + min(i, pd.ng - 1), Gf - 1));
+          wd.sb[i] = s_dsb[jw][gi * kDR + rd];
+        }
+#pragma unroll
+        for (int i = 0; i < 2 * kDGPP; ++i) {
+          const int c = max(0, min(2 * pd.g0 + min(i, 2 * pd.ng - 1), 2 * Gf - 1));
+          wd.q[i] = s_dq[jw][c * kDR + rd];
+        }
+        stage_store<kDP, kDGMAX, NPASS>(xa[jw], sr, Gf, lane, kWave);
+      }
+      __syncthreads();
+      if (wave_on) {
+        float v = lane_dot<kDP, kDGPP, kDGMAX>(wd, xa[jw], jd, pd, Gf, a.nck_d);
+        if (!ok2) v = f32_nan();
+        if (jd == 0) s_o[jw][rd] = v;
+      }
+      __syncthreads();
+      if (t < kDR) {
+        float y = 0.0f, z = 0.0f;
+        if (t < nr) {
+          y = xres;
+          for (int jj = 0; jj < a.k; ++jj) y = fmaf(s_w[jj], s_o[jj][t], y);
+          st_c(a.x_io + (int64_t)(l + 1) * a.d + r0 + t, y);
+          z = y * ((a.norm_w && l + 1 < a.L) ? reinterpret_cast<const float*>(s_rnw)[t] : 1.0f);
+        }
+        s_y[t] = y;
+        s_z[t] = z;
+      }
+      __syncthreads();
+      write_partials(a, t, l + 1, s_rw, s_z, s_y);
+    }
+    grid_sync(a, base + (uint32_t)++nbar);
+  }
+
+  // unit-RMS rescale of the last output for the next decode step
+  if (a.x_next) {
+    float ss = 0.0f;
+    for (int i = lane; i < a.G; i += kWave) ss += ldn(rSS, a.L * a.ss_ls + i);
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)a.d + a.eps);
+    if (t < nr) a.x_next[r0 + t] = s_y[t] * inv;
+  }
+  // the next launch on this workspace continues the barrier sequence (every
+  // workgroup read it before the first barrier)
+  if (g == 0 && t == 0) __hip_atomic_store(a.sync, (uint64_t)(base + (uint32_t)nbar), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ host side
+
+bool decode_fused_supported(int d, int f, int E, int k, int cus, int* G_out, int* rpw_out) {
+  if (d % kGroup || f % kGroup || d / kGroup > kGGMAX || f / kGroup > kDGMAX || E > kMaxE || k > kFWaves)
+    return false;
+  const int G = k * (f / kActCols);
+  const int rpw = ((d + G - 1) / G + 3) / 4 * 4;  // router rows go to LDS in 16-byte pieces
+  if (G > cus || G > 256 || rpw > kDR) return false;
+  *G_out = G;
+  *rpw_out = rpw;
+  return true;
+}
+
+namespace {
+struct FusedLayout {
+  int act_ls, part_ls, ss_ls;  // floats per layer region, multiples of 64 (256 bytes)
+  int64_t flags_off, act_off, part_off, ss_off, bytes;
+};
+FusedLayout fused_layout(int L, int f, int E, int k) {
+  const int G = k * (f / kActCols);
+  auto r64 = [](int64_t n) { return (int)((n + 63) / 64 * 64); };
+  FusedLayout o;
+  o.act_ls = r64((int64_t)k * f);
+  o.part_ls = r64((int64_t)E * G);
+  o.ss_ls = r64(G);
+  o.flags_off = 512;
+  o.act_off = 512 + 1024;
+  o.part_off = o.act_off + (int64_t)L * o.act_ls * 4;
+  o.ss_off = o.part_off + (int64_t)L * o.part_ls * 4;
+  o.bytes = o.ss_off + (int64_t)(L + 1) * o.ss_ls * 4;
+  return o;
+}
+}  // namespace
+
+size_t decode_fused_workspace_bytes(int L, int d, int f, int E, int k) {
+  (void)d;
+  return (size_t)fused_layout(L, f, E, k).bytes;
+}
+
+hipError_t launch_decode_fused(float* x_io, int L, const float* norm_w, float eps, const float* router_w,
+                               const float* router_bias, const int32_t* slot_tables, int n_slots,
+                               const uint8_t* arena, int64_t layer_stride, int64_t slot_stride, int d, int f, int E,
+                               int k, int64_t off_gq, int64_t off_uq, int64_t off_dq, int64_t off_gsb, int64_t off_usb,
+                               int64_t off_dsb, int32_t* topk_idx, float* topk_w, float* x_next, void* ws, int G,
+                               int rpw, hipStream_t s) {
+  FusedArgs a{};
+  a.x_io = x_io;
+  a.L = L;
+  a.norm_w = norm_w;
+  a.eps = eps;
+  a.router_w = router_w;
+  a.router_bias = router_bias;
+  a.slot_tables = slot_tables;
+  a.n_slots = n_slots;
+  a.arena = arena;
+  a.layer_stride = layer_stride;
+  a.slot_stride = slot_stride;
+  a.d = d; a.f = f; a.E = E; a.k = k;
+  a.off_gq = off_gq; a.off_uq = off_uq; a.off_dq = off_dq;
+  a.off_gsb = off_gsb; a.off_usb = off_usb; a.off_dsb = off_dsb;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.x_next = x_next;
+  char* c = reinterpret_cast<char*>(ws);
+  a.sync = reinterpret_cast<uint64_t*>(c);
+  a.err = reinterpret_cast<uint32_t*>(c + kDecodeErrOffset);
+  const FusedLayout lay = fused_layout(L, f, E, k);
+  a.flags = reinterpret_cast<uint32_t*>(c + lay.flags_off);
+  a.act = reinterpret_cast<float*>(c + lay.act_off);
+  a.part = reinterpret_cast<float*>(c + lay.part_off);
+  a.sumsq = reinterpret_cast<float*>(c + lay.ss_off);
+  a.act_ls = lay.act_ls;
+  a.part_ls = lay.part_ls;
+  a.ss_ls = lay.ss_ls;
+  a.G = G;
+  a.rpw = rpw;
+  a.nck_g = 2 * kGGPP;
+  a.nck_d = 2 * kDGPP;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  take_profile_events(MOE_CALL_DECODE_LAYERS, &ev0, &ev1);
+  launch_maybe_timed(k_decode_fused, G, kFThreads, s, ev0, ev1, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

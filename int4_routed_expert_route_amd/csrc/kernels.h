@@ -83,6 +83,17 @@ hipError_t launch_down_mfma(bool f16, const void* act_in, const int32_t* offsets
                             int T, int d, int f, int E, int k, int64_t off_q, int64_t off_sb, const float* topk_w,
                             const float* residual, float* y, void* ws, hipStream_t s);
 
+// ---- fused batch-1 decode through many layers (decode_fused.hip)
+bool decode_fused_supported(int d, int f, int E, int k, int cus, int* G, int* rpw);
+size_t decode_fused_workspace_bytes(int L, int d, int f, int E, int k);
+constexpr int kDecodeErrOffset = 384;  // byte offset of the error word in the workspace
+hipError_t launch_decode_fused(float* x_io, int L, const float* norm_w, float eps, const float* router_w,
+                               const float* router_bias, const int32_t* slot_tables, int n_slots,
+                               const uint8_t* arena, int64_t layer_stride, int64_t slot_stride, int d, int f, int E,
+                               int k, int64_t off_gq, int64_t off_uq, int64_t off_dq, int64_t off_gsb, int64_t off_usb,
+                               int64_t off_dsb, int32_t* topk_idx, float* topk_w, float* x_next, void* ws, int G,
+                               int rpw, hipStream_t s);
+
 // ---- bf16 shared-path GEMV (shared_gemv.hip)
 hipError_t launch_shared_gemv_bf16(const uint16_t* w, const float* h, int T, int rows, int cols,
                                    float* out, hipStream_t s);
