@@ -19,15 +19,16 @@
 //    64 consecutive rows sit side by side, so each 128-bit load instruction
 //    reads P runs of R*16 bytes.  Every lane issues all of its nibble and
 //    (scale, bias) loads before it computes anything.
-//  * Dequant without converts: a nibble pair masked into the two halves of a
-//    32-bit word is a pair of fp16 subnormals q * 2^-24, exactly; v_dot2_f32_f16
-//    multiplies it with an activation pair and accumulates in fp32.  The 2^24
-//    is folded into the group scale.  Activations are split into fp16 hi + lo
-//    pairs (x = hi + lo to ~22 bits) after scaling each 64-column group by a
-//    power of two that puts its largest magnitude in [2^14, 2^15), so the
-//    result keeps fp32-grade accuracy: 7 bit operations and 8 dot2 per 8 weights.
-//  * Group-factored dequant: sum_c (s q_c + b) x_c = s * sum_c q_c x_c + b * sum_c x_c.
-//  * The activation row is staged once per workgroup in LDS as hi/lo pairs,
+//  * Dequant without converts, in exact integer arithmetic: each 64-column
+//    group of the activation row is scaled by a power of two that puts its
+//    largest magnitude in [2^13, 2^14) and rounded to integers (16-bit fixed
+//    point per group, relative error <= 2^-14 of the group maximum), held as
+//    four balanced base-16 digits.  v_dot8_i32_i4 multiplies eight weight
+//    nibbles (xor 8 makes them the signed q - 8) with eight digits at once, so
+//    8 weights cost 1 xor and 4 dot8: exact int32 sums per group.
+//  * Group-factored dequant: sum_c (s q_c + b) x_c = s * 2^e * sum_c (q_c - 8) x_c
+//    + (b + 8 s) * sum_c x_c, with the fp32 group sum for the second term.
+//  * The activation row is staged once per workgroup in LDS as digit words,
 //    each K-part at its own bank offset so the parts' broadcast reads do not
 //    conflict; group sums and group exponents are reduced during the staging.
 //  * K-parts are summed with cross-lane shuffles; gate and up (two waves of

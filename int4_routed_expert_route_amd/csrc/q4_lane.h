@@ -1,6 +1,8 @@
 // Lane-level pieces of the int4 dequant-GEMV shared by the decode kernels:
-// nibble pairs as fp16 subnormals dotted with fp16 hi/lo activation pairs,
-// K-part bookkeeping, per-lane weight loads and the LDS activation row.
+// exact integer dot products of the weight nibbles with activations held as
+// 16-bit fixed point per group of 64 (a power-of-two scale per group, four
+// balanced base-16 digits per value), K-part bookkeeping, per-lane weight
+// loads and the LDS activation row.
 #pragma once
 
 #include "common.h"
@@ -8,31 +10,17 @@
 namespace moe {
 namespace lane {
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2(uint32_t q, uint32_t x, float acc) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q), __builtin_bit_cast(half2_t, x), acc, false);
-}
-
-// Dot of the 8 nibbles of one 32-bit word (columns 0..7, even column = low
-// nibble) with 8 activations given as 4 hi and 4 lo fp16 pairs ordered
-// (x0,x4) (x1,x5) (x2,x6) (x3,x7).  Result scaled by 2^-24.
-__device__ __forceinline__ float dot8(uint32_t w, const uint4 xh, const uint4 xl, float acc) {
-  const uint32_t m = 0x000F000Fu;
-  uint32_t w4 = w >> 4;
-  const uint32_t p0 = w & m;           // columns 0, 4
-  const uint32_t p1 = w4 & m;          // columns 1, 5
-  const uint32_t p2 = (w >> 8) & m;    // columns 2, 6
-  const uint32_t p3 = (w4 >> 8) & m;   // columns 3, 7
-  acc = dot2(p0, xh.x, acc);
-  acc = dot2(p1, xh.y, acc);
-  acc = dot2(p2, xh.z, acc);
-  acc = dot2(p3, xh.w, acc);
-  acc = dot2(p0, xl.x, acc);
-  acc = dot2(p1, xl.y, acc);
-  acc = dot2(p2, xl.z, acc);
-  acc = dot2(p3, xl.w, acc);
-  return acc;
+// Eight weight nibbles (column i in bits 4i..4i+3 of w, unsigned 0..15)
+// against eight activations given as four words of balanced base-16 digits
+// (digit k of column i in bits 4i..4i+3 of word k, each in [-8, 7]).  The xor
+// turns nibble q into the signed nibble q - 8, so a[k] += sum_i (q_i - 8) *
+// digit_k(x_i); every product and sum is an exact integer.
+__device__ __forceinline__ void dot8d(uint32_t w, const uint4 xd, int& a0, int& a1, int& a2, int& a3) {
+  const int ws = (int)(w ^ 0x88888888u);
+  a0 = __builtin_amdgcn_sdot8(ws, (int)xd.x, a0, false);
+  a1 = __builtin_amdgcn_sdot8(ws, (int)xd.y, a1, false);
+  a2 = __builtin_amdgcn_sdot8(ws, (int)xd.z, a2, false);
+  a3 = __builtin_amdgcn_sdot8(ws, (int)xd.w, a3, false);
 }
 
 // K-part j of a row with G groups split over P parts: groups [g0, g0 + ng).
@@ -80,13 +68,14 @@ __device__ __forceinline__ void load_lane(LaneSlice<GPP>& s, const uint8_t* q, c
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// LDS image of one activation row of G <= GMAX groups: per 8-column word 4 hi
-// and 4 lo fp16 pairs (32 bytes); part j's words start 16*j bytes later than
-// packed (bank offset); per group its fp32 sum and its power-of-two scale.
+// LDS image of one activation row of G <= GMAX groups: per 8-column word its
+// four digit words (16 bytes); part j's words start 16*j bytes later than
+// packed (bank offset); per group its fp32 sum and its power-of-two scale
+// (NaN when the group holds a non-finite value, so that it propagates).
 template <int P, int GMAX>
 struct XRow {
   static constexpr int kWords = GMAX * 8;
-  uint4 v[2 * kWords + 2 * P];  // 16-byte units: word w of part j at 2*w + j
+  uint4 v[kWords + P];  // word w (group w / 8) of part j at w + j
   float gsum[GMAX];
   float gscale[GMAX];
 };
@@ -132,82 +121,88 @@ __device__ __forceinline__ void stage_store(XRow<P, GMAX>& dst, const StageRegs<
       s += __shfl_xor(s, o, kWave);
       mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
     }
-    // 2^-e with max * 2^-e in [2^14, 2^15) (1 for zero or non-finite maxima)
+    // 2^-e with max * 2^-e in [2^13, 2^14): every value rounds to an integer
+    // of magnitude <= 2^14, which four balanced base-16 digits hold
+    const bool finite = mx < INFINITY && fabsf(s) < INFINITY;
     int e = 0;
-    if (mx > 0.0f && mx < INFINITY) e = __builtin_amdgcn_frexp_expf(mx) - 15;
-    const float down = __builtin_ldexpf(1.0f, -e);
+    if (finite && mx > 0.0f) e = __builtin_amdgcn_frexp_expf(mx) - 14;
+    const float down = finite ? __builtin_ldexpf(1.0f, -e) : 0.0f;
     if (live) {
-      const float xs[8] = {a.x * down, a.y * down, a.z * down, a.w * down,
-                           b.x * down, b.y * down, b.z * down, b.w * down};
-      uint32_t hi[4], lo[4];
+      // balanced digits of v are the base-16 digits of u = v + 0x8888 minus
+      // 8, and a nibble n - 8 in two's complement is n ^ 8
+      const float xs[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint32_t dw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const _Float16 h0 = (_Float16)xs[i], h1 = (_Float16)xs[i + 4];
-        const _Float16 l0 = (_Float16)(xs[i] - (float)h0), l1 = (_Float16)(xs[i + 4] - (float)h1);
-        hi[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-        lo[i] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t u = (uint32_t)((int)__builtin_rintf(xs[i] * down) + 0x8888);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dw[k] |= __builtin_amdgcn_ubfe(u, 4 * k, 4) << (4 * i);
       }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dw[k] ^= 0x88888888u;
       const int g = wi / 8;
       const int j = part_of_group<P>(g, G);
-      dst.v[2 * wi + j] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      dst.v[2 * wi + j + 1] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      dst.v[wi + j] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
       if ((wi % 8) == 0) {
         dst.gsum[g] = s;
-        dst.gscale[g] = __builtin_ldexpf(16777216.0f, e);  // 2^24 * 2^e
+        dst.gscale[g] = finite ? __builtin_ldexpf(1.0f, e) : __builtin_nanf("");
       }
     }
   }
 }
 
 // sum over the lane's groups of s_g * (q . x)_g + b_g * xsum_g, then over the
-// P K-parts (lanes r, r + R, r + 2R, ...).  Every lane runs GPP groups (padding
-// groups have zero weights and reuse finite activations).  The next
-// 32-column chunk's activations are read from LDS while the current chunk is
-// multiplied.
+// P K-parts (lanes r, r + R, r + 2R, ...).  Per group the digit sums give
+// D = sum_i (q_i - 8) x_i exactly (x_i the group's integers), and
+// sum_i (s q_i + b) x_i = s 2^e D + (b + 8 s) xsum.  Every lane runs GPP
+// groups (padding groups have zero scale and bias and reuse an earlier
+// chunk's activations).  The next 32-column chunk's activations are read
+// from LDS while the current chunk is multiplied.
 //
 // `nck` is 2*GPP passed at run time: the branch on it puts every chunk in its
 // own basic block, which keeps the scheduler from hoisting all LDS reads and
-// nibble extractions to the top (that needs hundreds of registers).
+// nibble work to the top (that needs hundreds of registers).
 template <int P, int GPP, int GMAX>
 __device__ __forceinline__ float lane_dot(const LaneSlice<GPP>& s, const XRow<P, GMAX>& x, int j, Part pt, int G,
                                           int nck) {
-  float acc = 0.0f, d0 = 0.0f, d1 = 0.0f;
-  // chunk c's activations live in xb[c & 1]; padding chunks keep the finite
-  // values of an earlier chunk (their weights are zero)
-  uint4 xb[2][8];
+  float acc = 0.0f;
+  int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+  // chunk c's activations (4 words) live in xb[c & 1]
+  uint4 xb[2][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     xb[0][i] = make_uint4(0u, 0u, 0u, 0u);
     xb[1][i] = make_uint4(0u, 0u, 0u, 0u);
   }
   if (pt.ng > 0) {
-    const uint4* xv = &x.v[16 * pt.g0 + j];
+    const uint4* xv = &x.v[8 * pt.g0 + j];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xb[0][i] = xv[i];
+    for (int i = 0; i < 4; ++i) xb[0][i] = xv[i];
   }
 #pragma unroll
   for (int c = 0; c < 2 * GPP; ++c) {
     if (c < nck) {
       if (c + 1 < 2 * GPP && c + 1 < 2 * pt.ng) {
-        const uint4* xv = &x.v[16 * (pt.g0 + (c + 1) / 2) + j + 8 * ((c + 1) & 1)];
+        const uint4* xv = &x.v[8 * (pt.g0 + (c + 1) / 2) + 4 * ((c + 1) & 1) + j];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xb[(c + 1) & 1][i] = xv[i];
+        for (int i = 0; i < 4; ++i) xb[(c + 1) & 1][i] = xv[i];
       }
       const uint4* xc = xb[c & 1];
-      // opaque copy: waits for this chunk only and keeps its nibble extraction
-      // here (not hoisted out of the token loop)
+      // opaque copy: waits for this chunk only and keeps its nibble work here
+      // (not hoisted out of the token loop)
       uint4 w = s.q[c];
       asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
-      d0 = dot8(w.x, xc[0], xc[1], d0);
-      d1 = dot8(w.y, xc[2], xc[3], d1);
-      d0 = dot8(w.z, xc[4], xc[5], d0);
-      d1 = dot8(w.w, xc[6], xc[7], d1);
+      dot8d(w.x, xc[0], a0, a1, a2, a3);
+      dot8d(w.y, xc[1], a0, a1, a2, a3);
+      dot8d(w.z, xc[2], a0, a1, a2, a3);
+      dot8d(w.w, xc[3], a0, a1, a2, a3);
       if (c & 1) {
         const int g = min(pt.g0 + c / 2, G - 1);
         const uint32_t sb = (c / 2 < pt.ng) ? s.sb[c / 2] : 0u;  // padding group: zero scale and bias
-        acc = fmaf(half_lo(sb) * x.gscale[g], d0 + d1, fmaf(half_hi(sb), x.gsum[g], acc));
-        d0 = 0.0f;
-        d1 = 0.0f;
+        const int D = ((a3 * 16 + a2) * 16 + a1) * 16 + a0;
+        const float sc = half_lo(sb);
+        acc = fmaf(sc * x.gscale[g], (float)D, fmaf(fmaf(8.0f, sc, half_hi(sb)), x.gsum[g], acc));
+        a0 = a1 = a2 = a3 = 0;
       }
     }
   }
