@@ -76,9 +76,10 @@ struct FusedArgs {
   // part_ls, ss_ls floats apart): a cache line read in one layer never holds
   // values that another XCD writes later in the launch.
   float* act;    // [L][act_ls]: [k][f] act rows of the chosen experts
-  float* part;   // [L][part_ls]: [E][G] router partials of each layer's input
+  float* part;   // [L][part_ls]: [G][epad] router partials of each layer's input (one row per workgroup)
   float* sumsq;  // [L+1][ss_ls]: [G] partial sums of squares of each layer's input (and of the last output)
   int act_ls, part_ls, ss_ls;
+  int epad;      // E rounded up to 32: each workgroup's partials fill whole 128-byte lines
   int G, rpw;    // workgroups, down rows per workgroup (a multiple of 4, at most 16)
   int nck_g, nck_d;
 };
@@ -99,6 +100,11 @@ __device__ __forceinline__ float4 ldn4(__amdgpu_buffer_rsrc_t r, int idx) {  // 
 }
 __device__ __forceinline__ void st_c(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16-byte store written through to memory (sc1), like st_c.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st_c4(__amdgpu_buffer_rsrc_t r, int idx, float4 v) {  // idx % 4 == 0
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, idx * 4, 0, 16);
 }
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ lds_ptr_t to_lds(void* p) { return (lds_ptr_t)(p); }
@@ -190,10 +196,11 @@ __device__ __forceinline__ void down_rows_to_lds(const FusedArgs& a, int t, cons
 
 // Router partials of `layer` over this workgroup's rows, from the router rows
 // in LDS and z = w * y (w the norm weight, 1 without one; z = 0 past the
-// rows): part[e][g] = sum_i Wr[e][r0 + i] * z[i], plus sumsq[g] = sum_i y[i]^2.
-// Fixed summation order, the same in every launch.
+// rows): part[g][e] = sum_i Wr[e][r0 + i] * z[i], plus sumsq[g] = sum_i y[i]^2.
+// The row of E values goes out as whole 128-byte lines (s_pe holds zeros past
+// E).  Fixed summation order, the same in every launch.
 __device__ __forceinline__ void write_partials(const FusedArgs& a, int t, int layer, const float4* rw, const float* z,
-                                               const float* y) {
+                                               const float* y, float* s_pe) {
   const int g = blockIdx.x;
   if (layer < a.L) {
     const int tq = threads_per_expert(a.E), rpt = kDR / tq;
@@ -206,12 +213,17 @@ __device__ __forceinline__ void write_partials(const FusedArgs& a, int t, int la
         if (i < rpt) s = fmaf(w[i], z[q * rpt + i], s);
     }
     for (int o = 1; o < tq; o <<= 1) s += __shfl_xor(s, o, kWave);
-    if (e < a.E && q == 0) st_c(a.part + (int64_t)layer * a.part_ls + e * a.G + g, s);
+    if (e < a.E && q == 0) s_pe[e] = s;
   }
   if (t < kWave) {
     const float v = t < kDR ? y[t] : 0.0f;
     const float ss = wave_sum(v * v);
     if (t == 0) st_c(a.sumsq + (int64_t)layer * a.ss_ls + g, ss);
+  }
+  __syncthreads();
+  if (layer < a.L && t < a.epad / 4) {
+    const __amdgpu_buffer_rsrc_t r = rsrc_of(a.part + (int64_t)layer * a.part_ls, (int64_t)a.part_ls * 4);
+    st_c4(r, g * a.epad + 4 * t, reinterpret_cast<const float4*>(s_pe)[t]);
   }
 }
 
@@ -223,6 +235,8 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
   __shared__ float4 s_rw[kMaxE * kDR / 4];     // next layer's router rows over this workgroup's rows
   __shared__ float4 s_rnw[kWave];              // next layer's norm weight over the rows (first 4 used)
   __shared__ float4 s_logit4[kMaxE / 4 + 1];   // logits, padded with -inf to a multiple of 4
+  __shared__ float4 s_pe4[kMaxE / 4];          // this workgroup's router partials (zeros past E)
+  __shared__ float4 s_red4[kFThreads];         // router partial sums per (slice, quad of experts)
   __shared__ int s_table[kMaxE];               // this layer's slot per expert
   __shared__ float s_val[16];
   __shared__ float s_inv;
@@ -237,7 +251,9 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
   const int g = blockIdx.x;
   const int t = t0, lane = t0 % kWave;
   if (t == 0) s_base = (uint32_t)__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float* s_pe = reinterpret_cast<float*>(s_pe4);
   if (t < 4) s_logit[a.E + t] = -INFINITY;
+  if (t >= a.E && t < a.epad) s_pe[t] = 0.0f;
   const int Gd = a.d / kGroup, Gf = a.f / kGroup;
   const int r0 = g * a.rpw, nr = max(0, min(a.rpw, a.d - r0));
   const __amdgpu_buffer_rsrc_t rX = rsrc_of(a.x_io, (int64_t)(a.L + 1) * a.d * 4);
@@ -255,7 +271,7 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
   int nbar = 0;
   if (t < kDR) s_z[t] = t < nr ? s_y[t] * (a.norm_w ? reinterpret_cast<const float*>(s_rnw)[t] : 1.0f) : 0.0f;
   __syncthreads();
-  write_partials(a, t, 0, s_rw, s_z, s_y);
+  write_partials(a, t, 0, s_rw, s_z, s_y, s_pe);
   grid_sync(a, base + (uint32_t)++nbar);
 
   for (int l = 0; l < a.L; ++l) {
@@ -268,38 +284,13 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
     const int xo = l * a.d;  // x = x_io[l]
     // ================= gate/up phase =================
     // Everything that does not depend on the routing goes out at once: the
-    // slot table, the router bias, the sums of squares, the router partials,
-    // then x and the norm weight.
+    // slot table, the router bias, the sums of squares, x and the norm
+    // weight, then the router partials.
     if (t < a.E) s_table[t] = a.slot_tables[(int64_t)l * a.E + t];
-    const int e = t / tq, q = t % tq;
-    const float bias = (a.router_bias && e < a.E) ? a.router_bias[(int64_t)l * a.E + e] : 0.0f;
+    const float bias = (a.router_bias && t < a.E) ? a.router_bias[(int64_t)l * a.E + t] : 0.0f;
     float ssv[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) ssv[c] = ldn(rSS, l * a.ss_ls + min(lane + c * kWave, a.G - 1));
-    float s = 0.0f;
-    {
-      // tq consecutive threads per expert each sum a contiguous share of the G
-      // partials, then combine in a fixed order (the same in every workgroup)
-      const bool vec = a.G % 4 == 0;
-      const int share = vec ? ((a.G + tq - 1) / tq + 3) / 4 * 4 : (a.G + tq - 1) / tq;
-      if (e < a.E) {
-        const int i0 = min(a.G, q * share), i1 = min(a.G, i0 + share);
-        const int pb = l * a.part_ls + e * a.G;
-        if (vec) {
-          for (int b = i0; b < i1; b += 4 * kPartBatch) {
-            float4 v[kPartBatch];
-#pragma unroll
-            for (int c = 0; c < kPartBatch; ++c) v[c] = ldn4(rPart, pb + min(b + 4 * c, i1 - 4));
-#pragma unroll
-            for (int c = 0; c < kPartBatch; ++c)
-              if (b + 4 * c < i1) s += (v[c].x + v[c].y) + (v[c].z + v[c].w);
-          }
-        } else {
-#pragma unroll 8
-          for (int i = i0; i < i1; ++i) s += ldn(rPart, pb + i);
-        }
-      }
-    }
     constexpr int NPASSG = (8 * kGGMAX + kFThreads - 1) / kFThreads;
     StageRegs<NPASSG> xr, nwr;
     const float* nw = a.norm_w ? a.norm_w + (int64_t)l * a.d : nullptr;
@@ -311,17 +302,51 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
       nwr.a[ps] = nw ? *reinterpret_cast<const float4*>(nw + wi * 8) : make_float4(1.f, 1.f, 1.f, 1.f);
       nwr.b[ps] = nw ? *reinterpret_cast<const float4*>(nw + wi * 8 + 4) : make_float4(1.f, 1.f, 1.f, 1.f);
     }
-    for (int o = 1; o < tq; o <<= 1) s += __shfl_xor(s, o, kWave);
+    {
+      // part[l] is [G][epad]: thread t sums the quad of experts qd over its
+      // slice of the G rows; the slices meet in LDS
+      const int nq = (a.E + 3) / 4, ns = kFThreads / nq;
+      const int qd = t % nq, sl = t / nq;
+      const int gper = (a.G + ns - 1) / ns;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (sl < ns) {
+        const int g0 = sl * gper, g1 = min(a.G, g0 + gper);
+        const int pb = l * a.part_ls + 4 * qd;
+        for (int b = g0; b < g1; b += kPartBatch) {
+          float4 v[kPartBatch];
+#pragma unroll
+          for (int c = 0; c < kPartBatch; ++c) v[c] = ldn4(rPart, pb + min(b + c, g1 - 1) * a.epad);
+#pragma unroll
+          for (int c = 0; c < kPartBatch; ++c)
+            if (b + c < g1) {
+              acc.x += v[c].x;
+              acc.y += v[c].y;
+              acc.z += v[c].z;
+              acc.w += v[c].w;
+            }
+        }
+        s_red4[sl * nq + qd] = acc;
+      }
+    }
     float ss = 0.0f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) ss += lane + c * kWave < a.G ? ssv[c] : 0.0f;
     ss = wave_sum(ss);
     const float inv = a.norm_w ? 1.0f / sqrtf(ss / (float)a.d + a.eps) : 1.0f;
-    if (e < a.E && q == 0) s_logit[e] = s * inv + bias;
+    __syncthreads();
+    if (t < a.E) {
+      // the slices in a fixed order (the same in every workgroup)
+      const int nq = (a.E + 3) / 4, ns = kFThreads / nq;
+      const float* red = reinterpret_cast<const float*>(s_red4);
+      float s = 0.0f;
+      for (int k = 0; k < ns; ++k) s += red[(k * nq + t / 4) * 4 + t % 4];
+      s_logit[t] = s * inv + bias;
+    }
     __syncthreads();
     {
       // rank of expert e = experts with a larger logit, or an equal one and a
       // lower id (tq threads per expert, each over a quarter/half/eighth)
+      const int e = t / tq, q = t % tq;
       int beats = 0;
       float v = 0.0f;
       if (e < a.E) {
@@ -457,7 +482,7 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
         s_z[t] = z;
       }
       __syncthreads();
-      write_partials(a, t, l + 1, s_rw, s_z, s_y);
+      write_partials(a, t, l + 1, s_rw, s_z, s_y, s_pe);
     }
     grid_sync(a, base + (uint32_t)++nbar);
   }
@@ -494,6 +519,7 @@ bool decode_fused_supported(int d, int f, int E, int k, int cus, int* G_out, int
 namespace {
 struct FusedLayout {
   int act_ls, part_ls, ss_ls;  // floats per layer region, multiples of 64 (256 bytes)
+  int epad;
   int64_t flags_off, act_off, part_off, ss_off, bytes;
 };
 FusedLayout fused_layout(int L, int f, int E, int k) {
@@ -501,7 +527,8 @@ FusedLayout fused_layout(int L, int f, int E, int k) {
   auto r64 = [](int64_t n) { return (int)((n + 63) / 64 * 64); };
   FusedLayout o;
   o.act_ls = r64((int64_t)k * f);
-  o.part_ls = r64((int64_t)E * G);
+  o.epad = (E + 31) / 32 * 32;
+  o.part_ls = r64((int64_t)G * o.epad);
   o.ss_ls = r64(G);
   o.flags_off = 512;
   o.act_off = 512 + 1024;
@@ -551,6 +578,7 @@ hipError_t launch_decode_fused(float* x_io, int L, const float* norm_w, float ep
   a.sumsq = reinterpret_cast<float*>(c + lay.ss_off);
   a.act_ls = lay.act_ls;
   a.part_ls = lay.part_ls;
+  a.epad = lay.epad;
   a.ss_ls = lay.ss_ls;
   a.G = G;
   a.rpw = rpw;
