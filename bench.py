@@ -50,8 +50,10 @@ CSRC = os.path.join(ROOT, "int4_routed_expert_route_amd", "csrc")
 # (scaled by a 256 MiB copy's readings), keyed by the workload, for the kernel
 # sources with this fingerprint; reported as null once the sources differ.
 TRAFFIC = {
-    "decode": {"sources": ("q4_gemv.hip", "common.h"), "sha256_16": "925f59ad45a09c0d",
-               "fetch_bytes": 18126153, "write_bytes": 22528},
+    "decode": {"sources": ('q4_gemv.hip', 'q4_lane.h', 'common.h'), "sha256_16": "2d15adede551ea2a",
+               "fetch_bytes": 18093517, "write_bytes": 22528},
+    "decode_fused": {"sources": ('decode_fused.hip', 'q4_lane.h', 'common.h'), "sha256_16": "aa9dea22c4107faf",
+                     "fetch_bytes": 955022384, "write_bytes": 4249152},
     "prefill": {"sources": ("q4_grouped_mfma.hip", "common.h"), "sha256_16": "b7d97c1408f289ec",
                 "fetch_bytes": 241528376, "write_bytes": 23917840},
 }
