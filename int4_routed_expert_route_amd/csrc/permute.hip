@@ -4,11 +4,16 @@
 // "Optimizing a 14.3 GB model for an 8 GB machine", section "Splitting the work
 // improved attention and prefill").
 //
-// One workgroup of 1024 threads.  Counts come from LDS atomics (order free);
-// the scatter walks the pairs in ascending order, 1024 at a time: inside a wave
-// the pairs with equal expert are found with ballots over the expert id bits,
-// their rank is a popcount, and wave totals are scanned per expert in LDS, so
-// every bucket lists its pairs in ascending pair id without ordered atomics.
+// One workgroup of 1024 threads (16 waves).  Wave w owns a contiguous
+// stretch of pair ids and walks it 64 at a time in ascending order: the lanes
+// holding the same expert are found with ballots over the expert id bits, a
+// lane's rank among them is a popcount, and a wave-private counter per expert
+// in LDS gives each pair its position among the wave's pairs of that expert
+// (kept in pair_pos meanwhile).  The waves' counts are then scanned per expert
+// in wave order and over the experts, and a second walk writes every pair's
+// final position: each bucket lists its pairs in ascending pair id, with no
+// atomics.  Expert ids are loaded 16 rounds at a time, so each walk pays one
+// memory round trip per 1024 pairs of its stretch.
 #include "common.h"
 #include "kernels.h"
 
@@ -19,6 +24,19 @@ namespace {
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / kWave;
 constexpr int kMaxE = 256;
+constexpr int kBatch = 16;  // rounds of 64 pairs whose ids are loaded together
+
+// lanes whose expert id equals this lane's (invalid ids, -1, match only each other)
+__device__ __forceinline__ uint64_t same_expert(int e) {
+  uint64_t same = __ballot(e >= 0);
+  if (e < 0) same = ~same;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const uint64_t set = __ballot(e >= 0 && ((e >> b) & 1));
+    same &= ((e >= 0) && ((e >> b) & 1)) ? set : ~set;
+  }
+  return same;
+}
 
 __global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restrict__ topk_idx,
                                                           int n_pairs, int E,
@@ -26,65 +44,97 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restr
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ sorted_pair,
                                                           int32_t* __restrict__ pair_pos) {
-  __shared__ int s_count[kMaxE];
-  __shared__ int s_base[kMaxE];
-  __shared__ int s_wave[kPermWaves][kMaxE];
+  __shared__ int s_cnt[kPermWaves][kMaxE];  // per wave and expert: count, then the wave's base
+  __shared__ int s_base[kMaxE];             // per expert: first position of its bucket
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
-  for (int e = tid; e < kMaxE; e += kPermThreads) s_count[e] = 0;
+  for (int i = tid; i < kPermWaves * kMaxE; i += kPermThreads) (&s_cnt[0][0])[i] = 0;
   __syncthreads();
-  for (int p = tid; p < n_pairs; p += kPermThreads) {
-    int e = topk_idx[p];
-    if (e >= 0 && e < E) atomicAdd(&s_count[e], 1);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      s_base[e] = run;
-      offsets[e] = run;
-      counts[e] = s_count[e];
-      run += s_count[e];
-    }
-    offsets[E] = run;
-  }
-  __syncthreads();
+  const int seg = ((n_pairs + kPermWaves - 1) / kPermWaves + kWave - 1) / kWave * kWave;
+  const int p0 = min(n_pairs, wave * seg), p1 = min(n_pairs, p0 + seg);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = 0; base < n_pairs; base += kPermThreads) {
-    for (int i = tid; i < kPermWaves * kMaxE; i += kPermThreads) (&s_wave[0][0])[i] = 0;
-    __syncthreads();
-    const int p = base + tid;
-    int e = p < n_pairs ? topk_idx[p] : -1;
-    if (e < 0 || e >= E) e = -1;
-    // lanes holding the same expert id (invalid ids match only each other)
-    uint64_t same = __ballot(e >= 0);
-    if (e < 0) same = ~same;
+  auto expert_of = [&](int v) { return (v >= 0 && v < E) ? v : -1; };
+
+  // walk 1: position of each pair among its wave's pairs of the same expert
+  for (int b0 = p0; b0 < p1; b0 += kBatch * kWave) {
+    int ids[kBatch];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const uint64_t set = __ballot(e >= 0 && ((e >> b) & 1));
-      same &= ((e >= 0) && ((e >> b) & 1)) ? set : ~set;
+    for (int r = 0; r < kBatch; ++r) ids[r] = topk_idx[min(b0 + r * kWave + lane, max(p1 - 1, 0))];
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {
+      const int p = b0 + r * kWave + lane;
+      if (b0 + r * kWave >= p1) break;  // wave-uniform
+      const int e = p < p1 ? expert_of(ids[r]) : -1;
+      const uint64_t same = same_expert(e);
+      const int rank = __popcll(same & lt_mask);
+      int before = 0;
+      if (e >= 0) before = s_cnt[wave][e];
+      if (e >= 0 && rank == 0) s_cnt[wave][e] = before + __popcll(same);
+      if (p < p1) pair_pos[p] = e >= 0 ? before + rank : -1;
     }
-    const int rank = __popcll(same & lt_mask);
-    if (e >= 0 && rank == 0) s_wave[wave][e] = __popcll(same);
-    __syncthreads();
-    // per expert: exclusive scan over the waves of this chunk
-    for (int ee = tid; ee < E; ee += kPermThreads) {
-      int run = s_base[ee];
-      for (int w = 0; w < kPermWaves; ++w) {
-        const int c = s_wave[w][ee];
-        s_wave[w][ee] = run;
-        run += c;
+  }
+  __syncthreads();
+  // per expert: the waves' counts become exclusive bases in wave order
+  if (tid < E) {
+    int run = 0;
+    for (int w = 0; w < kPermWaves; ++w) {
+      const int c = s_cnt[w][tid];
+      s_cnt[w][tid] = run;
+      run += c;
+    }
+    s_base[tid] = run;
+  }
+  __syncthreads();
+  // exclusive scan of the counts over the experts (wave 0, 4 experts per lane)
+  if (wave == 0) {
+    int c[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane * 4 + i;
+      c[i] = e < E ? s_base[e] : 0;
+      sum += c[i];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int u = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += u;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane * 4 + i;
+      if (e < E) {
+        s_base[e] = run;
+        offsets[e] = run;
+        counts[e] = c[i];
       }
-      s_base[ee] = run;
+      run += c[i];
     }
-    __syncthreads();
-    if (e >= 0) {
-      const int pos = s_wave[wave][e] + rank;
-      sorted_pair[pos] = p;
-      pair_pos[p] = pos;
+    if (lane == kWave - 1) offsets[E] = incl;
+  }
+  __syncthreads();
+  // walk 2: final positions
+  for (int b0 = p0; b0 < p1; b0 += kBatch * kWave) {
+    int ids[kBatch], loc[kBatch];
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {
+      const int p = min(b0 + r * kWave + lane, max(p1 - 1, 0));
+      ids[r] = topk_idx[p];
+      loc[r] = pair_pos[p];
     }
-    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {
+      const int p = b0 + r * kWave + lane;
+      if (b0 + r * kWave >= p1) break;  // wave-uniform
+      const int e = p < p1 ? expert_of(ids[r]) : -1;
+      if (e >= 0) {
+        const int pos = s_base[e] + s_cnt[wave][e] + loc[r];
+        sorted_pair[pos] = p;
+        pair_pos[p] = pos;
+      }
+    }
   }
 }
 

@@ -115,117 +115,116 @@ __device__ __forceinline__ float exp2i(int e) { return __builtin_bit_cast(float,
 // Work list: experts by pair count (descending, ties by id); per expert, M tile
 // by M tile, its N tiles in order (the N tiles of one M tile share the
 // activation rows; the expert's weights stay in L2 across its M tiles).
-// Entry = (expert, m0, n tile).  The list is cut into 8 stretches of about
+// Item = (expert, m0, n tile).  The list is cut into 8 stretches of about
 // equal cost, one per XCD; an item costs 4 + (row groups of 16 in its M tile)
 // units (weights stream whatever the rows, MFMA work follows the rows).
-// meta[0] = items, meta[1 + x] = first item of XCD x (meta[9] = items).
-__global__ __launch_bounds__(256) void k_q4_schedule(const int32_t* __restrict__ offsets, int E, int n_pairs,
-                                                     int NT, int4* __restrict__ work, int* __restrict__ meta) {
-  __shared__ int s_cnt[256];
-  __shared__ int s_expert[256];
-  __shared__ int s_rcnt[256];  // pair count by rank
-  __shared__ int s_base[257];
-  __shared__ int s_wsum[256 / kWave];
-  __shared__ int s_start[9];
-  const int t = threadIdx.x;
-  int cnt = 0;
+//
+// Every workgroup of the GEMM derives the same list from the expert offsets
+// at its start (a separate scheduling launch cost more than this): ranks by
+// counting, block scans of items and cost over the ranks, and each XCD
+// boundary in closed form from the rank whose cost range holds it.  Items are
+// not stored: an item index maps to its rank by binary search over the ranks'
+// first items.
+struct Plan {
+  int expert[256];  // expert of each rank
+  int ibase[256];   // first item of each rank (the item count W for ranks without items)
+  int xstart[9];    // first item of each XCD's stretch; xstart[8] = W
+};
+
+// Called by all 256 threads; `scratch` (520 ints of LDS) is free until the
+// caller's next barrier.
+__device__ void plan_items(const int32_t* __restrict__ offsets, int E, int n_pairs, int NT, int* scratch,
+                           Plan& pl) {
+  int4* s_cnt4 = reinterpret_cast<int4*>(scratch);  // [256] counts by expert (-1 past E)
+  int* s_cnt = scratch;
+  int* s_rcnt = scratch + 256;                      // [256] counts by rank
+  int* s_wsum = scratch + 512;                      // [2][4] per-wave scan totals
+  int* s_start = pl.xstart;
+  const int t = threadIdx.x, lane = t % kWave, wv = t / kWave;
+  int cnt = -1;
   if (t < E) {
     const int a = max(0, min(offsets[t], n_pairs)), b = max(a, min(offsets[t + 1], n_pairs));
     cnt = b - a;
   }
-  s_cnt[t] = t < E ? cnt : -1;
+  s_cnt[t] = cnt;
+  if (t < 9) s_start[t] = -1;
   __syncthreads();
   if (t < E) {
     int rank = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = s_cnt[e];
-      rank += (c > cnt || (c == cnt && e < t)) ? 1 : 0;
+#pragma unroll 8
+    for (int e4 = 0; e4 < (E + 3) / 4; ++e4) {
+      const int4 c = s_cnt4[e4];
+      const int e = 4 * e4;
+      rank += (c.x > cnt || (c.x == cnt && e < t)) ? 1 : 0;
+      rank += (c.y > cnt || (c.y == cnt && e + 1 < t)) ? 1 : 0;
+      rank += (c.z > cnt || (c.z == cnt && e + 2 < t)) ? 1 : 0;
+      rank += (c.w > cnt || (c.w == cnt && e + 3 < t)) ? 1 : 0;
     }
-    s_expert[rank] = t;
+    pl.expert[rank] = t;
     s_rcnt[rank] = cnt;
   }
-  if (t < 9) s_start[t] = -1;
   __syncthreads();
-  // exclusive scan of items per rank (M tiles * NT) in one wave
-  if (t < kWave) {
-    int run = 0;
-    for (int r0 = 0; r0 < E; r0 += kWave) {
-      const int r = r0 + t;
-      const int v = r < E ? (s_rcnt[r] + BM - 1) / BM * NT : 0;
-      int incl = v;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int u = __shfl_up(incl, o, kWave);
-        if (t >= o) incl += u;
-      }
-      if (r < E) s_base[r] = run + incl - v;
-      run += __shfl(incl, kWave - 1, kWave);
-    }
-    if (t == 0) s_base[E] = run;
-  }
-  __syncthreads();
-  const int W = s_base[E];
-  // item i -> (rank, local index) and its cost
-  auto rank_of = [&](int i) {
-    int lo = 0, hi = E - 1;  // last rank with base <= i
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) / 2;
-      if (s_base[mid] <= i) lo = mid;
-      else hi = mid - 1;
-    }
-    return lo;
-  };
-  auto cost_of = [&](int r, int local) {
-    const int rows = min(BM, s_rcnt[r] - (local / NT) * BM);
-    return 4 + (rows + 15) / 16;
-  };
-  const int chunk = (W + blockDim.x - 1) / blockDim.x;
-  const int i0 = min(W, t * chunk), i1 = min(W, i0 + chunk);
-  int sum = 0;
-  for (int i = i0; i < i1; ++i) {
-    const int r = rank_of(i), local = i - s_base[r];
-    work[i] = make_int4(s_expert[r], (local / NT) * BM, local % NT, 0);
-    sum += cost_of(r, local);
-  }
-  // block-wide exclusive scan of the per-thread costs
-  const int lane = t % kWave, wv = t / kWave;
-  int incl = sum;
+  // rank r = t: its items (M tiles x NT) and their cost
+  const int r = t;
+  const int rc = r < E ? s_rcnt[r] : 0;
+  const int mt = (rc + BM - 1) / BM;
+  const int n_items = mt * NT;
+  const int full = rc / BM, tail = rc % BM;
+  const int c_full = 4 + BM / 16, c_tail = 4 + (tail + 15) / 16;
+  const int cost = NT * (full * c_full + (tail ? c_tail : 0));
+  int inc_i = n_items, inc_c = cost;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
-    const int u = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += u;
+    const int ui = __shfl_up(inc_i, o, kWave), uc = __shfl_up(inc_c, o, kWave);
+    if (lane >= o) {
+      inc_i += ui;
+      inc_c += uc;
+    }
   }
-  if (lane == kWave - 1) s_wsum[wv] = incl;
+  if (lane == kWave - 1) {
+    s_wsum[wv] = inc_i;
+    s_wsum[4 + wv] = inc_c;
+  }
   __syncthreads();
-  int wbase = 0, total = 0;
-  for (int w = 0; w < (int)(blockDim.x / kWave); ++w) {
-    if (w < wv) wbase += s_wsum[w];
-    total += s_wsum[w];
+  int base_i = inc_i - n_items, base_c = inc_c - cost, W = 0, total = 0;
+  for (int w = 0; w < 4; ++w) {
+    if (w < wv) {
+      base_i += s_wsum[w];
+      base_c += s_wsum[4 + w];
+    }
+    W += s_wsum[w];
+    total += s_wsum[4 + w];
   }
-  int pre = wbase + incl - sum;  // cost before item i0
-  auto xcd_of = [&](int before) { return min(7, (int)((int64_t)before * 8 / max(total, 1))); };
-  int x_prev = -1;
-  if (i0 > 0 && i0 < i1) {
-    const int r = rank_of(i0 - 1);
-    x_prev = xcd_of(pre - cost_of(r, i0 - 1 - s_base[r]));
+  pl.ibase[r] = base_i;
+  // XCD x starts at the first item whose cost before it is >= ceil(x * total / 8)
+  // (item i belongs to XCD min(7, cost_before_i * 8 / total)); the rank whose
+  // cost range holds that target finds the item tile by tile
+  if (n_items > 0) {
+    for (int x = 1; x < 8; ++x) {
+      const int target = (x * total + 7) / 8;
+      if (target < base_c || target >= base_c + cost) continue;
+      int pre = base_c, li = n_items;
+      for (int m = 0; m < mt; ++m) {
+        const int c = (m < full) ? c_full : c_tail;
+        if (pre + NT * c > target) {
+          li = m * NT + (target - pre + c - 1) / c;
+          break;
+        }
+        pre += NT * c;
+      }
+      s_start[x] = base_i + li;
+    }
   }
-  for (int i = i0; i < i1; ++i) {
-    const int r = rank_of(i);
-    const int x = xcd_of(pre);
-    for (int xx = x_prev + 1; xx <= x; ++xx) s_start[xx] = i;
-    x_prev = x;
-    pre += cost_of(r, i - s_base[r]);
-  }
+  if (t == 0) s_start[0] = 0;
   __syncthreads();
   if (t == 0) {
-    meta[0] = W;
     int next = W;  // XCDs past the last boundary get empty stretches
     for (int x = 8; x >= 0; --x) {
       if (x == 8 || s_start[x] < 0) s_start[x] = next;
       next = s_start[x];
-      meta[1 + x] = s_start[x];
     }
   }
+  __syncthreads();
 }
 
 // h (fp32 [n8 * 8]) -> 16-bit, slot order inside each 8-column block.
@@ -259,8 +258,6 @@ struct GemmArgs {
   int K;                  // reduction length (d for gate/up, f for down)
   int NT;                 // N tiles
   int64_t off_q0, off_q1, off_sb0, off_sb1;  // gate/up sections, or down in q0/sb0
-  const int4* work;
-  const int* meta;        // [0] items, [1 + x] first item of XCD x, [9] items
   void* out;              // gate/up: act values [T*k][f] (ET); down: pair values [T*k][d] fp16
   int8_t* out_exp;        // exponents [T*k][cols/64]
 };
@@ -323,7 +320,7 @@ __device__ __forceinline__ void lds_wait(u32x4 (&r)[4], u32x2 (&q)[4], uint32_t 
 
 // GATEUP: wave w of N tile nt owns act columns nt*128 + 32w .. +31 (gate rows
 // and up rows of those indices).  Down: wave w owns output rows nt*256 + 64w .. +63.
-// Persistent: workgroup j of XCD x runs items meta[1+x] + j, + gridDim/8, ...
+// Persistent: workgroup j of XCD x runs items xstart[x] + j, + gridDim/8, ...
 template <typename ET, bool GATEUP>
 __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
   typedef Op<ET> O;
@@ -334,6 +331,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
   __shared__ float s_wmax[kWaves];
   __shared__ int s_gexp[kMaxSteps];  // down: tile exponent of each K group
   __shared__ int s_fix;              // down: some row's exponents differ from its tile's
+  __shared__ Plan s_plan;
   const int t = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(t / kWave), lane = t % kWave;
   const int n = lane % 16, kq = lane / 16;  // MFMA lane coordinates
@@ -351,16 +349,27 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
   const uint32_t q_rd = lds_addr(&lds[0].q[wid][kq >> 1][n]) + (kq & 1) * 8;
   const uint32_t sb_rd = lds_addr(&lds[0].sb[wid][n]);
 
+  // the work list, in LDS (stage 0 of the pipeline serves as scratch)
+  plan_items(a.offsets, a.E, n_pairs, a.NT, reinterpret_cast<int*>(&lds[0]), s_plan);
   const int xcd = (int)(blockIdx.x % 8), nper = (int)(gridDim.x / 8);
-  const int i_end = __builtin_amdgcn_readfirstlane(a.meta[2 + xcd]);
-  for (int item = __builtin_amdgcn_readfirstlane(a.meta[1 + xcd]) + (int)(blockIdx.x / 8); item < i_end;
+  const int i_end = __builtin_amdgcn_readfirstlane(s_plan.xstart[xcd + 1]);
+  for (int item = __builtin_amdgcn_readfirstlane(s_plan.xstart[xcd]) + (int)(blockIdx.x / 8); item < i_end;
        item += nper) {
-    __syncthreads();  // the previous item's LDS is no longer in use
+    __syncthreads();  // the previous item's LDS (or the plan's scratch) is no longer in use
     // values the whole workgroup shares, made wave-uniform for the compiler
-    const int4 wk = a.work[item];
-    const int e = __builtin_amdgcn_readfirstlane(wk.x);
-    const int m0 = __builtin_amdgcn_readfirstlane(wk.y);
-    const int nt = __builtin_amdgcn_readfirstlane(wk.z);
+    int rk = 0;
+    {
+      int hi = a.E - 1;  // last rank whose first item is <= item
+      while (rk < hi) {
+        const int mid = (rk + hi + 1) / 2;
+        if (s_plan.ibase[mid] <= item) rk = mid;
+        else hi = mid - 1;
+      }
+    }
+    const int li = item - s_plan.ibase[rk];
+    const int e = __builtin_amdgcn_readfirstlane(s_plan.expert[rk]);
+    const int m0 = __builtin_amdgcn_readfirstlane((li / a.NT) * BM);
+    const int nt = __builtin_amdgcn_readfirstlane(li % a.NT);
     const int beg = __builtin_amdgcn_readfirstlane(max(0, min(a.offsets[e], n_pairs)));
     const int end = __builtin_amdgcn_readfirstlane(max(beg, min(a.offsets[e + 1], n_pairs)));
     const int rows = max(0, min(BM, end - beg - m0));
@@ -691,18 +700,10 @@ static int max_items(int T, int k, int E, int NT) { return ((T * k + BM - 1) / B
 size_t mfma_act_bytes(int T, int f, int k) { return (size_t)T * k * f * 2 + (size_t)T * k * (f / kGroup); }
 
 size_t mfma_workspace_bytes(int call, int T, int d, int f, int E, int k) {
-  const bool gu = call == MOE_CALL_GATEUP;
-  size_t b = 256 + round256((int64_t)max_items(T, k, E, gemm_nt(gu, d, f)) * 16);
-  if (gu) b += round256((int64_t)T * d * 2);  // h in 16-bit, slot order
-  else b += round256((int64_t)T * k * d * 2) + round256((int64_t)T * k * (d / kGroup));
-  return b;
-}
-
-static void carve(void* ws, int items, int** meta, int4** work, char** rest) {
-  char* c = reinterpret_cast<char*>(ws);
-  *meta = reinterpret_cast<int*>(c);
-  *work = reinterpret_cast<int4*>(c + 256);
-  *rest = c + 256 + round256((int64_t)items * 16);
+  (void)f;
+  (void)E;
+  if (call == MOE_CALL_GATEUP) return round256((int64_t)T * d * 2);  // h in 16-bit, slot order
+  return round256((int64_t)T * k * d * 2) + round256((int64_t)T * k * (d / kGroup));  // pair outputs
 }
 
 // Persistent grid: two workgroups per compute unit (the kernel's occupancy),
@@ -732,10 +733,7 @@ hipError_t launch_gateup_mfma(bool f16, const float* h, const int32_t* offsets, 
                               int64_t off_sb1, void* act_out, void* ws, hipStream_t s) {
   const int NT = gemm_nt(true, d, f);
   const int items = max_items(T, k, E, NT);
-  int* meta;
-  int4* work;
-  char* rest;
-  carve(ws, items, &meta, &work, &rest);
+  char* rest = reinterpret_cast<char*>(ws);
   const int64_t n8 = (int64_t)T * d / 8;
   if (f16)
     hipLaunchKernelGGL(k_h_to_slots<_Float16>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, h, n8,
@@ -743,7 +741,6 @@ hipError_t launch_gateup_mfma(bool f16, const float* h, const int32_t* offsets, 
   else
     hipLaunchKernelGGL(k_h_to_slots<__bf16>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, h, n8,
                        reinterpret_cast<__bf16*>(rest));
-  hipLaunchKernelGGL(k_q4_schedule, dim3(1), dim3(256), 0, s, offsets, E, T * k, NT, work, meta);
   GemmArgs a{};
   a.a_rows = rest;
   a.a_bytes = (int)((int64_t)T * d * 2);
@@ -759,8 +756,6 @@ hipError_t launch_gateup_mfma(bool f16, const float* h, const int32_t* offsets, 
   a.K = d;
   a.NT = NT;
   a.off_q0 = off_q0; a.off_q1 = off_q1; a.off_sb0 = off_sb0; a.off_sb1 = off_sb1;
-  a.work = work;
-  a.meta = meta;
   a.out = act_out;
   a.out_exp = reinterpret_cast<int8_t*>(act_out) + (int64_t)T * k * f * 2;
   if (f16) launch_gemm<_Float16, true>(a, items, s, MOE_CALL_GATEUP);
@@ -774,13 +769,9 @@ hipError_t launch_down_mfma(bool f16, const void* act_in, const int32_t* offsets
                             const float* residual, float* y, void* ws, hipStream_t s) {
   const int NT = gemm_nt(false, d, f);
   const int items = max_items(T, k, E, NT);
-  int* meta;
-  int4* work;
-  char* rest;
-  carve(ws, items, &meta, &work, &rest);
+  char* rest = reinterpret_cast<char*>(ws);
   _Float16* pair_val = reinterpret_cast<_Float16*>(rest);
   int8_t* pair_exp = reinterpret_cast<int8_t*>(rest + round256((int64_t)T * k * d * 2));
-  hipLaunchKernelGGL(k_q4_schedule, dim3(1), dim3(256), 0, s, offsets, E, T * k, NT, work, meta);
   GemmArgs a{};
   a.a_rows = act_in;
   a.a_bytes = (int)((int64_t)T * k * f * 2);
@@ -796,8 +787,6 @@ hipError_t launch_down_mfma(bool f16, const void* act_in, const int32_t* offsets
   a.K = f;
   a.NT = NT;
   a.off_q0 = off_q; a.off_sb0 = off_sb;
-  a.work = work;
-  a.meta = meta;
   a.out = pair_val;
   a.out_exp = pair_exp;
   if (f16) launch_gemm<_Float16, false>(a, items, s, MOE_CALL_DOWN_COMBINE);

@@ -341,18 +341,27 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial,
   const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= T) return;
-  float v[4];
+  // every slice's partial goes out before the first add (a loop of dependent
+  // loads would pay one memory round trip per slice)
+  float p[4][kMaxSlices];
   bool ok[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + kWave * i;
     ok[i] = e < E;
+    const int ec = min(e, E - 1);
+#pragma unroll
+    for (int s = 0; s < kMaxSlices; ++s) p[i][s] = partial[((size_t)min(s, slices - 1) * T + t) * E + ec];
+  }
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
     float acc = 0.0f;
-    if (ok[i]) {
-      for (int s = 0; s < slices; ++s) acc += partial[((size_t)s * T + t) * E + e];
-      if (router_bias) acc += router_bias[e];
-    }
-    v[i] = acc;
+#pragma unroll
+    for (int s = 0; s < kMaxSlices; ++s)
+      if (s < slices) acc += p[i][s];
+    if (ok[i] && router_bias) acc += router_bias[lane + kWave * i];
+    v[i] = ok[i] ? acc : 0.0f;
   }
   wave_topk_vals(v, ok, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
 }
