@@ -216,33 +216,11 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void k_route_small(
   if (threadIdx.x == 0) reset_counter(counter);
 }
 
-// ---- larger T: norm, tiled fp32 router GEMM, then top-k
+// ---- larger T: fp32 MFMA router GEMM (split-K), then norm factor + top-k per token
 
-__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x,
-                                                 const float* __restrict__ norm_w, float eps, int T,
-                                                 int d, float* __restrict__ h_out) {
-  const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (t >= T) return;
-  const float* xt = x + (size_t)t * d;
-  float rinv = norm_w ? wave_rinv(xt, d, eps) : 1.0f;
-  const float4* x4 = reinterpret_cast<const float4*>(xt);
-  const float4* n4 = reinterpret_cast<const float4*>(norm_w);
-  float4* h4 = reinterpret_cast<float4*>(h_out + (size_t)t * d);
-  for (int i = lane; i < d / 4; i += kWave) {
-    float4 a = x4[i];
-    if (norm_w) {
-      float4 n = n4[i];
-      a.x = a.x * rinv * n.x; a.y = a.y * rinv * n.y;
-      a.z = a.z * rinv * n.z; a.w = a.w * rinv * n.w;
-    }
-    h4[i] = a;
-  }
-}
-
-// logits[T][E] = h[T][d] * Wr[E][d]^T (+ bias).  32x32 output tile per
-// workgroup of 256 threads (2x2 outputs each), K staged through LDS 64 at a time.
-// Router GEMM for many tokens on fp32 MFMA: logits = h . Wr^T.  Workgroup =
+// Router GEMM for many tokens on fp32 MFMA: logits = (x * w) . Wr^T, the
+// RMSNorm's 1/rms factor applied per token afterwards (by k_topk, which also
+// writes h).  Workgroup =
 // 16 tokens x all experts x one K slice; wave w owns expert blocks w, w+4, ...
 // (16 experts each).  Each lane holds 4 consecutive columns of one token row
 // and one expert row per 16-column chunk and feeds them to 4 MFMAs
@@ -265,7 +243,8 @@ inline RouterSplit router_split(int T, int d) {
   return RouterSplit{(d + kslice - 1) / kslice, kslice};
 }
 
-__global__ __launch_bounds__(kRWaves * kWave) void k_router_mfma(const float* __restrict__ h,
+__global__ __launch_bounds__(kRWaves * kWave) void k_router_mfma(const float* __restrict__ x,
+                                                                 const float* __restrict__ norm_w,
                                                                  const float* __restrict__ router_w, int T,
                                                                  int d, int E, int kslice,
                                                                  float* __restrict__ partial) {
@@ -275,7 +254,8 @@ __global__ __launch_bounds__(kRWaves * kWave) void k_router_mfma(const float* __
   const int k_begin = ks * kslice, k_end = min(d, k_begin + kslice);
   const int nb = (E + 15) / 16;
   const int t = t0 + tn;
-  const float* hrow = h + (size_t)min(t, T - 1) * d + kq * 4;
+  const float* hrow = x + (size_t)min(t, T - 1) * d + kq * 4;
+  const float* nrow = norm_w ? norm_w + kq * 4 : nullptr;
   const float* wrow[4];
   bool eok[4];
 #pragma unroll
@@ -289,16 +269,17 @@ __global__ __launch_bounds__(kRWaves * kWave) void k_router_mfma(const float* __
   for (int b = 0; b < 4; ++b) acc[b] = floatx4r{0.f, 0.f, 0.f, 0.f};
   // chunks of 16 columns, loaded two ahead of their MFMAs
   struct Chunk {
-    float4 a, b[4];
+    float4 a, n, b[4];
   };
   auto load = [&](Chunk& c, int k0) {
     c.a = *reinterpret_cast<const float4*>(hrow + k0);
+    c.n = nrow ? *reinterpret_cast<const float4*>(nrow + k0) : make_float4(1.f, 1.f, 1.f, 1.f);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
       if (w + b * kRWaves < nb) c.b[b] = *reinterpret_cast<const float4*>(wrow[b] + k0);
   };
   auto mma = [&](const Chunk& c) {
-    const float av[4] = {c.a.x, c.a.y, c.a.z, c.a.w};
+    const float av[4] = {c.a.x * c.n.x, c.a.y * c.n.y, c.a.z * c.n.z, c.a.w * c.n.w};
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       if (w + b * kRWaves >= nb) continue;  // wave-uniform
@@ -333,16 +314,19 @@ __global__ __launch_bounds__(kRWaves * kWave) void k_router_mfma(const float* __
   }
 }
 
-// Per token (one wave): logits = sum of the K-slice partials in slice order +
-// bias, then top-k and the renormalised softmax weights.
+// Per token (one wave): the RMSNorm factor r = 1/sqrt(mean(x^2) + eps) from
+// the token's row, logits = r * (sum of the K-slice partials in slice order) +
+// bias, top-k and the renormalised weights, and h = x * r * w.
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial, int slices,
-                                              const float* __restrict__ router_bias, int T, int E, int k,
+                                              const float* __restrict__ x, const float* __restrict__ norm_w,
+                                              float eps, int d, const float* __restrict__ router_bias, int T,
+                                              int E, int k, float* __restrict__ h_out,
                                               int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= T) return;
-  // every slice's partial goes out before the first add (a loop of dependent
-  // loads would pay one memory round trip per slice)
+  // every slice's partial and the token's row go out before the first add (a
+  // loop of dependent loads would pay one memory round trip per slice)
   float p[4][kMaxSlices];
   bool ok[4];
 #pragma unroll
@@ -353,6 +337,14 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial,
 #pragma unroll
     for (int s = 0; s < kMaxSlices; ++s) p[i][s] = partial[((size_t)min(s, slices - 1) * T + t) * E + ec];
   }
+  const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)t * d);
+  float ss = 0.0f;
+#pragma unroll 4
+  for (int fi = lane; fi < d / 4; fi += kWave) {
+    const float4 a = x4[fi];
+    ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+  }
+  const float rinv = norm_w ? 1.0f / sqrtf(wave_sum(ss) / (float)d + eps) : 1.0f;
   float v[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -360,8 +352,21 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial,
 #pragma unroll
     for (int s = 0; s < kMaxSlices; ++s)
       if (s < slices) acc += p[i][s];
+    acc *= rinv;
     if (ok[i] && router_bias) acc += router_bias[lane + kWave * i];
     v[i] = ok[i] ? acc : 0.0f;
+  }
+  float4* h4 = reinterpret_cast<float4*>(h_out + (size_t)t * d);
+  const float4* n4 = reinterpret_cast<const float4*>(norm_w);
+#pragma unroll 4
+  for (int fi = lane; fi < d / 4; fi += kWave) {
+    float4 a = x4[fi];
+    if (norm_w) {
+      const float4 n = n4[fi];
+      a.x = a.x * rinv * n.x; a.y = a.y * rinv * n.y;
+      a.z = a.z * rinv * n.z; a.w = a.w * rinv * n.w;
+    }
+    h4[fi] = a;
   }
   wave_topk_vals(v, ok, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
 }
@@ -387,12 +392,11 @@ hipError_t launch_route(const float* x, const float* norm_w, float eps, const fl
                        router_bias, T, d, E, k, h_out, topk_idx, topk_w, logits, counter);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_rmsnorm, dim3((T + 3) / 4), dim3(256), 0, s, x, norm_w, eps, T, d, h_out);
   const RouterSplit sp = router_split(T, d);
-  launch_maybe_timed2(k_router_mfma, dim3((T + kRT - 1) / kRT, sp.slices), kRWaves * kWave, s, ev0, ev1, h_out,
-                      router_w, T, d, E, sp.kslice, logits);
-  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, sp.slices, router_bias, T, E, k,
-                     topk_idx, topk_w);
+  launch_maybe_timed2(k_router_mfma, dim3((T + kRT - 1) / kRT, sp.slices), kRWaves * kWave, s, ev0, ev1, x,
+                      norm_w, router_w, T, d, E, sp.kslice, logits);
+  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, sp.slices, x, norm_w, eps, d, router_bias,
+                     T, E, k, h_out, topk_idx, topk_w);
   return hipGetLastError();
 }
 
