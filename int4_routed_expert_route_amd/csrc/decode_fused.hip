@@ -114,22 +114,27 @@ __device__ __forceinline__ int threads_per_expert(int E) { return E <= 64 ? 8 : 
 
 // Device-wide barrier with sequence number `seq` (it grows across launches;
 // compared modulo 2^32).  Each workgroup publishes its arrival in its own
-// flag word with a write-through store; wave 0 of every workgroup then reads
-// all G flags at once with coherent (sc1) loads until none is behind.  No
+// flag word with a write-through store; kPollWaves waves of every workgroup
+// then read all G flags at once with coherent (sc1) loads until none is
+// behind, their rounds staggered by a quarter of a round trip, and the first
+// wave to see the last arrival tells the others through LDS.  No
 // read-modify-write: atomics on one shared counter serialise at the memory
 // side (~15 ns per arrival), flags cost one store and one round of loads.
-__device__ __forceinline__ void grid_sync(const FusedArgs& a, uint32_t seq) {
+constexpr int kPollWaves = 4;
+__device__ __forceinline__ void grid_sync(const FusedArgs& a, uint32_t seq, volatile int* s_done) {
   __builtin_amdgcn_s_waitcnt(0);  // this thread's stores (and LDS copies) are complete
+  if (threadIdx.x == 0) *s_done = 0;
   __syncthreads();
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    if (lane == 0) __hip_atomic_store(a.flags + blockIdx.x, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (wave == 0 && lane == 0) __hip_atomic_store(a.flags + blockIdx.x, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (wave < kPollWaves) {
+    for (int i = 0; i < 4 * wave; ++i) __builtin_amdgcn_s_sleep(2);  // ~128 clocks each
     const uint32_t* p0 = a.flags + min(lane, a.G - 1);
     const uint32_t* p1 = a.flags + min(lane + kWave, a.G - 1);
     const uint32_t* p2 = a.flags + min(lane + 2 * kWave, a.G - 1);
     const uint32_t* p3 = a.flags + min(lane + 3 * kWave, a.G - 1);
     uint32_t spins = 0;
-    while (true) {
+    while (*s_done == 0) {
       uint32_t v0, v1, v2, v3;
       asm volatile(
           "global_load_dword %0, %4, off sc1\n\t"
@@ -142,9 +147,13 @@ __device__ __forceinline__ void grid_sync(const FusedArgs& a, uint32_t seq) {
           : "memory");
       const bool behind = (int32_t)(v0 - seq) < 0 || (int32_t)(v1 - seq) < 0 || (int32_t)(v2 - seq) < 0 ||
                           (int32_t)(v3 - seq) < 0;
-      if (!__any(behind)) break;
+      if (!__any(behind)) {
+        *s_done = 1;
+        break;
+      }
       if (++spins > kSpinLimit) {
         if (lane == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_done = 1;
         break;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -234,7 +243,8 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
   __shared__ uint32_t s_dsb[kFWaves][kDGMAX * kDR];  // and their (scale, bias) words
   __shared__ float4 s_rw[kMaxE * kDR / 4];     // next layer's router rows over this workgroup's rows
   __shared__ float4 s_rnw[kWave];              // next layer's norm weight over the rows (first 4 used)
-  __shared__ float4 s_logit4[kMaxE / 4 + 1];   // logits, padded with -inf to a multiple of 4
+  __shared__ float4 s_logit4[kMaxE / 4 + 1];   // logits
+  __shared__ uint4 s_key4[kMaxE / 2 + 2];      // rank keys (logit, then lower id), zeros past E
   __shared__ float4 s_pe4[kMaxE / 4];          // this workgroup's router partials (zeros past E)
   __shared__ float4 s_red4[kFThreads];         // router partial sums per (slice, quad of experts)
   __shared__ int s_table[kMaxE];               // this layer's slot per expert
@@ -246,13 +256,15 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
   __shared__ float s_o[kFWaves][kDR];          // down outputs per expert rank
   __shared__ float s_y[kDR], s_z[kDR];         // this workgroup's output rows, and norm weight * rows
   __shared__ uint32_t s_base;
+  __shared__ int s_done;                       // barrier: some polling wave saw every arrival
   float* s_logit = reinterpret_cast<float*>(s_logit4);
   const int t0 = threadIdx.x;
   const int g = blockIdx.x;
   const int t = t0, lane = t0 % kWave;
   if (t == 0) s_base = (uint32_t)__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   float* s_pe = reinterpret_cast<float*>(s_pe4);
-  if (t < 4) s_logit[a.E + t] = -INFINITY;
+  uint64_t* s_key = reinterpret_cast<uint64_t*>(s_key4);
+  if (t < 4) s_key[a.E + t] = 0;
   if (t >= a.E && t < a.epad) s_pe[t] = 0.0f;
   const int Gd = a.d / kGroup, Gf = a.f / kGroup;
   const int r0 = g * a.rpw, nr = max(0, min(a.rpw, a.d - r0));
@@ -272,7 +284,7 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
   if (t < kDR) s_z[t] = t < nr ? s_y[t] * (a.norm_w ? reinterpret_cast<const float*>(s_rnw)[t] : 1.0f) : 0.0f;
   __syncthreads();
   write_partials(a, t, 0, s_rw, s_z, s_y, s_pe);
-  grid_sync(a, base + (uint32_t)++nbar);
+  grid_sync(a, base + (uint32_t)++nbar, &s_done);
 
   for (int l = 0; l < a.L; ++l) {
     // Thread-derived indices are recomputed from an opaque copy of the thread
@@ -340,25 +352,31 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
       const float* red = reinterpret_cast<const float*>(s_red4);
       float s = 0.0f;
       for (int k = 0; k < ns; ++k) s += red[(k * nq + t / 4) * 4 + t % 4];
-      s_logit[t] = s * inv + bias;
+      const float lg = s * inv + bias + 0.0f;  // + 0: -0 becomes +0
+      s_logit[t] = lg;
+      // one unsigned key orders (larger logit, then lower id): the float's
+      // bits made monotone, then the complement of the id
+      const uint32_t u = __builtin_bit_cast(uint32_t, lg);
+      const uint32_t mono = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+      s_key[t] = ((uint64_t)mono << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)t);
     }
     __syncthreads();
     {
       // rank of expert e = experts with a larger logit, or an equal one and a
-      // lower id (tq threads per expert, each over a quarter/half/eighth)
+      // lower id = experts with a larger key (tq threads per expert, each
+      // over a quarter/half/eighth of the keys, two per LDS read)
       const int e = t / tq, q = t % tq;
       int beats = 0;
       float v = 0.0f;
       if (e < a.E) {
         v = s_logit[e];
+        const uint64_t kv = s_key[e];
         const int span = ((a.E + tq - 1) / tq + 3) / 4 * 4, j0 = q * span, j1 = min(a.E, j0 + span);
 #pragma unroll 8
-        for (int jj = j0; jj < j1; jj += 4) {
-          const float4 u = s_logit4[jj / 4];
-          beats += (u.x > v || (u.x == v && jj < e)) ? 1 : 0;
-          beats += (u.y > v || (u.y == v && jj + 1 < e)) ? 1 : 0;
-          beats += (u.z > v || (u.z == v && jj + 2 < e)) ? 1 : 0;
-          beats += (u.w > v || (u.w == v && jj + 3 < e)) ? 1 : 0;
+        for (int jj = j0; jj < j1; jj += 2) {
+          const uint4 u = s_key4[jj / 2];
+          beats += (((uint64_t)u.y << 32 | u.x) > kv) ? 1 : 0;
+          beats += (((uint64_t)u.w << 32 | u.z) > kv) ? 1 : 0;
         }
       }
       for (int o = 1; o < tq; o <<= 1) beats += __shfl_xor(beats, o, kWave);
@@ -391,19 +409,6 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
     const int e2 = wave < a.k ? s_idx[wave] : -1;
     const int slot2 = (e2 >= 0 && e2 < a.E) ? s_table[e2] : -1;
     const uint8_t* blob2 = larena + ((slot2 >= 0 && slot2 < a.n_slots) ? (int64_t)slot2 * a.slot_stride : 0);
-    if (wave == 0) {
-      // weights: softmax over the chosen logits (largest first)
-      const float m = s_val[0];
-      const float ex = lane < a.k ? expf(s_val[lane < a.k ? lane : 0] - m) : 0.0f;
-      const float sum = wave_sum(ex);
-      if (lane < a.k) {
-        s_w[lane] = ex / sum;
-        if (g == 0) {
-          a.topk_idx[(int64_t)l * a.k + lane] = s_idx[lane];
-          a.topk_w[(int64_t)l * a.k + lane] = ex / sum;
-        }
-      }
-    }
     {
       // h = x * inv * w in 8-column words: thread t stages word t
       StageRegs<NPASSG> sr;
@@ -427,7 +432,22 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
       __syncthreads();
       if (mat == 1 && j == 0) st_c(a.act + (int64_t)l * a.act_ls + jr * a.f + row, gelu_tanh(s_g[rb][r]) * v);
     }
-    grid_sync(a, base + (uint32_t)++nbar);
+    if (wave == kFWaves - 1) {
+      // weights: softmax over the chosen logits (largest first), off the
+      // gate/up critical path (the down phase reads them)
+      const float m = s_val[0];
+      const float ex = lane < a.k ? expf(s_val[lane < a.k ? lane : 0] - m) : 0.0f;
+      const float sum = wave_sum(ex);
+      if (lane < a.k) {
+        s_w[lane] = ex / sum;
+        if (g == 0) {
+          a.topk_idx[(int64_t)l * a.k + lane] = s_idx[lane];
+          a.topk_w[(int64_t)l * a.k + lane] = ex / sum;
+        }
+      }
+    }
+
+    grid_sync(a, base + (uint32_t)++nbar, &s_done);
 
     // ================= down phase =================
     {
@@ -484,7 +504,7 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
       __syncthreads();
       write_partials(a, t, l + 1, s_rw, s_z, s_y, s_pe);
     }
-    grid_sync(a, base + (uint32_t)++nbar);
+    grid_sync(a, base + (uint32_t)++nbar, &s_done);
   }
 
   // unit-RMS rescale of the last output for the next decode step
