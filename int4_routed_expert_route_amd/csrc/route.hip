@@ -18,38 +18,64 @@ constexpr int kSmallT = 8;         // fused single-launch path up to this many t
 typedef float floatx4r __attribute__((ext_vector_type(4)));
 constexpr int kRouteWaves = 4;     // waves per workgroup in the fused path
 
-// Top-k of one token's logits by one wave: k rounds of a wave-wide arg-max with
-// (larger value, then lower id) order.  Writes idx/w for the token.
+// Top-k of one token's logits by one wave: k rounds of a wave-wide arg-max.
+// Each (logit, expert) is one unsigned 64-bit key, larger for a larger logit
+// and then for a lower id (the float's bits made monotone, then the
+// complemented id), so the arg-max is a plain maximum, reduced with DPP row
+// operations (no LDS round trips).  Writes idx/w for the token.
 // v[i], ok[i]: the logit of expert lane + 64 i and whether that expert exists.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v + 0.0f);  // + 0: -0 becomes +0
+  const uint32_t mono = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)mono << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t k) {
+  const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+  // lanes the operation does not write keep their own key (the max identity)
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROW_MASK, 0xF, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > k ? o : k;
+}
+// Maximum of k over the wave, in every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  k = dpp_max_step<0xB1, 0xF>(k);   // quad_perm [1,0,3,2]
+  k = dpp_max_step<0x4E, 0xF>(k);   // quad_perm [2,3,0,1]
+  k = dpp_max_step<0x141, 0xF>(k);  // row_half_mirror
+  k = dpp_max_step<0x140, 0xF>(k);  // row_mirror: every lane holds its row's maximum
+  k = dpp_max_step<0x142, 0xA>(k);  // row_bcast:15 into rows 1 and 3
+  k = dpp_max_step<0x143, 0xC>(k);  // row_bcast:31 into rows 2 and 3: lane 63 holds the maximum
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ void wave_topk_vals(float (&v)[4], bool (&ok)[4], int k, int32_t* idx_out, float* w_out) {
   const int lane = threadIdx.x % kWave;
+  uint64_t key[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) key[i] = ok[i] ? topk_key(v[i], lane + kWave * i) : 0ull;
   // lane j keeps the j-th choice
   float my_v = 0.0f;
   int my_e = -1;
   for (int j = 0; j < k; ++j) {
-    // lane-local best
-    bool bok = false;
-    float bv = 0.0f;
-    int be = 0x7fffffff;
+    uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int e = lane + kWave * i;
-      bool better = ok[i] && (!bok || v[i] > bv || (v[i] == bv && e < be));
-      if (better) { bok = true; bv = v[i]; be = e; }
-    }
-    // wave butterfly
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      int ook = __shfl_xor((int)bok, o, kWave);
-      float ov = __shfl_xor(bv, o, kWave);
-      int oe = __shfl_xor(be, o, kWave);
-      bool take = ook && (!bok || ov > bv || (ov == bv && oe < be));
-      if (take) { bok = true; bv = ov; be = oe; }
-    }
-    if (lane == j) { my_v = bv; my_e = be; }
+    for (int i = 0; i < 4; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int be = (int)(0xFFFFFFFFu - (uint32_t)best);
+    if (best == 0) break;  // fewer than k experts
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (lane + kWave * i == be) ok[i] = false;
+      if (lane + kWave * i == be) key[i] = 0;
+    // the chosen logit, back from the key's monotone bits
+    const uint32_t mono = (uint32_t)(best >> 32);
+    const float bv = __builtin_bit_cast(float, (mono & 0x80000000u) ? (mono & 0x7FFFFFFFu) : ~mono);
+    if (lane == j) {
+      my_v = bv;
+      my_e = be;
+    }
   }
   const float m = __shfl(my_v, 0, kWave);
   const float ex = lane < k ? expf(my_v - m) : 0.0f;
@@ -220,29 +246,34 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void k_route_small(
 
 // Router GEMM for many tokens on fp32 MFMA: logits = (x * w) . Wr^T, the
 // RMSNorm's 1/rms factor applied per token afterwards (by k_topk, which also
-// writes h).  Workgroup =
-// 16 tokens x all experts x one K slice; wave w owns expert blocks w, w+4, ...
-// (16 experts each).  Each lane holds 4 consecutive columns of one token row
-// and one expert row per 16-column chunk and feeds them to 4 MFMAs
-// (v_mfma_f32_16x16x4f32), column j of each group of 4 in MFMA j.  Partial
-// logits of K slice ks go to partial[ks][t][e]; the top-k kernel adds the
-// slices in order, so the sums do not depend on scheduling.
-constexpr int kRT = 16;        // tokens per workgroup
+// writes h).  Workgroup = NSUB MFMA row tiles of 16 tokens (2 for many
+// tokens, 1 for few, so that enough workgroups exist) x all experts x one K
+// slice; wave w owns expert blocks w, w+4, ... (16 experts each).
+// Each lane holds 4 consecutive columns of two token rows and of one expert
+// row per 16-column chunk and feeds them to v_mfma_f32_16x16x4f32, column j
+// of each group of 4 in MFMA j; every router load serves all NSUB token tiles.
+// Partial logits of K slice ks go to partial[ks][t][e]; the top-k kernel adds
+// the slices in order, so the sums do not depend on scheduling.
 constexpr int kRWaves = 4;
 constexpr int kMaxSlices = 16;
+
+// token tiles of 16 per workgroup
+inline int router_nsub(int T) { return T > 256 ? 2 : 1; }
 
 struct RouterSplit {
   int slices, kslice;
 };
 inline RouterSplit router_split(int T, int d) {
-  const int tiles = (T + kRT - 1) / kRT;
-  int ks = (1024 + tiles - 1) / tiles;  // ~4 workgroups per compute unit
+  const int rt = 16 * router_nsub(T);
+  const int tiles = (T + rt - 1) / rt;
+  int ks = (512 + tiles - 1) / tiles;  // ~2 workgroups per compute unit
   ks = ks < 1 ? 1 : (ks > kMaxSlices ? kMaxSlices : ks);
   int kslice = (d + ks - 1) / ks;
   kslice = (kslice + 15) / 16 * 16;
   return RouterSplit{(d + kslice - 1) / kslice, kslice};
 }
 
+template <int NSUB>
 __global__ __launch_bounds__(kRWaves * kWave) void k_router_mfma(const float* __restrict__ x,
                                                                  const float* __restrict__ norm_w,
                                                                  const float* __restrict__ router_w, int T,
@@ -250,11 +281,12 @@ __global__ __launch_bounds__(kRWaves * kWave) void k_router_mfma(const float* __
                                                                  float* __restrict__ partial) {
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int tn = lane % 16, kq = lane / 16;
-  const int t0 = blockIdx.x * kRT, ks = blockIdx.y;
+  const int t0 = blockIdx.x * 16 * NSUB, ks = blockIdx.y;
   const int k_begin = ks * kslice, k_end = min(d, k_begin + kslice);
   const int nb = (E + 15) / 16;
-  const int t = t0 + tn;
-  const float* hrow = x + (size_t)min(t, T - 1) * d + kq * 4;
+  const float* hrow[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) hrow[s] = x + (size_t)min(t0 + 16 * s + tn, T - 1) * d + kq * 4;
   const float* nrow = norm_w ? norm_w + kq * 4 : nullptr;
   const float* wrow[4];
   bool eok[4];
@@ -264,28 +296,35 @@ __global__ __launch_bounds__(kRWaves * kWave) void k_router_mfma(const float* __
     eok[b] = (w + b * kRWaves) < nb && e < E;
     wrow[b] = router_w + (size_t)(eok[b] ? e : 0) * d + kq * 4;
   }
-  floatx4r acc[4];
+  floatx4r acc[NSUB][4];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) acc[b] = floatx4r{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[s][b] = floatx4r{0.f, 0.f, 0.f, 0.f};
   // chunks of 16 columns, loaded two ahead of their MFMAs
   struct Chunk {
-    float4 a, n, b[4];
+    float4 a[NSUB], n, b[4];
   };
   auto load = [&](Chunk& c, int k0) {
-    c.a = *reinterpret_cast<const float4*>(hrow + k0);
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) c.a[s] = *reinterpret_cast<const float4*>(hrow[s] + k0);
     c.n = nrow ? *reinterpret_cast<const float4*>(nrow + k0) : make_float4(1.f, 1.f, 1.f, 1.f);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
       if (w + b * kRWaves < nb) c.b[b] = *reinterpret_cast<const float4*>(wrow[b] + k0);
   };
   auto mma = [&](const Chunk& c) {
-    const float av[4] = {c.a.x * c.n.x, c.a.y * c.n.y, c.a.z * c.n.z, c.a.w * c.n.w};
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      if (w + b * kRWaves >= nb) continue;  // wave-uniform
-      const float bv[4] = {c.b[b].x, c.b[b].y, c.b[b].z, c.b[b].w};
+    for (int s = 0; s < NSUB; ++s) {
+      const float av[4] = {c.a[s].x * c.n.x, c.a[s].y * c.n.y, c.a[s].z * c.n.z, c.a[s].w * c.n.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc[b], 0, 0, 0);
+      for (int b = 0; b < 4; ++b) {
+        if (w + b * kRWaves >= nb) continue;  // wave-uniform
+        const float bv[4] = {c.b[b].x, c.b[b].y, c.b[b].z, c.b[b].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[s][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc[s][b], 0, 0, 0);
+      }
     }
   };
   Chunk c0, c1, c2;
@@ -301,16 +340,18 @@ __global__ __launch_bounds__(kRWaves * kWave) void k_router_mfma(const float* __
     if (k0 + 64 < k_end) load(c1, k0 + 64);
     mma(c2);
   }
-  // lane holds C[token kq*4 + i][expert tn] of each block
+  // lane holds C[token 16 s + kq*4 + i][expert tn] of each block
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     if (w + b * kRWaves >= nb || !eok[b]) continue;
     const int e = (w + b * kRWaves) * 16 + tn;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tt = t0 + kq * 4 + i;
-      if (tt < T) partial[((size_t)ks * T + tt) * E + e] = acc[b][i];
-    }
+    for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tt = t0 + 16 * s + kq * 4 + i;
+        if (tt < T) partial[((size_t)ks * T + tt) * E + e] = acc[s][b][i];
+      }
   }
 }
 
@@ -333,16 +374,32 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial,
   for (int i = 0; i < 4; ++i) {
     const int e = lane + kWave * i;
     ok[i] = e < E;
+    if (kWave * i >= E) continue;  // wave-uniform: no expert of this lane group
     const int ec = min(e, E - 1);
 #pragma unroll
     for (int s = 0; s < kMaxSlices; ++s) p[i][s] = partial[((size_t)min(s, slices - 1) * T + t) * E + ec];
   }
+  // the token's row: all of it at once when it fits in registers
   const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)t * d);
+  const bool in_regs = d <= kWave * 4 * kMaxV;
+  float4 xv[kMaxV];
   float ss = 0.0f;
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < kMaxV; ++i) {
+      const int fi = lane + kWave * i;
+      if (kWave * i < d / 4) xv[i] = x4[min(fi, d / 4 - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxV; ++i)
+      if (kWave * i < d / 4 && lane + kWave * i < d / 4)
+        ss += xv[i].x * xv[i].x + xv[i].y * xv[i].y + xv[i].z * xv[i].z + xv[i].w * xv[i].w;
+  } else {
 #pragma unroll 4
-  for (int fi = lane; fi < d / 4; fi += kWave) {
-    const float4 a = x4[fi];
-    ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    for (int fi = lane; fi < d / 4; fi += kWave) {
+      const float4 a = x4[fi];
+      ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    }
   }
   const float rinv = norm_w ? 1.0f / sqrtf(wave_sum(ss) / (float)d + eps) : 1.0f;
   float v[4];
@@ -358,15 +415,21 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial,
   }
   float4* h4 = reinterpret_cast<float4*>(h_out + (size_t)t * d);
   const float4* n4 = reinterpret_cast<const float4*>(norm_w);
-#pragma unroll 4
-  for (int fi = lane; fi < d / 4; fi += kWave) {
-    float4 a = x4[fi];
+  auto put = [&](int fi, float4 a) {
     if (norm_w) {
       const float4 n = n4[fi];
       a.x = a.x * rinv * n.x; a.y = a.y * rinv * n.y;
       a.z = a.z * rinv * n.z; a.w = a.w * rinv * n.w;
     }
     h4[fi] = a;
+  };
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < kMaxV; ++i)
+      if (lane + kWave * i < d / 4) put(lane + kWave * i, xv[i]);
+  } else {
+#pragma unroll 4
+    for (int fi = lane; fi < d / 4; fi += kWave) put(fi, x4[fi]);
   }
   wave_topk_vals(v, ok, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
 }
@@ -393,8 +456,13 @@ hipError_t launch_route(const float* x, const float* norm_w, float eps, const fl
     return hipGetLastError();
   }
   const RouterSplit sp = router_split(T, d);
-  launch_maybe_timed2(k_router_mfma, dim3((T + kRT - 1) / kRT, sp.slices), kRWaves * kWave, s, ev0, ev1, x,
-                      norm_w, router_w, T, d, E, sp.kslice, logits);
+  const int rt = 16 * router_nsub(T);
+  if (router_nsub(T) == 2)
+    launch_maybe_timed2(k_router_mfma<2>, dim3((T + rt - 1) / rt, sp.slices), kRWaves * kWave, s, ev0, ev1, x,
+                        norm_w, router_w, T, d, E, sp.kslice, logits);
+  else
+    launch_maybe_timed2(k_router_mfma<1>, dim3((T + rt - 1) / rt, sp.slices), kRWaves * kWave, s, ev0, ev1, x,
+                        norm_w, router_w, T, d, E, sp.kslice, logits);
   hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, sp.slices, x, norm_w, eps, d, router_bias,
                      T, E, k, h_out, topk_idx, topk_w);
   return hipGetLastError();
