@@ -51,11 +51,11 @@ CSRC = os.path.join(ROOT, "int4_routed_expert_route_amd", "csrc")
 # sources with this fingerprint; reported as null once the sources differ.
 TRAFFIC = {
     "decode": {"sources": ('q4_gemv.hip', 'q4_lane.h', 'common.h'), "sha256_16": "2d15adede551ea2a",
-               "fetch_bytes": 18093517, "write_bytes": 22528},
-    "decode_fused": {"sources": ('decode_fused.hip', 'q4_lane.h', 'common.h'), "sha256_16": "aa9dea22c4107faf",
-                     "fetch_bytes": 955022384, "write_bytes": 4249152},
-    "prefill": {"sources": ("q4_grouped_mfma.hip", "common.h"), "sha256_16": "b7d97c1408f289ec",
-                "fetch_bytes": 241528376, "write_bytes": 23917840},
+               "fetch_bytes": 18093516, "write_bytes": 22528},
+    "decode_fused": {"sources": ('decode_fused.hip', 'q4_lane.h', 'common.h'), "sha256_16": "e0bd41a3820796a7",
+                     "fetch_bytes": 954399718, "write_bytes": 4249984},
+    "prefill": {"sources": ('q4_grouped_mfma.hip', 'common.h'), "sha256_16": "b51be121cb1394b5",
+                "fetch_bytes": 241497275, "write_bytes": 23925280},
 }
 
 
@@ -519,7 +519,7 @@ def run_prefill(args, api, torch):
         "kernel_us": {"route": round(rt_us, 2), "permute": round(pm_us, 2), "gateup_gemm": round(gu_us, 2),
                       "down_gemm": round(dn_us, 2)},
         "roofline": {
-            "kernel": f"k_grouped_mfma gate/up ({args.operands} MFMA 16x16x32, int4 tiles dequantised in LDS)",
+            "kernel": f"k_q4_gemm gate/up ({args.operands} MFMA 16x16x32, int4 tiles staged in LDS, dequantised in registers)",
             "bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": traffic_of("prefill"),
             "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated, median "

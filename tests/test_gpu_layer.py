@@ -102,7 +102,9 @@ def test_route_parity(layer0, dev_layer, T, norm, bias):
 
 
 def test_route_equal_logits_and_ties(dev_layer):
-    for T in (1, 20):
+    # one token (fused small path), 20 (one 16-token router tile) and 300
+    # (two tiles per workgroup, ragged last tile)
+    for T in (1, 20, 300):
         x = torch.from_numpy(synth.tokens(T, D, seed=1)).cuda()
         zero_w = torch.zeros(E, D, dtype=torch.float32, device="cuda")
         bias = torch.full((E,), 0.5, dtype=torch.float32, device="cuda")
