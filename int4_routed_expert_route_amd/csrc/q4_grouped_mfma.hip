@@ -269,17 +269,24 @@ struct StageLds {
   uint32_t sb[kWaves][WN];     // per wave: (scale, bias) of 64 weight rows
 };
 constexpr int kStages = 3;        // K steps in flight: DMA runs two steps ahead
-constexpr int kDmaPerStep = 7;    // per wave and step: 4 activation + 2 nibble + 1 scale/bias loads
+// per wave and step: 1..4 activation loads (as many as the tile's rows need)
+// + 2 nibble + 1 scale/bias loads
 constexpr int kMaxSteps = 128;    // K steps (groups) a down GEMM may have: f <= 8192
 
 // Chunk position of 16-byte chunk c in activation row r: c ^ swz(r % 16).  Any
 // 8 (or 16) consecutive rows read at one chunk index hit distinct LDS banks.
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-__device__ __forceinline__ void vm_wait_steps(bool one_more_in_flight) {
+// Wait until this wave's loads for step s have landed: with one more step in
+// flight, at most that step's n_a + 3 loads may still be outstanding.
+__device__ __forceinline__ void vm_wait_steps(bool one_more_in_flight, int n_a) {
   // s_waitcnt vmcnt(N), expcnt and lgkmcnt left unconstrained (gfx9 encoding)
-  if (one_more_in_flight) __builtin_amdgcn_s_waitcnt((kDmaPerStep & 0xF) | (0x7 << 4) | (0xF << 8));
-  else __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+  constexpr int kRest = (0x7 << 4) | (0xF << 8);
+  if (!one_more_in_flight) __builtin_amdgcn_s_waitcnt(kRest);
+  else if (n_a == 1) __builtin_amdgcn_s_waitcnt(4 | kRest);
+  else if (n_a == 2) __builtin_amdgcn_s_waitcnt(5 | kRest);
+  else if (n_a == 3) __builtin_amdgcn_s_waitcnt(6 | kRest);
+  else __builtin_amdgcn_s_waitcnt(7 | kRest);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -388,12 +395,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
     const uint8_t* blob = a.arena + (ok ? (int64_t)slot * a.slot_stride : 0);
     __syncthreads();
 
-    // ---- DMA sources.  Activations: wave w, load i fills slots (4w + i)*64 + lane
-    // = row (4w + i)*8 + lane/8, chunk position lane%8.  Padding rows read row 0.
+    // ---- DMA sources.  Activations: load i of wave w fills slots (4i + w)*64 + lane
+    // = row (4i + w)*8 + lane/8, chunk position lane%8, so every wave issues
+    // n_a = ceil(rows / 32) loads and rows past 32 n_a are not fetched (no
+    // MFMA reads them).  Padding rows read row 0.
+    const int n_a = __builtin_amdgcn_readfirstlane(min(4, max(1, (rows + 31) / 32)));
     int a_off[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = (wid * 4 + i) * 8 + lane / 8;
+      const int r = (i * 4 + wid) * 8 + lane / 8;
       const int p = s_pair[r];
       const int arow = p < 0 ? 0 : (a.a_by_token ? p / a.k : p);
       a_off[i] = (arow * a.K + ((lane % 8) ^ swz(r % 16)) * 8) * 2;
@@ -418,8 +428,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
       const int so_a = __builtin_amdgcn_readfirstlane(s * BK * 2);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, to_lds(&lds[st].a[(wid * 4 + i) * kWave]), 16, a_off[i], so_a,
-                                                 0, 0);
+        if (i < n_a)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, to_lds(&lds[st].a[(i * 4 + wid) * kWave]), 16, a_off[i],
+                                                   so_a, 0, 0);
       const int so_q = __builtin_amdgcn_readfirstlane(s * 2048);
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -567,7 +578,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
     };
     for (int s = 0; s < G; ++s) {
       const int st = s % kStages;
-      vm_wait_steps(s + 1 < G);            // this wave's DMA for step s has landed
+      vm_wait_steps(s + 1 < G, n_a);       // this wave's DMA for step s has landed
       __builtin_amdgcn_s_waitcnt(0xC07F);  // and its LDS accesses (lgkmcnt 0)
       __builtin_amdgcn_s_barrier();        // ... and every other wave's
       if (fix_rows) {
