@@ -86,6 +86,32 @@ def test_decode_layers_parity(api, d, f, E, k, L):
     _check_layers(st, x_io, idx, w)
 
 
+def test_decode_layers_ragged_shape(api):
+    """E not a multiple of 4 or 32 (padded partial rows and rank keys), odd k, and
+    rows that do not divide over the workgroups (a short last block and
+    workgroups with no down rows)."""
+    d, f, E, k, L = 128, 128, 20, 3, 3
+    st = Stack(api, d, f, E, k, L, seed=17)
+    x_io, idx, w = st.run(api, synth.tokens(1, d, 17)[0])
+    assert np.all(np.isfinite(x_io))
+    _check_layers(st, x_io, idx, w)
+
+
+def test_decode_layers_absent_slot_gives_nan(api):
+    """A chosen expert whose slot table entry is -1 is never read: that layer's
+    output is NaN, and the launch still completes without a barrier error."""
+    d, f, E, k, L = 256, 128, 16, 4, 2
+    st = Stack(api, d, f, E, k, L, seed=18)
+    x0 = synth.tokens(1, d, 18)[0]
+    _, idx, _ = st.run(api, x0)
+    tables = st.tables.cpu().numpy()
+    tables[0, idx[0][0]] = -1  # layer 0's first choice becomes absent
+    st.tables = torch.from_numpy(tables).cuda()
+    x_io, idx2, _ = st.run(api, x0)
+    assert np.array_equal(idx2[0], idx[0])
+    assert np.all(np.isnan(x_io[1]))
+
+
 def test_decode_layers_without_norm_or_bias(api):
     st = Stack(api, 256, 128, 16, 4, 2, seed=12, norm=False, bias=False, permute=False)
     x_io, idx, w = st.run(api, synth.tokens(1, 256, 12)[0])
