@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kMaxMfmaPairs = 1 << 22;  // T*k bound of the MFMA path (int32 work lists)
+constexpr int kMaxMfmaPairs = 1 << 22;  // T*k bound of the MFMA path (int32 item and row indices)
 
 // The MFMA kernels address h, act and one slot with 32-bit buffer offsets.
 bool mfma_fits_32bit(int32_t T, const moe_dims& d, int64_t slot_stride) {

@@ -30,7 +30,8 @@
 // current phase's loads are in flight.  Every wait is bounded: a stalled barrier (a workgroup
 // that never became resident) sets the error word and the kernel runs out
 // instead of hanging.  The int4 dot products are those of the decode GEMV
-// kernels (fp16-subnormal nibble pairs against fp16 hi/lo activations).
+// kernels (exact integer v_dot8_i32_i4 of the nibbles against 16-bit fixed
+// point activations per group).
 #include "common.h"
 #include "kernels.h"
 #include "q4_lane.h"

@@ -8,20 +8,23 @@
 // staged affine tiles).
 //
 // gfx950 design
-//  * Work item = (expert, 128-pair M tile, N tile).  A one-workgroup scheduler
-//    lists experts by pair count, largest first, and within an expert M tile
-//    by M tile its N tiles.  Workgroup b takes item (b % 8) * per + b / 8:
-//    each XCD works through one contiguous stretch of the list, so an
+//  * Work item = (expert, 128-pair M tile, N tile).  The list orders experts
+//    by pair count, largest first, and within an expert M tile by M tile its N
+//    tiles; it is cut into 8 stretches of equal cost, one per XCD, so an
 //    expert's weights and an M tile's activation rows are shared in one L2.
+//    Every persistent workgroup derives the list in its prologue; workgroup j
+//    of XCD x runs items j, j + grid/8, ... of stretch x.
 //  * Workgroup = 4 waves side by side along N.  A wave owns all 128 M rows x 64
 //    weight rows: 8 x 4 tiles of v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulate.
-//  * K step = one quantisation group (64 columns).  The activation tile
-//    (128 rows x 64 columns, 16-bit) is staged in LDS, double buffered, and
-//    read by all four waves.  The weights do not go through LDS: each lane
-//    loads the 8 nibble bytes and the (scale, bias) word that its own MFMA B
-//    fragments need and dequantises them in registers.  The K order inside
-//    each 8-column block is (0,4,1,5,2,6,3,7), the order in which nibbles
-//    come out of a 32-bit word; activations are stored in LDS in that order.
+//  * K step = one quantisation group (64 columns), three steps in flight: per
+//    step each wave copies, with LDS-DMA (buffer_load ... lds), its share of
+//    the activation tile (only the 32-row blocks the tile's rows need, rows
+//    gathered through sorted_pair) and its 64 weight rows' nibble chunks and
+//    (scale, bias) words.  Waves read the tile with explicit ds_read and
+//    dequantise the nibbles in registers (exact fp16 via the 1024-exponent
+//    trick, or bf16 via fp32).  The K order inside each 8-column block is
+//    (0,4,1,5,2,6,3,7), the order in which nibbles come out of a 32-bit word;
+//    activations are stored in that order.
 //  * Gate/up: a wave's 64 weight rows are 32 gate rows and the same 32 up
 //    rows, so gelu(gate) * up is formed from accumulators held by one lane.
 //  * fp16 results are block-scaled: one power-of-two exponent per row and
