@@ -44,9 +44,12 @@ using namespace lane;
 
 constexpr int kFWaves = 8;
 constexpr int kFThreads = kFWaves * kWave;
-// gate/up phase: 8 waves = (gate, up) x 4 blocks of 8 rows; lanes 8 K-parts x 8 rows
-constexpr int kGP = 8, kGR = kWave / kGP, kGGPP = 6, kGGMAX = kGP * kGGPP;  // d/64 <= 48
-constexpr int kActCols = 4 * kGR;                                          // 32 act columns per workgroup
+// gate/up phase: the workgroup's 32 act columns x 16 K-parts; wave w holds
+// columns 16 (w % 2) .. +15 and K-parts 4 (w / 2) .. +3, lane = 4 parts x 16
+// columns, and each lane computes the gate row and the up row of its column
+// (one read of the activations for both)
+constexpr int kGP = 16, kGPW = 4, kGR = kWave / kGPW, kGGPP = 3, kGGMAX = kGP * kGGPP;  // d/64 <= 48
+constexpr int kActCols = 2 * kGR;                                                        // 32 act columns
 // down phase: one wave per selected expert; lanes 4 K-parts x 16 rows
 constexpr int kDP = 4, kDR = kWave / kDP, kDGPP = 3, kDGMAX = kDP * kDGPP;  // f/64 <= 12
 constexpr int kDChunks = 2 * kDGMAX;  // 16-byte chunks (32 nibbles) of one down row at most
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
   __shared__ float s_inv;
   __shared__ int s_idx[16];
   __shared__ float s_w[16];
-  __shared__ float s_g[4][kGR];                // gate values of the 32 act columns
+  __shared__ float2 s_gu[kGP / kGPW][kActCols];  // (gate, up) partial sums per part block and column
   __shared__ float s_o[kFWaves][kDR];          // down outputs per expert rank
   __shared__ float s_y[kDR], s_z[kDR];         // this workgroup's output rows, and norm weight * rows
   __shared__ uint32_t s_base;
@@ -395,16 +398,17 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
     const int slot = (layer_expert >= 0 && layer_expert < a.E) ? s_table[layer_expert] : -1;
     const bool ok = slot >= 0 && slot < a.n_slots;
     const uint8_t* blob = larena + (ok ? (int64_t)slot * a.slot_stride : 0);
-    const int mat = wave / 4, rb = wave % 4;
-    const int j = lane / kGR, r = lane % kGR;
+    const int cb = wave % 2, pb = wave / 2;
+    const int j = pb * kGPW + lane / kGR, r = lane % kGR;
     const Part pt = part_of<kGP>(j, Gd);
-    const int row = c0 + rb * kGR + r;
-    LaneSlice<kGGPP> w;
+    const int row = c0 + cb * kGR + r;
+    LaneSlice<kGGPP> wg, wu;
     {
       const int64_t tile = row / kTileRows;
       const int trow = row % kTileRows;
-      load_lane<kGGPP>(w, blob + (mat ? a.off_uq : a.off_gq) + tile * (kTileRows * a.d / 2) + trow * 16,
-                       blob + (mat ? a.off_usb : a.off_gsb) + tile * (kTileRows * Gd * 4) + trow * 4, pt, Gd);
+      const int64_t qo = tile * (kTileRows * a.d / 2) + trow * 16, so = tile * (kTileRows * Gd * 4) + trow * 4;
+      load_lane<kGGPP>(wg, blob + a.off_gq + qo, blob + a.off_gsb + so, pt, Gd);
+      load_lane<kGGPP>(wu, blob + a.off_uq + qo, blob + a.off_usb + so, pt, Gd);
     }
     // the down phase's expert of this wave (rank = wave)
     const int e2 = wave < a.k ? s_idx[wave] : -1;
@@ -427,11 +431,20 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
     if (l + 1 < a.L) router_rows_to_lds(a, t, l + 1, r0, s_rw, s_rnw);
     __syncthreads();
     {
-      float v = lane_dot<kGP, kGGPP, kGGMAX>(w, xh, j, pt, Gd, a.nck_g);
-      if (!ok) v = f32_nan();
-      if (mat == 0 && j == 0) s_g[rb][r] = v;
+      const float2 v = lane_dot2<kGP, kGPW, kGGPP, kGGMAX>(wg, wu, xh, j, pt, Gd, a.nck_g);
+      if (lane < kGR) s_gu[pb][cb * kGR + r] = v;
       __syncthreads();
-      if (mat == 1 && j == 0) st_c(a.act + (int64_t)l * a.act_ls + jr * a.f + row, gelu_tanh(s_g[rb][r]) * v);
+      if (t < kActCols) {
+        // the part blocks in a fixed order
+        float gs = 0.0f, us = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kGP / kGPW; ++q) {
+          gs += s_gu[q][t].x;
+          us += s_gu[q][t].y;
+        }
+        const float v2 = ok ? gelu_tanh(gs) * us : f32_nan();
+        st_c(a.act + (int64_t)l * a.act_ls + jr * a.f + c0 + t, v2);
+      }
     }
     if (wave == kFWaves - 1) {
       // weights: softmax over the chosen logits (largest first), off the

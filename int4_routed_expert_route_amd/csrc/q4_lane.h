@@ -212,5 +212,69 @@ __device__ __forceinline__ float lane_dot(const LaneSlice<GPP>& s, const XRow<P,
   return acc;
 }
 
+// lane_dot for two rows at once (the gate row and the up row of one column)
+// that read the same activations: each chunk's activation words are read
+// from LDS once for both.  Returns the sums reduced over the PW K-parts a wave
+// holds (lanes r, r + 64/PW, ...); the caller adds the other waves' parts.
+// P is the number of K-parts of the LDS row layout.
+template <int P, int PW, int GPP, int GMAX>
+__device__ __forceinline__ float2 lane_dot2(const LaneSlice<GPP>& s0, const LaneSlice<GPP>& s1,
+                                            const XRow<P, GMAX>& x, int j, Part pt, int G, int nck) {
+  float acc0 = 0.0f, acc1 = 0.0f;
+  int a0 = 0, a1 = 0, a2 = 0, a3 = 0, b0 = 0, b1 = 0, b2 = 0, b3 = 0;
+  uint4 xb[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xb[0][i] = make_uint4(0u, 0u, 0u, 0u);
+    xb[1][i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (pt.ng > 0) {
+    const uint4* xv = &x.v[8 * pt.g0 + j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xb[0][i] = xv[i];
+  }
+#pragma unroll
+  for (int c = 0; c < 2 * GPP; ++c) {
+    if (c < nck) {
+      if (c + 1 < 2 * GPP && c + 1 < 2 * pt.ng) {
+        const uint4* xv = &x.v[8 * (pt.g0 + (c + 1) / 2) + 4 * ((c + 1) & 1) + j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xb[(c + 1) & 1][i] = xv[i];
+      }
+      const uint4* xc = xb[c & 1];
+      uint4 w = s0.q[c], u = s1.q[c];
+      asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+      asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
+      dot8d(w.x, xc[0], a0, a1, a2, a3);
+      dot8d(u.x, xc[0], b0, b1, b2, b3);
+      dot8d(w.y, xc[1], a0, a1, a2, a3);
+      dot8d(u.y, xc[1], b0, b1, b2, b3);
+      dot8d(w.z, xc[2], a0, a1, a2, a3);
+      dot8d(u.z, xc[2], b0, b1, b2, b3);
+      dot8d(w.w, xc[3], a0, a1, a2, a3);
+      dot8d(u.w, xc[3], b0, b1, b2, b3);
+      if (c & 1) {
+        const int g = min(pt.g0 + c / 2, G - 1);
+        const bool real = c / 2 < pt.ng;  // padding group: zero scale and bias
+        const uint32_t sb0 = real ? s0.sb[c / 2] : 0u, sb1 = real ? s1.sb[c / 2] : 0u;
+        const float gs = x.gscale[g], gsum = x.gsum[g];
+        const int D0 = ((a3 * 16 + a2) * 16 + a1) * 16 + a0, D1 = ((b3 * 16 + b2) * 16 + b1) * 16 + b0;
+        const float sc0 = half_lo(sb0), sc1 = half_lo(sb1);
+        acc0 = fmaf(sc0 * gs, (float)D0, fmaf(fmaf(8.0f, sc0, half_hi(sb0)), gsum, acc0));
+        acc1 = fmaf(sc1 * gs, (float)D1, fmaf(fmaf(8.0f, sc1, half_hi(sb1)), gsum, acc1));
+        a0 = a1 = a2 = a3 = 0;
+        b0 = b1 = b2 = b3 = 0;
+      }
+    }
+  }
+  constexpr int R = kWave / PW;
+#pragma unroll
+  for (int o = R; o < kWave; o <<= 1) {
+    acc0 += __shfl_xor(acc0, o, kWave);
+    acc1 += __shfl_xor(acc1, o, kWave);
+  }
+  return make_float2(acc0, acc1);
+}
+
 }  // namespace lane
 }  // namespace moe
