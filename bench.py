@@ -50,12 +50,12 @@ CSRC = os.path.join(ROOT, "int4_routed_expert_route_amd", "csrc")
 # (scaled by a 256 MiB copy's readings), keyed by the workload, for the kernel
 # sources with this fingerprint; reported as null once the sources differ.
 TRAFFIC = {
-    "decode": {"sources": ('q4_gemv.hip', 'q4_lane.h', 'common.h'), "sha256_16": "2d15adede551ea2a",
+    "decode": {"sources": ('q4_gemv.hip', 'q4_lane.h', 'common.h'), "sha256_16": "4fb8e1792d1f9193",
                "fetch_bytes": 18093516, "write_bytes": 22528},
-    "decode_fused": {"sources": ('decode_fused.hip', 'q4_lane.h', 'common.h'), "sha256_16": "e0bd41a3820796a7",
-                     "fetch_bytes": 954399718, "write_bytes": 4249984},
-    "prefill": {"sources": ('q4_grouped_mfma.hip', 'common.h'), "sha256_16": "b51be121cb1394b5",
-                "fetch_bytes": 241497275, "write_bytes": 23925280},
+    "decode_fused": {"sources": ('decode_fused.hip', 'q4_lane.h', 'common.h'), "sha256_16": "bab4ca0ec72f74cc",
+                     "fetch_bytes": 954255731, "write_bytes": 4249728},
+    "prefill": {"sources": ('q4_grouped_mfma.hip', 'common.h'), "sha256_16": "27391d2c1695c7f2",
+                "fetch_bytes": 240052090, "write_bytes": 23891904},
 }
 
 
