@@ -536,6 +536,11 @@ def run_prefill(args, api, torch):
 
 # ----------------------------------------------------------------------------- bounded cache
 
+def policy_name(args):
+    return {"lru": "LRU", "lfu": "LFU (whole-run counts)",
+            "lfu-window": f"LFU ({args.lfu_window}-step window)"}[args.policy]
+
+
 def run_cache(args, api, torch):
     n_slots = args.slots
     dm = api.dims(D, F, E, K)
@@ -552,6 +557,8 @@ def run_cache(args, api, torch):
     arena = torch.zeros(NL * n_slots * stride, dtype=torch.uint8, device=dev)
     tables = torch.full((NL, E), -1, dtype=torch.int32, device=dev)
     cache = api.MoeCache(NL, E, n_slots, K, pool, blob, arena, stride, tables)
+    policy = {"lru": api.MOE_CACHE_LRU, "lfu": api.MOE_CACHE_LFU, "lfu-window": api.MOE_CACHE_LFU_WINDOW}[args.policy]
+    api.moe_cache_set_policy(cache, policy, args.lfu_window)
     sel = np.stack([synth.markov_selections(E, K, total_steps, args.seed, l) for l in range(NL)], axis=1)
     bias = torch.from_numpy(synth.selection_bias(sel, E)).to(dev)  # [steps, NL, E]
     router_w = [torch.from_numpy(synth.router_weight(D, E, args.seed, l)).to(dev) for l in range(NL)]
@@ -618,9 +625,11 @@ def run_cache(args, api, torch):
         f"(timed {th / max(1, th + tm):.4f}); {tb / args.steps / 1e6:.1f} MB staged per token")
     out = base_record(tok_s, args.steps, args.warmup, ms, "fp32",
                       f"batch-1 decode with a bounded expert cache: {n_slots} HBM slots per layer of 128 experts, "
+                      f"{policy_name(args)} eviction, "
                       "expert pool in pinned host memory, misses staged on a side stream, Markov routing "
                       "(keep 0.8, Zipf refill), bf16 shared-path GEMV (4d x d) overlapped on the compute stream",
-                      {"tokens_per_step": 1, "slots_per_layer": n_slots, "graph": False})
+                      {"tokens_per_step": 1, "slots_per_layer": n_slots, "policy": policy_name(args),
+                       "graph": False})
     out.update({
         "hit_rate": round(hits / max(1, hits + misses), 5),
         "hit_rate_timed": round(th / max(1, th + tm), 5),
@@ -666,6 +675,8 @@ def main():
     ap.add_argument("--batched-prec", choices=["fp32", "f16", "bf16"], default="fp32",
                     help="batched: fp32 dequant-GEMV or grouped GEMM on MFMA")
     ap.add_argument("--slots", type=int, default=64, help="cache: HBM slots per layer")
+    ap.add_argument("--policy", choices=["lru", "lfu", "lfu-window"], default="lru", help="cache: eviction policy")
+    ap.add_argument("--lfu-window", type=int, default=64, help="cache: steps counted by --policy lfu-window")
     ap.add_argument("--kernel-samples", type=int, default=62)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")

@@ -279,6 +279,35 @@ moe_status moe_slot_stage(moe_cache* c, int32_t layer, int32_t step, const int32
                           hipStream_t side, hipStream_t compute,
                           uint8_t* hit_mask_dev, uint8_t* hit_mask_host,
                           moe_stage_stats* stats);
+/* Eviction policy of a cache (default MOE_CACHE_LRU).  The pages replace LRU
+ * by LFU, pushing out the expert used least, and try a 64-token LFU window
+ * beside the whole-run count ("Optimizing a 14.3 GB model for an 8 GB
+ * machine", section "MoE needed parallel work, reuse, and coarse overlap";
+ * TurboFieldfare video transcript, paragraph on the expert cache).
+ * Use count of expert e of a layer = the number of counted steps of that layer
+ * (moe_slot_stage calls, the current one included) whose selection holds e:
+ * every step so far for MOE_CACHE_LFU (resident or not), the last `window`
+ * steps for MOE_CACHE_LFU_WINDOW.  A step stamps its hits first; then each
+ * miss, in ascending expert id, takes the lowest empty slot, else the slot not
+ * used in this step whose expert has the smallest (use count, stamp, slot).
+ * window: 1..MOE_CACHE_MAX_WINDOW for MOE_CACHE_LFU_WINDOW, ignored otherwise.
+ * Errors: MOE_ERR_ARG (unknown policy, window out of range), MOE_ERR_STATE
+ * (called after the cache staged a step or imported usage). */
+enum {
+  MOE_CACHE_LRU = 0,
+  MOE_CACHE_LFU = 1,
+  MOE_CACHE_LFU_WINDOW = 2,
+  MOE_CACHE_MAX_WINDOW = 4096
+};
+moe_status moe_cache_set_policy(moe_cache* c, int32_t policy, int32_t window);
+/* Checkpoint of the use counts: counts_host int64 [n_layers][n_experts];
+ * recent_host int32 [n_layers][window][top_k], the selections of each layer's
+ * last `window` steps, oldest first, -1 before the first steps (required for
+ * MOE_CACHE_LFU_WINDOW, unused otherwise).  Import checks that windowed counts
+ * equal those of recent_host (else MOE_ERR_STATE); with moe_cache_export /
+ * moe_cache_import it resumes a run exactly. */
+moe_status moe_cache_export_usage(const moe_cache* c, int64_t* counts_host, int32_t* recent_host);
+moe_status moe_cache_import_usage(moe_cache* c, const int64_t* counts_host, const int32_t* recent_host);
 /* Make `compute` wait until the layer's last staging has landed. */
 moe_status moe_cache_wait(moe_cache* c, int32_t layer, hipStream_t compute);
 /* Host copy of a layer's slot table (expert -> slot, -1 absent), int32 [E]. */

@@ -66,6 +66,9 @@ _SIGNATURES = {
     "moe_cache_slot_table": (ctypes.c_int, [_P, _I32, _P]),
     "moe_cache_export": (ctypes.c_int, [_P, _P, _P]),
     "moe_cache_import": (ctypes.c_int, [_P, _P, _P]),
+    "moe_cache_set_policy": (ctypes.c_int, [_P, _I32, _I32]),
+    "moe_cache_export_usage": (ctypes.c_int, [_P, _P, _P]),
+    "moe_cache_import_usage": (ctypes.c_int, [_P, _P, _P]),
     "moe_shared_gemv_bf16": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P]),
     "moe_rms_rescale": (ctypes.c_int, [_P, _I32, _I32, _F, _P, _P]),
     "moe_profile_next_launch": (ctypes.c_int, [ctypes.c_int, _P, _P]),
@@ -267,3 +270,18 @@ def moe_cache_export(cache: MoeCache, slot_expert_host, stamp_host):
 
 def moe_cache_import(cache: MoeCache, slot_expert_host, stamp_host):
     _check(lib().moe_cache_import(cache.handle, _host(slot_expert_host, "slot_expert"), _host(stamp_host, "stamp")))
+
+
+MOE_CACHE_LRU, MOE_CACHE_LFU, MOE_CACHE_LFU_WINDOW = 0, 1, 2
+
+
+def moe_cache_set_policy(cache: MoeCache, policy, window=0):
+    _check(lib().moe_cache_set_policy(cache.handle, int(policy), int(window)))
+
+
+def moe_cache_export_usage(cache: MoeCache, counts_host, recent_host=None):
+    _check(lib().moe_cache_export_usage(cache.handle, _host(counts_host, "counts"), _host(recent_host, "recent")))
+
+
+def moe_cache_import_usage(cache: MoeCache, counts_host, recent_host=None):
+    _check(lib().moe_cache_import_usage(cache.handle, _host(counts_host, "counts"), _host(recent_host, "recent")))

@@ -6,8 +6,11 @@
 // misses are still arriving ("Optimizing a 14.3 GB model for an 8 GB machine",
 // sections "Explicit reads made expert streaming work" and "MoE needed parallel
 // work, reuse, and coarse overlap"); goinfer ("When the model doesn't fit")
-// keeps an LRU over resident slots.  On MI355X the pool sits in pinned host
-// memory and a miss is one DMA copy of the expert blob, verbatim, over PCIe.
+// keeps an LRU over resident slots.  The first page then replaces LRU by LFU
+// (the expert used least is pushed out) and tries a 64-token LFU window beside
+// the whole-run count; both are policies here.  On MI355X the pool sits in
+// pinned host memory and a miss is one DMA copy of the expert blob, verbatim,
+// over PCIe.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -33,6 +36,13 @@ struct moe_cache {
   std::vector<char> staged_used, masked_used;
   hipEvent_t compute_mark = nullptr;
   moe_stage_stats stats{0, 0, 0};
+  // eviction policy (moe_cache_set_policy) and, for LFU, the use counts
+  int policy = MOE_CACHE_LRU;
+  int window = 0;                    // MOE_CACHE_LFU_WINDOW: steps counted
+  std::vector<int64_t> count;        // [L][E] selections within the counted steps
+  std::vector<int32_t> recent;       // [L][window][k] ring of the last selections, -1 = none
+  std::vector<int64_t> steps_seen;   // [L] moe_slot_stage calls so far
+  bool staged_any = false;
 };
 
 // Failures are reported through the library's thread-local error text (api.cpp).
@@ -87,6 +97,8 @@ moe_status moe_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_slots
   c->masked.assign(n_layers, nullptr);
   c->staged_used.assign(n_layers, 0);
   c->masked_used.assign(n_layers, 0);
+  c->count.assign((size_t)n_layers * n_experts, 0);
+  c->steps_seen.assign(n_layers, 0);
   moe_status st = MOE_OK;
   if ((st = hipcheck(hipHostMalloc((void**)&c->table_host, sizeof(int32_t) * n_layers * n_experts,
                                    hipHostMallocDefault), "hipHostMalloc")) ||
@@ -150,6 +162,19 @@ moe_status moe_slot_stage(moe_cache* c, int32_t layer, int32_t step, const int32
   std::vector<int> where(c->E, -1);
   for (int s = 0; s < c->S; ++s)
     if (se[s] >= 0) where[se[s]] = s;
+  // use counts: this step's selection enters, and with a window the step
+  // that falls out of it leaves
+  int64_t* cnt = c->count.data() + (int64_t)layer * c->E;
+  if (c->policy == MOE_CACHE_LFU_WINDOW) {
+    int32_t* ring = c->recent.data() + ((int64_t)layer * c->window + c->steps_seen[layer] % c->window) * c->k;
+    for (int j = 0; j < c->k; ++j) {
+      if (ring[j] >= 0) --cnt[ring[j]];
+      ring[j] = sel_host[j];
+    }
+  }
+  for (int j = 0; j < c->k; ++j) ++cnt[sel_host[j]];
+  ++c->steps_seen[layer];
+  c->staged_any = true;
   // phase 1: stamp the hits
   uint8_t* mask = c->mask_host + (int64_t)layer * c->k;
   std::vector<int> misses;
@@ -166,8 +191,24 @@ moe_status moe_slot_stage(moe_cache* c, int32_t layer, int32_t step, const int32
   std::vector<std::pair<int, int>> installs;  // (expert, slot)
   for (int e : sorted) {
     int victim = 0;
-    for (int s = 1; s < c->S; ++s)
-      if (sp[s] < sp[victim]) victim = s;
+    if (c->policy == MOE_CACHE_LRU) {
+      // smallest (stamp, slot): empty slots (stamp -1) first
+      for (int s = 1; s < c->S; ++s)
+        if (sp[s] < sp[victim]) victim = s;
+    } else {
+      // lowest empty slot, else among slots not used in this step the
+      // smallest (use count of its expert, stamp, slot)
+      victim = -1;
+      for (int s = 0; s < c->S && victim < 0; ++s)
+        if (se[s] < 0) victim = s;
+      if (victim < 0)
+        for (int s = 0; s < c->S; ++s) {
+          if (sp[s] == step) continue;
+          if (victim < 0 || cnt[se[s]] < cnt[se[victim]] ||
+              (cnt[se[s]] == cnt[se[victim]] && sp[s] < sp[victim]))
+            victim = s;
+        }
+    }
     se[victim] = e;
     sp[victim] = step;
     installs.emplace_back(e, victim);
@@ -201,6 +242,62 @@ moe_status moe_slot_stage(moe_cache* c, int32_t layer, int32_t step, const int32
   c->stats.misses += (int64_t)misses.size();
   c->stats.bytes_staged += (int64_t)misses.size() * c->blob;
   if (stats) *stats = c->stats;
+  return MOE_OK;
+}
+
+moe_status moe_cache_set_policy(moe_cache* c, int32_t policy, int32_t window) {
+  if (!c) return cfail(MOE_ERR_ARG, "moe_cache_set_policy: null cache");
+  if (policy != MOE_CACHE_LRU && policy != MOE_CACHE_LFU && policy != MOE_CACHE_LFU_WINDOW)
+    return cfail(MOE_ERR_ARG, "moe_cache_set_policy: unknown policy");
+  if (policy == MOE_CACHE_LFU_WINDOW && (window < 1 || window > MOE_CACHE_MAX_WINDOW))
+    return cfail(MOE_ERR_ARG, "moe_cache_set_policy: window must be in 1..4096 steps");
+  if (c->staged_any) return cfail(MOE_ERR_STATE, "moe_cache_set_policy: the cache has already staged a step");
+  c->policy = policy;
+  c->window = policy == MOE_CACHE_LFU_WINDOW ? window : 0;
+  c->recent.assign((size_t)c->L * c->window * c->k, -1);
+  return MOE_OK;
+}
+
+moe_status moe_cache_export_usage(const moe_cache* c, int64_t* counts_host, int32_t* recent_host) {
+  if (!c || !counts_host) return cfail(MOE_ERR_ARG, "moe_cache_export_usage: null pointer");
+  if (c->policy == MOE_CACHE_LFU_WINDOW && !recent_host)
+    return cfail(MOE_ERR_ARG, "moe_cache_export_usage: the windowed policy needs recent_host");
+  std::memcpy(counts_host, c->count.data(), sizeof(int64_t) * c->count.size());
+  if (c->policy == MOE_CACHE_LFU_WINDOW)
+    for (int l = 0; l < c->L; ++l)
+      for (int i = 0; i < c->window; ++i) {
+        // oldest first: the ring position the next step overwrites
+        const int64_t pos = (c->steps_seen[l] + i) % c->window;
+        std::memcpy(recent_host + ((int64_t)l * c->window + i) * c->k,
+                    c->recent.data() + ((int64_t)l * c->window + pos) * c->k, sizeof(int32_t) * c->k);
+      }
+  return MOE_OK;
+}
+
+moe_status moe_cache_import_usage(moe_cache* c, const int64_t* counts_host, const int32_t* recent_host) {
+  if (!c || !counts_host) return cfail(MOE_ERR_ARG, "moe_cache_import_usage: null pointer");
+  if (c->policy == MOE_CACHE_LFU_WINDOW && !recent_host)
+    return cfail(MOE_ERR_ARG, "moe_cache_import_usage: the windowed policy needs recent_host");
+  for (size_t i = 0; i < c->count.size(); ++i)
+    if (counts_host[i] < 0) return cfail(MOE_ERR_STATE, "moe_cache_import_usage: negative use count");
+  if (c->policy == MOE_CACHE_LFU_WINDOW) {
+    // the counts must be those of the window's selections
+    std::vector<int64_t> want((size_t)c->L * c->E, 0);
+    for (int l = 0; l < c->L; ++l)
+      for (int i = 0; i < c->window * c->k; ++i) {
+        const int e = recent_host[(int64_t)l * c->window * c->k + i];
+        if (e < -1 || e >= c->E) return cfail(MOE_ERR_STATE, "moe_cache_import_usage: bad expert id");
+        if (e >= 0) ++want[(int64_t)l * c->E + e];
+      }
+    for (size_t i = 0; i < want.size(); ++i)
+      if (want[i] != counts_host[i])
+        return cfail(MOE_ERR_STATE, "moe_cache_import_usage: counts differ from the window's selections");
+    std::memcpy(c->recent.data(), recent_host, sizeof(int32_t) * c->recent.size());
+    // the ring restarts at position 0 holding the oldest step
+    for (int l = 0; l < c->L; ++l) c->steps_seen[l] = 0;
+  }
+  std::memcpy(c->count.data(), counts_host, sizeof(int64_t) * c->count.size());
+  c->staged_any = true;
   return MOE_OK;
 }
 

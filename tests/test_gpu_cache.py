@@ -1,6 +1,7 @@
 """GPU tests of the bounded expert cache (moe_slot_stage and friends) against
-the oracle's LRU rule: slot tables, hit masks, staged bytes and arena contents
-after every step, and a layer computed through the cache against the oracle."""
+the oracle's LRU and LFU rules: slot tables, hit masks, staged bytes and arena
+contents after every step, checkpoint and resume, and a layer computed through
+the cache against the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -51,12 +52,23 @@ def _stage(api, pool, l, t, sel, side, compute):
     return st, hit_dev, hit_host
 
 
+def _oracle_cache(policy, window, n_slots, E):
+    if policy == "lru":
+        return orc.LruSlotCache(n_slots, E)
+    return orc.LfuSlotCache(n_slots, E, window=window if policy == "lfu_window" else None)
+
+
+_POLICY = {"lru": 0, "lfu": 1, "lfu_window": 2}
+
+
+@pytest.mark.parametrize("policy,window", [("lru", 0), ("lfu", 0), ("lfu_window", 6)])
 @pytest.mark.parametrize("n_slots,steps", [(8, 60), (16, 40)])
-def test_slot_tables_follow_oracle_lru(api, n_slots, steps):
+def test_slot_tables_follow_oracle(api, n_slots, steps, policy, window):
     d, f, E, k, nl = 256, 128, 32, 4, 2
     pool = Pool(api, d, f, E, k, nl, n_slots, seed=3)
+    api.moe_cache_set_policy(pool.cache, _POLICY[policy], window)
     side, compute = torch.cuda.Stream(), torch.cuda.current_stream()
-    lru = [orc.LruSlotCache(n_slots, E) for _ in range(nl)]
+    lru = [_oracle_cache(policy, window, n_slots, E) for _ in range(nl)]
     sels = [synth.markov_selections(E, k, steps, 3, l) for l in range(nl)]
     hits = misses = 0
     for t in range(steps):
@@ -85,7 +97,82 @@ def test_slot_tables_follow_oracle_lru(api, n_slots, steps):
         for s, e in enumerate(lru[l].export_state()[0]):
             if e >= 0:
                 assert np.array_equal(pool.slot_bytes(l, s), pool.blobs[l][e])
+    if policy != "lru":
+        counts = torch.zeros(nl, E, dtype=torch.int64)
+        recent = torch.zeros(nl, max(window, 1), k, dtype=torch.int32)
+        api.moe_cache_export_usage(pool.cache, counts, recent)
+        for l in range(nl):
+            assert counts[l].tolist() == lru[l].counts(), l
     pool.cache.close()
+
+
+def test_policy_refusals(api):
+    d, f, E, k, S = 256, 128, 16, 4, 8
+    pool = Pool(api, d, f, E, k, 1, S, seed=4)
+    with pytest.raises(api.MoeError):
+        api.moe_cache_set_policy(pool.cache, 7, 0)
+    with pytest.raises(api.MoeError):
+        api.moe_cache_set_policy(pool.cache, api.MOE_CACHE_LFU_WINDOW, 0)
+    with pytest.raises(api.MoeError):
+        api.moe_cache_set_policy(pool.cache, api.MOE_CACHE_LFU_WINDOW, 4097)
+    api.moe_cache_set_policy(pool.cache, api.MOE_CACHE_LFU_WINDOW, 4)
+    side, compute = torch.cuda.Stream(), torch.cuda.current_stream()
+    _stage(api, pool, 0, 0, [0, 1, 2, 3], side, compute)
+    with pytest.raises(api.MoeError):  # a cache that has staged keeps its policy
+        api.moe_cache_set_policy(pool.cache, api.MOE_CACHE_LFU, 0)
+    counts = torch.zeros(1, E, dtype=torch.int64)
+    with pytest.raises(api.MoeError):  # the windowed policy's checkpoint needs the window
+        api.moe_cache_export_usage(pool.cache, counts, None)
+    recent = torch.zeros(1, 4, k, dtype=torch.int32)
+    api.moe_cache_export_usage(pool.cache, counts, recent)
+    assert recent[0, :3].tolist() == [[-1] * k] * 3 and recent[0, 3].tolist() == [0, 1, 2, 3]
+    counts[0, 5] += 1  # counts that do not match the window are refused
+    with pytest.raises(api.MoeError):
+        api.moe_cache_import_usage(pool.cache, counts, recent)
+    api.moe_cache_wait(pool.cache, 0, compute)
+    torch.cuda.synchronize()
+    pool.cache.close()
+
+
+@pytest.mark.parametrize("policy,window", [("lfu", 0), ("lfu_window", 5)])
+def test_lfu_checkpoint_resume(api, policy, window):
+    d, f, E, k, nl, S = 256, 128, 16, 4, 1, 8
+    pool = Pool(api, d, f, E, k, nl, S, seed=6)
+    api.moe_cache_set_policy(pool.cache, _POLICY[policy], window)
+    side, compute = torch.cuda.Stream(), torch.cuda.current_stream()
+    sels = synth.markov_selections(E, k, 30, 6, 0)
+    ref = _oracle_cache(policy, window, S, E)
+    for t in range(13):
+        _stage(api, pool, 0, t, sels[t], side, compute)
+        ref.step(t, [int(e) for e in sels[t]])
+    api.moe_cache_wait(pool.cache, 0, compute)
+    torch.cuda.synchronize()
+    se = torch.zeros(nl, S, dtype=torch.int32)
+    stp = torch.zeros(nl, S, dtype=torch.int64)
+    counts = torch.zeros(nl, E, dtype=torch.int64)
+    recent = torch.zeros(nl, max(window, 1), k, dtype=torch.int32)
+    api.moe_cache_export(pool.cache, se, stp)
+    api.moe_cache_export_usage(pool.cache, counts, recent)
+    assert counts[0].tolist() == ref.counts()
+    if window:
+        want = [sorted(int(e) for e in sels[t]) for t in range(13 - window, 13)]
+        assert [sorted(r) for r in recent[0].tolist()] == want
+    # a fresh cache with the same policy restored from the checkpoint continues like the oracle
+    pool2 = Pool(api, d, f, E, k, nl, S, seed=6)
+    api.moe_cache_set_policy(pool2.cache, _POLICY[policy], window)
+    api.moe_cache_import(pool2.cache, se, stp)
+    api.moe_cache_import_usage(pool2.cache, counts, recent)
+    for t in range(13, 30):
+        _, _, hit_host = _stage(api, pool2, 0, t, sels[t], side, compute)
+        want_hit, _ = ref.step(t, [int(e) for e in sels[t]])
+        assert hit_host.numpy().astype(bool).tolist() == want_hit, t
+    api.moe_cache_wait(pool2.cache, 0, compute)
+    torch.cuda.synchronize()
+    table = torch.zeros(E, dtype=torch.int32)
+    api.moe_cache_slot_table(pool2.cache, 0, table)
+    assert np.array_equal(table.numpy(), np.array(ref.slot_of_expert(), dtype=np.int32))
+    pool.cache.close()
+    pool2.cache.close()
 
 
 def test_export_import_round_trip(api):

@@ -341,3 +341,70 @@ def test_lru_invariants_and_resume():
         hit, _ = full.step(t, sel[t].tolist())
         assert hit == [e in seen for e in sel[t].tolist()]
         seen |= set(sel[t].tolist())
+
+
+# ----------------------------------------------------------------------------- LFU
+
+@pytest.mark.parametrize("key", ["whole_run", "window_2"])
+def test_lfu_hand_worked_trace(key):
+    g = _load("lfu_trace_3slots.json")
+    c = orc.LfuSlotCache(g["n_slots"], g["n_experts"], window=g[key]["window"])
+    for t, st in enumerate(g[key]["steps"]):
+        hit, installs = c.step(t, st["sel"])
+        assert hit == st["hit"], t
+        assert [list(i) for i in installs] == st["installs"], t
+        assert c.slot_expert == st["slots"], t
+        assert c.stamp == st["stamps"], t
+
+
+def test_lfu_window_one_is_lru():
+    # a one-step window gives every resident expert not chosen now a count of
+    # zero, so the choice falls to (stamp, slot): exactly the LRU rule
+    for S, k, layer in ((64, 8, 0), (12, 4, 5)):
+        E = 128 if S == 64 else 32
+        sel = synth.markov_selections(E, k, 300, seed=1, layer=layer)
+        a, b = orc.LruSlotCache(S, E), orc.LfuSlotCache(S, E, window=1)
+        for t in range(300):
+            assert a.step(t, sel[t].tolist()) == b.step(t, sel[t].tolist()), (S, t)
+            assert a.slot_expert == b.slot_expert and a.stamp == b.stamp
+
+
+@pytest.mark.parametrize("window", [None, 16])
+def test_lfu_invariants_and_resume(window):
+    E, S, k, steps = 64, 16, 4, 240
+    sel = synth.markov_selections(E, k, steps, seed=2, layer=1)
+    a = orc.LfuSlotCache(S, E, window=window)
+    for t in range(steps):
+        before = list(a.slot_expert)
+        hit, installs = a.step(t, sel[t].tolist())
+        after = set(e for e in a.slot_expert if e >= 0)
+        assert set(sel[t].tolist()) <= after
+        assert sum(not h for h in hit) == len(set(sel[t].tolist()) - set(e for e in before if e >= 0))
+        # an evicted expert was not chosen in this step, and every unchosen
+        # resident that stayed is used at least as often as any evicted one
+        chosen = set(sel[t].tolist())
+        evicted = [ev for _, _, ev in installs if ev >= 0]
+        kept = [e for e in before if e >= 0 and e not in chosen and e not in evicted]
+        assert not (set(evicted) & chosen)
+        if evicted and kept:
+            cnt = a.counts()
+            assert max(cnt[e] for e in evicted) <= min(cnt[e] for e in kept), t
+        if t == 119:
+            state = a.export_state()
+    b = orc.LfuSlotCache(S, E, window=window)
+    b.import_state(state)
+    for t in range(120, steps):
+        b.step(t, sel[t].tolist())
+    assert b.export_state() == a.export_state()
+
+
+def test_lfu_whole_run_keeps_the_popular_expert():
+    # two slots, one choice per step: once expert 0 has been chosen twice it
+    # outlives the experts seen once (hits at steps 6 and 9), where LRU
+    # evicts it every time
+    E, S, k = 8, 2, 1
+    seq = [[0], [1], [2], [0], [3], [4], [0], [5], [6], [0]]
+    lfu, lru = orc.LfuSlotCache(S, E), orc.LruSlotCache(S, E)
+    lfu_hits = sum(lfu.step(t, s)[0][0] for t, s in enumerate(seq))
+    lru_hits = sum(lru.step(t, s)[0][0] for t, s in enumerate(seq))
+    assert lfu_hits == 2 and lru_hits == 0
