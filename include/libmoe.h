@@ -326,8 +326,9 @@ moe_status moe_cache_import(moe_cache* c, const int32_t* slot_expert_host, const
  * moe_expert_q4_gateup + moe_expert_q4_down_combine (MOE_PREC_FP32) compute
  * them, layer after layer (the routed MoE of "Optimizing a 14.3 GB model for an
  * 8 GB machine" and the router of the TurboFieldfare video transcript).  The
- * workgroups of the launch meet at device-wide barriers instead of kernel
- * boundaries (two per layer).
+ * workgroups of the launch hand values to each other through the workspace
+ * (written once per launch, read by polling until written) instead of kernel
+ * boundaries or device-wide barriers.
  *   x_io         device fp32 [n_layers + 1][d]: x_io[0] is the input token;
  *                layer l writes its output (with the residual) to x_io[l + 1]
  *   norm_w       device fp32 [n_layers][d] or NULL (no RMSNorm)
@@ -342,11 +343,14 @@ moe_status moe_cache_import(moe_cache* c, const int32_t* slot_expert_host, const
  *                moe_workspace_size(MOE_CALL_DECODE_LAYERS, n_layers, ...)
  *                bytes (the T argument counts layers for this call),
  *                zero-filled before its first use and then passed
- *                unchanged to every call (it carries the barrier state); calls
- *                that share a workspace must be stream-ordered.
+ *                unchanged to every call with the same n_layers and dims (it
+ *                carries a launch count and two sets of exchange regions that
+ *                alternate between launches); calls that share a workspace
+ *                must be stream-ordered.  A call with other shapes on a used
+ *                workspace writes nothing and sets the error word.
  * Requires the device to run all k*f/32 workgroups at once (one per compute
- * unit is enough); a barrier that does not complete within ~0.25 s sets an
- * error word instead of hanging: moe_decode_check reports it.
+ * unit is enough); a value that does not arrive within ~0.25 s sets an error
+ * word instead of hanging: moe_decode_check reports it.
  * Supported: d <= 3072, f <= 768, E <= 256, k <= 8, k * f / 32 <= 256 and
  * d <= 16 * k * f / 32; otherwise MOE_ERR_UNSUPPORTED.
  * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_CAPACITY, MOE_ERR_UNSUPPORTED.
@@ -359,8 +363,9 @@ moe_status moe_decode_layers(float* x_io, int32_t n_layers, const float* norm_w,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Waits for `stream` and reports MOE_ERR_STATE if a moe_decode_layers call on
- * this workspace hit its barrier time limit (its outputs are then invalid and
- * the workspace must be zero-filled again). */
+ * this workspace hit its wait time limit or found the workspace laid out for
+ * other shapes (its outputs are then invalid and the workspace must be
+ * zero-filled again). */
 moe_status moe_decode_check(const void* ws, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------

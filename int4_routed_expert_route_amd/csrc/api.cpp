@@ -350,7 +350,8 @@ moe_status moe_decode_check(const void* ws, hipStream_t stream) {
                                 hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, fn);
-  if (flag) return fail(MOE_ERR_STATE, "%s: a device-wide barrier timed out", fn);
+  if (flag == 2u) return fail(MOE_ERR_STATE, "%s: the workspace was laid out for other shapes (zero-fill it)", fn);
+  if (flag) return fail(MOE_ERR_STATE, "%s: a wait for another workgroup's values timed out", fn);
   return MOE_OK;
 }
 

@@ -7,31 +7,34 @@
 // experts).  The separate calls (moe_route, moe_expert_q4_gateup,
 // moe_expert_q4_down_combine) cost three kernel launches per layer, and at
 // batch 1 each of them is dominated by its fixed start/drain time, not by its
-// ~27 MB of weights.  Here the layers run inside one kernel whose workgroups
-// meet at device-wide barriers, two per layer:
+// ~27 MB of weights.  Here the layers run inside one kernel, in two phases per
+// layer:
 //
 //   gate/up phase  every workgroup reduces the router partials of the layer
 //                  (written by the previous phase), takes the top-k and the
 //                  weights, stages h = RMSNorm(x) in LDS and computes 32 act
 //                  columns of one selected expert (k * f/32 workgroups);
-//   --- barrier ---
 //   down phase     workgroup g owns d/G output rows: the k experts' down rows,
 //                  the rank-ordered combine with the residual, and the next
 //                  layer's router partials over its rows (sum_i Wr[e][i] w[i] y[i]
-//                  and sum_i y[i]^2), so the next router needs no phase of its own;
-//   --- barrier ---
+//                  and sum_i y[i]^2), so the next router needs no phase of its own.
 //
-// The first layer's router partials come from a prologue phase (+1 barrier).
-// Values shared between workgroups are stored at agent scope (written through
-// to memory) into one region per layer and loaded with plain loads; a barrier
-// arrival follows the acknowledgement of the workgroup's stores.  Weights that
-// a later phase needs and that are known earlier (the down rows of the chosen
-// experts, the next layer's router rows) are copied into LDS while the
-// current phase's loads are in flight.  Every wait is bounded: a stalled barrier (a workgroup
-// that never became resident) sets the error word and the kernel runs out
-// instead of hanging.  The int4 dot products are those of the decode GEMV
-// kernels (exact integer v_dot8_i32_i4 of the nibbles against 16-bit fixed
-// point activations per group).
+// There is no device-wide barrier.  Every value one workgroup hands to another
+// (act, router partials, sums of squares, the next layer's input) is written
+// once per launch, through to memory, in a region of its own, encoded so that
+// a zero word means "not written yet"; the reader loads the value itself with
+// coherent loads until it is nonzero.  A barrier would cost the writer's wait
+// for its stores, a flag round trip and then the data round trip; polling the
+// data costs one round trip after the last write lands.  Two sets of regions
+// alternate between launches: a launch clears, as it goes, its own entries of
+// the set the previous launch used, which the next launch then finds zeroed.
+// Weights that a later phase needs and that are known earlier (the down rows
+// of the chosen experts, the next layer's router rows) are copied into LDS
+// while the current phase's loads are in flight.  Every wait is bounded: a
+// value that never arrives (a workgroup that never became resident) sets the
+// error word and the kernel runs out instead of hanging.  The int4 dot
+// products are those of the decode GEMV kernels (exact integer v_dot8_i32_i4
+// of the nibbles against 16-bit fixed point activations per group).
 #include "common.h"
 #include "kernels.h"
 #include "q4_lane.h"
@@ -55,7 +58,7 @@ constexpr int kDP = 4, kDR = kWave / kDP, kDGPP = 3, kDGMAX = kDP * kDGPP;  // f
 constexpr int kDChunks = 2 * kDGMAX;  // 16-byte chunks (32 nibbles) of one down row at most
 constexpr int kMaxE = 256;
 constexpr int kPartBatch = 12;         // float4 loads in flight per thread when summing router partials
-constexpr uint32_t kSpinLimit = 300000u;  // polling rounds (~1 us each) per barrier at most
+constexpr uint32_t kSpinLimit = 300000u;  // polling rounds (~1 us each) per wait at most
 
 struct FusedArgs {
   float* x_io;  // [L+1][d]
@@ -73,16 +76,17 @@ struct FusedArgs {
   int32_t* topk_idx;  // [L][k]
   float* topk_w;      // [L][k]
   float* x_next;      // [d] or null
-  uint64_t* sync;     // [0] last barrier sequence number of the previous launch
-  uint32_t* err;
-  uint32_t* flags;    // [G] barrier arrival flags (sequence numbers)
-  // Per-layer regions, each starting on its own 256-byte boundary (act_ls,
-  // part_ls, ss_ls floats apart): a cache line read in one layer never holds
-  // values that another XCD writes later in the launch.
-  float* act;    // [L][act_ls]: [k][f] act rows of the chosen experts
-  float* part;   // [L][part_ls]: [G][epad] router partials of each layer's input (one row per workgroup)
-  float* sumsq;  // [L+1][ss_ls]: [G] partial sums of squares of each layer's input (and of the last output)
-  int act_ls, part_ls, ss_ls;
+  uint64_t* launches; // launches run on this workspace (its parity picks the region set)
+  uint64_t* sig;      // shape signature of the launches that use this workspace (0: none yet)
+  uint64_t my_sig;
+  uint32_t* err;      // 1: a wait timed out; 2: the workspace was used with other shapes
+  // Two sets of per-layer regions (set 1 at set_floats after set 0), each
+  // region on its own 256-byte boundary; encoded values, 0 = not written yet.
+  uint32_t* regions;
+  int64_t set_floats;
+  int64_t act_off, part_off, ss_off, xs_off;  // region offsets inside a set (words)
+  int act_ls, part_ls, ss_ls, xs_ls;  // words per layer: [k][f] act, [G][epad] router
+                                      // partials, [G] sums of squares, [d] layer input
   int epad;      // E rounded up to 32: each workgroup's partials fill whole 128-byte lines
   int G, rpw;    // workgroups, down rows per workgroup (a multiple of 4, at most 16)
   int nck_g, nck_d;
@@ -92,78 +96,117 @@ constexpr int kRsrcWord3F = 0x00020000;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3F);
 }
-// Plain (L2-cached) loads of values written earlier in this launch by other
-// workgroups: every such buffer has one region per layer, so no address is
-// read before its last write in a launch, and the first read on an XCD fetches
-// the written-through line from memory.
+// Plain loads (the caller's input token, which no workgroup writes).
 __device__ __forceinline__ float ldn(__amdgpu_buffer_rsrc_t r, int idx) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, idx * 4, 0, 0));
 }
 __device__ __forceinline__ float4 ldn4(__amdgpu_buffer_rsrc_t r, int idx) {  // idx % 4 == 0
   return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, idx * 4, 0, 0));
 }
-__device__ __forceinline__ void st_c(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// 16-byte store written through to memory (sc1), like st_c.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void st_c4(__amdgpu_buffer_rsrc_t r, int idx, float4 v) {  // idx % 4 == 0
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, idx * 4, 0, 16);
+
+// Values handed between workgroups travel as the complement of their bits,
+// NaNs made canonical first: no value encodes to zero, and a zero word (the
+// zero-filled workspace, or an entry cleared by the previous launch) is one
+// that has not been written yet.
+__device__ __forceinline__ uint32_t enc(float v) {
+  return ~(v != v ? 0x7FC00000u : __builtin_bit_cast(uint32_t, v));
 }
+__device__ __forceinline__ float dec(uint32_t u) { return __builtin_bit_cast(float, ~u); }
+__device__ __forceinline__ float4 dec4(u32x4_t u) { return make_float4(dec(u.x), dec(u.y), dec(u.z), dec(u.w)); }
+__device__ __forceinline__ bool ready4(u32x4_t u) { return u.x != 0u && u.y != 0u && u.z != 0u && u.w != 0u; }
+
+// Stores written through to memory (sc1) and coherent (sc1) loads, which see
+// what other XCDs wrote in this launch.
+constexpr int kSc1 = 16;
+__device__ __forceinline__ void st_e(__amdgpu_buffer_rsrc_t r, int idx, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(enc(v), r, idx * 4, 0, kSc1);
+}
+__device__ __forceinline__ void st_e4(__amdgpu_buffer_rsrc_t r, int idx, float4 v) {  // idx % 4 == 0
+  const u32x4_t u = {enc(v.x), enc(v.y), enc(v.z), enc(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(u, r, idx * 4, 0, kSc1);
+}
+__device__ __forceinline__ void st_zero4(__amdgpu_buffer_rsrc_t r, int idx) {  // idx % 4 == 0
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  __builtin_amdgcn_raw_buffer_store_b128(z, r, idx * 4, 0, kSc1);
+}
+__device__ __forceinline__ uint32_t ldc(__amdgpu_buffer_rsrc_t r, int idx) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, idx * 4, 0, kSc1);
+}
+__device__ __forceinline__ u32x4_t ldc4(__amdgpu_buffer_rsrc_t r, int idx) {  // idx % 4 == 0
+  return __builtin_amdgcn_raw_buffer_load_b128(r, idx * 4, 0, kSc1);
+}
+
+// Re-load an encoded word (or four) until it has been written.  A wait that
+// outlasts kSpinLimit rounds, or any wait after one in this workgroup did,
+// gives up: the error word is set and the value decodes to NaN.
+__device__ __forceinline__ bool give_up(const FusedArgs& a, uint32_t& spins, volatile int* s_fail) {
+  if (*s_fail) return true;
+  if (++spins > kSpinLimit) {
+    __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_fail = 1;
+    return true;
+  }
+  __builtin_amdgcn_s_sleep(1);
+  asm volatile("" ::: "memory");  // the next load is a new load
+  return false;
+}
+// Waits for N words (or N groups of four) at once: every round re-issues the
+// loads of all entries not written yet, so a wait costs one round trip after
+// the last write lands, however many entries it covers.
+template <int N>
+__device__ __forceinline__ void wait_all(const FusedArgs& a, __amdgpu_buffer_rsrc_t r, const int (&idx)[N],
+                                         uint32_t (&v)[N], volatile int* s_fail) {
+  uint32_t spins = 0;
+  for (;;) {
+    bool pend = false;
+#pragma unroll
+    for (int c = 0; c < N; ++c) pend |= v[c] == 0u;
+    if (!pend || give_up(a, spins, s_fail)) return;
+#pragma unroll
+    for (int c = 0; c < N; ++c)
+      if (v[c] == 0u) v[c] = ldc(r, idx[c]);
+  }
+}
+template <int N>
+__device__ __forceinline__ void wait_all4(const FusedArgs& a, __amdgpu_buffer_rsrc_t r, const int (&idx)[N],
+                                          u32x4_t (&v)[N], volatile int* s_fail) {
+  uint32_t spins = 0;
+  for (;;) {
+    bool pend = false;
+#pragma unroll
+    for (int c = 0; c < N; ++c) pend |= !ready4(v[c]);
+    if (!pend || give_up(a, spins, s_fail)) return;
+#pragma unroll
+    for (int c = 0; c < N; ++c)
+      if (!ready4(v[c])) v[c] = ldc4(r, idx[c]);
+  }
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ lds_ptr_t to_lds(void* p) { return (lds_ptr_t)(p); }
 
 // Threads that share one expert in the sums over experts (E <= 256).
 __device__ __forceinline__ int threads_per_expert(int E) { return E <= 64 ? 8 : (E <= 128 ? 4 : 2); }
 
-// Device-wide barrier with sequence number `seq` (it grows across launches;
-// compared modulo 2^32).  Each workgroup publishes its arrival in its own
-// flag word with a write-through store; kPollWaves waves of every workgroup
-// then read all G flags at once with coherent (sc1) loads until none is
-// behind, their rounds staggered by a quarter of a round trip, and the first
-// wave to see the last arrival tells the others through LDS.  No
-// read-modify-write: atomics on one shared counter serialise at the memory
-// side (~15 ns per arrival), flags cost one store and one round of loads.
-constexpr int kPollWaves = 4;
-__device__ __forceinline__ void grid_sync(const FusedArgs& a, uint32_t seq, volatile int* s_done) {
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores (and LDS copies) are complete
-  if (threadIdx.x == 0) *s_done = 0;
-  __syncthreads();
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  if (wave == 0 && lane == 0) __hip_atomic_store(a.flags + blockIdx.x, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (wave < kPollWaves) {
-    for (int i = 0; i < 4 * wave; ++i) __builtin_amdgcn_s_sleep(2);  // ~128 clocks each
-    const uint32_t* p0 = a.flags + min(lane, a.G - 1);
-    const uint32_t* p1 = a.flags + min(lane + kWave, a.G - 1);
-    const uint32_t* p2 = a.flags + min(lane + 2 * kWave, a.G - 1);
-    const uint32_t* p3 = a.flags + min(lane + 3 * kWave, a.G - 1);
-    uint32_t spins = 0;
-    while (*s_done == 0) {
-      uint32_t v0, v1, v2, v3;
-      asm volatile(
-          "global_load_dword %0, %4, off sc1\n\t"
-          "global_load_dword %1, %5, off sc1\n\t"
-          "global_load_dword %2, %6, off sc1\n\t"
-          "global_load_dword %3, %7, off sc1\n\t"
-          "s_waitcnt vmcnt(0)"
-          : "=v"(v0), "=v"(v1), "=v"(v2), "=v"(v3)
-          : "v"(p0), "v"(p1), "v"(p2), "v"(p3)
-          : "memory");
-      const bool behind = (int32_t)(v0 - seq) < 0 || (int32_t)(v1 - seq) < 0 || (int32_t)(v2 - seq) < 0 ||
-                          (int32_t)(v3 - seq) < 0;
-      if (!__any(behind)) {
-        *s_done = 1;
-        break;
-      }
-      if (++spins > kSpinLimit) {
-        if (lane == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *s_done = 1;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
+// The region words of one set that this workgroup writes for `layer` are
+// cleared for the launch after next (the one that uses that set again):
+// its act columns, its row of router partials and its sum of squares, and
+// its rows of the layer input (layer >= 1).  `clear_last` adds the sum of
+// squares of the last output.
+__device__ __forceinline__ void clear_own(const FusedArgs& a, int t, __amdgpu_buffer_rsrc_t r, int layer,
+                                          int act0, int r0, int nr, bool clear_last) {
+  const int g = blockIdx.x;
+  const int na = 32 / 4, np = a.epad / 4, nx = (nr + 3) / 4;
+  if (t < na) st_zero4(r, (int)a.act_off + layer * a.act_ls + act0 + 4 * t);
+  else if (t < na + np) st_zero4(r, (int)a.part_off + layer * a.part_ls + g * a.epad + 4 * (t - na));
+  else if (t < na + np + nx) {
+    if (layer >= 1) st_zero4(r, (int)a.xs_off + layer * a.xs_ls + r0 + 4 * (t - na - np));
+  } else if (t == na + np + nx) {
+    __builtin_amdgcn_raw_buffer_store_b32(0u, r, ((int)a.ss_off + layer * a.ss_ls + g) * 4, 0, kSc1);
+    if (clear_last)
+      __builtin_amdgcn_raw_buffer_store_b32(0u, r, ((int)a.ss_off + (layer + 1) * a.ss_ls + g) * 4, 0, kSc1);
   }
-  __syncthreads();
 }
 
 // Copies into LDS (no registers held while in flight): router rows
@@ -213,7 +256,7 @@ __device__ __forceinline__ void down_rows_to_lds(const FusedArgs& a, int t, cons
 // The row of E values goes out as whole 128-byte lines (s_pe holds zeros past
 // E).  Fixed summation order, the same in every launch.
 __device__ __forceinline__ void write_partials(const FusedArgs& a, int t, int layer, const float4* rw, const float* z,
-                                               const float* y, float* s_pe) {
+                                               const float* y, float* s_pe, __amdgpu_buffer_rsrc_t rc) {
   const int g = blockIdx.x;
   if (layer < a.L) {
     const int tq = threads_per_expert(a.E), rpt = kDR / tq;
@@ -231,13 +274,11 @@ __device__ __forceinline__ void write_partials(const FusedArgs& a, int t, int la
   if (t < kWave) {
     const float v = t < kDR ? y[t] : 0.0f;
     const float ss = wave_sum(v * v);
-    if (t == 0) st_c(a.sumsq + (int64_t)layer * a.ss_ls + g, ss);
+    if (t == 0) st_e(rc, (int)a.ss_off + layer * a.ss_ls + g, ss);
   }
   __syncthreads();
-  if (layer < a.L && t < a.epad / 4) {
-    const __amdgpu_buffer_rsrc_t r = rsrc_of(a.part + (int64_t)layer * a.part_ls, (int64_t)a.part_ls * 4);
-    st_c4(r, g * a.epad + 4 * t, reinterpret_cast<const float4*>(s_pe)[t]);
-  }
+  if (layer < a.L && t < a.epad / 4)
+    st_e4(rc, (int)a.part_off + layer * a.part_ls + g * a.epad + 4 * t, reinterpret_cast<const float4*>(s_pe)[t]);
 }
 
 __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
@@ -253,29 +294,40 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
   __shared__ float4 s_red4[kFThreads];         // router partial sums per (slice, quad of experts)
   __shared__ int s_table[kMaxE];               // this layer's slot per expert
   __shared__ float s_val[16];
-  __shared__ float s_inv;
   __shared__ int s_idx[16];
   __shared__ float s_w[16];
   __shared__ float2 s_gu[kGP / kGPW][kActCols];  // (gate, up) partial sums per part block and column
   __shared__ float s_o[kFWaves][kDR];          // down outputs per expert rank
-  __shared__ float s_y[kDR], s_z[kDR];         // this workgroup's output rows, and norm weight * rows
-  __shared__ uint32_t s_base;
-  __shared__ int s_done;                       // barrier: some polling wave saw every arrival
+  __shared__ float s_y[kDR], s_z[kDR];         // this workgroup's rows of the layer input / output, norm weight * rows
+  __shared__ uint64_t s_launch;
+  __shared__ int s_stop;                       // the workspace belongs to other shapes
+  __shared__ int s_fail;                       // a wait of this workgroup gave up
   float* s_logit = reinterpret_cast<float*>(s_logit4);
   const int t0 = threadIdx.x;
   const int g = blockIdx.x;
   const int t = t0, lane = t0 % kWave;
-  if (t == 0) s_base = (uint32_t)__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (t == 0) {
+    const uint64_t sig = __hip_atomic_load(a.sig, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_launch = __hip_atomic_load(a.launches, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_stop = (sig != 0u && sig != a.my_sig) ? 1 : 0;
+    s_fail = 0;
+    if (s_stop) __hip_atomic_store(a.err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   float* s_pe = reinterpret_cast<float*>(s_pe4);
   uint64_t* s_key = reinterpret_cast<uint64_t*>(s_key4);
   if (t < 4) s_key[a.E + t] = 0;
   if (t >= a.E && t < a.epad) s_pe[t] = 0.0f;
+  __syncthreads();
+  if (s_stop) return;  // regions laid out for other shapes: nothing is read or written
+  const uint64_t launch = s_launch;
+  const int set = (int)(launch & 1u);
   const int Gd = a.d / kGroup, Gf = a.f / kGroup;
   const int r0 = g * a.rpw, nr = max(0, min(a.rpw, a.d - r0));
+  const int jr0 = g / (a.f / kActCols), c00 = (g % (a.f / kActCols)) * kActCols;  // gate/up expert rank, act columns
   const __amdgpu_buffer_rsrc_t rX = rsrc_of(a.x_io, (int64_t)(a.L + 1) * a.d * 4);
-  const __amdgpu_buffer_rsrc_t rAct = rsrc_of(a.act, (int64_t)a.L * a.act_ls * 4);
-  const __amdgpu_buffer_rsrc_t rPart = rsrc_of(a.part, (int64_t)a.L * a.part_ls * 4);
-  const __amdgpu_buffer_rsrc_t rSS = rsrc_of(a.sumsq, (int64_t)(a.L + 1) * a.ss_ls * 4);
+  // this launch's region set, and the one the previous launch used (cleared for the next)
+  const __amdgpu_buffer_rsrc_t rc = rsrc_of(a.regions + set * a.set_floats, a.set_floats * 4);
+  const __amdgpu_buffer_rsrc_t ro = rsrc_of(a.regions + (1 - set) * a.set_floats, a.set_floats * 4);
   const int tq = threads_per_expert(a.E);
 
   // ---- prologue: router partials of layer 0 over this workgroup's rows of x_io[0]
@@ -283,12 +335,9 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
   router_rows_to_lds(a, t, 0, r0, s_rw, s_rnw);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  const uint32_t base = s_base;
-  int nbar = 0;
   if (t < kDR) s_z[t] = t < nr ? s_y[t] * (a.norm_w ? reinterpret_cast<const float*>(s_rnw)[t] : 1.0f) : 0.0f;
   __syncthreads();
-  write_partials(a, t, 0, s_rw, s_z, s_y, s_pe);
-  grid_sync(a, base + (uint32_t)++nbar, &s_done);
+  write_partials(a, t, 0, s_rw, s_z, s_y, s_pe, rc);
 
   for (int l = 0; l < a.L; ++l) {
     // Thread-derived indices are recomputed from an opaque copy of the thread
@@ -297,24 +346,37 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
     int tid = t0;
     asm volatile("" : "+v"(tid));
     const int t = tid, lane = t % kWave, wave = __builtin_amdgcn_readfirstlane(t / kWave);
-    const int xo = l * a.d;  // x = x_io[l]
     // ================= gate/up phase =================
     // Everything that does not depend on the routing goes out at once: the
     // slot table, the router bias, the sums of squares, x and the norm
     // weight, then the router partials.
     if (t < a.E) s_table[t] = a.slot_tables[(int64_t)l * a.E + t];
     const float bias = (a.router_bias && t < a.E) ? a.router_bias[(int64_t)l * a.E + t] : 0.0f;
-    float ssv[4];
+    uint32_t ssu[4];
+    int ssi[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) ssv[c] = ldn(rSS, l * a.ss_ls + min(lane + c * kWave, a.G - 1));
+    for (int c = 0; c < 4; ++c) {
+      ssi[c] = (int)a.ss_off + l * a.ss_ls + min(lane + c * kWave, a.G - 1);
+      ssu[c] = ldc(rc, ssi[c]);
+    }
     constexpr int NPASSG = (8 * kGGMAX + kFThreads - 1) / kFThreads;
     StageRegs<NPASSG> xr, nwr;
     const float* nw = a.norm_w ? a.norm_w + (int64_t)l * a.d : nullptr;
+    const int xs0 = (int)a.xs_off + l * a.xs_ls;
+    u32x4_t xu[2 * NPASSG];
+    int xi[2 * NPASSG];
 #pragma unroll
     for (int ps = 0; ps < NPASSG; ++ps) {
       const int wi = min(ps * kFThreads + t, 8 * Gd - 1);
-      xr.a[ps] = ldn4(rX, xo + wi * 8);
-      xr.b[ps] = ldn4(rX, xo + wi * 8 + 4);
+      xi[2 * ps] = xs0 + wi * 8;
+      xi[2 * ps + 1] = xs0 + wi * 8 + 4;
+      if (l == 0) {
+        xr.a[ps] = ldn4(rX, wi * 8);
+        xr.b[ps] = ldn4(rX, wi * 8 + 4);
+      } else {
+        xu[2 * ps] = ldc4(rc, xi[2 * ps]);
+        xu[2 * ps + 1] = ldc4(rc, xi[2 * ps + 1]);
+      }
       nwr.a[ps] = nw ? *reinterpret_cast<const float4*>(nw + wi * 8) : make_float4(1.f, 1.f, 1.f, 1.f);
       nwr.b[ps] = nw ? *reinterpret_cast<const float4*>(nw + wi * 8 + 4) : make_float4(1.f, 1.f, 1.f, 1.f);
     }
@@ -327,28 +389,43 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
       if (sl < ns) {
         const int g0 = sl * gper, g1 = min(a.G, g0 + gper);
-        const int pb = l * a.part_ls + 4 * qd;
+        const int pb = (int)a.part_off + l * a.part_ls + 4 * qd;
         for (int b = g0; b < g1; b += kPartBatch) {
-          float4 v[kPartBatch];
+          u32x4_t v[kPartBatch];
+          int vi[kPartBatch];
 #pragma unroll
-          for (int c = 0; c < kPartBatch; ++c) v[c] = ldn4(rPart, pb + min(b + c, g1 - 1) * a.epad);
+          for (int c = 0; c < kPartBatch; ++c) {
+            vi[c] = pb + min(b + c, g1 - 1) * a.epad;
+            v[c] = ldc4(rc, vi[c]);
+          }
+          wait_all4<kPartBatch>(a, rc, vi, v, &s_fail);
 #pragma unroll
           for (int c = 0; c < kPartBatch; ++c)
             if (b + c < g1) {
-              acc.x += v[c].x;
-              acc.y += v[c].y;
-              acc.z += v[c].z;
-              acc.w += v[c].w;
+              const float4 u = dec4(v[c]);
+              acc.x += u.x;
+              acc.y += u.y;
+              acc.z += u.z;
+              acc.w += u.w;
             }
         }
         s_red4[sl * nq + qd] = acc;
       }
     }
+    wait_all<4>(a, rc, ssi, ssu, &s_fail);
     float ss = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) ss += lane + c * kWave < a.G ? ssv[c] : 0.0f;
+    for (int c = 0; c < 4; ++c) ss += lane + c * kWave < a.G ? dec(ssu[c]) : 0.0f;
     ss = wave_sum(ss);
     const float inv = a.norm_w ? 1.0f / sqrtf(ss / (float)a.d + a.eps) : 1.0f;
+    if (l > 0) {
+      wait_all4<2 * NPASSG>(a, rc, xi, xu, &s_fail);
+#pragma unroll
+      for (int ps = 0; ps < NPASSG; ++ps) {
+        xr.a[ps] = dec4(xu[2 * ps]);
+        xr.b[ps] = dec4(xu[2 * ps + 1]);
+      }
+    }
     __syncthreads();
     if (t < a.E) {
       // the slices in a fixed order (the same in every workgroup)
@@ -443,7 +520,7 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
           us += s_gu[q][t].y;
         }
         const float v2 = ok ? gelu_tanh(gs) * us : f32_nan();
-        st_c(a.act + (int64_t)l * a.act_ls + jr * a.f + c0 + t, v2);
+        st_e(rc, (int)a.act_off + l * a.act_ls + jr * a.f + c0 + t, v2);
       }
     }
     if (wave == kFWaves - 1) {
@@ -459,9 +536,15 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
           a.topk_w[(int64_t)l * a.k + lane] = ex / sum;
         }
       }
+    } else if (wave == kFWaves - 2) {
+      // this workgroup's entries of the other set for this layer are cleared
+      // for the launch after next
+      clear_own(a, lane + kWave, ro, l, jr0 * a.f + c00, r0, nr, l + 1 == a.L);
+    } else if (wave == kFWaves - 3) {
+      clear_own(a, lane, ro, l, jr0 * a.f + c00, r0, nr, l + 1 == a.L);
+    } else if (wave == kFWaves - 4) {
+      clear_own(a, lane + 2 * kWave, ro, l, jr0 * a.f + c00, r0, nr, l + 1 == a.L);
     }
-
-    grid_sync(a, base + (uint32_t)++nbar, &s_done);
 
     // ================= down phase =================
     {
@@ -475,14 +558,26 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
       constexpr int NPASS = (8 * kDGMAX + kWave - 1) / kWave;
       StageRegs<NPASS> sr;
       if (wave_on) {
+        const int ab = (int)a.act_off + l * a.act_ls + jw * a.f;
+        u32x4_t au[2 * NPASS];
+        int ai[2 * NPASS];
 #pragma unroll
         for (int ps = 0; ps < NPASS; ++ps) {
           const int wi = min(ps * kWave + lane, 8 * Gf - 1);
-          sr.a[ps] = ldn4(rAct, l * a.act_ls + jw * a.f + wi * 8);
-          sr.b[ps] = ldn4(rAct, l * a.act_ls + jw * a.f + wi * 8 + 4);
+          ai[2 * ps] = ab + wi * 8;
+          ai[2 * ps + 1] = ab + wi * 8 + 4;
+          au[2 * ps] = ldc4(rc, ai[2 * ps]);
+          au[2 * ps + 1] = ldc4(rc, ai[2 * ps + 1]);
+        }
+        wait_all4<2 * NPASS>(a, rc, ai, au, &s_fail);
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps) {
+          sr.a[ps] = dec4(au[2 * ps]);
+          sr.b[ps] = dec4(au[2 * ps + 1]);
         }
       }
-      const float xres = (t < nr) ? ldn(rX, xo + r0 + t) : 0.0f;
+      // the residual: this workgroup's rows of the layer input
+      const float xres = (t < nr) ? s_y[t] : 0.0f;
       LaneSlice<kDGPP> wd;
       if (wave_on) {
 #pragma unroll
@@ -509,30 +604,43 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
         if (t < nr) {
           y = xres;
           for (int jj = 0; jj < a.k; ++jj) y = fmaf(s_w[jj], s_o[jj][t], y);
-          st_c(a.x_io + (int64_t)(l + 1) * a.d + r0 + t, y);
+          a.x_io[(int64_t)(l + 1) * a.d + r0 + t] = y;
           z = y * ((a.norm_w && l + 1 < a.L) ? reinterpret_cast<const float*>(s_rnw)[t] : 1.0f);
         }
         s_y[t] = y;
         s_z[t] = z;
       }
       __syncthreads();
-      write_partials(a, t, l + 1, s_rw, s_z, s_y, s_pe);
+      // the next layer's input rows for the other workgroups, then its router partials
+      if (l + 1 < a.L && t < nr / 4)
+        st_e4(rc, (int)a.xs_off + (l + 1) * a.xs_ls + r0 + 4 * t, reinterpret_cast<const float4*>(s_y)[t]);
+      write_partials(a, t, l + 1, s_rw, s_z, s_y, s_pe, rc);
     }
-    grid_sync(a, base + (uint32_t)++nbar, &s_done);
   }
 
   // unit-RMS rescale of the last output for the next decode step
   if (a.x_next) {
+    uint32_t su[4];
+    int si[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      si[c] = (int)a.ss_off + a.L * a.ss_ls + min(lane + c * kWave, a.G - 1);
+      su[c] = ldc(rc, si[c]);
+    }
+    wait_all<4>(a, rc, si, su, &s_fail);
     float ss = 0.0f;
-    for (int i = lane; i < a.G; i += kWave) ss += ldn(rSS, a.L * a.ss_ls + i);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ss += lane + c * kWave < a.G ? dec(su[c]) : 0.0f;
     ss = wave_sum(ss);
     const float inv = 1.0f / sqrtf(ss / (float)a.d + a.eps);
     if (t < nr) a.x_next[r0 + t] = s_y[t] * inv;
   }
-  // the next launch on this workspace continues the barrier sequence (every
-  // workgroup read it before the first barrier)
-  if (g == 0 && t == 0) __hip_atomic_store(a.sync, (uint64_t)(base + (uint32_t)nbar), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+  // the next launch on this workspace uses the other set (every workgroup
+  // read the count before it wrote anything that workgroup 0 waited for)
+  if (g == 0 && t == 0) {
+    __hip_atomic_store(a.sig, a.my_sig, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.launches, launch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 }  // namespace
@@ -551,12 +659,15 @@ bool decode_fused_supported(int d, int f, int E, int k, int cus, int* G_out, int
 }
 
 namespace {
+// Workspace: a 512-byte header (launch count at 0, shape signature at 8, error
+// word at kDecodeErrOffset), then two region sets of set_floats words each.
 struct FusedLayout {
-  int act_ls, part_ls, ss_ls;  // floats per layer region, multiples of 64 (256 bytes)
+  int act_ls, part_ls, ss_ls, xs_ls;  // words per layer region, multiples of 64 (256 bytes)
   int epad;
-  int64_t flags_off, act_off, part_off, ss_off, bytes;
+  int64_t act_off, part_off, ss_off, xs_off, set_floats;  // words inside a set
+  int64_t regions_off, bytes;
 };
-FusedLayout fused_layout(int L, int f, int E, int k) {
+FusedLayout fused_layout(int L, int d, int f, int E, int k) {
   const int G = k * (f / kActCols);
   auto r64 = [](int64_t n) { return (int)((n + 63) / 64 * 64); };
   FusedLayout o;
@@ -564,18 +675,20 @@ FusedLayout fused_layout(int L, int f, int E, int k) {
   o.epad = (E + 31) / 32 * 32;
   o.part_ls = r64((int64_t)G * o.epad);
   o.ss_ls = r64(G);
-  o.flags_off = 512;
-  o.act_off = 512 + 1024;
-  o.part_off = o.act_off + (int64_t)L * o.act_ls * 4;
-  o.ss_off = o.part_off + (int64_t)L * o.part_ls * 4;
-  o.bytes = o.ss_off + (int64_t)(L + 1) * o.ss_ls * 4;
+  o.xs_ls = r64(d);
+  o.act_off = 0;
+  o.part_off = o.act_off + (int64_t)L * o.act_ls;
+  o.ss_off = o.part_off + (int64_t)L * o.part_ls;
+  o.xs_off = o.ss_off + (int64_t)(L + 1) * o.ss_ls;
+  o.set_floats = o.xs_off + (int64_t)L * o.xs_ls;
+  o.regions_off = 512;
+  o.bytes = o.regions_off + 2 * o.set_floats * 4;
   return o;
 }
 }  // namespace
 
 size_t decode_fused_workspace_bytes(int L, int d, int f, int E, int k) {
-  (void)d;
-  return (size_t)fused_layout(L, f, E, k).bytes;
+  return (size_t)fused_layout(L, d, f, E, k).bytes;
 }
 
 hipError_t launch_decode_fused(float* x_io, int L, const float* norm_w, float eps, const float* router_w,
@@ -603,17 +716,28 @@ hipError_t launch_decode_fused(float* x_io, int L, const float* norm_w, float ep
   a.topk_w = topk_w;
   a.x_next = x_next;
   char* c = reinterpret_cast<char*>(ws);
-  a.sync = reinterpret_cast<uint64_t*>(c);
+  a.launches = reinterpret_cast<uint64_t*>(c);
+  a.sig = reinterpret_cast<uint64_t*>(c + 8);
   a.err = reinterpret_cast<uint32_t*>(c + kDecodeErrOffset);
-  const FusedLayout lay = fused_layout(L, f, E, k);
-  a.flags = reinterpret_cast<uint32_t*>(c + lay.flags_off);
-  a.act = reinterpret_cast<float*>(c + lay.act_off);
-  a.part = reinterpret_cast<float*>(c + lay.part_off);
-  a.sumsq = reinterpret_cast<float*>(c + lay.ss_off);
+  const FusedLayout lay = fused_layout(L, d, f, E, k);
+  a.regions = reinterpret_cast<uint32_t*>(c + lay.regions_off);
+  a.set_floats = lay.set_floats;
+  a.act_off = lay.act_off;
+  a.part_off = lay.part_off;
+  a.ss_off = lay.ss_off;
+  a.xs_off = lay.xs_off;
   a.act_ls = lay.act_ls;
   a.part_ls = lay.part_ls;
-  a.epad = lay.epad;
   a.ss_ls = lay.ss_ls;
+  a.xs_ls = lay.xs_ls;
+  a.epad = lay.epad;
+  // the shapes that fix the region layout, never 0
+  uint64_t sig = 1469598103934665603ull;
+  for (int64_t v : {(int64_t)L, (int64_t)d, (int64_t)f, (int64_t)E, (int64_t)k, (int64_t)G, (int64_t)rpw}) {
+    sig ^= (uint64_t)v;
+    sig *= 1099511628211ull;
+  }
+  a.my_sig = sig | 1u;
   a.G = G;
   a.rpw = rpw;
   a.nck_g = 2 * kGGPP;

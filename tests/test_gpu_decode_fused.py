@@ -99,7 +99,8 @@ def test_decode_layers_ragged_shape(api):
 
 def test_decode_layers_absent_slot_gives_nan(api):
     """A chosen expert whose slot table entry is -1 is never read: that layer's
-    output is NaN, and the launch still completes without a barrier error."""
+    output is NaN (which the next layer's waits still see as written), and the
+    launch completes without a wait error."""
     d, f, E, k, L = 256, 128, 16, 4, 2
     st = Stack(api, d, f, E, k, L, seed=18)
     x0 = synth.tokens(1, d, 18)[0]
@@ -146,9 +147,10 @@ def test_decode_layers_matches_per_call_path(api):
 
 
 def test_decode_layers_repeat_and_feedback(api):
-    """Several launches on one workspace (the barrier state carries over): a
-    fixed input gives identical outputs every time, and x_next is the unit-RMS
-    rescale of the last layer's output."""
+    """Several launches on one workspace (its two region sets alternate, each
+    launch clearing the set the previous one used): a fixed input gives
+    identical outputs every time, and x_next is the unit-RMS rescale of the
+    last layer's output."""
     d, f, E, k, L = 640, 192, 32, 8, 3
     st = Stack(api, d, f, E, k, L, seed=14)
     x0 = synth.tokens(1, d, 14)[0]
@@ -198,3 +200,34 @@ def test_decode_layers_rejects_bad_arguments(api):
     with pytest.raises(api.MoeError):  # layer stride below n_slots * slot_stride
         api.moe_decode_layers(x_io, 1, st.nw_d, 1e-6, st.rw_d, st.bias_d, st.tables, 16, st.arena, st.stride,
                               st.stride, st.dm, idx, w, None, st.ws)
+
+
+def test_decode_layers_workspace_bound_to_its_shapes(api):
+    """A workspace that served one shape is refused for another (its regions
+    are laid out for the first): the launch writes nothing and
+    moe_decode_check reports it; zero-filled again it serves the new shape."""
+    a = Stack(api, 256, 128, 16, 4, 2, seed=19)
+    b = Stack(api, 256, 128, 16, 4, 3, seed=20)
+    x0 = synth.tokens(1, 256, 19)[0]
+    a.run(api, x0)
+    b.ws[:512].copy_(a.ws[:512])  # the header: launch count and the 2-layer shape's signature
+    with pytest.raises(api.MoeError):
+        b.run(api, x0)
+    b.ws.zero_()
+    x_io, idx, w = b.run(api, x0)
+    _check_layers(b, x_io, idx, w)
+
+
+def test_decode_layers_two_workspaces_interleaved(api):
+    """Two stacks, each with its own workspace, launched alternately on one
+    stream: each keeps giving the result of its first launch."""
+    a = Stack(api, 256, 128, 16, 4, 2, seed=21)
+    b = Stack(api, 256, 128, 24, 4, 3, seed=22)
+    xa, xb = synth.tokens(1, 256, 21)[0], synth.tokens(1, 256, 22)[0]
+    ra, rb = a.run(api, xa), b.run(api, xb)
+    _check_layers(a, *ra)
+    _check_layers(b, *rb)
+    for _ in range(3):
+        for st, x, ref in ((a, xa, ra), (b, xb, rb)):
+            got = st.run(api, x)
+            assert all(np.array_equal(u, v) for u, v in zip(got, ref))
