@@ -28,9 +28,10 @@
 // data costs one round trip after the last write lands.  Two sets of regions
 // alternate between launches: a launch clears, as it goes, its own entries of
 // the set the previous launch used, which the next launch then finds zeroed.
-// Weights that a later phase needs and that are known earlier (the down rows
-// of the chosen experts, the next layer's router rows) are copied into LDS
-// while the current phase's loads are in flight.  Every wait is bounded: a
+// Weights that the down phase needs (the chosen experts' down rows, into
+// registers, and the next layer's router rows, into LDS) are requested as the
+// phase begins and arrive while it waits for the act values, so the gate/up
+// phase streams only the gate and up rows.  Every wait is bounded: a
 // value that never arrives (a workgroup that never became resident) sets the
 // error word and the kernel runs out instead of hanging.  The int4 dot
 // products are those of the decode GEMV kernels (exact integer v_dot8_i32_i4
@@ -55,7 +56,6 @@ constexpr int kGP = 16, kGPW = 4, kGR = kWave / kGPW, kGGPP = 3, kGGMAX = kGP * 
 constexpr int kActCols = 2 * kGR;                                                        // 32 act columns
 // down phase: one wave per selected expert; lanes 4 K-parts x 16 rows
 constexpr int kDP = 4, kDR = kWave / kDP, kDGPP = 3, kDGMAX = kDP * kDGPP;  // f/64 <= 12
-constexpr int kDChunks = 2 * kDGMAX;  // 16-byte chunks (32 nibbles) of one down row at most
 constexpr int kMaxE = 256;
 constexpr int kPartBatch = 12;         // float4 loads in flight per thread when summing router partials
 constexpr uint32_t kSpinLimit = 300000u;  // polling rounds (~1 us each) per wait at most
@@ -228,28 +228,6 @@ __device__ __forceinline__ void router_rows_to_lds(const FusedArgs& a, int t, in
   }
 }
 
-// Down rows [r0, r0 + nr) of one expert blob into LDS: 16-byte chunk c of row
-// r at dq[c*16 + r], (scale, bias) word of group i of row r at dsb[i*16 + r].
-// Called by one whole wave; nr >= 1.
-__device__ __forceinline__ void down_rows_to_lds(const FusedArgs& a, int t, const uint8_t* blob, int r0, int nr,
-                                                 uint4* dq, uint32_t* dsb) {
-  const int lane = t % kWave;
-  const int Gf = a.f / kGroup;
-  const __amdgpu_buffer_rsrc_t r = rsrc_of(blob, a.slot_stride);
-  const int row = r0 + min(lane % kDR, nr - 1);
-  const int tile = row / kTileRows, trow = row % kTileRows;
-  const int qb = (int)(a.off_dq + (int64_t)tile * (kTileRows * a.f / 2)) + trow * 16;
-  const int sb = (int)(a.off_dsb + (int64_t)tile * (kTileRows * Gf * 4)) + trow * 4;
-  for (int n = 0; n * 4 < 2 * Gf; ++n) {
-    const int c = min(n * 4 + lane / kDR, 2 * Gf - 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(&dq[n * kWave]), 16, qb + c * (kTileRows * 16), 0, 0, 0);
-  }
-  for (int n = 0; n * 4 < Gf; ++n) {
-    const int gi = min(n * 4 + lane / kDR, Gf - 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(&dsb[n * kWave]), 4, sb + gi * (kTileRows * 4), 0, 0, 0);
-  }
-}
-
 // Router partials of `layer` over this workgroup's rows, from the router rows
 // in LDS and z = w * y (w the norm weight, 1 without one; z = 0 past the
 // rows): part[g][e] = sum_i Wr[e][r0 + i] * z[i], plus sumsq[g] = sum_i y[i]^2.
@@ -284,8 +262,6 @@ __device__ __forceinline__ void write_partials(const FusedArgs& a, int t, int la
 __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
   __shared__ XRow<kGP, kGGMAX> xh;             // h of the current layer (gate/up phase)
   __shared__ XRow<kDP, kDGMAX> xa[kFWaves];    // act rows of the selected experts (down phase)
-  __shared__ uint4 s_dq[kFWaves][kDChunks * kDR];    // down rows of each selected expert
-  __shared__ uint32_t s_dsb[kFWaves][kDGMAX * kDR];  // and their (scale, bias) words
   __shared__ float4 s_rw[kMaxE * kDR / 4];     // next layer's router rows over this workgroup's rows
   __shared__ float4 s_rnw[kWave];              // next layer's norm weight over the rows (first 4 used)
   __shared__ float4 s_logit4[kMaxE / 4 + 1];   // logits
@@ -487,10 +463,6 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
       load_lane<kGGPP>(wg, blob + a.off_gq + qo, blob + a.off_gsb + so, pt, Gd);
       load_lane<kGGPP>(wu, blob + a.off_uq + qo, blob + a.off_usb + so, pt, Gd);
     }
-    // the down phase's expert of this wave (rank = wave)
-    const int e2 = wave < a.k ? s_idx[wave] : -1;
-    const int slot2 = (e2 >= 0 && e2 < a.E) ? s_table[e2] : -1;
-    const uint8_t* blob2 = larena + ((slot2 >= 0 && slot2 < a.n_slots) ? (int64_t)slot2 * a.slot_stride : 0);
     {
       // h = x * inv * w in 8-column words: thread t stages word t
       StageRegs<NPASSG> sr;
@@ -502,10 +474,6 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
       }
       stage_store<kGP, kGGMAX, NPASSG>(xh, sr, Gd, t, kFThreads);
     }
-    // the down phase's weights and the next layer's router rows go to LDS
-    // while the gate/up weights are in flight
-    if (wave < a.k && nr > 0) down_rows_to_lds(a, t, blob2, r0, nr, s_dq[wave], s_dsb[wave]);
-    if (l + 1 < a.L) router_rows_to_lds(a, t, l + 1, r0, s_rw, s_rnw);
     __syncthreads();
     {
       const float2 v = lane_dot2<kGP, kGPW, kGGPP, kGGMAX>(wg, wu, xh, j, pt, Gd, a.nck_g);
@@ -555,6 +523,19 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
       const int ed = wave_on ? s_idx[jw] : -1;
       const int sd = (ed >= 0 && ed < a.E) ? s_table[ed] : -1;
       const bool ok2 = sd >= 0 && sd < a.n_slots;
+      // The expert's down rows go straight to registers and the next layer's
+      // router rows to LDS: both arrive while the act values are awaited,
+      // which leaves the gate/up phase only its own weights to stream.
+      LaneSlice<kDGPP> wd;
+      if (wave_on) {
+        const uint8_t* blob2 = larena + (ok2 ? (int64_t)sd * a.slot_stride : 0);
+        const int rowd = r0 + min(rd, nr - 1);
+        const int64_t tile = rowd / kTileRows;
+        const int trow = rowd % kTileRows;
+        const int64_t qo = tile * (kTileRows * a.f / 2) + trow * 16, so = tile * (kTileRows * Gf * 4) + trow * 4;
+        load_lane<kDGPP>(wd, blob2 + a.off_dq + qo, blob2 + a.off_dsb + so, pd, Gf);
+      }
+      if (l + 1 < a.L) router_rows_to_lds(a, t, l + 1, r0, s_rw, s_rnw);
       constexpr int NPASS = (8 * kDGMAX + kWave - 1) / kWave;
       StageRegs<NPASS> sr;
       if (wave_on) {
@@ -578,20 +559,8 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
       }
       // the residual: this workgroup's rows of the layer input
       const float xres = (t < nr) ? s_y[t] : 0.0f;
-      LaneSlice<kDGPP> wd;
-      if (wave_on) {
-#pragma unroll
-        for (int i = 0; i < kDGPP; ++i) {
-          const int gi = max(0, min(pd.g0 + min(i, pd.ng - 1), Gf - 1));
-          wd.sb[i] = s_dsb[jw][gi * kDR + rd];
-        }
-#pragma unroll
-        for (int i = 0; i < 2 * kDGPP; ++i) {
-          const int c = max(0, min(2 * pd.g0 + min(i, 2 * pd.ng - 1), 2 * Gf - 1));
-          wd.q[i] = s_dq[jw][c * kDR + rd];
-        }
-        stage_store<kDP, kDGMAX, NPASS>(xa[jw], sr, Gf, lane, kWave);
-      }
+      if (wave_on) stage_store<kDP, kDGMAX, NPASS>(xa[jw], sr, Gf, lane, kWave);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's router-row copies have landed in LDS
       __syncthreads();
       if (wave_on) {
         float v = lane_dot<kDP, kDGPP, kDGMAX>(wd, xa[jw], jd, pd, Gf, a.nck_d);
