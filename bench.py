@@ -52,8 +52,8 @@ CSRC = os.path.join(ROOT, "int4_routed_expert_route_amd", "csrc")
 TRAFFIC = {
     "decode": {"sources": ('q4_gemv.hip', 'q4_lane.h', 'common.h'), "sha256_16": "4fb8e1792d1f9193",
                "fetch_bytes": 18093516, "write_bytes": 22528},
-    "decode_fused": {"sources": ('decode_fused.hip', 'q4_lane.h', 'common.h'), "sha256_16": "bab4ca0ec72f74cc",
-                     "fetch_bytes": 954255731, "write_bytes": 4249728},
+    "decode_fused": {"sources": ('decode_fused.hip', 'q4_lane.h', 'common.h'), "sha256_16": "e38b527d1b6f8d39",
+                     "fetch_bytes": 954574168, "write_bytes": 8112864},
     "prefill": {"sources": ('q4_grouped_mfma.hip', 'common.h'), "sha256_16": "27391d2c1695c7f2",
                 "fetch_bytes": 240052090, "write_bytes": 23891904},
 }

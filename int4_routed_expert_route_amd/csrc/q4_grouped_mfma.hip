@@ -72,18 +72,30 @@ struct Op<_Float16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
   // One nibble word (columns 0..7 of a block) -> 8 weights in slot order.
-  // Nibble pairs are masked into fp16 1024 + q (exact), 1024 is subtracted
-  // (exact) and w = fma(q, s, b) rounds once.
-  static __device__ __forceinline__ uint4 dequant8(uint32_t w, uint32_t sb, uint32_t m, uint32_t M) {
-    const f16x2 s2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sb, sb, 0x01000100u));
-    const f16x2 b2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sb, sb, 0x03020302u));
-    const f16x2 off = {(_Float16)1024.0f, (_Float16)1024.0f};
-    const uint32_t p[4] = {(w & m) | M, ((w >> 4) & m) | M, ((w >> 8) & m) | M, ((w >> 12) & m) | M};
-    uint32_t v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      v[j] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2, p[j]) - off, s2, b2));
-    return make_uint4(v[0], v[1], v[2], v[3]);
+  // A nibble pair at bits 0-3 / 16-19 masked under the fp16 exponent of 1024
+  // reads 1024 + q; a pair at bits 4-7 / 20-23 under the exponent of 64 reads
+  // 64 + q (its mantissa step is 1/16).  So one shift by 8 serves all four
+  // pairs.  The offset is subtracted (exact) and w = fma(q, s, b) rounds once.
+  // k holds the masks 0x000F000F, 0x00F000F0 and the exponents 0x64006400,
+  // 0x54005400 in registers (a gfx9 VOP3 takes no literal).
+  struct Consts {
+    uint32_t m0, m4, e10, e6;
+  };
+  static __device__ __forceinline__ uint4 dequant8(uint32_t w, f16x2 s2, f16x2 b2, const Consts& k) {
+    const f16x2 o10 = {(_Float16)1024.0f, (_Float16)1024.0f}, o6 = {(_Float16)64.0f, (_Float16)64.0f};
+    const uint32_t t = w >> 8;
+    const uint32_t p0 = (w & k.m0) | k.e10, p1 = (w & k.m4) | k.e6, p2 = (t & k.m0) | k.e10, p3 = (t & k.m4) | k.e6;
+    uint4 v;
+    v.x = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2, p0) - o10, s2, b2));
+    v.y = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2, p1) - o6, s2, b2));
+    v.z = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2, p2) - o10, s2, b2));
+    v.w = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2, p3) - o6, s2, b2));
+    return v;
+  }
+  // (scale, scale) and (bias, bias) of one (scale, bias) word
+  static __device__ __forceinline__ void split_sb(uint32_t sb, f16x2& s2, f16x2& b2) {
+    s2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sb, sb, 0x01000100u));
+    b2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sb, sb, 0x03020302u));
   }
   static constexpr bool kScaled = true;
 };
@@ -95,7 +107,16 @@ struct Op<__bf16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   // w = s*q + b in fp32 (exact for fp16 s, b), rounded to nearest-even bf16.
-  static __device__ __forceinline__ uint4 dequant8(uint32_t w, uint32_t sb, uint32_t, uint32_t) {
+  // (The fp16 (scale, bias) word travels in both halves of s2; b2 is unused.)
+  struct Consts {
+    uint32_t m0, m4, e10, e6;
+  };
+  static __device__ __forceinline__ void split_sb(uint32_t sb, f16x2& s2, f16x2& b2) {
+    s2 = __builtin_bit_cast(f16x2, sb);
+    b2 = s2;
+  }
+  static __device__ __forceinline__ uint4 dequant8(uint32_t w, f16x2 s2, f16x2, const Consts&) {
+    const uint32_t sb = __builtin_bit_cast(uint32_t, s2);
     const float s = half_lo(sb), b = half_hi(sb);
     __bf16 v[8];
 #pragma unroll
@@ -350,8 +371,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
   const int Nrows = GATEUP ? a.f : a.d;
   const __amdgpu_buffer_rsrc_t rsA =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.a_rows), (short)0, a.a_bytes, kRsrcWord3);
-  uint32_t kMask = 0x000F000Fu, kMagic = 0x64006400u;  // in VGPRs: a gfx9 VOP3 takes no literal
-  asm volatile("" : "+v"(kMask), "+v"(kMagic));
+  typename O::Consts kc{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
+  asm volatile("" : "+v"(kc.m0), "+v"(kc.m4), "+v"(kc.e10), "+v"(kc.e6));  // in VGPRs
   // per-lane LDS addresses inside stage 0 (stage st adds st * sizeof(StageLds))
   const uint32_t lds0 = lds_addr(&lds[0]);
   const uint32_t a_rd0 = lds0 + n * 128 + (((kq * 2) ^ swz(n)) * 16);
@@ -528,10 +549,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
                                         : O::mfma(fb[ng], __builtin_bit_cast(V8, fa[i]), acc[4 * h + i][ng]);
         }
     };
-    auto dequant = [&](V8 (&fb)[4], const u32x2 (&qv)[4], const uint32_t (&sbv)[4], int j) {
+    auto dequant = [&](V8 (&fb)[4], const u32x2 (&qv)[4], const f16x2 (&s2)[4], const f16x2 (&b2)[4], int j) {
 #pragma unroll
       for (int ng = 0; ng < 4; ++ng)
-        fb[ng] = __builtin_bit_cast(V8, O::dequant8(j == 0 ? qv[ng].x : qv[ng].y, sbv[ng], kMask, kMagic));
+        fb[ng] = __builtin_bit_cast(V8, O::dequant8(j == 0 ? qv[ng].x : qv[ng].y, s2[ng], b2[ng], kc));
     };
     auto compute = [&](int s, int st) {
       const uint32_t so = (uint32_t)st * (uint32_t)sizeof(StageLds);
@@ -559,8 +580,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
             sbv[ng] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, sbv[ng]) * c2);
         }
       }
+      f16x2 s2[4], b2[4];
+#pragma unroll
+      for (int ng = 0; ng < 4; ++ng) O::split_sb(sbv[ng], s2[ng], b2[ng]);
       V8 fb[4];
-      dequant(fb, qv, sbv, 0);
+      dequant(fb, qv, s2, b2, 0);
       if (half1) read_half(fy, a_rd0 + so + 8192);  // j = 0, rows 64..127
       mfma_half(fx, fb, 0);
       if (half1) {
@@ -570,7 +594,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
       } else {
         read_half(fx, a_rd1 + so);
       }
-      dequant(fb, qv, sbv, 1);
+      dequant(fb, qv, s2, b2, 1);
       lds_wait(fx);
       if (half1) read_half(fy, a_rd1 + so + 8192);  // j = 1, rows 64..127
       mfma_half(fx, fb, 0);
