@@ -536,6 +536,40 @@ def run_prefill(args, api, torch):
 
 # ----------------------------------------------------------------------------- bounded cache
 
+def staging_burst(api, torch, pool, blob, stride, n_streams, steps=8, slots=64):
+    """Pinned-host -> HBM staging rate of each staging mode: `steps` steps of 8
+    misses each (64 distinct experts of layer 0 into an empty 64-slot layer),
+    timed from the first stage call to the last copy landing."""
+    res = {}
+    for name, mode in (("copy", (api.MOE_STAGE_COPY, 0)), (f"split{n_streams}", (api.MOE_STAGE_COPY_SPLIT, n_streams)),
+                       ("kernel", (api.MOE_STAGE_KERNEL, 0))):
+        arena = torch.zeros(slots * stride, dtype=torch.uint8, device="cuda")
+        tables = torch.full((1, E), -1, dtype=torch.int32, device="cuda")
+        hit = torch.zeros(16, dtype=torch.uint8, device="cuda")[:K]
+        side, compute = torch.cuda.Stream(), torch.cuda.current_stream()
+        best = 0.0
+        for rep in range(3):
+            cache = api.MoeCache(1, E, slots, K, pool, blob, arena, stride, tables)
+            api.moe_cache_set_staging(cache, *mode)
+            sels = [torch.arange(8 * i, 8 * i + 8, dtype=torch.int32) for i in range(steps)]
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i, sel in enumerate(sels):
+                api.moe_slot_stage(cache, 0, i, sel, side, compute, hit)
+            api.moe_cache_wait(cache, 0, compute)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            best = max(best, steps * 8 * blob / dt / 1e9)
+            cache.close()
+        # every slot holds its blob
+        want = pool[:8 * steps * blob].view(8 * steps, blob)
+        got = arena.view(slots, stride)[:8 * steps, :blob].cpu()
+        assert torch.equal(got, want), name
+        res[name] = round(best, 2)
+        del arena
+    return res
+
+
 def policy_name(args):
     return {"lru": "LRU", "lfu": "LFU (whole-run counts)",
             "lfu-window": f"LFU ({args.lfu_window}-step window)"}[args.policy]
@@ -559,6 +593,9 @@ def run_cache(args, api, torch):
     cache = api.MoeCache(NL, E, n_slots, K, pool, blob, arena, stride, tables)
     policy = {"lru": api.MOE_CACHE_LRU, "lfu": api.MOE_CACHE_LFU, "lfu-window": api.MOE_CACHE_LFU_WINDOW}[args.policy]
     api.moe_cache_set_policy(cache, policy, args.lfu_window)
+    staging = {"copy": (api.MOE_STAGE_COPY, 0), "split": (api.MOE_STAGE_COPY_SPLIT, args.staging_streams),
+               "kernel": (api.MOE_STAGE_KERNEL, 0)}[args.staging]
+    api.moe_cache_set_staging(cache, *staging)
     sel = np.stack([synth.markov_selections(E, K, total_steps, args.seed, l) for l in range(NL)], axis=1)
     bias = torch.from_numpy(synth.selection_bias(sel, E)).to(dev)  # [steps, NL, E]
     router_w = [torch.from_numpy(synth.router_weight(D, E, args.seed, l)).to(dev) for l in range(NL)]
@@ -637,8 +674,12 @@ def run_cache(args, api, torch):
         "staged_GBps": round(tb / t_wall / 1e9, 2),
         "routing_matches_selection": routed_ok[0] == routed_ok[1],
         "wall_s_timed": round(t_wall, 3),
+        "staging": args.staging + (str(args.staging_streams) if args.staging == "split" else ""),
     })
     cache.close()
+    del arena
+    out["staging_burst_GBps"] = staging_burst(api, torch, pool, blob, stride, args.staging_streams)
+    log(f"staging bursts (GB/s): {out['staging_burst_GBps']}")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(args.seed, 1, 20.0, "batch-1 decode (Markov routing)",
@@ -677,6 +718,9 @@ def main():
     ap.add_argument("--slots", type=int, default=64, help="cache: HBM slots per layer")
     ap.add_argument("--policy", choices=["lru", "lfu", "lfu-window"], default="lru", help="cache: eviction policy")
     ap.add_argument("--lfu-window", type=int, default=64, help="cache: steps counted by --policy lfu-window")
+    ap.add_argument("--staging", choices=["copy", "split", "kernel"], default="copy",
+                    help="cache: how misses are copied (one DMA copy, split over streams, device-pulled kernel)")
+    ap.add_argument("--staging-streams", type=int, default=4, help="cache: streams for --staging split")
     ap.add_argument("--kernel-samples", type=int, default=62)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")

@@ -308,6 +308,30 @@ moe_status moe_cache_set_policy(moe_cache* c, int32_t policy, int32_t window);
  * moe_cache_import it resumes a run exactly. */
 moe_status moe_cache_export_usage(const moe_cache* c, int64_t* counts_host, int32_t* recent_host);
 moe_status moe_cache_import_usage(moe_cache* c, const int64_t* counts_host, const int32_t* recent_host);
+/* How misses are copied into their slots (default MOE_STAGE_COPY).  The pages
+ * read misses explicitly into slots and keep several reads in flight
+ * ("Optimizing a 14.3 GB model for an 8 GB machine", sections "Explicit reads
+ * made expert streaming work" and "MoE needed parallel work, reuse, and coarse
+ * overlap": bounded parallel reads).
+ *   MOE_STAGE_COPY        one hipMemcpyAsync per miss on the side stream.
+ *   MOE_STAGE_COPY_SPLIT  each blob cut into n_streams pieces (4 KiB
+ *                         multiples), piece i copied on library-owned stream
+ *                         i (2..MOE_STAGE_MAX_STREAMS), joined back into the
+ *                         side stream.
+ *   MOE_STAGE_KERNEL      one kernel launch on the side stream per step copies
+ *                         all misses, the GPU reading the pinned pool through
+ *                         its device mapping (checked here: a pool the device
+ *                         cannot address, or blob_bytes % 16 != 0, gives
+ *                         MOE_ERR_UNSUPPORTED).
+ * Slot tables, hit masks and ordering against the compute stream are the same
+ * in every mode.  Set once, before the first staged step (else MOE_ERR_STATE). */
+enum {
+  MOE_STAGE_COPY = 0,
+  MOE_STAGE_COPY_SPLIT = 1,
+  MOE_STAGE_KERNEL = 2,
+  MOE_STAGE_MAX_STREAMS = 8
+};
+moe_status moe_cache_set_staging(moe_cache* c, int32_t mode, int32_t n_streams);
 /* Make `compute` wait until the layer's last staging has landed. */
 moe_status moe_cache_wait(moe_cache* c, int32_t layer, hipStream_t compute);
 /* Host copy of a layer's slot table (expert -> slot, -1 absent), int32 [E]. */

@@ -67,6 +67,7 @@ _SIGNATURES = {
     "moe_cache_export": (ctypes.c_int, [_P, _P, _P]),
     "moe_cache_import": (ctypes.c_int, [_P, _P, _P]),
     "moe_cache_set_policy": (ctypes.c_int, [_P, _I32, _I32]),
+    "moe_cache_set_staging": (ctypes.c_int, [_P, _I32, _I32]),
     "moe_cache_export_usage": (ctypes.c_int, [_P, _P, _P]),
     "moe_cache_import_usage": (ctypes.c_int, [_P, _P, _P]),
     "moe_shared_gemv_bf16": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P]),
@@ -277,6 +278,13 @@ MOE_CACHE_LRU, MOE_CACHE_LFU, MOE_CACHE_LFU_WINDOW = 0, 1, 2
 
 def moe_cache_set_policy(cache: MoeCache, policy, window=0):
     _check(lib().moe_cache_set_policy(cache.handle, int(policy), int(window)))
+
+
+MOE_STAGE_COPY, MOE_STAGE_COPY_SPLIT, MOE_STAGE_KERNEL = 0, 1, 2
+
+
+def moe_cache_set_staging(cache: MoeCache, mode, n_streams=0):
+    _check(lib().moe_cache_set_staging(cache.handle, int(mode), int(n_streams)))
 
 
 def moe_cache_export_usage(cache: MoeCache, counts_host, recent_host=None):

@@ -83,6 +83,18 @@ hipError_t launch_down_mfma(bool f16, const void* act_in, const int32_t* offsets
                             int T, int d, int f, int E, int k, int64_t off_q, int64_t off_sb, const float* topk_w,
                             const float* residual, float* y, void* ws, hipStream_t s);
 
+// ---- device-pulled staging of expert blobs (stage_copy.hip): copy i moves
+// `bytes` (a multiple of 16) from src[i] (device-mapped pinned host memory,
+// 16-byte aligned) to dst[i] (device, 16-byte aligned)
+constexpr int kMaxStageCopies = 32;
+struct StageCopyArgs {
+  const uint8_t* src[kMaxStageCopies];
+  uint8_t* dst[kMaxStageCopies];
+  int n;
+  int64_t bytes;
+};
+hipError_t launch_stage_copy(const StageCopyArgs& a, hipStream_t s);
+
 // ---- fused batch-1 decode through many layers (decode_fused.hip)
 bool decode_fused_supported(int d, int f, int E, int k, int cus, int* G, int* rpw);
 size_t decode_fused_workspace_bytes(int L, int d, int f, int E, int k);

@@ -13,12 +13,14 @@
 // over PCIe.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
 #include <string>
 #include <vector>
 
 #include "../../include/libmoe.h"
+#include "kernels.h"
 
 struct moe_cache {
   int L = 0, E = 0, S = 0, k = 0;
@@ -43,6 +45,12 @@ struct moe_cache {
   std::vector<int32_t> recent;       // [L][window][k] ring of the last selections, -1 = none
   std::vector<int64_t> steps_seen;   // [L] moe_slot_stage calls so far
   bool staged_any = false;
+  // how misses are copied (moe_cache_set_staging)
+  int staging = MOE_STAGE_COPY;
+  std::vector<hipStream_t> helpers;  // MOE_STAGE_COPY_SPLIT: library-owned copy streams
+  std::vector<hipEvent_t> joins;     // one per helper stream
+  hipEvent_t fork = nullptr;
+  const uint8_t* pool_dev = nullptr; // MOE_STAGE_KERNEL: the pool as the device addresses it
 };
 
 // Failures are reported through the library's thread-local error text (api.cpp).
@@ -127,6 +135,11 @@ moe_status moe_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_slots
 
 moe_status moe_cache_destroy(moe_cache* c) {
   if (!c) return MOE_OK;
+  for (size_t i = 0; i < c->helpers.size(); ++i) {
+    if (c->helpers[i]) { hipStreamSynchronize(c->helpers[i]); hipStreamDestroy(c->helpers[i]); }
+    if (c->joins[i]) hipEventDestroy(c->joins[i]);
+  }
+  if (c->fork) hipEventDestroy(c->fork);
   for (size_t l = 0; l < c->staged.size(); ++l) {
     if (c->staged[l]) { hipEventSynchronize(c->staged[l]); hipEventDestroy(c->staged[l]); }
     if (c->masked[l]) { hipEventSynchronize(c->masked[l]); hipEventDestroy(c->masked[l]); }
@@ -217,11 +230,47 @@ moe_status moe_slot_stage(moe_cache* c, int32_t layer, int32_t step, const int32
   if ((st = hipcheck(hipEventRecord(c->compute_mark, compute), "hipEventRecord")) ||
       (st = hipcheck(hipStreamWaitEvent(side, c->compute_mark, 0), "hipStreamWaitEvent")))
     return st;
-  for (const auto& in : installs) {
-    const uint8_t* src = c->pool + ((int64_t)layer * c->E + in.first) * c->blob;
-    uint8_t* dst = c->arena + ((int64_t)layer * c->S + in.second) * c->stride;
-    if ((st = hipcheck(hipMemcpyAsync(dst, src, c->blob, hipMemcpyHostToDevice, side), "hipMemcpyAsync")))
-      return st;
+  if (!installs.empty()) {
+    if (c->staging == MOE_STAGE_KERNEL) {
+      // one launch per kMaxStageCopies misses; the GPU reads the pool itself
+      for (size_t i0 = 0; i0 < installs.size(); i0 += moe::kMaxStageCopies) {
+        moe::StageCopyArgs a{};
+        a.bytes = c->blob;
+        a.n = (int)std::min(installs.size() - i0, (size_t)moe::kMaxStageCopies);
+        for (int i = 0; i < a.n; ++i) {
+          a.src[i] = c->pool_dev + ((int64_t)layer * c->E + installs[i0 + i].first) * c->blob;
+          a.dst[i] = c->arena + ((int64_t)layer * c->S + installs[i0 + i].second) * c->stride;
+        }
+        if ((st = hipcheck(moe::launch_stage_copy(a, side), "stage copy kernel"))) return st;
+      }
+    } else if (c->staging == MOE_STAGE_COPY_SPLIT) {
+      // each blob in as many pieces as helper streams, one piece per stream
+      // (each stream can drive its own copy engine); `side` joins them
+      const int n = (int)c->helpers.size();
+      const int64_t piece = ((c->blob + n - 1) / n + 4095) / 4096 * 4096;
+      if ((st = hipcheck(hipEventRecord(c->fork, side), "hipEventRecord"))) return st;
+      for (int i = 0; i < n; ++i) {
+        if ((st = hipcheck(hipStreamWaitEvent(c->helpers[i], c->fork, 0), "hipStreamWaitEvent"))) return st;
+        for (const auto& in : installs) {
+          const int64_t o = (int64_t)i * piece, len = std::min(piece, c->blob - o);
+          if (len <= 0) continue;
+          const uint8_t* src = c->pool + ((int64_t)layer * c->E + in.first) * c->blob + o;
+          uint8_t* dst = c->arena + ((int64_t)layer * c->S + in.second) * c->stride + o;
+          if ((st = hipcheck(hipMemcpyAsync(dst, src, len, hipMemcpyHostToDevice, c->helpers[i]), "hipMemcpyAsync")))
+            return st;
+        }
+        if ((st = hipcheck(hipEventRecord(c->joins[i], c->helpers[i]), "hipEventRecord")) ||
+            (st = hipcheck(hipStreamWaitEvent(side, c->joins[i], 0), "hipStreamWaitEvent")))
+          return st;
+      }
+    } else {
+      for (const auto& in : installs) {
+        const uint8_t* src = c->pool + ((int64_t)layer * c->E + in.first) * c->blob;
+        uint8_t* dst = c->arena + ((int64_t)layer * c->S + in.second) * c->stride;
+        if ((st = hipcheck(hipMemcpyAsync(dst, src, c->blob, hipMemcpyHostToDevice, side), "hipMemcpyAsync")))
+          return st;
+      }
+    }
   }
   if (!installs.empty()) {
     rebuild_table(c, layer);
@@ -255,6 +304,39 @@ moe_status moe_cache_set_policy(moe_cache* c, int32_t policy, int32_t window) {
   c->policy = policy;
   c->window = policy == MOE_CACHE_LFU_WINDOW ? window : 0;
   c->recent.assign((size_t)c->L * c->window * c->k, -1);
+  return MOE_OK;
+}
+
+moe_status moe_cache_set_staging(moe_cache* c, int32_t mode, int32_t n_streams) {
+  if (!c) return cfail(MOE_ERR_ARG, "moe_cache_set_staging: null cache");
+  if (mode != MOE_STAGE_COPY && mode != MOE_STAGE_COPY_SPLIT && mode != MOE_STAGE_KERNEL)
+    return cfail(MOE_ERR_ARG, "moe_cache_set_staging: unknown mode");
+  if (mode == MOE_STAGE_COPY_SPLIT && (n_streams < 2 || n_streams > MOE_STAGE_MAX_STREAMS))
+    return cfail(MOE_ERR_ARG, "moe_cache_set_staging: split staging needs 2..8 streams");
+  if (c->staged_any || c->staging != MOE_STAGE_COPY)
+    return cfail(MOE_ERR_STATE, "moe_cache_set_staging: set once, before the first staged step");
+  moe_status st = MOE_OK;
+  if (mode == MOE_STAGE_KERNEL) {
+    // the kernel reads the pool through its device mapping; refuse a pool
+    // the device cannot address instead of letting the kernel fault
+    void* d = nullptr;
+    if (c->blob % 16 || hipHostGetDevicePointer(&d, const_cast<uint8_t*>(c->pool), 0) != hipSuccess || !d ||
+        reinterpret_cast<uintptr_t>(d) % 16) {
+      (void)hipGetLastError();
+      return cfail(MOE_ERR_UNSUPPORTED, "moe_cache_set_staging: the host pool is not device-mapped pinned memory "
+                                        "(or blob_bytes % 16 != 0)");
+    }
+    c->pool_dev = static_cast<const uint8_t*>(d);
+  } else if (mode == MOE_STAGE_COPY_SPLIT) {
+    c->helpers.assign(n_streams, nullptr);
+    c->joins.assign(n_streams, nullptr);
+    if ((st = hipcheck(hipEventCreateWithFlags(&c->fork, hipEventDisableTiming), "hipEventCreate"))) return st;
+    for (int i = 0; i < n_streams; ++i)
+      if ((st = hipcheck(hipStreamCreateWithFlags(&c->helpers[i], hipStreamNonBlocking), "hipStreamCreate")) ||
+          (st = hipcheck(hipEventCreateWithFlags(&c->joins[i], hipEventDisableTiming), "hipEventCreate")))
+        return st;
+  }
+  c->staging = mode;
   return MOE_OK;
 }
 

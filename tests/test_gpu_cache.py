@@ -61,12 +61,17 @@ def _oracle_cache(policy, window, n_slots, E):
 _POLICY = {"lru": 0, "lfu": 1, "lfu_window": 2}
 
 
-@pytest.mark.parametrize("policy,window", [("lru", 0), ("lfu", 0), ("lfu_window", 6)])
+_STAGING = {"copy": (0, 0), "split3": (1, 3), "kernel": (2, 0)}
+
+
+@pytest.mark.parametrize("policy,window,staging", [("lru", 0, "copy"), ("lfu", 0, "copy"), ("lfu_window", 6, "copy"),
+                                                   ("lru", 0, "split3"), ("lfu", 0, "kernel")])
 @pytest.mark.parametrize("n_slots,steps", [(8, 60), (16, 40)])
-def test_slot_tables_follow_oracle(api, n_slots, steps, policy, window):
+def test_slot_tables_follow_oracle(api, n_slots, steps, policy, window, staging):
     d, f, E, k, nl = 256, 128, 32, 4, 2
     pool = Pool(api, d, f, E, k, nl, n_slots, seed=3)
     api.moe_cache_set_policy(pool.cache, _POLICY[policy], window)
+    api.moe_cache_set_staging(pool.cache, *_STAGING[staging])
     side, compute = torch.cuda.Stream(), torch.cuda.current_stream()
     lru = [_oracle_cache(policy, window, n_slots, E) for _ in range(nl)]
     sels = [synth.markov_selections(E, k, steps, 3, l) for l in range(nl)]
@@ -103,6 +108,21 @@ def test_slot_tables_follow_oracle(api, n_slots, steps, policy, window):
         api.moe_cache_export_usage(pool.cache, counts, recent)
         for l in range(nl):
             assert counts[l].tolist() == lru[l].counts(), l
+    pool.cache.close()
+
+
+def test_staging_refusals(api):
+    d, f, E, k, S = 256, 128, 16, 4, 8
+    pool = Pool(api, d, f, E, k, 1, S, seed=7)
+    with pytest.raises(api.MoeError):
+        api.moe_cache_set_staging(pool.cache, 5, 0)
+    with pytest.raises(api.MoeError):  # split staging needs 2..8 streams
+        api.moe_cache_set_staging(pool.cache, api.MOE_STAGE_COPY_SPLIT, 1)
+    with pytest.raises(api.MoeError):
+        api.moe_cache_set_staging(pool.cache, api.MOE_STAGE_COPY_SPLIT, 9)
+    api.moe_cache_set_staging(pool.cache, api.MOE_STAGE_COPY_SPLIT, 2)
+    with pytest.raises(api.MoeError):  # set once
+        api.moe_cache_set_staging(pool.cache, api.MOE_STAGE_KERNEL, 0)
     pool.cache.close()
 
 
