@@ -483,7 +483,8 @@ def run_batched(args, api, torch):
 
 def run_prefill(args, api, torch):
     T = args.tokens or 2048
-    prec = api.MOE_PREC_BF16_MFMA if args.operands == "bf16" else api.MOE_PREC_F16_MFMA
+    prec = {"bf16": api.MOE_PREC_BF16_MFMA, "f16": api.MOE_PREC_F16_MFMA,
+            "f16direct": api.MOE_PREC_F16_MFMA_DIRECT}[args.operands]
     stack = BatchStack(api, torch, args.seed, T, prec, decode=False)
     graph = None if args.no_graph else graph_of(torch, stack.step)
     run = (lambda n: [stack.step() for _ in range(n)]) if graph is None else \
@@ -507,7 +508,7 @@ def run_prefill(args, api, torch):
     dn_tflops = flop_dn / (dn_us * 1e-6) / 1e12
     log(f"kernels (eager, mean us): route {rt_us:.1f}  permute {pm_us:.1f}  gate/up GEMM {gu_us:.1f} "
         f"({achieved:.0f} TFLOP/s)  down GEMM {dn_us:.1f} ({dn_tflops:.0f} TFLOP/s)")
-    out = base_record(tok_s, args.steps, args.warmup, ms, "fp16" if args.operands == "f16" else "bf16",
+    out = base_record(tok_s, args.steps, args.warmup, ms, "bf16" if args.operands == "bf16" else "fp16",
                       f"prefill, {T} tokens x 30 routed MoE layers x 128 experts (d=2816, f=704, top-8, int4 "
                       "groups of 64), Zipf(1.1) routing, expert-grouped int4 GEMM on MFMA "
                       f"({args.operands} operands, fp32 accumulate)",
@@ -519,7 +520,9 @@ def run_prefill(args, api, torch):
         "kernel_us": {"route": round(rt_us, 2), "permute": round(pm_us, 2), "gateup_gemm": round(gu_us, 2),
                       "down_gemm": round(dn_us, 2)},
         "roofline": {
-            "kernel": f"k_q4_gemm gate/up ({args.operands} MFMA 16x16x32, int4 tiles staged in LDS, dequantised in registers)",
+            "kernel": f"k_q4_gemm gate/up ({args.operands} MFMA 16x16x32, int4 "
+                      + ("loaded straight into registers" if args.operands == "f16direct" else "tiles staged in LDS")
+                      + ", dequantised in registers)",
             "bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": traffic_of("prefill"),
             "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated, median "
@@ -712,7 +715,9 @@ def main():
     ap.add_argument("--tokens", type=int, default=0, help="batched / prefill: tokens per step (32 / 2048)")
     ap.add_argument("--decode-path", choices=["fused", "calls"], default="fused",
                     help="decode: one moe_decode_layers launch per token, or the three calls per layer")
-    ap.add_argument("--operands", choices=["f16", "bf16"], default="f16", help="prefill: MFMA operand type")
+    ap.add_argument("--operands", choices=["f16", "bf16", "f16direct"], default="f16",
+                    help="prefill: MFMA operand type (f16direct: fp16 with int4 weights loaded straight into "
+                         "registers, the ablation of the staged tile)")
     ap.add_argument("--batched-prec", choices=["fp32", "f16", "bf16"], default="fp32",
                     help="batched: fp32 dequant-GEMV or grouped GEMM on MFMA")
     ap.add_argument("--slots", type=int, default=64, help="cache: HBM slots per layer")

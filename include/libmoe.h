@@ -92,9 +92,14 @@ typedef enum moe_precision {
   MOE_PREC_FP32 = 0,      /* int4 weights, activations kept to ~fp32 accuracy, fp32 accumulate (decode) */
   MOE_PREC_BF16_MFMA = 1, /* grouped GEMM: int4 -> bf16 weights, bf16 activations, bf16 MFMA, fp32
                              accumulate (batched prefill) */
-  MOE_PREC_F16_MFMA = 2   /* grouped GEMM: int4 -> fp16 weights, fp16 activations, fp16 MFMA, fp32
+  MOE_PREC_F16_MFMA = 2,  /* grouped GEMM: int4 -> fp16 weights, fp16 activations, fp16 MFMA, fp32
                              accumulate: the same MFMA rate as bf16 with 3 more significand bits;
                              intermediate values are block-scaled, so fp16's range does not bind */
+  MOE_PREC_F16_MFMA_DIRECT = 3  /* the same results as MOE_PREC_F16_MFMA, with the int4 weights loaded
+                             straight into registers instead of through a staged LDS tile: the
+                             ablation of the staged dequant tile ("Optimizing a 14.3 GB model for
+                             an 8 GB machine", section "Splitting the work improved attention and
+                             prefill": staged tiles against direct UInt4 reads) */
 } moe_precision;
 
 typedef enum moe_call {

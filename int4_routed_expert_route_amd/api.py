@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_STATE, MOE_ERR_CAPACITY = range(7)
-MOE_PREC_FP32, MOE_PREC_BF16_MFMA, MOE_PREC_F16_MFMA = 0, 1, 2
+MOE_PREC_FP32, MOE_PREC_BF16_MFMA, MOE_PREC_F16_MFMA, MOE_PREC_F16_MFMA_DIRECT = 0, 1, 2, 3
 MOE_CALL_ROUTE, MOE_CALL_PERMUTE, MOE_CALL_GATEUP, MOE_CALL_DOWN_COMBINE, MOE_CALL_DECODE_LAYERS = range(5)
 
 

@@ -352,7 +352,11 @@ __device__ __forceinline__ void lds_wait(u32x4 (&r)[4], u32x2 (&q)[4], uint32_t 
 // GATEUP: wave w of N tile nt owns act columns nt*128 + 32w .. +31 (gate rows
 // and up rows of those indices).  Down: wave w owns output rows nt*256 + 64w .. +63.
 // Persistent: workgroup j of XCD x runs items xstart[x] + j, + gridDim/8, ...
-template <typename ET, bool GATEUP>
+// DIRECT (the ablation of the staged tile): each lane loads its weight
+// nibbles and (scale, bias) words from memory straight into registers, one
+// K step ahead, instead of taking them from an LDS stage; activations are
+// staged as before.
+template <typename ET, bool GATEUP, bool DIRECT>
 __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
   typedef Op<ET> O;
   typedef typename O::V8 V8;
@@ -455,6 +459,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
         if (i < n_a)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, to_lds(&lds[st].a[(i * 4 + wid) * kWave]), 16, a_off[i],
                                                    so_a, 0, 0);
+      if (DIRECT) return;
       const int so_q = __builtin_amdgcn_readfirstlane(s * 2048);
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -463,8 +468,34 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, to_lds(&lds[st].sb[wid][0]), 4, sb_off,
                                                __builtin_amdgcn_readfirstlane(s * 256), 0, 0);
     };
-    // the first two K steps go out before anything else
+    // DIRECT: lane (n, kq) reads, for row group ng, 8 bytes (kq & 1) of chunk
+    // 2s + kq/2 of wave row 16 ng + n, and that row's (scale, bias) word.
+    // Rows 16 ng + n of one wave sit 256 bytes apart in their 64-row tile;
+    // gate/up's up rows (ng >= 2) are the gate rows' offsets in the up section.
+    int dq0 = 0, dsb0 = 0;
+    if (DIRECT) {
+      const int r = wave_ok ? wave_base + n : 0;
+      dq0 = (int)(a.off_q0 + (int64_t)(r / kTileRows) * (kTileRows * a.K / 2) + (r % kTileRows) * 16) +
+            (kq >> 1) * 1024 + (kq & 1) * 8;
+      dsb0 = (int)(a.off_sb0 + (int64_t)(r / kTileRows) * (kTileRows * G * 4) + (r % kTileRows) * 4);
+    }
+    const int dq_up = GATEUP ? (int)(a.off_q1 - a.off_q0) - 512 : 0;   // ng 2, 3: up section, rows n, n + 16
+    const int dsb_up = GATEUP ? (int)(a.off_sb1 - a.off_sb0) - 128 : 0;
+    auto load_b = [&](int s, u32x2 (&q)[4], uint32_t (&sb)[4]) {
+#pragma unroll
+      for (int ng = 0; ng < 4; ++ng) {
+        const int uq = __builtin_amdgcn_readfirstlane(s * 2048 + (ng >= 2 ? dq_up : 0));
+        const int us = __builtin_amdgcn_readfirstlane(s * 256 + (ng >= 2 ? dsb_up : 0));
+        q[ng] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsB, dq0 + ng * 256, uq, 0));
+        sb[ng] = __builtin_amdgcn_raw_buffer_load_b32(rsB, dsb0 + ng * 64, us, 0);
+      }
+    };
+    u32x2 bq[4];
+    uint32_t bsb[4];
+    // the first two K steps go out before anything else (DIRECT: the
+    // activations of step 0, the weights of step 0, the activations of step 1)
     issue(0, 0);
+    if (DIRECT) load_b(0, bq, bsb);
     if (G > 1) issue(1, 1);
 
     // down: each group's tile exponent.  Activations written by the gate/up
@@ -554,21 +585,30 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
       for (int ng = 0; ng < 4; ++ng)
         fb[ng] = __builtin_bit_cast(V8, O::dequant8(j == 0 ? qv[ng].x : qv[ng].y, s2[ng], b2[ng], kc));
     };
-    auto compute = [&](int s, int st) {
+    auto compute = [&](int s, int st, const u32x2 (&dq)[4], const uint32_t (&dsb)[4]) {
       const uint32_t so = (uint32_t)st * (uint32_t)sizeof(StageLds);
       u32x4 fx[4], fy[4];
       u32x2 qv[4];
       uint32_t sbv[4];
       read_half(fx, a_rd0 + so);  // j = 0, rows 0..63
-      qv[0] = lds_read64<0>(q_rd + so);
-      qv[1] = lds_read64<256>(q_rd + so);
-      qv[2] = lds_read64<512>(q_rd + so);
-      qv[3] = lds_read64<768>(q_rd + so);
-      sbv[0] = lds_read32<0>(sb_rd + so);
-      sbv[1] = lds_read32<64>(sb_rd + so);
-      sbv[2] = lds_read32<128>(sb_rd + so);
-      sbv[3] = lds_read32<192>(sb_rd + so);
-      lds_wait(fx, qv, sbv);
+      if (DIRECT) {
+#pragma unroll
+        for (int ng = 0; ng < 4; ++ng) {
+          qv[ng] = dq[ng];
+          sbv[ng] = dsb[ng];
+        }
+        lds_wait(fx);
+      } else {
+        qv[0] = lds_read64<0>(q_rd + so);
+        qv[1] = lds_read64<256>(q_rd + so);
+        qv[2] = lds_read64<512>(q_rd + so);
+        qv[3] = lds_read64<768>(q_rd + so);
+        sbv[0] = lds_read32<0>(sb_rd + so);
+        sbv[1] = lds_read32<64>(sb_rd + so);
+        sbv[2] = lds_read32<128>(sb_rd + so);
+        sbv[3] = lds_read32<192>(sb_rd + so);
+        lds_wait(fx, qv, sbv);
+      }
       if (kScaledA) {
         // this group's activations carry 2^(s_gexp[s] - tile_exp) <= 1: fold it into s and b
         const int d = s_gexp[s] - tile_exp;
@@ -605,15 +645,39 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
     };
     for (int s = 0; s < G; ++s) {
       const int st = s % kStages;
-      vm_wait_steps(s + 1 < G, n_a);       // this wave's DMA for step s has landed
+      if (DIRECT) {
+        // issue order per step: weights of s + 1, then activations of s + 2,
+        // so only the activations of step s + 1 may still be in flight here
+        constexpr int kRest = (0x7 << 4) | (0xF << 8);
+        if (s + 1 < G) {
+          if (n_a == 1) __builtin_amdgcn_s_waitcnt(1 | kRest);
+          else if (n_a == 2) __builtin_amdgcn_s_waitcnt(2 | kRest);
+          else if (n_a == 3) __builtin_amdgcn_s_waitcnt(3 | kRest);
+          else __builtin_amdgcn_s_waitcnt(4 | kRest);
+        } else {
+          __builtin_amdgcn_s_waitcnt(kRest);
+        }
+      } else {
+        vm_wait_steps(s + 1 < G, n_a);     // this wave's DMA for step s has landed
+      }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // and its LDS accesses (lgkmcnt 0)
       __builtin_amdgcn_s_barrier();        // ... and every other wave's
       if (fix_rows) {
         fix_step(s, st);
         __syncthreads();
       }
+      u32x2 nq[4];
+      uint32_t nsb[4];
+      if (DIRECT && s + 1 < G) load_b(s + 1, nq, nsb);
       if (s + 2 < G) issue(s + 2, (s + 2) % kStages);
-      if (wave_ok) compute(s, st);
+      if (wave_ok) compute(s, st, bq, bsb);
+      if (DIRECT && s + 1 < G) {
+#pragma unroll
+        for (int ng = 0; ng < 4; ++ng) {
+          bq[ng] = nq[ng];
+          bsb[ng] = nsb[ng];
+        }
+      }
     }
 
     // ---- epilogue
@@ -758,14 +822,14 @@ static int persistent_grid(int items) {
   return std::max(8, std::min(g, (items + 7) / 8 * 8));
 }
 
-template <typename ET, bool GATEUP>
+template <typename ET, bool GATEUP, bool DIRECT = false>
 static void launch_gemm(const GemmArgs& a, int items, hipStream_t s, int call) {
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   take_profile_events(call, &ev0, &ev1);
-  launch_maybe_timed(k_q4_gemm<ET, GATEUP>, persistent_grid(items), kThreads, s, ev0, ev1, a);
+  launch_maybe_timed(k_q4_gemm<ET, GATEUP, DIRECT>, persistent_grid(items), kThreads, s, ev0, ev1, a);
 }
 
-hipError_t launch_gateup_mfma(bool f16, const float* h, const int32_t* offsets, const int32_t* sorted_pair,
+hipError_t launch_gateup_mfma(bool f16, bool direct, const float* h, const int32_t* offsets, const int32_t* sorted_pair,
                               const int32_t* slot_of_expert, int n_slots, const uint8_t* arena, int64_t slot_stride,
                               int T, int d, int f, int E, int k, int64_t off_q0, int64_t off_q1, int64_t off_sb0,
                               int64_t off_sb1, void* act_out, void* ws, hipStream_t s) {
@@ -796,12 +860,13 @@ hipError_t launch_gateup_mfma(bool f16, const float* h, const int32_t* offsets, 
   a.off_q0 = off_q0; a.off_q1 = off_q1; a.off_sb0 = off_sb0; a.off_sb1 = off_sb1;
   a.out = act_out;
   a.out_exp = reinterpret_cast<int8_t*>(act_out) + (int64_t)T * k * f * 2;
-  if (f16) launch_gemm<_Float16, true>(a, items, s, MOE_CALL_GATEUP);
+  if (f16 && direct) launch_gemm<_Float16, true, true>(a, items, s, MOE_CALL_GATEUP);
+  else if (f16) launch_gemm<_Float16, true>(a, items, s, MOE_CALL_GATEUP);
   else launch_gemm<__bf16, true>(a, items, s, MOE_CALL_GATEUP);
   return hipGetLastError();
 }
 
-hipError_t launch_down_mfma(bool f16, const void* act_in, const int32_t* offsets, const int32_t* sorted_pair,
+hipError_t launch_down_mfma(bool f16, bool direct, const void* act_in, const int32_t* offsets, const int32_t* sorted_pair,
                             const int32_t* slot_of_expert, int n_slots, const uint8_t* arena, int64_t slot_stride,
                             int T, int d, int f, int E, int k, int64_t off_q, int64_t off_sb, const float* topk_w,
                             const float* residual, float* y, void* ws, hipStream_t s) {
@@ -827,7 +892,8 @@ hipError_t launch_down_mfma(bool f16, const void* act_in, const int32_t* offsets
   a.off_q0 = off_q; a.off_sb0 = off_sb;
   a.out = pair_val;
   a.out_exp = pair_exp;
-  if (f16) launch_gemm<_Float16, false>(a, items, s, MOE_CALL_DOWN_COMBINE);
+  if (f16 && direct) launch_gemm<_Float16, false, true>(a, items, s, MOE_CALL_DOWN_COMBINE);
+  else if (f16) launch_gemm<_Float16, false>(a, items, s, MOE_CALL_DOWN_COMBINE);
   else launch_gemm<__bf16, false>(a, items, s, MOE_CALL_DOWN_COMBINE);
   const int64_t n8 = (int64_t)T * d / 8;
   hipLaunchKernelGGL(k_combine_scaled, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, pair_val, pair_exp,

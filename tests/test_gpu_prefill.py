@@ -29,7 +29,8 @@ def _np(t):
 
 
 PRECS = {"f16": ("MOE_PREC_F16_MFMA", torch.float16, TOL_BF16),
-         "bf16": ("MOE_PREC_BF16_MFMA", torch.bfloat16, TOL_BF16_OPERANDS)}
+         "bf16": ("MOE_PREC_BF16_MFMA", torch.bfloat16, TOL_BF16_OPERANDS),
+         "f16direct": ("MOE_PREC_F16_MFMA_DIRECT", torch.float16, TOL_BF16)}
 
 
 def run_prefill(api, x_np, layer, blobs_dev, d, f, E_, k, slots=None, n_slots=None, prec="f16"):
@@ -74,7 +75,7 @@ class SmallLayer:
         return self.blobs[e]
 
 
-@pytest.mark.parametrize("prec", ["f16", "bf16"])
+@pytest.mark.parametrize("prec", ["f16", "bf16", "f16direct"])
 @pytest.mark.parametrize("d,f,E_,k,T", [(256, 128, 16, 4, 40), (320, 192, 8, 2, 7), (2816, 704, 128, 8, 1),
                                         (2816, 704, 128, 8, 48), (384, 256, 4, 2, 300)])
 def test_prefill_parity_small(api, d, f, E_, k, T, prec):
@@ -124,7 +125,7 @@ def test_prefill_large_activations(api, prec):
     assert e_act < tol and e_y < tol
 
 
-@pytest.mark.parametrize("prec", ["f16", "bf16"])
+@pytest.mark.parametrize("prec", ["f16", "bf16", "f16direct"])
 def test_prefill_exact_gateup(api, prec):
     """Unit scale, zero bias, h in {0,1} with 8 ones per token, gate nibbles in
     8..15: 16-bit operands are exact, fp32 sums of integers are exact and GELU
@@ -173,7 +174,7 @@ def test_prefill_exact_gateup(api, prec):
             assert np.array_equal(got[t * k + j], ref), (t, j)
 
 
-@pytest.mark.parametrize("prec", ["f16", "bf16"])
+@pytest.mark.parametrize("prec", ["f16", "bf16", "f16direct"])
 def test_prefill_full_size_sampled(api, prec):
     """One layer at the full prefill shape (2048 tokens, Zipf routing), in the
     bench's launch configuration; the oracle recomputes a sample of tokens."""
@@ -195,3 +196,18 @@ def test_prefill_full_size_sampled(api, prec):
     assert row_rel_err(_np(out["y"])[sample], ry) < PRECS[prec][2]
     assert e_y < PRECS[prec][2]
     assert np.all(np.isfinite(_np(out["y"])))
+
+
+@pytest.mark.parametrize("d,f,E_,k,T", [(256, 128, 16, 4, 40), (2816, 704, 128, 8, 300)])
+def test_prefill_direct_loads_match_staged_tiles(api, d, f, E_, k, T):
+    """Weights loaded straight into registers give bit for bit the staged-tile
+    path's act and output: the same dequantised values meet the same MFMAs in
+    the same order; only where the nibbles come from differs."""
+    layer = SmallLayer(d, f, E_, seed=31)
+    arena = torch.from_numpy(np.concatenate([layer.blobs[e] for e in range(E_)])).cuda()
+    x_np = synth.tokens(T, d, seed=31, stream=5)
+    a = run_prefill(api, x_np, layer, arena, d, f, E_, k, prec="f16")
+    b = run_prefill(api, x_np, layer, arena, d, f, E_, k, prec="f16direct")
+    assert np.array_equal(_np(a["idx"]), _np(b["idx"]))
+    assert np.array_equal(a["act"], b["act"])
+    assert np.array_equal(_np(a["y"]), _np(b["y"]))
