@@ -40,6 +40,9 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 D, F, E, K, NL = synth.D_MODEL, synth.D_FF, synth.N_EXPERTS, synth.TOP_K, synth.N_LAYERS
+# shared expert width: the pages give none; 3776 = 4d/3 rounded up to 64 makes its three bf16
+# matrices as large as the d x 4d filler GEMV (63.8 MB against 63.4 MB per layer)
+F_SH = 3776
 METRIC = "routed-MoE tokens/s + achieved HBM GB/s (int4 decode), MFMA util (prefill)"
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16
@@ -603,9 +606,20 @@ def run_cache(args, api, torch):
     bias = torch.from_numpy(synth.selection_bias(sel, E)).to(dev)  # [steps, NL, E]
     router_w = [torch.from_numpy(synth.router_weight(D, E, args.seed, l)).to(dev) for l in range(NL)]
     norm_w = [torch.from_numpy(synth.norm_weight(D, args.seed, l)).to(dev) for l in range(NL)]
-    w_sh = torch.from_numpy(synth.shared_weight_bf16(4 * D, D, args.seed, 0).view(np.int16)).to(dev)
-    w_sh_layers = w_sh.unsqueeze(0).repeat(NL, 1, 1)  # one HBM copy per layer: no cache reuse across layers
-    del w_sh
+    shared = args.overlap == "shared"
+    if shared:
+        # the shared expert: gated bf16 FFN of width F_SH, one copy per layer
+        w_sh_gu = torch.from_numpy(synth.shared_weight_bf16(2 * F_SH, D, args.seed, 0).view(np.int16)).to(dev)
+        w_sh_dn = torch.from_numpy(synth.shared_weight_bf16(D, F_SH, args.seed, 1).view(np.int16)).to(dev)
+        gu_layers = w_sh_gu.unsqueeze(0).repeat(NL, 1, 1)
+        dn_layers = w_sh_dn.unsqueeze(0).repeat(NL, 1, 1)
+        del w_sh_gu, w_sh_dn
+        res = torch.empty(1, D, dtype=torch.float32, device=dev)
+        sh_ws = torch.zeros(api.moe_shared_expert_workspace_size(1, F_SH), dtype=torch.uint8, device=dev)
+    else:
+        w_sh = torch.from_numpy(synth.shared_weight_bf16(4 * D, D, args.seed, 0).view(np.int16)).to(dev)
+        w_sh_layers = w_sh.unsqueeze(0).repeat(NL, 1, 1)  # one HBM copy per layer: no cache reuse across layers
+        del w_sh
     s_out = torch.empty(1, 4 * D, dtype=torch.float32, device=dev)
     x = torch.zeros(NL + 1, 1, D, dtype=torch.float32, device=dev)
     x[0].copy_(torch.from_numpy(synth.tokens(1, D, args.seed)))
@@ -635,13 +649,17 @@ def run_cache(args, api, torch):
             # hits first: their slots are already resident
             api.moe_expert_q4_gateup(h, idx[l], table, n_slots, a_l, stride, None, None, hit_dev[l], 1, 1, dm,
                                      api.MOE_PREC_FP32, act, ws_gu)
-            # shared-path work on the compute stream while misses land
-            api.moe_shared_gemv_bf16(w_sh_layers[l], h, 1, 4 * D, D, s_out)
+            # shared-path work on the compute stream while misses land: the
+            # shared expert (into the combine's residual) or the filler GEMV
+            if shared:
+                api.moe_shared_expert_bf16(gu_layers[l], dn_layers[l], h, x[l], 1, D, F_SH, res, sh_ws)
+            else:
+                api.moe_shared_gemv_bf16(w_sh_layers[l], h, 1, 4 * D, D, s_out)
             api.moe_cache_wait(cache, l, compute)
             api.moe_expert_q4_gateup(h, idx[l], table, n_slots, a_l, stride, None, None, hit_dev[l], 0, 1, dm,
                                      api.MOE_PREC_FP32, act, ws_gu)
             api.moe_expert_q4_down_combine(act, idx[l], wts[l], table, n_slots, a_l, stride, None, None, None,
-                                           x[l], 1, dm, api.MOE_PREC_FP32, x[l + 1], ws_dn)
+                                           res if shared else x[l], 1, dm, api.MOE_PREC_FP32, x[l + 1], ws_dn)
         api.moe_rms_rescale(x[NL], 1, D, EPS, x[0])
         return stats
 
@@ -667,8 +685,11 @@ def run_cache(args, api, torch):
                       f"batch-1 decode with a bounded expert cache: {n_slots} HBM slots per layer of 128 experts, "
                       f"{policy_name(args)} eviction, "
                       "expert pool in pinned host memory, misses staged on a side stream, Markov routing "
-                      "(keep 0.8, Zipf refill), bf16 shared-path GEMV (4d x d) overlapped on the compute stream",
+                      "(keep 0.8, Zipf refill), "
+                      + (f"bf16 shared expert (gated, width {F_SH}) into the combine" if shared else
+                         "bf16 shared-path GEMV (4d x d)") + " overlapped on the compute stream",
                       {"tokens_per_step": 1, "slots_per_layer": n_slots, "policy": policy_name(args),
+                       "overlap": args.overlap,
                        "graph": False})
     out.update({
         "hit_rate": round(hits / max(1, hits + misses), 5),
@@ -726,6 +747,8 @@ def main():
     ap.add_argument("--staging", choices=["copy", "split", "kernel"], default="copy",
                     help="cache: how misses are copied (one DMA copy, split over streams, device-pulled kernel)")
     ap.add_argument("--staging-streams", type=int, default=4, help="cache: streams for --staging split")
+    ap.add_argument("--overlap", choices=["filler", "shared"], default="filler",
+                    help="cache: work overlapped with staging (the d x 4d filler GEMV, or the shared expert)")
     ap.add_argument("--kernel-samples", type=int, default=62)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")

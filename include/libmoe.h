@@ -408,6 +408,28 @@ moe_status moe_decode_check(const void* ws, hipStream_t stream);
 moe_status moe_shared_gemv_bf16(const uint16_t* w, const float* h, int32_t T,
                                 int32_t rows, int32_t cols, float* out, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * The always-resident shared expert, bf16 weights, in the routed experts'
+ * gated form: out = residual + W_down (gelu_tanh(W_gate h) * (W_up h)).  One
+ * shared expert runs for every token (TurboFieldfare video transcript,
+ * paragraph on the two weight piles), and it is the work the GPU does while
+ * expert misses are read ("Optimizing a 14.3 GB model for an 8 GB machine",
+ * section "MoE needed parallel work, reuse, and coarse overlap").  Passing
+ * `out` as the residual of moe_expert_q4_down_combine adds the routed experts
+ * to it: y = (x + shared(h)) + sum_j w_j o_j.
+ *   w_gu      device bf16 bits [2*f_sh][d]: the f_sh gate rows, then the f_sh up rows
+ *   w_down    device bf16 bits [d][f_sh]
+ *   h         device fp32 [T][d];  residual device fp32 [T][d] or NULL
+ *   out       device fp32 [T][d] (may be the residual)
+ *   ws        device, moe_shared_expert_workspace_size(T, f_sh) bytes (g, u, act)
+ * d and f_sh multiples of 8; 16-byte aligned pointers.
+ * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_CAPACITY.
+ * ------------------------------------------------------------------------- */
+size_t moe_shared_expert_workspace_size(int32_t T, int32_t f_sh);
+moe_status moe_shared_expert_bf16(const uint16_t* w_gu, const uint16_t* w_down, const float* h,
+                                  const float* residual, int32_t T, int32_t d, int32_t f_sh, float* out,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Kernel timing: the next launch of `call`'s main kernel (the dequant-GEMV of
  * gate/up or down, or the router kernel) records `start` and `stop` at the
  * kernel's own begin and end (hipExtLaunchKernelGGL events), so the caller

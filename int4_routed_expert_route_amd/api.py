@@ -71,6 +71,8 @@ _SIGNATURES = {
     "moe_cache_export_usage": (ctypes.c_int, [_P, _P, _P]),
     "moe_cache_import_usage": (ctypes.c_int, [_P, _P, _P]),
     "moe_shared_gemv_bf16": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P]),
+    "moe_shared_expert_workspace_size": (_SZ, [_I32, _I32]),
+    "moe_shared_expert_bf16": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "moe_rms_rescale": (ctypes.c_int, [_P, _I32, _I32, _F, _P, _P]),
     "moe_profile_next_launch": (ctypes.c_int, [ctypes.c_int, _P, _P]),
     "moe_decode_layers": (ctypes.c_int, [_P, _I32, _P, _F, _P, _P, _P, _I32, _P, _I64, _I64, moe_dims, _P, _P, _P,
@@ -193,6 +195,16 @@ def moe_expert_q4_down_combine(act, topk_idx, topk_w, slot_of_expert, n_slots, a
 def moe_shared_gemv_bf16(w, h, T, rows, cols, out, stream=None):
     _check(lib().moe_shared_gemv_bf16(_dev(w, "w"), _dev(h, "h"), int(T), int(rows), int(cols),
                                       _dev(out, "out"), _stream(stream)))
+
+
+def moe_shared_expert_workspace_size(T, f_sh) -> int:
+    return int(lib().moe_shared_expert_workspace_size(int(T), int(f_sh)))
+
+
+def moe_shared_expert_bf16(w_gu, w_down, h, residual, T, d, f_sh, out, ws, stream=None):
+    _check(lib().moe_shared_expert_bf16(_dev(w_gu, "w_gu"), _dev(w_down, "w_down"), _dev(h, "h"),
+                                        _dev(residual, "residual"), int(T), int(d), int(f_sh), _dev(out, "out"),
+                                        _dev(ws, "ws"), int(ws.numel() * ws.element_size()), _stream(stream)))
 
 
 def moe_rms_rescale(x, T, d, eps, out, stream=None):

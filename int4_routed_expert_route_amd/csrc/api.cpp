@@ -303,6 +303,27 @@ moe_status moe_shared_gemv_bf16(const uint16_t* w, const float* h, int32_t T, in
   return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
 }
 
+size_t moe_shared_expert_workspace_size(int32_t T, int32_t f_sh) {
+  if (T < 1 || f_sh < 8 || f_sh % 8) return SIZE_MAX;
+  return moe::shared_expert_workspace_bytes(T, f_sh);
+}
+
+moe_status moe_shared_expert_bf16(const uint16_t* w_gu, const uint16_t* w_down, const float* h,
+                                  const float* residual, int32_t T, int32_t d, int32_t f_sh, float* out,
+                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "moe_shared_expert_bf16";
+  CHECK_PTR(w_gu); CHECK_PTR(w_down); CHECK_PTR(h); CHECK_PTR(out); CHECK_PTR(ws);
+  CHECK_ALIGN(w_gu); CHECK_ALIGN(w_down); CHECK_ALIGN(h); CHECK_ALIGN(out); CHECK_ALIGN(ws);
+  if (residual) CHECK_ALIGN(residual);
+  if (T < 1 || d < 8 || d % 8 || f_sh < 8 || f_sh % 8)
+    return fail(MOE_ERR_ARG, "%s: T=%d d=%d f_sh=%d (d, f_sh multiples of 8)", fn, T, d, f_sh);
+  if (ws_bytes < moe::shared_expert_workspace_bytes(T, f_sh))
+    return fail(MOE_ERR_CAPACITY, "%s: workspace of %zu bytes, need %zu", fn, ws_bytes,
+                moe::shared_expert_workspace_bytes(T, f_sh));
+  hipError_t e = moe::launch_shared_expert_bf16(w_gu, w_down, h, residual, T, d, f_sh, out, ws, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
+}
+
 static int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||

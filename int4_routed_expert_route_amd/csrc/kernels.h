@@ -107,6 +107,10 @@ hipError_t launch_decode_fused(float* x_io, int L, const float* norm_w, float ep
                                int rpw, hipStream_t s);
 
 // ---- bf16 shared-path GEMV (shared_gemv.hip)
+size_t shared_expert_workspace_bytes(int T, int f_sh);
+hipError_t launch_shared_expert_bf16(const uint16_t* w_gu, const uint16_t* w_down, const float* h,
+                                     const float* residual, int T, int d, int f_sh, float* out, void* ws,
+                                     hipStream_t s);
 hipError_t launch_shared_gemv_bf16(const uint16_t* w, const float* h, int T, int rows, int cols,
                                    float* out, hipStream_t s);
 

@@ -1,7 +1,10 @@
-// Shared-path GEMV with bf16 weights, out[t][r] = sum_c W[r][c] h[t][c].
-// It is the always-resident work the GPU runs while expert misses are copied in
+// Shared path with bf16 weights: the GEMV out[t][r] = sum_c W[r][c] h[t][c]
+// (+ residual[t][r]), and the shared expert built from it.  It is the
+// always-resident work the GPU runs while expert misses are copied in
 // ("Optimizing a 14.3 GB model for an 8 GB machine", section "MoE needed
-// parallel work, reuse, and coarse overlap": coarse overlap with the shared MLP).
+// parallel work, reuse, and coarse overlap": coarse overlap with the shared MLP;
+// TurboFieldfare video transcript, paragraph on the two weight piles: one
+// shared expert runs for every token).
 // HBM-bound: one wave per row, 16-byte loads of 8 bf16 weights, fp32 FMA, wave
 // reduction.  Up to 4 tokens share each weight load.
 #include "common.h"
@@ -13,9 +16,11 @@ namespace {
 
 constexpr int kSgTok = 4;
 
+template <bool RESID>
 __global__ __launch_bounds__(256) void k_shared_gemv_bf16(const uint16_t* __restrict__ w,
                                                           const float* __restrict__ h, int T,
                                                           int rows, int cols,
+                                                          const float* __restrict__ residual,
                                                           float* __restrict__ out) {
   const int lane = threadIdx.x % kWave;
   const int r = blockIdx.x * 4 + threadIdx.x / kWave;
@@ -48,17 +53,50 @@ __global__ __launch_bounds__(256) void k_shared_gemv_bf16(const uint16_t* __rest
     }
 #pragma unroll
     for (int tt = 0; tt < kSgTok; ++tt) {
-      const float v = wave_sum(acc[tt]);
-      if (tt < nt && lane == 0) out[(size_t)(t0 + tt) * rows + r] = v;
+      float v = wave_sum(acc[tt]);
+      if (tt < nt && lane == 0) {
+        if (RESID) v = residual[(size_t)(t0 + tt) * rows + r] + v;
+        out[(size_t)(t0 + tt) * rows + r] = v;
+      }
     }
   }
 }
 
+// act[t][c] = gelu_tanh(gu[t][c]) * gu[t][f + c] for gu [T][2f]
+__global__ __launch_bounds__(256) void k_gated_act(const float* __restrict__ gu, int T, int f,
+                                                   float* __restrict__ act) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)T * f) return;
+  const int64_t t = i / f, c = i % f;
+  act[i] = gelu_tanh(gu[t * 2 * f + c]) * gu[t * 2 * f + f + c];
+}
+
 }  // namespace
+
+size_t shared_expert_workspace_bytes(int T, int f_sh) { return (size_t)T * 3 * f_sh * 4; }
+
+hipError_t launch_shared_expert_bf16(const uint16_t* w_gu, const uint16_t* w_down, const float* h,
+                                     const float* residual, int T, int d, int f_sh, float* out, void* ws,
+                                     hipStream_t s) {
+  float* gu = reinterpret_cast<float*>(ws);
+  float* act = gu + (size_t)T * 2 * f_sh;
+  hipLaunchKernelGGL(k_shared_gemv_bf16<false>, dim3((2 * f_sh + 3) / 4), dim3(256), 0, s, w_gu, h, T, 2 * f_sh, d,
+                     nullptr, gu);
+  const int64_t n = (int64_t)T * f_sh;
+  hipLaunchKernelGGL(k_gated_act, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gu, T, f_sh, act);
+  if (residual)
+    hipLaunchKernelGGL(k_shared_gemv_bf16<true>, dim3((d + 3) / 4), dim3(256), 0, s, w_down, act, T, d, f_sh,
+                       residual, out);
+  else
+    hipLaunchKernelGGL(k_shared_gemv_bf16<false>, dim3((d + 3) / 4), dim3(256), 0, s, w_down, act, T, d, f_sh,
+                       nullptr, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_shared_gemv_bf16(const uint16_t* w, const float* h, int T, int rows, int cols,
                                    float* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_shared_gemv_bf16, dim3((rows + 3) / 4), dim3(256), 0, s, w, h, T, rows, cols, out);
+  hipLaunchKernelGGL(k_shared_gemv_bf16<false>, dim3((rows + 3) / 4), dim3(256), 0, s, w, h, T, rows, cols, nullptr,
+                     out);
   return hipGetLastError();
 }
 

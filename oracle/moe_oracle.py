@@ -435,7 +435,7 @@ class LfuSlotCache:
 
 
 # --------------------------------------------------------------------------------------
-# shared-path filler GEMV (bf16 weights)
+# shared path: the filler GEMV and the shared expert (bf16 weights)
 # --------------------------------------------------------------------------------------
 
 def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
@@ -446,6 +446,24 @@ def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
 def shared_gemv(w_bits: np.ndarray, h) -> np.ndarray:
     """s = W h with W given as bf16 bits [rows, cols]; h [T, cols] -> [T, rows]."""
     return np.atleast_2d(np.asarray(h, dtype=np.float64)) @ bf16_bits_to_float(w_bits).T
+
+
+def shared_expert(h, w_gu_bits: np.ndarray, w_down_bits: np.ndarray, residual=None) -> np.ndarray:
+    """The always-resident shared expert (TurboFieldfare video transcript,
+    paragraph on the two weight piles: one shared expert runs for every token;
+    "Optimizing a 14.3 GB model for an 8 GB machine", section "MoE needed
+    parallel work, reuse, and coarse overlap": the shared MLP is the work that
+    hides expert reads).  Taken here in the routed experts' gated form with
+    bf16 weights: w_gu [2 f_sh, d] holds the gate rows, then the up rows;
+    w_down [d, f_sh]; out = residual + W_down (gelu_tanh(W_gate h) * (W_up h))."""
+    h = np.atleast_2d(np.asarray(h, dtype=np.float64))
+    gu = h @ bf16_bits_to_float(w_gu_bits).T
+    f_sh = gu.shape[1] // 2
+    act = gelu_tanh(gu[:, :f_sh]) * gu[:, f_sh:]
+    out = act @ bf16_bits_to_float(w_down_bits).T
+    if residual is not None:
+        out = out + np.atleast_2d(np.asarray(residual, dtype=np.float64))
+    return out
 
 
 # --------------------------------------------------------------------------------------

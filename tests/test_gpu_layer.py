@@ -320,6 +320,58 @@ def test_shared_gemv_bf16():
     assert row_rel_err(_np(out), orc.shared_gemv(wb, h_np)) < TOL_FP32
 
 
+@pytest.mark.parametrize("d,f_sh,T,resid", [(256, 96, 1, True), (256, 96, 5, False), (2816, 3776, 1, True)])
+def test_shared_expert_bf16(d, f_sh, T, resid):
+    """The shared expert (bf16 gated FFN plus residual) against the oracle, and
+    as the residual of the routed combine: y = (x + shared(h)) + sum_j w_j o_j."""
+    w_gu = synth.shared_weight_bf16(2 * f_sh, d, 3, 0)
+    w_dn = synth.shared_weight_bf16(d, f_sh, 3, 1)
+    h_np = synth.tokens(T, d, 3)
+    x_np = synth.tokens(T, d, 4)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    out = torch.empty(T, d, device="cuda")
+    ws = torch.zeros(L.moe_shared_expert_workspace_size(T, f_sh), dtype=torch.uint8, device="cuda")
+    L.moe_shared_expert_bf16(dev(w_gu.view(np.int16)), dev(w_dn.view(np.int16)), dev(h_np),
+                             dev(x_np) if resid else None, T, d, f_sh, out, ws)
+    want = orc.shared_expert(h_np, w_gu, w_dn, residual=x_np if resid else None)
+    if resid:  # the shared expert's own contribution, not hidden under the residual
+        assert row_rel_err(_np(out) - x_np, want - x_np) < TOL_FP32
+    assert row_rel_err(_np(out), want) < TOL_FP32
+
+
+def test_shared_expert_into_routed_combine(layer0, dev_layer):
+    """One decode token: shared expert into the residual, then the routed
+    layer's down + combine on top, against the oracle's layer plus the
+    oracle's shared expert."""
+    d, f_sh, T = D, 512, 1
+    w_gu = synth.shared_weight_bf16(2 * f_sh, d, 5, 0)
+    w_dn = synth.shared_weight_bf16(d, f_sh, 5, 1)
+    x_np = synth.tokens(T, d, 6)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    dm = L.dims(D, F, E, K)
+    ws = lambda c: torch.zeros(max(L.moe_workspace_size(c, T, dm), 256), dtype=torch.uint8, device="cuda")
+    x = dev(x_np)
+    h = torch.empty(T, d, device="cuda")
+    idx = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, K, device="cuda")
+    L.moe_route(x, dev_layer["norm_w"], 1e-6, dev_layer["router_w"], dev_layer["bias"], T, dm, h, idx, w, ws(0))
+    res = torch.empty(T, d, device="cuda")
+    sws = torch.zeros(L.moe_shared_expert_workspace_size(T, f_sh), dtype=torch.uint8, device="cuda")
+    L.moe_shared_expert_bf16(dev(w_gu.view(np.int16)), dev(w_dn.view(np.int16)), h, x, T, d, f_sh, res, sws)
+    act = torch.empty(T * K, F, device="cuda")
+    L.moe_expert_q4_gateup(h, idx, dev_layer["slots"], E, dev_layer["arena"], dev_layer["stride"], None, None, None,
+                           0, T, dm, L.MOE_PREC_FP32, act, ws(2))
+    y = torch.empty(T, d, device="cuda")
+    L.moe_expert_q4_down_combine(act, idx, w, dev_layer["slots"], E, dev_layer["arena"], dev_layer["stride"], None,
+                                 None, None, res, T, dm, L.MOE_PREC_FP32, y, ws(3))
+    gi = _np(idx)
+    ry, *_ = orc.moe_layer(x_np, layer0.norm_w, layer0.router_w, layer0.bias, layer0.blob_of, D, F, K,
+                           idx_override=gi)
+    hh = orc.rmsnorm(x_np, layer0.norm_w)
+    want = ry + orc.shared_expert(hh, w_gu, w_dn)
+    assert row_rel_err(_np(y) - x_np, want - x_np) < TOL_FP32
+
+
 def test_rms_rescale():
     x_np = synth.tokens(5, D, seed=9) * 13.0
     x = torch.from_numpy(x_np).cuda()

@@ -408,3 +408,41 @@ def test_lfu_whole_run_keeps_the_popular_expert():
     lfu_hits = sum(lfu.step(t, s)[0][0] for t, s in enumerate(seq))
     lru_hits = sum(lru.step(t, s)[0][0] for t, s in enumerate(seq))
     assert lfu_hits == 2 and lru_hits == 0
+
+
+# ----------------------------------------------------------------------------- shared expert
+
+def _bf16_bits_exact(w: np.ndarray) -> np.ndarray:
+    """bf16 bits of values that bf16 holds exactly (small integers)."""
+    bits = np.asarray(w, dtype=np.float32).view(np.uint32)
+    assert np.all((bits & 0xFFFF) == 0)
+    return (bits >> 16).astype(np.uint16)
+
+
+def test_shared_expert_is_the_routed_expert_ffn():
+    # an int4 expert with unit scale and zero bias has integer weights 0..15,
+    # which bf16 holds exactly: the shared expert on those weights must be the
+    # routed oracle's gate/up + down of that expert (independent code paths)
+    d, f = 128, 64
+    rs = np.random.default_rng(4)
+    m = {name: (rs.integers(0, 16, (R, C)), np.ones((R, C // 64)), np.zeros((R, C // 64)))
+         for name, (R, C) in (("gate", (f, d)), ("up", (f, d)), ("down", (d, f)))}
+    blob = orc.encode_expert(m, d, f)
+    h = rs.normal(0.0, 0.05, (3, d))
+    x = rs.normal(0.0, 1.0, (3, d))
+    w_gu = _bf16_bits_exact(np.concatenate([m["gate"][0], m["up"][0]]))
+    w_dn = _bf16_bits_exact(m["down"][0])
+    got = orc.shared_expert(h, w_gu, w_dn, residual=x)
+    for t in range(3):
+        act = orc.expert_gateup(blob, h[t], d, f)
+        want = x[t] + orc.expert_down(blob, act, d, f)
+        assert np.allclose(got[t], want, rtol=1e-12, atol=1e-9)
+
+
+def test_shared_expert_zero_up_gives_the_residual():
+    d, f_sh = 64, 32
+    rs = np.random.default_rng(5)
+    w_gu = _bf16_bits_exact(np.concatenate([rs.integers(-3, 4, (f_sh, d)), np.zeros((f_sh, d))]))
+    w_dn = _bf16_bits_exact(rs.integers(-3, 4, (d, f_sh)))
+    x = rs.normal(0.0, 1.0, (2, d))
+    assert np.array_equal(orc.shared_expert(rs.normal(0, 1, (2, d)), w_gu, w_dn, residual=x), x)
