@@ -126,6 +126,19 @@ struct Op<__bf16> {
   static constexpr bool kScaled = false;  // bf16 has fp32's range: exponents stay 0
 };
 
+// tanh-form GELU for the 16-bit act tiles, with tanh(y) = 1 - 2 / (1 + e^{2y})
+// on the hardware exp2 and reciprocal: absolute error of the tanh ~1e-7,
+// far below the 16-bit act's rounding; e^{2y} overflowing gives exactly 1,
+// underflowing exactly -1, as tanh saturates (|z| >= 10 gives g or 0 exactly).
+__device__ __forceinline__ float gelu_tanh_act16(float z) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  const float k1 = 0.044715f;
+  const float y = k0 * (z + k1 * z * z * z);
+  const float e = __builtin_amdgcn_exp2f(y * 2.8853900817779268f);  // e^{2y} = 2^{2y log2 e}
+  const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e);
+  return 0.5f * z * (1.0f + t);
+}
+
 // Block exponent for a group whose largest magnitude is m: m * 2^-e in [2^14, 2^15).
 __device__ __forceinline__ int block_exp(float m) {
   if (!(m > 0.0f) || !(m <= 3.0e38f)) return 0;  // zero, NaN or inf: leave as is
@@ -687,15 +700,23 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
       float v[8][2][4];
       float m = 0.0f;
 #pragma unroll
-      for (int mg = 0; mg < 8; ++mg)
+      for (int mg = 0; mg < 8; ++mg) {
+        if (mg >= n_mg) {  // row groups past the tile's rows are not stored
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[mg][c][i] = 0.0f;
+          continue;
+        }
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float g = acc[mg][c][i], u = acc[mg][c + 2][i];
-            v[mg][c][i] = ok ? gelu_tanh(g) * u : f32_nan();
+            v[mg][c][i] = ok ? gelu_tanh_act16(g) * u : f32_nan();
             if (mg * 16 + kq * 4 + i < rows) m = fmaxf(m, fabsf(v[mg][c][i]));
           }
+      }
       int ex = 0;
       if (O::kScaled) {
         // one exponent per M tile and 64-column group (waves 2g', 2g'+1)
