@@ -48,6 +48,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 128;               // pair rows per work item
+constexpr int kItemFixedCost = 32;    // schedule cost of an item beyond its row groups of 16
 constexpr int WN = 64;                // weight rows per wave
 constexpr int kWaves = 4;             // waves per workgroup, side by side along N
 constexpr int BN = WN * kWaves;       // weight rows per workgroup
@@ -153,8 +154,13 @@ __device__ __forceinline__ float exp2i(int e) { return __builtin_bit_cast(float,
 // by M tile, its N tiles in order (the N tiles of one M tile share the
 // activation rows; the expert's weights stay in L2 across its M tiles).
 // Item = (expert, m0, n tile).  The list is cut into 8 stretches of about
-// equal cost, one per XCD; an item costs 4 + (row groups of 16 in its M tile)
-// units (weights stream whatever the rows, MFMA work follows the rows).
+// equal cost, one per XCD; an item costs kItemFixedCost + (row groups of 16 in
+// its M tile).  Most of a K step's time does not depend on the rows (the
+// dequant, the step barrier, the DMA round trip) and the prologue and epilogue
+// are per item: timed per item, a one-group tile takes 0.7-0.85 of a full
+// one.  32 fixed units (0.83) measured best (4: 173.7k, 16: 184.0k, 32: 184.4k
+// prefill tokens/s); what remains is the whole-item granularity, about 2
+// items per workgroup per launch.
 //
 // Every workgroup of the GEMM derives the same list from the expert offsets
 // at its start (a separate scheduling launch cost more than this): ranks by
@@ -207,7 +213,7 @@ __device__ void plan_items(const int32_t* __restrict__ offsets, int E, int n_pai
   const int mt = (rc + BM - 1) / BM;
   const int n_items = mt * NT;
   const int full = rc / BM, tail = rc % BM;
-  const int c_full = 4 + BM / 16, c_tail = 4 + (tail + 15) / 16;
+  const int c_full = kItemFixedCost + BM / 16, c_tail = kItemFixedCost + (tail + 15) / 16;
   const int cost = NT * (full * c_full + (tail ? c_tail : 0));
   int inc_i = n_items, inc_c = cost;
 #pragma unroll
