@@ -169,7 +169,8 @@ __device__ __forceinline__ float exp2i(int e) { return __builtin_bit_cast(float,
 // not stored: an item index maps to its rank by binary search over the ranks'
 // first items.
 struct Plan {
-  int expert[256];  // expert of each rank
+  int ecnt[256];    // expert of each rank | its pair count << 8 (pair counts < 2^24)
+  int beg[256];     // each rank's first position in sorted_pair (offsets, clamped)
   int ibase[256];   // first item of each rank (the item count W for ranks without items)
   int xstart[9];    // first item of each XCD's stretch; xstart[8] = W
 };
@@ -184,9 +185,10 @@ __device__ void plan_items(const int32_t* __restrict__ offsets, int E, int n_pai
   int* s_wsum = scratch + 512;                      // [2][4] per-wave scan totals
   int* s_start = pl.xstart;
   const int t = threadIdx.x, lane = t % kWave, wv = t / kWave;
-  int cnt = -1;
+  int cnt = -1, a = 0;
   if (t < E) {
-    const int a = max(0, min(offsets[t], n_pairs)), b = max(a, min(offsets[t + 1], n_pairs));
+    a = max(0, min(offsets[t], n_pairs));
+    const int b = max(a, min(offsets[t + 1], n_pairs));
     cnt = b - a;
   }
   s_cnt[t] = cnt;
@@ -203,7 +205,8 @@ __device__ void plan_items(const int32_t* __restrict__ offsets, int E, int n_pai
       rank += (c.z > cnt || (c.z == cnt && e + 2 < t)) ? 1 : 0;
       rank += (c.w > cnt || (c.w == cnt && e + 3 < t)) ? 1 : 0;
     }
-    pl.expert[rank] = t;
+    pl.ecnt[rank] = t | (cnt << 8);
+    pl.beg[rank] = a;
     s_rcnt[rank] = cnt;
   }
   __syncthreads();
@@ -421,11 +424,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
       }
     }
     const int li = item - s_plan.ibase[rk];
-    const int e = __builtin_amdgcn_readfirstlane(s_plan.expert[rk]);
+    // the expert, its pair count and first position come from the plan in
+    // LDS (no global round trip before the item's first load)
+    const int ec = __builtin_amdgcn_readfirstlane(s_plan.ecnt[rk]);
+    const int e = ec & 255;
     const int m0 = __builtin_amdgcn_readfirstlane((li / a.NT) * BM);
     const int nt = __builtin_amdgcn_readfirstlane(li % a.NT);
-    const int beg = __builtin_amdgcn_readfirstlane(max(0, min(a.offsets[e], n_pairs)));
-    const int end = __builtin_amdgcn_readfirstlane(max(beg, min(a.offsets[e + 1], n_pairs)));
+    const int beg = __builtin_amdgcn_readfirstlane(s_plan.beg[rk]);
+    const int end = beg + (ec >> 8);
     const int rows = max(0, min(BM, end - beg - m0));
     if (t < BM) {
       int p = -1;
