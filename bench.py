@@ -57,8 +57,8 @@ TRAFFIC = {
                "fetch_bytes": 18093516, "write_bytes": 22528},
     "decode_fused": {"sources": ('decode_fused.hip', 'q4_lane.h', 'common.h'), "sha256_16": "e38b527d1b6f8d39",
                      "fetch_bytes": 954574168, "write_bytes": 8112864},
-    "prefill": {"sources": ('q4_grouped_mfma.hip', 'common.h'), "sha256_16": "27391d2c1695c7f2",
-                "fetch_bytes": 240052090, "write_bytes": 23891904},
+    "prefill": {"sources": ('q4_grouped_mfma.hip', 'common.h'), "sha256_16": "7c13c9afac927a7b",
+                "fetch_bytes": 226824131, "write_bytes": 23869520},
 }
 
 
