@@ -602,6 +602,9 @@ def run_cache(args, api, torch):
     staging = {"copy": (api.MOE_STAGE_COPY, 0), "split": (api.MOE_STAGE_COPY_SPLIT, args.staging_streams),
                "kernel": (api.MOE_STAGE_KERNEL, 0)}[args.staging]
     api.moe_cache_set_staging(cache, *staging)
+    on_device = args.cache_path == "device"
+    if on_device:
+        api.moe_cache_enable_device(cache)
     sel = np.stack([synth.markov_selections(E, K, total_steps, args.seed, l) for l in range(NL)], axis=1)
     bias = torch.from_numpy(synth.selection_bias(sel, E)).to(dev)  # [steps, NL, E]
     router_w = [torch.from_numpy(synth.router_weight(D, E, args.seed, l)).to(dev) for l in range(NL)]
@@ -635,17 +638,25 @@ def run_cache(args, api, torch):
     side = torch.cuda.Stream()
     routed_ok = [0, 0]
 
-    def step(t):
+    idx_all = torch.zeros(total_steps, NL, K, dtype=torch.int32, device=dev) if on_device else None
+
+    def step(t, read_stats=True):
         stats = None
+        compute = torch.cuda.current_stream()  # the capture stream while a graph is recorded
         for l in range(NL):
             a_l = arena[l * n_slots * stride:(l + 1) * n_slots * stride]
             table = tables[l]
             api.moe_route(x[l], norm_w[l], EPS, router_w[l], bias[t, l], 1, dm, h, idx[l], wts[l], ws_route)
-            idx_host[l].copy_(idx[l, 0], non_blocking=True)
-            compute.synchronize()
-            routed_ok[0] += int(np.array_equal(np.sort(idx_host[l].numpy()), sel[t, l]))
-            routed_ok[1] += 1
-            stats = api.moe_slot_stage(cache, l, t, idx_host[l], side, compute, hit_dev[l])
+            if on_device:
+                # the rule and the miss copies on the device: no host round trip
+                idx_all[t, l].copy_(idx[l, 0])
+                api.moe_slot_stage_device(cache, l, t, idx[l, 0], side, compute, hit_dev[l])
+            else:
+                idx_host[l].copy_(idx[l, 0], non_blocking=True)
+                compute.synchronize()
+                routed_ok[0] += int(np.array_equal(np.sort(idx_host[l].numpy()), sel[t, l]))
+                routed_ok[1] += 1
+                stats = api.moe_slot_stage(cache, l, t, idx_host[l], side, compute, hit_dev[l])
             # hits first: their slots are already resident
             api.moe_expert_q4_gateup(h, idx[l], table, n_slots, a_l, stride, None, None, hit_dev[l], 1, 1, dm,
                                      api.MOE_PREC_FP32, act, ws_gu)
@@ -661,23 +672,49 @@ def run_cache(args, api, torch):
             api.moe_expert_q4_down_combine(act, idx[l], wts[l], table, n_slots, a_l, stride, None, None, None,
                                            res if shared else x[l], 1, dm, api.MOE_PREC_FP32, x[l + 1], ws_dn)
         api.moe_rms_rescale(x[NL], 1, D, EPS, x[0])
-        return stats
+        return api.moe_cache_stats(cache) if (on_device and read_stats and t in stat_steps) else stats
 
+    stat_steps = {args.warmup - 1, total_steps - 1}  # device mode: read the statistics back only here
     log(f"warmup {args.warmup} steps (cold cache included in the hit statistics)")
     st0 = None
     for t in range(args.warmup):
         st0 = step(t)
     torch.cuda.synchronize()
     h0, m0, b0 = (st0.hits, st0.misses, st0.bytes_staged) if st0 is not None else (0, 0, 0)
+    graphs = None
+    if on_device and not args.no_graph:
+        # With the cache on the device a step never waits for the host, so each
+        # step (its own routing bias and step number) is recorded as one HIP
+        # graph before the timed region and replayed in order.
+        t_cap = time.time()
+        cap = torch.cuda.Stream()
+        graphs = []
+        for t in range(args.warmup, total_steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(t, read_stats=False)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        log(f"{len(graphs)} step graphs recorded in {time.time() - t_cap:.1f} s")
     t_wall = time.perf_counter()
     st = None
-    for t in range(args.warmup, total_steps):
-        st = step(t)
+    if graphs is not None:
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        st = api.moe_cache_stats(cache)
+    else:
+        for t in range(args.warmup, total_steps):
+            st = step(t)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = t_wall * 1000.0 / args.steps
     tok_s = 1000.0 / ms
     hits, misses, staged = st.hits, st.misses, st.bytes_staged
+    if on_device:  # the router's choices against the Markov selections, after the run
+        got = np.sort(idx_all.cpu().numpy(), axis=-1)
+        routed_ok[0] = int((got == np.sort(sel, axis=-1)).all(axis=-1).sum())
+        routed_ok[1] = got.shape[0] * got.shape[1]
     th, tm, tb = hits - h0, misses - m0, staged - b0
     log(f"{args.steps} steps: {ms:.3f} ms/step, {tok_s:.1f} tok/s; hit rate {hits / (hits + misses):.4f} "
         f"(timed {th / max(1, th + tm):.4f}); {tb / args.steps / 1e6:.1f} MB staged per token")
@@ -690,7 +727,7 @@ def run_cache(args, api, torch):
                          "bf16 shared-path GEMV (4d x d)") + " overlapped on the compute stream",
                       {"tokens_per_step": 1, "slots_per_layer": n_slots, "policy": policy_name(args),
                        "overlap": args.overlap,
-                       "graph": False})
+                       "graph": on_device and not args.no_graph})
     out.update({
         "hit_rate": round(hits / max(1, hits + misses), 5),
         "hit_rate_timed": round(th / max(1, th + tm), 5),
@@ -699,6 +736,8 @@ def run_cache(args, api, torch):
         "routing_matches_selection": routed_ok[0] == routed_ok[1],
         "wall_s_timed": round(t_wall, 3),
         "staging": args.staging + (str(args.staging_streams) if args.staging == "split" else ""),
+        "cache_path": args.cache_path,
+        "graph": graphs is not None,
     })
     cache.close()
     del arena
@@ -747,6 +786,8 @@ def main():
     ap.add_argument("--staging", choices=["copy", "split", "kernel"], default="copy",
                     help="cache: how misses are copied (one DMA copy, split over streams, device-pulled kernel)")
     ap.add_argument("--staging-streams", type=int, default=4, help="cache: streams for --staging split")
+    ap.add_argument("--cache-path", choices=["host", "device"], default="host",
+                    help="cache: eviction rule and miss copies on the host (one sync per layer) or on the device")
     ap.add_argument("--overlap", choices=["filler", "shared"], default="filler",
                     help="cache: work overlapped with staging (the d x 4d filler GEMV, or the shared expert)")
     ap.add_argument("--kernel-samples", type=int, default=62)

@@ -337,6 +337,29 @@ enum {
   MOE_STAGE_MAX_STREAMS = 8
 };
 moe_status moe_cache_set_staging(moe_cache* c, int32_t mode, int32_t n_streams);
+/* The cache on the device, for decode steps that never wait for the host.
+ * After moe_cache_enable_device (which allocates the device copy of the cache
+ * state and copies the current state there; LRU or whole-run LFU; the pool
+ * must be device-mapped pinned memory, as for MOE_STAGE_KERNEL), each step of
+ * a layer is moe_slot_stage_device instead of moe_slot_stage:
+ *   sel_dev       device int32 [k]: the layer's chosen experts (a row of
+ *                 moe_route's topk_idx), read on `compute`;
+ *   on `compute`  one wave runs the same eviction rule as the host cache,
+ *                 updates the device slot table and writes hit_mask_dev;
+ *   on `side`     after that, one copy kernel pulls the misses' blobs from the
+ *                 pinned pool into their slots (moe_cache_wait as before).
+ * Nothing is copied to or waited for on the host.  moe_cache_slot_table,
+ * moe_cache_export, moe_cache_export_usage and moe_cache_stats bring the host
+ * view up to date first (they wait for the device).  In device mode
+ * moe_slot_stage and moe_cache_import give MOE_ERR_STATE.  A selection out of
+ * range or repeating an expert changes nothing and is reported as MOE_ERR_ARG
+ * by the next call that reads the state back.  The ordering is the pages':
+ * kernels of hits may run on `compute` before moe_cache_wait. */
+moe_status moe_cache_enable_device(moe_cache* c);
+moe_status moe_slot_stage_device(moe_cache* c, int32_t layer, int32_t step, const int32_t* sel_dev,
+                                 hipStream_t side, hipStream_t compute, uint8_t* hit_mask_dev);
+/* Cumulative hits, misses and staged bytes (device mode: waits for the device). */
+moe_status moe_cache_stats(const moe_cache* c, moe_stage_stats* out);
 /* Make `compute` wait until the layer's last staging has landed. */
 moe_status moe_cache_wait(moe_cache* c, int32_t layer, hipStream_t compute);
 /* Host copy of a layer's slot table (expert -> slot, -1 absent), int32 [E]. */

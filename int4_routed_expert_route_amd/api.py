@@ -68,6 +68,9 @@ _SIGNATURES = {
     "moe_cache_import": (ctypes.c_int, [_P, _P, _P]),
     "moe_cache_set_policy": (ctypes.c_int, [_P, _I32, _I32]),
     "moe_cache_set_staging": (ctypes.c_int, [_P, _I32, _I32]),
+    "moe_cache_enable_device": (ctypes.c_int, [_P]),
+    "moe_slot_stage_device": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _P]),
+    "moe_cache_stats": (ctypes.c_int, [_P, ctypes.POINTER(moe_stage_stats)]),
     "moe_cache_export_usage": (ctypes.c_int, [_P, _P, _P]),
     "moe_cache_import_usage": (ctypes.c_int, [_P, _P, _P]),
     "moe_shared_gemv_bf16": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P]),
@@ -297,6 +300,21 @@ MOE_STAGE_COPY, MOE_STAGE_COPY_SPLIT, MOE_STAGE_KERNEL = 0, 1, 2
 
 def moe_cache_set_staging(cache: MoeCache, mode, n_streams=0):
     _check(lib().moe_cache_set_staging(cache.handle, int(mode), int(n_streams)))
+
+
+def moe_cache_enable_device(cache: MoeCache):
+    _check(lib().moe_cache_enable_device(cache.handle))
+
+
+def moe_slot_stage_device(cache: MoeCache, layer, step, sel_dev, side, compute, hit_mask_dev):
+    _check(lib().moe_slot_stage_device(cache.handle, int(layer), int(step), _dev(sel_dev, "sel_dev"), _stream(side),
+                                       _stream(compute), _dev(hit_mask_dev, "hit_mask_dev")))
+
+
+def moe_cache_stats(cache: MoeCache):
+    stats = moe_stage_stats()
+    _check(lib().moe_cache_stats(cache.handle, ctypes.byref(stats)))
+    return stats
 
 
 def moe_cache_export_usage(cache: MoeCache, counts_host, recent_host=None):

@@ -13,7 +13,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 
 SOURCES = ["api.cpp", "slot_cache.cpp", "route.hip", "permute.hip", "q4_gemv.hip",
-           "q4_grouped_mfma.hip", "shared_gemv.hip", "decode_fused.hip", "stage_copy.hip"]
+           "q4_grouped_mfma.hip", "shared_gemv.hip", "decode_fused.hip", "stage_copy.hip", "cache_device.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -95,6 +95,27 @@ struct StageCopyArgs {
 };
 hipError_t launch_stage_copy(const StageCopyArgs& a, hipStream_t s);
 
+// ---- the expert cache on the device (cache_device.hip): one layer step of
+// the eviction rule (policy 0 LRU, 1 LFU over every step), then the copies of
+// its misses from the device-mapped pinned pool.  Pointers are this layer's.
+struct CacheStepArgs {
+  int E, S, k, policy;
+  int64_t step, blob;
+  const int32_t* sel;    // [k] chosen experts
+  int32_t* table;        // [E] slot of each expert, -1 absent
+  int32_t* slot_expert;  // [S] expert of each slot, -1 empty
+  int64_t* stamp;        // [S] last step each slot was used, -1 never
+  int64_t* count;        // [E] use counts (LFU)
+  uint8_t* hit_mask;     // [k] out
+  int32_t* miss;         // [k][2] out: (expert, slot) installs in order
+  int32_t* n_miss;       // [1] out
+  int64_t* stats;        // [3] cumulative hits, misses, staged bytes
+  uint32_t* err;         // set when a selection is out of range or repeats an expert
+};
+hipError_t launch_cache_step(const CacheStepArgs& a, hipStream_t s);
+hipError_t launch_stage_misses(const uint8_t* pool_dev, uint8_t* arena, int E, int S, int k, int64_t blob,
+                               int64_t stride, const int32_t* miss, const int32_t* n_miss, hipStream_t s);
+
 // ---- fused batch-1 decode through many layers (decode_fused.hip)
 bool decode_fused_supported(int d, int f, int E, int k, int cus, int* G, int* rpw);
 size_t decode_fused_workspace_bytes(int L, int d, int f, int E, int k);

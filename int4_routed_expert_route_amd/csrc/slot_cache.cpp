@@ -51,6 +51,16 @@ struct moe_cache {
   std::vector<hipEvent_t> joins;     // one per helper stream
   hipEvent_t fork = nullptr;
   const uint8_t* pool_dev = nullptr; // MOE_STAGE_KERNEL: the pool as the device addresses it
+  // device mode (moe_cache_enable_device): the state lives in device memory
+  bool device = false;
+  int32_t* d_slot_expert = nullptr;  // [L][S]
+  int64_t* d_stamp = nullptr;        // [L][S]
+  int64_t* d_count = nullptr;        // [L][E]
+  int32_t* d_miss = nullptr;         // [L][k][2]
+  int32_t* d_nmiss = nullptr;        // [L]
+  int64_t* d_stats = nullptr;        // [3]
+  uint32_t* d_err = nullptr;         // [1]
+  std::vector<hipEvent_t> routed;    // per layer: the rule has run on the compute stream
 };
 
 // Failures are reported through the library's thread-local error text (api.cpp).
@@ -79,6 +89,28 @@ void rebuild_table(moe_cache* c, int layer) {
   }
 }
 
+// Device mode: bring the host mirror up to date (waits for the device).
+moe_status pull_device_state(const moe_cache* cc) {
+  moe_cache* c = const_cast<moe_cache*>(cc);
+  if (!c->device) return MOE_OK;
+  moe_status st;
+  if ((st = hipcheck(hipDeviceSynchronize(), "hipDeviceSynchronize")) ||
+      (st = hipcheck(hipMemcpy(c->slot_expert.data(), c->d_slot_expert, sizeof(int32_t) * c->slot_expert.size(),
+                               hipMemcpyDeviceToHost), "hipMemcpy")) ||
+      (st = hipcheck(hipMemcpy(c->stamp.data(), c->d_stamp, sizeof(int64_t) * c->stamp.size(), hipMemcpyDeviceToHost),
+                     "hipMemcpy")) ||
+      (st = hipcheck(hipMemcpy(c->count.data(), c->d_count, sizeof(int64_t) * c->count.size(), hipMemcpyDeviceToHost),
+                     "hipMemcpy")))
+    return st;
+  int64_t stats[3];
+  uint32_t err = 0;
+  if ((st = hipcheck(hipMemcpy(stats, c->d_stats, sizeof(stats), hipMemcpyDeviceToHost), "hipMemcpy")) ||
+      (st = hipcheck(hipMemcpy(&err, c->d_err, 4, hipMemcpyDeviceToHost), "hipMemcpy")))
+    return st;
+  c->stats = moe_stage_stats{stats[0], stats[1], stats[2]};
+  if (err) return cfail(MOE_ERR_ARG, "device cache: a selection was out of range or repeated an expert");
+  return MOE_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -135,6 +167,12 @@ moe_status moe_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_slots
 
 moe_status moe_cache_destroy(moe_cache* c) {
   if (!c) return MOE_OK;
+  if (c->device) hipDeviceSynchronize();
+  for (hipEvent_t e : c->routed)
+    if (e) hipEventDestroy(e);
+  for (void* p : {(void*)c->d_slot_expert, (void*)c->d_stamp, (void*)c->d_count, (void*)c->d_miss,
+                  (void*)c->d_nmiss, (void*)c->d_stats, (void*)c->d_err})
+    if (p) hipFree(p);
   for (size_t i = 0; i < c->helpers.size(); ++i) {
     if (c->helpers[i]) { hipStreamSynchronize(c->helpers[i]); hipStreamDestroy(c->helpers[i]); }
     if (c->joins[i]) hipEventDestroy(c->joins[i]);
@@ -155,6 +193,7 @@ moe_status moe_slot_stage(moe_cache* c, int32_t layer, int32_t step, const int32
                           hipStream_t side, hipStream_t compute, uint8_t* hit_mask_dev,
                           uint8_t* hit_mask_host, moe_stage_stats* stats) {
   if (!c || !sel_host || !hit_mask_dev) return cfail(MOE_ERR_ARG, "moe_slot_stage: null pointer");
+  if (c->device) return cfail(MOE_ERR_STATE, "moe_slot_stage: the cache runs on the device (moe_slot_stage_device)");
   if (layer < 0 || layer >= c->L) return cfail(MOE_ERR_ARG, "moe_slot_stage: layer out of range");
   for (int j = 0; j < c->k; ++j) {
     if (sel_host[j] < 0 || sel_host[j] >= c->E)
@@ -342,6 +381,8 @@ moe_status moe_cache_set_staging(moe_cache* c, int32_t mode, int32_t n_streams) 
 
 moe_status moe_cache_export_usage(const moe_cache* c, int64_t* counts_host, int32_t* recent_host) {
   if (!c || !counts_host) return cfail(MOE_ERR_ARG, "moe_cache_export_usage: null pointer");
+  moe_status pst = pull_device_state(c);
+  if (pst) return pst;
   if (c->policy == MOE_CACHE_LFU_WINDOW && !recent_host)
     return cfail(MOE_ERR_ARG, "moe_cache_export_usage: the windowed policy needs recent_host");
   std::memcpy(counts_host, c->count.data(), sizeof(int64_t) * c->count.size());
@@ -383,6 +424,96 @@ moe_status moe_cache_import_usage(moe_cache* c, const int64_t* counts_host, cons
   return MOE_OK;
 }
 
+moe_status moe_cache_enable_device(moe_cache* c) {
+  if (!c) return cfail(MOE_ERR_ARG, "moe_cache_enable_device: null cache");
+  if (c->device) return MOE_OK;
+  if (c->policy == MOE_CACHE_LFU_WINDOW)
+    return cfail(MOE_ERR_UNSUPPORTED, "moe_cache_enable_device: LRU or whole-run LFU only");
+  if (c->E > 256 || c->S > 256) return cfail(MOE_ERR_UNSUPPORTED, "moe_cache_enable_device: at most 256 experts");
+  void* d = nullptr;
+  if (c->blob % 16 || hipHostGetDevicePointer(&d, const_cast<uint8_t*>(c->pool), 0) != hipSuccess || !d ||
+      reinterpret_cast<uintptr_t>(d) % 16) {
+    (void)hipGetLastError();
+    return cfail(MOE_ERR_UNSUPPORTED, "moe_cache_enable_device: the host pool is not device-mapped pinned memory "
+                                      "(or blob_bytes % 16 != 0)");
+  }
+  c->pool_dev = static_cast<const uint8_t*>(d);
+  // finish every host-side staging first
+  for (int l = 0; l < c->L; ++l) {
+    if (c->staged_used[l]) hipEventSynchronize(c->staged[l]);
+    if (c->masked_used[l]) hipEventSynchronize(c->masked[l]);
+  }
+  const size_t nLS = (size_t)c->L * c->S, nLE = (size_t)c->L * c->E;
+  moe_status st;
+  if ((st = hipcheck(hipMalloc(&c->d_slot_expert, sizeof(int32_t) * nLS), "hipMalloc")) ||
+      (st = hipcheck(hipMalloc(&c->d_stamp, sizeof(int64_t) * nLS), "hipMalloc")) ||
+      (st = hipcheck(hipMalloc(&c->d_count, sizeof(int64_t) * nLE), "hipMalloc")) ||
+      (st = hipcheck(hipMalloc(&c->d_miss, sizeof(int32_t) * 2 * c->L * c->k), "hipMalloc")) ||
+      (st = hipcheck(hipMalloc(&c->d_nmiss, sizeof(int32_t) * c->L), "hipMalloc")) ||
+      (st = hipcheck(hipMalloc(&c->d_stats, sizeof(int64_t) * 3), "hipMalloc")) ||
+      (st = hipcheck(hipMalloc(&c->d_err, sizeof(uint32_t)), "hipMalloc")))
+    return st;
+  const int64_t stats[3] = {c->stats.hits, c->stats.misses, c->stats.bytes_staged};
+  const uint32_t zero = 0;
+  if ((st = hipcheck(hipMemcpy(c->d_slot_expert, c->slot_expert.data(), sizeof(int32_t) * nLS, hipMemcpyHostToDevice),
+                     "hipMemcpy")) ||
+      (st = hipcheck(hipMemcpy(c->d_stamp, c->stamp.data(), sizeof(int64_t) * nLS, hipMemcpyHostToDevice),
+                     "hipMemcpy")) ||
+      (st = hipcheck(hipMemcpy(c->d_count, c->count.data(), sizeof(int64_t) * nLE, hipMemcpyHostToDevice),
+                     "hipMemcpy")) ||
+      (st = hipcheck(hipMemcpy(c->d_stats, stats, sizeof(stats), hipMemcpyHostToDevice), "hipMemcpy")) ||
+      (st = hipcheck(hipMemcpy(c->d_err, &zero, 4, hipMemcpyHostToDevice), "hipMemcpy")))
+    return st;
+  c->routed.assign(c->L, nullptr);
+  for (int l = 0; l < c->L; ++l)
+    if ((st = hipcheck(hipEventCreateWithFlags(&c->routed[l], hipEventDisableTiming), "hipEventCreate"))) return st;
+  c->device = true;
+  c->staged_any = true;
+  return MOE_OK;
+}
+
+moe_status moe_slot_stage_device(moe_cache* c, int32_t layer, int32_t step, const int32_t* sel_dev,
+                                 hipStream_t side, hipStream_t compute, uint8_t* hit_mask_dev) {
+  if (!c || !sel_dev || !hit_mask_dev) return cfail(MOE_ERR_ARG, "moe_slot_stage_device: null pointer");
+  if (!c->device) return cfail(MOE_ERR_STATE, "moe_slot_stage_device: call moe_cache_enable_device first");
+  if (layer < 0 || layer >= c->L || step < 0) return cfail(MOE_ERR_ARG, "moe_slot_stage_device: bad layer or step");
+  moe::CacheStepArgs a{};
+  a.E = c->E; a.S = c->S; a.k = c->k;
+  a.policy = c->policy == MOE_CACHE_LFU ? 1 : 0;
+  a.step = step;
+  a.blob = c->blob;
+  a.sel = sel_dev;
+  a.table = c->tables_dev + (int64_t)layer * c->E;
+  a.slot_expert = c->d_slot_expert + (int64_t)layer * c->S;
+  a.stamp = c->d_stamp + (int64_t)layer * c->S;
+  a.count = c->d_count + (int64_t)layer * c->E;
+  a.hit_mask = hit_mask_dev;
+  a.miss = c->d_miss + (int64_t)layer * 2 * c->k;
+  a.n_miss = c->d_nmiss + layer;
+  a.stats = c->d_stats;
+  a.err = c->d_err;
+  moe_status st;
+  // the rule on the compute stream, after the router and after every kernel
+  // that still reads this layer's slots; the copies then on the side stream
+  if ((st = hipcheck(moe::launch_cache_step(a, compute), "cache step kernel")) ||
+      (st = hipcheck(hipEventRecord(c->routed[layer], compute), "hipEventRecord")) ||
+      (st = hipcheck(hipStreamWaitEvent(side, c->routed[layer], 0), "hipStreamWaitEvent")) ||
+      (st = hipcheck(moe::launch_stage_misses(c->pool_dev + (int64_t)layer * c->E * c->blob,
+                                              c->arena + (int64_t)layer * c->S * c->stride, c->E, c->S, c->k, c->blob,
+                                              c->stride, a.miss, a.n_miss, side), "stage kernel")) ||
+      (st = hipcheck(hipEventRecord(c->staged[layer], side), "hipEventRecord")))
+    return st;
+  c->staged_used[layer] = 1;
+  return MOE_OK;
+}
+
+moe_status moe_cache_stats(const moe_cache* c, moe_stage_stats* out) {
+  if (!c || !out) return cfail(MOE_ERR_ARG, "moe_cache_stats: null pointer");
+  moe_status st = pull_device_state(c);
+  *out = c->stats;
+  return st;
+}
+
 moe_status moe_cache_wait(moe_cache* c, int32_t layer, hipStream_t compute) {
   if (!c || layer < 0 || layer >= c->L) return cfail(MOE_ERR_ARG, "moe_cache_wait: bad cache or layer");
   if (!c->staged_used[layer]) return MOE_OK;
@@ -392,6 +523,8 @@ moe_status moe_cache_wait(moe_cache* c, int32_t layer, hipStream_t compute) {
 moe_status moe_cache_slot_table(const moe_cache* c, int32_t layer, int32_t* out_host) {
   if (!c || !out_host || layer < 0 || layer >= c->L)
     return cfail(MOE_ERR_ARG, "moe_cache_slot_table: bad argument");
+  moe_status pst = pull_device_state(c);
+  if (pst) return pst;
   for (int e = 0; e < c->E; ++e) out_host[e] = -1;
   for (int s = 0; s < c->S; ++s) {
     const int e = c->slot_expert[(int64_t)layer * c->S + s];
@@ -402,6 +535,8 @@ moe_status moe_cache_slot_table(const moe_cache* c, int32_t layer, int32_t* out_
 
 moe_status moe_cache_export(const moe_cache* c, int32_t* slot_expert_host, int64_t* stamp_host) {
   if (!c || !slot_expert_host || !stamp_host) return cfail(MOE_ERR_ARG, "moe_cache_export: null pointer");
+  moe_status pst = pull_device_state(c);
+  if (pst) return pst;
   std::memcpy(slot_expert_host, c->slot_expert.data(), sizeof(int32_t) * c->slot_expert.size());
   std::memcpy(stamp_host, c->stamp.data(), sizeof(int64_t) * c->stamp.size());
   return MOE_OK;
@@ -409,6 +544,7 @@ moe_status moe_cache_export(const moe_cache* c, int32_t* slot_expert_host, int64
 
 moe_status moe_cache_import(moe_cache* c, const int32_t* slot_expert_host, const int64_t* stamp_host) {
   if (!c || !slot_expert_host || !stamp_host) return cfail(MOE_ERR_ARG, "moe_cache_import: null pointer");
+  if (c->device) return cfail(MOE_ERR_STATE, "moe_cache_import: import before moe_cache_enable_device");
   for (int l = 0; l < c->L; ++l) {
     std::vector<char> seen(c->E, 0);
     for (int s = 0; s < c->S; ++s) {

@@ -273,3 +273,119 @@ def test_layer_through_cache_matches_oracle(api):
         assert row_rel_err(y.cpu().numpy() - x_np, ry - x_np) < TOL_FP32, t
         x_np = orc.rms_rescale(y.cpu().numpy().astype(np.float64), 1e-6).astype(np.float32)
     pool.cache.close()
+
+
+@pytest.mark.parametrize("policy", ["lru", "lfu"])
+@pytest.mark.parametrize("n_slots,steps", [(8, 60), (16, 40)])
+def test_device_cache_follows_oracle(api, n_slots, steps, policy):
+    """The rule run on the device (moe_slot_stage_device): hit masks, the device
+    slot tables and every staged slot's bytes after each step equal the
+    oracle's; the cumulative statistics and the exported state at the end too."""
+    d, f, E, k, nl = 256, 128, 32, 4, 2
+    pool = Pool(api, d, f, E, k, nl, n_slots, seed=8)
+    api.moe_cache_set_policy(pool.cache, _POLICY[policy], 0)
+    api.moe_cache_enable_device(pool.cache)
+    side, compute = torch.cuda.Stream(), torch.cuda.current_stream()
+    ref = [_oracle_cache(policy, 0, n_slots, E) for _ in range(nl)]
+    sels = [synth.markov_selections(E, k, steps, 8, l) for l in range(nl)]
+    hits = misses = 0
+    for t in range(steps):
+        for l in range(nl):
+            sel = np.random.default_rng(t * 5 + l).permutation(sels[l][t]).astype(np.int32)
+            sel_dev = torch.from_numpy(sel).cuda()
+            hit_dev = torch.zeros(16, dtype=torch.uint8, device="cuda")[:k]
+            api.moe_slot_stage_device(pool.cache, l, t, sel_dev, side, compute, hit_dev)
+            want_hit, installs = ref[l].step(t, [int(e) for e in sel])
+            hits += sum(want_hit)
+            misses += len(installs)
+            api.moe_cache_wait(pool.cache, l, compute)
+            torch.cuda.synchronize()
+            assert hit_dev.cpu().numpy().astype(bool).tolist() == want_hit, (t, l)
+            assert np.array_equal(pool.tables[l].cpu().numpy(), np.array(ref[l].slot_of_expert(), np.int32)), (t, l)
+            for e, s, _ in installs:
+                assert np.array_equal(pool.slot_bytes(l, s), pool.blobs[l][e]), (t, l, e, s)
+    st = api.moe_cache_stats(pool.cache)
+    assert (st.hits, st.misses, st.bytes_staged) == (hits, misses, misses * pool.blob)
+    se = torch.zeros(nl, n_slots, dtype=torch.int32)
+    stp = torch.zeros(nl, n_slots, dtype=torch.int64)
+    api.moe_cache_export(pool.cache, se, stp)
+    for l in range(nl):
+        want_se, want_st = ref[l].export_state()[:2]
+        assert se[l].tolist() == want_se and stp[l].tolist() == want_st, l
+    if policy == "lfu":
+        counts = torch.zeros(nl, E, dtype=torch.int64)
+        api.moe_cache_export_usage(pool.cache, counts, None)
+        for l in range(nl):
+            assert counts[l].tolist() == ref[l].counts(), l
+    pool.cache.close()
+
+
+def test_device_cache_refusals(api):
+    d, f, E, k, S = 256, 128, 16, 4, 8
+    pool = Pool(api, d, f, E, k, 1, S, seed=9)
+    api.moe_cache_set_policy(pool.cache, api.MOE_CACHE_LFU_WINDOW, 4)
+    with pytest.raises(api.MoeError):  # the windowed policy stays on the host
+        api.moe_cache_enable_device(pool.cache)
+    pool.cache.close()
+    pool = Pool(api, d, f, E, k, 1, S, seed=9)
+    api.moe_cache_enable_device(pool.cache)
+    side, compute = torch.cuda.Stream(), torch.cuda.current_stream()
+    hit_dev = torch.zeros(16, dtype=torch.uint8, device="cuda")[:k]
+    with pytest.raises(api.MoeError):  # host staging is off in device mode
+        _stage(api, pool, 0, 0, [0, 1, 2, 3], side, compute)
+    # a repeated expert changes nothing and is reported when the state is read
+    api.moe_slot_stage_device(pool.cache, 0, 0, torch.tensor([1, 1, 2, 3], dtype=torch.int32, device="cuda"), side,
+                              compute, hit_dev)
+    api.moe_cache_wait(pool.cache, 0, compute)
+    torch.cuda.synchronize()
+    with pytest.raises(api.MoeError):
+        api.moe_cache_stats(pool.cache)
+    assert np.all(pool.tables[0].cpu().numpy() == -1)
+    pool.cache.close()
+
+
+def test_layer_through_device_cache_matches_oracle(api):
+    """Decode steps of one layer with 8 of 32 experts resident and the cache on
+    the device: route, device rule on the router's own indices, gate/up for
+    hits, filler GEMV, wait, gate/up for misses, down + combine; no host copy
+    of the indices anywhere; against the oracle layer every step."""
+    d, f, E, k, S = 256, 128, 32, 4, 8
+    pool = Pool(api, d, f, E, k, 1, S, seed=10)
+    api.moe_cache_enable_device(pool.cache)
+    side, compute = torch.cuda.Stream(), torch.cuda.current_stream()
+    rw = synth.router_weight(d, E, 10, 0)
+    nw = synth.norm_weight(d, 10, 0)
+    sels = synth.markov_selections(E, k, 12, 10, 0)
+    dm = pool.dm
+    rw_d, nw_d = torch.from_numpy(rw).cuda(), torch.from_numpy(nw).cuda()
+    w_sh = torch.from_numpy(synth.shared_weight_bf16(4 * d, d, 10, 0).view(np.int16)).cuda()
+    ws = lambda c: torch.zeros(max(api.moe_workspace_size(c, 1, dm), 256), dtype=torch.uint8, device="cuda")
+    x_np = synth.tokens(1, d, 10)
+    for t in range(len(sels)):
+        bias = synth.selection_bias(sels[t], E)
+        x = torch.from_numpy(x_np).cuda()
+        h = torch.empty(1, d, device="cuda")
+        idx = torch.empty(1, k, dtype=torch.int32, device="cuda")
+        w = torch.empty(1, k, device="cuda")
+        api.moe_route(x, nw_d, 1e-6, rw_d, torch.from_numpy(bias).cuda(), 1, dm, h, idx, w, ws(0))
+        hit_dev = torch.zeros(16, dtype=torch.uint8, device="cuda")[:k]
+        api.moe_slot_stage_device(pool.cache, 0, t, idx[0], side, compute, hit_dev)
+        act = torch.zeros(k, f, device="cuda")
+        table = pool.tables[0]
+        api.moe_expert_q4_gateup(h, idx, table, S, pool.arena, pool.stride, None, None, hit_dev, 1, 1, dm,
+                                 api.MOE_PREC_FP32, act, ws(2))
+        s_out = torch.empty(1, 4 * d, device="cuda")
+        api.moe_shared_gemv_bf16(w_sh, h, 1, 4 * d, d, s_out)
+        api.moe_cache_wait(pool.cache, 0, compute)
+        api.moe_expert_q4_gateup(h, idx, table, S, pool.arena, pool.stride, None, None, hit_dev, 0, 1, dm,
+                                 api.MOE_PREC_FP32, act, ws(2))
+        y = torch.empty(1, d, device="cuda")
+        api.moe_expert_q4_down_combine(act, idx, w, table, S, pool.arena, pool.stride, None, None, None, x, 1, dm,
+                                       api.MOE_PREC_FP32, y, ws(3))
+        torch.cuda.synchronize()
+        assert sorted(idx.cpu().numpy()[0].tolist()) == sorted(sels[t].tolist())
+        ry, ridx, _, _, lg = orc.moe_layer(x_np, nw, rw, bias, lambda e: pool.blobs[0][e], d, f, k)
+        check_topk(idx.cpu().numpy(), ridx, lg)
+        assert row_rel_err(y.cpu().numpy() - x_np, ry - x_np) < TOL_FP32, t
+        x_np = orc.rms_rescale(y.cpu().numpy().astype(np.float64), 1e-6).astype(np.float32)
+    pool.cache.close()
