@@ -15,7 +15,9 @@
  *  - Every pointer named *_dev or documented as "device" is device memory the
  *    caller allocated (hipMalloc or a torch tensor); *_host is host memory.
  *    The library keeps no pointer after a call returns, except those registered
- *    with moe_cache_create.  It allocates no device memory on any compute call.
+ *    with moe_cache_create.  It allocates no device memory on any compute call;
+ *    the only set-up calls that do are moe_cache_enable_device (the cache's
+ *    device state) and moe_cache_set_staging (its copy streams).
  *  - Every compute call is asynchronous and ordered on the stream it is given
  *    (0 = the null stream).  Argument checks run on the host before anything is
  *    enqueued; a failed check enqueues nothing and returns an error code.
