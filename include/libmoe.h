@@ -446,7 +446,7 @@ moe_status moe_shared_gemv_bf16(const uint16_t* w, const float* h, int32_t T,
  *   w_down    device bf16 bits [d][f_sh]
  *   h         device fp32 [T][d];  residual device fp32 [T][d] or NULL
  *   out       device fp32 [T][d] (may be the residual)
- *   ws        device, moe_shared_expert_workspace_size(T, f_sh) bytes (g, u, act)
+ *   ws        device, moe_shared_expert_workspace_size(T, f_sh) bytes (the fp32 act)
  * d and f_sh multiples of 8; 16-byte aligned pointers.
  * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_CAPACITY.
  * ------------------------------------------------------------------------- */

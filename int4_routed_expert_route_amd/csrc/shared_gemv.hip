@@ -62,28 +62,66 @@ __global__ __launch_bounds__(256) void k_shared_gemv_bf16(const uint16_t* __rest
   }
 }
 
-// act[t][c] = gelu_tanh(gu[t][c]) * gu[t][f + c] for gu [T][2f]
-__global__ __launch_bounds__(256) void k_gated_act(const float* __restrict__ gu, int T, int f,
-                                                   float* __restrict__ act) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)T * f) return;
-  const int64_t t = i / f, c = i % f;
-  act[i] = gelu_tanh(gu[t * 2 * f + c]) * gu[t * 2 * f + f + c];
+// The shared expert's gate/up: wave c computes gate row c and up row f + c
+// of w_gu [2f][cols] against the same activation loads, then
+// act[t][c] = gelu_tanh(gate) * up.
+__global__ __launch_bounds__(256) void k_shared_gateup_bf16(const uint16_t* __restrict__ w,
+                                                            const float* __restrict__ h, int T, int f,
+                                                            int cols, float* __restrict__ act) {
+  const int lane = threadIdx.x % kWave;
+  const int c = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (c >= f) return;
+  const uint4* wg = reinterpret_cast<const uint4*>(w + (size_t)c * cols);
+  const uint4* wu = reinterpret_cast<const uint4*>(w + (size_t)(f + c) * cols);
+  const int n8 = cols / 8;
+  for (int t0 = 0; t0 < T; t0 += kSgTok) {
+    const int nt = min(kSgTok, T - t0);
+    float ag[kSgTok] = {0.f, 0.f, 0.f, 0.f}, au[kSgTok] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = lane; i < n8; i += kWave) {
+      const uint4 qg = wg[i], qu = wu[i];
+      const uint32_t ug[4] = {qg.x, qg.y, qg.z, qg.w}, uu[4] = {qu.x, qu.y, qu.z, qu.w};
+      float gv[8], uv[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        gv[2 * j] = __uint_as_float(ug[j] << 16);
+        gv[2 * j + 1] = __uint_as_float(ug[j] & 0xffff0000u);
+        uv[2 * j] = __uint_as_float(uu[j] << 16);
+        uv[2 * j + 1] = __uint_as_float(uu[j] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int tt = 0; tt < kSgTok; ++tt) {
+        if (tt < nt) {
+          const float4* hx = reinterpret_cast<const float4*>(h + (size_t)(t0 + tt) * cols + i * 8);
+          const float4 a = hx[0], b = hx[1];
+          const float hv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          float sg = ag[tt], su = au[tt];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            sg = fmaf(gv[j], hv[j], sg);
+            su = fmaf(uv[j], hv[j], su);
+          }
+          ag[tt] = sg;
+          au[tt] = su;
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < kSgTok; ++tt) {
+      const float g = wave_sum(ag[tt]), u = wave_sum(au[tt]);
+      if (tt < nt && lane == 0) act[(size_t)(t0 + tt) * f + c] = gelu_tanh(g) * u;
+    }
+  }
 }
 
 }  // namespace
 
-size_t shared_expert_workspace_bytes(int T, int f_sh) { return (size_t)T * 3 * f_sh * 4; }
+size_t shared_expert_workspace_bytes(int T, int f_sh) { return (size_t)T * f_sh * 4; }
 
 hipError_t launch_shared_expert_bf16(const uint16_t* w_gu, const uint16_t* w_down, const float* h,
                                      const float* residual, int T, int d, int f_sh, float* out, void* ws,
                                      hipStream_t s) {
-  float* gu = reinterpret_cast<float*>(ws);
-  float* act = gu + (size_t)T * 2 * f_sh;
-  hipLaunchKernelGGL(k_shared_gemv_bf16<false>, dim3((2 * f_sh + 3) / 4), dim3(256), 0, s, w_gu, h, T, 2 * f_sh, d,
-                     nullptr, gu);
-  const int64_t n = (int64_t)T * f_sh;
-  hipLaunchKernelGGL(k_gated_act, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gu, T, f_sh, act);
+  float* act = reinterpret_cast<float*>(ws);
+  hipLaunchKernelGGL(k_shared_gateup_bf16, dim3((f_sh + 3) / 4), dim3(256), 0, s, w_gu, h, T, f_sh, d, act);
   if (residual)
     hipLaunchKernelGGL(k_shared_gemv_bf16<true>, dim3((d + 3) / 4), dim3(256), 0, s, w_down, act, T, d, f_sh,
                        residual, out);

@@ -320,7 +320,8 @@ def test_shared_gemv_bf16():
     assert row_rel_err(_np(out), orc.shared_gemv(wb, h_np)) < TOL_FP32
 
 
-@pytest.mark.parametrize("d,f_sh,T,resid", [(256, 96, 1, True), (256, 96, 5, False), (2816, 3776, 1, True)])
+@pytest.mark.parametrize("d,f_sh,T,resid", [(256, 96, 1, True), (256, 96, 5, False), (256, 104, 9, True),
+                                           (2816, 3776, 1, True)])
 def test_shared_expert_bf16(d, f_sh, T, resid):
     """The shared expert (bf16 gated FFN plus residual) against the oracle, and
     as the residual of the routed combine: y = (x + shared(h)) + sum_j w_j o_j."""
