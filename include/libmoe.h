@@ -208,7 +208,10 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t T, moe_dims dims,
  *   prec           MOE_PREC_FP32: act is fp32 [T*k][f];
  *                  MOE_PREC_BF16_MFMA / MOE_PREC_F16_MFMA: grouped GEMM on MFMA
  *                  (needs offsets, T*k <= 2^22); act is block-scaled 16-bit
- *                  (layout and size: moe_act_bytes).
+ *                  (layout and size: moe_act_bytes).  With few tokens, experts
+ *                  of at most 32 routed rows are split along K over several
+ *                  workgroups; their partial sums and arrival counters live in
+ *                  ws, and the result is the same bits whichever arrives last.
  *   act            device, moe_act_bytes(T, dims, prec) bytes
  * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_CAPACITY, MOE_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------- */

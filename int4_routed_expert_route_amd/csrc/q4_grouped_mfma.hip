@@ -57,6 +57,18 @@ constexpr int LDA = BK + 8;           // padded LDS row (16-bit elements)
 constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxExp = 100;          // block exponents are clamped to [-kMaxExp, kMaxExp]
 constexpr int kRsrcWord3 = 0x00020000;  // buffer resource word 3: raw 32-bit data, no swizzle
+// Split-K: when a launch has fewer items than workgroups, items of at most
+// kSplitRows rows are cut into up to kMaxSplit K ranges of at least
+// kMinSplitSteps steps.  Each range's workgroup writes its fp32 accumulators
+// to the workspace; the last to arrive sums them in range order and runs the
+// epilogue (so the result does not depend on which arrives last).
+constexpr int kSplitRows = 32;
+constexpr int kMaxSplit = 4;
+constexpr int kMinSplitSteps = 6;
+constexpr int kMaxSplitItems = 512;      // items of a launch that splits (bounds the partials)
+constexpr int kPartF4 = 8 * kThreads;     // partials per split item, in floatx4: 2 row groups x 4 x the lanes
+constexpr int64_t kCntBytes = 2048;      // arrival counters, one per split item group
+constexpr int kSc1 = 16;                 // buffer op cache policy: device-coherent (write-through store)
 
 // Position p inside an 8-column block holds column kSlot[p].
 __host__ __device__ constexpr int slot_col(int p) { return (p & 1) ? 4 + (p >> 1) : (p >> 1); }
@@ -173,16 +185,18 @@ struct Plan {
   int beg[256];     // each rank's first position in sorted_pair (offsets, clamped)
   int ibase[256];   // first item of each rank (the item count W for ranks without items)
   int xstart[9];    // first item of each XCD's stretch; xstart[8] = W
+  int split;        // K ranges of each item of at most kSplitRows rows (1: no split)
 };
 
-// Called by all 256 threads; `scratch` (520 ints of LDS) is free until the
-// caller's next barrier.
-__device__ void plan_items(const int32_t* __restrict__ offsets, int E, int n_pairs, int NT, int* scratch,
-                           Plan& pl) {
+// Called by all 256 threads; `scratch` (528 ints of LDS) is free until the
+// caller's next barrier.  G = K steps; cap = most items a split launch may have.
+__device__ void plan_items(const int32_t* __restrict__ offsets, int E, int n_pairs, int NT, int G, int cap,
+                           int* scratch, Plan& pl) {
   int4* s_cnt4 = reinterpret_cast<int4*>(scratch);  // [256] counts by expert (-1 past E)
   int* s_cnt = scratch;
   int* s_rcnt = scratch + 256;                      // [256] counts by rank
   int* s_wsum = scratch + 512;                      // [2][4] per-wave scan totals
+  int* s_red = scratch + 520;                       // [2][4] per-wave item totals
   int* s_start = pl.xstart;
   const int t = threadIdx.x, lane = t % kWave, wv = t / kWave;
   int cnt = -1, a = 0;
@@ -214,10 +228,29 @@ __device__ void plan_items(const int32_t* __restrict__ offsets, int E, int n_pai
   const int r = t;
   const int rc = r < E ? s_rcnt[r] : 0;
   const int mt = (rc + BM - 1) / BM;
-  const int n_items = mt * NT;
+  // the split: as many K ranges as the workgroups left idle by the unsplit
+  // items allow, the same for every small item
+  const bool small = rc > 0 && rc <= kSplitRows;
+  int red_w = mt * NT, red_s = small ? NT : 0;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    red_w += __shfl_xor(red_w, o, kWave);
+    red_s += __shfl_xor(red_s, o, kWave);
+  }
+  if (lane == 0) {
+    s_red[wv] = red_w;
+    s_red[4 + wv] = red_s;
+  }
+  __syncthreads();
+  const int W1 = s_red[0] + s_red[1] + s_red[2] + s_red[3], Ws = s_red[4] + s_red[5] + s_red[6] + s_red[7];
+  int S = 1;
+  if (Ws > 0) S = max(1, min(min(kMaxSplit, G / kMinSplitSteps), (cap - (W1 - Ws)) / Ws));
+  const int sr = small ? S : 1;
+  const int ipt = NT * sr;  // items per M tile
+  const int n_items = mt * ipt;
   const int full = rc / BM, tail = rc % BM;
-  const int c_full = kItemFixedCost + BM / 16, c_tail = kItemFixedCost + (tail + 15) / 16;
-  const int cost = NT * (full * c_full + (tail ? c_tail : 0));
+  const int c_full = kItemFixedCost + BM / 16, c_tail = (kItemFixedCost + (tail + 15) / 16 + sr - 1) / sr;
+  const int cost = ipt * (full * c_full + (tail ? c_tail : 0));
   int inc_i = n_items, inc_c = cost;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
@@ -252,16 +285,19 @@ __device__ void plan_items(const int32_t* __restrict__ offsets, int E, int n_pai
       int pre = base_c, li = n_items;
       for (int m = 0; m < mt; ++m) {
         const int c = (m < full) ? c_full : c_tail;
-        if (pre + NT * c > target) {
-          li = m * NT + (target - pre + c - 1) / c;
+        if (pre + ipt * c > target) {
+          li = m * ipt + (target - pre + c - 1) / c;
           break;
         }
-        pre += NT * c;
+        pre += ipt * c;
       }
       s_start[x] = base_i + li;
     }
   }
-  if (t == 0) s_start[0] = 0;
+  if (t == 0) {
+    s_start[0] = 0;
+    pl.split = S;
+  }
   __syncthreads();
   if (t == 0) {
     int next = W;  // XCDs past the last boundary get empty stretches
@@ -306,6 +342,9 @@ struct GemmArgs {
   int64_t off_q0, off_q1, off_sb0, off_sb1;  // gate/up sections, or down in q0/sb0
   void* out;              // gate/up: act values [T*k][f] (ET); down: pair values [T*k][d] fp16
   int8_t* out_exp;        // exponents [T*k][cols/64]
+  floatx4* part;          // split items' partial accumulators [split_cap][kPartF4]
+  uint32_t* cnt;          // arrival counters [split_cap], zero between launches
+  int split_cap;          // most items a split launch may have (also capped by the grid)
 };
 
 // LDS of one pipeline stage (one K step).
@@ -389,6 +428,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
   __shared__ int s_gexp[kMaxSteps];  // down: tile exponent of each K group
   __shared__ int s_fix;              // down: some row's exponents differ from its tile's
   __shared__ Plan s_plan;
+  __shared__ uint32_t s_ticket;
   const int t = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(t / kWave), lane = t % kWave;
   const int n = lane % 16, kq = lane / 16;  // MFMA lane coordinates
@@ -407,7 +447,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
   const uint32_t sb_rd = lds_addr(&lds[0].sb[wid][n]);
 
   // the work list, in LDS (stage 0 of the pipeline serves as scratch)
-  plan_items(a.offsets, a.E, n_pairs, a.NT, reinterpret_cast<int*>(&lds[0]), s_plan);
+  plan_items(a.offsets, a.E, n_pairs, a.NT, G, min(a.split_cap, (int)gridDim.x), reinterpret_cast<int*>(&lds[0]),
+             s_plan);
   const int xcd = (int)(blockIdx.x % 8), nper = (int)(gridDim.x / 8);
   const int i_end = __builtin_amdgcn_readfirstlane(s_plan.xstart[xcd + 1]);
   for (int item = __builtin_amdgcn_readfirstlane(s_plan.xstart[xcd]) + (int)(blockIdx.x / 8); item < i_end;
@@ -423,13 +464,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
         else hi = mid - 1;
       }
     }
-    const int li = item - s_plan.ibase[rk];
+    const int li = __builtin_amdgcn_readfirstlane(item - s_plan.ibase[rk]);
     // the expert, its pair count and first position come from the plan in
     // LDS (no global round trip before the item's first load)
     const int ec = __builtin_amdgcn_readfirstlane(s_plan.ecnt[rk]);
     const int e = ec & 255;
-    const int m0 = __builtin_amdgcn_readfirstlane((li / a.NT) * BM);
-    const int nt = __builtin_amdgcn_readfirstlane(li % a.NT);
+    // item = (M tile, N tile, K range): K steps s0 .. s1 - 1
+    const int sr = __builtin_amdgcn_readfirstlane((ec >> 8) <= kSplitRows ? s_plan.split : 1);
+    const int tile = __builtin_amdgcn_readfirstlane(li / sr), ks = __builtin_amdgcn_readfirstlane(li - tile * sr);
+    const int s0 = __builtin_amdgcn_readfirstlane(ks * G / sr), s1 = __builtin_amdgcn_readfirstlane((ks + 1) * G / sr);
+    const int m0 = __builtin_amdgcn_readfirstlane((tile / a.NT) * BM);
+    const int nt = __builtin_amdgcn_readfirstlane(tile % a.NT);
     const int beg = __builtin_amdgcn_readfirstlane(s_plan.beg[rk]);
     const int end = beg + (ec >> 8);
     const int rows = max(0, min(BM, end - beg - m0));
@@ -519,9 +564,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
     uint32_t bsb[4];
     // the first two K steps go out before anything else (DIRECT: the
     // activations of step 0, the weights of step 0, the activations of step 1)
-    issue(0, 0);
-    if (DIRECT) load_b(0, bq, bsb);
-    if (G > 1) issue(1, 1);
+    issue(s0, 0);
+    if (DIRECT) load_b(s0, bq, bsb);
+    if (s1 - s0 > 1) issue(s0 + 1, 1);
 
     // down: each group's tile exponent.  Activations written by the gate/up
     // kernel share one exponent per tile and group, so the first row's are the
@@ -668,13 +713,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
         mfma_half(fy, fb, 1);
       }
     };
-    for (int s = 0; s < G; ++s) {
-      const int st = s % kStages;
+    for (int s = s0; s < s1; ++s) {
+      const int st = (s - s0) % kStages;
       if (DIRECT) {
         // issue order per step: weights of s + 1, then activations of s + 2,
         // so only the activations of step s + 1 may still be in flight here
         constexpr int kRest = (0x7 << 4) | (0xF << 8);
-        if (s + 1 < G) {
+        if (s + 1 < s1) {
           if (n_a == 1) __builtin_amdgcn_s_waitcnt(1 | kRest);
           else if (n_a == 2) __builtin_amdgcn_s_waitcnt(2 | kRest);
           else if (n_a == 3) __builtin_amdgcn_s_waitcnt(3 | kRest);
@@ -683,7 +728,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
           __builtin_amdgcn_s_waitcnt(kRest);
         }
       } else {
-        vm_wait_steps(s + 1 < G, n_a);     // this wave's DMA for step s has landed
+        vm_wait_steps(s + 1 < s1, n_a);    // this wave's DMA for step s has landed
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // and its LDS accesses (lgkmcnt 0)
       __builtin_amdgcn_s_barrier();        // ... and every other wave's
@@ -693,16 +738,63 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
       }
       u32x2 nq[4];
       uint32_t nsb[4];
-      if (DIRECT && s + 1 < G) load_b(s + 1, nq, nsb);
-      if (s + 2 < G) issue(s + 2, (s + 2) % kStages);
+      if (DIRECT && s + 1 < s1) load_b(s + 1, nq, nsb);
+      if (s + 2 < s1) issue(s + 2, (s - s0 + 2) % kStages);
       if (wave_ok) compute(s, st, bq, bsb);
-      if (DIRECT && s + 1 < G) {
+      if (DIRECT && s + 1 < s1) {
 #pragma unroll
         for (int ng = 0; ng < 4; ++ng) {
           bq[ng] = nq[ng];
           bsb[ng] = nsb[ng];
         }
       }
+    }
+
+    // ---- split items: partials out; the last K range to arrive sums them
+    // (in range order) and goes on to the epilogue, the others are done.
+    // The partials are written through to memory and read back with
+    // device-coherent loads, and each wave waits for its stores before the
+    // workgroup's arrival, so no cache-wide release or acquire is needed (an
+    // agent-scope acquire would drop the L2 lines every other workgroup of
+    // the XCD is streaming).
+    if (sr > 1) {
+      const int first = item - ks;  // the item group's first item: its counter
+      const __amdgpu_buffer_rsrc_t rsP = __builtin_amdgcn_make_buffer_rsrc(
+          a.part + (int64_t)first * kPartF4, (short)0, sr * kPartF4 * (int)sizeof(floatx4), kRsrcWord3);
+      const int lane_off = t * (int)sizeof(floatx4);
+      if (wave_ok) {
+        const int mine = __builtin_amdgcn_readfirstlane(ks * kPartF4 * (int)sizeof(floatx4));
+#pragma unroll
+        for (int mg = 0; mg < 2; ++mg)
+          if (mg < n_mg)
+#pragma unroll
+            for (int ng = 0; ng < 4; ++ng)
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[mg][ng]), rsP,
+                                                     lane_off + (mg * 4 + ng) * kThreads * (int)sizeof(floatx4),
+                                                     mine, kSc1);
+      }
+      __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0): this wave's partials are in memory
+      __syncthreads();
+      if (t == 0) s_ticket = __hip_atomic_fetch_add(a.cnt + first, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (s_ticket != (uint32_t)(sr - 1)) continue;
+      if (wave_ok) {
+#pragma unroll
+        for (int mg = 0; mg < 2; ++mg)
+          if (mg < n_mg)
+#pragma unroll
+            for (int ng = 0; ng < 4; ++ng) {
+              const int off = lane_off + (mg * 4 + ng) * kThreads * (int)sizeof(floatx4);
+              floatx4 v = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rsP, off, 0, kSc1));
+              for (int j = 1; j < sr; ++j)
+                v += __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rsP, off, __builtin_amdgcn_readfirstlane(
+                                                                   j * kPartF4 * (int)sizeof(floatx4)),
+                                                     kSc1));
+              acc[mg][ng] = v;
+            }
+      }
+      if (t == 0) __hip_atomic_store(a.cnt + first, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // ---- epilogue
@@ -834,11 +926,19 @@ static int max_items(int T, int k, int E, int NT) { return ((T * k + BM - 1) / B
 
 size_t mfma_act_bytes(int T, int f, int k) { return (size_t)T * k * f * 2 + (size_t)T * k * (f / kGroup); }
 
+// Workspace: arrival counters, then h in 16-bit slot order (gate/up) or the
+// pair outputs (down), then the split items' partials.
+static int split_item_cap(int T, int k, int E, int NT) { return std::min(kMaxSplitItems, max_items(T, k, E, NT)); }
+static int64_t part_bytes(int cap) { return (int64_t)cap * kPartF4 * (int64_t)sizeof(floatx4); }
+static int64_t gateup_body_bytes(int T, int d) { return round256((int64_t)T * d * 2); }
+static int64_t down_body_bytes(int T, int d, int k) {
+  return round256((int64_t)T * k * d * 2) + round256((int64_t)T * k * (d / kGroup));
+}
+
 size_t mfma_workspace_bytes(int call, int T, int d, int f, int E, int k) {
-  (void)f;
-  (void)E;
-  if (call == MOE_CALL_GATEUP) return round256((int64_t)T * d * 2);  // h in 16-bit, slot order
-  return round256((int64_t)T * k * d * 2) + round256((int64_t)T * k * (d / kGroup));  // pair outputs
+  if (call == MOE_CALL_GATEUP)
+    return kCntBytes + gateup_body_bytes(T, d) + part_bytes(split_item_cap(T, k, E, gemm_nt(true, d, f)));
+  return kCntBytes + down_body_bytes(T, d, k) + part_bytes(split_item_cap(T, k, E, gemm_nt(false, d, f)));
 }
 
 // Persistent grid: two workgroups per compute unit (the kernel's occupancy),
@@ -868,7 +968,7 @@ hipError_t launch_gateup_mfma(bool f16, bool direct, const float* h, const int32
                               int64_t off_sb1, void* act_out, void* ws, hipStream_t s) {
   const int NT = gemm_nt(true, d, f);
   const int items = max_items(T, k, E, NT);
-  char* rest = reinterpret_cast<char*>(ws);
+  char* rest = reinterpret_cast<char*>(ws) + kCntBytes;
   const int64_t n8 = (int64_t)T * d / 8;
   if (f16)
     hipLaunchKernelGGL(k_h_to_slots<_Float16>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, h, n8,
@@ -893,6 +993,9 @@ hipError_t launch_gateup_mfma(bool f16, bool direct, const float* h, const int32
   a.off_q0 = off_q0; a.off_q1 = off_q1; a.off_sb0 = off_sb0; a.off_sb1 = off_sb1;
   a.out = act_out;
   a.out_exp = reinterpret_cast<int8_t*>(act_out) + (int64_t)T * k * f * 2;
+  a.cnt = reinterpret_cast<uint32_t*>(ws);
+  a.part = reinterpret_cast<floatx4*>(rest + gateup_body_bytes(T, d));
+  a.split_cap = split_item_cap(T, k, E, NT);
   if (f16 && direct) launch_gemm<_Float16, true, true>(a, items, s, MOE_CALL_GATEUP);
   else if (f16) launch_gemm<_Float16, true>(a, items, s, MOE_CALL_GATEUP);
   else launch_gemm<__bf16, true>(a, items, s, MOE_CALL_GATEUP);
@@ -905,7 +1008,7 @@ hipError_t launch_down_mfma(bool f16, bool direct, const void* act_in, const int
                             const float* residual, float* y, void* ws, hipStream_t s) {
   const int NT = gemm_nt(false, d, f);
   const int items = max_items(T, k, E, NT);
-  char* rest = reinterpret_cast<char*>(ws);
+  char* rest = reinterpret_cast<char*>(ws) + kCntBytes;
   _Float16* pair_val = reinterpret_cast<_Float16*>(rest);
   int8_t* pair_exp = reinterpret_cast<int8_t*>(rest + round256((int64_t)T * k * d * 2));
   GemmArgs a{};
@@ -925,6 +1028,9 @@ hipError_t launch_down_mfma(bool f16, bool direct, const void* act_in, const int
   a.off_q0 = off_q; a.off_sb0 = off_sb;
   a.out = pair_val;
   a.out_exp = pair_exp;
+  a.cnt = reinterpret_cast<uint32_t*>(ws);
+  a.part = reinterpret_cast<floatx4*>(rest + down_body_bytes(T, d, k));
+  a.split_cap = split_item_cap(T, k, E, NT);
   if (f16 && direct) launch_gemm<_Float16, false, true>(a, items, s, MOE_CALL_DOWN_COMBINE);
   else if (f16) launch_gemm<_Float16, false>(a, items, s, MOE_CALL_DOWN_COMBINE);
   else launch_gemm<__bf16, false>(a, items, s, MOE_CALL_DOWN_COMBINE);

@@ -77,10 +77,17 @@ class SmallLayer:
 
 @pytest.mark.parametrize("prec", ["f16", "bf16", "f16direct"])
 @pytest.mark.parametrize("d,f,E_,k,T", [(256, 128, 16, 4, 40), (320, 192, 8, 2, 7), (2816, 704, 128, 8, 1),
-                                        (2816, 704, 128, 8, 48), (384, 256, 4, 2, 300)])
+                                        (2816, 704, 128, 8, 48), (384, 256, 4, 2, 300), (1088, 576, 16, 4, 40),
+                                        (1600, 768, 16, 4, 40)])
 def test_prefill_parity_small(api, d, f, E_, k, T, prec):
     """Several M tiles per expert (T=300 over 4 experts) with ragged tails,
-    N tiles with a partial last tile (f=192, d=320), and single tokens."""
+    N tiles with a partial last tile (f=192, d=320), and single tokens.  With
+    few items the small ones are split along K (at least 6 steps a range):
+    T=1 (one row each; gate/up in 4 ranges of 11 K steps, down's 11 steps not
+    split); d=1088, f=576 (gate/up's 17 steps in 8 + 9, a partial N tile);
+    d=1600, f=768 (gate/up's 25 steps in 6, 6, 6, 7, down's 12 in 6 + 6 with a
+    partial N tile).  The last two have experts of more than 32 rows, which
+    are not split, beside split ones."""
     tol = PRECS[prec][2]
     layer = SmallLayer(d, f, E_, seed=4)
     arena = torch.from_numpy(np.concatenate([layer.blobs[e] for e in range(E_)])).cuda()
@@ -198,7 +205,7 @@ def test_prefill_full_size_sampled(api, prec):
     assert np.all(np.isfinite(_np(out["y"])))
 
 
-@pytest.mark.parametrize("d,f,E_,k,T", [(256, 128, 16, 4, 40), (2816, 704, 128, 8, 300)])
+@pytest.mark.parametrize("d,f,E_,k,T", [(256, 128, 16, 4, 40), (2816, 704, 128, 8, 300), (1600, 768, 16, 4, 40)])
 def test_prefill_direct_loads_match_staged_tiles(api, d, f, E_, k, T):
     """Weights loaded straight into registers give bit for bit the staged-tile
     path's act and output: the same dequantised values meet the same MFMAs in
@@ -211,3 +218,41 @@ def test_prefill_direct_loads_match_staged_tiles(api, d, f, E_, k, T):
     assert np.array_equal(_np(a["idx"]), _np(b["idx"]))
     assert np.array_equal(a["act"], b["act"])
     assert np.array_equal(_np(a["y"]), _np(b["y"]))
+
+
+@pytest.mark.parametrize("d,f,E_,k,T", [(2816, 704, 128, 8, 1), (2816, 704, 128, 8, 32), (1600, 768, 16, 4, 40)])
+def test_split_k_deterministic_and_counters_reset(api, d, f, E_, k, T):
+    """Items split along K give the same bits on every call, whichever K range
+    arrives last (the partials are summed in range order), and each call
+    leaves the workspace's arrival counters at zero, so one workspace serves
+    call after call.  The 32-token case is the batched-decode shape; the last
+    splits the down GEMM too."""
+    layer = SmallLayer(d, f, E_, seed=12)
+    arena = torch.from_numpy(np.concatenate([layer.blobs[e] for e in range(E_)])).cuda()
+    x_np = synth.tokens(T, d, seed=12, stream=T)
+    ref = run_prefill(api, x_np, layer, arena, d, f, E_, k)
+    dm = api.dims(d, f, E_, k)
+    stride = api.moe_expert_blob_bytes(dm)
+    slots = torch.arange(E_, dtype=torch.int32, device="cuda")
+    counts = torch.empty(E_, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E_ + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    api.moe_permute(ref["idx"], T, dm, counts, offsets, sp, pp)
+    pc = api.MOE_PREC_F16_MFMA
+    wsg = torch.zeros(api.moe_workspace_size(api.MOE_CALL_GATEUP, T, dm, pc), dtype=torch.uint8, device="cuda")
+    wsd = torch.zeros(api.moe_workspace_size(api.MOE_CALL_DOWN_COMBINE, T, dm, pc), dtype=torch.uint8,
+                      device="cuda")
+    for _ in range(3):
+        act = torch.zeros(api.moe_act_bytes(T, dm, pc), dtype=torch.uint8, device="cuda")
+        api.moe_expert_q4_gateup(ref["h"], ref["idx"], slots, E_, arena, stride, offsets, sp, None, 0, T, dm, pc,
+                                 act, wsg)
+        y = torch.empty(T, d, device="cuda")
+        api.moe_expert_q4_down_combine(act, ref["idx"], ref["w"], slots, E_, arena, stride, offsets, sp, pp,
+                                       ref["x"], T, dm, pc, y, wsd)
+        assert np.array_equal(decode_scaled_act(act, T * k, f, torch.float16), ref["act"])
+        assert np.array_equal(_np(y), _np(ref["y"]))
+        assert not _np(wsg[:2048]).any() and not _np(wsd[:2048]).any()
+    ry, *_ = orc.moe_layer(x_np, layer.norm_w, layer.router_w, layer.bias, layer.blob_of, d, f, k,
+                           idx_override=_np(ref["idx"]))
+    assert row_rel_err(_np(ref["y"]) - x_np, ry - x_np) < TOL_BF16
