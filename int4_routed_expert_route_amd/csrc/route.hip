@@ -355,16 +355,20 @@ __global__ __launch_bounds__(kRWaves * kWave) void k_router_mfma(const float* __
   }
 }
 
-// Per token (one wave): the RMSNorm factor r = 1/sqrt(mean(x^2) + eps) from
-// the token's row, logits = r * (sum of the K-slice partials in slice order) +
-// bias, top-k and the renormalised weights, and h = x * r * w.
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partial, int slices,
+// Per token (one wave, one workgroup): the RMSNorm factor
+// r = 1/sqrt(mean(x^2) + eps) from the token's row, logits = r * (sum of the
+// K-slice partials in slice order) + bias, top-k and the renormalised weights,
+// and h = x * r * w.  A wave issues ~100 vector memory instructions (16 slice
+// partials per expert group, the row, the norm weights, the h stores); with one
+// wave per workgroup the tokens spread over T compute units instead of T/4,
+// whose instruction issue was the limit.
+__global__ __launch_bounds__(kWave) void k_topk(const float* __restrict__ partial, int slices,
                                               const float* __restrict__ x, const float* __restrict__ norm_w,
                                               float eps, int d, const float* __restrict__ router_bias, int T,
                                               int E, int k, float* __restrict__ h_out,
                                               int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
-  const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x;
+  const int t = blockIdx.x;
   if (t >= T) return;
   // every slice's partial and the token's row go out before the first add (a
   // loop of dependent loads would pay one memory round trip per slice)
@@ -463,7 +467,7 @@ hipError_t launch_route(const float* x, const float* norm_w, float eps, const fl
   else
     launch_maybe_timed2(k_router_mfma<1>, dim3((T + rt - 1) / rt, sp.slices), kRWaves * kWave, s, ev0, ev1, x,
                         norm_w, router_w, T, d, E, sp.kslice, logits);
-  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, sp.slices, x, norm_w, eps, d, router_bias,
+  hipLaunchKernelGGL(k_topk, dim3(T), dim3(kWave), 0, s, logits, sp.slices, x, norm_w, eps, d, router_bias,
                      T, E, k, h_out, topk_idx, topk_w);
   return hipGetLastError();
 }
