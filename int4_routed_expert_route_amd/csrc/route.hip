@@ -383,16 +383,24 @@ __global__ __launch_bounds__(kWave) void k_topk(const float* __restrict__ partia
 #pragma unroll
     for (int s = 0; s < kMaxSlices; ++s) p[i][s] = partial[((size_t)min(s, slices - 1) * T + t) * E + ec];
   }
-  // the token's row: all of it at once when it fits in registers
+  // the bias, and the token's row with its norm weights: all of it at once
+  // when it fits in registers (none of these loads waits for the row's sum)
+  float bv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bv[i] = (router_bias && kWave * i < E) ? router_bias[min(lane + kWave * i, E - 1)] : 0.0f;
   const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)t * d);
+  const float4* n4 = reinterpret_cast<const float4*>(norm_w);
   const bool in_regs = d <= kWave * 4 * kMaxV;
-  float4 xv[kMaxV];
+  float4 xv[kMaxV], nv[kMaxV];
   float ss = 0.0f;
   if (in_regs) {
 #pragma unroll
     for (int i = 0; i < kMaxV; ++i) {
       const int fi = lane + kWave * i;
-      if (kWave * i < d / 4) xv[i] = x4[min(fi, d / 4 - 1)];
+      if (kWave * i < d / 4) {
+        xv[i] = x4[min(fi, d / 4 - 1)];
+        if (norm_w) nv[i] = n4[min(fi, d / 4 - 1)];
+      }
     }
 #pragma unroll
     for (int i = 0; i < kMaxV; ++i)
@@ -414,14 +422,12 @@ __global__ __launch_bounds__(kWave) void k_topk(const float* __restrict__ partia
     for (int s = 0; s < kMaxSlices; ++s)
       if (s < slices) acc += p[i][s];
     acc *= rinv;
-    if (ok[i] && router_bias) acc += router_bias[lane + kWave * i];
+    acc += bv[i];
     v[i] = ok[i] ? acc : 0.0f;
   }
   float4* h4 = reinterpret_cast<float4*>(h_out + (size_t)t * d);
-  const float4* n4 = reinterpret_cast<const float4*>(norm_w);
-  auto put = [&](int fi, float4 a) {
+  auto put = [&](int fi, float4 a, float4 n) {
     if (norm_w) {
-      const float4 n = n4[fi];
       a.x = a.x * rinv * n.x; a.y = a.y * rinv * n.y;
       a.z = a.z * rinv * n.z; a.w = a.w * rinv * n.w;
     }
@@ -430,10 +436,10 @@ __global__ __launch_bounds__(kWave) void k_topk(const float* __restrict__ partia
   if (in_regs) {
 #pragma unroll
     for (int i = 0; i < kMaxV; ++i)
-      if (lane + kWave * i < d / 4) put(lane + kWave * i, xv[i]);
+      if (lane + kWave * i < d / 4) put(lane + kWave * i, xv[i], norm_w ? nv[i] : xv[i]);
   } else {
 #pragma unroll 4
-    for (int fi = lane; fi < d / 4; fi += kWave) put(fi, x4[fi]);
+    for (int fi = lane; fi < d / 4; fi += kWave) put(fi, x4[fi], norm_w ? n4[fi] : x4[fi]);
   }
   wave_topk_vals(v, ok, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
 }
