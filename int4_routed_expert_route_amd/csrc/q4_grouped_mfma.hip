@@ -68,6 +68,7 @@ constexpr int kMinSplitSteps = 6;
 constexpr int kMaxSplitItems = 512;      // items of a launch that splits (bounds the partials)
 constexpr int kPartF4 = 8 * kThreads;     // partials per split item, in floatx4: 2 row groups x 4 x the lanes
 constexpr int64_t kCntBytes = 2048;      // arrival counters, one per split item group
+static_assert(kCntBytes >= kMaxSplitItems * 4, "one 32-bit arrival counter per split item");
 constexpr int kSc1 = 16;                 // buffer op cache policy: device-coherent (write-through store)
 
 // Position p inside an 8-column block holds column kSlot[p].
