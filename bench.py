@@ -57,10 +57,10 @@ TRAFFIC = {
                "fetch_bytes": 18093516, "write_bytes": 22528},
     "decode_fused": {"sources": ('decode_fused.hip', 'q4_lane.h', 'common.h'), "sha256_16": "e38b527d1b6f8d39",
                      "fetch_bytes": 954574168, "write_bytes": 8112864},
-    "prefill": {"sources": ('q4_grouped_mfma.hip', 'common.h'), "sha256_16": "5be35f5c1be00e2f",
-                "fetch_bytes": 225747681, "write_bytes": 23863840},
-    "batched_f16": {"sources": ('q4_grouped_mfma.hip', 'common.h'), "sha256_16": "5be35f5c1be00e2f",
-                    "fetch_bytes": 48092804, "write_bytes": 9037792},
+    "prefill": {"sources": ('q4_grouped_mfma.hip', 'common.h'), "sha256_16": "6e9a36128a0f25f9",
+                "fetch_bytes": 226804165, "write_bytes": 23889872},
+    "batched_f16": {"sources": ('q4_grouped_mfma.hip', 'common.h'), "sha256_16": "6e9a36128a0f25f9",
+                    "fetch_bytes": 48092100, "write_bytes": 9037792},
 }
 
 

@@ -479,6 +479,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
     const int beg = __builtin_amdgcn_readfirstlane(s_plan.beg[rk]);
     const int end = beg + (ec >> 8);
     const int rows = max(0, min(BM, end - beg - m0));
+    // weights through the slot table; an absent expert gives NaN outputs.
+    // The slot is requested before the tile's pair ids, so the two loads
+    // share one memory round trip.
+    const int slot_ld = (e >= 0 && e < a.E) ? a.slot_of_expert[e] : -1;
     if (t < BM) {
       int p = -1;
       if (t < rows) {
@@ -488,8 +492,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
       s_pair[t] = p;
     }
     if (kScaledA && t == 0) s_fix = 0;
-    // weights through the slot table; an absent expert gives NaN outputs
-    const int slot = (e >= 0 && e < a.E) ? __builtin_amdgcn_readfirstlane(a.slot_of_expert[e]) : -1;
+    const int slot = __builtin_amdgcn_readfirstlane(slot_ld);
     const bool ok = slot >= 0 && slot < a.n_slots;
     const uint8_t* blob = a.arena + (ok ? (int64_t)slot * a.slot_stride : 0);
     __syncthreads();
