@@ -134,20 +134,45 @@ def time_launch(api, torch, call, launch, n):
     return float(np.mean(durs)), float(np.median(durs))
 
 
-def oracle_threads():
+def host_cpu():
+    """CPU model, physical cores and the threads this process may use (its
+    affinity, capped by OMP_NUM_THREADS when that is set)."""
+    model, cores = "unknown", set()
     try:
-        from threadpoolctl import threadpool_info
-        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        return os.cpu_count() or 1
+        phys = core = None
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and model == "unknown":
+                    model = v
+                elif k == "physical id":
+                    phys = v
+                elif k == "core id":
+                    core = v
+                elif not k and phys is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+        if phys is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        threads = min(threads, int(omp))
+    return model, len(cores) or None, threads
 
 
 def cpu_baseline(seed, T, budget_s, what, bias_of=None):
-    """The CPU oracle on a bounded sample of the workload: T tokens through the
-    layers in order until ~budget_s of oracle time (at most all 30); expert
-    blob generation is untimed.  Scaled to tokens/s of the 30-layer stack."""
+    """The CPU oracle (plain C++ fp32, std::thread over independent rows and
+    pairs) on a bounded sample of the workload: T tokens through the layers in
+    order until ~budget_s of oracle time (at most all 30); expert blob
+    generation is untimed.  Scaled to tokens/s of the 30-layer stack."""
     import oracle as orc
-    x = synth.tokens(T, D, seed, stream=7 if T > 1 else 0).astype(np.float64)
+    model, phys, threads = host_cpu()
+    orc.set_threads(threads)
+    x = synth.tokens(T, D, seed, stream=7 if T > 1 else 0)
     spent, done = 0.0, 0
     for l in range(NL):
         blobs = dict(zip(range(E), synth.expert_blobs(D, F, seed, l, range(E), threads=16)))
@@ -161,7 +186,9 @@ def cpu_baseline(seed, T, budget_s, what, bias_of=None):
         if spent >= budget_s:
             break
     per_pass = spent / done * NL
-    return {"value": T / per_pass, "unit": "tokens/s", "cores": int(oracle_threads()), "kind": "oracle",
+    return {"value": T / per_pass, "unit": "tokens/s", "cores": int(orc.threads()), "kind": "oracle",
+            "oracle": "plain C++17 fp32 (oracle/moe_oracle.cpp), sequential sums, std::thread",
+            "cpu_model": model, "physical_cores": phys,
             "sample": f"{T} token(s) through layers 0-{done - 1} of one {what} step, {spent:.1f} s of oracle time"
                       + ("" if done == NL else f", scaled x{NL / done:.2f} to the 30-layer stack")}
 

@@ -1,7 +1,12 @@
-"""Plain, slow, obviously-correct CPU oracle of the routed int4 MoE layer.
+"""Float64 textbook form of the routed int4 MoE layer, in numpy.
 
-TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
-benchmark's ``cpu_baseline`` leg may import this module.  It shares no code with
+TEST INFRASTRUCTURE.  This is the cross-check of the oracle proper (the plain
+C++ fp32 oracle in ``moe_oracle.cpp``, loaded through ``oracle.cpp``): the same
+steps written from the same definitions, in another language and in float64,
+with dense dequantised matrices and library matrix products.  The pins hold
+for both, and the two agree to fp32 rounding on random layers.  Only
+``tests/``, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline``
+leg may import this module.  It shares no code with
 the HIP library (no kernels, headers, tables or helpers) and parses the expert
 byte format on its own from the format's definition.  All floating point is
 float64 except where a float decides an integer (the top-k choice), which is
@@ -272,24 +277,6 @@ def moe_layer(x, norm_w, router_w, bias, blob_of, d: int, f: int, k: int,
             outs[t, j] = o[n]
     y = combine(np.atleast_2d(x) if residual else None, w, outs)
     return y, idx, w, h, lg
-
-
-def decode_stack(x0, layers, steps: int, d: int, f: int, k: int, eps: float = EPS):
-    """Batch-1 decode: per step, each layer computes x <- MoE_l(x) (residual
-    included); between steps the last layer's output is rescaled to unit RMS.
-    ``layers`` is a list of (norm_w, router_w, bias, blob_of).  Returns the list
-    of per-step outputs of the last layer and the routing of every layer."""
-    x = np.atleast_2d(np.asarray(x0, dtype=np.float64))
-    outs, routes = [], []
-    for _ in range(steps):
-        step_routes = []
-        for (nw, rw, bias, blob_of) in layers:
-            x, idx, w, _, _ = moe_layer(x, nw, rw, bias, blob_of, d, f, k, eps)
-            step_routes.append(idx.copy())
-        outs.append(x.copy())
-        routes.append(step_routes)
-        x = rms_rescale(x, eps)
-    return outs, routes
 
 
 # --------------------------------------------------------------------------------------
