@@ -284,7 +284,19 @@ moe_status moe_cache_destroy(moe_cache* c);
  * the layer's new slot table.  hit_mask_dev (device uint8 [k]) receives 1 for
  * hits and 0 for misses through a copy enqueued on `compute`; hit_mask_host
  * (may be NULL) gets the same on return.  Entries of hit experts keep their
- * slot, so kernels for hits may run on `compute` before moe_cache_wait. */
+ * slot, so kernels for hits may run on `compute` before moe_cache_wait.
+ * `step` is the stamp the rule records (callers pass a step counter; it
+ * orders LRU choices), and the hit mask is how the caller runs cache hits
+ * first and misses after moe_cache_wait ("Optimizing a 14.3 GB model for an
+ * 8 GB machine", section "MoE needed parallel work, reuse, and coarse
+ * overlap": cached hits first, then the experts that needed a read).
+ * Failure: a HIP error (MOE_ERR_HIP) before the step's copies are enqueued
+ * leaves the cache exactly as it was.  A failure after some were enqueued
+ * leaves the rest as it was but empties the slots those copies target (they
+ * may be overwritten): on the host at once, in the device table at the
+ * layer's next call.  Once the step's copies, table copy and event are
+ * enqueued the step is committed; if only the hit-mask copy then fails, the
+ * call returns MOE_ERR_HIP with the step committed. */
 moe_status moe_slot_stage(moe_cache* c, int32_t layer, int32_t step, const int32_t* sel_host,
                           hipStream_t side, hipStream_t compute,
                           uint8_t* hit_mask_dev, uint8_t* hit_mask_host,

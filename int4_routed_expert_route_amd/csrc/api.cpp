@@ -225,6 +225,8 @@ moe_status moe_expert_q4_gateup(const float* h, const int32_t* topk_idx, const i
   if (prec == MOE_PREC_BF16_MFMA || prec == MOE_PREC_F16_MFMA || prec == MOE_PREC_F16_MFMA_DIRECT) {
     if (!grouped)
       return fail(MOE_ERR_UNSUPPORTED, "%s: the MFMA path needs offsets and sorted_pair (moe_permute)", fn);
+    if (!moe::mfma_supported(dims.d, dims.f))
+      return fail(MOE_ERR_UNSUPPORTED, "%s: f=%d beyond the MFMA path's 8192 (128 groups of 64)", fn, dims.f);
     if ((int64_t)T * dims.top_k > kMaxMfmaPairs)
       return fail(MOE_ERR_ARG, "%s: T*k must be <= %d on the MFMA path", fn, kMaxMfmaPairs);
     if (!mfma_fits_32bit(T, dims, slot_stride))
@@ -276,6 +278,8 @@ moe_status moe_expert_q4_down_combine(const void* act, const int32_t* topk_idx, 
   if (prec == MOE_PREC_BF16_MFMA || prec == MOE_PREC_F16_MFMA || prec == MOE_PREC_F16_MFMA_DIRECT) {
     if (!grouped)
       return fail(MOE_ERR_UNSUPPORTED, "%s: the MFMA path needs offsets and sorted_pair (moe_permute)", fn);
+    if (!moe::mfma_supported(dims.d, dims.f))
+      return fail(MOE_ERR_UNSUPPORTED, "%s: f=%d beyond the MFMA path's 8192 (128 groups of 64)", fn, dims.f);
     if ((int64_t)T * dims.top_k > kMaxMfmaPairs)
       return fail(MOE_ERR_ARG, "%s: T*k must be <= %d on the MFMA path", fn, kMaxMfmaPairs);
     if (!mfma_fits_32bit(T, dims, slot_stride))

@@ -72,6 +72,7 @@ hipError_t launch_combine(const float* pair_out, const float* topk_w, const floa
 // ---- grouped int4 GEMM on MFMA for batched prefill (q4_grouped_mfma.hip).
 // act for these calls is block-scaled: 16-bit values [T*k][f], then int8
 // exponents [T*k][f/64]; element (p, c) = value * 2^exp[p][c/64].
+bool mfma_supported(int d, int f);
 size_t mfma_act_bytes(int T, int f, int k);
 size_t mfma_workspace_bytes(int call, int T, int d, int f, int E, int k);
 hipError_t launch_gateup_mfma(bool f16, bool direct, const float* h, const int32_t* offsets, const int32_t* sorted_pair,

@@ -928,6 +928,10 @@ static int gemm_nt(bool gateup, int d, int f) { return gateup ? (f + BN / 2 - 1)
 // Upper bound of work items: sum over experts of ceil(c_e / BM) <= T*k/BM + E.
 static int max_items(int T, int k, int E, int NT) { return ((T * k + BM - 1) / BM + E) * NT; }
 
+// The down GEMM keeps one tile exponent per K group in LDS (s_gexp), so its K
+// (= f) spans at most kMaxSteps groups; gate/up has no such bound.
+bool mfma_supported(int d, int f) { return d % BK == 0 && f % BK == 0 && f / BK <= kMaxSteps; }
+
 size_t mfma_act_bytes(int T, int f, int k) { return (size_t)T * k * f * 2 + (size_t)T * k * (f / kGroup); }
 
 // Workspace: arrival counters, then h in 16-bit slot order (gate/up) or the

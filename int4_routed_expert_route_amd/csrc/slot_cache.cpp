@@ -36,6 +36,7 @@ struct moe_cache {
   std::vector<hipEvent_t> staged;    // per layer: last staging on the side stream
   std::vector<hipEvent_t> masked;    // per layer: last hit-mask copy on the compute stream
   std::vector<char> staged_used, masked_used;
+  std::vector<char> table_stale;     // per layer: a failed step left the device table behind the host state
   hipEvent_t compute_mark = nullptr;
   moe_stage_stats stats{0, 0, 0};
   // eviction policy (moe_cache_set_policy) and, for LFU, the use counts
@@ -80,14 +81,15 @@ moe_status hipcheck(hipError_t e, const char* what) {
   return cfail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-void rebuild_table(moe_cache* c, int layer) {
+// The pinned source of a layer's slot-table copy, from a slot -> expert array.
+void fill_table(moe_cache* c, int layer, const int32_t* se) {
   int32_t* t = c->table_host + (int64_t)layer * c->E;
   for (int e = 0; e < c->E; ++e) t[e] = -1;
-  for (int s = 0; s < c->S; ++s) {
-    const int e = c->slot_expert[(int64_t)layer * c->S + s];
-    if (e >= 0) t[e] = s;
-  }
+  for (int s = 0; s < c->S; ++s)
+    if (se[s] >= 0) t[se[s]] = s;
 }
+
+void rebuild_table(moe_cache* c, int layer) { fill_table(c, layer, c->slot_expert.data() + (int64_t)layer * c->S); }
 
 // Device mode: bring the host mirror up to date (waits for the device).
 moe_status pull_device_state(const moe_cache* cc) {
@@ -136,6 +138,7 @@ moe_status moe_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_slots
   c->staged.assign(n_layers, nullptr);
   c->masked.assign(n_layers, nullptr);
   c->staged_used.assign(n_layers, 0);
+  c->table_stale.assign(n_layers, 0);
   c->masked_used.assign(n_layers, 0);
   c->count.assign((size_t)n_layers * n_experts, 0);
   c->steps_seen.assign(n_layers, 0);
@@ -207,28 +210,43 @@ moe_status moe_slot_stage(moe_cache* c, int32_t layer, int32_t step, const int32
     return st;
   if (c->masked_used[layer] && (st = hipcheck(hipEventSynchronize(c->masked[layer]), "hipEventSynchronize")))
     return st;
+  // An earlier step of this layer failed after some of its copies were
+  // enqueued: its victim slots were emptied on the host; the device table
+  // follows before anything else is staged.
+  if (c->table_stale[layer]) {
+    rebuild_table(c, layer);
+    if ((st = hipcheck(hipMemcpy(c->tables_dev + (int64_t)layer * c->E, c->table_host + (int64_t)layer * c->E,
+                                 sizeof(int32_t) * c->E, hipMemcpyHostToDevice), "hipMemcpy")))
+      return st;
+    c->table_stale[layer] = 0;
+  }
 
-  int32_t* se = c->slot_expert.data() + (int64_t)layer * c->S;
-  int64_t* sp = c->stamp.data() + (int64_t)layer * c->S;
+  // The step is worked out on copies of the layer's state and committed only
+  // once every copy of it is enqueued; a failure before that leaves the state
+  // as it was.
+  std::vector<int32_t> se(c->slot_expert.begin() + (int64_t)layer * c->S,
+                          c->slot_expert.begin() + (int64_t)(layer + 1) * c->S);
+  std::vector<int64_t> sp(c->stamp.begin() + (int64_t)layer * c->S, c->stamp.begin() + (int64_t)(layer + 1) * c->S);
+  std::vector<int64_t> cnt(c->count.begin() + (int64_t)layer * c->E, c->count.begin() + (int64_t)(layer + 1) * c->E);
+  std::vector<int32_t> ring;
+  int32_t* ring_at = nullptr;
   // expert -> slot for this layer
   std::vector<int> where(c->E, -1);
   for (int s = 0; s < c->S; ++s)
     if (se[s] >= 0) where[se[s]] = s;
   // use counts: this step's selection enters, and with a window the step
   // that falls out of it leaves
-  int64_t* cnt = c->count.data() + (int64_t)layer * c->E;
   if (c->policy == MOE_CACHE_LFU_WINDOW) {
-    int32_t* ring = c->recent.data() + ((int64_t)layer * c->window + c->steps_seen[layer] % c->window) * c->k;
+    ring_at = c->recent.data() + ((int64_t)layer * c->window + c->steps_seen[layer] % c->window) * c->k;
+    ring.assign(ring_at, ring_at + c->k);
     for (int j = 0; j < c->k; ++j) {
       if (ring[j] >= 0) --cnt[ring[j]];
       ring[j] = sel_host[j];
     }
   }
   for (int j = 0; j < c->k; ++j) ++cnt[sel_host[j]];
-  ++c->steps_seen[layer];
-  c->staged_any = true;
   // phase 1: stamp the hits
-  uint8_t* mask = c->mask_host + (int64_t)layer * c->k;
+  std::vector<uint8_t> mask(c->k);
   std::vector<int> misses;
   for (int j = 0; j < c->k; ++j) {
     const int e = sel_host[j];
@@ -265,10 +283,26 @@ moe_status moe_slot_stage(moe_cache* c, int32_t layer, int32_t step, const int32
     sp[victim] = step;
     installs.emplace_back(e, victim);
   }
+
+  bool copies_enqueued = false;
+  auto failed = [&](moe_status err) {
+    // Copies already enqueued may overwrite their victim slots: those slots no
+    // longer hold the expert the old state names, so they become empty, on
+    // the host now and on the device at the layer's next step.
+    if (copies_enqueued) {
+      for (const auto& in : installs) {
+        c->slot_expert[(int64_t)layer * c->S + in.second] = -1;
+        c->stamp[(int64_t)layer * c->S + in.second] = -1;
+      }
+      c->table_stale[layer] = 1;
+    }
+    rebuild_table(c, layer);
+    return err;
+  };
   // enqueue: side waits for everything already on compute, then copies
   if ((st = hipcheck(hipEventRecord(c->compute_mark, compute), "hipEventRecord")) ||
       (st = hipcheck(hipStreamWaitEvent(side, c->compute_mark, 0), "hipStreamWaitEvent")))
-    return st;
+    return failed(st);
   if (!installs.empty()) {
     if (c->staging == MOE_STAGE_KERNEL) {
       // one launch per kMaxStageCopies misses; the GPU reads the pool itself
@@ -280,56 +314,68 @@ moe_status moe_slot_stage(moe_cache* c, int32_t layer, int32_t step, const int32
           a.src[i] = c->pool_dev + ((int64_t)layer * c->E + installs[i0 + i].first) * c->blob;
           a.dst[i] = c->arena + ((int64_t)layer * c->S + installs[i0 + i].second) * c->stride;
         }
-        if ((st = hipcheck(moe::launch_stage_copy(a, side), "stage copy kernel"))) return st;
+        copies_enqueued = true;
+        if ((st = hipcheck(moe::launch_stage_copy(a, side), "stage copy kernel"))) return failed(st);
       }
     } else if (c->staging == MOE_STAGE_COPY_SPLIT) {
       // each blob in as many pieces as helper streams, one piece per stream
       // (each stream can drive its own copy engine); `side` joins them
       const int n = (int)c->helpers.size();
       const int64_t piece = ((c->blob + n - 1) / n + 4095) / 4096 * 4096;
-      if ((st = hipcheck(hipEventRecord(c->fork, side), "hipEventRecord"))) return st;
+      if ((st = hipcheck(hipEventRecord(c->fork, side), "hipEventRecord"))) return failed(st);
       for (int i = 0; i < n; ++i) {
-        if ((st = hipcheck(hipStreamWaitEvent(c->helpers[i], c->fork, 0), "hipStreamWaitEvent"))) return st;
+        if ((st = hipcheck(hipStreamWaitEvent(c->helpers[i], c->fork, 0), "hipStreamWaitEvent"))) return failed(st);
         for (const auto& in : installs) {
           const int64_t o = (int64_t)i * piece, len = std::min(piece, c->blob - o);
           if (len <= 0) continue;
           const uint8_t* src = c->pool + ((int64_t)layer * c->E + in.first) * c->blob + o;
           uint8_t* dst = c->arena + ((int64_t)layer * c->S + in.second) * c->stride + o;
+          copies_enqueued = true;
           if ((st = hipcheck(hipMemcpyAsync(dst, src, len, hipMemcpyHostToDevice, c->helpers[i]), "hipMemcpyAsync")))
-            return st;
+            return failed(st);
         }
         if ((st = hipcheck(hipEventRecord(c->joins[i], c->helpers[i]), "hipEventRecord")) ||
             (st = hipcheck(hipStreamWaitEvent(side, c->joins[i], 0), "hipStreamWaitEvent")))
-          return st;
+          return failed(st);
       }
     } else {
       for (const auto& in : installs) {
         const uint8_t* src = c->pool + ((int64_t)layer * c->E + in.first) * c->blob;
         uint8_t* dst = c->arena + ((int64_t)layer * c->S + in.second) * c->stride;
+        copies_enqueued = true;
         if ((st = hipcheck(hipMemcpyAsync(dst, src, c->blob, hipMemcpyHostToDevice, side), "hipMemcpyAsync")))
-          return st;
+          return failed(st);
       }
     }
-  }
-  if (!installs.empty()) {
-    rebuild_table(c, layer);
+    fill_table(c, layer, se.data());
     if ((st = hipcheck(hipMemcpyAsync(c->tables_dev + (int64_t)layer * c->E,
                                       c->table_host + (int64_t)layer * c->E, sizeof(int32_t) * c->E,
                                       hipMemcpyHostToDevice, side), "hipMemcpyAsync")))
-      return st;
+      return failed(st);
   }
-  if ((st = hipcheck(hipEventRecord(c->staged[layer], side), "hipEventRecord"))) return st;
+  if ((st = hipcheck(hipEventRecord(c->staged[layer], side), "hipEventRecord"))) return failed(st);
   c->staged_used[layer] = 1;
-  if ((st = hipcheck(hipMemcpyAsync(hit_mask_dev, mask, c->k, hipMemcpyHostToDevice, compute),
-                     "hipMemcpyAsync")) ||
-      (st = hipcheck(hipEventRecord(c->masked[layer], compute), "hipEventRecord")))
-    return st;
-  c->masked_used[layer] = 1;
-  if (hit_mask_host) std::memcpy(hit_mask_host, mask, c->k);
+  // commit: the copies, the table and the event are all enqueued
+  std::copy(se.begin(), se.end(), c->slot_expert.begin() + (int64_t)layer * c->S);
+  std::copy(sp.begin(), sp.end(), c->stamp.begin() + (int64_t)layer * c->S);
+  std::copy(cnt.begin(), cnt.end(), c->count.begin() + (int64_t)layer * c->E);
+  if (ring_at) std::copy(ring.begin(), ring.end(), ring_at);
+  ++c->steps_seen[layer];
+  c->staged_any = true;
   c->stats.hits += c->k - (int64_t)misses.size();
   c->stats.misses += (int64_t)misses.size();
   c->stats.bytes_staged += (int64_t)misses.size() * c->blob;
   if (stats) *stats = c->stats;
+  // the hit mask follows on the compute stream; if it cannot be enqueued the
+  // staging above still stands (the state is committed) and the call fails
+  uint8_t* pinned_mask = c->mask_host + (int64_t)layer * c->k;
+  std::memcpy(pinned_mask, mask.data(), c->k);
+  if ((st = hipcheck(hipMemcpyAsync(hit_mask_dev, pinned_mask, c->k, hipMemcpyHostToDevice, compute),
+                     "hipMemcpyAsync")) ||
+      (st = hipcheck(hipEventRecord(c->masked[layer], compute), "hipEventRecord")))
+    return st;
+  c->masked_used[layer] = 1;
+  if (hit_mask_host) std::memcpy(hit_mask_host, mask.data(), c->k);
   return MOE_OK;
 }
 

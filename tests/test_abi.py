@@ -96,6 +96,16 @@ def test_validation_before_any_hip_call(api):
     assert g(_p(A), _p(A), _p(A), 128, _p(A), stride, _p(A), None, None, 1, 1, dm, 0, _p(A), _p(A), wsg, None) == api.MOE_ERR_ARG
     # the bf16 MFMA path needs the permutation
     assert g(_p(A), _p(A), _p(A), 128, _p(A), stride, None, None, None, 0, 1, dm, 1, _p(A), _p(A), wsg, None) == api.MOE_ERR_UNSUPPORTED
+    # the MFMA path keeps one LDS entry per K group of the down GEMM: f past
+    # 128 groups of 64 is refused on the host for gate/up and down alike
+    big = api.dims(2816, 8256, 128, 8)
+    sbig = api.moe_expert_blob_bytes(big)
+    for prec in (api.MOE_PREC_BF16_MFMA, api.MOE_PREC_F16_MFMA, api.MOE_PREC_F16_MFMA_DIRECT):
+        assert g(_p(A), _p(A), _p(A), 128, _p(A), sbig, _p(A), _p(A), None, 0, 1, big, prec, _p(A), _p(A),
+                 1 << 30, None) == api.MOE_ERR_UNSUPPORTED
+        assert b"8192" in lib.moe_last_error()
+        assert lib.moe_expert_q4_down_combine(_p(A), _p(A), _p(A), _p(A), 128, _p(A), sbig, _p(A), _p(A), _p(A),
+                                              None, 1, big, prec, _p(A), _p(A), 1 << 30, None) == api.MOE_ERR_UNSUPPORTED
     dc = lib.moe_expert_q4_down_combine
     wsd = api.moe_workspace_size(api.MOE_CALL_DOWN_COMBINE, 1, dm)
     assert dc(_p(A), _p(A), None, _p(A), 128, _p(A), stride, None, None, None, None, 1, dm, 0, _p(A), _p(A), wsd, None) == api.MOE_ERR_ARG

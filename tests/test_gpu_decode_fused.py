@@ -169,8 +169,8 @@ def test_decode_layers_repeat_and_feedback(api):
 
 
 def test_decode_layers_steps_feed_back_in_place(api):
-    """Decode steps with x_next = x_io[0] (in place), against the oracle's
-    oracle teacher-forced per layer."""
+    """Decode steps with x_next = x_io[0] (in place), against the oracle
+    teacher-forced per layer."""
     d, f, E, k, L = 256, 128, 16, 4, 3
     st = Stack(api, d, f, E, k, L, seed=15)
     x_io = torch.zeros(L + 1, d, device="cuda")
