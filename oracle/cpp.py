@@ -106,7 +106,15 @@ def lib():
             fn.restype = res
             fn.argtypes = args
         _lib = L
+        L.oro_set_threads(default_threads())
     return _lib
+
+
+def default_threads() -> int:
+    """The CPUs this process may run on, capped by OMP_NUM_THREADS when set."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    return min(n, int(omp)) if omp.isdigit() and int(omp) > 0 else n
 
 
 def set_threads(n: int) -> None:
