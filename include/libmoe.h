@@ -166,6 +166,25 @@ moe_status moe_route(const float* x, const float* norm_w, float eps,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_route_noalloc — moe_route without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, results and
+ * errors as moe_route, bit for bit.  Its scratch is a static device array of
+ * 16 MiB per GPU (held until the process ends; looked up once per device on
+ * the first call there), so the call allocates nothing.  Calls needing more
+ * scratch than that (moe_workspace_size(MOE_CALL_ROUTE, T, ...) > 16 MiB,
+ * e.g. more than about 4000 tokens at E = 256) return MOE_ERR_CAPACITY.
+ * Every call on one GPU shares the array: calls that overlap in time on one
+ * GPU (on different streams, or from different threads) race and must not be
+ * issued.  A HIP failure to find the array gives MOE_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+moe_status moe_route_noalloc(const float* x, const float* norm_w, float eps,
+                             const float* router_w, const float* router_bias,
+                             int32_t T, moe_dims dims,
+                             float* h_out, int32_t* topk_idx, float* topk_w,
+                             hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_permute — group the T*k (token, rank) pairs by expert so that all tokens
  * routed to one expert run against one read of its weights (the batched routed
  * MoE of "Optimizing a 14.3 GB model for an 8 GB machine", section "Splitting

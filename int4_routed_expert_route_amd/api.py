@@ -54,6 +54,7 @@ _SIGNATURES = {
     "moe_workspace_size": (_SZ, [ctypes.c_int, _I32, moe_dims, ctypes.c_int]),
     "moe_act_bytes": (_SZ, [_I32, moe_dims, ctypes.c_int]),
     "moe_route": (ctypes.c_int, [_P, _P, _F, _P, _P, _I32, moe_dims, _P, _P, _P, _P, _SZ, _P]),
+    "moe_route_noalloc": (ctypes.c_int, [_P, _P, _F, _P, _P, _I32, moe_dims, _P, _P, _P, _P]),
     "moe_permute": (ctypes.c_int, [_P, _I32, moe_dims, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_expert_q4_gateup": (ctypes.c_int, [_P, _P, _P, _I32, _P, _I64, _P, _P, _P, _I32, _I32, moe_dims,
                                             ctypes.c_int, _P, _P, _SZ, _P]),
@@ -166,6 +167,12 @@ def moe_route(x, norm_w, eps, router_w, router_bias, T, dm, h_out, topk_idx, top
                            _dev(router_bias, "router_bias"), int(T), dm, _dev(h_out, "h_out"),
                            _dev(topk_idx, "topk_idx"), _dev(topk_w, "topk_w"), _dev(ws, "ws"),
                            _nbytes(ws), _stream(stream)))
+
+
+def moe_route_noalloc(x, norm_w, eps, router_w, router_bias, T, dm, h_out, topk_idx, topk_w, stream=None):
+    _check(lib().moe_route_noalloc(_dev(x, "x"), _dev(norm_w, "norm_w"), float(eps), _dev(router_w, "router_w"),
+                                   _dev(router_bias, "router_bias"), int(T), dm, _dev(h_out, "h_out"),
+                                   _dev(topk_idx, "topk_idx"), _dev(topk_w, "topk_w"), _stream(stream)))
 
 
 def moe_permute(topk_idx, T, dm, counts, offsets, sorted_pair, pair_pos, ws=None, stream=None):

@@ -173,6 +173,28 @@ moe_status moe_route(const float* x, const float* norm_w, float eps, const float
   return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
 }
 
+moe_status moe_route_noalloc(const float* x, const float* norm_w, float eps, const float* router_w,
+                             const float* router_bias, int32_t T, moe_dims dims, float* h_out,
+                             int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+  const char* fn = "moe_route_noalloc";
+  if (moe_status s = check_dims(dims)) return s;
+  if (T < 1) return fail(MOE_ERR_ARG, "%s: T=%d", fn, T);
+  CHECK_PTR(x); CHECK_PTR(router_w); CHECK_PTR(h_out); CHECK_PTR(topk_idx); CHECK_PTR(topk_w);
+  CHECK_ALIGN(x); CHECK_ALIGN(norm_w); CHECK_ALIGN(router_w); CHECK_ALIGN(router_bias);
+  CHECK_ALIGN(h_out); CHECK_ALIGN(topk_idx); CHECK_ALIGN(topk_w);
+  if (!(eps >= 0.0f)) return fail(MOE_ERR_ARG, "%s: eps must be >= 0", fn);
+  const size_t need = moe::route_workspace_bytes(T, dims.d, dims.n_experts);
+  if (need > moe::kRouteScratchBytes)
+    return fail(MOE_ERR_CAPACITY, "%s: T=%d E=%d needs %zu bytes of scratch; this entry point holds %zu per device",
+                fn, T, dims.n_experts, need, moe::kRouteScratchBytes);
+  void* scratch = nullptr;
+  hipError_t e = moe::route_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  e = moe::launch_route(x, norm_w, eps, router_w, router_bias, T, dims.d, dims.n_experts, dims.top_k, h_out,
+                        topk_idx, topk_w, scratch, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
+}
+
 moe_status moe_permute(const int32_t* topk_idx, int32_t T, moe_dims dims, int32_t* counts,
                        int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, void* ws,
                        size_t ws_bytes, hipStream_t stream) {

@@ -13,6 +13,10 @@ bool take_profile_events(int call, hipEvent_t* start, hipEvent_t* stop);
 
 // ---- routing (route.hip)
 size_t route_workspace_bytes(int T, int d, int E);
+// moe_route_noalloc: a static device array per GPU instead of a caller's workspace
+constexpr size_t kRouteScratchBytes = (size_t)16 << 20;
+constexpr int kMaxScratchDevices = 64;
+hipError_t route_scratch(void** out);
 hipError_t launch_route(const float* x, const float* norm_w, float eps, const float* router_w,
                         const float* router_bias, int T, int d, int E, int k, float* h_out,
                         int32_t* topk_idx, float* topk_w, void* ws, hipStream_t s);

@@ -7,6 +7,8 @@
 // which equals the softmax over the chosen logits alone.
 #include <hip/hip_ext.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -476,6 +478,41 @@ hipError_t launch_route(const float* x, const float* norm_w, float eps, const fl
   hipLaunchKernelGGL(k_topk, dim3(T), dim3(kWave), 0, s, logits, sp.slices, x, norm_w, eps, d, router_bias,
                      T, E, k, h_out, topk_idx, topk_w);
   return hipGetLastError();
+}
+
+}  // namespace moe
+
+// Scratch of moe_route_noalloc, for callers that cannot allocate: the route
+// kernels' workspace (the fused small path's arrival counter in the first 256
+// bytes, then the logits or the split-K partial logits).  One copy per GPU the
+// library runs on, held until the process ends.  It is zero when the module
+// loads and every launch of the small path leaves its counter at zero again
+// (the split path uses no counter), so no call has to clear it.  In host code
+// `scratch` only names the symbol: kernels get the device address from
+// route_scratch().
+static __device__ __align__(256) uint8_t scratch[moe::kRouteScratchBytes];
+
+namespace moe {
+
+// The device address of `scratch` on the current device, looked up with
+// hipGetSymbolAddress the first time a device asks and kept per device.
+hipError_t route_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* ptr[kMaxScratchDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
 }
 
 __global__ __launch_bounds__(256) void k_rms_rescale(const float* __restrict__ x, int T, int d,

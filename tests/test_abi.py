@@ -83,6 +83,13 @@ def test_validation_before_any_hip_call(api):
     assert lib.moe_route(_p(A), None, 1e-6, _p(A), None, 0, dm, _p(A), _p(A), _p(A), _p(A), ws, None) == api.MOE_ERR_ARG
     assert lib.moe_route(_p(A), None, 1e-6, _p(A), None, 1, api.dims(2816, 700, 128, 8), _p(A), _p(A), _p(A), _p(A), ws, None) == api.MOE_ERR_ARG
     assert lib.moe_route(_p(A), None, -1.0, _p(A), None, 1, dm, _p(A), _p(A), _p(A), _p(A), ws, None) == api.MOE_ERR_ARG
+    # the no-alloc router refuses sizes beyond its static scratch, before any HIP call
+    nr = lib.moe_route_noalloc
+    assert nr(_p(A), None, 1e-6, _p(A), None, 1 << 20, api.dims(2816, 704, 256, 8), _p(A), _p(A), _p(A),
+              None) == api.MOE_ERR_CAPACITY
+    assert b"16777216" in lib.moe_last_error()
+    assert nr(None, None, 1e-6, _p(A), None, 1, dm, _p(A), _p(A), _p(A), None) == api.MOE_ERR_ARG
+    assert nr(_p(A + 4), None, 1e-6, _p(A), None, 1, dm, _p(A), _p(A), _p(A), None) == api.MOE_ERR_ALIGN
     # permute limits
     assert lib.moe_permute(_p(A), 8193, dm, _p(A), _p(A), _p(A), _p(A), None, 0, None) == api.MOE_ERR_ARG
     # gate/up: slot stride, arena alignment, mask with grouping, offsets without sorted_pair
