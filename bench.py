@@ -393,7 +393,7 @@ def run_decode(args, api, torch):
 
 class BatchStack:
     """T tokens per step through the 30 layers, experts grouped by moe_permute.
-    prec FP32: grouped dequant-GEMV (batched decode); F16/BF16 MFMA: grouped
+    prec FP32: grouped dequant-GEMV (batched decode); F16 MFMA: grouped
     GEMM (prefill).  decode=True feeds the last layer's output back (unit-RMS
     rescale) as the next step's input; otherwise every step re-reads the same
     input tokens."""
@@ -460,7 +460,7 @@ def distinct_experts(torch, stack):
 
 def run_batched(args, api, torch):
     T = args.tokens or 32
-    prec = {"fp32": api.MOE_PREC_FP32, "f16": api.MOE_PREC_F16_MFMA, "bf16": api.MOE_PREC_BF16_MFMA}[args.batched_prec]
+    prec = {"fp32": api.MOE_PREC_FP32, "f16": api.MOE_PREC_F16_MFMA}[args.batched_prec]
     stack = BatchStack(api, torch, args.seed, T, prec, decode=True)
     graph = None if args.no_graph else graph_of(torch, stack.step)
     run = (lambda n: [stack.step() for _ in range(n)]) if graph is None else \
@@ -519,7 +519,7 @@ def run_batched(args, api, torch):
 
 def run_prefill(args, api, torch):
     T = args.tokens or 2048
-    prec = {"bf16": api.MOE_PREC_BF16_MFMA, "f16": api.MOE_PREC_F16_MFMA,
+    prec = {"f16": api.MOE_PREC_F16_MFMA,
             "f16direct": api.MOE_PREC_F16_MFMA_DIRECT}[args.operands]
     stack = BatchStack(api, torch, args.seed, T, prec, decode=False)
     graph = None if args.no_graph else graph_of(torch, stack.step)
@@ -547,7 +547,7 @@ def run_prefill(args, api, torch):
     dn_tflops = flop_dn / (dn_us * 1e-6) / 1e12
     log(f"kernels (eager, mean us): route {rt_us:.1f}  permute {pm_us:.1f}  gate/up GEMM {gu_us:.1f} "
         f"({achieved:.0f} TFLOP/s)  down GEMM {dn_us:.1f} ({dn_tflops:.0f} TFLOP/s)")
-    out = base_record(tok_s, args.steps, args.warmup, ms, "bf16" if args.operands == "bf16" else "fp16",
+    out = base_record(tok_s, args.steps, args.warmup, ms, "fp16",
                       f"prefill, {T} tokens x 30 routed MoE layers x 128 experts (d=2816, f=704, top-8, int4 "
                       "groups of 64), Zipf(1.1) routing, expert-grouped int4 GEMM on MFMA "
                       f"({args.operands} operands, fp32 accumulate)",
@@ -811,10 +811,10 @@ def main():
     ap.add_argument("--tokens", type=int, default=0, help="batched / prefill: tokens per step (32 / 2048)")
     ap.add_argument("--decode-path", choices=["fused", "calls"], default="fused",
                     help="decode: one moe_decode_layers launch per token, or the three calls per layer")
-    ap.add_argument("--operands", choices=["f16", "bf16", "f16direct"], default="f16",
+    ap.add_argument("--operands", choices=["f16", "f16direct"], default="f16",
                     help="prefill: MFMA operand type (f16direct: fp16 with int4 weights loaded straight into "
                          "registers, the ablation of the staged tile)")
-    ap.add_argument("--batched-prec", choices=["fp32", "f16", "bf16"], default="f16",
+    ap.add_argument("--batched-prec", choices=["fp32", "f16"], default="f16",
                     help="batched: fp32 dequant-GEMV or grouped GEMM on MFMA")
     ap.add_argument("--slots", type=int, default=64, help="cache: HBM slots per layer")
     ap.add_argument("--policy", choices=["lru", "lfu", "lfu-window"], default="lru", help="cache: eviction policy")

@@ -92,8 +92,10 @@ typedef struct moe_dims {
 
 typedef enum moe_precision {
   MOE_PREC_FP32 = 0,      /* int4 weights, activations kept to ~fp32 accuracy, fp32 accumulate (decode) */
-  MOE_PREC_BF16_MFMA = 1, /* grouped GEMM: int4 -> bf16 weights, bf16 activations, bf16 MFMA, fp32
-                             accumulate (batched prefill) */
+  MOE_PREC_BF16_MFMA = 1, /* refused (MOE_ERR_UNSUPPORTED): bf16 operands (8-bit significand) on
+                             weights whose per-group means are far from zero lose 1-6% per output
+                             row to the cancellation of 2816-term sums, beyond the 1e-2 tolerance;
+                             the value is kept so that the codes stay stable */
   MOE_PREC_F16_MFMA = 2,  /* grouped GEMM: int4 -> fp16 weights, fp16 activations, fp16 MFMA, fp32
                              accumulate: the same MFMA rate as bf16 with 3 more significand bits;
                              intermediate values are block-scaled, so fp16's range does not bind */
@@ -130,7 +132,7 @@ size_t moe_workspace_size(moe_call call, int32_t T, moe_dims dims, moe_precision
 /* Bytes of the act buffer that moe_expert_q4_gateup writes and
  * moe_expert_q4_down_combine reads, for T tokens at precision prec:
  *   MOE_PREC_FP32       fp32 [T*k][f].
- *   MOE_PREC_*_MFMA     block-scaled: 16-bit values (bf16 or fp16) [T*k][f],
+ *   MOE_PREC_F16_MFMA*  block-scaled: fp16 values [T*k][f],
  *                       then int8 exponents [T*k][f/64] at byte offset
  *                       T*k*f*2.  Inside each block of 8 columns the values
  *                       are stored in the order 0,4,1,5,2,6,3,7 (the order the
@@ -138,8 +140,7 @@ size_t moe_workspace_size(moe_call call, int32_t T, moe_dims dims, moe_precision
  *                       value[p][8b + pos(j)] * 2^exp[p][(8b + j) / 64] with
  *                       pos(j) = 2*(j%4) + j/4.  fp16 exponents are shared by
  *                       the pairs an expert processes together and put the
- *                       group's largest magnitude in [2^14, 2^15); bf16
- *                       exponents are 0.
+ *                       group's largest magnitude in [2^14, 2^15).
  * SIZE_MAX for invalid dims. */
 size_t moe_act_bytes(int32_t T, moe_dims dims, moe_precision prec);
 
@@ -225,7 +226,7 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t T, moe_dims dims,
  *                  parallel work, reuse, and coarse overlap").  Only with
  *                  offsets == NULL.
  *   prec           MOE_PREC_FP32: act is fp32 [T*k][f];
- *                  MOE_PREC_BF16_MFMA / MOE_PREC_F16_MFMA: grouped GEMM on MFMA
+ *                  MOE_PREC_F16_MFMA(_DIRECT): grouped GEMM on MFMA
  *                  (needs offsets, T*k <= 2^22); act is block-scaled 16-bit
  *                  (layout and size: moe_act_bytes).  With few tokens, experts
  *                  of at most 32 routed rows are split along K over several

@@ -133,9 +133,9 @@ size_t moe_act_bytes(int32_t T, moe_dims dims, moe_precision prec) {
   if (T < 1 || check_dims(dims) != MOE_OK) return SIZE_MAX;
   switch (prec) {
     case MOE_PREC_FP32: return (size_t)T * dims.top_k * dims.f * 4;
-    case MOE_PREC_BF16_MFMA:
     case MOE_PREC_F16_MFMA:
     case MOE_PREC_F16_MFMA_DIRECT: return moe::mfma_act_bytes(T, dims.f, dims.top_k);
+    case MOE_PREC_BF16_MFMA: return SIZE_MAX;  // refused: see moe_precision
   }
   return SIZE_MAX;
 }
@@ -147,7 +147,8 @@ size_t moe_workspace_size(moe_call call, int32_t T, moe_dims dims, moe_precision
     case MOE_CALL_PERMUTE: return 0;
     case MOE_CALL_GATEUP:
     case MOE_CALL_DOWN_COMBINE:
-      if (prec == MOE_PREC_BF16_MFMA || prec == MOE_PREC_F16_MFMA || prec == MOE_PREC_F16_MFMA_DIRECT)
+      if (prec == MOE_PREC_BF16_MFMA) return SIZE_MAX;  // refused: see moe_precision
+      if (prec == MOE_PREC_F16_MFMA || prec == MOE_PREC_F16_MFMA_DIRECT)
         return moe::mfma_workspace_bytes((int)call, T, dims.d, dims.f, dims.n_experts, dims.top_k);
       return moe::gemv_workspace_bytes((int)call, T, dims.d, dims.top_k, true);
     case MOE_CALL_DECODE_LAYERS:  // T = number of layers
@@ -244,7 +245,11 @@ moe_status moe_expert_q4_gateup(const float* h, const int32_t* topk_idx, const i
     hipError_t e = moe::launch_gateup_fp32(a, stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
   }
-  if (prec == MOE_PREC_BF16_MFMA || prec == MOE_PREC_F16_MFMA || prec == MOE_PREC_F16_MFMA_DIRECT) {
+  if (prec == MOE_PREC_BF16_MFMA)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "%s: bf16 operands (8-bit significand) miss the 1e-2 output tolerance on these weights; "
+                "MOE_PREC_F16_MFMA runs at the same MFMA rate with 3 more bits", fn);
+  if (prec == MOE_PREC_F16_MFMA || prec == MOE_PREC_F16_MFMA_DIRECT) {
     if (!grouped)
       return fail(MOE_ERR_UNSUPPORTED, "%s: the MFMA path needs offsets and sorted_pair (moe_permute)", fn);
     if (!moe::mfma_supported(dims.d, dims.f))
@@ -256,7 +261,7 @@ moe_status moe_expert_q4_gateup(const float* h, const int32_t* topk_idx, const i
     const size_t need = moe::mfma_workspace_bytes(MOE_CALL_GATEUP, T, dims.d, dims.f, dims.n_experts, dims.top_k);
     if (!ws) return fail(MOE_ERR_ARG, "%s: ws is null", fn);
     if (ws_bytes < need) return fail(MOE_ERR_CAPACITY, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
-    hipError_t e = moe::launch_gateup_mfma(prec != MOE_PREC_BF16_MFMA, prec == MOE_PREC_F16_MFMA_DIRECT, h, offsets, sorted_pair, slot_of_expert,
+    hipError_t e = moe::launch_gateup_mfma(prec == MOE_PREC_F16_MFMA_DIRECT, h, offsets, sorted_pair, slot_of_expert,
                                            n_slots, arena, slot_stride, T, dims.d, dims.f, dims.n_experts,
                                            dims.top_k, L.gate_q, L.up_q, L.gate_sb, L.up_sb, act, ws, stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
@@ -297,7 +302,11 @@ moe_status moe_expert_q4_down_combine(const void* act, const int32_t* topk_idx, 
     hipError_t e = moe::launch_down_fp32(a, ws, stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
   }
-  if (prec == MOE_PREC_BF16_MFMA || prec == MOE_PREC_F16_MFMA || prec == MOE_PREC_F16_MFMA_DIRECT) {
+  if (prec == MOE_PREC_BF16_MFMA)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "%s: bf16 operands (8-bit significand) miss the 1e-2 output tolerance on these weights; "
+                "MOE_PREC_F16_MFMA runs at the same MFMA rate with 3 more bits", fn);
+  if (prec == MOE_PREC_F16_MFMA || prec == MOE_PREC_F16_MFMA_DIRECT) {
     if (!grouped)
       return fail(MOE_ERR_UNSUPPORTED, "%s: the MFMA path needs offsets and sorted_pair (moe_permute)", fn);
     if (!moe::mfma_supported(dims.d, dims.f))
@@ -310,7 +319,7 @@ moe_status moe_expert_q4_down_combine(const void* act, const int32_t* topk_idx, 
         moe::mfma_workspace_bytes(MOE_CALL_DOWN_COMBINE, T, dims.d, dims.f, dims.n_experts, dims.top_k);
     if (!ws) return fail(MOE_ERR_ARG, "%s: ws is null", fn);
     if (ws_bytes < need) return fail(MOE_ERR_CAPACITY, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
-    hipError_t e = moe::launch_down_mfma(prec != MOE_PREC_BF16_MFMA, prec == MOE_PREC_F16_MFMA_DIRECT, act, offsets, sorted_pair, slot_of_expert,
+    hipError_t e = moe::launch_down_mfma(prec == MOE_PREC_F16_MFMA_DIRECT, act, offsets, sorted_pair, slot_of_expert,
                                          n_slots, arena, slot_stride, T, dims.d, dims.f, dims.n_experts,
                                          dims.top_k, L.down_q, L.down_sb, topk_w, residual, y, ws, stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, fn);

@@ -79,11 +79,11 @@ hipError_t launch_combine(const float* pair_out, const float* topk_w, const floa
 bool mfma_supported(int d, int f);
 size_t mfma_act_bytes(int T, int f, int k);
 size_t mfma_workspace_bytes(int call, int T, int d, int f, int E, int k);
-hipError_t launch_gateup_mfma(bool f16, bool direct, const float* h, const int32_t* offsets, const int32_t* sorted_pair,
+hipError_t launch_gateup_mfma(bool direct, const float* h, const int32_t* offsets, const int32_t* sorted_pair,
                               const int32_t* slot_of_expert, int n_slots, const uint8_t* arena, int64_t slot_stride,
                               int T, int d, int f, int E, int k, int64_t off_q0, int64_t off_q1, int64_t off_sb0,
                               int64_t off_sb1, void* act_out, void* ws, hipStream_t s);
-hipError_t launch_down_mfma(bool f16, bool direct, const void* act_in, const int32_t* offsets, const int32_t* sorted_pair,
+hipError_t launch_down_mfma(bool direct, const void* act_in, const int32_t* offsets, const int32_t* sorted_pair,
                             const int32_t* slot_of_expert, int n_slots, const uint8_t* arena, int64_t slot_stride,
                             int T, int d, int f, int E, int k, int64_t off_q, int64_t off_sb, const float* topk_w,
                             const float* residual, float* y, void* ws, hipStream_t s);

@@ -9,13 +9,7 @@ import synth
 D, F, E, K = synth.D_MODEL, synth.D_FF, synth.N_EXPERTS, synth.TOP_K
 
 TOL_FP32 = 2e-3   # max |gpu - ref| / max |ref| per output row, fp32-accumulate path
-TOL_BF16 = 1e-2   # same, 16-bit-operand MFMA path (met with fp16 operands)
-# bf16 operands (8-bit significand, unit roundoff 2^-9) applied to weights whose
-# per-group mean is far from zero: sums over 2816 terms cancel ~50x, so operand
-# rounding alone measures 1.2-5.6% by the per-row metric on these inputs.  The
-# bf16 variant is held to this looser bound, which still fails on any indexing,
-# scale or bias mistake (those give O(1) errors).
-TOL_BF16_OPERANDS = 1e-1
+TOL_BF16 = 1e-2   # same, 16-bit-operand MFMA path (fp16 operands)
 
 
 def row_rel_err(gpu, ref) -> float:

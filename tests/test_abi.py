@@ -101,13 +101,17 @@ def test_validation_before_any_hip_call(api):
     assert g(_p(A), _p(A), _p(A), 0, _p(A), stride, None, None, None, 0, 1, dm, 0, _p(A), _p(A), wsg, None) == api.MOE_ERR_ARG
     assert g(_p(A), _p(A), _p(A), 128, _p(A), stride, _p(A), _p(A), _p(A), 1, 1, dm, 0, _p(A), _p(A), wsg, None) == api.MOE_ERR_UNSUPPORTED
     assert g(_p(A), _p(A), _p(A), 128, _p(A), stride, _p(A), None, None, 1, 1, dm, 0, _p(A), _p(A), wsg, None) == api.MOE_ERR_ARG
-    # the bf16 MFMA path needs the permutation
-    assert g(_p(A), _p(A), _p(A), 128, _p(A), stride, None, None, None, 0, 1, dm, 1, _p(A), _p(A), wsg, None) == api.MOE_ERR_UNSUPPORTED
+    # bf16 operands are refused whatever the other arguments; the MFMA path needs the permutation
+    assert g(_p(A), _p(A), _p(A), 128, _p(A), stride, _p(A), _p(A), None, 0, 1, dm, api.MOE_PREC_BF16_MFMA, _p(A),
+             _p(A), 1 << 30, None) == api.MOE_ERR_UNSUPPORTED
+    assert b"bf16" in lib.moe_last_error()
+    assert api.moe_workspace_size(api.MOE_CALL_GATEUP, 4, dm, api.MOE_PREC_BF16_MFMA) == (1 << 64) - 1
+    assert g(_p(A), _p(A), _p(A), 128, _p(A), stride, None, None, None, 0, 1, dm, 2, _p(A), _p(A), wsg, None) == api.MOE_ERR_UNSUPPORTED
     # the MFMA path keeps one LDS entry per K group of the down GEMM: f past
     # 128 groups of 64 is refused on the host for gate/up and down alike
     big = api.dims(2816, 8256, 128, 8)
     sbig = api.moe_expert_blob_bytes(big)
-    for prec in (api.MOE_PREC_BF16_MFMA, api.MOE_PREC_F16_MFMA, api.MOE_PREC_F16_MFMA_DIRECT):
+    for prec in (api.MOE_PREC_F16_MFMA, api.MOE_PREC_F16_MFMA_DIRECT):
         assert g(_p(A), _p(A), _p(A), 128, _p(A), sbig, _p(A), _p(A), None, 0, 1, big, prec, _p(A), _p(A),
                  1 << 30, None) == api.MOE_ERR_UNSUPPORTED
         assert b"8192" in lib.moe_last_error()

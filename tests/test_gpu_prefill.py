@@ -1,15 +1,14 @@
 """GPU parity of the batched (prefill) path: route -> permute -> grouped MFMA
 gate/up -> grouped MFMA down + rank-ordered combine, against the CPU oracle.
-The fp16-operand path is held to 1e-2 per output row; the bf16-operand path to
-the looser bound its 8-bit significand allows on these inputs."""
+The fp16-operand path (staged tiles, and direct loads) is held to 1e-2 per
+output row; bf16 operands are refused by the library."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as orc
 import synth
-from helpers import (D, E, F, K, TOL_BF16, TOL_BF16_OPERANDS, LayerData, check_topk, decode_scaled_act,
-                     row_rel_err)
+from helpers import D, E, F, K, TOL_BF16, LayerData, check_topk, decode_scaled_act, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -29,7 +28,6 @@ def _np(t):
 
 
 PRECS = {"f16": ("MOE_PREC_F16_MFMA", torch.float16, TOL_BF16),
-         "bf16": ("MOE_PREC_BF16_MFMA", torch.bfloat16, TOL_BF16_OPERANDS),
          "f16direct": ("MOE_PREC_F16_MFMA_DIRECT", torch.float16, TOL_BF16)}
 
 
@@ -75,7 +73,7 @@ class SmallLayer:
         return self.blobs[e]
 
 
-@pytest.mark.parametrize("prec", ["f16", "bf16", "f16direct"])
+@pytest.mark.parametrize("prec", ["f16", "f16direct"])
 @pytest.mark.parametrize("d,f,E_,k,T", [(256, 128, 16, 4, 40), (320, 192, 8, 2, 7), (2816, 704, 128, 8, 1),
                                         (2816, 704, 128, 8, 48), (384, 256, 4, 2, 300), (1088, 576, 16, 4, 40),
                                         (1600, 768, 16, 4, 40)])
@@ -109,7 +107,7 @@ def test_prefill_parity_small(api, d, f, E_, k, T, prec):
     assert e_y < tol
 
 
-@pytest.mark.parametrize("prec", ["f16", "bf16"])
+@pytest.mark.parametrize("prec", ["f16", "f16direct"])
 def test_prefill_large_activations(api, prec):
     """Inputs close to a constant vector make every gate/up sum coherent
     (g, u ~ 260 with these weights), so gelu(g) * u ~ 7e4 exceeds fp16's
@@ -132,7 +130,7 @@ def test_prefill_large_activations(api, prec):
     assert e_act < tol and e_y < tol
 
 
-@pytest.mark.parametrize("prec", ["f16", "bf16", "f16direct"])
+@pytest.mark.parametrize("prec", ["f16", "f16direct"])
 def test_prefill_exact_gateup(api, prec):
     """Unit scale, zero bias, h in {0,1} with 8 ones per token, gate nibbles in
     8..15: 16-bit operands are exact, fp32 sums of integers are exact and GELU
@@ -181,7 +179,7 @@ def test_prefill_exact_gateup(api, prec):
             assert np.array_equal(got[t * k + j], ref), (t, j)
 
 
-@pytest.mark.parametrize("prec", ["f16", "bf16", "f16direct"])
+@pytest.mark.parametrize("prec", ["f16", "f16direct"])
 def test_prefill_full_size_sampled(api, prec):
     """One layer at the full prefill shape (2048 tokens, Zipf routing), in the
     bench's launch configuration; the oracle recomputes a sample of tokens."""
