@@ -389,6 +389,90 @@ def run_decode(args, api, torch):
     return out
 
 
+def run_decode_timeline(args, api, torch):
+    """Per-stage timeline of the fused decode kernel (measurement build
+    libmoe_timeline.so): every workgroup's clock at the end of each stage of
+    each layer, over several eager launches after the warmup, summarised as
+    markdown into args.decode_timeline."""
+    import ctypes
+    lib = api.lib()
+    fn = lib.moe_debug_decode_timeline
+    fn.argtypes = [ctypes.c_void_p]
+    stack = DecodeStack(api, torch, args.seed, cold=args.control == "cold")
+    for i in range(args.warmup):
+        stack.fused_step(i % stack.period)
+    torch.cuda.synchronize()
+    G = K * F // 32  # workgroups of the launch (32 act columns each)
+    tl = np.zeros((64, 256, 12), dtype=np.uint64)
+    runs = []
+    for i in range(args.steps):
+        stack.fused_step((args.warmup + i) % stack.period)
+        torch.cuda.synchronize()
+        assert fn(tl.ctypes.data) == 0
+        runs.append(tl[:NL, :G].astype(np.int64).copy())
+    api.moe_decode_check(stack.ws_fused)
+    us = 0.01  # s_memrealtime ticks at 100 MHz
+    names = ["router partials, sums of squares, x arrived", "logits + top-k", "h staged, gate/up loads issued",
+             "gate/up weights landed + dot", "act store + act wait (down rows, router rows landing)",
+             "down dot", "combine + next partials written"]
+    stage = {n: [] for n in names}
+    stage_max = {n: [] for n in names}
+    hop_part, hop_act, skew7, skew4, layer_us, launch_us = [], [], [], [], [], []
+    xcd_end = np.zeros(8)
+    red_in, red_out, qs_in = [], [], []
+    nq = (E + 3) // 4
+    for r in runs:
+        launch_us.append((r[NL - 1, :, 7].max() - r[0, :, 0].min()) * us)
+        for l in range(1, NL):
+            t = r[l]
+            for s_i, n in enumerate(names):
+                d = (t[:, s_i + 1] - t[:, s_i]) * us
+                stage[n].append(np.median(d))
+                stage_max[n].append(d.max())
+            last7 = r[l - 1, :, 7].max()
+            hop_part.append(np.median((t[:, 1] - last7) * us))
+            hop_act.append(np.median((t[:, 5] - t[:, 4].max()) * us))
+            skew7.append((r[l - 1, :, 7].max() - r[l - 1, :, 7].min()) * us)
+            skew4.append((t[:, 4].max() - t[:, 4].min()) * us)
+            layer_us.append((r[l, :, 0].min() - r[l - 1, :, 0].min()) * us)
+            for x in range(8):
+                xcd_end[x] += (t[x::8, 7].mean() - t[:, 0].min()) * us
+            # the router's two steps: reducers' column in, their sums out, everyone's sums in
+            red_in.append(np.median((t[:nq, 8] - last7) * us))
+            red_out.append(np.median((t[:nq, 9] - last7) * us))
+            qs_in.append(np.median((t[:, 10] - t[:nq, 9].max()) * us))
+    xcd_end /= len(runs) * (NL - 1)
+    lines = [f"Per-layer stages of `k_decode_fused` ({G} workgroups, one per compute unit), "
+             f"{'cold-routing control' if stack.cold else 'Zipf(1.1) routing'}, {len(runs)} eager launches "
+             f"after {args.warmup} warmup launches; layers 1-{NL - 1} (layer 0 follows the prologue).",
+             "", f"Launch: {np.mean(launch_us):.1f} us (first layer start to last layer end); "
+             f"layer: {np.median(layer_us):.2f} us median.", "",
+             "| stage (ends when every thread of the workgroup is past it) | median over workgroups, us | "
+             "slowest workgroup, us |", "|---|---|---|"]
+    for n in names:
+        lines.append(f"| {n} | {np.mean(stage[n]):.2f} | {np.mean(stage_max[n]):.2f} |")
+    lines += ["", "| exchange | us |", "|---|---|",
+              f"| partials hop: a workgroup has every partial, after the last one was written (median) | "
+              f"{np.mean(hop_part):.2f} |",
+              f"| act hop + down rows: act values in, after the last act was written (median) | "
+              f"{np.mean(hop_act):.2f} |",
+              f"| spread of the partials writes over workgroups | {np.mean(skew7):.2f} |",
+              f"| spread of the gate/up dot ends over workgroups | {np.mean(skew4):.2f} |",
+              f"| router step 1: a reducer has its column of every row, after the last row was written (median) | "
+              f"{np.mean(red_in):.2f} |",
+              f"| router step 1: a reducer has written its sums, after the last row was written (median) | "
+              f"{np.mean(red_out):.2f} |",
+              f"| router step 2: a workgroup has the sums, after the last reducer wrote (median) | "
+              f"{np.mean(qs_in):.2f} |", "",
+              "Mean end of layer per XCD (workgroups g with g % 8 = x), us after the layer's first start: "
+              + ", ".join(f"{v:.2f}" for v in xcd_end)]
+    text = "\n".join(lines)
+    with open(args.decode_timeline, "w") as fh:
+        fh.write(text + "\n")
+    log("timeline:\n" + text)
+    return {"timeline": args.decode_timeline, "launch_us": round(float(np.mean(launch_us)), 2)}
+
+
 # ----------------------------------------------------------------------------- batched / prefill
 
 class BatchStack:
@@ -829,6 +913,11 @@ def main():
     ap.add_argument("--kernel-samples", type=int, default=62)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--decode-timeline", default="", metavar="OUT.md",
+                    help="decode: per-stage timeline of the fused kernel from the measurement build "
+                         "libmoe_timeline.so, summarised into OUT.md (no timing line)")
+    ap.add_argument("--library", default="", metavar="SO",
+                    help="load this build of libmoe instead of the in-tree one (compare builds on one box)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (for scaling HBM counters)")
     args = ap.parse_args()
@@ -847,9 +936,18 @@ def main():
 
     import torch
     import int4_routed_expert_route_amd.api as api
+    if args.decode_timeline:
+        from int4_routed_expert_route_amd import build as moe_build
+        api.LIB_PATH = moe_build.TIMELINE_LIB
+        args.workload = "decode"
+        args.warmup, args.steps = min(args.warmup, 16), min(args.steps, 8)
+    if args.library:
+        api.LIB_PATH = os.path.abspath(args.library)
     api.lib()
     torch.cuda.set_device(0)
     run = {"decode": run_decode, "batched": run_batched, "prefill": run_prefill, "cache": run_cache}[args.workload]
+    if args.decode_timeline:
+        run = run_decode_timeline
     print(json.dumps(run(args, api, torch)), flush=True)
 
 

@@ -65,6 +65,44 @@ __device__ __forceinline__ float sum16(float v) {
 
 __device__ __forceinline__ int wave_bcast(int v, int lane) { return __shfl(v, lane, kWave); }
 
+// Top-k keys: each (logit, expert) is one unsigned 64-bit key, larger for a
+// larger logit and then for a lower id (the float's bits made monotone, then
+// the complemented id), so "larger logit, ties to the lower id" is a plain
+// integer maximum, reduced across a wave with DPP row operations.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v + 0.0f);  // + 0: -0 becomes +0
+  const uint32_t mono = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)mono << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t k) {
+  const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+  // lanes the operation does not write keep their own key (the max identity)
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROW_MASK, 0xF, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > k ? o : k;
+}
+// Maximum of k over the wave, in every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  k = dpp_max_step<0xB1, 0xF>(k);   // quad_perm [1,0,3,2]
+  k = dpp_max_step<0x4E, 0xF>(k);   // quad_perm [2,3,0,1]
+  k = dpp_max_step<0x141, 0xF>(k);  // row_half_mirror
+  k = dpp_max_step<0x140, 0xF>(k);  // row_mirror: every lane holds its row's maximum
+  k = dpp_max_step<0x142, 0xA>(k);  // row_bcast:15 into rows 1 and 3
+  k = dpp_max_step<0x143, 0xC>(k);  // row_bcast:31 into rows 2 and 3: lane 63 holds the maximum
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// The logit back from a key's monotone bits.
+__device__ __forceinline__ float topk_key_value(uint64_t key) {
+  const uint32_t mono = (uint32_t)(key >> 32);
+  return __builtin_bit_cast(float, (mono & 0x80000000u) ? (mono & 0x7FFFFFFFu) : ~mono);
+}
+__device__ __forceinline__ int topk_key_expert(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+
 __device__ __forceinline__ float f32_nan() { return __builtin_nanf(""); }
 
 // Device-scope (all XCDs) release/acquire helpers for last-arriver reductions.

@@ -40,6 +40,26 @@
 #include "kernels.h"
 #include "q4_lane.h"
 
+// Stage timeline (a build option for measurement, off in the library): with
+// MOE_DECODE_TIMELINE defined, thread 0 of every workgroup records the global
+// 100 MHz clock (s_memrealtime) at the end of each stage of each layer of
+// the last launch; moe_debug_decode_timeline() copies the table to the host.
+#ifdef MOE_DECODE_TIMELINE
+namespace moe {
+constexpr int kTlLayers = 64, kTlGroups = 256, kTlStages = 12;
+__device__ uint64_t g_decode_timeline[kTlLayers][kTlGroups][kTlStages];
+}  // namespace moe
+#define DECODE_TL(layer, stage)                                                                       \
+  do {                                                                                                \
+    if (threadIdx.x == 0 && (layer) < moe::kTlLayers)                                                 \
+      moe::g_decode_timeline[(layer)][blockIdx.x][(stage)] = __builtin_amdgcn_s_memrealtime();        \
+  } while (0)
+#else
+#define DECODE_TL(layer, stage) \
+  do {                          \
+  } while (0)
+#endif
+
 namespace moe {
 
 namespace {
@@ -51,7 +71,10 @@ constexpr int kFThreads = kFWaves * kWave;
 // gate/up phase: the workgroup's 32 act columns x 16 K-parts; wave w holds
 // columns 16 (w % 2) .. +15 and K-parts 4 (w / 2) .. +3, lane = 4 parts x 16
 // columns, and each lane computes the gate row and the up row of its column
-// (one read of the activations for both)
+// (one read of the activations for both).  (Spreading a layer over all 256
+// compute units, 22 columns each, measured slower in every stage: more
+// requests in flight, weight lines split between workgroups and more
+// pollers of each exchange.)
 constexpr int kGP = 16, kGPW = 4, kGR = kWave / kGPW, kGGPP = 3, kGGMAX = kGP * kGGPP;  // d/64 <= 48
 constexpr int kActCols = 2 * kGR;                                                        // 32 act columns
 // down phase: one wave per selected expert; lanes 4 K-parts x 16 rows
@@ -59,6 +82,13 @@ constexpr int kDP = 4, kDR = kWave / kDP, kDGPP = 3, kDGMAX = kDP * kDGPP;  // f
 constexpr int kMaxE = 256;
 constexpr int kPartBatch = 12;         // float4 loads in flight per thread when summing router partials
 constexpr uint32_t kSpinLimit = 300000u;  // polling rounds (~1 us each) per wait at most
+// Router partials are reduced in two steps: workgroup q < E/4 (a reducer)
+// sums column quad q (experts 4q..4q+3) over every workgroup's row of
+// partials and publishes the 4 sums; then every workgroup reads the E sums.
+// A coherent load brings ~23 GB/s into one compute unit, so what bounds the
+// exchange is the bytes each workgroup reads: 16 bytes per row for a reducer
+// and 4 bytes per expert for everyone, where every workgroup reading every
+// row of partials (~90 KB) took ~5 us.
 
 struct FusedArgs {
   float* x_io;  // [L+1][d]
@@ -84,9 +114,10 @@ struct FusedArgs {
   // region on its own 256-byte boundary; encoded values, 0 = not written yet.
   uint32_t* regions;
   int64_t set_floats;
-  int64_t act_off, part_off, ss_off, xs_off;  // region offsets inside a set (words)
-  int act_ls, part_ls, ss_ls, xs_ls;  // words per layer: [k][f] act, [G][epad] router
-                                      // partials, [G] sums of squares, [d] layer input
+  int64_t act_off, part_off, ss_off, xs_off, qs_off;  // region offsets inside a set (words)
+  int act_ls, part_ls, ss_ls, xs_ls, qs_ls;  // words per layer: [k][f] act, [G][epad] router
+                                             // partials, [G] sums of squares, [d] layer input,
+                                             // [E] router sums (summed partials)
   int epad;      // E rounded up to 32: each workgroup's partials fill whole 128-byte lines
   int G, rpw;    // workgroups, down rows per workgroup (a multiple of 4, at most 16)
   int nck_g, nck_d;
@@ -206,6 +237,8 @@ __device__ __forceinline__ void clear_own(const FusedArgs& a, int t, __amdgpu_bu
     __builtin_amdgcn_raw_buffer_store_b32(0u, r, ((int)a.ss_off + layer * a.ss_ls + g) * 4, 0, kSc1);
     if (clear_last)
       __builtin_amdgcn_raw_buffer_store_b32(0u, r, ((int)a.ss_off + (layer + 1) * a.ss_ls + g) * 4, 0, kSc1);
+  } else if (t == na + np + nx + 1 && g < (a.E + 3) / 4) {
+    st_zero4(r, (int)a.qs_off + layer * a.qs_ls + 4 * g);  // this reducer's 4 router sums
   }
 }
 
@@ -276,9 +309,9 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
   __shared__ float s_o[kFWaves][kDR];          // down outputs per expert rank
   __shared__ float s_y[kDR], s_z[kDR];         // this workgroup's rows of the layer input / output, norm weight * rows
   __shared__ uint64_t s_launch;
+  __shared__ float s_inv;                      // 1/rms of the current layer input
   __shared__ int s_stop;                       // the workspace belongs to other shapes
   __shared__ int s_fail;                       // a wait of this workgroup gave up
-  float* s_logit = reinterpret_cast<float*>(s_logit4);
   const int t0 = threadIdx.x;
   const int g = blockIdx.x;
   const int t = t0, lane = t0 % kWave;
@@ -289,6 +322,7 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
     s_fail = 0;
     if (s_stop) __hip_atomic_store(a.err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  float* s_logit = reinterpret_cast<float*>(s_logit4);
   float* s_pe = reinterpret_cast<float*>(s_pe4);
   uint64_t* s_key = reinterpret_cast<uint64_t*>(s_key4);
   if (t < 4) s_key[a.E + t] = 0;
@@ -316,6 +350,7 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
   write_partials(a, t, 0, s_rw, s_z, s_y, s_pe, rc);
 
   for (int l = 0; l < a.L; ++l) {
+    DECODE_TL(l, 0);  // layer start
     // Thread-derived indices are recomputed from an opaque copy of the thread
     // id every layer: hoisted out of the loop they would hold hundreds of
     // registers for the whole launch.
@@ -326,14 +361,20 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
     // Everything that does not depend on the routing goes out at once: the
     // slot table, the router bias, the sums of squares, x and the norm
     // weight, then the router partials.
-    if (t < a.E) s_table[t] = a.slot_tables[(int64_t)l * a.E + t];
+    // the slot table goes to LDS only after the waits below: storing it now
+    // would wait for this load, and with it for every store still in flight
+    const int stbl = t < a.E ? a.slot_tables[(int64_t)l * a.E + t] : -1;
     const float bias = (a.router_bias && t < a.E) ? a.router_bias[(int64_t)l * a.E + t] : 0.0f;
-    uint32_t ssu[4];
+    const int nq = (a.E + 3) / 4;
+    // the sums of squares (G <= 256 words): wave 1 alone polls them and
+    // shares 1/rms through LDS (every wave polling them multiplied the
+    // coherent requests of the wait eightfold)
+    uint32_t ssu[4] = {1u, 1u, 1u, 1u};
     int ssi[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       ssi[c] = (int)a.ss_off + l * a.ss_ls + min(lane + c * kWave, a.G - 1);
-      ssu[c] = ldc(rc, ssi[c]);
+      if (wave == 1) ssu[c] = ldc(rc, ssi[c]);
     }
     constexpr int NPASSG = (8 * kGGMAX + kFThreads - 1) / kFThreads;
     StageRegs<NPASSG> xr, nwr;
@@ -356,44 +397,50 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
       nwr.a[ps] = nw ? *reinterpret_cast<const float4*>(nw + wi * 8) : make_float4(1.f, 1.f, 1.f, 1.f);
       nwr.b[ps] = nw ? *reinterpret_cast<const float4*>(nw + wi * 8 + 4) : make_float4(1.f, 1.f, 1.f, 1.f);
     }
-    {
-      // part[l] is [G][epad]: thread t sums the quad of experts qd over its
-      // slice of the G rows; the slices meet in LDS
-      const int nq = (a.E + 3) / 4, ns = kFThreads / nq;
-      const int qd = t % nq, sl = t / nq;
-      const int gper = (a.G + ns - 1) / ns;
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (sl < ns) {
-        const int g0 = sl * gper, g1 = min(a.G, g0 + gper);
-        const int pb = (int)a.part_off + l * a.part_ls + 4 * qd;
-        for (int b = g0; b < g1; b += kPartBatch) {
-          u32x4_t v[kPartBatch];
-          int vi[kPartBatch];
-#pragma unroll
-          for (int c = 0; c < kPartBatch; ++c) {
-            vi[c] = pb + min(b + c, g1 - 1) * a.epad;
-            v[c] = ldc4(rc, vi[c]);
-          }
-          wait_all4<kPartBatch>(a, rc, vi, v, &s_fail);
-#pragma unroll
-          for (int c = 0; c < kPartBatch; ++c)
-            if (b + c < g1) {
-              const float4 u = dec4(v[c]);
-              acc.x += u.x;
-              acc.y += u.y;
-              acc.z += u.z;
-              acc.w += u.w;
-            }
+    if (g < nq) {
+      // reducer of quad g: row t of the partials (16 bytes), summed in row
+      // order by wave 0 (a fixed order, the same in every launch)
+      u32x4_t pv[1] = {{1u, 1u, 1u, 1u}};
+      int pix[1] = {(int)a.part_off + l * a.part_ls + min(t, a.G - 1) * a.epad + 4 * g};
+      if (t < a.G) {
+        pv[0] = ldc4(rc, pix[0]);
+        wait_all4<1>(a, rc, pix, pv, &s_fail);
+        s_red4[t] = dec4(pv[0]);
+      }
+      __syncthreads();
+      DECODE_TL(l, 8);  // reducer: its column of every row of partials has arrived
+      if (wave == 0) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int r = lane; r < a.G; r += kWave) {
+          const float4 u = s_red4[r];
+          acc.x += u.x;
+          acc.y += u.y;
+          acc.z += u.z;
+          acc.w += u.w;
         }
-        s_red4[sl * nq + qd] = acc;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          acc.x += __shfl_xor(acc.x, o, kWave);
+          acc.y += __shfl_xor(acc.y, o, kWave);
+          acc.z += __shfl_xor(acc.z, o, kWave);
+          acc.w += __shfl_xor(acc.w, o, kWave);
+        }
+        if (lane == 0) st_e4(rc, (int)a.qs_off + l * a.qs_ls + 4 * g, acc);
+        DECODE_TL(l, 9);  // reducer: its 4 sums written
       }
     }
-    wait_all<4>(a, rc, ssi, ssu, &s_fail);
-    float ss = 0.0f;
+    // every workgroup: the E router sums, 4 per thread
+    u32x4_t qv[1] = {{1u, 1u, 1u, 1u}};
+    int qix[1] = {(int)a.qs_off + l * a.qs_ls + 4 * min(t, nq - 1)};
+    if (t < nq) qv[0] = ldc4(rc, qix[0]);
+    if (wave == 1) {
+      wait_all<4>(a, rc, ssi, ssu, &s_fail);
+      float ss = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) ss += lane + c * kWave < a.G ? dec(ssu[c]) : 0.0f;
-    ss = wave_sum(ss);
-    const float inv = a.norm_w ? 1.0f / sqrtf(ss / (float)a.d + a.eps) : 1.0f;
+      for (int c = 0; c < 4; ++c) ss += lane + c * kWave < a.G ? dec(ssu[c]) : 0.0f;
+      ss = wave_sum(ss);
+      if (lane == 0) s_inv = a.norm_w ? 1.0f / sqrtf(ss / (float)a.d + a.eps) : 1.0f;
+    }
     if (l > 0) {
       wait_all4<2 * NPASSG>(a, rc, xi, xu, &s_fail);
 #pragma unroll
@@ -402,14 +449,17 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
         xr.b[ps] = dec4(xu[2 * ps + 1]);
       }
     }
+    if (t < nq) {
+      wait_all4<1>(a, rc, qix, qv, &s_fail);
+      s_pe4[t] = dec4(qv[0]);  // the E sums (s_pe is free until the partials are written)
+    }
+    DECODE_TL(l, 10);  // thread 0: the router sums of its quad have arrived
+    if (t < a.E) s_table[t] = stbl;
     __syncthreads();
+    DECODE_TL(l, 1);  // router sums, sums of squares and x have arrived
+    const float inv = s_inv;
     if (t < a.E) {
-      // the slices in a fixed order (the same in every workgroup)
-      const int nq = (a.E + 3) / 4, ns = kFThreads / nq;
-      const float* red = reinterpret_cast<const float*>(s_red4);
-      float s = 0.0f;
-      for (int k = 0; k < ns; ++k) s += red[(k * nq + t / 4) * 4 + t % 4];
-      const float lg = s * inv + bias + 0.0f;  // + 0: -0 becomes +0
+      const float lg = s_pe[t] * inv + bias + 0.0f;  // + 0: -0 becomes +0
       s_logit[t] = lg;
       // one unsigned key orders (larger logit, then lower id): the float's
       // bits made monotone, then the complement of the id
@@ -443,6 +493,7 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
       }
     }
     __syncthreads();
+    DECODE_TL(l, 2);  // top-k known
     // this workgroup's expert (rank jr) and act columns [c0, c0 + 32)
     const int jr = g / (a.f / kActCols);
     const int c0 = (g % (a.f / kActCols)) * kActCols;
@@ -475,10 +526,12 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
       stage_store<kGP, kGGMAX, NPASSG>(xh, sr, Gd, t, kFThreads);
     }
     __syncthreads();
+    DECODE_TL(l, 3);  // h staged in LDS, gate/up weight loads issued
     {
       const float2 v = lane_dot2<kGP, kGPW, kGGPP, kGGMAX>(wg, wu, xh, j, pt, Gd, a.nck_g);
       if (lane < kGR) s_gu[pb][cb * kGR + r] = v;
       __syncthreads();
+      DECODE_TL(l, 4);  // gate/up dot products done
       if (t < kActCols) {
         // the part blocks in a fixed order
         float gs = 0.0f, us = 0.0f;
@@ -562,12 +615,14 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
       if (wave_on) stage_store<kDP, kDGMAX, NPASS>(xa[jw], sr, Gf, lane, kWave);
       __builtin_amdgcn_s_waitcnt(0);  // this wave's router-row copies have landed in LDS
       __syncthreads();
+      DECODE_TL(l, 5);  // act values arrived, down rows and next router rows landed
       if (wave_on) {
         float v = lane_dot<kDP, kDGPP, kDGMAX>(wd, xa[jw], jd, pd, Gf, a.nck_d);
         if (!ok2) v = f32_nan();
         if (jd == 0) s_o[jw][rd] = v;
       }
       __syncthreads();
+      DECODE_TL(l, 6);  // down dot products done
       if (t < kDR) {
         float y = 0.0f, z = 0.0f;
         if (t < nr) {
@@ -584,6 +639,7 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
       if (l + 1 < a.L && t < nr / 4)
         st_e4(rc, (int)a.xs_off + (l + 1) * a.xs_ls + r0 + 4 * t, reinterpret_cast<const float4*>(s_y)[t]);
       write_partials(a, t, l + 1, s_rw, s_z, s_y, s_pe, rc);
+      DECODE_TL(l, 7);  // combine done, next layer input and router partials written
     }
   }
 
@@ -631,9 +687,9 @@ namespace {
 // Workspace: a 512-byte header (launch count at 0, shape signature at 8, error
 // word at kDecodeErrOffset), then two region sets of set_floats words each.
 struct FusedLayout {
-  int act_ls, part_ls, ss_ls, xs_ls;  // words per layer region, multiples of 64 (256 bytes)
+  int act_ls, part_ls, ss_ls, xs_ls, qs_ls;  // words per layer region, multiples of 64 (256 bytes)
   int epad;
-  int64_t act_off, part_off, ss_off, xs_off, set_floats;  // words inside a set
+  int64_t act_off, part_off, ss_off, xs_off, qs_off, set_floats;  // words inside a set
   int64_t regions_off, bytes;
 };
 FusedLayout fused_layout(int L, int d, int f, int E, int k) {
@@ -645,11 +701,13 @@ FusedLayout fused_layout(int L, int d, int f, int E, int k) {
   o.part_ls = r64((int64_t)G * o.epad);
   o.ss_ls = r64(G);
   o.xs_ls = r64(d);
+  o.qs_ls = r64(E + 3);
   o.act_off = 0;
   o.part_off = o.act_off + (int64_t)L * o.act_ls;
   o.ss_off = o.part_off + (int64_t)L * o.part_ls;
   o.xs_off = o.ss_off + (int64_t)(L + 1) * o.ss_ls;
-  o.set_floats = o.xs_off + (int64_t)L * o.xs_ls;
+  o.qs_off = o.xs_off + (int64_t)L * o.xs_ls;
+  o.set_floats = o.qs_off + (int64_t)L * o.qs_ls;
   o.regions_off = 512;
   o.bytes = o.regions_off + 2 * o.set_floats * 4;
   return o;
@@ -695,6 +753,8 @@ hipError_t launch_decode_fused(float* x_io, int L, const float* norm_w, float ep
   a.part_off = lay.part_off;
   a.ss_off = lay.ss_off;
   a.xs_off = lay.xs_off;
+  a.qs_off = lay.qs_off;
+  a.qs_ls = lay.qs_ls;
   a.act_ls = lay.act_ls;
   a.part_ls = lay.part_ls;
   a.ss_ls = lay.ss_ls;
@@ -718,3 +778,11 @@ hipError_t launch_decode_fused(float* x_io, int L, const float* norm_w, float ep
 }
 
 }  // namespace moe
+
+#ifdef MOE_DECODE_TIMELINE
+// The timeline of the last launch: uint64 [64][256][12] (layer, workgroup, stage).
+extern "C" int moe_debug_decode_timeline(uint64_t* host_out) {
+  return (int)hipMemcpyFromSymbol(host_out, HIP_SYMBOL(moe::g_decode_timeline), sizeof(moe::g_decode_timeline), 0,
+                                  hipMemcpyDeviceToHost);
+}
+#endif

@@ -20,39 +20,10 @@ constexpr int kSmallT = 8;         // fused single-launch path up to this many t
 typedef float floatx4r __attribute__((ext_vector_type(4)));
 constexpr int kRouteWaves = 4;     // waves per workgroup in the fused path
 
-// Top-k of one token's logits by one wave: k rounds of a wave-wide arg-max.
-// Each (logit, expert) is one unsigned 64-bit key, larger for a larger logit
-// and then for a lower id (the float's bits made monotone, then the
-// complemented id), so the arg-max is a plain maximum, reduced with DPP row
-// operations (no LDS round trips).  Writes idx/w for the token.
+// Top-k of one token's logits by one wave: k rounds of a wave-wide arg-max
+// over one 64-bit key per (logit, expert) (topk_key, wave_max_u64 in common.h).
+// Writes idx/w for the token.
 // v[i], ok[i]: the logit of expert lane + 64 i and whether that expert exists.
-__device__ __forceinline__ uint64_t topk_key(float v, int e) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, v + 0.0f);  // + 0: -0 becomes +0
-  const uint32_t mono = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)mono << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint64_t dpp_max_step(uint64_t k) {
-  const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
-  // lanes the operation does not write keep their own key (the max identity)
-  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROW_MASK, 0xF, false);
-  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROW_MASK, 0xF, false);
-  const uint64_t o = ((uint64_t)ohi << 32) | olo;
-  return o > k ? o : k;
-}
-// Maximum of k over the wave, in every lane.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-  k = dpp_max_step<0xB1, 0xF>(k);   // quad_perm [1,0,3,2]
-  k = dpp_max_step<0x4E, 0xF>(k);   // quad_perm [2,3,0,1]
-  k = dpp_max_step<0x141, 0xF>(k);  // row_half_mirror
-  k = dpp_max_step<0x140, 0xF>(k);  // row_mirror: every lane holds its row's maximum
-  k = dpp_max_step<0x142, 0xA>(k);  // row_bcast:15 into rows 1 and 3
-  k = dpp_max_step<0x143, 0xC>(k);  // row_bcast:31 into rows 2 and 3: lane 63 holds the maximum
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, 63);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 __device__ void wave_topk_vals(float (&v)[4], bool (&ok)[4], int k, int32_t* idx_out, float* w_out) {
   const int lane = threadIdx.x % kWave;
   uint64_t key[4];
