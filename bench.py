@@ -55,8 +55,8 @@ CSRC = os.path.join(ROOT, "int4_routed_expert_route_amd", "csrc")
 TRAFFIC = {
     "decode": {"sources": ('q4_gemv.hip', 'q4_lane.h', 'common.h'), "sha256_16": "4fb8e1792d1f9193",
                "fetch_bytes": 18093516, "write_bytes": 22528},
-    "decode_fused": {"sources": ('decode_fused.hip', 'q4_lane.h', 'common.h'), "sha256_16": "e38b527d1b6f8d39",
-                     "fetch_bytes": 954574168, "write_bytes": 8112864},
+    "decode_fused": {"sources": ('decode_fused.hip', 'q4_lane.h', 'common.h'), "sha256_16": "acaba618e38ad1dd",
+                     "fetch_bytes": 954449621, "write_bytes": 8174464},
     "prefill": {"sources": ('q4_grouped_mfma.hip', 'common.h'), "sha256_16": "6e9a36128a0f25f9",
                 "fetch_bytes": 226804165, "write_bytes": 23889872},
     "batched_f16": {"sources": ('q4_grouped_mfma.hip', 'common.h'), "sha256_16": "6e9a36128a0f25f9",
@@ -237,10 +237,10 @@ def rounded_steps(n, period):
 class DecodeStack:
     """Device state of the 30-layer batch-1 decode workload."""
 
-    def __init__(self, api, torch, seed=0, cold=False):
+    def __init__(self, api, torch, seed=0, cold=False, arena=None):
         self.api, self.torch = api, torch
         self.dm = api.dims(D, F, E, K)
-        self.arena, self.stride = build_arena(torch, api, seed)
+        self.arena, self.stride = build_arena(torch, api, seed) if arena is None else arena
         dev = "cuda"
         self.slots = torch.arange(E, dtype=torch.int32, device=dev)
         self.tables = self.slots.repeat(NL, 1).contiguous()  # [NL][E], identity slots
@@ -316,24 +316,71 @@ class DecodeStack:
 
 
 def run_decode(args, api, torch):
-    stack = DecodeStack(api, torch, args.seed, cold=args.control == "cold")
-    period = stack.period
-    steps, warm = rounded_steps(args.steps, period), rounded_steps(args.warmup, period)
+    """The 30-layer batch-1 decode workload (Zipf routing) and its control arm
+    (cold routing that defeats the last-level cache) in one invocation: after
+    the warmup, timed segments alternate between the arms in both orders
+    (ZC, CZ, ZC, ...), args.repeats pairs.  The Zipf segments add up to
+    exactly args.steps timed steps; `value` is their overall rate, and each
+    arm's per-segment median and spread are reported beside it."""
+    stack = DecodeStack(api, torch, args.seed, cold=False)
+    ctrl = DecodeStack(api, torch, args.seed, cold=True, arena=(stack.arena, stack.stride))
     fused = args.decode_path == "fused"
-    body = (lambda: stack.fused_steps(1)) if fused else (lambda: stack.steps(1))
-    if args.no_graph:
-        run = lambda n: [body() for _ in range(n // period)]
-    else:
-        # one replay = one routing period (1 step for Zipf, 16 for the cold arm)
-        graph = graph_of(torch, body)
-        run = lambda n: [graph.replay() for _ in range(n // period)]
-    ms, t_wall = timed(torch, run, steps, warm)
+    period = stack.period
+    R = max(1, args.repeats)
+    seg = [args.steps // R + (1 if i < args.steps % R else 0) for i in range(R)]  # Zipf steps per segment
+    cseg = rounded_steps(max(1, args.steps // R), ctrl.period)                     # control steps per segment
+
+    def runner(st):
+        body = (lambda: st.fused_steps(1)) if fused else (lambda: st.steps(1))
+        if args.no_graph:
+            return lambda n: [body() for _ in range(n // st.period)]
+        graph = graph_of(torch, body)  # one replay = one routing period (1 step, or 16 for the control)
+        return lambda n: [graph.replay() for _ in range(n // st.period)]
+
+    run_z, run_c = runner(stack), runner(ctrl)
+    log(f"warmup {args.warmup} steps per arm")
+    run_z(args.warmup)
+    run_c(rounded_steps(args.warmup, ctrl.period))
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def segment(run, n):
+        torch.cuda.synchronize()
+        e0.record()
+        run(n)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1000.0
+
+    z_times, c_times, z_rates, c_rates = [], [], [], []
+    t_wall = time.perf_counter()
+    for r in range(R):
+        order = ("z", "c") if r % 2 == 0 else ("c", "z")
+        for arm in order:
+            if arm == "z":
+                if seg[r] == 0:
+                    continue
+                dt = segment(run_z, seg[r])
+                z_times.append(dt)
+                z_rates.append(seg[r] / dt)
+            else:
+                dt = segment(run_c, cseg)
+                c_times.append(dt)
+                c_rates.append(cseg / dt)
+    t_wall = time.perf_counter() - t_wall
     if fused:
         api.moe_decode_check(stack.ws_fused)
-    tok_s = 1000.0 / ms
+        api.moe_decode_check(ctrl.ws_fused)
+    steps, warm = args.steps, args.warmup
+    tok_s = steps / sum(z_times)
+    ms = 1000.0 / tok_s
     per_layer, gu_bytes, _ = decode_bytes()
     step_bytes = NL * per_layer
-    log(f"{steps} steps ({args.decode_path}): {ms * 1000:.1f} us/step, {tok_s:.1f} tok/s, "
+    c_tok_s = len(c_times) * cseg / sum(c_times)
+    log(f"{steps} Zipf steps ({args.decode_path}) in {len(z_times)} segments: {ms * 1000:.1f} us/step, "
+        f"{tok_s:.1f} tok/s (median {np.median(z_rates):.1f}, {min(z_rates):.1f}-{max(z_rates):.1f}); control "
+        f"{c_tok_s:.1f} tok/s (median {np.median(c_rates):.1f}, {min(c_rates):.1f}-{max(c_rates):.1f}); "
         f"{step_bytes * tok_s / 1e9:.0f} GB/s algorithmic")
 
     # the step's kernels one at a time, each at its own begin/end; layer and
@@ -351,15 +398,25 @@ def run_decode(args, api, torch):
         f_achieved = step_bytes / (fu_us * 1e-6) / 1e9
         log(f"fused decode kernel (eager, mean): {fu_us:.1f} us per token, {f_achieved:.0f} GB/s algorithmic")
 
-    out = base_record(tok_s, steps, warm, ms, "fp32",
+    out = base_record(tok_s, steps, warm, ms, "int4-fx16-fp32",
                       "batch-1 decode, 30 routed MoE layers x 128 experts (d=2816, f=704, top-8, int4 groups of "
-                      "64, fp16 scale/bias), all experts resident in HBM, "
-                      + ("Zipf(1.1) routing" if not stack.cold else
-                         "cold routing control (no expert reuse within 16 steps)"),
+                      "64, fp16 scale/bias), all experts resident in HBM, Zipf(1.1) routing",
                       {"tokens_per_step": 1, "graph": not args.no_graph,
                        "path": "moe_decode_layers (one launch per token)" if fused else
                                "moe_route + moe_expert_q4_gateup + moe_expert_q4_down_combine per layer"})
     out.update({
+        "dtype_detail": "int4 weights (exact) x activations as 16-bit fixed point per 64-column group, exact "
+                        "int32 sums inside a group, fp32 across groups; router, softmax and combine fp32",
+        "protocol": {"segments": "Zipf and control alternated, orders ZC, CZ, ...", "repeats": R,
+                     "zipf_tok_s": {"median": round(float(np.median(z_rates)), 1),
+                                    "min": round(min(z_rates), 1), "max": round(max(z_rates), 1),
+                                    "segments_steps": seg},
+                     "control_tok_s": {"overall": round(c_tok_s, 1), "median": round(float(np.median(c_rates)), 1),
+                                       "min": round(min(c_rates), 1), "max": round(max(c_rates), 1),
+                                       "segment_steps": cseg,
+                                       "routing": "step s selects experts (8s + j + 3l) mod 128: no expert "
+                                                  "comes back within 16 steps (defeats the 256 MB last-level "
+                                                  "cache)"}},
         "algorithmic_bytes_per_token": step_bytes,
         "algorithmic_GBps": round(step_bytes * tok_s / 1e9, 1),
         "hbm_frac_step": round(step_bytes * tok_s / 1e9 / HBM_PEAK_GBPS, 4),
@@ -391,7 +448,7 @@ def run_decode(args, api, torch):
 
 def run_decode_timeline(args, api, torch):
     """Per-stage timeline of the fused decode kernel (measurement build
-    libmoe_timeline.so): every workgroup's clock at the end of each stage of
+    libmoe_measure.so): every workgroup's clock at the end of each stage of
     each layer, over several eager launches after the warmup, summarised as
     markdown into args.decode_timeline."""
     import ctypes
@@ -631,6 +688,9 @@ def run_prefill(args, api, torch):
     dn_tflops = flop_dn / (dn_us * 1e-6) / 1e12
     log(f"kernels (eager, mean us): route {rt_us:.1f}  permute {pm_us:.1f}  gate/up GEMM {gu_us:.1f} "
         f"({achieved:.0f} TFLOP/s)  down GEMM {dn_us:.1f} ({dn_tflops:.0f} TFLOP/s)")
+    yard = gemm_yardstick(torch, int(cnt.max()))
+    log(f"yardstick: torch fp16 GEMM {yard['M']} x {yard['N']} x {yard['K']} (the hottest expert's gate/up): "
+        f"{yard['TFLOPs']:.0f} TFLOP/s ({yard['frac']:.1%} of peak)")
     out = base_record(tok_s, args.steps, args.warmup, ms, "fp16",
                       f"prefill, {T} tokens x 30 routed MoE layers x 128 experts (d=2816, f=704, top-8, int4 "
                       "groups of 64), Zipf(1.1) routing, expert-grouped int4 GEMM on MFMA "
@@ -653,11 +713,34 @@ def run_prefill(args, api, torch):
             "algorithmic_flop_per_launch": flop_gu, "avg_launch_us": round(gu_us, 2),
         },
         "wall_s_timed": round(t_wall, 3),
+        "yardstick": yard,
     })
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(args.seed, 256, 20.0, "prefill")
     return out
+
+
+def gemm_yardstick(torch, M, reps=50):
+    """Achievable-peak yardstick: a dense fp16 GEMM through torch (hipBLASLt)
+    at the hottest expert's gate/up shape, M routed rows x N = 2f weight rows
+    x K = d, contiguous operands, fp32 accumulate; run, never disassembled."""
+    a = torch.randn(M, D, dtype=torch.float16, device="cuda")
+    b = torch.randn(D, 2 * F, dtype=torch.float16, device="cuda")
+    for _ in range(5):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / reps
+    tf = 2.0 * M * D * 2 * F / (us * 1e-6) / 1e12
+    return {"what": "torch.matmul fp16 (hipBLASLt) at the hottest expert's gate/up shape", "M": M, "N": 2 * F,
+            "K": D, "us": round(us, 2), "TFLOPs": round(tf, 1), "frac": round(tf / MFMA_PEAK_TFLOPS, 4)}
 
 
 # ----------------------------------------------------------------------------- bounded cache
@@ -871,7 +954,13 @@ def run_cache(args, api, torch):
 
 
 def run_copy_calibration(mib):
+    """Known-bytes kernels for scaling HBM counters: a device-to-device copy of
+    MIB MiB (torch), and, from the measurement build, reads of the same bytes
+    with 128-bit loads into registers and with LDS-DMA loads (three launches
+    each, on buffers larger than the last-level cache)."""
+    import ctypes
     import torch
+    from int4_routed_expert_route_amd import build as moe_build
     n = mib << 20
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -879,7 +968,18 @@ def run_copy_calibration(mib):
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}))
+    rec = {"copy_bytes_per_launch": n, "launches": 3}
+    if os.path.exists(moe_build.MEASURE_LIB):
+        lib = ctypes.CDLL(moe_build.MEASURE_LIB)
+        fn = lib.moe_debug_read
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        out = torch.zeros(1024 * 256, dtype=torch.int32, device="cuda")
+        for mode in (0, 1):
+            for _ in range(3):
+                assert fn(src.data_ptr(), n, mode, out.data_ptr(), None) == 0
+        torch.cuda.synchronize()
+        rec.update({"read_bytes_per_launch": n, "read_modes": ["vgpr_b128", "lds_dma_16B"]})
+    print(json.dumps(rec))
 
 
 def main():
@@ -890,8 +990,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", choices=["decode", "batched", "prefill", "cache"], default="decode")
     ap.add_argument("--control", choices=["zipf", "cold"], default="zipf",
-                    help="decode: zipf = the Zipf(1.1) routing workload; cold = routing that never reuses an "
-                         "expert within 16 steps (defeats the last-level cache)")
+                    help="--decode-timeline: zipf = the Zipf(1.1) routing workload; cold = routing that never "
+                         "reuses an expert within 16 steps (defeats the last-level cache).  The decode timing "
+                         "line always runs both, alternated")
     ap.add_argument("--tokens", type=int, default=0, help="batched / prefill: tokens per step (32 / 2048)")
     ap.add_argument("--decode-path", choices=["fused", "calls"], default="fused",
                     help="decode: one moe_decode_layers launch per token, or the three calls per layer")
@@ -911,11 +1012,13 @@ def main():
     ap.add_argument("--overlap", choices=["filler", "shared"], default="filler",
                     help="cache: work overlapped with staging (the d x 4d filler GEMV, or the shared expert)")
     ap.add_argument("--kernel-samples", type=int, default=62)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="decode: timed segments per arm (Zipf workload and cold-routing control, alternated)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--decode-timeline", default="", metavar="OUT.md",
                     help="decode: per-stage timeline of the fused kernel from the measurement build "
-                         "libmoe_timeline.so, summarised into OUT.md (no timing line)")
+                         "libmoe_measure.so, summarised into OUT.md (no timing line)")
     ap.add_argument("--library", default="", metavar="SO",
                     help="load this build of libmoe instead of the in-tree one (compare builds on one box)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -938,7 +1041,7 @@ def main():
     import int4_routed_expert_route_amd.api as api
     if args.decode_timeline:
         from int4_routed_expert_route_amd import build as moe_build
-        api.LIB_PATH = moe_build.TIMELINE_LIB
+        api.LIB_PATH = moe_build.MEASURE_LIB
         args.workload = "decode"
         args.warmup, args.steps = min(args.warmup, 16), min(args.steps, 8)
     if args.library:

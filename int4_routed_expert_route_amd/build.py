@@ -22,10 +22,13 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-# Measurement variant: the fused decode kernel records a per-stage timeline
-# (MOE_DECODE_TIMELINE, see decode_fused.hip); everything else is the library.
-TIMELINE_LIB = os.path.join(HERE, "libmoe_timeline.so")
-TIMELINE_DEFINES = {"decode_fused.hip": ["-DMOE_DECODE_TIMELINE"]}
+# Measurement variant (libmoe_measure.so): the library, with the fused decode
+# kernel recording a per-stage timeline (MOE_DECODE_TIMELINE, see
+# decode_fused.hip) and known-bytes read kernels for scaling HBM counters
+# (measure.hip).  Never loaded by the tests or the timing line.
+MEASURE_LIB = os.path.join(HERE, "libmoe_measure.so")
+MEASURE_DEFINES = {"decode_fused.hip": ["-DMOE_DECODE_TIMELINE"]}
+MEASURE_SOURCES = ["measure.hip"]
 
 
 def _compile(src: str, build_dir: str = BUILD, defines=None) -> str:
@@ -39,14 +42,14 @@ def _compile(src: str, build_dir: str = BUILD, defines=None) -> str:
     return obj
 
 
-def build(verbose: bool = False, timeline: bool = False) -> str:
-    """Compile every source for gfx950 and link libmoe.so (timeline=True: the
-    measurement variant libmoe_timeline.so)."""
-    build_dir = os.path.join(BUILD, "timeline") if timeline else BUILD
-    out = TIMELINE_LIB if timeline else LIB
-    defines = TIMELINE_DEFINES if timeline else None
+def build(verbose: bool = False, measure: bool = False) -> str:
+    """Compile every source for gfx950 and link libmoe.so (measure=True: the
+    measurement variant libmoe_measure.so)."""
+    build_dir = os.path.join(BUILD, "measure") if measure else BUILD
+    out = MEASURE_LIB if measure else LIB
+    defines = MEASURE_DEFINES if measure else None
     os.makedirs(build_dir, exist_ok=True)
-    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    srcs = [s for s in SOURCES + (MEASURE_SOURCES if measure else []) if os.path.exists(os.path.join(CSRC, s))]
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda src: _compile(src, build_dir, defines), srcs))
     tmp = out + ".tmp"
@@ -61,4 +64,4 @@ def build(verbose: bool = False, timeline: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True, timeline="--timeline" in sys.argv)
+    build(verbose=True, measure="--measure" in sys.argv)
