@@ -246,7 +246,12 @@ moe_status moe_expert_q4_gateup(const float* h, const int32_t* topk_idx,
 /* ---------------------------------------------------------------------------
  * moe_expert_q4_down_combine — out[p] = W_down[e] act[p], then
  * y[t] = residual[t] + sum_j topk_w[t][j] * out[t*k+j], summed in rank order
- * (deterministic).  Same slot-table, offsets and precision rules as gateup.
+ * (deterministic).  The token's output mixes only the experts its router
+ * named, weighted by the router (TurboFieldfare video transcript, paragraph
+ * on Gemma 4 as a mixture-of-experts model; "Optimizing a 14.3 GB model for an
+ * 8 GB machine", section "MoE needed parallel work, reuse, and coarse
+ * overlap": the routed MoE of each layer).  Same slot-table, offsets and
+ * precision rules as gateup.
  *   act       device, from moe_expert_q4_gateup at the same prec (layout: moe_act_bytes)
  *   topk_w    device fp32 [T][k]
  *   pair_pos  device int32 [T*k] from moe_permute, or NULL with offsets NULL
@@ -314,7 +319,8 @@ moe_status moe_cache_destroy(moe_cache* c);
  * leaves the cache exactly as it was.  A failure after some were enqueued
  * leaves the rest as it was but empties the slots those copies target (they
  * may be overwritten): on the host at once, in the device table at the
- * layer's next call.  Once the step's copies, table copy and event are
+ * layer's next call (until that call succeeds, kernels must not read the
+ * layer's device table).  Once the step's copies, table copy and event are
  * enqueued the step is committed; if only the hit-mask copy then fails, the
  * call returns MOE_ERR_HIP with the step committed. */
 moe_status moe_slot_stage(moe_cache* c, int32_t layer, int32_t step, const int32_t* sel_host,

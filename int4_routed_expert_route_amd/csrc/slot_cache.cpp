@@ -91,6 +91,30 @@ void fill_table(moe_cache* c, int layer, const int32_t* se) {
 
 void rebuild_table(moe_cache* c, int layer) { fill_table(c, layer, c->slot_expert.data() + (int64_t)layer * c->S); }
 
+// The device copy of the state (moe_cache_enable_device), also after a
+// part-way failure of that call.
+void release_device_state(moe_cache* c) {
+  for (hipEvent_t& e : c->routed)
+    if (e) { hipEventDestroy(e); e = nullptr; }
+  c->routed.clear();
+  for (void** p : {(void**)&c->d_slot_expert, (void**)&c->d_stamp, (void**)&c->d_count, (void**)&c->d_miss,
+                   (void**)&c->d_nmiss, (void**)&c->d_stats, (void**)&c->d_err})
+    if (*p) { hipFree(*p); *p = nullptr; }
+}
+
+// The helper streams of split staging, also after a part-way failure of
+// moe_cache_set_staging.
+void release_split_streams(moe_cache* c) {
+  for (size_t i = 0; i < c->helpers.size(); ++i) {
+    if (c->helpers[i]) { hipStreamSynchronize(c->helpers[i]); hipStreamDestroy(c->helpers[i]); }
+    if (c->joins[i]) hipEventDestroy(c->joins[i]);
+  }
+  c->helpers.clear();
+  c->joins.clear();
+  if (c->fork) hipEventDestroy(c->fork);
+  c->fork = nullptr;
+}
+
 // Device mode: bring the host mirror up to date (waits for the device).
 moe_status pull_device_state(const moe_cache* cc) {
   moe_cache* c = const_cast<moe_cache*>(cc);
@@ -171,16 +195,8 @@ moe_status moe_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_slots
 moe_status moe_cache_destroy(moe_cache* c) {
   if (!c) return MOE_OK;
   if (c->device) hipDeviceSynchronize();
-  for (hipEvent_t e : c->routed)
-    if (e) hipEventDestroy(e);
-  for (void* p : {(void*)c->d_slot_expert, (void*)c->d_stamp, (void*)c->d_count, (void*)c->d_miss,
-                  (void*)c->d_nmiss, (void*)c->d_stats, (void*)c->d_err})
-    if (p) hipFree(p);
-  for (size_t i = 0; i < c->helpers.size(); ++i) {
-    if (c->helpers[i]) { hipStreamSynchronize(c->helpers[i]); hipStreamDestroy(c->helpers[i]); }
-    if (c->joins[i]) hipEventDestroy(c->joins[i]);
-  }
-  if (c->fork) hipEventDestroy(c->fork);
+  release_device_state(c);
+  release_split_streams(c);
   for (size_t l = 0; l < c->staged.size(); ++l) {
     if (c->staged[l]) { hipEventSynchronize(c->staged[l]); hipEventDestroy(c->staged[l]); }
     if (c->masked[l]) { hipEventSynchronize(c->masked[l]); hipEventDestroy(c->masked[l]); }
@@ -413,13 +429,19 @@ moe_status moe_cache_set_staging(moe_cache* c, int32_t mode, int32_t n_streams) 
     }
     c->pool_dev = static_cast<const uint8_t*>(d);
   } else if (mode == MOE_STAGE_COPY_SPLIT) {
+    // a failure part-way releases what was made: the mode stays unset
     c->helpers.assign(n_streams, nullptr);
     c->joins.assign(n_streams, nullptr);
-    if ((st = hipcheck(hipEventCreateWithFlags(&c->fork, hipEventDisableTiming), "hipEventCreate"))) return st;
+    if ((st = hipcheck(hipEventCreateWithFlags(&c->fork, hipEventDisableTiming), "hipEventCreate"))) {
+      release_split_streams(c);
+      return st;
+    }
     for (int i = 0; i < n_streams; ++i)
       if ((st = hipcheck(hipStreamCreateWithFlags(&c->helpers[i], hipStreamNonBlocking), "hipStreamCreate")) ||
-          (st = hipcheck(hipEventCreateWithFlags(&c->joins[i], hipEventDisableTiming), "hipEventCreate")))
+          (st = hipcheck(hipEventCreateWithFlags(&c->joins[i], hipEventDisableTiming), "hipEventCreate"))) {
+        release_split_streams(c);
         return st;
+      }
   }
   c->staging = mode;
   return MOE_OK;
@@ -498,7 +520,7 @@ moe_status moe_cache_enable_device(moe_cache* c) {
       (st = hipcheck(hipMalloc(&c->d_nmiss, sizeof(int32_t) * c->L), "hipMalloc")) ||
       (st = hipcheck(hipMalloc(&c->d_stats, sizeof(int64_t) * 3), "hipMalloc")) ||
       (st = hipcheck(hipMalloc(&c->d_err, sizeof(uint32_t)), "hipMalloc")))
-    return st;
+    return release_device_state(c), st;
   const int64_t stats[3] = {c->stats.hits, c->stats.misses, c->stats.bytes_staged};
   const uint32_t zero = 0;
   if ((st = hipcheck(hipMemcpy(c->d_slot_expert, c->slot_expert.data(), sizeof(int32_t) * nLS, hipMemcpyHostToDevice),
@@ -509,10 +531,11 @@ moe_status moe_cache_enable_device(moe_cache* c) {
                      "hipMemcpy")) ||
       (st = hipcheck(hipMemcpy(c->d_stats, stats, sizeof(stats), hipMemcpyHostToDevice), "hipMemcpy")) ||
       (st = hipcheck(hipMemcpy(c->d_err, &zero, 4, hipMemcpyHostToDevice), "hipMemcpy")))
-    return st;
+    return release_device_state(c), st;
   c->routed.assign(c->L, nullptr);
   for (int l = 0; l < c->L; ++l)
-    if ((st = hipcheck(hipEventCreateWithFlags(&c->routed[l], hipEventDisableTiming), "hipEventCreate"))) return st;
+    if ((st = hipcheck(hipEventCreateWithFlags(&c->routed[l], hipEventDisableTiming), "hipEventCreate")))
+      return release_device_state(c), st;
   c->device = true;
   c->staged_any = true;
   return MOE_OK;
