@@ -50,18 +50,10 @@ EPS = 1e-6
 CSRC = os.path.join(ROOT, "int4_routed_expert_route_amd", "csrc")
 
 # HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
-# (scaled by a 256 MiB copy's readings), keyed by the workload, for the kernel
-# sources with this fingerprint; reported as null once the sources differ.
-TRAFFIC = {
-    "decode": {"sources": ('q4_gemv.hip', 'q4_lane.h', 'common.h'), "sha256_16": "4fb8e1792d1f9193",
-               "fetch_bytes": 18093516, "write_bytes": 22528},
-    "decode_fused": {"sources": ('decode_fused.hip', 'q4_lane.h', 'common.h'), "sha256_16": "acaba618e38ad1dd",
-                     "fetch_bytes": 954449621, "write_bytes": 8174464},
-    "prefill": {"sources": ('q4_grouped_mfma.hip', 'common.h'), "sha256_16": "6e9a36128a0f25f9",
-                "fetch_bytes": 226804165, "write_bytes": 23889872},
-    "batched_f16": {"sources": ('q4_grouped_mfma.hip', 'common.h'), "sha256_16": "6e9a36128a0f25f9",
-                    "fetch_bytes": 48092100, "write_bytes": 9037792},
-}
+# (scaled by a 1 GiB copy's readings), keyed by the workload, for the kernel
+# sources and the input recipe with this fingerprint (paths from the repository
+# root); reported as null once either differs.
+TRAFFIC = {}
 
 
 def log(msg):
@@ -94,7 +86,7 @@ def traffic_of(workload):
     if not t:
         return None
     try:
-        src = b"".join(open(os.path.join(CSRC, n), "rb").read() for n in t["sources"])
+        src = b"".join(open(os.path.join(ROOT, n), "rb").read() for n in t["sources"])
     except OSError:
         return None
     if hashlib.sha256(src).hexdigest()[:16] != t["sha256_16"]:

@@ -93,9 +93,10 @@ typedef struct moe_dims {
 typedef enum moe_precision {
   MOE_PREC_FP32 = 0,      /* int4 weights, activations kept to ~fp32 accuracy, fp32 accumulate (decode) */
   MOE_PREC_BF16_MFMA = 1, /* refused (MOE_ERR_UNSUPPORTED): bf16 operands (8-bit significand) on
-                             weights whose per-group means are far from zero lose 1-6% per output
-                             row to the cancellation of 2816-term sums, beyond the 1e-2 tolerance;
-                             the value is kept so that the codes stay stable */
+                             weights whose per-group means sit far from zero lose 1-6% per output
+                             row to the cancellation of 2816-term sums, beyond the 1e-2 tolerance,
+                             and fp16 runs at the same rate; the value is kept so that the codes
+                             stay stable */
   MOE_PREC_F16_MFMA = 2,  /* grouped GEMM: int4 -> fp16 weights, fp16 activations, fp16 MFMA, fp32
                              accumulate: the same MFMA rate as bf16 with 3 more significand bits;
                              intermediate values are block-scaled, so fp16's range does not bind */

@@ -247,7 +247,7 @@ moe_status moe_expert_q4_gateup(const float* h, const int32_t* topk_idx, const i
   }
   if (prec == MOE_PREC_BF16_MFMA)
     return fail(MOE_ERR_UNSUPPORTED,
-                "%s: bf16 operands (8-bit significand) miss the 1e-2 output tolerance on these weights; "
+                "%s: bf16 operands (8-bit significand) can miss the 1e-2 output tolerance on offset weights; "
                 "MOE_PREC_F16_MFMA runs at the same MFMA rate with 3 more bits", fn);
   if (prec == MOE_PREC_F16_MFMA || prec == MOE_PREC_F16_MFMA_DIRECT) {
     if (!grouped)
@@ -304,7 +304,7 @@ moe_status moe_expert_q4_down_combine(const void* act, const int32_t* topk_idx, 
   }
   if (prec == MOE_PREC_BF16_MFMA)
     return fail(MOE_ERR_UNSUPPORTED,
-                "%s: bf16 operands (8-bit significand) miss the 1e-2 output tolerance on these weights; "
+                "%s: bf16 operands (8-bit significand) can miss the 1e-2 output tolerance on offset weights; "
                 "MOE_PREC_F16_MFMA runs at the same MFMA rate with 3 more bits", fn);
   if (prec == MOE_PREC_F16_MFMA || prec == MOE_PREC_F16_MFMA_DIRECT) {
     if (!grouped)

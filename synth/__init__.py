@@ -14,8 +14,15 @@ transcript, paragraphs on the 128 experts and on the two weight piles;
 "Optimizing a 14.3 GB model for an 8 GB machine", section "Vectorization
 helped when it respected the storage layout").  The value distributions are
 the synthetic recipe of this library (nibbles uniform 0..15, scale
-U(0.005, 0.02), bias U(-0.1, 0.1), router N(0, 0.02^2), norm weight
-N(1, 0.1^2), tokens N(0, 1), Zipf(1.1) expert popularity).
+s ~ U(0.005, 0.02), bias -s * (7.5 + U(-1, 1)), router N(0, 0.02^2), norm
+weight N(1, 0.1^2), tokens N(0, 1), Zipf(1.1) expert popularity).
+
+The bias is the group's minimum, as an affine quantiser stores it, so that
+the dequantised weights s * q + b are centred near zero with a small offset
+per group, like those of a trained model.  (A bias drawn independently of
+the scale leaves every weight with a mean of about +0.09; every expert's
+output then points along one common direction, and after a single MoE layer
+all tokens are nearly parallel and select the same experts.)
 """
 from __future__ import annotations
 
@@ -50,14 +57,16 @@ def blob_payload_sizes(d: int, f: int) -> tuple[int, int]:
 
 
 def expert_blob(d: int, f: int, seed: int, layer: int, expert: int) -> np.ndarray:
-    """One expert blob (uint8): uniform nibbles, then fp16 (scale, bias) pairs."""
+    """One expert blob (uint8): uniform nibbles, then fp16 (scale, bias) pairs
+    with the bias at the group's minimum (weights centred near zero)."""
     nib_bytes, n_pairs = blob_payload_sizes(d, f)
     g = rng(seed, _BLOB, layer, expert)
     out = np.empty(nib_bytes + 4 * n_pairs, dtype=np.uint8)
     out[:nib_bytes] = np.frombuffer(g.bytes(nib_bytes), dtype=np.uint8)
     sb = np.empty((n_pairs, 2), dtype=np.float16)
-    sb[:, 0] = g.uniform(0.005, 0.02, n_pairs).astype(np.float16)
-    sb[:, 1] = g.uniform(-0.1, 0.1, n_pairs).astype(np.float16)
+    scale = g.uniform(0.005, 0.02, n_pairs)
+    sb[:, 0] = scale.astype(np.float16)
+    sb[:, 1] = (-scale * (7.5 + g.uniform(-1.0, 1.0, n_pairs))).astype(np.float16)
     out[nib_bytes:] = sb.reshape(-1).view(np.uint8)
     return out
 

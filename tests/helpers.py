@@ -51,15 +51,25 @@ def check_topk(gpu_idx, oracle_idx, logits64, tau_rel=1e-4):
 
 
 class LayerData:
-    """One seeded MoE layer on the host (blobs, router, norm, bias)."""
+    """One seeded MoE layer on the host (blobs, router, norm, bias).
 
-    def __init__(self, seed: int, layer: int, zipf: bool = True, norm: bool = True, experts=None):
+    offset_weights=True redraws every group's bias as U(-0.1, 0.1),
+    independent of its scale: the weights then carry a mean of about +0.09,
+    so sums over near-constant inputs add up coherently (large activations)."""
+
+    def __init__(self, seed: int, layer: int, zipf: bool = True, norm: bool = True, experts=None,
+                 offset_weights: bool = False):
         self.seed, self.layer = seed, layer
         self.router_w = synth.router_weight(D, E, seed, layer)
         self.bias = synth.zipf_bias(E, seed, layer) if zipf else None
         self.norm_w = synth.norm_weight(D, seed, layer) if norm else None
         ids = range(E) if experts is None else experts
         self.blobs = dict(zip(ids, synth.expert_blobs(D, F, seed, layer, ids)))
+        if offset_weights:
+            nib, n_pairs = synth.blob_payload_sizes(D, F)
+            for e, b in self.blobs.items():
+                pairs = b[nib:].view(np.float16).reshape(n_pairs, 2)
+                pairs[:, 1] = synth.rng(seed, 99, layer, e).uniform(-0.1, 0.1, n_pairs).astype(np.float16)
 
     def blob_of(self, e):
         return self.blobs[e]

@@ -109,11 +109,12 @@ def test_prefill_parity_small(api, d, f, E_, k, T, prec):
 
 @pytest.mark.parametrize("prec", ["f16", "f16direct"])
 def test_prefill_large_activations(api, prec):
-    """Inputs close to a constant vector make every gate/up sum coherent
-    (g, u ~ 260 with these weights), so gelu(g) * u ~ 7e4 exceeds fp16's
-    largest value: the block-scaled intermediates must still match the oracle."""
+    """On weights with a positive mean offset, inputs close to a constant
+    vector make every gate/up sum coherent (g, u ~ 260), so gelu(g) * u ~ 7e4
+    exceeds fp16's largest value: the block-scaled intermediates must still
+    match the oracle."""
     T = 24
-    layer = LayerData(seed=0, layer=1)
+    layer = LayerData(seed=0, layer=1, offset_weights=True)
     arena = torch.from_numpy(np.concatenate([layer.blobs[e] for e in range(E)])).cuda()
     x_np = (1.0 + 0.01 * synth.tokens(T, D, seed=0, stream=5)).astype(np.float32)
     out = run_prefill(api, x_np, layer, arena, D, F, E, K, prec=prec)
