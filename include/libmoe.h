@@ -306,8 +306,8 @@ moe_status moe_cache_destroy(moe_cache* c);
 /* One step of one layer.  sel_host: the k chosen experts (host int32, rank
  * order).  Runs the LRU rule on the host, then enqueues on `side`: a wait for
  * all work already enqueued on `compute` (so no kernel still reads a victim
- * slot), one hipMemcpyAsync per miss (pinned pool -> its slot), and the copy of
- * the layer's new slot table.  hit_mask_dev (device uint8 [k]) receives 1 for
+ * slot), the copy of the layer's new slot table, then one hipMemcpyAsync per
+ * miss (pinned pool -> its slot).  hit_mask_dev (device uint8 [k]) receives 1 for
  * hits and 0 for misses through a copy enqueued on `compute`; hit_mask_host
  * (may be NULL) gets the same on return.  Entries of hit experts keep their
  * slot, so kernels for hits may run on `compute` before moe_cache_wait.
@@ -406,6 +406,17 @@ moe_status moe_slot_stage_device(moe_cache* c, int32_t layer, int32_t step, cons
 moe_status moe_cache_stats(const moe_cache* c, moe_stage_stats* out);
 /* Make `compute` wait until the layer's last staging has landed. */
 moe_status moe_cache_wait(moe_cache* c, int32_t layer, hipStream_t compute);
+/* Finer overlap: make `compute` wait only until the expert at rank `rank`
+ * (0..top_k-1) of the layer's last moe_slot_stage step is in its slot, so that
+ * its kernels can start while later misses are still being copied (the pages
+ * try launching each routed expert as soon as its own read lands and measure
+ * it against hits-first: "Optimizing a 14.3 GB model for an 8 GB machine",
+ * section "MoE needed parallel work, reuse, and coarse overlap").  A hit
+ * returns at once; in MOE_STAGE_COPY mode each miss has its own event (the
+ * slot table is copied before the misses, so it is covered too); in the other
+ * staging modes this waits for the whole step, as moe_cache_wait does.
+ * Errors: MOE_ERR_ARG, MOE_ERR_STATE (device mode), MOE_ERR_HIP. */
+moe_status moe_cache_wait_expert(moe_cache* c, int32_t layer, int32_t rank, hipStream_t compute);
 /* Host copy of a layer's slot table (expert -> slot, -1 absent), int32 [E]. */
 moe_status moe_cache_slot_table(const moe_cache* c, int32_t layer, int32_t* out_host);
 /* Checkpoint: per layer the expert of each slot [L][S] and its stamp [L][S]. */

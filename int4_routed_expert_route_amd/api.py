@@ -64,6 +64,7 @@ _SIGNATURES = {
     "moe_cache_destroy": (ctypes.c_int, [_P]),
     "moe_slot_stage": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _P, _P, ctypes.POINTER(moe_stage_stats)]),
     "moe_cache_wait": (ctypes.c_int, [_P, _I32, _P]),
+    "moe_cache_wait_expert": (ctypes.c_int, [_P, _I32, _I32, _P]),
     "moe_cache_slot_table": (ctypes.c_int, [_P, _I32, _P]),
     "moe_cache_export": (ctypes.c_int, [_P, _P, _P]),
     "moe_cache_import": (ctypes.c_int, [_P, _P, _P]),
@@ -281,6 +282,10 @@ def moe_slot_stage(cache: MoeCache, layer, step, sel_host, side, compute, hit_ma
 
 def moe_cache_wait(cache: MoeCache, layer, compute):
     _check(lib().moe_cache_wait(cache.handle, int(layer), _stream(compute)))
+
+
+def moe_cache_wait_expert(cache: MoeCache, layer, rank, compute):
+    _check(lib().moe_cache_wait_expert(cache.handle, int(layer), int(rank), _stream(compute)))
 
 
 def moe_cache_slot_table(cache: MoeCache, layer, out_host):

@@ -35,6 +35,8 @@ struct moe_cache {
   uint8_t* mask_host = nullptr;      // pinned [L][k]: source of the hit-mask copies
   std::vector<hipEvent_t> staged;    // per layer: last staging on the side stream
   std::vector<hipEvent_t> masked;    // per layer: last hit-mask copy on the compute stream
+  std::vector<hipEvent_t> landed;    // [L][k]: MOE_STAGE_COPY, after the copy of the step's i-th miss
+  std::vector<int32_t> rank_miss;    // [L][k]: miss index of the expert at rank j of the last step, -1 hit
   std::vector<char> staged_used, masked_used;
   std::vector<char> table_stale;     // per layer: a failed step left the device table behind the host state
   hipEvent_t compute_mark = nullptr;
@@ -160,6 +162,8 @@ moe_status moe_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_slots
   c->slot_expert.assign((size_t)n_layers * n_slots, -1);
   c->stamp.assign((size_t)n_layers * n_slots, -1);
   c->staged.assign(n_layers, nullptr);
+  c->landed.assign((size_t)n_layers * top_k, nullptr);
+  c->rank_miss.assign((size_t)n_layers * top_k, -1);
   c->masked.assign(n_layers, nullptr);
   c->staged_used.assign(n_layers, 0);
   c->table_stale.assign(n_layers, 0);
@@ -181,6 +185,12 @@ moe_status moe_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_slots
       moe_cache_destroy(c);
       return st;
     }
+    for (int j = 0; j < top_k; ++j)
+      if ((st = hipcheck(hipEventCreateWithFlags(&c->landed[(size_t)l * top_k + j], hipEventDisableTiming),
+                         "hipEventCreate"))) {
+        moe_cache_destroy(c);
+        return st;
+      }
     rebuild_table(c, l);
   }
   if ((st = hipcheck(hipMemcpy(slot_tables, c->table_host, sizeof(int32_t) * n_layers * n_experts,
@@ -201,6 +211,8 @@ moe_status moe_cache_destroy(moe_cache* c) {
     if (c->staged[l]) { hipEventSynchronize(c->staged[l]); hipEventDestroy(c->staged[l]); }
     if (c->masked[l]) { hipEventSynchronize(c->masked[l]); hipEventDestroy(c->masked[l]); }
   }
+  for (hipEvent_t e : c->landed)
+    if (e) hipEventDestroy(e);
   if (c->compute_mark) hipEventDestroy(c->compute_mark);
   if (c->table_host) hipHostFree(c->table_host);
   if (c->mask_host) hipHostFree(c->mask_host);
@@ -300,18 +312,20 @@ moe_status moe_slot_stage(moe_cache* c, int32_t layer, int32_t step, const int32
     installs.emplace_back(e, victim);
   }
 
-  bool copies_enqueued = false;
+  bool table_enqueued = false, copies_enqueued = false;
   auto failed = [&](moe_status err) {
     // Copies already enqueued may overwrite their victim slots: those slots no
     // longer hold the expert the old state names, so they become empty, on
-    // the host now and on the device at the layer's next step.
-    if (copies_enqueued) {
+    // the host now and on the device at the layer's next step.  The side
+    // stream is drained first: its enqueued table copy reads the pinned table
+    // this rewrites.
+    if (table_enqueued || copies_enqueued) (void)hipStreamSynchronize(side);
+    if (copies_enqueued)
       for (const auto& in : installs) {
         c->slot_expert[(int64_t)layer * c->S + in.second] = -1;
         c->stamp[(int64_t)layer * c->S + in.second] = -1;
       }
-      c->table_stale[layer] = 1;
-    }
+    if (table_enqueued) c->table_stale[layer] = 1;
     rebuild_table(c, layer);
     return err;
   };
@@ -320,6 +334,14 @@ moe_status moe_slot_stage(moe_cache* c, int32_t layer, int32_t step, const int32
       (st = hipcheck(hipStreamWaitEvent(side, c->compute_mark, 0), "hipStreamWaitEvent")))
     return failed(st);
   if (!installs.empty()) {
+    // the layer's new slot table first: a wait on one miss's copy
+    // (moe_cache_wait_expert) then also covers the table that names its slot
+    fill_table(c, layer, se.data());
+    table_enqueued = true;
+    if ((st = hipcheck(hipMemcpyAsync(c->tables_dev + (int64_t)layer * c->E,
+                                      c->table_host + (int64_t)layer * c->E, sizeof(int32_t) * c->E,
+                                      hipMemcpyHostToDevice, side), "hipMemcpyAsync")))
+      return failed(st);
     if (c->staging == MOE_STAGE_KERNEL) {
       // one launch per kMaxStageCopies misses; the GPU reads the pool itself
       for (size_t i0 = 0; i0 < installs.size(); i0 += moe::kMaxStageCopies) {
@@ -355,19 +377,17 @@ moe_status moe_slot_stage(moe_cache* c, int32_t layer, int32_t step, const int32
           return failed(st);
       }
     } else {
-      for (const auto& in : installs) {
+      // one copy per miss, each followed by its own event (moe_cache_wait_expert)
+      for (size_t i = 0; i < installs.size(); ++i) {
+        const auto& in = installs[i];
         const uint8_t* src = c->pool + ((int64_t)layer * c->E + in.first) * c->blob;
         uint8_t* dst = c->arena + ((int64_t)layer * c->S + in.second) * c->stride;
         copies_enqueued = true;
-        if ((st = hipcheck(hipMemcpyAsync(dst, src, c->blob, hipMemcpyHostToDevice, side), "hipMemcpyAsync")))
+        if ((st = hipcheck(hipMemcpyAsync(dst, src, c->blob, hipMemcpyHostToDevice, side), "hipMemcpyAsync")) ||
+            (st = hipcheck(hipEventRecord(c->landed[(size_t)layer * c->k + i], side), "hipEventRecord")))
           return failed(st);
       }
     }
-    fill_table(c, layer, se.data());
-    if ((st = hipcheck(hipMemcpyAsync(c->tables_dev + (int64_t)layer * c->E,
-                                      c->table_host + (int64_t)layer * c->E, sizeof(int32_t) * c->E,
-                                      hipMemcpyHostToDevice, side), "hipMemcpyAsync")))
-      return failed(st);
   }
   if ((st = hipcheck(hipEventRecord(c->staged[layer], side), "hipEventRecord"))) return failed(st);
   c->staged_used[layer] = 1;
@@ -376,6 +396,12 @@ moe_status moe_slot_stage(moe_cache* c, int32_t layer, int32_t step, const int32
   std::copy(sp.begin(), sp.end(), c->stamp.begin() + (int64_t)layer * c->S);
   std::copy(cnt.begin(), cnt.end(), c->count.begin() + (int64_t)layer * c->E);
   if (ring_at) std::copy(ring.begin(), ring.end(), ring_at);
+  for (int j = 0; j < c->k; ++j) {
+    int32_t& m = c->rank_miss[(size_t)layer * c->k + j];
+    m = -1;
+    for (size_t i = 0; i < installs.size(); ++i)
+      if (installs[i].first == sel_host[j]) m = (int32_t)i;
+  }
   ++c->steps_seen[layer];
   c->staged_any = true;
   c->stats.hits += c->k - (int64_t)misses.size();
@@ -589,6 +615,17 @@ moe_status moe_cache_wait(moe_cache* c, int32_t layer, hipStream_t compute) {
   return hipcheck(hipStreamWaitEvent(compute, c->staged[layer], 0), "hipStreamWaitEvent");
 }
 
+moe_status moe_cache_wait_expert(moe_cache* c, int32_t layer, int32_t rank, hipStream_t compute) {
+  if (!c || layer < 0 || layer >= c->L || rank < 0 || rank >= c->k)
+    return cfail(MOE_ERR_ARG, "moe_cache_wait_expert: bad cache, layer or rank");
+  if (c->device) return cfail(MOE_ERR_STATE, "moe_cache_wait_expert: the cache runs on the device");
+  if (!c->staged_used[layer]) return MOE_OK;
+  const int32_t m = c->rank_miss[(size_t)layer * c->k + rank];
+  if (m < 0) return MOE_OK;  // a hit: resident before the step
+  hipEvent_t ev = c->staging == MOE_STAGE_COPY ? c->landed[(size_t)layer * c->k + m] : c->staged[layer];
+  return hipcheck(hipStreamWaitEvent(compute, ev, 0), "hipStreamWaitEvent");
+}
+
 moe_status moe_cache_slot_table(const moe_cache* c, int32_t layer, int32_t* out_host) {
   if (!c || !out_host || layer < 0 || layer >= c->L)
     return cfail(MOE_ERR_ARG, "moe_cache_slot_table: bad argument");
@@ -630,8 +667,12 @@ moe_status moe_cache_import(moe_cache* c, const int32_t* slot_expert_host, const
   std::memcpy(c->slot_expert.data(), slot_expert_host, sizeof(int32_t) * c->slot_expert.size());
   std::memcpy(c->stamp.data(), stamp_host, sizeof(int64_t) * c->stamp.size());
   for (int l = 0; l < c->L; ++l) rebuild_table(c, l);
-  return hipcheck(hipMemcpy(c->tables_dev, c->table_host, sizeof(int32_t) * c->L * c->E,
-                            hipMemcpyHostToDevice), "hipMemcpy");
+  std::fill(c->rank_miss.begin(), c->rank_miss.end(), -1);
+  const moe_status st = hipcheck(hipMemcpy(c->tables_dev, c->table_host, sizeof(int32_t) * c->L * c->E,
+                                           hipMemcpyHostToDevice), "hipMemcpy");
+  // a failed rewrite leaves the device tables to each layer's next step
+  std::fill(c->table_stale.begin(), c->table_stale.end(), st == MOE_OK ? 0 : 1);
+  return st;
 }
 
 }  // extern "C"

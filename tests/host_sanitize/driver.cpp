@@ -434,6 +434,9 @@ void run_cache(int policy, int window, int staging, int streams, bool inject) {
           EXPECT(mask[j] == (resident ? 1 : 0));
         }
       EXPECT_STATUS(moe_cache_wait(c, l, compute), MOE_OK);
+      for (int j = 0; j < r.k; ++j) EXPECT_STATUS(moe_cache_wait_expert(c, l, j, compute), MOE_OK);
+      EXPECT_STATUS(moe_cache_wait_expert(c, l, r.k, compute), MOE_ERR_ARG);
+      EXPECT_STATUS(moe_cache_wait_expert(c, l, -1, compute), MOE_ERR_ARG);
     }
   // the cache refuses a policy or staging change now
   EXPECT_STATUS(moe_cache_set_policy(c, MOE_CACHE_LRU, 0), MOE_ERR_STATE);

@@ -275,6 +275,73 @@ def test_layer_through_cache_matches_oracle(api):
     pool.cache.close()
 
 
+@pytest.mark.parametrize("staging", ["copy", "split3", "kernel"])
+def test_layer_through_cache_fine_overlap(api, staging):
+    """The finer overlap: hits first, then each miss's gate/up as soon as its
+    own copy has landed (moe_cache_wait_expert, misses in the order they are
+    copied: ascending expert id), then down + combine.  Compared with the
+    oracle layer every step, and bit for bit with the hits-first order over the
+    same resident slots."""
+    d, f, E, k, S = 256, 128, 32, 4, 8
+    pool = Pool(api, d, f, E, k, 1, S, seed=19)
+    api.moe_cache_set_staging(pool.cache, *_STAGING[staging])
+    side, compute = torch.cuda.Stream(), torch.cuda.current_stream()
+    rw = synth.router_weight(d, E, 19, 0)
+    nw = synth.norm_weight(d, 19, 0)
+    sels = synth.markov_selections(E, k, 16, 19, 0)
+    dm = pool.dm
+    rw_d, nw_d = torch.from_numpy(rw).cuda(), torch.from_numpy(nw).cuda()
+    ws = lambda c: torch.zeros(max(api.moe_workspace_size(c, 1, dm), 256), dtype=torch.uint8, device="cuda")
+    onehot = torch.zeros(k, 16, dtype=torch.uint8)
+    for j in range(k):
+        onehot[j, j] = 1
+    onehot = onehot.cuda()
+    x_np = synth.tokens(1, d, 19)
+    n_miss_steps = 0
+    for t in range(len(sels)):
+        bias = synth.selection_bias(sels[t], E)
+        x = torch.from_numpy(x_np).cuda()
+        h = torch.empty(1, d, device="cuda")
+        idx = torch.empty(1, k, dtype=torch.int32, device="cuda")
+        w = torch.empty(1, k, device="cuda")
+        api.moe_route(x, nw_d, 1e-6, rw_d, torch.from_numpy(bias).cuda(), 1, dm, h, idx, w, ws(0))
+        sel = idx.cpu().numpy()[0]
+        _, hit_dev, hit_host = _stage(api, pool, 0, t, sel, side, compute)
+        misses = sorted((int(sel[j]), j) for j in range(k) if hit_host[j] == 0)
+        n_miss_steps += bool(misses)
+        act = torch.zeros(k, f, device="cuda")
+        table = pool.tables[0]
+        api.moe_expert_q4_gateup(h, idx, table, S, pool.arena, pool.stride, None, None, hit_dev, 1, 1, dm,
+                                 api.MOE_PREC_FP32, act, ws(2))
+        for _, j in misses:
+            api.moe_cache_wait_expert(pool.cache, 0, j, compute)
+            api.moe_expert_q4_gateup(h, idx, table, S, pool.arena, pool.stride, None, None, onehot[j, :k], 1, 1,
+                                     dm, api.MOE_PREC_FP32, act, ws(2))
+        api.moe_cache_wait(pool.cache, 0, compute)
+        y = torch.empty(1, d, device="cuda")
+        api.moe_expert_q4_down_combine(act, idx, w, table, S, pool.arena, pool.stride, None, None, None, x, 1, dm,
+                                       api.MOE_PREC_FP32, y, ws(3))
+        # hits-first order over the same slots
+        act2 = torch.zeros(k, f, device="cuda")
+        api.moe_expert_q4_gateup(h, idx, table, S, pool.arena, pool.stride, None, None, hit_dev, 1, 1, dm,
+                                 api.MOE_PREC_FP32, act2, ws(2))
+        api.moe_expert_q4_gateup(h, idx, table, S, pool.arena, pool.stride, None, None, hit_dev, 0, 1, dm,
+                                 api.MOE_PREC_FP32, act2, ws(2))
+        y2 = torch.empty(1, d, device="cuda")
+        api.moe_expert_q4_down_combine(act2, idx, w, table, S, pool.arena, pool.stride, None, None, None, x, 1,
+                                       dm, api.MOE_PREC_FP32, y2, ws(3))
+        torch.cuda.synchronize()
+        assert torch.equal(act, act2) and torch.equal(y, y2), t
+        ry, ridx, _, _, lg = orc.moe_layer(x_np, nw, rw, bias, lambda e: pool.blobs[0][e], d, f, k)
+        check_topk(idx.cpu().numpy(), ridx, lg)
+        assert row_rel_err(y.cpu().numpy() - x_np, ry - x_np) < TOL_FP32, t
+        x_np = orc.rms_rescale(y.cpu().numpy().astype(np.float64), 1e-6).astype(np.float32)
+    assert n_miss_steps > 4
+    with pytest.raises(api.MoeError):
+        api.moe_cache_wait_expert(pool.cache, 0, k, compute)
+    pool.cache.close()
+
+
 @pytest.mark.parametrize("policy", ["lru", "lfu"])
 @pytest.mark.parametrize("n_slots,steps", [(8, 60), (16, 40)])
 def test_device_cache_follows_oracle(api, n_slots, steps, policy):
