@@ -635,7 +635,9 @@ def run_batched(args, api, torch):
         "kernel_us": {"route": round(rt_us, 3), "permute": round(pm_us, 3), "gateup": round(gu_us, 3),
                       "down_combine": round(dn_us, 3)},
         "roofline": {
-            "kernel": ("k_q4_gemm gate/up (grouped int4 GEMM on MFMA)" if mfma else
+            "kernel": (("k_q4_small gate/up (int4 GEMM on MFMA for experts with at most 32 pairs: one item per "
+                        "(expert, 64 act columns), two waves on its K halves, weights through per-wave LDS-DMA rings)"
+                        if T <= 32 else "k_q4_gemm + k_q4_small gate/up (grouped int4 GEMM on MFMA)") if mfma else
                        "k_gateup grouped (int4 gate/up dequant-GEMV over experts' token groups)"),
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -129,7 +129,7 @@ __device__ __forceinline__ void reset_counter(uint32_t* counter) {
 template <typename Kernel, typename... Args>
 inline void launch_maybe_timed(Kernel k, int grid, int block, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
                                Args... args) {
-  if (ev0 && ev1)
+  if (ev0 || ev1)  // either may be null: a timed span over several launches
     hipExtLaunchKernelGGL(k, dim3(grid), dim3(block), 0, s, ev0, ev1, 0, args...);
   else
     hipLaunchKernelGGL(k, dim3(grid), dim3(block), 0, s, args...);

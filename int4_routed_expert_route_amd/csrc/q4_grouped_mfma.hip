@@ -168,7 +168,7 @@ struct Plan {
 // Called by all 256 threads; `scratch` (528 ints of LDS) is free until the
 // caller's next barrier.  G = K steps; cap = most items a split launch may have.
 __device__ void plan_items(const int32_t* __restrict__ offsets, int E, int n_pairs, int NT, int G, int cap,
-                           int* scratch, Plan& pl) {
+                           int min_rows, int* scratch, Plan& pl) {
   int4* s_cnt4 = reinterpret_cast<int4*>(scratch);  // [256] counts by expert (-1 past E)
   int* s_cnt = scratch;
   int* s_rcnt = scratch + 256;                      // [256] counts by rank
@@ -180,7 +180,7 @@ __device__ void plan_items(const int32_t* __restrict__ offsets, int E, int n_pai
   if (t < E) {
     a = max(0, min(offsets[t], n_pairs));
     const int b = max(a, min(offsets[t + 1], n_pairs));
-    cnt = b - a;
+    cnt = b - a < min_rows ? 0 : b - a;
   }
   s_cnt[t] = cnt;
   if (t < 9) s_start[t] = -1;
@@ -322,6 +322,7 @@ struct GemmArgs {
   floatx4* part;          // split items' partial accumulators [split_cap][kPartF4]
   uint32_t* cnt;          // arrival counters [split_cap], zero between launches
   int split_cap;          // most items a split launch may have (also capped by the grid)
+  int min_rows;           // experts with fewer pairs are left to the few-pairs kernel
 };
 
 // LDS of one pipeline stage (one K step).
@@ -424,8 +425,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
   const uint32_t sb_rd = lds_addr(&lds[0].sb[wid][n]);
 
   // the work list, in LDS (stage 0 of the pipeline serves as scratch)
-  plan_items(a.offsets, a.E, n_pairs, a.NT, G, min(a.split_cap, (int)gridDim.x), reinterpret_cast<int*>(&lds[0]),
-             s_plan);
+  plan_items(a.offsets, a.E, n_pairs, a.NT, G, min(a.split_cap, (int)gridDim.x), a.min_rows,
+             reinterpret_cast<int*>(&lds[0]), s_plan);
   const int xcd = (int)(blockIdx.x % 8), nper = (int)(gridDim.x / 8);
   const int i_end = __builtin_amdgcn_readfirstlane(s_plan.xstart[xcd + 1]);
   for (int item = __builtin_amdgcn_readfirstlane(s_plan.xstart[xcd]) + (int)(blockIdx.x / 8); item < i_end;
@@ -895,6 +896,365 @@ __global__ __launch_bounds__(256) void k_combine_scaled(const _Float16* __restri
   reinterpret_cast<float4*>(y)[2 * i8 + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
+// ------------------------------------------------------------------ experts with few pairs
+//
+// An expert with at most 32 routed pairs (every expert when T <= 32, the many
+// cold experts of a prefill batch) is bound by streaming its weights, not by
+// the matrix cores.  The work-list GEMM above spends most of such an item on
+// fixed costs (the shared activation tile, barrier-separated K steps, split-K
+// partials through memory), and a workgroup runs one item at a time, so the
+// memory round trips of an item's start (pair ids, slot, exponents) and of its
+// K loop form one serial chain per workgroup.  Here every wave is on its own:
+//  * Work item = (expert, 16 of its pairs, chunk of 64 outputs), one wave:
+//    gate/up the 64 gate and 64 up rows of 64 act columns (one block exponent
+//    group), down 64 output rows; an expert with 17..32 pairs has two items
+//    per chunk, on the same XCD, whose second weight read hits L2 (two row
+//    groups per wave would double the accumulator and operand registers and
+//    spill).  Down: the four waves of a workgroup take four different items,
+//    so many items' round trips overlap, with no barrier after the start.
+//    Gate/up (44 K steps, and few items when T is small): two waves per item,
+//    each half of the K steps, the halves summed through LDS (first plus
+//    second: deterministic).
+//    Items of expert rank r run on XCD r % 8, so an expert's activation rows
+//    are fetched into one L2.
+//  * The wave streams its weights through its own ring of K steps in LDS,
+//    filled by LDS-DMA (buffer_load ... lds) kDepth steps ahead, and takes its
+//    16-bit activation operand (h in slot order, or the block-scaled act) into
+//    registers three steps ahead.
+//  * The MFMA K order inside each 8-column block is the slot order
+//    (0,4,1,5,2,6,3,7) in which dequant8 emits nibbles; the activations are
+//    stored in that order.
+//  * Outputs match the work-list GEMM's formats: gate/up act in slot order
+//    with one exponent per (pair, 64-column group), here shared by the item's
+//    rows; down fp16 pair values with one exponent per (pair, 64-row group).
+constexpr int kSRows = 32;                // most pairs per expert on this path
+constexpr int kSWaves = 4;
+constexpr int kSThreads = kSWaves * kWave;
+constexpr int kSAhead = 3;                // activation steps in flight per wave
+
+struct SmallArgs {
+  const void* a_rows;     // gate/up: h fp16 [T][d] in slot order; down: act values fp16 [T*k][f]
+  int a_bytes;
+  const int8_t* a_exp;    // down: act exponents [T*k][f/64]
+  const int32_t* offsets;
+  const int32_t* sorted_pair;
+  const int32_t* slot_of_expert;
+  int n_slots;
+  const uint8_t* arena;
+  int64_t slot_stride;
+  int T, d, f, E, k;
+  int K;                  // reduction length: d (gate/up) or f (down)
+  int NC;                 // chunks of 64 outputs
+  int64_t off_q0, off_q1, off_sb0, off_sb1;
+  void* out;              // gate/up: act values [T*k][f]; down: pair values [T*k][d] (fp16)
+  int8_t* out_exp;
+};
+
+// One K step of one wave's weights in LDS, per matrix m (gate/up: gate, up;
+// down: one): q[m][h][r] the 16 bytes of chunk 2s + h of tile row r, sb[m][r]
+// the row's (scale, bias) word.  Each is one LDS-DMA load (lane = row).
+template <bool GATEUP>
+struct SStage {
+  uint4 q[GATEUP ? 2 : 1][2][kWave];
+  uint32_t sb[GATEUP ? 2 : 1][kWave];
+};
+template <bool GATEUP>
+struct SDepth {
+  static constexpr int value = GATEUP ? 3 : 6;  // weight steps in flight per wave (>= kSAhead)
+};
+// Per-step activation operand of one lane: the 16 columns this lane
+// multiplies (two MFMA K slices of 8) and (down) the row's exponent for the step.
+struct SAct {
+  u32x4 v[2];
+  int ex;
+};
+
+// A 16-byte LDS-DMA load, kept in a device function: written inside a kernel
+// template's lambda, the call makes the host pass drop the kernel's launch
+// stub without a diagnostic.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, to_lds(dst), 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, void* dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, to_lds(dst), 4, voff, soff, 0, 0);
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(kSThreads, 2) void k_q4_small(SmallArgs a) {
+  constexpr int NM = GATEUP ? 2 : 1;  // matrices
+  constexpr int NG = 4 * NM;          // row groups of 16 per wave (gate/up: 4 gate, then the same 4 up)
+  constexpr int D = SDepth<GATEUP>::value;
+  constexpr int KS = GATEUP ? 2 : 1;        // waves per item (K parts)
+  constexpr int IPW = kSWaves / KS;         // items per workgroup at a time
+  static_assert(D >= kSAhead, "a step's weights must be requested before its activations");
+  typedef Op<_Float16> O;
+  __shared__ SStage<GATEUP> s_ring[kSWaves][D];
+  __shared__ floatx4 s_red[KS > 1 ? IPW : 1][KS > 1 ? NG : 1][kWave];  // the second K part's accumulators
+  __shared__ int s_rank_e[256];             // expert of each small rank
+  __shared__ int s_rank_beg[256];
+  __shared__ int s_rank_cnt[256];
+  __shared__ int s_wave_n[kSWaves];
+  __shared__ int s_xpre[256 / 8 + 1];       // this XCD's experts: 16-pair parts before each
+  const int t = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(t / kWave), lane = t % kWave;
+  const int n = lane % 16, kq = lane / 16;
+  const int G = a.K / kGroup;
+  const int n_pairs = a.T * a.k;
+  typename O::Consts kc{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
+  asm volatile("" : "+v"(kc.m0), "+v"(kc.m4), "+v"(kc.e10), "+v"(kc.e6));
+
+  // experts with 1..32 pairs, ranked by id (E <= 256: one thread each)
+  {
+    int cnt = 0, beg = 0;
+    if (t < a.E) {
+      beg = max(0, min(a.offsets[t], n_pairs));
+      cnt = max(beg, min(a.offsets[t + 1], n_pairs)) - beg;
+    }
+    const bool small = cnt >= 1 && cnt <= kSRows;
+    const uint64_t bal = __ballot(small);
+    const int below = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) s_wave_n[wid] = __builtin_popcountll(bal);
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wid; ++w) base += s_wave_n[w];
+    if (small) {
+      s_rank_e[base + below] = t;
+      s_rank_beg[base + below] = beg;
+      s_rank_cnt[base + below] = cnt;
+    }
+    __syncthreads();
+  }
+  const int n_small = s_wave_n[0] + s_wave_n[1] + s_wave_n[2] + s_wave_n[3];
+  const int xcd = (int)(blockIdx.x % 8), nper = (int)(gridDim.x / 8);
+  const int mine = n_small > xcd ? (n_small - xcd + 7) / 8 : 0;  // experts of this XCD: ranks xcd + 8 i
+  if (t == 0) {
+    int acc_parts = 0;
+    for (int i = 0; i < mine; ++i) {
+      s_xpre[i] = acc_parts;
+      acc_parts += s_rank_cnt[xcd + 8 * i] > 16 ? 2 : 1;
+    }
+    s_xpre[mine] = acc_parts;
+  }
+  __syncthreads();
+  const int n_parts = s_xpre[mine];
+  const __amdgpu_buffer_rsrc_t rsA =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.a_rows), (short)0, a.a_bytes, kRsrcWord3);
+  SStage<GATEUP>* ring = s_ring[wid];
+  // LDS reads of this lane: row group ng = tile rows 16 (ng % 4) + n of matrix ng / 4
+  const int rd_q = (kq >> 1) * (kWave * 16) + n * 16 + (kq & 1) * 8;
+  // activation columns of this lane in a step: those of its two weight words
+  const int colq = 32 * (kq >> 1) + 16 * (kq & 1);
+
+  const int n_items = n_parts * a.NC;
+  const int is = wid / KS, kh = wid % KS;  // item of this wave within the workgroup, its K part
+  // K steps of this wave's part
+  const int s0 = __builtin_amdgcn_readfirstlane(kh * G / KS), s1 = __builtin_amdgcn_readfirstlane((kh + 1) * G / KS);
+  // every wave runs every round (the K parts meet at barriers); a wave without an item skips its work
+  for (int qq = (int)(blockIdx.x / 8); qq * IPW < n_items; qq += nper) {
+    const int q = qq * IPW + is;
+    const bool has = q < n_items;
+    const int u = (has ? q : 0) / a.NC, c = (has ? q : 0) % a.NC;
+    // the expert whose parts hold u: s_xpre[i] <= u < s_xpre[i + 1]
+    int i = 0;
+    for (int lo = 0, hi = mine - 1; lo <= hi;) {
+      const int mid = (lo + hi) / 2;
+      if (s_xpre[mid] <= u) {
+        i = mid;
+        lo = mid + 1;
+      } else {
+        hi = mid - 1;
+      }
+    }
+    const int rank = xcd + 8 * i, part = u - s_xpre[i];
+    const int e = __builtin_amdgcn_readfirstlane(s_rank_e[rank]);
+    const int beg = __builtin_amdgcn_readfirstlane(s_rank_beg[rank] + 16 * part);
+    const int all_rows = s_rank_cnt[rank] - 16 * part;
+    const int rows = __builtin_amdgcn_readfirstlane(all_rows < 16 ? all_rows : 16);
+    // the item's pair ids (lane r holds row r's) and its slot, requested together
+    int pr = -1;
+    if (lane < rows) pr = a.sorted_pair[beg + lane];
+    const int slot = __builtin_amdgcn_readfirstlane(a.slot_of_expert[e]);
+    const bool ok = slot >= 0 && slot < a.n_slots;
+    const uint8_t* blob = a.arena + (ok ? (int64_t)slot * a.slot_stride : 0);
+    const __amdgpu_buffer_rsrc_t rsB =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blob), (short)0, (int)a.slot_stride, kRsrcWord3);
+    const int tile_q = (int)(a.off_q0 + (int64_t)c * (kTileRows * a.K / 2)) + lane * 16;
+    const int tile_sb = (int)(a.off_sb0 + (int64_t)c * (kTileRows * G * 4)) + lane * 4;
+    const int up_q = GATEUP ? (int)(a.off_q1 - a.off_q0) : 0;
+    const int up_sb = GATEUP ? (int)(a.off_sb1 - a.off_sb0) : 0;
+    // weights of step s into ring slot s % D
+    auto dma = [&](int s) {
+      SStage<GATEUP>& st = ring[(s - s0) % D];
+      const int so_q = __builtin_amdgcn_readfirstlane(s * 2048), so_sb = __builtin_amdgcn_readfirstlane(s * 256);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        dma16(rsB, &st.q[m][0][0], tile_q + m * up_q, so_q);
+        dma16(rsB, &st.q[m][1][0], tile_q + m * up_q + 1024, so_q);
+        dma4(rsB, &st.sb[m][0], tile_sb + m * up_sb, so_sb);
+      }
+    };
+    const int pre = s1 - s0 < D ? s1 - s0 : D;
+    if (has)
+      for (int i = 0; i < pre; ++i) dma(s0 + i);
+
+    if (pr < 0 || pr >= n_pairs) pr = -1;
+    // activation row of this lane (MFMA row n)
+    const int prow = __shfl(pr, n, kWave);
+    const int arow = prow < 0 ? 0 : (GATEUP ? prow / a.k : prow);
+    // down: the item's largest act exponent over its rows and K groups
+    int texp = 0;
+    if (!GATEUP) {
+      int m = -128;
+      if (pr >= 0)
+        for (int g = 0; g < G; ++g) m = max(m, (int)a.a_exp[(int64_t)pr * G + g]);
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) m = max(m, __shfl_xor(m, o, kWave));
+      texp = m < -127 ? 0 : m;
+    }
+    // (a lane past the pairs reads at the buffer's end: zeros, no memory access)
+    auto fetch_a = [&](int s, SAct& v) {
+      const bool live = prow >= 0;
+      const int off = live ? (arow * a.K + s * kGroup + colq) * 2 : a.a_bytes;
+      v.v[0] = __builtin_amdgcn_raw_buffer_load_b128(rsA, off, 0, 0);
+      v.v[1] = __builtin_amdgcn_raw_buffer_load_b128(rsA, off + 16, 0, 0);
+      if (!GATEUP) {
+        const int ev = (int)a.a_exp[(int64_t)arow * G + s];
+        v.ex = live ? ev : texp;
+      }
+    };
+    // the activation operand has landed: every load issued before it has too
+    // (loads complete in order), among them the DMA of the same step
+    auto landed = [&](const SAct& v) { asm volatile("" ::"v"(v.v[0]), "v"(v.v[1]) : "memory"); };
+    floatx4 acc[NG];
+#pragma unroll
+    for (int ng = 0; ng < NG; ++ng) acc[ng] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // the A operand of K slice j (8 columns in slot order)
+    auto a_slice = [&](const SAct& v, int j) -> f16x8 {
+      f16x8 h = __builtin_bit_cast(f16x8, v.v[j]);
+      if (!GATEUP) {
+        // a row whose exponent for this group is below the item's: scale down
+        const int dx = v.ex - texp;
+        if (dx != 0) {
+          const _Float16 cf = dx < -24 ? (_Float16)0.0f : (_Float16)exp2i(dx);
+          h = h * cf;
+        }
+      }
+      return h;
+    };
+    // step s: its weights from the ring (the slot is then refilled with step
+    // s + D), the activations of step s + kSAhead, dequant and MFMAs
+    auto one = [&](int s, const SAct& vc, SAct& vf) {
+      landed(vc);
+      const SStage<GATEUP>& st = ring[(s - s0) % D];
+      u32x2 qv[NG];
+      uint32_t sbv[NG];
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng) {
+        const int m = ng / 4, rr = 16 * (ng % 4);
+        qv[ng] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(&st.q[m][0][0]) + rd_q + rr * 16);
+        sbv[ng] = st.sb[m][rr + n];
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(qv[0]), "+v"(sbv[0])::"memory");
+      // the weights of step s + D, then the activations of step s + kSAhead
+      // (the latter unconditional: no half-defined buffer)
+      if (s + D < s1) dma(s + D);
+      fetch_a(s + kSAhead < s1 ? s + kSAhead : s1 - 1, vf);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const f16x8 av = a_slice(vc, j);
+#pragma unroll
+        for (int ng = 0; ng < NG; ++ng) {
+          f16x2 s2, b2;
+          O::split_sb(sbv[ng], s2, b2);
+          const f16x8 fb = __builtin_bit_cast(f16x8, O::dequant8(j == 0 ? qv[ng].x : qv[ng].y, s2, b2, kc));
+          acc[ng] = O::mfma(av, fb, acc[ng]);
+        }
+      }
+    };
+    if (has && s0 < s1) {
+      SAct v0, v1, v2, v3;
+      fetch_a(s0, v0);
+      fetch_a(s0 + 1 < s1 ? s0 + 1 : s1 - 1, v1);
+      fetch_a(s0 + 2 < s1 ? s0 + 2 : s1 - 1, v2);
+      for (int s = s0; s < s1; s += 4) {
+        one(s, v0, v3);
+        if (s + 1 >= s1) break;
+        one(s + 1, v1, v0);
+        if (s + 2 >= s1) break;
+        one(s + 2, v2, v1);
+        if (s + 3 >= s1) break;
+        one(s + 3, v3, v2);
+      }
+    }
+    if (KS > 1) {
+      // the second K part's accumulators join the first's
+      if (has && kh == 1)
+#pragma unroll
+        for (int ng = 0; ng < NG; ++ng) s_red[is][ng][lane] = acc[ng];
+      __syncthreads();
+      if (has && kh == 0)
+#pragma unroll
+        for (int ng = 0; ng < NG; ++ng) acc[ng] += s_red[is][ng][lane];
+      __syncthreads();  // s_red is free for the next round
+    }
+    if (!has || kh != 0) continue;
+    if (GATEUP) {
+      // acc[g][i] (g = 0..3) = C[pair row kq*4 + i][gate row 16 g + n], acc[g + 4][i] the
+      // up row: act column 64 c + 16 g + n; act overwrites the gate accumulators.  The
+      // exponent is the part's; the act of an expert's two parts may differ in it.
+      float m = 0.0f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool live = kq * 4 + i < rows;
+          const float x = live ? (ok ? gelu_tanh_act16(acc[g][i]) * acc[g + 4][i] : f32_nan()) : 0.0f;
+          acc[g][i] = x;
+          if (live) m = fmaxf(m, fabsf(x));
+        }
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+      const int ex = block_exp(m);
+      const float sc = exp2i(-ex);
+      const int Gf = a.f / kGroup;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = kq * 4 + i;
+        const int p = __shfl(pr, r, kWave);
+        if (r >= rows || p < 0) continue;
+        _Float16* dst = reinterpret_cast<_Float16*>(a.out) + (int64_t)p * a.f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = c * kGroup + g * 16 + n;  // stored at its slot position
+          dst[(col & ~7) + (col & 3) * 2 + ((col >> 2) & 1)] = (_Float16)(acc[g][i] * sc);
+        }
+        if (n == 0) a.out_exp[(int64_t)p * Gf + c] = (int8_t)ex;
+      }
+    } else {
+      // acc[ng][i] = C[pair row kq*4 + i][output row 64 c + 16 ng + n] * 2^-texp;
+      // one exponent per (pair row, 64 output rows)
+      const int Gd = a.d / kGroup;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float m = 0.0f;
+#pragma unroll
+        for (int ng = 0; ng < NG; ++ng) m = fmaxf(m, fabsf(acc[ng][i]));
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+        const int r = kq * 4 + i;
+        const int p = __shfl(pr, r, kWave);
+        if (r >= rows || p < 0) continue;
+        const int ex = block_exp(m);
+        const float sc = exp2i(-ex);
+        _Float16* dst = reinterpret_cast<_Float16*>(a.out) + (int64_t)p * a.d + c * kGroup + n;
+#pragma unroll
+        for (int ng = 0; ng < NG; ++ng) dst[ng * 16] = ok ? (_Float16)(acc[ng][i] * sc) : (_Float16)f32_nan();
+        if (n == 0) a.out_exp[(int64_t)p * Gd + c] = (int8_t)max(-127, min(127, ex + texp));
+      }
+    }
+  }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ host side
@@ -940,10 +1300,42 @@ static int persistent_grid(int items) {
 }
 
 template <typename ET, bool GATEUP, bool DIRECT = false>
-static void launch_gemm(const GemmArgs& a, int items, hipStream_t s, int call) {
-  hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  take_profile_events(call, &ev0, &ev1);
+static void launch_gemm(const GemmArgs& a, int items, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   launch_maybe_timed(k_q4_gemm<ET, GATEUP, DIRECT>, persistent_grid(items), kThreads, s, ev0, ev1, a);
+}
+
+// The few-pairs kernel's arguments from the work-list GEMM's.
+static SmallArgs small_args(const GemmArgs& g, const void* a_rows, int a_bytes, int NC) {
+  SmallArgs a{};
+  a.a_rows = a_rows;
+  a.a_bytes = a_bytes;
+  a.a_exp = g.a_exp;
+  a.offsets = g.offsets;
+  a.sorted_pair = g.sorted_pair;
+  a.slot_of_expert = g.slot_of_expert;
+  a.n_slots = g.n_slots;
+  a.arena = g.arena;
+  a.slot_stride = g.slot_stride;
+  a.T = g.T; a.d = g.d; a.f = g.f; a.E = g.E; a.k = g.k;
+  a.K = g.K;
+  a.NC = NC;
+  a.off_q0 = g.off_q0; a.off_q1 = g.off_q1; a.off_sb0 = g.off_sb0; a.off_sb1 = g.off_sb1;
+  a.out = g.out;
+  a.out_exp = g.out_exp;
+  return a;
+}
+
+// Batches of at most kSmallPathT tokens: experts with at most kSRows pairs go
+// to k_q4_small, the others to the work-list GEMM (with T <= kSRows no expert
+// has more, and the work-list GEMM is skipped).  Larger batches run every
+// expert through the work-list GEMM: at 2048 prefill tokens moving the
+// few-pairs experts to k_q4_small measured 4% slower for the step.
+constexpr int kSmallPathT = 64;
+template <bool GATEUP>
+static void launch_small(const SmallArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  const int items = std::min(a.E, a.T * a.k) * a.NC;
+  const int per_wg = GATEUP ? kSWaves / 2 : kSWaves;  // items a workgroup runs at a time
+  launch_maybe_timed(k_q4_small<GATEUP>, persistent_grid((items + per_wg - 1) / per_wg), kSThreads, s, ev0, ev1, a);
 }
 
 hipError_t launch_gateup_mfma(bool direct, const float* h, const int32_t* offsets, const int32_t* sorted_pair,
@@ -954,6 +1346,7 @@ hipError_t launch_gateup_mfma(bool direct, const float* h, const int32_t* offset
   const int items = max_items(T, k, E, NT);
   char* rest = reinterpret_cast<char*>(ws) + kCntBytes;
   const int64_t n8 = (int64_t)T * d / 8;
+  const bool use_small = T <= kSmallPathT, only_small = T <= kSRows;
   hipLaunchKernelGGL(k_h_to_slots<_Float16>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, h, n8,
                      reinterpret_cast<_Float16*>(rest));
   GemmArgs a{};
@@ -976,8 +1369,14 @@ hipError_t launch_gateup_mfma(bool direct, const float* h, const int32_t* offset
   a.cnt = reinterpret_cast<uint32_t*>(ws);
   a.part = reinterpret_cast<floatx4*>(rest + gateup_body_bytes(T, d));
   a.split_cap = split_item_cap(T, k, E, NT);
-  if (direct) launch_gemm<_Float16, true, true>(a, items, s, MOE_CALL_GATEUP);
-  else launch_gemm<_Float16, true>(a, items, s, MOE_CALL_GATEUP);
+  a.min_rows = use_small ? kSRows + 1 : 1;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  take_profile_events(MOE_CALL_GATEUP, &ev0, &ev1);
+  if (!only_small) {
+    if (direct) launch_gemm<_Float16, true, true>(a, items, s, ev0, use_small ? nullptr : ev1);
+    else launch_gemm<_Float16, true>(a, items, s, ev0, use_small ? nullptr : ev1);
+  }
+  if (use_small) launch_small<true>(small_args(a, rest, a.a_bytes, f / kGroup), s, only_small ? ev0 : nullptr, ev1);
   return hipGetLastError();
 }
 
@@ -1010,8 +1409,16 @@ hipError_t launch_down_mfma(bool direct, const void* act_in, const int32_t* offs
   a.cnt = reinterpret_cast<uint32_t*>(ws);
   a.part = reinterpret_cast<floatx4*>(rest + down_body_bytes(T, d, k));
   a.split_cap = split_item_cap(T, k, E, NT);
-  if (direct) launch_gemm<_Float16, false, true>(a, items, s, MOE_CALL_DOWN_COMBINE);
-  else launch_gemm<_Float16, false>(a, items, s, MOE_CALL_DOWN_COMBINE);
+  const bool use_small = T <= kSmallPathT, only_small = T <= kSRows;
+  a.min_rows = use_small ? kSRows + 1 : 1;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  take_profile_events(MOE_CALL_DOWN_COMBINE, &ev0, &ev1);
+  if (!only_small) {
+    if (direct) launch_gemm<_Float16, false, true>(a, items, s, ev0, use_small ? nullptr : ev1);
+    else launch_gemm<_Float16, false>(a, items, s, ev0, use_small ? nullptr : ev1);
+  }
+  if (use_small)
+    launch_small<false>(small_args(a, act_in, a.a_bytes, d / kGroup), s, only_small ? ev0 : nullptr, ev1);
   const int64_t n8 = (int64_t)T * d / 8;
   hipLaunchKernelGGL(k_combine_scaled, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, pair_val, pair_exp,
                      topk_w, residual, y, T, d, k);

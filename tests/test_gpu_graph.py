@@ -88,10 +88,12 @@ def test_fused_decode_graph_replays(api):
     api.moe_decode_check(ws)
 
 
-@pytest.mark.parametrize("T", [1, 32])
+@pytest.mark.parametrize("T", [1, 32, 200])
 def test_split_k_grouped_gemm_graph_replays(api, T):
-    """The 32-token batched-decode shape (gate/up split along K) and a single
-    token, captured as gate/up + down-combine."""
+    """The grouped GEMMs captured as gate/up + down-combine: a single token
+    and the 32-token batched-decode shape (the few-pairs kernel, K parts
+    summed through LDS), and 200 tokens (the work-list GEMM, whose items of
+    few pairs are split along K and summed through memory)."""
     d, f, E, k = 2816, 704, 128, 8
     dm = api.dims(d, f, E, k)
     stride = api.moe_expert_blob_bytes(dm)

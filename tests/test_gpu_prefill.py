@@ -219,13 +219,16 @@ def test_prefill_direct_loads_match_staged_tiles(api, d, f, E_, k, T):
     assert np.array_equal(_np(a["y"]), _np(b["y"]))
 
 
-@pytest.mark.parametrize("d,f,E_,k,T", [(2816, 704, 128, 8, 1), (2816, 704, 128, 8, 32), (1600, 768, 16, 4, 40)])
+@pytest.mark.parametrize("d,f,E_,k,T", [(2816, 704, 128, 8, 1), (2816, 704, 128, 8, 32), (1600, 768, 16, 4, 40),
+                                        (2816, 704, 128, 8, 200), (1600, 768, 16, 4, 120)])
 def test_split_k_deterministic_and_counters_reset(api, d, f, E_, k, T):
-    """Items split along K give the same bits on every call, whichever K range
-    arrives last (the partials are summed in range order), and each call
-    leaves the workspace's arrival counters at zero, so one workspace serves
-    call after call.  The 32-token case is the batched-decode shape; the last
-    splits the down GEMM too."""
+    """Every call gives the same bits and leaves the workspace's arrival
+    counters at zero, so one workspace serves call after call.  Up to 64
+    tokens the experts with few pairs run on the few-pairs kernel (K parts
+    summed through LDS in a fixed order; 32 tokens is the batched-decode
+    shape); beyond, the work-list GEMM splits their items along K and the last
+    K range to arrive sums the partials in range order (the last case splits
+    the down GEMM too)."""
     layer = SmallLayer(d, f, E_, seed=12)
     arena = torch.from_numpy(np.concatenate([layer.blobs[e] for e in range(E_)])).cuda()
     x_np = synth.tokens(T, d, seed=12, stream=T)
