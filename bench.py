@@ -53,7 +53,16 @@ CSRC = os.path.join(ROOT, "int4_routed_expert_route_amd", "csrc")
 # (scaled by a 1 GiB copy's readings), keyed by the workload, for the kernel
 # sources and the input recipe with this fingerprint (paths from the repository
 # root); reported as null once either differs.
-TRAFFIC = {}
+TRAFFIC = {
+    "decode": {"sources": ('int4_routed_expert_route_amd/csrc/q4_gemv.hip', 'int4_routed_expert_route_amd/csrc/q4_lane.h', 'int4_routed_expert_route_amd/csrc/common.h', 'synth/__init__.py'),
+              "sha256_16": "8e70e53b26418e64", "fetch_bytes": 18095155, "write_bytes": 22528},
+    "decode_fused": {"sources": ('int4_routed_expert_route_amd/csrc/decode_fused.hip', 'int4_routed_expert_route_amd/csrc/q4_lane.h', 'int4_routed_expert_route_amd/csrc/common.h', 'synth/__init__.py'),
+                    "sha256_16": "623ed829d9719102", "fetch_bytes": 954423481, "write_bytes": 8174496},
+    "prefill": {"sources": ('int4_routed_expert_route_amd/csrc/q4_grouped_mfma.hip', 'int4_routed_expert_route_amd/csrc/common.h', 'synth/__init__.py'),
+               "sha256_16": "1d4db5f38f10c610", "fetch_bytes": 431803137, "write_bytes": 23955408},
+    "batched_f16": {"sources": ('int4_routed_expert_route_amd/csrc/q4_grouped_mfma.hip', 'int4_routed_expert_route_amd/csrc/common.h', 'synth/__init__.py'),
+                   "sha256_16": "1d4db5f38f10c610", "fetch_bytes": 100029678, "write_bytes": 369616},
+}
 
 
 def log(msg):
