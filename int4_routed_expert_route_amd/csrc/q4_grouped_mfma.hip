@@ -50,7 +50,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 128;               // pair rows per work item
-constexpr int kItemFixedCost = 32;    // schedule cost of an item beyond its row groups of 16
+constexpr int kItemFixedCost = 8;     // schedule cost of an item beyond its row groups of 16
 constexpr int WN = 64;                // weight rows per wave
 constexpr int kWaves = 4;             // waves per workgroup, side by side along N
 constexpr int BN = WN * kWaves;       // weight rows per workgroup
@@ -139,24 +139,27 @@ __device__ __forceinline__ float exp2i(int e) { return __builtin_bit_cast(float,
 
 // ------------------------------------------------------------------ schedule
 
-// Work list: experts by pair count (descending, ties by id); per expert, M tile
-// by M tile, its N tiles in order (the N tiles of one M tile share the
-// activation rows; the expert's weights stay in L2 across its M tiles).
-// Item = (expert, m0, n tile).  The list is cut into 8 stretches of about
-// equal cost, one per XCD; an item costs kItemFixedCost + (row groups of 16 in
-// its M tile).  Most of a K step's time does not depend on the rows (the
-// dequant, the step barrier, the DMA round trip) and the prologue and epilogue
-// are per item: timed per item, a one-group tile takes 0.7-0.85 of a full
-// one.  32 fixed units (0.83) measured best (4: 173.7k, 16: 184.0k, 32: 184.4k
-// prefill tokens/s); what remains is the whole-item granularity, about 2
-// items per workgroup per launch.
+// Work list: experts by size class (row groups of 16, descending, capped at
+// kClasses - 1; ties by id); per expert, M tile by M tile, its N tiles in order
+// (the N tiles of one M tile share the activation rows; the expert's weights
+// stay in L2 across its M tiles).  Item = (expert, m0, n tile).  The list is
+// cut into 8 stretches of about equal cost, one per XCD; an item costs
+// kItemFixedCost + (row groups of 16 in its M tile).  Timed per item on the
+// 2048-token layer, a K step costs about the same whatever the rows (the
+// dequant, the step barrier, the DMA round trip), so a one-group tile takes a
+// bit over half as long as a full one: about 7 (gate/up) to 9 (down) row
+// groups of fixed cost.  Swept on the prefill step: 4 fixed units 147k, 6:
+// 156k, 8: 157k, 10: 156k, 16: 155k, 32: 149k tokens/s.  What remains is the
+// whole-item granularity, about 3 items per workgroup per launch.
 //
 // Every workgroup of the GEMM derives the same list from the expert offsets
-// at its start (a separate scheduling launch cost more than this): ranks by
-// counting, block scans of items and cost over the ranks, and each XCD
-// boundary in closed form from the rank whose cost range holds it.  Items are
-// not stored: an item index maps to its rank by binary search over the ranks'
-// first items.
+// at its start (a separate scheduling launch cost more than this): ranks from
+// wave ballots over the size classes, block scans of items and cost over the
+// ranks, and each XCD boundary in closed form from the rank whose cost range
+// holds it (3.7 us from launch to the first item, against 7.7 us with ranks by
+// counting).  Items are not stored: an item index maps to its rank by binary
+// search over the ranks' first items.
+constexpr int kClasses = 32;
 struct Plan {
   int ecnt[256];    // expert of each rank | its pair count << 8 (pair counts < 2^24)
   int beg[256];     // each rank's first position in sorted_pair (offsets, clamped)
@@ -165,45 +168,55 @@ struct Plan {
   int split;        // K ranges of each item of at most kSplitRows rows (1: no split)
 };
 
-// Called by all 256 threads; `scratch` (528 ints of LDS) is free until the
+// Called by all 256 threads; `scratch` (176 ints of LDS) is free until the
 // caller's next barrier.  G = K steps; cap = most items a split launch may have.
 __device__ void plan_items(const int32_t* __restrict__ offsets, int E, int n_pairs, int NT, int G, int cap,
                            int min_rows, int* scratch, Plan& pl) {
-  int4* s_cnt4 = reinterpret_cast<int4*>(scratch);  // [256] counts by expert (-1 past E)
-  int* s_cnt = scratch;
-  int* s_rcnt = scratch + 256;                      // [256] counts by rank
-  int* s_wsum = scratch + 512;                      // [2][4] per-wave scan totals
-  int* s_red = scratch + 520;                       // [2][4] per-wave item totals
+  int* s_wc = scratch;             // [4][kClasses] experts of each class, per wave
+  int* s_above = scratch + 128;    // [kClasses] experts in larger classes
+  int* s_red = scratch + 160;      // [2][4] per-wave item totals
+  int* s_wsum = scratch + 168;     // [2][4] per-wave scan totals
   int* s_start = pl.xstart;
   const int t = threadIdx.x, lane = t % kWave, wv = t / kWave;
-  int cnt = -1, a = 0;
+  int cnt = 0, a = 0, cls = -1;
   if (t < E) {
     a = max(0, min(offsets[t], n_pairs));
     const int b = max(a, min(offsets[t + 1], n_pairs));
     cnt = b - a < min_rows ? 0 : b - a;
+    cls = kClasses - 1 - min(kClasses - 1, (cnt + 15) / 16);  // 0 = largest
   }
-  s_cnt[t] = cnt;
   if (t < 9) s_start[t] = -1;
-  __syncthreads();
-  if (t < E) {
-    int rank = 0;
+  // rank = experts of earlier classes + experts of this class with smaller ids
+  const uint64_t below = (1ull << lane) - 1ull;
+  int pos = 0;
 #pragma unroll 8
-    for (int e4 = 0; e4 < (E + 3) / 4; ++e4) {
-      const int4 c = s_cnt4[e4];
-      const int e = 4 * e4;
-      rank += (c.x > cnt || (c.x == cnt && e < t)) ? 1 : 0;
-      rank += (c.y > cnt || (c.y == cnt && e + 1 < t)) ? 1 : 0;
-      rank += (c.z > cnt || (c.z == cnt && e + 2 < t)) ? 1 : 0;
-      rank += (c.w > cnt || (c.w == cnt && e + 3 < t)) ? 1 : 0;
+  for (int c = 0; c < kClasses; ++c) {
+    const uint64_t m = __ballot(cls == c);
+    if (cls == c) pos = __popcll(m & below);
+    if (lane == 0) s_wc[wv * kClasses + c] = __popcll(m);
+  }
+  __syncthreads();
+  if (t < kClasses) {
+    const int n = s_wc[t] + s_wc[kClasses + t] + s_wc[2 * kClasses + t] + s_wc[3 * kClasses + t];
+    int inc = n;  // inclusive prefix over classes 0..t
+#pragma unroll
+    for (int o = 1; o < kClasses; o <<= 1) {
+      const int v = __shfl_up(inc, o, kClasses);
+      if (t >= o) inc += v;
     }
+    s_above[t] = inc - n;
+  }
+  __syncthreads();
+  if (cls >= 0) {
+    int rank = s_above[cls] + pos;
+    for (int w = 0; w < wv; ++w) rank += s_wc[w * kClasses + cls];
     pl.ecnt[rank] = t | (cnt << 8);
     pl.beg[rank] = a;
-    s_rcnt[rank] = cnt;
   }
   __syncthreads();
   // rank r = t: its items (M tiles x NT) and their cost
   const int r = t;
-  const int rc = r < E ? s_rcnt[r] : 0;
+  const int rc = r < E ? pl.ecnt[r] >> 8 : 0;
   const int mt = (rc + BM - 1) / BM;
   // the split: as many K ranges as the workgroups left idle by the unsplit
   // items allow, the same for every small item
@@ -243,32 +256,29 @@ __device__ void plan_items(const int32_t* __restrict__ offsets, int E, int n_pai
   }
   __syncthreads();
   int base_i = inc_i - n_items, base_c = inc_c - cost, W = 0, total = 0;
+#pragma unroll
   for (int w = 0; w < 4; ++w) {
+    const int si = s_wsum[w], sc = s_wsum[4 + w];
     if (w < wv) {
-      base_i += s_wsum[w];
-      base_c += s_wsum[4 + w];
+      base_i += si;
+      base_c += sc;
     }
-    W += s_wsum[w];
-    total += s_wsum[4 + w];
+    W += si;
+    total += sc;
   }
   pl.ibase[r] = base_i;
   // XCD x starts at the first item whose cost before it is >= ceil(x * total / 8)
   // (item i belongs to XCD min(7, cost_before_i * 8 / total)); the rank whose
-  // cost range holds that target finds the item tile by tile
+  // cost range holds that target finds the item: its full tiles' items come
+  // first, c_full each, then the tail tile's, c_tail each
   if (n_items > 0) {
+    const int fc = full * ipt * c_full;
     for (int x = 1; x < 8; ++x) {
       const int target = (x * total + 7) / 8;
       if (target < base_c || target >= base_c + cost) continue;
-      int pre = base_c, li = n_items;
-      for (int m = 0; m < mt; ++m) {
-        const int c = (m < full) ? c_full : c_tail;
-        if (pre + ipt * c > target) {
-          li = m * ipt + (target - pre + c - 1) / c;
-          break;
-        }
-        pre += ipt * c;
-      }
-      s_start[x] = base_i + li;
+      const int off = target - base_c;
+      const int li = off < fc ? (off + c_full - 1) / c_full : full * ipt + (off - fc + c_tail - 1) / c_tail;
+      s_start[x] = base_i + min(li, n_items);
     }
   }
   if (t == 0) {
@@ -276,12 +286,17 @@ __device__ void plan_items(const int32_t* __restrict__ offsets, int E, int n_pai
     pl.split = S;
   }
   __syncthreads();
-  if (t == 0) {
-    int next = W;  // XCDs past the last boundary get empty stretches
-    for (int x = 8; x >= 0; --x) {
-      if (x == 8 || s_start[x] < 0) s_start[x] = next;
-      next = s_start[x];
+  if (t < kWave) {
+    // XCDs past the last boundary get empty stretches: each unset start takes
+    // the next set one (W past the last); the set starts rise with x
+    int v = W;
+    if (t < 8 && s_start[t] >= 0) v = s_start[t];
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int u = __shfl_down(v, o, 16);
+      if (t + o < 16) v = min(v, u);
     }
+    if (t < 9) s_start[t] = v;
   }
   __syncthreads();
 }
@@ -358,34 +373,53 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
 }
 
-// LDS reads the compiler does not see: it would otherwise wait for every
-// outstanding DMA before each of them.  lds_wait() completes them and ties the
-// registers it names to that point.
+// The work-list GEMM's LDS-DMA is written as asm, so that the compiler does not
+// see it: it would otherwise make every later LDS read wait for every DMA in
+// flight (it cannot tell the stages apart), which empties the pipeline.  Each
+// K step waits for its own DMA explicitly (vm_wait_steps, then the barrier),
+// and the LDS reads are ordinary loads whose waits the compiler places.  The
+// asm sets M0 to the LDS address itself; nothing else in the kernel uses M0.
+// rs: buffer resource words (SGPRs); lane l's bytes land at lds + l * size.
+__device__ __forceinline__ void dma_lds16(u32x4 rs, uint32_t lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rs), "s"(soff)
+               : "memory");
+}
+__device__ __forceinline__ void dma_lds4(u32x4 rs, uint32_t lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rs), "s"(soff)
+               : "memory");
+}
+// Raw buffer resource words for `bytes` bytes at p (stride 0, raw 32-bit data).
+__device__ __forceinline__ u32x4 rsrc_words(const void* p, int bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)p;
+  u32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xFFFFu);
+  r.z = __builtin_amdgcn_readfirstlane((uint32_t)bytes);
+  r.w = (uint32_t)kRsrcWord3;
+  return r;
+}
+// Keeps the compiler from moving LDS reads above a step barrier.
+__device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
+
+template <typename T>
+__device__ __forceinline__ T lds_load(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) T*)(uintptr_t)addr;
+}
 template <int OFF>
 __device__ __forceinline__ u32x4 lds_read128(uint32_t addr) {
-  u32x4 v;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
-  return v;
+  return lds_load<u32x4>(addr + OFF);
 }
 template <int OFF>
 __device__ __forceinline__ u32x2 lds_read64(uint32_t addr) {
-  u32x2 v;
-  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
-  return v;
+  return lds_load<u32x2>(addr + OFF);
 }
 template <int OFF>
 __device__ __forceinline__ uint32_t lds_read32(uint32_t addr) {
-  uint32_t v;
-  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
-  return v;
-}
-__device__ __forceinline__ void lds_wait(u32x4 (&r)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
-}
-__device__ __forceinline__ void lds_wait(u32x4 (&r)[4], u32x2 (&q)[4], uint32_t (&sb)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]),
-                 "+v"(sb[0]), "+v"(sb[1]), "+v"(sb[2]), "+v"(sb[3]));
+  return lds_load<uint32_t>(addr + OFF);
 }
 
 // GATEUP: wave w of N tile nt owns act columns nt*128 + 32w .. +31 (gate rows
@@ -413,8 +447,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
   const int G = a.K / kGroup;               // K steps
   const int n_pairs = a.T * a.k;
   const int Nrows = GATEUP ? a.f : a.d;
-  const __amdgpu_buffer_rsrc_t rsA =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.a_rows), (short)0, a.a_bytes, kRsrcWord3);
+  const u32x4 rwA = rsrc_words(a.a_rows, a.a_bytes);
   typename O::Consts kc{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
   asm volatile("" : "+v"(kc.m0), "+v"(kc.m4), "+v"(kc.e10), "+v"(kc.e6));  // in VGPRs
   // per-lane LDS addresses inside stage 0 (stage st adds st * sizeof(StageLds))
@@ -503,21 +536,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
       sb_off = (int)((up ? a.off_sb1 : a.off_sb0) + (int64_t)(r / kTileRows) * (kTileRows * G * 4) +
                      (r % kTileRows) * 4);
     }
+    const u32x4 rwB = rsrc_words(blob, (int)a.slot_stride);
     auto issue = [&](int s, int st) {
       const int so_a = __builtin_amdgcn_readfirstlane(s * BK * 2);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (i < n_a)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, to_lds(&lds[st].a[(i * 4 + wid) * kWave]), 16, a_off[i],
-                                                   so_a, 0, 0);
+          dma_lds16(rwA, __builtin_amdgcn_readfirstlane(lds_addr(&lds[st].a[(i * 4 + wid) * kWave])), a_off[i], so_a);
       if (DIRECT) return;
       const int so_q = __builtin_amdgcn_readfirstlane(s * 2048);
 #pragma unroll
       for (int c = 0; c < 2; ++c)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, to_lds(&lds[st].q[wid][c][0]), 16, q_off + c * 1024, so_q, 0,
-                                                 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, to_lds(&lds[st].sb[wid][0]), 4, sb_off,
-                                               __builtin_amdgcn_readfirstlane(s * 256), 0, 0);
+        dma_lds16(rwB, __builtin_amdgcn_readfirstlane(lds_addr(&lds[st].q[wid][c][0])), q_off + c * 1024, so_q);
+      dma_lds4(rwB, __builtin_amdgcn_readfirstlane(lds_addr(&lds[st].sb[wid][0])), sb_off,
+               __builtin_amdgcn_readfirstlane(s * 256));
     };
     // DIRECT: lane (n, kq) reads, for row group ng, 8 bytes (kq & 1) of chunk
     // 2s + kq/2 of wave row 16 ng + n, and that row's (scale, bias) word.
@@ -648,7 +680,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
           qv[ng] = dq[ng];
           sbv[ng] = dsb[ng];
         }
-        lds_wait(fx);
       } else {
         qv[0] = lds_read64<0>(q_rd + so);
         qv[1] = lds_read64<256>(q_rd + so);
@@ -658,7 +689,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
         sbv[1] = lds_read32<64>(sb_rd + so);
         sbv[2] = lds_read32<128>(sb_rd + so);
         sbv[3] = lds_read32<192>(sb_rd + so);
-        lds_wait(fx, qv, sbv);
       }
       if (kScaledA) {
         // this group's activations carry 2^(s_gexp[s] - tile_exp) <= 1: fold it into s and b
@@ -679,20 +709,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
       if (half1) read_half(fy, a_rd0 + so + 8192);  // j = 0, rows 64..127
       mfma_half(fx, fb, 0);
       if (half1) {
-        lds_wait(fy);
         read_half(fx, a_rd1 + so);  // j = 1, rows 0..63
         mfma_half(fy, fb, 1);
       } else {
         read_half(fx, a_rd1 + so);
       }
       dequant(fb, qv, s2, b2, 1);
-      lds_wait(fx);
       if (half1) read_half(fy, a_rd1 + so + 8192);  // j = 1, rows 64..127
       mfma_half(fx, fb, 0);
-      if (half1) {
-        lds_wait(fy);
-        mfma_half(fy, fb, 1);
-      }
+      if (half1) mfma_half(fy, fb, 1);
     };
     for (int s = s0; s < s1; ++s) {
       const int st = (s - s0) % kStages;
@@ -713,6 +738,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // and its LDS accesses (lgkmcnt 0)
       __builtin_amdgcn_s_barrier();        // ... and every other wave's
+      lds_fence();
       if (fix_rows) {
         fix_step(s, st);
         __syncthreads();
