@@ -995,15 +995,6 @@ struct SAct {
   int ex;
 };
 
-// A 16-byte LDS-DMA load, kept in a device function: written inside a kernel
-// template's lambda, the call makes the host pass drop the kernel's launch
-// stub without a diagnostic.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* dst, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, to_lds(dst), 16, voff, soff, 0, 0);
-}
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, void* dst, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, to_lds(dst), 4, voff, soff, 0, 0);
-}
 
 template <bool GATEUP>
 __global__ __launch_bounds__(kSThreads, 2) void k_q4_small(SmallArgs a) {
@@ -1102,21 +1093,21 @@ __global__ __launch_bounds__(kSThreads, 2) void k_q4_small(SmallArgs a) {
     const int slot = __builtin_amdgcn_readfirstlane(a.slot_of_expert[e]);
     const bool ok = slot >= 0 && slot < a.n_slots;
     const uint8_t* blob = a.arena + (ok ? (int64_t)slot * a.slot_stride : 0);
-    const __amdgpu_buffer_rsrc_t rsB =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blob), (short)0, (int)a.slot_stride, kRsrcWord3);
+    const u32x4 rwB = rsrc_words(blob, (int)a.slot_stride);
     const int tile_q = (int)(a.off_q0 + (int64_t)c * (kTileRows * a.K / 2)) + lane * 16;
     const int tile_sb = (int)(a.off_sb0 + (int64_t)c * (kTileRows * G * 4)) + lane * 4;
     const int up_q = GATEUP ? (int)(a.off_q1 - a.off_q0) : 0;
     const int up_sb = GATEUP ? (int)(a.off_sb1 - a.off_sb0) : 0;
-    // weights of step s into ring slot s % D
+    // weights of step s into ring slot s % D (asm LDS-DMA: the compiler would
+    // otherwise drain every ring slot in flight before each step's LDS reads)
     auto dma = [&](int s) {
       SStage<GATEUP>& st = ring[(s - s0) % D];
       const int so_q = __builtin_amdgcn_readfirstlane(s * 2048), so_sb = __builtin_amdgcn_readfirstlane(s * 256);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        dma16(rsB, &st.q[m][0][0], tile_q + m * up_q, so_q);
-        dma16(rsB, &st.q[m][1][0], tile_q + m * up_q + 1024, so_q);
-        dma4(rsB, &st.sb[m][0], tile_sb + m * up_sb, so_sb);
+        dma_lds16(rwB, __builtin_amdgcn_readfirstlane(lds_addr(&st.q[m][0][0])), tile_q + m * up_q, so_q);
+        dma_lds16(rwB, __builtin_amdgcn_readfirstlane(lds_addr(&st.q[m][1][0])), tile_q + m * up_q + 1024, so_q);
+        dma_lds4(rwB, __builtin_amdgcn_readfirstlane(lds_addr(&st.sb[m][0])), tile_sb + m * up_sb, so_sb);
       }
     };
     const int pre = s1 - s0 < D ? s1 - s0 : D;
