@@ -55,7 +55,6 @@ constexpr int WN = 64;                // weight rows per wave
 constexpr int kWaves = 4;             // waves per workgroup, side by side along N
 constexpr int BN = WN * kWaves;       // weight rows per workgroup
 constexpr int BK = 64;                // K step = one quantisation group
-constexpr int LDA = BK + 8;           // padded LDS row (16-bit elements)
 constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxExp = 100;          // block exponents are clamped to [-kMaxExp, kMaxExp]
 constexpr int kRsrcWord3 = 0x00020000;  // buffer resource word 3: raw 32-bit data, no swizzle
