@@ -563,7 +563,7 @@ class BatchStack:
         self.y_probe = torch.empty(T, D, dtype=torch.float32, device=dev)
         ws = lambda c: torch.zeros(max(api.moe_workspace_size(c, T, self.dm, prec if c >= 2 else 0), 256),
                                    dtype=torch.uint8, device=dev)
-        self.ws_route, self.ws_gateup, self.ws_down = ws(0), ws(2), ws(3)
+        self.ws_route, self.ws_perm, self.ws_gateup, self.ws_down = ws(0), ws(1), ws(2), ws(3)
 
     def arena_of(self, l):
         return self.arena[l * E * self.stride:(l + 1) * E * self.stride]
@@ -573,7 +573,7 @@ class BatchStack:
         a.moe_route(self.x[l], self.norm_w[l], EPS, self.router_w[l], self.bias[l], self.T, self.dm, self.h,
                     self.idx[l], self.w[l], self.ws_route, stream)
         a.moe_permute(self.idx[l], self.T, self.dm, self.counts[l], self.offsets[l], self.sp[l], self.pp[l],
-                      None, stream)
+                      self.ws_perm, stream)
 
     def gateup(self, l, stream=None):
         self.api.moe_expert_q4_gateup(self.h, self.idx[l], self.slots, E, self.arena_of(l), self.stride,

@@ -196,6 +196,11 @@ moe_status moe_route_noalloc(const float* x, const float* norm_w, float eps,
  *   offsets     device int32 [E+1]    exclusive prefix sum of counts; offsets[E] = T*k
  *   sorted_pair device int32 [T*k]    pair ids grouped by expert, ascending inside a group
  *   pair_pos    device int32 [T*k]    inverse: sorted_pair[pair_pos[p]] = p
+ *   ws          device, moe_workspace_size(MOE_CALL_PERMUTE) bytes (non-zero
+ *               past 1024 pairs), or NULL.  Given: chunks of 1024 pairs are
+ *               ranked by one workgroup each and placed by a second launch.
+ *               NULL (or too small): one workgroup walks every pair (slower
+ *               for many pairs).  The outputs are the same either way.
  * Deterministic; no atomics whose order reaches the output.  T*k <= 65536.
  * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN.
  * ------------------------------------------------------------------------- */

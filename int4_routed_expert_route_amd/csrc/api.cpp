@@ -144,7 +144,7 @@ size_t moe_workspace_size(moe_call call, int32_t T, moe_dims dims, moe_precision
   if (T < 1 || check_dims(dims) != MOE_OK) return SIZE_MAX;
   switch (call) {
     case MOE_CALL_ROUTE: return moe::route_workspace_bytes(T, dims.d, dims.n_experts);
-    case MOE_CALL_PERMUTE: return 0;
+    case MOE_CALL_PERMUTE: return moe::permute_workspace_bytes(T * dims.top_k, dims.n_experts);
     case MOE_CALL_GATEUP:
     case MOE_CALL_DOWN_COMBINE:
       if (prec == MOE_PREC_BF16_MFMA) return SIZE_MAX;  // refused: see moe_precision
@@ -200,14 +200,13 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t T, moe_dims dims, int32_
                        int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, void* ws,
                        size_t ws_bytes, hipStream_t stream) {
   const char* fn = "moe_permute";
-  (void)ws;
-  (void)ws_bytes;
   if (moe_status s = check_dims(dims)) return s;
   if (T < 1 || (int64_t)T * dims.top_k > 65536) return fail(MOE_ERR_ARG, "%s: T=%d (T*k <= 65536)", fn, T);
   CHECK_PTR(topk_idx); CHECK_PTR(counts); CHECK_PTR(offsets); CHECK_PTR(sorted_pair); CHECK_PTR(pair_pos);
   CHECK_ALIGN(topk_idx); CHECK_ALIGN(counts); CHECK_ALIGN(offsets); CHECK_ALIGN(sorted_pair); CHECK_ALIGN(pair_pos);
+  CHECK_ALIGN(ws);
   hipError_t e = moe::launch_permute(topk_idx, T * dims.top_k, dims.n_experts, counts, offsets,
-                                     sorted_pair, pair_pos, stream);
+                                     sorted_pair, pair_pos, ws, ws ? ws_bytes : 0, stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e, fn);
 }
 

@@ -23,8 +23,10 @@ hipError_t launch_route(const float* x, const float* norm_w, float eps, const fl
 hipError_t launch_rms_rescale(const float* x, int T, int d, float eps, float* out, hipStream_t s);
 
 // ---- pair permutation (permute.hip)
-hipError_t launch_permute(const int32_t* topk_idx, int n_pairs, int E, int32_t* counts,
-                          int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, hipStream_t s);
+// Workspace of the two-launch path (0: one workgroup walks every pair).
+size_t permute_workspace_bytes(int n_pairs, int E);
+hipError_t launch_permute(const int32_t* topk_idx, int n_pairs, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_pos, void* ws, size_t ws_bytes, hipStream_t s);
 
 // ---- fp32 dequant-GEMV (q4_gemv.hip)
 struct GateupArgs {

@@ -14,6 +14,15 @@
 // final position: each bucket lists its pairs in ascending pair id, with no
 // atomics.  Expert ids are loaded 16 rounds at a time, so each walk pays one
 // memory round trip per 1024 pairs of its stretch.
+//
+// Many pairs (a prefill batch) with a workspace: two launches over chunks of
+// 1024 pairs, one workgroup each.  k_perm_chunk ranks each pair among its
+// chunk's pairs of the same expert (the same ballot matching, one round per
+// wave) and writes the chunk's count per expert; k_perm_scatter sums, per
+// expert, the counts of all chunks (the offsets) and of the chunks before its
+// own (the chunk's base in the bucket), and writes the final positions.  The
+// result is the one-workgroup kernel's, bit for bit: buckets list their pairs
+// in ascending pair id.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,6 +34,8 @@ constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / kWave;
 constexpr int kMaxE = 256;
 constexpr int kBatch = 16;  // rounds of 64 pairs whose ids are loaded together
+constexpr int kChunk = kPermThreads;  // pairs per workgroup of the two-launch path
+constexpr int kMaxChunks = 64;        // T*k <= 65536
 
 // lanes whose expert id equals this lane's (invalid ids, -1, match only each other)
 __device__ __forceinline__ uint64_t same_expert(int e) {
@@ -138,13 +149,117 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restr
   }
 }
 
+// Chunk b = pairs b*kChunk .. +kChunk: each pair's rank among the chunk's pairs
+// of its expert (to pair_pos), the chunk's count per expert (to chunk_cnt[b][e]).
+__global__ __launch_bounds__(kPermThreads) void k_perm_chunk(const int32_t* __restrict__ topk_idx, int n_pairs,
+                                                             int E, int32_t* __restrict__ chunk_cnt,
+                                                             int32_t* __restrict__ pair_pos) {
+  __shared__ int s_cnt[kPermWaves][kMaxE];  // per wave and expert: count, then the wave's base
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  for (int i = tid; i < kPermWaves * kMaxE; i += kPermThreads) (&s_cnt[0][0])[i] = 0;
+  const int p = (int)blockIdx.x * kChunk + tid;
+  const int v = p < n_pairs ? topk_idx[p] : -1;
+  const int e = (v >= 0 && v < E) ? v : -1;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint64_t same = same_expert(e);
+  const int rank = __popcll(same & lt_mask);
+  __syncthreads();
+  if (e >= 0 && rank == 0) s_cnt[wave][e] = __popcll(same);
+  __syncthreads();
+  // per expert: the waves' counts become exclusive bases in wave order
+  if (tid < E) {
+    int run = 0;
+    for (int w = 0; w < kPermWaves; ++w) {
+      const int c = s_cnt[w][tid];
+      s_cnt[w][tid] = run;
+      run += c;
+    }
+    chunk_cnt[(int64_t)blockIdx.x * E + tid] = run;
+  }
+  __syncthreads();
+  if (p < n_pairs) pair_pos[p] = e >= 0 ? s_cnt[wave][e] + rank : -1;
+}
+
+// Chunk b: bucket bases from every chunk's counts, then final positions.
+// Workgroup 0 also writes counts and offsets.
+__global__ __launch_bounds__(kPermThreads) void k_perm_scatter(const int32_t* __restrict__ topk_idx, int n_pairs,
+                                                               int E, int n_chunks,
+                                                               const int32_t* __restrict__ chunk_cnt,
+                                                               int32_t* __restrict__ counts,
+                                                               int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ sorted_pair,
+                                                               int32_t* __restrict__ pair_pos) {
+  __shared__ int s_base[kMaxE];   // per expert: this chunk's first position in the bucket
+  __shared__ int s_wsum[kMaxE / kWave];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int b = (int)blockIdx.x;
+  // this thread's pair (requested first: the count sums below take a while)
+  const int p = b * kChunk + tid;
+  const int v = p < n_pairs ? topk_idx[p] : -1;
+  const int loc = p < n_pairs ? pair_pos[p] : -1;
+  int total = 0, before = 0;
+  if (tid < E) {
+    for (int c = 0; c < n_chunks; ++c) {
+      const int n = chunk_cnt[(int64_t)c * E + tid];
+      total += n;
+      if (c < b) before += n;
+    }
+  }
+  // exclusive scan of the totals over the experts (waves 0..3, then their sums)
+  int incl = total;
+  if (tid < kMaxE) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int u = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += u;
+    }
+    if (lane == kWave - 1) s_wsum[wave] = incl;
+  }
+  __syncthreads();
+  if (tid < kMaxE) {
+    int off = incl - total;
+    for (int w = 0; w < wave; ++w) off += s_wsum[w];
+    if (tid < E) {
+      s_base[tid] = off + before;
+      if (b == 0) {
+        offsets[tid] = off;
+        counts[tid] = total;
+        if (tid == E - 1) offsets[E] = off + total;
+      }
+    }
+  }
+  __syncthreads();
+  const int e = (v >= 0 && v < E) ? v : -1;
+  if (p < n_pairs && e >= 0) {
+    const int pos = s_base[e] + loc;
+    sorted_pair[pos] = p;
+    pair_pos[p] = pos;
+  }
+}
+
 }  // namespace
 
+size_t permute_workspace_bytes(int n_pairs, int E) {
+  return n_pairs > kChunk ? (size_t)kMaxChunks * (size_t)E * sizeof(int32_t) : 0;
+}
+
 hipError_t launch_permute(const int32_t* topk_idx, int n_pairs, int E, int32_t* counts,
-                          int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, hipStream_t s) {
+                          int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, void* ws, size_t ws_bytes,
+                          hipStream_t s) {
   if (E > kMaxE) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_permute, dim3(1), dim3(kPermThreads), 0, s, topk_idx, n_pairs, E, counts,
-                     offsets, sorted_pair, pair_pos);
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  take_profile_events(MOE_CALL_PERMUTE, &ev0, &ev1);
+  const int n_chunks = (n_pairs + kChunk - 1) / kChunk;
+  if (n_chunks > 1 && n_chunks <= kMaxChunks && ws && ws_bytes >= permute_workspace_bytes(n_pairs, E)) {
+    int32_t* chunk_cnt = static_cast<int32_t*>(ws);
+    launch_maybe_timed(k_perm_chunk, n_chunks, kPermThreads, s, ev0, nullptr, topk_idx, n_pairs, E, chunk_cnt,
+                       pair_pos);
+    launch_maybe_timed(k_perm_scatter, n_chunks, kPermThreads, s, nullptr, ev1, topk_idx, n_pairs, E, n_chunks,
+                       static_cast<const int32_t*>(chunk_cnt), counts, offsets, sorted_pair, pair_pos);
+    return hipGetLastError();
+  }
+  launch_maybe_timed(k_permute, 1, kPermThreads, s, ev0, ev1, topk_idx, n_pairs, E, counts, offsets, sorted_pair,
+                     pair_pos);
   return hipGetLastError();
 }
 

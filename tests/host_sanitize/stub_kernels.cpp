@@ -29,7 +29,9 @@ hipError_t launch_route(const float*, const float*, float, const float*, const f
   return launched();
 }
 hipError_t launch_rms_rescale(const float*, int, int, float, float*, hipStream_t) { return launched(); }
-hipError_t launch_permute(const int32_t*, int, int, int32_t*, int32_t*, int32_t*, int32_t*, hipStream_t) {
+size_t permute_workspace_bytes(int n_pairs, int E) { return n_pairs > 1024 ? (size_t)64 * E * 4 : 0; }
+hipError_t launch_permute(const int32_t*, int, int, int32_t*, int32_t*, int32_t*, int32_t*, void*, size_t,
+                          hipStream_t) {
   return launched();
 }
 

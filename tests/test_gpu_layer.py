@@ -269,17 +269,25 @@ def test_pair_mask_hits_then_misses(layer0, dev_layer):
 
 # ----------------------------------------------------------------------------- permute + grouped
 
+@pytest.mark.parametrize("with_ws", [False, True])
 @pytest.mark.parametrize("T", [1, 3, 32, 257, 2048, 8192])
-def test_permute_exact(T):
+def test_permute_exact(T, with_ws):
+    """Both permute paths against the oracle: one workgroup walking every pair
+    (no workspace), and, past 1024 pairs with a workspace, the two launches over
+    chunks of 1024 pairs (257 tokens: a ragged last chunk; 8192: the 64-chunk
+    maximum)."""
     rs = np.random.default_rng(T)
     p = synth.zipf_probs(E, 0, 0)
     idx_np = np.stack([rs.choice(E, K, replace=False, p=p) for _ in range(T)]).astype(np.int32)
     idx = torch.from_numpy(idx_np).cuda()
-    counts = torch.empty(E, dtype=torch.int32, device="cuda")
-    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
-    sp = torch.empty(T * K, dtype=torch.int32, device="cuda")
-    pp = torch.empty(T * K, dtype=torch.int32, device="cuda")
-    L.moe_permute(idx, T, DM, counts, offsets, sp, pp)
+    counts = torch.full((E,), -5, dtype=torch.int32, device="cuda")
+    offsets = torch.full((E + 1,), -5, dtype=torch.int32, device="cuda")
+    sp = torch.full((T * K,), -5, dtype=torch.int32, device="cuda")
+    pp = torch.full((T * K,), -5, dtype=torch.int32, device="cuda")
+    nb = L.moe_workspace_size(L.MOE_CALL_PERMUTE, T, DM)
+    assert (nb > 0) == (T * K > 1024)
+    ws = torch.full((max(nb, 256),), 0x5A, dtype=torch.uint8, device="cuda") if with_ws else None
+    L.moe_permute(idx, T, DM, counts, offsets, sp, pp, ws)
     rc, ro, rsp, rpp = orc.permute(idx_np, E)
     assert np.array_equal(_np(counts), rc) and np.array_equal(_np(offsets), ro)
     assert np.array_equal(_np(sp), rsp) and np.array_equal(_np(pp), rpp)
