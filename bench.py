@@ -531,6 +531,147 @@ def run_decode_timeline(args, api, torch):
     return {"timeline": args.decode_timeline, "launch_us": round(float(np.mean(launch_us)), 2)}
 
 
+def run_gemm_timeline(args, api, torch):
+    """Per-item timeline of the work-list GEMM (measurement build
+    libmoe_measure.so) at prefill: for several layers, one eager gate/up and
+    one down launch on that layer's routing, every workgroup's clock at its
+    start, plan, each item's start, first K step and K-loop end, and its end;
+    summarised as markdown into args.gemm_timeline."""
+    import ctypes
+    lib = api.lib()
+    fn = lib.moe_debug_gemm_timeline
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    T = args.tokens or 2048
+    stack = BatchStack(api, torch, args.seed, T, api.MOE_PREC_F16_MFMA, decode=False)
+    for _ in range(max(args.warmup, 1)):
+        stack.step()
+    torch.cuda.synchronize()
+    tl = np.zeros((2, 1024, 100), dtype=np.uint64)
+    assert fn(tl.ctypes.data, 1) == 0
+    layers = list(range(0, NL, max(1, NL // max(1, min(args.steps, NL)))))[:args.steps]
+    rec = {0: [], 1: []}
+    for l in layers:
+        stack.gateup(l)
+        stack.down(l, stack.y_probe)
+        torch.cuda.synchronize()
+        assert fn(tl.ctypes.data, 1) == 0
+        for g in (0, 1):
+            rec[g].append(tl[g].astype(np.int64).copy())
+    lines, summary = summarize_gemm_timeline(rec, T, layers, max(args.warmup, 1))
+    text = "\n".join(lines)
+    with open(args.gemm_timeline, "w") as fh:
+        fh.write(text + "\n")
+    log("timeline:\n" + text)
+    return {"timeline": args.gemm_timeline, **summary}
+
+
+def summarize_gemm_timeline(rec, T, layers, warmup):
+    """Markdown lines and summary numbers of the work-list GEMM's item
+    timeline: rec[0] gate/up, rec[1] down, each a list of int64 tables
+    [workgroup][slot] (slots: start, plan ready, end, compute unit << 32 |
+    items; then per item: start, (item, rows, K ranges, K range) word, first
+    K step's barrier, K-loop end)."""
+    us = 0.01  # s_memrealtime ticks at 100 MHz
+    lines = [f"Work-list GEMM `k_q4_gemm` (f16 MFMA, int4 tiles staged in LDS) at prefill, {T} tokens, "
+             f"Zipf(1.1) routing: one eager launch of each GEMM on the routing of layers "
+             f"{', '.join(map(str, layers))}, after {warmup} warmup steps. Clock: s_memrealtime "
+             "(100 MHz), thread 0 of each workgroup. An item is (expert, tile of up to 128 pair rows, N tile, "
+             "K range); its row groups are its rows in 16s.", ""]
+    summary = {}
+    for g, name in ((0, "gate/up"), (1, "down")):
+        span, plan, tail_idle, per_wg, cu_tail, n_cu = [], [], [], [], [], []
+        mate_gap, mate, kl_paired, kl_alone = {}, {}, [], []
+        xcd_end = np.zeros(8)
+        by_mg = {}
+        first_item, kloop_step = [], []
+        for r in rec[g]:
+            used = r[:, 0] > 0
+            r = r[used]
+            t0 = r[:, 0].min()
+            t_end = r[:, 2].max()
+            span.append((t_end - t0) * us)
+            plan.append(np.median((r[:, 1] - r[:, 0]) * us))
+            tail_idle.append(np.mean((t_end - r[:, 2]) * us) / ((t_end - t0) * us))
+            n_items = r[:, 3] & 0xFFFFFFFF
+            per_wg.append(n_items)
+            # a compute unit is idle once both of its workgroups are done
+            cu = r[:, 3] >> 32
+            cu_end = {}
+            for w in range(r.shape[0]):
+                cu_end[int(cu[w])] = max(cu_end.get(int(cu[w]), 0), int(r[w, 2]))
+            cu_tail.append(np.mean([(t_end - v) * us for v in cu_end.values()]) / ((t_end - t0) * us))
+            n_cu.append(len(cu_end))
+            # which workgroups share a compute unit, and a K loop with the other one running or done
+            first = {}
+            for w in range(r.shape[0]):
+                c = int(cu[w])
+                if c in first:
+                    mate_gap[w - first[c]] = mate_gap.get(w - first[c], 0) + 1
+                    mate[w], mate[first[c]] = first[c], w
+                else:
+                    first[c] = w
+            for w in range(r.shape[0]):
+                if w not in mate:
+                    continue
+                m_end = r[mate[w], 2]
+                for j in range(int(min(n_items[w], 24))):
+                    meta, b0, k1 = r[w, 5 + 4 * j], r[w, 6 + 4 * j], r[w, 7 + 4 * j]
+                    if ((meta >> 16) & 0xFFFF) != 128:
+                        continue
+                    if k1 <= m_end:
+                        kl_paired.append((k1 - b0) * us)
+                    elif b0 >= m_end:
+                        kl_alone.append((k1 - b0) * us)
+            mate.clear()
+            for x in range(8):
+                xcd_end[x] += (r[x::8, 2].mean() - t0) * us
+            first_item.append(np.median((r[:, 4] - r[:, 0]) * us))
+            for w in range(r.shape[0]):
+                n = int(min(n_items[w], 24))
+                for j in range(n):
+                    s0, meta, b0, k1 = r[w, 4 + 4 * j: 8 + 4 * j]
+                    nxt = r[w, 4 + 4 * (j + 1)] if j + 1 < n else r[w, 2]
+                    rows = int((meta >> 16) & 0xFFFF)
+                    sr = int((meta >> 8) & 0xFF)
+                    mg = (rows + 15) // 16
+                    d = by_mg.setdefault((mg, sr), {"setup": [], "kloop": [], "tail": []})
+                    d["setup"].append((b0 - s0) * us)
+                    d["kloop"].append((k1 - b0) * us)
+                    d["tail"].append((nxt - k1) * us)
+        xcd_end /= len(rec[g])
+        allw = np.concatenate(per_wg)
+        n_launch = len(rec[g])
+        lines += [f"## {name}", "",
+                  f"Launch span (first workgroup start to last workgroup end): {np.mean(span):.1f} us mean; "
+                  f"{allw.size // n_launch} workgroups; items per workgroup min {allw.min()}, median "
+                  f"{np.median(allw):.0f}, max {allw.max()}.", "",
+                  f"Plan (workgroup start to work list ready in LDS): {np.mean(plan):.2f} us median. "
+                  f"First item's start after workgroup start: {np.mean(first_item):.2f} us median. "
+                  f"Idle tail (mean over workgroups of launch end minus own end, over the span): "
+                  f"{np.mean(tail_idle):.1%}; by compute unit (launch end minus the end of the later of its "
+                  f"workgroups, {np.mean(n_cu):.0f} compute units): {np.mean(cu_tail):.1%}.", "",
+                  "| row groups | K ranges | items | setup: item start to first K step's barrier, us | "
+                  "K loop, us | after the K loop (split sum, epilogue, next item's wait), us |",
+                  "|---|---|---|---|---|---|"]
+        for (mg, sr) in sorted(by_mg):
+            d = by_mg[(mg, sr)]
+            lines.append(f"| {mg} | {sr} | {len(d['setup']) // n_launch} per launch | "
+                         f"{np.median(d['setup']):.2f} | {np.median(d['kloop']):.2f} | "
+                         f"{np.median(d['tail']):.2f} |")
+        lines += ["", "Mean workgroup end per XCD (workgroups g with g % 8 = x), us after the launch's first "
+                  "start: " + ", ".join(f"{v:.1f}" for v in xcd_end), "",
+                  "Workgroups sharing a compute unit, by the difference of their indices (pairs over all "
+                  "launches): " + ", ".join(f"{k}: {v}" for k, v in sorted(mate_gap.items())) + ". "
+                  f"K loop of a 128-row item: {np.median(kl_paired) if kl_paired else float('nan'):.1f} us "
+                  f"median while the other workgroup of its compute unit runs ({len(kl_paired)} items), "
+                  f"{np.median(kl_alone) if kl_alone else float('nan'):.1f} us once it has ended "
+                  f"({len(kl_alone)} items).", ""]
+        summary[name] = {"span_us": round(float(np.mean(span)), 2), "plan_us": round(float(np.mean(plan)), 2),
+                         "idle_tail": round(float(np.mean(tail_idle)), 4),
+                         "idle_tail_cu": round(float(np.mean(cu_tail)), 4)}
+    return lines, summary
+
+
 # ----------------------------------------------------------------------------- batched / prefill
 
 class BatchStack:
@@ -1117,6 +1258,50 @@ def run_cache_overlap(args, api, torch):
     return out
 
 
+def run_issue_probe(out_md):
+    """Whether packed fp16 VALU work runs alongside fp16 MFMAs on one SIMD
+    (measurement build): the issue probe's four modes, one workgroup of 8
+    waves per compute unit, each timed 3 times (fastest kept)."""
+    import ctypes
+    import torch
+    from int4_routed_expert_route_amd import build as moe_build
+    lib = ctypes.CDLL(moe_build.MEASURE_LIB)
+    fn = lib.moe_debug_issue_probe
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    groups, iters = torch.cuda.get_device_properties(0).multi_processor_count, 20000
+    out = torch.zeros(groups * 512, dtype=torch.float32, device="cuda")
+    names = {1: "MFMA waves only (one per SIMD: 8 MFMAs per step)",
+             2: "VALU waves only (one per SIMD: 32 v_pk_fma_f16 per step)",
+             3: "both at once: one MFMA wave and one VALU wave per SIMD",
+             4: "mixed: every wave runs half the steps with 4 v_pk_fma_f16 after each MFMA"}
+    ms = {}
+    for mode in (1, 2, 3, 4):
+        best = float("inf")
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            assert fn(mode, groups, iters, out.data_ptr(), None) == 0
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        ms[mode] = best
+    lines = [f"Issue probe (`k_issue_probe`, measurement build): {groups} workgroups of 8 waves (one per compute "
+             f"unit, two waves per SIMD), {iters} steps per working wave; fastest of 3 launches.", "",
+             "| mode | ms | us per step |", "|---|---|---|"]
+    for mode in (1, 2, 3, 4):
+        lines.append(f"| {names[mode]} | {ms[mode]:.3f} | {ms[mode] * 1e3 / iters:.4f} |")
+    lines += ["", f"Sum of the MFMA-only and VALU-only times: {ms[1] + ms[2]:.3f} ms; the longer of the two: "
+              f"{max(ms[1], ms[2]):.3f} ms. Both at once took {ms[3]:.3f} ms and mixed {ms[4]:.3f} ms, so "
+              f"{(ms[1] + ms[2] - ms[3]) / min(ms[1], ms[2]):.0%} (separate waves) and "
+              f"{(ms[1] + ms[2] - ms[4]) / min(ms[1], ms[2]):.0%} (mixed in each wave) of the shorter part was "
+              "hidden under the longer."]
+    text = "\n".join(lines)
+    with open(out_md, "w") as fh:
+        fh.write(text + "\n")
+    log("issue probe:\n" + text)
+    print(json.dumps({"issue_probe": out_md, "ms": ms}), flush=True)
+
+
 def run_copy_calibration(mib):
     """Known-bytes kernels for scaling HBM counters: a device-to-device copy of
     MIB MiB (torch), and, from the measurement build, reads of the same bytes
@@ -1185,6 +1370,11 @@ def main():
     ap.add_argument("--decode-timeline", default="", metavar="OUT.md",
                     help="decode: per-stage timeline of the fused kernel from the measurement build "
                          "libmoe_measure.so, summarised into OUT.md (no timing line)")
+    ap.add_argument("--gemm-timeline", default="", metavar="OUT.md",
+                    help="prefill: per-item timeline of the work-list GEMM from the measurement build "
+                         "libmoe_measure.so over --steps layers, summarised into OUT.md (no timing line)")
+    ap.add_argument("--issue-probe", default="", metavar="OUT.md",
+                    help="only run the MFMA / packed-fp16 VALU issue probe of the measurement build, into OUT.md")
     ap.add_argument("--library", default="", metavar="SO",
                     help="load this build of libmoe instead of the in-tree one (compare builds on one box)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -1192,6 +1382,9 @@ def main():
     args = ap.parse_args()
     if args.copy_calibration:
         run_copy_calibration(args.copy_calibration)
+        return
+    if args.issue_probe:
+        run_issue_probe(args.issue_probe)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the routed MoE hot path is built and "
@@ -1205,11 +1398,15 @@ def main():
 
     import torch
     import int4_routed_expert_route_amd.api as api
-    if args.decode_timeline:
+    if args.decode_timeline or args.gemm_timeline:
         from int4_routed_expert_route_amd import build as moe_build
         api.LIB_PATH = moe_build.MEASURE_LIB
+    if args.decode_timeline:
         args.workload = "decode"
         args.warmup, args.steps = min(args.warmup, 16), min(args.steps, 8)
+    if args.gemm_timeline:
+        args.workload = "prefill"
+        args.warmup, args.steps = min(args.warmup, 2), min(args.steps, 6)
     if args.library:
         api.LIB_PATH = os.path.abspath(args.library)
     api.lib()
@@ -1217,6 +1414,8 @@ def main():
     run = {"decode": run_decode, "batched": run_batched, "prefill": run_prefill, "cache": run_cache}[args.workload]
     if args.decode_timeline:
         run = run_decode_timeline
+    if args.gemm_timeline:
+        run = run_gemm_timeline
     if args.overlap_study:
         if args.workload != "cache":
             raise SystemExit("--overlap-study belongs to --workload cache")

@@ -24,10 +24,11 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
 
 # Measurement variant (libmoe_measure.so): the library, with the fused decode
 # kernel recording a per-stage timeline (MOE_DECODE_TIMELINE, see
-# decode_fused.hip) and known-bytes read kernels for scaling HBM counters
-# (measure.hip).  Never loaded by the tests or the timing line.
+# decode_fused.hip), the work-list GEMM a per-item timeline (MOE_GEMM_TIMELINE,
+# see q4_grouped_mfma.hip), and known-bytes read kernels for scaling HBM
+# counters (measure.hip).  Never loaded by the tests or the timing line.
 MEASURE_LIB = os.path.join(HERE, "libmoe_measure.so")
-MEASURE_DEFINES = {"decode_fused.hip": ["-DMOE_DECODE_TIMELINE"]}
+MEASURE_DEFINES = {"decode_fused.hip": ["-DMOE_DECODE_TIMELINE"], "q4_grouped_mfma.hip": ["-DMOE_GEMM_TIMELINE"]}
 MEASURE_SOURCES = ["measure.hip"]
 
 

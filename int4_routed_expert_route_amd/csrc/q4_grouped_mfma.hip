@@ -428,6 +428,36 @@ __device__ __forceinline__ uint32_t lds_read32(uint32_t addr) {
 // nibbles and (scale, bias) words from memory straight into registers, one
 // K step ahead, instead of taking them from an LDS stage; activations are
 // staged as before.
+// Item timeline (a build option for measurement, off in the library): with
+// MOE_GEMM_TIMELINE defined, thread 0 of every workgroup records the global
+// 100 MHz clock (s_memrealtime) at its start, when its plan is ready and at its
+// end, its compute unit (__smid) with its item count, and per item (the first kGtItems): the item's start, its (item, rows,
+// K ranges, K range) word, the first K step's barrier and the end of its K
+// loop; moe_debug_gemm_timeline() copies the table of the last launch of each
+// GEMM (gate/up, down) to the host.
+#ifdef MOE_GEMM_TIMELINE
+constexpr int kGtGroups = 1024, kGtItems = 24, kGtRow = 4 + 4 * kGtItems;
+__device__ uint64_t g_gemm_timeline[2][kGtGroups][kGtRow];
+#define GEMM_TL(slot, value)                                                        \
+  do {                                                                               \
+    if (threadIdx.x == 0 && blockIdx.x < kGtGroups)                                  \
+      g_gemm_timeline[GATEUP ? 0 : 1][blockIdx.x][(slot)] = (uint64_t)(value);       \
+  } while (0)
+#define GEMM_TL_ITEM(j, k, value)                                                   \
+  do {                                                                               \
+    if ((j) < kGtItems) GEMM_TL(4 + 4 * (j) + (k), value);                           \
+  } while (0)
+#define GEMM_TL_ON 1
+#else
+#define GEMM_TL(slot, value) \
+  do {                       \
+  } while (0)
+#define GEMM_TL_ITEM(j, k, value) \
+  do {                            \
+  } while (0)
+#define GEMM_TL_ON 0
+#endif
+
 template <typename ET, bool GATEUP, bool DIRECT>
 __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
   typedef Op<ET> O;
@@ -441,6 +471,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
   __shared__ Plan s_plan;
   __shared__ uint32_t s_ticket;
   const int t = threadIdx.x;
+  GEMM_TL(0, __builtin_amdgcn_s_memrealtime());
+  int tl_j = 0;  // items this workgroup has started (timeline build)
   const int wid = __builtin_amdgcn_readfirstlane(t / kWave), lane = t % kWave;
   const int n = lane % 16, kq = lane / 16;  // MFMA lane coordinates
   const int G = a.K / kGroup;               // K steps
@@ -459,11 +491,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
   // the work list, in LDS (stage 0 of the pipeline serves as scratch)
   plan_items(a.offsets, a.E, n_pairs, a.NT, G, min(a.split_cap, (int)gridDim.x), a.min_rows,
              reinterpret_cast<int*>(&lds[0]), s_plan);
+  GEMM_TL(1, __builtin_amdgcn_s_memrealtime());
   const int xcd = (int)(blockIdx.x % 8), nper = (int)(gridDim.x / 8);
   const int i_end = __builtin_amdgcn_readfirstlane(s_plan.xstart[xcd + 1]);
   for (int item = __builtin_amdgcn_readfirstlane(s_plan.xstart[xcd]) + (int)(blockIdx.x / 8); item < i_end;
        item += nper) {
     __syncthreads();  // the previous item's LDS (or the plan's scratch) is no longer in use
+    GEMM_TL_ITEM(tl_j, 0, __builtin_amdgcn_s_memrealtime());
     // values the whole workgroup shares, made wave-uniform for the compiler
     int rk = 0;
     {
@@ -488,6 +522,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
     const int beg = __builtin_amdgcn_readfirstlane(s_plan.beg[rk]);
     const int end = beg + (ec >> 8);
     const int rows = max(0, min(BM, end - beg - m0));
+    GEMM_TL_ITEM(tl_j, 1, ((uint64_t)item << 32) | ((uint64_t)rows << 16) | (uint64_t)(sr << 8) | (uint64_t)ks);
     // weights through the slot table; an absent expert gives NaN outputs.
     // The slot is requested before the tile's pair ids, so the two loads
     // share one memory round trip.
@@ -737,6 +772,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // and its LDS accesses (lgkmcnt 0)
       __builtin_amdgcn_s_barrier();        // ... and every other wave's
+      if (GEMM_TL_ON && s == s0) GEMM_TL_ITEM(tl_j, 2, __builtin_amdgcn_s_memrealtime());
       lds_fence();
       if (fix_rows) {
         fix_step(s, st);
@@ -756,6 +792,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
       }
     }
 
+    GEMM_TL_ITEM(tl_j, 3, __builtin_amdgcn_s_memrealtime());
+    ++tl_j;
     // ---- split items: partials out; the last K range to arrive sums them
     // (in range order) and goes on to the epilogue, the others are done.
     // The partials are written through to memory and read back with
@@ -885,6 +923,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
       }
     }
   }
+  (void)tl_j;
+  GEMM_TL(3, ((uint64_t)__smid() << 32) | (uint64_t)tl_j);
+  GEMM_TL(2, __builtin_amdgcn_s_memrealtime());
 }
 
 // y[t] = residual[t] + sum_j w[t][j] * pair[t*k + j] in rank order, pair values
@@ -1442,3 +1483,20 @@ hipError_t launch_down_mfma(bool direct, const void* act_in, const int32_t* offs
 }
 
 }  // namespace moe
+
+#ifdef MOE_GEMM_TIMELINE
+// The item timeline of the last launch of each work-list GEMM: uint64
+// [2][1024][100] (gate/up, down; workgroup; slots).  clear != 0 zero-fills it
+// afterwards.
+extern "C" int moe_debug_gemm_timeline(uint64_t* host_out, int clear) {
+  hipError_t e = hipMemcpyFromSymbol(host_out, HIP_SYMBOL(moe::g_gemm_timeline), sizeof(moe::g_gemm_timeline), 0,
+                                     hipMemcpyDeviceToHost);
+  if (e == hipSuccess && clear) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(moe::g_gemm_timeline));
+    if (e == hipSuccess) e = hipMemset(p, 0, sizeof(moe::g_gemm_timeline));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+  }
+  return (int)e;
+}
+#endif
