@@ -232,11 +232,19 @@ __global__ __launch_bounds__(1024) void k_down_token(DownArgs a) {
   const int64_t tile = (int64_t)(row0 / kTileRows);
   constexpr int NPASS = (8 * GMAX + kWave - 1) / kWave;
   StageRegs<NPASS> sr;
-  stage_load<NPASS>(sr, a.act + (int64_t)p * a.f, G, lane, kWave);
   LaneSlice<GPP> w;
-  load_lane<GPP>(w, blob + a.off_q + tile * (kTileRows * a.f / 2) + trow * 16,
-                 blob + a.off_sb + tile * (kTileRows * G * 4) + trow * 4, pt, G);
-  stage_store<kDownP, GMAX, NPASS>(xs[jr], sr, G, lane, kWave);
+  stage_load<NPASS>(sr, a.act + (int64_t)p * a.f, G, lane, kWave);
+  if constexpr (GPP >= 7) {
+    // 16 waves leave 128 VGPRs a wave: the activations reach LDS before the
+    // weight slice is loaded, so the two are never in registers together
+    stage_store<kDownP, GMAX, NPASS>(xs[jr], sr, G, lane, kWave);
+    load_lane<GPP>(w, blob + a.off_q + tile * (kTileRows * a.f / 2) + trow * 16,
+                   blob + a.off_sb + tile * (kTileRows * G * 4) + trow * 4, pt, G);
+  } else {
+    load_lane<GPP>(w, blob + a.off_q + tile * (kTileRows * a.f / 2) + trow * 16,
+                   blob + a.off_sb + tile * (kTileRows * G * 4) + trow * 4, pt, G);
+    stage_store<kDownP, GMAX, NPASS>(xs[jr], sr, G, lane, kWave);
+  }
   __syncthreads();
   float v = lane_dot<kDownP, GPP, GMAX>(w, xs[jr], j, pt, G, a.nck);
   if (!ok) v = f32_nan();

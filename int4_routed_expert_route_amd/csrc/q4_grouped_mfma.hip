@@ -431,10 +431,12 @@ __device__ __forceinline__ uint32_t lds_read32(uint32_t addr) {
 // Item timeline (a build option for measurement, off in the library): with
 // MOE_GEMM_TIMELINE defined, thread 0 of every workgroup records the global
 // 100 MHz clock (s_memrealtime) at its start, when its plan is ready and at its
-// end, its compute unit (__smid) with its item count, and per item (the first kGtItems): the item's start, its (item, rows,
-// K ranges, K range) word, the first K step's barrier and the end of its K
+// end, its compute unit (__smid) with its item count, and per item (the first
+// kGtItems): the item's start, its (item, rows, K ranges, K range) word, the first K step's barrier and the end of its K
 // loop; moe_debug_gemm_timeline() copies the table of the last launch of each
-// GEMM (gate/up, down) to the host.
+// GEMM (gate/up, down) to the host.  The few-pairs kernel writes the same
+// table (per round of its wave 0's item: start, (item, rows) word, K loop
+// start, K loop end).
 #ifdef MOE_GEMM_TIMELINE
 constexpr int kGtGroups = 1024, kGtItems = 24, kGtRow = 4 + 4 * kGtItems;
 __device__ uint64_t g_gemm_timeline[2][kGtGroups][kGtRow];
@@ -1026,7 +1028,14 @@ struct SStage {
 };
 template <bool GATEUP>
 struct SDepth {
-  static constexpr int value = GATEUP ? 3 : 6;  // weight steps in flight per wave (>= kSAhead)
+  static constexpr int value = GATEUP ? 3 : 5;  // weight steps in flight per wave (>= kSAhead)
+};
+// Workgroups per compute unit: down runs three (12 waves; its LDS ring of 5
+// steps fits three times), so that a 32-token batch's ~2,100 down items take
+// one round instead of two for a few workgroups.
+template <bool GATEUP>
+struct SOcc {
+  static constexpr int value = GATEUP ? 2 : 3;
 };
 // Per-step activation operand of one lane: the 16 columns this lane
 // multiplies (two MFMA K slices of 8) and (down) the row's exponent for the step.
@@ -1037,7 +1046,7 @@ struct SAct {
 
 
 template <bool GATEUP>
-__global__ __launch_bounds__(kSThreads, 2) void k_q4_small(SmallArgs a) {
+__global__ __launch_bounds__(kSThreads, SOcc<GATEUP>::value) void k_q4_small(SmallArgs a) {
   constexpr int NM = GATEUP ? 2 : 1;  // matrices
   constexpr int NG = 4 * NM;          // row groups of 16 per wave (gate/up: 4 gate, then the same 4 up)
   constexpr int D = SDepth<GATEUP>::value;
@@ -1045,6 +1054,8 @@ __global__ __launch_bounds__(kSThreads, 2) void k_q4_small(SmallArgs a) {
   constexpr int IPW = kSWaves / KS;         // items per workgroup at a time
   static_assert(D >= kSAhead, "a step's weights must be requested before its activations");
   typedef Op<_Float16> O;
+  GEMM_TL(0, __builtin_amdgcn_s_memrealtime());
+  int tl_j = 0;  // rounds this workgroup has started (timeline build)
   __shared__ SStage<GATEUP> s_ring[kSWaves][D];
   __shared__ floatx4 s_red[KS > 1 ? IPW : 1][KS > 1 ? NG : 1][kWave];  // the second K part's accumulators
   __shared__ int s_rank_e[256];             // expert of each small rank
@@ -1094,6 +1105,7 @@ __global__ __launch_bounds__(kSThreads, 2) void k_q4_small(SmallArgs a) {
   }
   __syncthreads();
   const int n_parts = s_xpre[mine];
+  GEMM_TL(1, __builtin_amdgcn_s_memrealtime());
   const __amdgpu_buffer_rsrc_t rsA =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.a_rows), (short)0, a.a_bytes, kRsrcWord3);
   SStage<GATEUP>* ring = s_ring[wid];
@@ -1106,10 +1118,15 @@ __global__ __launch_bounds__(kSThreads, 2) void k_q4_small(SmallArgs a) {
   const int is = wid / KS, kh = wid % KS;  // item of this wave within the workgroup, its K part
   // K steps of this wave's part
   const int s0 = __builtin_amdgcn_readfirstlane(kh * G / KS), s1 = __builtin_amdgcn_readfirstlane((kh + 1) * G / KS);
-  // every wave runs every round (the K parts meet at barriers); a wave without an item skips its work
-  for (int qq = (int)(blockIdx.x / 8); qq * IPW < n_items; qq += nper) {
-    const int q = qq * IPW + is;
+  // every wave runs every round (the K parts meet at barriers); a wave without
+  // an item skips its work.  A round's items go slot by slot over the XCD's
+  // workgroups (item slot is of workgroup j runs item is * nper + j), so that
+  // a round with fewer items than slots spreads them over all compute units
+  // (workgroups j and j + nper / 2 share one) instead of doubling some up.
+  for (int base = 0; base < n_items; base += IPW * nper) {
+    const int q = base + is * nper + (int)(blockIdx.x / 8);
     const bool has = q < n_items;
+    GEMM_TL_ITEM(tl_j, 0, __builtin_amdgcn_s_memrealtime());
     const int u = (has ? q : 0) / a.NC, c = (has ? q : 0) % a.NC;
     // the expert whose parts hold u: s_xpre[i] <= u < s_xpre[i + 1]
     int i = 0;
@@ -1161,9 +1178,17 @@ __global__ __launch_bounds__(kSThreads, 2) void k_q4_small(SmallArgs a) {
     // down: the item's largest act exponent over its rows and K groups
     int texp = 0;
     if (!GATEUP) {
+      // 16 exponents per memory round trip (a loop of single loads paid one
+      // round trip per K group before the item's first step)
       int m = -128;
-      if (pr >= 0)
-        for (int g = 0; g < G; ++g) m = max(m, (int)a.a_exp[(int64_t)pr * G + g]);
+      const int8_t* ep = a.a_exp + (int64_t)max(pr, 0) * G;
+      for (int g0 = 0; g0 < G; g0 += 16) {
+        int v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = (pr >= 0 && g0 + i < G) ? (int)ep[g0 + i] : -128;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = max(m, v[i]);
+      }
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) m = max(m, __shfl_xor(m, o, kWave));
       texp = m < -127 ? 0 : m;
@@ -1228,6 +1253,8 @@ __global__ __launch_bounds__(kSThreads, 2) void k_q4_small(SmallArgs a) {
         }
       }
     };
+    GEMM_TL_ITEM(tl_j, 1, ((uint64_t)q << 32) | ((uint64_t)rows << 16));
+    GEMM_TL_ITEM(tl_j, 2, __builtin_amdgcn_s_memrealtime());
     if (has && s0 < s1) {
       SAct v0, v1, v2, v3;
       fetch_a(s0, v0);
@@ -1243,6 +1270,8 @@ __global__ __launch_bounds__(kSThreads, 2) void k_q4_small(SmallArgs a) {
         one(s + 3, v3, v2);
       }
     }
+    GEMM_TL_ITEM(tl_j, 3, __builtin_amdgcn_s_memrealtime());
+    ++tl_j;
     if (KS > 1) {
       // the second K part's accumulators join the first's
       if (has && kh == 1)
@@ -1310,6 +1339,9 @@ __global__ __launch_bounds__(kSThreads, 2) void k_q4_small(SmallArgs a) {
       }
     }
   }
+  (void)tl_j;
+  GEMM_TL(3, ((uint64_t)__smid() << 32) | (uint64_t)tl_j);
+  GEMM_TL(2, __builtin_amdgcn_s_memrealtime());
 }
 
 }  // namespace
@@ -1342,9 +1374,10 @@ size_t mfma_workspace_bytes(int call, int T, int d, int f, int E, int k) {
   return kCntBytes + down_body_bytes(T, d, k) + part_bytes(split_item_cap(T, k, E, gemm_nt(false, d, f)));
 }
 
-// Persistent grid: two workgroups per compute unit (the kernel's occupancy),
-// a multiple of 8 so that every XCD has the same number of workgroups.
-static int persistent_grid(int items) {
+// Persistent grid: per_cu workgroups per compute unit (the kernel's
+// occupancy), a multiple of 8 so that every XCD has the same number of
+// workgroups.
+static int persistent_grid(int items, int per_cu = 2) {
   static int cus = 0;
   if (cus == 0) {
     int dev = 0;
@@ -1352,7 +1385,7 @@ static int persistent_grid(int items) {
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
       cus = 256;
   }
-  const int g = (cus * 2) / 8 * 8;
+  const int g = (cus * per_cu) / 8 * 8;
   return std::max(8, std::min(g, (items + 7) / 8 * 8));
 }
 
@@ -1392,7 +1425,8 @@ template <bool GATEUP>
 static void launch_small(const SmallArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int items = std::min(a.E, a.T * a.k) * a.NC;
   const int per_wg = GATEUP ? kSWaves / 2 : kSWaves;  // items a workgroup runs at a time
-  launch_maybe_timed(k_q4_small<GATEUP>, persistent_grid((items + per_wg - 1) / per_wg), kSThreads, s, ev0, ev1, a);
+  launch_maybe_timed(k_q4_small<GATEUP>, persistent_grid((items + per_wg - 1) / per_wg, SOcc<GATEUP>::value),
+                     kSThreads, s, ev0, ev1, a);
 }
 
 hipError_t launch_gateup_mfma(bool direct, const float* h, const int32_t* offsets, const int32_t* sorted_pair,

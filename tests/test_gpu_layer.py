@@ -389,10 +389,11 @@ def test_rms_rescale():
 
 
 @pytest.mark.parametrize("d,f,E,k,T", [(256, 128, 16, 4, 2), (128, 64, 8, 2, 3), (640, 192, 32, 8, 1),
-                                       (2816, 704, 128, 8, 1)])
+                                       (2816, 704, 128, 8, 1), (256, 2048, 16, 4, 2), (128, 1792, 16, 16, 1)])
 def test_other_shapes_parity(d, f, E, k, T):
     """Shapes whose groups do not fill every K-part (and the full shape again),
-    ungrouped and grouped."""
+    ungrouped and grouped; f of 28 and 32 groups take the down kernels' widest
+    lane slice (8 groups per K-part), with 16 waves per workgroup at k = 16."""
     dm = L.dims(d, f, E, k)
     stride = L.moe_expert_blob_bytes(dm)
     blobs = [synth.expert_blob(d, f, 3, 0, e) for e in range(E)]
