@@ -1057,7 +1057,6 @@ __global__ __launch_bounds__(kSThreads, SOcc<GATEUP>::value) void k_q4_small(Sma
   GEMM_TL(0, __builtin_amdgcn_s_memrealtime());
   int tl_j = 0;  // rounds this workgroup has started (timeline build)
   __shared__ SStage<GATEUP> s_ring[kSWaves][D];
-  __shared__ floatx4 s_red[KS > 1 ? IPW : 1][KS > 1 ? NG : 1][kWave];  // the second K part's accumulators
   __shared__ int s_rank_e[256];             // expert of each small rank
   __shared__ int s_rank_beg[256];
   __shared__ int s_rank_cnt[256];
@@ -1115,17 +1114,26 @@ __global__ __launch_bounds__(kSThreads, SOcc<GATEUP>::value) void k_q4_small(Sma
   const int colq = 32 * (kq >> 1) + 16 * (kq & 1);
 
   const int n_items = n_parts * a.NC;
-  const int is = wid / KS, kh = wid % KS;  // item of this wave within the workgroup, its K part
-  // K steps of this wave's part
-  const int s0 = __builtin_amdgcn_readfirstlane(kh * G / KS), s1 = __builtin_amdgcn_readfirstlane((kh + 1) * G / KS);
+  const int jw = (int)(blockIdx.x / 8);  // this workgroup's index in its XCD
   // every wave runs every round (the K parts meet at barriers); a wave without
   // an item skips its work.  A round's items go slot by slot over the XCD's
-  // workgroups (item slot is of workgroup j runs item is * nper + j), so that
-  // a round with fewer items than slots spreads them over all compute units
+  // workgroups (item slot i of workgroup j runs item i * nper + j), so that a
+  // round with fewer items than slots spreads them over all compute units
   // (workgroups j and j + nper / 2 share one) instead of doubling some up.
-  for (int base = 0; base < n_items; base += IPW * nper) {
-    const int q = base + is * nper + (int)(blockIdx.x / 8);
+  // Gate/up: when the round's items number fewer than two per workgroup, the
+  // first workgroups run one item on all four waves (K quarters) and the rest
+  // two items (K halves), so that every wave has work.
+  for (int base = 0; base < n_items;) {
+    const int rem = n_items - base;
+    const int n4 = GATEUP ? max(0, min(nper, 2 * nper - rem)) : 0;  // workgroups with one item
+    const bool single = jw < n4;
+    const int ks = GATEUP ? (single ? 4 : 2) : 1;  // waves per item
+    const int is = wid / ks, kh = wid % ks;        // item slot of this wave, its K part
+    const int q = single ? base + jw : base + n4 + is * (nper - n4) + (jw - n4);
+    base += n4 + IPW * (nper - n4);
     const bool has = q < n_items;
+    // K steps of this wave's part
+    const int s0 = __builtin_amdgcn_readfirstlane(kh * G / ks), s1 = __builtin_amdgcn_readfirstlane((kh + 1) * G / ks);
     GEMM_TL_ITEM(tl_j, 0, __builtin_amdgcn_s_memrealtime());
     const int u = (has ? q : 0) / a.NC, c = (has ? q : 0) % a.NC;
     // the expert whose parts hold u: s_xpre[i] <= u < s_xpre[i + 1]
@@ -1273,15 +1281,21 @@ __global__ __launch_bounds__(kSThreads, SOcc<GATEUP>::value) void k_q4_small(Sma
     GEMM_TL_ITEM(tl_j, 3, __builtin_amdgcn_s_memrealtime());
     ++tl_j;
     if (KS > 1) {
-      // the second K part's accumulators join the first's
-      if (has && kh == 1)
+      // the other K parts' accumulators join the first's, in part order,
+      // through the weight rings (free once every wave is past its K loop;
+      // no ring DMA is in flight after a wave's last step)
+      floatx4(*red)[3][NG][kWave] = reinterpret_cast<floatx4(*)[3][NG][kWave]>(&s_ring[0][0]);
+      static_assert(sizeof(s_ring) >= 2 * 3 * NG * kWave * sizeof(floatx4), "the rings hold the partials");
+      __syncthreads();
+      if (has && kh != 0)
 #pragma unroll
-        for (int ng = 0; ng < NG; ++ng) s_red[is][ng][lane] = acc[ng];
+        for (int ng = 0; ng < NG; ++ng) red[is][kh - 1][ng][lane] = acc[ng];
       __syncthreads();
       if (has && kh == 0)
+        for (int pk = 1; pk < ks; ++pk)
 #pragma unroll
-        for (int ng = 0; ng < NG; ++ng) acc[ng] += s_red[is][ng][lane];
-      __syncthreads();  // s_red is free for the next round
+          for (int ng = 0; ng < NG; ++ng) acc[ng] += red[is][pk - 1][ng][lane];
+      __syncthreads();  // the rings are free for the next round
     }
     if (!has || kh != 0) continue;
     if (GATEUP) {
