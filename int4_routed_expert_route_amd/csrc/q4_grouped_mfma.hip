@@ -998,7 +998,12 @@ __global__ __launch_bounds__(256) void k_combine_scaled(const _Float16* __restri
 constexpr int kSRows = 32;                // most pairs per expert on this path
 constexpr int kSWaves = 4;
 constexpr int kSThreads = kSWaves * kWave;
-constexpr int kSAhead = 3;                // activation steps in flight per wave
+// activation steps in flight per wave: gate/up 2 (its ring of 2 steps lets
+// three workgroups share a compute unit), down 3
+template <bool GATEUP>
+struct SAhead {
+  static constexpr int value = GATEUP ? 2 : 3;
+};
 
 struct SmallArgs {
   const void* a_rows;     // gate/up: h fp16 [T][d] in slot order; down: act values fp16 [T*k][f]
@@ -1028,14 +1033,14 @@ struct SStage {
 };
 template <bool GATEUP>
 struct SDepth {
-  static constexpr int value = GATEUP ? 3 : 5;  // weight steps in flight per wave (>= kSAhead)
+  static constexpr int value = GATEUP ? 2 : 5;  // weight steps in flight per wave (>= SAhead)
 };
-// Workgroups per compute unit: down runs three (12 waves; its LDS ring of 5
-// steps fits three times), so that a 32-token batch's ~2,100 down items take
-// one round instead of two for a few workgroups.
+// Workgroups per compute unit: three (12 waves; the LDS rings of 2 gate/up or
+// 5 down steps fit three times), so that a 32-token batch's ~530 gate/up and
+// ~2,100 down items take one round, every gate/up item on four waves.
 template <bool GATEUP>
 struct SOcc {
-  static constexpr int value = GATEUP ? 2 : 3;
+  static constexpr int value = 3;
 };
 // Per-step activation operand of one lane: the 16 columns this lane
 // multiplies (two MFMA K slices of 8) and (down) the row's exponent for the step.
@@ -1052,7 +1057,8 @@ __global__ __launch_bounds__(kSThreads, SOcc<GATEUP>::value) void k_q4_small(Sma
   constexpr int D = SDepth<GATEUP>::value;
   constexpr int KS = GATEUP ? 2 : 1;        // waves per item (K parts)
   constexpr int IPW = kSWaves / KS;         // items per workgroup at a time
-  static_assert(D >= kSAhead, "a step's weights must be requested before its activations");
+  constexpr int kSA = SAhead<GATEUP>::value;
+  static_assert(D >= kSA, "a step's weights must be requested before its activations");
   typedef Op<_Float16> O;
   GEMM_TL(0, __builtin_amdgcn_s_memrealtime());
   int tl_j = 0;  // rounds this workgroup has started (timeline build)
@@ -1232,7 +1238,7 @@ __global__ __launch_bounds__(kSThreads, SOcc<GATEUP>::value) void k_q4_small(Sma
       return h;
     };
     // step s: its weights from the ring (the slot is then refilled with step
-    // s + D), the activations of step s + kSAhead, dequant and MFMAs
+    // s + D), the activations of step s + kSA, dequant and MFMAs
     auto one = [&](int s, const SAct& vc, SAct& vf) {
       landed(vc);
       const SStage<GATEUP>& st = ring[(s - s0) % D];
@@ -1245,10 +1251,10 @@ __global__ __launch_bounds__(kSThreads, SOcc<GATEUP>::value) void k_q4_small(Sma
         sbv[ng] = st.sb[m][rr + n];
       }
       asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(qv[0]), "+v"(sbv[0])::"memory");
-      // the weights of step s + D, then the activations of step s + kSAhead
+      // the weights of step s + D, then the activations of step s + kSA
       // (the latter unconditional: no half-defined buffer)
       if (s + D < s1) dma(s + D);
-      fetch_a(s + kSAhead < s1 ? s + kSAhead : s1 - 1, vf);
+      fetch_a(s + kSA < s1 ? s + kSA : s1 - 1, vf);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const f16x8 av = a_slice(vc, j);
@@ -1264,18 +1270,31 @@ __global__ __launch_bounds__(kSThreads, SOcc<GATEUP>::value) void k_q4_small(Sma
     GEMM_TL_ITEM(tl_j, 1, ((uint64_t)q << 32) | ((uint64_t)rows << 16));
     GEMM_TL_ITEM(tl_j, 2, __builtin_amdgcn_s_memrealtime());
     if (has && s0 < s1) {
-      SAct v0, v1, v2, v3;
-      fetch_a(s0, v0);
-      fetch_a(s0 + 1 < s1 ? s0 + 1 : s1 - 1, v1);
-      fetch_a(s0 + 2 < s1 ? s0 + 2 : s1 - 1, v2);
-      for (int s = s0; s < s1; s += 4) {
-        one(s, v0, v3);
-        if (s + 1 >= s1) break;
-        one(s + 1, v1, v0);
-        if (s + 2 >= s1) break;
-        one(s + 2, v2, v1);
-        if (s + 3 >= s1) break;
-        one(s + 3, v3, v2);
+      if constexpr (kSA == 3) {
+        SAct v0, v1, v2, v3;
+        fetch_a(s0, v0);
+        fetch_a(s0 + 1 < s1 ? s0 + 1 : s1 - 1, v1);
+        fetch_a(s0 + 2 < s1 ? s0 + 2 : s1 - 1, v2);
+        for (int s = s0; s < s1; s += 4) {
+          one(s, v0, v3);
+          if (s + 1 >= s1) break;
+          one(s + 1, v1, v0);
+          if (s + 2 >= s1) break;
+          one(s + 2, v2, v1);
+          if (s + 3 >= s1) break;
+          one(s + 3, v3, v2);
+        }
+      } else {
+        SAct v0, v1, v2;
+        fetch_a(s0, v0);
+        fetch_a(s0 + 1 < s1 ? s0 + 1 : s1 - 1, v1);
+        for (int s = s0; s < s1; s += 3) {
+          one(s, v0, v2);
+          if (s + 1 >= s1) break;
+          one(s + 1, v1, v0);
+          if (s + 2 >= s1) break;
+          one(s + 2, v2, v1);
+        }
       }
     }
     GEMM_TL_ITEM(tl_j, 3, __builtin_amdgcn_s_memrealtime());
@@ -1284,17 +1303,19 @@ __global__ __launch_bounds__(kSThreads, SOcc<GATEUP>::value) void k_q4_small(Sma
       // the other K parts' accumulators join the first's, in part order,
       // through the weight rings (free once every wave is past its K loop;
       // no ring DMA is in flight after a wave's last step)
-      floatx4(*red)[3][NG][kWave] = reinterpret_cast<floatx4(*)[3][NG][kWave]>(&s_ring[0][0]);
-      static_assert(sizeof(s_ring) >= 2 * 3 * NG * kWave * sizeof(floatx4), "the rings hold the partials");
+      // partial (slot is, part kh > 0) at is * (ks - 1) + kh - 1: at most 3
+      // (one item on four waves, or two items on two waves each)
+      floatx4(*red)[NG][kWave] = reinterpret_cast<floatx4(*)[NG][kWave]>(&s_ring[0][0]);
+      static_assert(sizeof(s_ring) >= 3 * NG * kWave * sizeof(floatx4), "the rings hold the partials");
       __syncthreads();
       if (has && kh != 0)
 #pragma unroll
-        for (int ng = 0; ng < NG; ++ng) red[is][kh - 1][ng][lane] = acc[ng];
+        for (int ng = 0; ng < NG; ++ng) red[is * (ks - 1) + kh - 1][ng][lane] = acc[ng];
       __syncthreads();
       if (has && kh == 0)
         for (int pk = 1; pk < ks; ++pk)
 #pragma unroll
-          for (int ng = 0; ng < NG; ++ng) acc[ng] += red[is][pk - 1][ng][lane];
+          for (int ng = 0; ng < NG; ++ng) acc[ng] += red[is * (ks - 1) + pk - 1][ng][lane];
       __syncthreads();  // the rings are free for the next round
     }
     if (!has || kh != 0) continue;
