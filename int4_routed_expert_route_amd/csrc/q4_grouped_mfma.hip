@@ -1067,7 +1067,8 @@ __global__ __launch_bounds__(kSThreads, SOcc<GATEUP>::value) void k_q4_small(Sma
   __shared__ int s_rank_beg[256];
   __shared__ int s_rank_cnt[256];
   __shared__ int s_wave_n[kSWaves];
-  __shared__ int s_xpre[256 / 8 + 1];       // this XCD's experts: 16-pair parts before each
+  __shared__ int s_ppre[256 + 1];           // 16-pair parts of the ranks before each rank
+  __shared__ int s_xb[2 * kSWaves];         // per wave: first rank of this XCD's stretch, of the next
   const int t = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(t / kWave), lane = t % kWave;
   const int n = lane % 16, kq = lane / 16;
@@ -1099,17 +1100,40 @@ __global__ __launch_bounds__(kSThreads, SOcc<GATEUP>::value) void k_q4_small(Sma
   }
   const int n_small = s_wave_n[0] + s_wave_n[1] + s_wave_n[2] + s_wave_n[3];
   const int xcd = (int)(blockIdx.x % 8), nper = (int)(gridDim.x / 8);
-  const int mine = n_small > xcd ? (n_small - xcd + 7) / 8 : 0;  // experts of this XCD: ranks xcd + 8 i
-  if (t == 0) {
-    int acc_parts = 0;
-    for (int i = 0; i < mine; ++i) {
-      s_xpre[i] = acc_parts;
-      acc_parts += s_rank_cnt[xcd + 8 * i] > 16 ? 2 : 1;
+  // XCD x runs the ranks whose first part falls in [x P / 8, (x + 1) P / 8)
+  // of the P parts (whole experts, so an expert's parts share one L2; the
+  // XCDs' part counts differ by at most one expert's).  Dealing the ranks
+  // round-robin left one XCD with half again the average, and a second round.
+  {
+    const int np = t < n_small ? (s_rank_cnt[t] > 16 ? 2 : 1) : 0;
+    int inc = np;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(inc, o, kWave);
+      if (lane >= o) inc += v;
     }
-    s_xpre[mine] = acc_parts;
+    if (lane == kWave - 1) s_wave_n[wid] = inc;  // s_wave_n's counts are no longer needed
+    __syncthreads();
+    int before = inc - np;
+    for (int w = 0; w < wid; ++w) before += s_wave_n[w];
+    s_ppre[t] = before;
+    if (t == 0) s_ppre[256] = s_wave_n[0] + s_wave_n[1] + s_wave_n[2] + s_wave_n[3];
+    __syncthreads();
+    const int P = s_ppre[256];
+    const int lo = (xcd * P + 7) / 8, hi = ((xcd + 1) * P + 7) / 8;
+    // first rank whose parts start at or past each bound (n_small past the last)
+    const bool at_lo = t < n_small && s_ppre[t] >= lo, at_hi = t < n_small && s_ppre[t] >= hi;
+    const uint64_t b_lo = __ballot(at_lo), b_hi = __ballot(at_hi);
+    if (lane == 0) {
+      s_xb[wid] = b_lo ? wid * kWave + __builtin_ctzll(b_lo) : 256;
+      s_xb[kSWaves + wid] = b_hi ? wid * kWave + __builtin_ctzll(b_hi) : 256;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  const int n_parts = s_xpre[mine];
+  const int r_lo = min(n_small, min(min(s_xb[0], s_xb[1]), min(s_xb[2], s_xb[3])));
+  const int r_hi = min(n_small, min(min(s_xb[4], s_xb[5]), min(s_xb[6], s_xb[7])));
+  const int p_lo = s_ppre[r_lo];  // s_ppre[n_small] = P: ranks past n_small have no parts
+  const int n_parts = s_ppre[r_hi] - p_lo;
   GEMM_TL(1, __builtin_amdgcn_s_memrealtime());
   const __amdgpu_buffer_rsrc_t rsA =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.a_rows), (short)0, a.a_bytes, kRsrcWord3);
@@ -1142,18 +1166,18 @@ __global__ __launch_bounds__(kSThreads, SOcc<GATEUP>::value) void k_q4_small(Sma
     const int s0 = __builtin_amdgcn_readfirstlane(kh * G / ks), s1 = __builtin_amdgcn_readfirstlane((kh + 1) * G / ks);
     GEMM_TL_ITEM(tl_j, 0, __builtin_amdgcn_s_memrealtime());
     const int u = (has ? q : 0) / a.NC, c = (has ? q : 0) % a.NC;
-    // the expert whose parts hold u: s_xpre[i] <= u < s_xpre[i + 1]
-    int i = 0;
-    for (int lo = 0, hi = mine - 1; lo <= hi;) {
+    // the rank whose parts hold part p_lo + u: s_ppre[r] <= p_lo + u < s_ppre[r + 1]
+    int rank = r_lo;
+    for (int lo = r_lo, hi = r_hi - 1; lo <= hi;) {
       const int mid = (lo + hi) / 2;
-      if (s_xpre[mid] <= u) {
-        i = mid;
+      if (s_ppre[mid] <= p_lo + u) {
+        rank = mid;
         lo = mid + 1;
       } else {
         hi = mid - 1;
       }
     }
-    const int rank = xcd + 8 * i, part = u - s_xpre[i];
+    const int part = p_lo + u - s_ppre[rank];
     const int e = __builtin_amdgcn_readfirstlane(s_rank_e[rank]);
     const int beg = __builtin_amdgcn_readfirstlane(s_rank_beg[rank] + 16 * part);
     const int all_rows = s_rank_cnt[rank] - 16 * part;
@@ -1459,7 +1483,7 @@ constexpr int kSmallPathT = 64;
 template <bool GATEUP>
 static void launch_small(const SmallArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int items = std::min(a.E, a.T * a.k) * a.NC;
-  const int per_wg = GATEUP ? kSWaves / 2 : kSWaves;  // items a workgroup runs at a time
+  const int per_wg = GATEUP ? 1 : kSWaves;  // items a workgroup runs at a time (gate/up: one on four waves)
   launch_maybe_timed(k_q4_small<GATEUP>, persistent_grid((items + per_wg - 1) / per_wg, SOcc<GATEUP>::value),
                      kSThreads, s, ev0, ev1, a);
 }
