@@ -59,9 +59,9 @@ TRAFFIC = {
     "decode_fused": {"sources": ('int4_routed_expert_route_amd/csrc/decode_fused.hip', 'int4_routed_expert_route_amd/csrc/q4_lane.h', 'int4_routed_expert_route_amd/csrc/common.h', 'synth/__init__.py'),
                     "sha256_16": "623ed829d9719102", "fetch_bytes": 954423481, "write_bytes": 8174496},
     "prefill": {"sources": ('int4_routed_expert_route_amd/csrc/q4_grouped_mfma.hip', 'int4_routed_expert_route_amd/csrc/common.h', 'synth/__init__.py'),
-               "sha256_16": "b837c34a38127c4f", "fetch_bytes": 424809754, "write_bytes": 24086400},
+               "sha256_16": "3006036b93657269", "fetch_bytes": 424993686, "write_bytes": 24089248},
     "batched_f16": {"sources": ('int4_routed_expert_route_amd/csrc/q4_grouped_mfma.hip', 'int4_routed_expert_route_amd/csrc/common.h', 'synth/__init__.py'),
-                   "sha256_16": "b837c34a38127c4f", "fetch_bytes": 99941296, "write_bytes": 369632},
+                   "sha256_16": "3006036b93657269", "fetch_bytes": 101580044, "write_bytes": 369760},
 }
 
 
