@@ -846,55 +846,62 @@ __global__ __launch_bounds__(kThreads, 2) void k_q4_gemm(GemmArgs a) {
     // ---- epilogue
     if (GATEUP) {
       // acc[mg][ng][i] = C[pair row mg*16 + kq*4 + i][weight row ng*16 + n of the wave];
-      // act = gelu(gate) * up for wave columns c*16 + n, c = 0, 1
-      float v[8][2][4];
+      // act = gelu(gate) * up for wave columns c*16 + n, c = 0, 1.  The act
+      // values go to an fp32 tile [128 rows][128 columns] in the stages' LDS
+      // (free after the K loop), the block maximum on the way; then every
+      // thread scales, converts and stores 16-byte runs of a row (each wave
+      // stored single 16-bit values before, 64 store instructions a lane).
+      float* tile = reinterpret_cast<float*>(&lds[0]);
+      static_assert(sizeof(lds) >= (size_t)BM * 128 * sizeof(float), "the stages hold the act tile");
       float m = 0.0f;
+      if (wave_ok) {
+        // this lane's element of row kq * 4, column c * 16 + n of the wave, at
+        // its slot position; the others lie at constant offsets from it (the
+        // address is made opaque here, or the compiler builds all 64 at the
+        // kernel's start and spills them)
+        const int col = wid * (WN / 2) + n;
+        uint32_t at = lds_addr(&lds[0]) + (uint32_t)(((kq * 4) * 128 + (col & ~7) + (col & 3) * 2 + ((col >> 2) & 1)) * 4);
+        asm volatile("" : "+v"(at));
+        typedef __attribute__((address_space(3))) float* lds_f32_t;
+        const lds_f32_t tp = (lds_f32_t)(uintptr_t)at;
 #pragma unroll
-      for (int mg = 0; mg < 8; ++mg) {
-        if (mg >= n_mg) {  // row groups past the tile's rows are not stored
+        for (int mg = 0; mg < 8; ++mg) {
+          if (mg >= n_mg) continue;  // row groups past the tile's rows are not stored
 #pragma unroll
           for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[mg][c][i] = 0.0f;
-          continue;
-        }
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float g = acc[mg][c][i], u = acc[mg][c + 2][i];
-            v[mg][c][i] = ok ? gelu_tanh_act16(g) * u : f32_nan();
-            if (mg * 16 + kq * 4 + i < rows) m = fmaxf(m, fabsf(v[mg][c][i]));
-          }
-      }
-      int ex = 0;
-      if (O::kScaled) {
-        // one exponent per M tile and 64-column group (waves 2g', 2g'+1)
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-        if (lane == 0) s_wmax[wid] = wave_ok ? m : 0.0f;
-        __syncthreads();
-        ex = block_exp(fmaxf(s_wmax[wid], s_wmax[wid ^ 1]));
-      }
-      if (wave_ok) {
-        const float sc = exp2i(-ex);
-        const int Gf = a.f / kGroup;
-        const int grp = wave_base / kGroup;
-#pragma unroll
-        for (int mg = 0; mg < 8; ++mg)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = mg * 16 + kq * 4 + i;
-            const int p = s_pair[r];
-            if (p < 0) continue;
-            ET* dst = reinterpret_cast<ET*>(a.out) + (int64_t)p * a.f;
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-              const int col = wave_base + c * 16 + n;  // stored at its slot position
-              dst[(col & ~7) + (col & 3) * 2 + ((col >> 2) & 1)] = (ET)(v[mg][c][i] * sc);
+            for (int i = 0; i < 4; ++i) {
+              const float g = acc[mg][c][i], u = acc[mg][c + 2][i];
+              const float x = ok ? gelu_tanh_act16(g) * u : f32_nan();
+              tp[(mg * 16 + i) * 128 + c * 16] = x;
+              if (mg * 16 + kq * 4 + i < rows) m = fmaxf(m, fabsf(x));
             }
-            if (n == 0 && (wid & 1) == 0) a.out_exp[(int64_t)p * Gf + grp] = (int8_t)ex;
-          }
+        }
+      }
+      // one exponent per M tile and 64-column group (waves 2g', 2g'+1)
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+      if (lane == 0) s_wmax[wid] = wave_ok ? m : 0.0f;
+      __syncthreads();
+      {
+        const int Gf = a.f / kGroup, col0 = nt * (BN / 2);
+        // chunk q: row q / 16, tile columns 8 (q % 16) .. + 7
+#pragma unroll 2
+        for (int k = 0; k < BM * 16 / kThreads; ++k) {
+          const int q = k * kThreads + t, r = q / 16, cc = (q % 16) * 8;
+          const int p = r < rows ? s_pair[r] : -1;
+          if (p < 0 || col0 + cc >= a.f) continue;
+          const int g2 = cc / kGroup;  // the tile's 64-column group: waves 2 g2, 2 g2 + 1
+          const int ex = block_exp(fmaxf(s_wmax[2 * g2], s_wmax[2 * g2 + 1]));
+          const float sc = exp2i(-ex);
+          const float4 lo = *reinterpret_cast<const float4*>(tile + r * 128 + cc);
+          const float4 hi = *reinterpret_cast<const float4*>(tile + r * 128 + cc + 4);
+          ET o[8] = {(ET)(lo.x * sc), (ET)(lo.y * sc), (ET)(lo.z * sc), (ET)(lo.w * sc),
+                     (ET)(hi.x * sc), (ET)(hi.y * sc), (ET)(hi.z * sc), (ET)(hi.w * sc)};
+          *reinterpret_cast<uint4*>(reinterpret_cast<ET*>(a.out) + (int64_t)p * a.f + col0 + cc) =
+              *reinterpret_cast<const uint4*>(o);
+          if (cc % kGroup == 0) a.out_exp[(int64_t)p * Gf + (col0 + cc) / kGroup] = (int8_t)ex;
+        }
       }
     } else if (wave_ok) {
       // acc[mg][ng][i] = C[output column ng*16 + kq*4 + i of the wave][pair row mg*16 + n]
