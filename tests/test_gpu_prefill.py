@@ -107,6 +107,45 @@ def test_prefill_parity_small(api, d, f, E_, k, T, prec):
     assert e_y < tol
 
 
+class UniformLayer(SmallLayer):
+    """No router bias: the choice spreads nearly evenly over the experts."""
+
+    def __init__(self, d, f, E_, seed):
+        super().__init__(d, f, E_, seed)
+        self.bias = None
+
+
+@pytest.mark.parametrize("d,f,E_,k,T", [(2816, 704, 128, 8, 64), (1024, 1408, 128, 8, 64)])
+def test_few_pairs_multi_item_rounds(api, d, f, E_, k, T):
+    """Batches of up to 64 tokens send experts of at most 32 pairs to the
+    few-pairs kernel.  Spread evenly, 512 pairs over 128 experts give every
+    XCD about 16 expert parts: with f=704 that is more gate/up items than the
+    XCD's 96 workgroups, so a round mixes workgroups running one item on four
+    waves with ones running two on K halves; with f=1408 a round of two items
+    per workgroup comes first.  d=2816 gives down two rounds of four items per
+    workgroup.  The premise is checked on the oracle's routing."""
+    tol = TOL_BF16
+    layer = UniformLayer(d, f, E_, seed=11)
+    x_np = synth.tokens(T, d, seed=11, stream=T)
+    _, lg, ridx, _ = orc.route(x_np, layer.norm_w, layer.router_w, layer.bias, k)
+    cnt = np.bincount(np.asarray(ridx).ravel(), minlength=E_)
+    parts = int(np.sum((cnt > 0) & (cnt <= 16)) + 2 * np.sum((cnt > 16) & (cnt <= 32)))
+    assert parts * (f // 64) > 8 * 96, f"only {parts} expert parts: no multi-item gate/up round"
+    arena = torch.from_numpy(np.concatenate([layer.blobs[e] for e in range(E_)])).cuda()
+    out = run_prefill(api, x_np, layer, arena, d, f, E_, k)
+    gi = _np(out["idx"])
+    check_topk(gi, ridx, lg)
+    ry, _, _, rh, _ = orc.moe_layer(x_np, layer.norm_w, layer.router_w, layer.bias, layer.blob_of, d, f, k,
+                                    idx_override=gi)
+    ract = np.stack([orc.expert_gateup(layer.blobs[int(gi[t, j])], rh[t], d, f)[0]
+                     for t in range(T) for j in range(k)])
+    e_act = row_rel_err(out["act"], ract)
+    e_y = row_rel_err(_np(out["y"]) - x_np, ry - x_np)
+    print(f"parts {parts}  act {e_act:.3e}  moe-out {e_y:.3e}", flush=True)
+    assert e_act < tol
+    assert e_y < tol
+
+
 @pytest.mark.parametrize("prec", ["f16", "f16direct"])
 def test_prefill_large_activations(api, prec):
     """On weights with a positive mean offset, inputs close to a constant
