@@ -67,7 +67,12 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restr
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   auto expert_of = [&](int v) { return (v >= 0 && v < E) ? v : -1; };
 
-  // walk 1: position of each pair among its wave's pairs of the same expert
+  // walk 1: position of each pair among its wave's pairs of the same expert.
+  // When the wave's pairs fit one batch (every wave of a launch with at most
+  // kBatch * kPermThreads pairs), walk 2 takes the experts and the positions
+  // from registers instead of reloading them.
+  const bool one = p1 - p0 <= kBatch * kWave;
+  int k_e[kBatch], k_loc[kBatch];
   for (int b0 = p0; b0 < p1; b0 += kBatch * kWave) {
     int ids[kBatch];
 #pragma unroll
@@ -82,7 +87,9 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restr
       int before = 0;
       if (e >= 0) before = s_cnt[wave][e];
       if (e >= 0 && rank == 0) s_cnt[wave][e] = before + __popcll(same);
-      if (p < p1) pair_pos[p] = e >= 0 ? before + rank : -1;
+      k_e[r] = e;
+      k_loc[r] = e >= 0 ? before + rank : -1;
+      if (p < p1 && (!one || e < 0)) pair_pos[p] = k_loc[r];
     }
   }
   __syncthreads();
@@ -127,6 +134,20 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restr
   }
   __syncthreads();
   // walk 2: final positions
+  if (one) {
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {
+      const int p = p0 + r * kWave + lane;
+      if (p0 + r * kWave >= p1) break;  // wave-uniform
+      const int e = k_e[r];             // -1 past p1
+      if (e >= 0) {
+        const int pos = s_base[e] + s_cnt[wave][e] + k_loc[r];
+        sorted_pair[pos] = p;
+        pair_pos[p] = pos;
+      }
+    }
+    return;
+  }
   for (int b0 = p0; b0 < p1; b0 += kBatch * kWave) {
     int ids[kBatch], loc[kBatch];
 #pragma unroll
