@@ -339,6 +339,9 @@ __global__ __launch_bounds__(kRWaves * kWave) void k_router_mfma(const float* __
 // partials per expert group, the row, the norm weights, the h stores); with one
 // wave per workgroup the tokens spread over T compute units instead of T/4,
 // whose instruction issue was the limit.
+// MS: slices the kernel holds (>= slices): 16 unless there are more, since the
+// partials' registers limit how many tokens' waves a SIMD holds.
+template <int MS>
 __global__ __launch_bounds__(kWave) void k_topk(const float* __restrict__ partial, int slices,
                                               const float* __restrict__ x, const float* __restrict__ norm_w,
                                               float eps, int d, const float* __restrict__ router_bias, int T,
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(kWave) void k_topk(const float* __restrict__ partia
   if (t >= T) return;
   // every slice's partial and the token's row go out before the first add (a
   // loop of dependent loads would pay one memory round trip per slice)
-  float p[4][kMaxSlices];
+  float p[4][MS];
   bool ok[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -358,7 +361,7 @@ __global__ __launch_bounds__(kWave) void k_topk(const float* __restrict__ partia
     if (kWave * i >= E) continue;  // wave-uniform: no expert of this lane group
     const int ec = min(e, E - 1);
 #pragma unroll
-    for (int s = 0; s < kMaxSlices; ++s) p[i][s] = partial[((size_t)min(s, slices - 1) * T + t) * E + ec];
+    for (int s = 0; s < MS; ++s) p[i][s] = partial[((size_t)min(s, slices - 1) * T + t) * E + ec];
   }
   // the bias, and the token's row with its norm weights: all of it at once
   // when it fits in registers (none of these loads waits for the row's sum)
@@ -396,7 +399,7 @@ __global__ __launch_bounds__(kWave) void k_topk(const float* __restrict__ partia
   for (int i = 0; i < 4; ++i) {
     float acc = 0.0f;
 #pragma unroll
-    for (int s = 0; s < kMaxSlices; ++s)
+    for (int s = 0; s < MS; ++s)
       if (s < slices) acc += p[i][s];
     acc *= rinv;
     acc += bv[i];
@@ -450,8 +453,12 @@ hipError_t launch_route(const float* x, const float* norm_w, float eps, const fl
   else
     launch_maybe_timed2(k_router_mfma<1>, dim3((T + rt - 1) / rt, sp.slices), kRWaves * kWave, s, ev0, ev1, x,
                         norm_w, router_w, T, d, E, sp.kslice, logits);
-  hipLaunchKernelGGL(k_topk, dim3(T), dim3(kWave), 0, s, logits, sp.slices, x, norm_w, eps, d, router_bias,
-                     T, E, k, h_out, topk_idx, topk_w);
+  if (sp.slices <= 16)
+    hipLaunchKernelGGL(k_topk<16>, dim3(T), dim3(kWave), 0, s, logits, sp.slices, x, norm_w, eps, d, router_bias,
+                       T, E, k, h_out, topk_idx, topk_w);
+  else
+    hipLaunchKernelGGL(k_topk<kMaxSlices>, dim3(T), dim3(kWave), 0, s, logits, sp.slices, x, norm_w, eps, d,
+                       router_bias, T, E, k, h_out, topk_idx, topk_w);
   return hipGetLastError();
 }
 
