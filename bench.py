@@ -59,9 +59,9 @@ TRAFFIC = {
     "decode_fused": {"sources": ('int4_routed_expert_route_amd/csrc/decode_fused.hip', 'int4_routed_expert_route_amd/csrc/q4_lane.h', 'int4_routed_expert_route_amd/csrc/common.h', 'synth/__init__.py'),
                     "sha256_16": "623ed829d9719102", "fetch_bytes": 954423481, "write_bytes": 8174496},
     "prefill": {"sources": ('int4_routed_expert_route_amd/csrc/q4_grouped_mfma.hip', 'int4_routed_expert_route_amd/csrc/common.h', 'synth/__init__.py'),
-               "sha256_16": "3006036b93657269", "fetch_bytes": 424993686, "write_bytes": 24089248},
+               "sha256_16": "4cb4c1ec9e489d26", "fetch_bytes": 424540512, "write_bytes": 24117024},
     "batched_f16": {"sources": ('int4_routed_expert_route_amd/csrc/q4_grouped_mfma.hip', 'int4_routed_expert_route_amd/csrc/common.h', 'synth/__init__.py'),
-                   "sha256_16": "3006036b93657269", "fetch_bytes": 101580044, "write_bytes": 369760},
+                   "sha256_16": "4cb4c1ec9e489d26", "fetch_bytes": 102118016, "write_bytes": 369760},
 }
 
 
