@@ -87,7 +87,8 @@ def _np(t):
 
 @pytest.mark.parametrize("T,norm,bias", [(1, False, False), (1, True, True), (3, True, True),
                                          (8, True, True), (9, True, True), (32, True, True),
-                                         (32, False, True), (40, False, False), (257, True, False)])
+                                         (32, False, True), (40, False, False), (257, True, False),
+                                         (600, True, True), (1024, True, True), (2048, False, True)])
 def test_route_parity(layer0, dev_layer, T, norm, bias):
     x = synth.tokens(T, D, seed=0, stream=T)
     h, idx, w = _route(torch.from_numpy(x).cuda(), dev_layer, T, norm, bias)
