@@ -61,7 +61,7 @@ TRAFFIC = {
     "prefill": {"sources": ('int4_routed_expert_route_amd/csrc/q4_grouped_mfma.hip', 'int4_routed_expert_route_amd/csrc/common.h', 'synth/__init__.py'),
                "sha256_16": "4cb4c1ec9e489d26", "fetch_bytes": 424540512, "write_bytes": 24117024},
     "batched_f16": {"sources": ('int4_routed_expert_route_amd/csrc/q4_grouped_mfma.hip', 'int4_routed_expert_route_amd/csrc/common.h', 'synth/__init__.py'),
-                   "sha256_16": "4cb4c1ec9e489d26", "fetch_bytes": 102118016, "write_bytes": 369760},
+                   "sha256_16": "4cb4c1ec9e489d26", "fetch_bytes": 102038722, "write_bytes": 369760},
 }
 
 
