@@ -83,6 +83,31 @@ __device__ __forceinline__ uint64_t dpp_max_step(uint64_t k) {
   const uint64_t o = ((uint64_t)ohi << 32) | olo;
   return o > k ? o : k;
 }
+// One DPP step of a sum: lanes the operation does not write add zero.
+template <int CTRL, int ROW_MASK, typename T>
+__device__ __forceinline__ T dpp_add_step(T v) {
+  const int o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false);
+  return v + __builtin_bit_cast(T, o);
+}
+// Sum over aligned groups of 2, 4 or 8 lanes (n), every lane of a group ending
+// with the group's sum: quad_perm [1,0,3,2], [2,3,0,1], then row_half_mirror.
+template <typename T>
+__device__ __forceinline__ T group_sum_dpp(T v, int n) {
+  if (n >= 2) v = dpp_add_step<0xB1, 0xF>(v);
+  if (n >= 4) v = dpp_add_step<0x4E, 0xF>(v);
+  if (n >= 8) v = dpp_add_step<0x141, 0xF>(v);
+  return v;
+}
+// Sum over a fully active wave by DPP row operations in a fixed order (no LDS
+// permutes): groups of 8, row_mirror for rows of 16, then row_bcast:15 and
+// :31 leave the total in lane 63, which every lane reads back.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = group_sum_dpp(v, 8);
+  v = dpp_add_step<0x140, 0xF>(v);
+  v = dpp_add_step<0x142, 0xA>(v);
+  v = dpp_add_step<0x143, 0xC>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
 // Maximum of k over the wave, in every lane.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
   k = dpp_max_step<0xB1, 0xF>(k);   // quad_perm [1,0,3,2]

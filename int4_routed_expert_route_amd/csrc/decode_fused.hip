@@ -279,12 +279,12 @@ __device__ __forceinline__ void write_partials(const FusedArgs& a, int t, int la
       for (int i = 0; i < 8; ++i)
         if (i < rpt) s = fmaf(w[i], z[q * rpt + i], s);
     }
-    for (int o = 1; o < tq; o <<= 1) s += __shfl_xor(s, o, kWave);
+    s = group_sum_dpp(s, tq);
     if (e < a.E && q == 0) s_pe[e] = s;
   }
   if (t < kWave) {
     const float v = t < kDR ? y[t] : 0.0f;
-    const float ss = wave_sum(v * v);
+    const float ss = wave_sum_dpp(v * v);
     if (t == 0) st_e(rc, (int)a.ss_off + layer * a.ss_ls + g, ss);
   }
   __syncthreads();
@@ -418,13 +418,10 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
           acc.z += u.z;
           acc.w += u.w;
         }
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          acc.x += __shfl_xor(acc.x, o, kWave);
-          acc.y += __shfl_xor(acc.y, o, kWave);
-          acc.z += __shfl_xor(acc.z, o, kWave);
-          acc.w += __shfl_xor(acc.w, o, kWave);
-        }
+        acc.x = wave_sum_dpp(acc.x);
+        acc.y = wave_sum_dpp(acc.y);
+        acc.z = wave_sum_dpp(acc.z);
+        acc.w = wave_sum_dpp(acc.w);
         if (lane == 0) st_e4(rc, (int)a.qs_off + l * a.qs_ls + 4 * g, acc);
         DECODE_TL(l, 9);  // reducer: its 4 sums written
       }
@@ -438,7 +435,7 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
       float ss = 0.0f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) ss += lane + c * kWave < a.G ? dec(ssu[c]) : 0.0f;
-      ss = wave_sum(ss);
+      ss = wave_sum_dpp(ss);
       if (lane == 0) s_inv = a.norm_w ? 1.0f / sqrtf(ss / (float)a.d + a.eps) : 1.0f;
     }
     if (l > 0) {
@@ -486,7 +483,7 @@ __global__ __launch_bounds__(kFThreads) void k_decode_fused(FusedArgs a) {
           beats += (((uint64_t)u.w << 32 | u.z) > kv) ? 1 : 0;
         }
       }
-      for (int o = 1; o < tq; o <<= 1) beats += __shfl_xor(beats, o, kWave);
+      beats = group_sum_dpp(beats, tq);
       if (e < a.E && q == 0 && beats < a.k) {
         s_idx[beats] = e;
         s_val[beats] = v;
