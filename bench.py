@@ -55,13 +55,13 @@ CSRC = os.path.join(ROOT, "int4_routed_expert_route_amd", "csrc")
 # root); reported as null once either differs.
 TRAFFIC = {
     "decode": {"sources": ('int4_routed_expert_route_amd/csrc/q4_gemv.hip', 'int4_routed_expert_route_amd/csrc/q4_lane.h', 'int4_routed_expert_route_amd/csrc/common.h', 'synth/__init__.py'),
-              "sha256_16": "559cc8c78d988888", "fetch_bytes": 18095667, "write_bytes": 22528},
+              "sha256_16": "8e9b70a6e5078a6f", "fetch_bytes": 18094707, "write_bytes": 22528},
     "decode_fused": {"sources": ('int4_routed_expert_route_amd/csrc/decode_fused.hip', 'int4_routed_expert_route_amd/csrc/q4_lane.h', 'int4_routed_expert_route_amd/csrc/common.h', 'synth/__init__.py'),
-                    "sha256_16": "dab34a1595859fbd", "fetch_bytes": 954445625, "write_bytes": 8174496},
+                    "sha256_16": "8f2bae3354a96ba3", "fetch_bytes": 954526903, "write_bytes": 8174496},
     "prefill": {"sources": ('int4_routed_expert_route_amd/csrc/q4_grouped_mfma.hip', 'int4_routed_expert_route_amd/csrc/common.h', 'synth/__init__.py'),
-               "sha256_16": "4c2dbfd3d4d9b482", "fetch_bytes": 424127529, "write_bytes": 24117872},
+               "sha256_16": "0f438898effa6248", "fetch_bytes": 424294437, "write_bytes": 24117024},
     "batched_f16": {"sources": ('int4_routed_expert_route_amd/csrc/q4_grouped_mfma.hip', 'int4_routed_expert_route_amd/csrc/common.h', 'synth/__init__.py'),
-                   "sha256_16": "4c2dbfd3d4d9b482", "fetch_bytes": 102048130, "write_bytes": 369760},
+                   "sha256_16": "0f438898effa6248", "fetch_bytes": 102122368, "write_bytes": 369744},
 }
 
 

@@ -98,6 +98,18 @@ __device__ __forceinline__ T group_sum_dpp(T v, int n) {
   if (n >= 8) v = dpp_add_step<0x141, 0xF>(v);
   return v;
 }
+// Maximum over aligned groups of 8 lanes, in every lane of the group (lanes
+// the operation does not write keep their own value, the identity).
+template <int CTRL>
+__device__ __forceinline__ float dpp_max_stepf(float v) {
+  const int o = __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
+  return fmaxf(v, __builtin_bit_cast(float, o));
+}
+__device__ __forceinline__ float group8_max_dpp(float v) {
+  v = dpp_max_stepf<0xB1>(v);
+  v = dpp_max_stepf<0x4E>(v);
+  return dpp_max_stepf<0x141>(v);
+}
 // Sum over a fully active wave by DPP row operations in a fixed order (no LDS
 // permutes): groups of 8, row_mirror for rows of 16, then row_bcast:15 and
 // :31 leave the total in lane 63, which every lane reads back.

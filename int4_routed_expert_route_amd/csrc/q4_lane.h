@@ -116,11 +116,9 @@ __device__ __forceinline__ void stage_store(XRow<P, GMAX>& dst, const StageRegs<
     float s = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
     float mx = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
                      fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
-#pragma unroll
-    for (int o = 4; o >= 1; o >>= 1) {
-      s += __shfl_xor(s, o, kWave);
-      mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-    }
+    // DPP row operations (the shuffles compiled to LDS permutes)
+    s = group_sum_dpp(s, 8);
+    mx = group8_max_dpp(mx);
     // 2^-e with max * 2^-e in [2^13, 2^14): every value rounds to an integer
     // of magnitude <= 2^14, which four balanced base-16 digits hold
     const bool finite = mx < INFINITY && fabsf(s) < INFINITY;
